@@ -1,0 +1,195 @@
+"""CPU oracle for the quantized GEMM (test infrastructure only).
+
+Only the test-suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The library never does.  It shares no
+code with the HIP path: the arithmetic lives in ``hq_oracle.c`` (plain C,
+fp64 accumulation) and this module only marshals numpy arrays into it.
+
+Functions mirror the C entry points; each returns fp64 outputs for the
+requested rows (all rows when ``rows`` is None).  Functions that the pages
+and the mathematics pin are listed with their pins in the test-suite
+(``tests/test_oracle_pins.py``).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+                               "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = C.CDLL(_LIB)
+        d, i64, p = C.c_double, C.c_int64, C.c_void_p
+        L.hq_oracle_e2m1.restype = d
+        L.hq_oracle_e2m1.argtypes = [C.c_uint]
+        L.hq_oracle_e8m0.restype = d
+        L.hq_oracle_e8m0.argtypes = [C.c_uint]
+        L.hq_oracle_e4m3.restype = d
+        L.hq_oracle_e4m3.argtypes = [C.c_uint]
+        L.hq_oracle_e4m3_encode.restype = C.c_uint
+        L.hq_oracle_e4m3_encode.argtypes = [C.c_float]
+        L.hq_oracle_bf16.restype = d
+        L.hq_oracle_bf16.argtypes = [C.c_uint16]
+        L.hq_oracle_fp16.restype = d
+        L.hq_oracle_fp16.argtypes = [C.c_uint16]
+        L.hq_oracle_quant_act_e4m3.restype = None
+        L.hq_oracle_quant_act_e4m3.argtypes = [i64, i64, p, p, p]
+        L.hq_oracle_gemm_wna16.restype = C.c_int
+        L.hq_oracle_gemm_wna16.argtypes = [i64, i64, i64, i64, C.c_int, p, C.c_int, p, p, p, p, i64, p]
+        L.hq_oracle_gemm_w4a8_mxfp4.restype = C.c_int
+        L.hq_oracle_gemm_w4a8_mxfp4.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
+        L.hq_oracle_gemm_w8a8.restype = C.c_int
+        L.hq_oracle_gemm_w8a8.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p, p]
+        L.hq_oracle_moe_route.restype = C.c_int
+        L.hq_oracle_moe_route.argtypes = [i64, i64, i64, p, p, p, p]
+        L.hq_oracle_moe_mxfp4_bf16.restype = C.c_int
+        L.hq_oracle_moe_mxfp4_bf16.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64, p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _rows(rows, M):
+    if rows is None:
+        return None, M
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    assert r.ndim == 1 and (r.size == 0 or (r.min() >= 0 and r.max() < M))
+    return r, r.size
+
+
+# scalar decoders ---------------------------------------------------------
+
+def e2m1(code: int) -> float:
+    return lib().hq_oracle_e2m1(code)
+
+
+def e8m0(e: int) -> float:
+    return lib().hq_oracle_e8m0(e)
+
+
+def e4m3(code: int) -> float:
+    return lib().hq_oracle_e4m3(code)
+
+
+def e4m3_encode(x: float) -> int:
+    return lib().hq_oracle_e4m3_encode(x)
+
+
+def bf16(bits: int) -> float:
+    return lib().hq_oracle_bf16(bits)
+
+
+def fp16(bits: int) -> float:
+    return lib().hq_oracle_fp16(bits)
+
+
+# activation quantisation -------------------------------------------------
+
+def quant_act_e4m3(x: np.ndarray):
+    """Tokenwise E4M3: returns (codes uint8 [M,K], scales fp32 [M])."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M,), dtype=np.float32)
+    lib().hq_oracle_quant_act_e4m3(M, K, _ptr(x), _ptr(q), _ptr(s))
+    return q, s
+
+
+# GEMMs -----------------------------------------------------------------
+
+def gemm_wna16(A, q, s, z=None, *, N, K, G, a_bf16: bool, w_signed: bool, rows=None):
+    A = _c(A, np.uint16)
+    M = A.shape[0]
+    r, R = _rows(rows, M)
+    out = np.empty((R, N), dtype=np.float64)
+    rc = lib().hq_oracle_gemm_wna16(M, N, K, G, int(a_bf16), _ptr(A), int(w_signed), _ptr(_c(q, np.uint32)),
+                                    _ptr(_c(s, np.uint16)), _ptr(_c(z, np.uint32)), _ptr(r), R, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle gemm_wna16 failed ({rc})")
+    return out
+
+
+def gemm_w4a8_mxfp4(qa, s_a, q, e, *, N, K, rows=None):
+    qa = _c(qa, np.uint8)
+    M = qa.shape[0]
+    r, R = _rows(rows, M)
+    out = np.empty((R, N), dtype=np.float64)
+    rc = lib().hq_oracle_gemm_w4a8_mxfp4(M, N, K, _ptr(qa), _ptr(_c(s_a, np.float32)), _ptr(_c(q, np.uint32)),
+                                         _ptr(_c(e, np.uint8)), _ptr(r), R, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle gemm_w4a8_mxfp4 failed ({rc})")
+    return out
+
+
+def gemm_w8a8(a, s_a, w, s_w, *, rows=None):
+    a = _c(a, np.int8)
+    w = _c(w, np.int8)
+    M, K = a.shape
+    N = w.shape[1]
+    r, R = _rows(rows, M)
+    acc = np.empty((R, N), dtype=np.int64)
+    out = np.empty((R, N), dtype=np.float64)
+    rc = lib().hq_oracle_gemm_w8a8(M, N, K, _ptr(a), _ptr(_c(s_a, np.float32)), _ptr(w), _ptr(_c(s_w, np.float32)),
+                                   _ptr(r), R, _ptr(acc), _ptr(out))
+    if rc == 3:
+        raise OverflowError("int32 accumulator overflow")
+    if rc:
+        raise ValueError(f"oracle gemm_w8a8 failed ({rc})")
+    return acc, out
+
+
+def moe_route(ids: np.ndarray, E: int):
+    """Returns (counts [E], offsets [E+1], perm [T*top_k]) as int64."""
+    ids = _c(ids, np.int32)
+    T, top_k = ids.shape
+    counts = np.empty(E, dtype=np.int64)
+    offsets = np.empty(E + 1, dtype=np.int64)
+    perm = np.empty(T * top_k, dtype=np.int64)
+    if lib().hq_oracle_moe_route(T, top_k, E, _ptr(ids), _ptr(counts), _ptr(offsets), _ptr(perm)):
+        raise ValueError("bad expert id")
+    return counts, offsets, perm
+
+
+def moe_mxfp4_bf16(A, ids, q, e, *, N, K, pairs=None):
+    """Rows of the Indexed output ``[T*top_k, N]`` for the listed pairs (all when None)."""
+    A = _c(A, np.uint16)
+    ids = _c(ids, np.int32)
+    T, top_k = ids.shape
+    E = q.shape[0]
+    p = np.arange(T * top_k, dtype=np.int64) if pairs is None else np.ascontiguousarray(pairs, dtype=np.int64)
+    out = np.empty((p.size, N), dtype=np.float64)
+    rc = lib().hq_oracle_moe_mxfp4_bf16(T, top_k, E, N, K, _ptr(A), _ptr(ids), _ptr(_c(q, np.uint32)),
+                                        _ptr(_c(e, np.uint8)), _ptr(p), p.size, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle moe failed ({rc})")
+    return out

@@ -1,0 +1,292 @@
+/*
+ * hq_oracle.c -- plain CPU oracle for the quantized GEMM  D = A x dequant(W).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library links, includes or calls
+ * this file; only the test-suite, the smoke check and the benchmark's CPU
+ * baseline leg load it.  It shares no code, header, table or helper with the
+ * HIP path.
+ *
+ * What it computes (the plain definition the method reaches up to rounding
+ * order): decode every quantized weight to its real value, decode every
+ * activation to its real value, multiply-accumulate in fp64, apply the
+ * per-token / per-channel epilogue scales last.  The pages ("Humming wird
+ * angekuendigt", section "Eine einheitliche Quantisierungsdarstellung") give the
+ * parameters -- weight format, scale granularity and dtype, zero-points --
+ * and the readers' checklist ("Humming v0.1.0-0.1.4", section
+ * "上手核对清单") compares outputs against an unquantized matmul; that
+ * matmul is what is written here.
+ *
+ * Number formats come from the OCP Microscaling Formats (MX) specification
+ * v1.0 (FP4 E2M1 and the E8M0 scale) and the OCP 8-bit floating point
+ * specification (E4M3, the "FN" variant without infinities).
+ *
+ * Logical layouts (the "export" form):
+ *   4-bit codes   uint32 [K/8][N]   code k=8j+i of column n in bits 4i..4i+3 of word [j][n]
+ *   INT8 weights  int8   [K][N]
+ *   group scales  [K/G][N]  (bf16 / fp16 raw bits)
+ *   zero-points   uint32 [K/G][ceil(N/8)]  column n=8j+i in bits 4i..4i+3 of word [g][j]
+ *   E8M0          uint8  [K/32][N]
+ *   activations   [M][K] row-major
+ *
+ * Every GEMM entry computes only the output rows listed in rows[0..nrows)
+ * (or all rows when rows == NULL) and writes them densely to out[nrows][N].
+ * Loop order is k-outer so that each weight is decoded once per call; the
+ * arithmetic per output is the textbook sum over k in increasing order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* scalar decoders                                                      */
+/* ------------------------------------------------------------------ */
+
+/* OCP MX v1.0, FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit;
+ * exponent field 0 is subnormal with value 0.5*m. */
+double hq_oracle_e2m1(unsigned code)
+{
+    unsigned s = (code >> 3) & 1u, e = (code >> 1) & 3u, m = code & 1u;
+    double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+/* OCP MX v1.0, E8M0 scale: 2^(e-127); 0xFF is NaN. */
+double hq_oracle_e8m0(unsigned e)
+{
+    if ((e & 0xFFu) == 0xFFu) return NAN;
+    return ldexp(1.0, (int)(e & 0xFFu) - 127);
+}
+
+/* OCP FP8 E4M3 (bias 7, no infinities, S.1111.111 is NaN). */
+double hq_oracle_e4m3(unsigned code)
+{
+    unsigned s = (code >> 7) & 1u, e = (code >> 3) & 15u, m = code & 7u;
+    double mag;
+    if (e == 15u && m == 7u) return NAN;
+    if (e == 0) mag = ldexp((double)m, -9);                 /* m/8 * 2^(1-7) */
+    else        mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -mag : mag;
+}
+
+/* Round-to-nearest-even fp32 -> E4M3 with saturation to +-448 (satfinite). */
+unsigned hq_oracle_e4m3_encode(float x)
+{
+    if (isnan(x)) return 0x7Fu;
+    unsigned sign = signbit(x) ? 0x80u : 0u;
+    double a = fabs((double)x);
+    if (a > 448.0) return sign | 0x7Eu;
+    if (a < ldexp(1.0, -6)) {                 /* subnormal range, step 2^-9 */
+        double m = nearbyint(a * 512.0);      /* m == 8 lands on code 0x08 = 2^-6 */
+        return sign | (unsigned)m;
+    }
+    int ex;
+    double f = frexp(a, &ex);                 /* a = f * 2^ex, f in [0.5, 1) */
+    int eu = ex - 1;                          /* a = (2f) * 2^eu, 2f in [1, 2) */
+    double m = nearbyint((2.0 * f - 1.0) * 8.0);
+    if (m == 8.0) { m = 0.0; eu += 1; }
+    unsigned code = (unsigned)(((eu + 7) << 3) | (int)m);
+    if (code > 0x7Eu) code = 0x7Eu;
+    return sign | code;
+}
+
+double hq_oracle_bf16(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+double hq_oracle_fp16(uint16_t h)
+{
+    unsigned s = (h >> 15) & 1u, e = (h >> 10) & 31u, m = h & 1023u;
+    double mag;
+    if (e == 31u) mag = m ? NAN : INFINITY;
+    else if (e == 0) mag = ldexp((double)m, -24);
+    else mag = ldexp(1.0 + (double)m / 1024.0, (int)e - 15);
+    return s ? -mag : mag;
+}
+
+static double act16(int is_bf16, uint16_t v) { return is_bf16 ? hq_oracle_bf16(v) : hq_oracle_fp16(v); }
+
+static unsigned nib_along_k(const uint32_t* q, int64_t N, int64_t k, int64_t n)
+{
+    return (q[(k >> 3) * N + n] >> (4 * (k & 7))) & 15u;
+}
+
+static int64_t row_of(const int64_t* rows, int64_t r) { return rows ? rows[r] : r; }
+
+/* ------------------------------------------------------------------ */
+/* activation quantisation (tokenwise E4M3)                             */
+/* ------------------------------------------------------------------ */
+
+/* Per row m: s[m] = max_k |x| / 448 in fp32 (1 for an all-zero row), and
+ * q[m][k] = E4M3_RNE_satfinite(x / s[m]) with the division in fp32. */
+void hq_oracle_quant_act_e4m3(int64_t M, int64_t K, const float* x, uint8_t* q, float* s)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(x[m * K + k]);
+            if (a > amax) amax = a;
+        }
+        float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+        s[m] = sc;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = x[m * K + k] / sc;
+            q[m * K + k] = (uint8_t)hq_oracle_e4m3_encode(v);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* dense GEMMs                                                          */
+/* ------------------------------------------------------------------ */
+
+/* W4A16: W[k][n] = (code - zero) * s[k/G][n]
+ *   w_signed = 1: code is two's-complement INT4 (-8..7), zero = 0
+ *   w_signed = 0: code is UINT4 (0..15), zero from z (or 0 when z == NULL)
+ * A and s are bf16 (a_bf16 = 1) or fp16 (a_bf16 = 0) raw bits. */
+int hq_oracle_gemm_wna16(int64_t M, int64_t N, int64_t K, int64_t G, int a_bf16,
+                         const uint16_t* A, int w_signed, const uint32_t* q,
+                         const uint16_t* s, const uint32_t* z,
+                         const int64_t* rows, int64_t nrows, double* out)
+{
+    if (K % 8 || G <= 0 || K % G) return 1;
+    int64_t R = rows ? nrows : M;
+    int64_t zw = (N + 7) / 8;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(R * K + 1));
+    if (!a) return 2;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k) a[r * K + k] = act16(a_bf16, A[row_of(rows, r) * K + k]);
+    memset(out, 0, sizeof(double) * (size_t)(R * N));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t g = k / G;
+            int code = (int)nib_along_k(q, N, k, n);
+            int zero = 0;
+            if (w_signed) code = code >= 8 ? code - 16 : code;
+            else if (z) zero = (int)((z[g * zw + n / 8] >> (4 * (n % 8))) & 15u);
+            double w = (double)(code - zero) * act16(a_bf16, s[g * N + n]);
+            for (int64_t r = 0; r < R; ++r) out[r * N + n] += a[r * K + k] * w;
+        }
+    }
+    free(a);
+    return 0;
+}
+
+/* W4A8-MXFP4: W[k][n] = e2m1(code) * 2^(E[k/32][n]-127),
+ * A_real[m][k] = e4m3(qa[m][k]) * s_a[m];  D = A_real x W. */
+int hq_oracle_gemm_w4a8_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* qa,
+                              const float* s_a, const uint32_t* q, const uint8_t* e8,
+                              const int64_t* rows, int64_t nrows, double* out)
+{
+    if (K % 32) return 1;
+    int64_t R = rows ? nrows : M;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(R * K + 1));
+    if (!a) return 2;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k) a[r * K + k] = hq_oracle_e4m3(qa[row_of(rows, r) * K + k]);
+    memset(out, 0, sizeof(double) * (size_t)(R * N));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            double w = hq_oracle_e2m1(nib_along_k(q, N, k, n)) * hq_oracle_e8m0(e8[(k / 32) * N + n]);
+            for (int64_t r = 0; r < R; ++r) out[r * N + n] += a[r * K + k] * w;
+        }
+        for (int64_t r = 0; r < R; ++r) out[r * N + n] *= (double)s_a[row_of(rows, r)];
+    }
+    free(a);
+    return 0;
+}
+
+/* W8A8 INT8: acc[m][n] = sum_k a[m][k] * w[k][n] (exact, int64; returns 3 if
+ * any |acc| exceeds int32), D = acc * s_a[m] * s_w[n]. */
+int hq_oracle_gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t* a, const float* s_a,
+                        const int8_t* w, const float* s_w, const int64_t* rows, int64_t nrows,
+                        int64_t* acc, double* out)
+{
+    int64_t R = rows ? nrows : M;
+    int overflow = 0;
+    memset(acc, 0, sizeof(int64_t) * (size_t)(R * N));
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t wv = w[k * N + n];
+            for (int64_t r = 0; r < R; ++r) acc[r * N + n] += (int64_t)a[row_of(rows, r) * K + k] * wv;
+        }
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t v = acc[r * N + n];
+            if (v > INT32_MAX || v < INT32_MIN) overflow = 1;
+            out[r * N + n] = (double)v * (double)s_a[row_of(rows, r)] * (double)s_w[n];
+        }
+    }
+    return overflow ? 3 : 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* MoE                                                                   */
+/* ------------------------------------------------------------------ */
+
+/* Routing metadata over the flattened pairs p = t*top_k + j:
+ * counts[e] = #pairs routed to e, offsets = exclusive prefix sum (E+1),
+ * perm = pairs stably sorted by expert (counting sort). Returns 1 on a bad id. */
+int hq_oracle_moe_route(int64_t T, int64_t top_k, int64_t E, const int32_t* ids,
+                        int64_t* counts, int64_t* offsets, int64_t* perm)
+{
+    int64_t P = T * top_k;
+    for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        if (ids[p] < 0 || ids[p] >= E) return 1;
+        counts[ids[p]]++;
+    }
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int64_t* cur = (int64_t*)malloc(sizeof(int64_t) * (size_t)(E + 1));
+    if (!cur) return 2;
+    for (int64_t e = 0; e < E; ++e) cur[e] = offsets[e];
+    for (int64_t p = 0; p < P; ++p) perm[cur[ids[p]]++] = p;
+    free(cur);
+    return 0;
+}
+
+/* MoE W4A16-MXFP4 (bf16 tokens): for each requested pair p (t = p / top_k),
+ * out[i][:] = A[t][:] x W_real[ids[p]] with W_real as in the W4A8-MXFP4 entry.
+ * q is expert-stacked [E][K/8][N], e8 is [E][K/32][N]. Each expert's weights
+ * are decoded once for all of its requested pairs. */
+int hq_oracle_moe_mxfp4_bf16(int64_t T, int64_t top_k, int64_t E, int64_t N, int64_t K,
+                             const uint16_t* A, const int32_t* ids, const uint32_t* q,
+                             const uint8_t* e8, const int64_t* pairs, int64_t npairs, double* out)
+{
+    if (K % 32) return 1;
+    for (int64_t i = 0; i < npairs; ++i)
+        if (pairs[i] < 0 || pairs[i] >= T * top_k || ids[pairs[i]] < 0 || ids[pairs[i]] >= E) return 1;
+    memset(out, 0, sizeof(double) * (size_t)(npairs * N));
+    int64_t* sel = (int64_t*)malloc(sizeof(int64_t) * (size_t)(npairs + 1));
+    double* a = (double*)malloc(sizeof(double) * (size_t)(npairs * K + 1));
+    if (!sel || !a) { free(sel); free(a); return 2; }
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t R = 0;
+        for (int64_t i = 0; i < npairs; ++i)
+            if (ids[pairs[i]] == e) sel[R++] = i;
+        if (!R) continue;
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t t = pairs[sel[r]] / top_k;
+            for (int64_t k = 0; k < K; ++k) a[r * K + k] = hq_oracle_bf16(A[t * K + k]);
+        }
+        const uint32_t* qe = q + e * (K / 8) * N;
+        const uint8_t* ee = e8 + e * (K / 32) * N;
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k) {
+                double w = hq_oracle_e2m1(nib_along_k(qe, N, k, n)) * hq_oracle_e8m0(ee[(k / 32) * N + n]);
+                for (int64_t r = 0; r < R; ++r) out[sel[r] * N + n] += a[r * K + k] * w;
+            }
+        }
+    }
+    free(sel);
+    free(a);
+    return 0;
+}
