@@ -1,0 +1,253 @@
+// hq_api.cpp -- the extern "C" boundary of libhq: descriptor validation,
+// sizing, repack, workspace queries and per-call dispatch to the kernels.
+//
+// Dispatch follows the pages' scheme of configurations prepared per range of
+// input sizes and selected at run time ("Humming wird angekuendigt", section
+// "Tuning und JIT-Kompilierung fuer jeden Workload"), with kernels compiled
+// ahead of time.  The host path does O(1) checks and no allocation, in the
+// spirit of the launch-overhead work in "Humming v0.1.0-0.1.4", section
+// "v0.1.1".
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "hq_common.h"
+#include "hq_internal.h"
+
+namespace hq {
+
+namespace {
+thread_local char g_err[512] = {0};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+}  // namespace
+
+hq_status set_error(hq_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+static hq_status ok() {
+    g_err[0] = 0;
+    return HQ_OK;
+}
+
+hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
+    if (!d) return set_error(HQ_ERR_INVALID_ARG, "descriptor is NULL");
+    if (d->abi_version != HQ_ABI_VERSION)
+        return set_error(HQ_ERR_ABI, "descriptor abi_version %d, library %d", d->abi_version, HQ_ABI_VERSION);
+    for (int i = 0; i < 3; ++i)
+        if (d->reserved[i]) return set_error(HQ_ERR_INVALID_ARG, "reserved fields must be zero");
+    if (d->N < 1 || d->K < 1 || d->N > (1LL << 24) || d->K > (1LL << 24))
+        return set_error(HQ_ERR_INVALID_ARG, "N=%lld K=%lld out of range [1, 2^24]", (long long)d->N, (long long)d->K);
+    if (d->num_experts < 0 || d->num_experts > 4096)
+        return set_error(HQ_ERR_INVALID_ARG, "num_experts=%d out of range [0, 4096]", d->num_experts);
+    if (d->scale2 != HQ_S2_NONE) return set_error(HQ_ERR_UNSUPPORTED, "second-level scales are not supported");
+    LayerInfo I{};
+    I.N = d->N;
+    I.K = d->K;
+    I.Np = pad16(d->N);
+    I.E = d->num_experts ? d->num_experts : 1;
+    I.G = d->group_size;
+    const int a = d->a_dtype, w = d->w_dtype;
+    if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT4 || w == HQ_DT_UINT4)) {
+        I.kind = Kind::WNA16;
+        I.a_bf16 = a == HQ_DT_BF16;
+        I.zp = w == HQ_DT_UINT4;
+        if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 INT4/UINT4 is dense-only");
+        if (d->w_scale_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 scale dtype must equal the activation dtype");
+        if (d->w_scale_gran != HQ_GRAN_PER_GROUP_K) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 needs per-group scales");
+        if (d->group_size < 128 || d->group_size % 128 || d->K % d->group_size)
+            return set_error(HQ_ERR_UNSUPPORTED, "W4A16 group_size=%d must be a multiple of 128 dividing K=%lld",
+                             d->group_size, (long long)d->K);
+        if (d->zp_dtype != (I.zp ? HQ_DT_UINT4 : HQ_DT_NONE))
+            return set_error(HQ_ERR_UNSUPPORTED, "zero-points: UINT4 codes need UINT4 zero-points, INT4 codes none");
+        if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 takes no activation scale");
+        if (d->out_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 output dtype must equal the activation dtype");
+    } else if (w == HQ_DT_FP4_E2M1 && (a == HQ_DT_FP8_E4M3 || a == HQ_DT_BF16)) {
+        const bool moe = d->num_experts > 0;
+        if (a == HQ_DT_FP8_E4M3) {
+            if (moe) return set_error(HQ_ERR_UNSUPPORTED, "W4A8-MXFP4 MoE is not built");
+            I.kind = Kind::W4A8_MX;
+            if (d->a_scale != HQ_ASCALE_PER_TOKEN_F32) return set_error(HQ_ERR_UNSUPPORTED, "W4A8 needs per-token fp32 activation scales");
+        } else {
+            if (!moe) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x MXFP4 is built for MoE layers only");
+            I.kind = Kind::MOE_MX_BF16;
+            if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "bf16 MoE takes no activation scale");
+        }
+        if (d->w_scale_dtype != HQ_DT_E8M0 || d->w_scale_gran != HQ_GRAN_PER_GROUP_K || d->group_size != 32)
+            return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 needs E8M0 scales per 32 K elements");
+        if (d->K % 128) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 needs K %% 128 == 0 (K=%lld)", (long long)d->K);
+        if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 takes no zero-points");
+        if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 paths output bf16");
+        I.G = 32;
+    } else if (a == HQ_DT_INT8 && w == HQ_DT_INT8) {
+        I.kind = Kind::W8A8;
+        if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "W8A8 is dense-only");
+        if (d->a_scale != HQ_ASCALE_PER_TOKEN_F32) return set_error(HQ_ERR_UNSUPPORTED, "W8A8 needs per-token fp32 activation scales");
+        if (d->w_scale_dtype != HQ_DT_FP32 || d->w_scale_gran != HQ_GRAN_PER_CHANNEL)
+            return set_error(HQ_ERR_UNSUPPORTED, "W8A8 needs fp32 per-channel weight scales");
+        if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "W8A8 takes no zero-points");
+        if (d->K % 64) return set_error(HQ_ERR_UNSUPPORTED, "W8A8 needs K %% 64 == 0 (K=%lld)", (long long)d->K);
+        if (d->out_dtype != HQ_DT_BF16 && d->out_dtype != HQ_DT_INT32)
+            return set_error(HQ_ERR_UNSUPPORTED, "W8A8 outputs bf16 or raw int32");
+        I.out_i32 = d->out_dtype == HQ_DT_INT32;
+        I.G = d->K;
+    } else {
+        return set_error(HQ_ERR_UNSUPPORTED, "unsupported activation/weight dtype pair (%d, %d)", a, w);
+    }
+    if (I.Np / 16 > kMaxCounters) return set_error(HQ_ERR_UNSUPPORTED, "N too large");
+    *L = I;
+    return HQ_OK;
+}
+
+static size_t dense_workspace(const LayerInfo& L, int64_t M) {
+    switch (L.kind) {
+        case Kind::WNA16: return wna16_workspace(M, L.N, L.K, (int)L.G);
+        default: return 0;
+    }
+}
+
+static hq_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return set_error(HQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace hq
+
+using namespace hq;
+
+extern "C" {
+
+int32_t hq_abi_version(void) { return HQ_ABI_VERSION; }
+
+const char* hq_status_str(hq_status s) {
+    switch (s) {
+        case HQ_OK: return "HQ_OK";
+        case HQ_ERR_INVALID_ARG: return "HQ_ERR_INVALID_ARG";
+        case HQ_ERR_UNSUPPORTED: return "HQ_ERR_UNSUPPORTED";
+        case HQ_ERR_ALIGNMENT: return "HQ_ERR_ALIGNMENT";
+        case HQ_ERR_WORKSPACE: return "HQ_ERR_WORKSPACE";
+        case HQ_ERR_ABI: return "HQ_ERR_ABI";
+        case HQ_ERR_HIP: return "HQ_ERR_HIP";
+    }
+    return "HQ_ERR_UNKNOWN";
+}
+
+const char* hq_last_error(void) { return g_err; }
+
+hq_status hq_desc_validate(const hq_layer_desc* desc) {
+    LayerInfo L;
+    hq_status st = describe(desc, &L);
+    return st == HQ_OK ? ok() : st;
+}
+
+hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w, size_t* s, size_t* z, size_t* s2) {
+    LayerInfo L;
+    hq_status st = describe(desc, &L);
+    if (st != HQ_OK) return st;
+    if (!w || !s || !z || !s2) return set_error(HQ_ERR_INVALID_ARG, "size outputs must be non-NULL");
+    packed_sizes(L, w, s, z, s2);
+    return ok();
+}
+
+hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale, const void* zp,
+                    const void* scale2, void* w_out, void* s_out, void* z_out, void* s2_out) {
+    LayerInfo L;
+    hq_status st = describe(desc, &L);
+    if (st != HQ_OK) return st;
+    if (!w || !scale || !w_out || !s_out) return set_error(HQ_ERR_INVALID_ARG, "weights and scales are required");
+    const bool need_z = L.kind == Kind::WNA16 && L.zp;
+    if (need_z && (!zp || !z_out)) return set_error(HQ_ERR_INVALID_ARG, "zero-points are required for UINT4 weights");
+    if (!need_z && (zp || z_out)) return set_error(HQ_ERR_INVALID_ARG, "zero-point buffers must be NULL for this format");
+    if (scale2 || s2_out) return set_error(HQ_ERR_INVALID_ARG, "second-level scale buffers must be NULL");
+    repack_all(L, w, scale, zp, w_out, s_out, z_out);
+    return ok();
+}
+
+hq_status hq_workspace_bytes(const hq_layer_desc* desc, int64_t M_or_T, int32_t top_k, size_t* bytes) {
+    LayerInfo L;
+    hq_status st = describe(desc, &L);
+    if (st != HQ_OK) return st;
+    if (!bytes) return set_error(HQ_ERR_INVALID_ARG, "bytes is NULL");
+    if (M_or_T < 0 || M_or_T > (1LL << 30)) return set_error(HQ_ERR_INVALID_ARG, "M/T out of range");
+    (void)top_k;
+    *bytes = desc->num_experts ? 0 : dense_workspace(L, M_or_T);
+    return ok();
+}
+
+hq_status hq_workspace_init(void* workspace, size_t bytes, hq_stream_t stream) {
+    if (!bytes) return ok();
+    if (!workspace) return set_error(HQ_ERR_INVALID_ARG, "workspace is NULL");
+    if (!aligned16(workspace) || bytes % 16) return set_error(HQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned and sized");
+    return hip_status(fill_zero_launch(workspace, bytes, (hipStream_t)stream), "hq_workspace_init");
+}
+
+hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const float* a_scale,
+                  const void* w, const void* s, const void* z, const void* s2, void* D,
+                  void* workspace, size_t ws_bytes, hq_stream_t stream) {
+    LayerInfo L;
+    hq_status st = describe(desc, &L);
+    if (st != HQ_OK) return st;
+    if (desc->num_experts) return set_error(HQ_ERR_INVALID_ARG, "hq_gemm takes a dense descriptor (num_experts == 0)");
+    if (M < 0 || M > (1LL << 30)) return set_error(HQ_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+    if (M == 0) return ok();
+    if (!A || !w || !s || !D) return set_error(HQ_ERR_INVALID_ARG, "A, w, s and D are required");
+    const bool need_z = L.kind == Kind::WNA16 && L.zp;
+    if (need_z != (z != nullptr)) return set_error(HQ_ERR_INVALID_ARG, need_z ? "zero-points required" : "z must be NULL");
+    const bool need_as = desc->a_scale == HQ_ASCALE_PER_TOKEN_F32;
+    if (need_as != (a_scale != nullptr)) return set_error(HQ_ERR_INVALID_ARG, need_as ? "a_scale required" : "a_scale must be NULL");
+    if (s2) return set_error(HQ_ERR_INVALID_ARG, "s2 must be NULL");
+    if (!aligned16(A) || !aligned16(w) || !aligned16(s) || !aligned16(D) || (z && !aligned16(z)) ||
+        (a_scale && !aligned16(a_scale)))
+        return set_error(HQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    const size_t need = dense_workspace(L, M);
+    if (need) {
+        if (!workspace || ws_bytes < need)
+            return set_error(HQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? ws_bytes : (size_t)0);
+        if (!aligned16(workspace)) return set_error(HQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    }
+    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, a_scale, w, s, z, D, workspace, ws_bytes, (hipStream_t)stream};
+    switch (L.kind) {
+        case Kind::WNA16: return hip_status(wna16_launch(a, L.a_bf16, L.zp), "hq_gemm(W4A16)");
+        default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind is not built yet");
+    }
+}
+
+hq_status hq_moe_gemm(const hq_layer_desc* desc, int32_t mode, int64_t T, int32_t top_k, const void* A,
+                      const float* a_scale, const int32_t* topk_ids, const int32_t* expert_offsets,
+                      const void* w, const void* s, const void* z, const void* s2, void* D,
+                      void* workspace, size_t ws_bytes, hq_stream_t stream) {
+    (void)mode; (void)T; (void)top_k; (void)A; (void)a_scale; (void)topk_ids; (void)expert_offsets;
+    (void)w; (void)s; (void)z; (void)s2; (void)D; (void)workspace; (void)ws_bytes; (void)stream;
+    LayerInfo L;
+    hq_status st = describe(desc, &L);
+    if (st != HQ_OK) return st;
+    return set_error(HQ_ERR_UNSUPPORTED, "MoE kernels are not built yet");
+}
+
+hq_status hq_quantize_act(int32_t out_dtype, int64_t M, int64_t K, const float* x, void* q, float* s,
+                          hq_stream_t stream) {
+    (void)out_dtype; (void)M; (void)K; (void)x; (void)q; (void)s; (void)stream;
+    return set_error(HQ_ERR_UNSUPPORTED, "activation quantisation is not built yet");
+}
+
+hq_status hq_moe_align(int64_t T, int32_t top_k, int32_t num_experts, const int32_t* topk_ids,
+                       int32_t* expert_offsets, int32_t* sorted_pairs, void* workspace, size_t ws_bytes,
+                       hq_stream_t stream) {
+    (void)T; (void)top_k; (void)num_experts; (void)topk_ids; (void)expert_offsets; (void)sorted_pairs;
+    (void)workspace; (void)ws_bytes; (void)stream;
+    return set_error(HQ_ERR_UNSUPPORTED, "routing metadata is not built yet");
+}
+
+hq_status hq_moe_gather(int32_t dtype, int64_t T, int32_t top_k, int64_t K, const void* A,
+                        const int32_t* sorted_pairs, void* A_sorted, hq_stream_t stream) {
+    (void)dtype; (void)T; (void)top_k; (void)K; (void)A; (void)sorted_pairs; (void)A_sorted; (void)stream;
+    return set_error(HQ_ERR_UNSUPPORTED, "gather is not built yet");
+}
+
+}  // extern "C"

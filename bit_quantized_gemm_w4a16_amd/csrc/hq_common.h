@@ -1,0 +1,39 @@
+// Host-only definitions shared by the C-ABI layer and the repack code.
+// No HIP types: this header compiles with any C++17 compiler.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/hq.h"
+
+namespace hq {
+
+// The operation families the kernels implement (one per supported row of the
+// descriptor table in include/hq.h).
+enum class Kind {
+    WNA16,        // bf16/fp16 A, INT4 or UINT4+zp W, 16-bit group scales
+    W4A8_MX,      // fp8-e4m3 A (per-token fp32 scale), e2m1 W, E8M0 per 32 K
+    W8A8,         // int8 A (per-token fp32 scale), int8 W, fp32 per-channel
+    MOE_MX_BF16,  // MoE: bf16 A, e2m1 W, E8M0 per 32 K
+};
+
+struct LayerInfo {
+    Kind kind;
+    int64_t N, K, Np, E, G;
+    bool a_bf16;   // WNA16: activations (and scales, output) are bf16
+    bool zp;       // WNA16: UINT4 codes with UINT4 zero-points
+    bool out_i32;  // W8A8: raw int32 accumulators
+};
+
+// Validates a descriptor; fills `info` on success.  Sets the thread-local
+// error message on failure.
+hq_status describe(const hq_layer_desc* d, LayerInfo* info);
+
+void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s2);
+void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z, void* w_out,
+                void* s_out, void* z_out);
+
+hq_status set_error(hq_status st, const char* fmt, ...);
+
+}  // namespace hq

@@ -1,0 +1,61 @@
+// Device-side helpers for the gfx950 kernels: vector types, MFMA wrappers,
+// 4-bit decode, stores.  Header-only, included by the *.hip files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace hq {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+union Frag8 {  // eight 16-bit values = one MFMA A/B operand of 16x16x32 f16/bf16
+    v4u u;
+    v8h h;
+    v8bf b;
+};
+
+// One 16x16x32 MFMA step with fp32 accumulation.  Lane l supplies row/column
+// (l & 15) and eight K values; A and B use the same K labelling, so any
+// consistent assignment of K values to (lane >> 4, element) is a valid GEMM.
+template <bool BF16>
+__device__ __forceinline__ v4f mfma16(const Frag8& a, const Frag8& b, v4f c) {
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.b, b.b, c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.h, b.h, c, 0, 0, 0);
+}
+
+// fp32 -> bf16 / fp16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+    _Float16 h = (_Float16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+template <bool BF16>
+__device__ __forceinline__ uint16_t f32_to_16(float f) {
+    if constexpr (BF16) return f32_to_bf16_bits(f);
+    else return f32_to_f16_bits(f);
+}
+template <bool BF16>
+__device__ __forceinline__ float bits16_to_f32(uint16_t v) {
+    if constexpr (BF16) return __uint_as_float((uint32_t)v << 16);
+    else return (float)__builtin_bit_cast(_Float16, v);
+}
+
+// 16-byte global loads: a non-temporal hint for data read exactly once.
+__device__ __forceinline__ v4u ld_nt(const v4u* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ v4u ld16(const void* p) { return *(const v4u*)p; }
+
+}  // namespace hq

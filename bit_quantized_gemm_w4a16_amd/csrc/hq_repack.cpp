@@ -1,0 +1,165 @@
+// hq_repack: host-side transform from the logical export form to the packed
+// layout every hq kernel reads.  Integer bit permutation only (exact).
+//
+// The pages describe this step as converting each export format into one
+// standard representation and then validating, padding and repacking it into
+// a layout suited to the target kernel ("Humming wird angekuendigt", sections
+// "Eine einheitliche Quantisierungsdarstellung" and "Tuning und
+// JIT-Kompilierung fuer jeden Workload").  The packed layout below is our own,
+// chosen for CDNA4: a wavefront's 64 lanes read 1 KB contiguous with one
+// 16-byte load each, and that 16-byte load is directly the MFMA operand
+// fragment (see include/hq.h for the exact layout).
+#include <cstdint>
+#include <cstring>
+
+#include "hq_common.h"
+
+namespace hq {
+
+namespace {
+
+// nibble position p of a packed INT4/UINT4 word holds element kPairOrder[p]
+constexpr int kPairOrder[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+
+inline uint32_t logical_word(const uint32_t* w, int64_t N, int64_t j, int64_t n) {
+    return w[j * N + n];
+}
+
+void repack_4bit(const LayerInfo& L, const uint32_t* w, uint8_t* out, bool pair_order) {
+    const int64_t N = L.N, K = L.K, nst = L.Np / 16, nc = K / 128;
+    for (int64_t e = 0; e < L.E; ++e) {
+        const uint32_t* we = w + e * (K / 8) * N;
+        uint32_t* oe = (uint32_t*)(out + (size_t)e * (size_t)(nst * nc * 1024));
+        for (int64_t st = 0; st < nst; ++st)
+            for (int64_t c = 0; c < nc; ++c)
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int64_t n = st * 16 + (lane & 15);
+                    for (int t = 0; t < 4; ++t) {
+                        const int64_t j = (c * 128 + 32 * (lane >> 4) + 8 * t) / 8;
+                        const uint32_t src = n < N ? logical_word(we, N, j, n) : 0u;
+                        uint32_t dst = src;
+                        if (pair_order) {
+                            dst = 0;
+                            for (int p = 0; p < 8; ++p) dst |= ((src >> (4 * kPairOrder[p])) & 15u) << (4 * p);
+                        }
+                        oe[((st * nc + c) * 64 + lane) * 4 + t] = dst;
+                    }
+                }
+    }
+}
+
+void repack_int8(const LayerInfo& L, const int8_t* w, int8_t* out) {
+    const int64_t N = L.N, K = L.K, nst = L.Np / 16, nc = K / 64;
+    for (int64_t e = 0; e < L.E; ++e) {
+        const int8_t* we = w + e * K * N;
+        int8_t* oe = out + (size_t)e * (size_t)(nst * nc * 1024);
+        for (int64_t st = 0; st < nst; ++st)
+            for (int64_t c = 0; c < nc; ++c)
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int64_t n = st * 16 + (lane & 15);
+                    for (int j = 0; j < 16; ++j) {
+                        const int64_t k = c * 64 + 16 * (lane >> 4) + j;
+                        oe[((st * nc + c) * 64 + lane) * 16 + j] = n < N ? we[k * N + n] : 0;
+                    }
+                }
+    }
+}
+
+void repack_scale16(const LayerInfo& L, const uint16_t* s, uint16_t* out, uint16_t one) {
+    const int64_t N = L.N, nst = L.Np / 16, ng = L.K / L.G;
+    for (int64_t e = 0; e < L.E; ++e) {
+        const uint16_t* se = s + e * ng * N;
+        uint16_t* oe = out + e * nst * ng * 16;
+        for (int64_t st = 0; st < nst; ++st)
+            for (int64_t g = 0; g < ng; ++g)
+                for (int i = 0; i < 16; ++i) {
+                    const int64_t n = st * 16 + i;
+                    oe[(st * ng + g) * 16 + i] = n < N ? se[g * N + n] : one;
+                }
+    }
+}
+
+void repack_zero4(const LayerInfo& L, const uint32_t* z, uint64_t* out) {
+    const int64_t N = L.N, nst = L.Np / 16, ng = L.K / L.G, zw = (N + 7) / 8;
+    for (int64_t e = 0; e < L.E; ++e) {
+        const uint32_t* ze = z + e * ng * zw;
+        uint64_t* oe = out + e * nst * ng;
+        for (int64_t st = 0; st < nst; ++st)
+            for (int64_t g = 0; g < ng; ++g) {
+                uint64_t v = 0;
+                for (int i = 0; i < 16; ++i) {
+                    const int64_t n = st * 16 + i;
+                    const uint64_t code = n < N ? (ze[g * zw + n / 8] >> (4 * (n % 8))) & 15u : 0u;
+                    v |= code << (4 * i);
+                }
+                oe[st * ng + g] = v;
+            }
+    }
+}
+
+void repack_e8m0(const LayerInfo& L, const uint8_t* s, uint8_t* out) {
+    const int64_t N = L.N, nst = L.Np / 16, nc = L.K / 128, c4n = (nc + 3) / 4, nb = L.K / 32;
+    for (int64_t e = 0; e < L.E; ++e) {
+        const uint8_t* se = s + e * nb * N;
+        uint8_t* oe = out + (size_t)e * (size_t)(nst * c4n * 256);
+        for (int64_t st = 0; st < nst; ++st)
+            for (int64_t c4 = 0; c4 < c4n; ++c4)
+                for (int lane = 0; lane < 64; ++lane)
+                    for (int b = 0; b < 4; ++b) {
+                        const int64_t n = st * 16 + (lane & 15), c = 4 * c4 + b;
+                        uint8_t v = 127;
+                        if (c < nc && n < N) v = se[(4 * c + (lane >> 4)) * N + n];
+                        oe[((st * c4n + c4) * 64 + lane) * 4 + b] = v;
+                    }
+    }
+}
+
+void repack_chan32(const LayerInfo& L, const float* s, float* out) {
+    for (int64_t e = 0; e < L.E; ++e)
+        for (int64_t n = 0; n < L.Np; ++n) out[e * L.Np + n] = n < L.N ? s[e * L.N + n] : 1.0f;
+}
+
+}  // namespace
+
+void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s2) {
+    const size_t E = (size_t)L.E, nst = (size_t)(L.Np / 16);
+    *w = *s = *z = *s2 = 0;
+    switch (L.kind) {
+        case Kind::WNA16:
+            *w = E * nst * (size_t)(L.K / 128) * 1024;
+            *s = E * nst * (size_t)(L.K / L.G) * 16 * 2;
+            if (L.zp) *z = E * nst * (size_t)(L.K / L.G) * 8;
+            break;
+        case Kind::W4A8_MX:
+        case Kind::MOE_MX_BF16:
+            *w = E * nst * (size_t)(L.K / 128) * 1024;
+            *s = E * nst * (size_t)((L.K / 128 + 3) / 4) * 256;
+            break;
+        case Kind::W8A8:
+            *w = E * nst * (size_t)(L.K / 64) * 1024;
+            *s = E * (size_t)L.Np * 4;
+            break;
+    }
+}
+
+void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z, void* w_out,
+                void* s_out, void* z_out) {
+    switch (L.kind) {
+        case Kind::WNA16:
+            repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, true);
+            repack_scale16(L, (const uint16_t*)s, (uint16_t*)s_out, L.a_bf16 ? 0x3F80 : 0x3C00);
+            if (L.zp) repack_zero4(L, (const uint32_t*)z, (uint64_t*)z_out);
+            break;
+        case Kind::W4A8_MX:
+        case Kind::MOE_MX_BF16:
+            repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, false);
+            repack_e8m0(L, (const uint8_t*)s, (uint8_t*)s_out);
+            break;
+        case Kind::W8A8:
+            repack_int8(L, (const int8_t*)w, (int8_t*)w_out);
+            repack_chan32(L, (const float*)s, (float*)s_out);
+            break;
+    }
+}
+
+}  // namespace hq

@@ -1,0 +1,211 @@
+"""ctypes binding of libhq (include/hq.h).  Argument marshalling only.
+
+Every function here has the name of the C entry point it wraps and calls it
+directly; all arithmetic runs in the library's HIP kernels (device entry
+points) or its C++ repack (host).  PyTorch is used only to hold device memory
+and to name the current HIP stream.  A missing library raises at import of
+the first call: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhq.so")
+
+HQ_ABI_VERSION = 1
+
+# hq_status
+HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_ALIGNMENT, HQ_ERR_WORKSPACE, HQ_ERR_ABI, HQ_ERR_HIP = range(7)
+# hq_dtype
+(HQ_DT_NONE, HQ_DT_BF16, HQ_DT_FP16, HQ_DT_FP32, HQ_DT_FP8_E4M3, HQ_DT_INT8, HQ_DT_INT4, HQ_DT_UINT4,
+ HQ_DT_FP4_E2M1, HQ_DT_E8M0, HQ_DT_INT32) = range(11)
+HQ_GRAN_NONE, HQ_GRAN_PER_GROUP_K, HQ_GRAN_PER_CHANNEL = range(3)
+HQ_ASCALE_NONE, HQ_ASCALE_PER_TOKEN_F32 = range(2)
+HQ_S2_NONE = 0
+HQ_MOE_INDEXED, HQ_MOE_GROUPED = 1, 2
+
+
+class HQError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: status {status}: {msg}")
+        self.status = status
+
+
+class hq_layer_desc(C.Structure):
+    _fields_ = [
+        ("abi_version", C.c_int32), ("num_experts", C.c_int32),
+        ("N", C.c_int64), ("K", C.c_int64),
+        ("a_dtype", C.c_int32), ("a_scale", C.c_int32), ("w_dtype", C.c_int32),
+        ("w_scale_dtype", C.c_int32), ("w_scale_gran", C.c_int32), ("group_size", C.c_int32),
+        ("zp_dtype", C.c_int32), ("scale2", C.c_int32), ("out_dtype", C.c_int32),
+        ("reserved", C.c_int32 * 3),
+    ]
+
+
+_lib = None
+
+_P = C.c_void_p
+_SIGS = {
+    "hq_abi_version": (C.c_int32, []),
+    "hq_status_str": (C.c_char_p, [C.c_int]),
+    "hq_last_error": (C.c_char_p, []),
+    "hq_desc_validate": (C.c_int, [_P]),
+    "hq_repacked_bytes": (C.c_int, [_P, _P, _P, _P, _P]),
+    "hq_repack": (C.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "hq_workspace_bytes": (C.c_int, [_P, C.c_int64, C.c_int32, _P]),
+    "hq_workspace_init": (C.c_int, [_P, C.c_size_t, _P]),
+    "hq_gemm": (C.c_int, [_P, C.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "hq_moe_gemm": (C.c_int, [_P, C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                              C.c_size_t, _P]),
+    "hq_quantize_act": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, _P, _P, _P, _P]),
+    "hq_moe_align": (C.c_int, [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]),
+    "hq_moe_gather": (C.c_int, [C.c_int32, C.c_int64, C.c_int32, C.c_int64, _P, _P, _P, _P]),
+}
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libhq.so not built at {LIB_PATH}: run python -m bit_quantized_gemm_w4a16_amd.build")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        if L.hq_abi_version() != HQ_ABI_VERSION:
+            raise ImportError("libhq ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != HQ_OK:
+        raise HQError(status, where, lib().hq_last_error().decode())
+
+
+def _dp(t):
+    """Device (or host numpy) pointer of a tensor/array; None -> NULL."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# descriptors
+# ---------------------------------------------------------------------------
+
+def make_desc(N, K, a_dtype, w_dtype, w_scale_dtype, w_scale_gran, group_size, out_dtype,
+              zp_dtype=HQ_DT_NONE, a_scale=HQ_ASCALE_NONE, num_experts=0) -> hq_layer_desc:
+    d = hq_layer_desc()
+    d.abi_version = HQ_ABI_VERSION
+    d.num_experts = num_experts
+    d.N, d.K = N, K
+    d.a_dtype, d.a_scale, d.w_dtype = a_dtype, a_scale, w_dtype
+    d.w_scale_dtype, d.w_scale_gran, d.group_size = w_scale_dtype, w_scale_gran, group_size
+    d.zp_dtype, d.scale2, d.out_dtype = zp_dtype, HQ_S2_NONE, out_dtype
+    return d
+
+
+def desc_w4a16(N, K, group_size=128, bf16=True, zp=False) -> hq_layer_desc:
+    a = HQ_DT_BF16 if bf16 else HQ_DT_FP16
+    return make_desc(N, K, a, HQ_DT_UINT4 if zp else HQ_DT_INT4, a, HQ_GRAN_PER_GROUP_K, group_size, a,
+                     zp_dtype=HQ_DT_UINT4 if zp else HQ_DT_NONE)
+
+
+def desc_w4a8_mxfp4(N, K) -> hq_layer_desc:
+    return make_desc(N, K, HQ_DT_FP8_E4M3, HQ_DT_FP4_E2M1, HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K, 32, HQ_DT_BF16,
+                     a_scale=HQ_ASCALE_PER_TOKEN_F32)
+
+
+def desc_w8a8(N, K, raw_int32=False) -> hq_layer_desc:
+    return make_desc(N, K, HQ_DT_INT8, HQ_DT_INT8, HQ_DT_FP32, HQ_GRAN_PER_CHANNEL, K,
+                     HQ_DT_INT32 if raw_int32 else HQ_DT_BF16, a_scale=HQ_ASCALE_PER_TOKEN_F32)
+
+
+def desc_moe_mxfp4(E, N, K) -> hq_layer_desc:
+    return make_desc(N, K, HQ_DT_BF16, HQ_DT_FP4_E2M1, HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K, 32, HQ_DT_BF16,
+                     num_experts=E)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def hq_desc_validate(desc: hq_layer_desc) -> None:
+    _check(lib().hq_desc_validate(C.byref(desc)), "hq_desc_validate")
+
+
+def hq_repacked_bytes(desc: hq_layer_desc):
+    w, s, z, s2 = C.c_size_t(), C.c_size_t(), C.c_size_t(), C.c_size_t()
+    _check(lib().hq_repacked_bytes(C.byref(desc), C.byref(w), C.byref(s), C.byref(z), C.byref(s2)),
+           "hq_repacked_bytes")
+    return w.value, s.value, z.value, s2.value
+
+
+def hq_repack(desc: hq_layer_desc, w: np.ndarray, scale: np.ndarray, zp: np.ndarray | None = None):
+    """Host repack; returns the packed (w, s, z) as uint8 numpy arrays (z None if unused)."""
+    wb, sb, zb, _ = hq_repacked_bytes(desc)
+    w = np.ascontiguousarray(w)
+    scale = np.ascontiguousarray(scale)
+    zp = None if zp is None else np.ascontiguousarray(zp)
+    wo = np.empty(wb, dtype=np.uint8)
+    so = np.empty(sb, dtype=np.uint8)
+    zo = np.empty(zb, dtype=np.uint8) if zb else None
+    _check(lib().hq_repack(C.byref(desc), _dp(w), _dp(scale), _dp(zp), None, _dp(wo), _dp(so), _dp(zo), None),
+           "hq_repack")
+    return wo, so, zo
+
+
+def hq_workspace_bytes(desc: hq_layer_desc, M_or_T: int, top_k: int = 0) -> int:
+    b = C.c_size_t()
+    _check(lib().hq_workspace_bytes(C.byref(desc), M_or_T, top_k, C.byref(b)), "hq_workspace_bytes")
+    return b.value
+
+
+def hq_workspace_init(workspace, nbytes: int, stream=None) -> None:
+    _check(lib().hq_workspace_init(_dp(workspace), nbytes, _stream(stream)), "hq_workspace_init")
+
+
+def hq_gemm(desc, M, A, a_scale, w, s, z, D, workspace=None, ws_bytes=0, stream=None) -> None:
+    _check(lib().hq_gemm(C.byref(desc), M, _dp(A), _dp(a_scale), _dp(w), _dp(s), _dp(z), None, _dp(D),
+                         _dp(workspace), ws_bytes, _stream(stream)), "hq_gemm")
+
+
+def hq_moe_gemm(desc, mode, T, top_k, A, a_scale, topk_ids, expert_offsets, w, s, z, D, workspace=None,
+                ws_bytes=0, stream=None) -> None:
+    _check(lib().hq_moe_gemm(C.byref(desc), mode, T, top_k, _dp(A), _dp(a_scale), _dp(topk_ids),
+                             _dp(expert_offsets), _dp(w), _dp(s), _dp(z), None, _dp(D), _dp(workspace),
+                             ws_bytes, _stream(stream)), "hq_moe_gemm")
+
+
+def hq_quantize_act(out_dtype, M, K, x, q, s, stream=None) -> None:
+    _check(lib().hq_quantize_act(out_dtype, M, K, _dp(x), _dp(q), _dp(s), _stream(stream)), "hq_quantize_act")
+
+
+def hq_moe_align(T, top_k, num_experts, topk_ids, expert_offsets, sorted_pairs, workspace=None, ws_bytes=0,
+                 stream=None) -> None:
+    _check(lib().hq_moe_align(T, top_k, num_experts, _dp(topk_ids), _dp(expert_offsets), _dp(sorted_pairs),
+                              _dp(workspace), ws_bytes, _stream(stream)), "hq_moe_align")
+
+
+def hq_moe_gather(dtype, T, top_k, K, A, sorted_pairs, A_sorted, stream=None) -> None:
+    _check(lib().hq_moe_gather(dtype, T, top_k, K, _dp(A), _dp(sorted_pairs), _dp(A_sorted), _stream(stream)),
+           "hq_moe_gather")

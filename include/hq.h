@@ -1,0 +1,277 @@
+/*
+ * hq.h -- C ABI of the hq quantized-GEMM library for AMD Instinct MI355X (gfx950).
+ *
+ *   D[M,N] = A[M,K] x dequant(W[K,N])
+ *
+ * for weight-only W4A16 (symmetric INT4, or UINT4 with zero-points; group
+ * scales along K), W4A8 with MXFP4 weights (e2m1 codes, E8M0 scale per 32 K)
+ * and tokenwise FP8-e4m3 activations, W8A8 INT8 with a per-token x
+ * per-channel epilogue, and the MoE Indexed / Grouped variants.
+ *
+ * Sources.  The operation and its parameters follow the Humming pages:
+ *  - "Humming wird angekuendigt", section "Eine einheitliche
+ *    Quantisierungsdarstellung": weights, scales, zero-points and second-level
+ *    scales are separate tensors; weight format, scale granularity and scale
+ *    dtype are separate parameters; activations have their own format.
+ *  - same page, section "Tuning und JIT-Kompilierung fuer jeden Workload":
+ *    preprocessing validates, pads and repacks into a kernel layout; a layer
+ *    description (shapes, dtypes, quantization parameters) plus a compute
+ *    description (GEMM type, input-scale layout) configure the kernel; the
+ *    kernel is chosen per input-size range at run time.
+ *  - same page, sections "WnA16" and "W8A8 / W4A8 / W4A4": the dense
+ *    W4A16, MoE Indexed / Grouped, W8A8 and W4A8-MXFP4 paths.
+ *  - "Humming v0.1.0-0.1.4", section "v0.1.1": low launch CPU overhead and a
+ *    stable launcher ABI.
+ * Number formats: OCP Microscaling Formats v1.0 (E2M1, E8M0) and OCP 8-bit
+ * floating point (E4M3, no infinities).
+ *
+ * Conventions (all entry points):
+ *  - Every function returns hq_status.  HQ_OK = 0.  Arguments are validated
+ *    before any HIP call; on an error nothing is launched and the stream is
+ *    not touched.  hq_last_error() returns a thread-local message for the
+ *    last failing call on this thread.
+ *  - The caller owns every buffer.  The library never allocates device
+ *    memory, never synchronises, and keeps no pointer after returning.
+ *  - Device entry points enqueue work asynchronously on `stream` (a
+ *    hipStream_t passed as void*; NULL is the default stream).  Device-side
+ *    faults surface at the caller's next synchronisation.
+ *  - Device pointers must be 16-byte aligned (HQ_ERR_ALIGNMENT otherwise).
+ *  - A workspace is needed only where hq_workspace_bytes() says so; it must
+ *    be zero-filled once before its first use (hq_workspace_init) and is left
+ *    ready for reuse by every call.  Two calls that share a workspace must not
+ *    run concurrently.
+ *  - Thread safety: the library holds no mutable global state besides a
+ *    per-device property cache filled once.
+ */
+#ifndef HQ_H
+#define HQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HQ_ABI_VERSION 1
+
+typedef void* hq_stream_t; /* a hipStream_t */
+
+typedef enum hq_status {
+    HQ_OK = 0,
+    HQ_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad enum           */
+    HQ_ERR_UNSUPPORTED = 2,  /* dtype combination or shape the kernels lack     */
+    HQ_ERR_ALIGNMENT = 3,    /* a device pointer is not 16-byte aligned         */
+    HQ_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required      */
+    HQ_ERR_ABI = 5,          /* descriptor abi_version != HQ_ABI_VERSION        */
+    HQ_ERR_HIP = 6           /* a HIP call failed; message has the HIP error    */
+} hq_status;
+
+typedef enum hq_dtype {
+    HQ_DT_NONE = 0,
+    HQ_DT_BF16 = 1,
+    HQ_DT_FP16 = 2,
+    HQ_DT_FP32 = 3,
+    HQ_DT_FP8_E4M3 = 4,  /* OCP E4M3 ("fn": no inf, S.1111.111 = NaN) */
+    HQ_DT_INT8 = 5,
+    HQ_DT_INT4 = 6,      /* two's-complement nibble, -8..7             */
+    HQ_DT_UINT4 = 7,     /* 0..15; with zero-points: value = q - z     */
+    HQ_DT_FP4_E2M1 = 8,  /* OCP MX E2M1                                */
+    HQ_DT_E8M0 = 9,      /* OCP MX shared scale, 2^(e-127)             */
+    HQ_DT_INT32 = 10
+} hq_dtype;
+
+typedef enum hq_scale_gran {
+    HQ_GRAN_NONE = 0,
+    HQ_GRAN_PER_GROUP_K = 1, /* one scale per (group of group_size along K, column) */
+    HQ_GRAN_PER_CHANNEL = 2  /* one scale per output column                         */
+} hq_scale_gran;
+
+typedef enum hq_ascale {
+    HQ_ASCALE_NONE = 0,
+    HQ_ASCALE_PER_TOKEN_F32 = 1 /* fp32 a_scale[M], applied in the epilogue */
+} hq_ascale;
+
+typedef enum hq_scale2 {
+    HQ_S2_NONE = 0 /* second-level scales: slot kept in the ABI, no kernel uses one yet */
+} hq_scale2;
+
+typedef enum hq_moe_mode {
+    HQ_MOE_INDEXED = 1, /* A is [T,K] token rows; rows are gathered by topk_ids      */
+    HQ_MOE_GROUPED = 2  /* A is [T*top_k,K] already sorted by expert (offsets given) */
+} hq_moe_mode;
+
+/*
+ * Layer descriptor: shapes, dtypes and quantization parameters of one linear
+ * layer (dense when num_experts == 0, else expert-stacked).  Plain data,
+ * copied by value inside every call.
+ *
+ * Supported combinations:
+ *   a_dtype   w_dtype    w_scale (gran, group)         zp      a_scale   out
+ *   BF16|FP16 INT4       same as a_dtype, PER_GROUP_K  NONE    NONE      a_dtype
+ *   BF16|FP16 UINT4      same as a_dtype, PER_GROUP_K  UINT4   NONE      a_dtype
+ *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    PER_TOKEN BF16
+ *   INT8      INT8       FP32, PER_CHANNEL             NONE    PER_TOKEN BF16|INT32
+ *   BF16      FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MoE)
+ * Group sizes for 16-bit scales: a multiple of 128 that divides K.
+ * K: a multiple of 128 (4-bit weights) or of 64 (INT8).  N: any value >= 1.
+ * out_dtype INT32 returns the raw INT8 x INT8 accumulators (bit-exact).
+ */
+typedef struct hq_layer_desc {
+    int32_t abi_version;    /* HQ_ABI_VERSION                                  */
+    int32_t num_experts;    /* 0 = dense layer                                 */
+    int64_t N;              /* output features                                 */
+    int64_t K;              /* input features                                  */
+    int32_t a_dtype;        /* hq_dtype of A                                   */
+    int32_t a_scale;        /* hq_ascale                                       */
+    int32_t w_dtype;        /* hq_dtype of the weight codes                    */
+    int32_t w_scale_dtype;  /* hq_dtype of the weight scales                   */
+    int32_t w_scale_gran;   /* hq_scale_gran                                   */
+    int32_t group_size;     /* K elements per scale (PER_GROUP_K)              */
+    int32_t zp_dtype;       /* HQ_DT_NONE or HQ_DT_UINT4                       */
+    int32_t scale2;         /* hq_scale2                                       */
+    int32_t out_dtype;      /* hq_dtype of D                                   */
+    int32_t reserved[3];    /* must be zero                                    */
+} hq_layer_desc;
+
+/* ---------------------------------------------------------------------- */
+/* general                                                                 */
+/* ---------------------------------------------------------------------- */
+
+int32_t hq_abi_version(void);
+const char* hq_status_str(hq_status s);
+/* Message for the last failing call on the calling thread ("" if none). */
+const char* hq_last_error(void);
+/* Checks a descriptor against the supported combinations above. Host only. */
+hq_status hq_desc_validate(const hq_layer_desc* desc);
+
+/* ---------------------------------------------------------------------- */
+/* repack (host only): logical export form -> hq standard packed layout     */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Byte sizes of the four packed tensors (weights, scales, zero-points,
+ * second-level scales), covering all experts.  Unused tensors report 0.
+ */
+hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* s_bytes,
+                            size_t* z_bytes, size_t* s2_bytes);
+
+/*
+ * Host-memory transform of one layer (all experts) from the logical export
+ * form into the packed layout the kernels read.  Pure, deterministic,
+ * thread-safe; integer bit permutation only (exact).  Outputs are allocated
+ * by the caller with hq_repacked_bytes(); unused tensors are NULL.
+ *
+ * Logical inputs (per expert, experts stacked along a leading axis):
+ *   w  4-bit codes: uint32 [K/8][N]; code k = 8j+i of column n in bits
+ *      4i..4i+3 of word [j][n]            INT8: int8 [K][N]
+ *   scale  [K/group][N] in w_scale_dtype (16-bit raw bits, uint8 for E8M0);
+ *          PER_CHANNEL fp32: [N]
+ *   zp     UINT4: uint32 [K/group][ceil(N/8)]; column n = 8j+i in bits
+ *          4i..4i+3 of word [g][j]
+ *   scale2 must be NULL (no second-level scale kernels yet)
+ *
+ * Packed outputs (N padded to Np = ceil(N/16)*16; padding decodes to 0 with
+ * unit scale).  A "strip" is 16 consecutive columns; a lane is one of the 64
+ * lanes of a wavefront reading 16 bytes:
+ *   w  4-bit: [E][Np/16][K/128][64 lanes][16 B]; lane l holds column
+ *      16*strip + (l & 15), k = 128*chunk + 32*(l >> 4) + j, j = 0..31,
+ *      bytes 4t..4t+3 holding j = 8t..8t+7.  Inside a word FP4 codes are in
+ *      natural order (j in nibble j%8); INT4/UINT4 codes are in pair order
+ *      (nibble p holds j%8 = {0,2,4,6,1,3,5,7}[p]) so that one shift+mask
+ *      yields two consecutive codes in the two 16-bit halves.
+ *      INT8: [Np/16][K/64][64 lanes][16 B]; lane l holds column
+ *      16*strip + (l & 15), k = 64*chunk + 16*(l >> 4) + j, j = 0..15.
+ *   scale  16-bit group scales: [E][Np/16][K/group][16];
+ *          E8M0: [E][Np/16][ceil(K/512)][64 lanes][4 B], byte b of lane l is
+ *          the exponent of column 16*strip + (l & 15), K-block
+ *          4*(4*c4 + b) + (l >> 4) (padding bytes are 127);
+ *          PER_CHANNEL fp32: [Np]
+ *   zp     [E][Np/16][K/group] uint64, column 16*strip + i in bits 4i..4i+3
+ */
+hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale, const void* zp,
+                    const void* scale2, void* w_out, void* s_out, void* z_out, void* s2_out);
+
+/* ---------------------------------------------------------------------- */
+/* workspace                                                               */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Workspace bytes for a call with M rows (dense) or T tokens and top_k
+ * (MoE; top_k is ignored for dense layers).  0 means none is needed.
+ */
+hq_status hq_workspace_bytes(const hq_layer_desc* desc, int64_t M_or_T, int32_t top_k, size_t* bytes);
+
+/* Zero-fills a workspace on `stream` with a fill kernel (graph-capturable). */
+hq_status hq_workspace_init(void* workspace, size_t bytes, hq_stream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* GEMMs (device)                                                          */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Dense D[M,N] = A[M,K] x dequant(W).
+ *   A        device, [M][K] row-major, a_dtype
+ *   a_scale  device fp32 [M] when a_scale == PER_TOKEN_F32, else NULL
+ *   w, s, z, s2  device, packed by hq_repack (unused ones NULL)
+ *   D        device, [M][N] row-major, out_dtype
+ * Floating outputs: fp32 accumulation, rounded once (RNE) to out_dtype.
+ * M == 0 returns HQ_OK without launching.
+ */
+hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const float* a_scale,
+                  const void* w, const void* s, const void* z, const void* s2, void* D,
+                  void* workspace, size_t ws_bytes, hq_stream_t stream);
+
+/*
+ * MoE GEMM over top_k experts per token (expert-stacked packed weights).
+ *   INDEXED: A [T][K]; topk_ids device int32 [T][top_k] (distinct per token,
+ *            0 <= id < num_experts); D [T*top_k][N], row t*top_k + j is
+ *            A[t] x W[topk_ids[t][j]].  expert_offsets must be NULL.
+ *   GROUPED: A [T*top_k][K] already sorted by expert; expert_offsets device
+ *            int32 [num_experts+1] (nondecreasing, offsets[0] = 0,
+ *            offsets[E] = T*top_k); D [T*top_k][N] in the same row order.
+ *            topk_ids must be NULL.
+ * Routing weights are not applied.  T == 0 returns HQ_OK.
+ */
+hq_status hq_moe_gemm(const hq_layer_desc* desc, int32_t mode, int64_t T, int32_t top_k,
+                      const void* A, const float* a_scale, const int32_t* topk_ids,
+                      const int32_t* expert_offsets, const void* w, const void* s, const void* z,
+                      const void* s2, void* D, void* workspace, size_t ws_bytes, hq_stream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* input preparation (device)                                              */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Tokenwise activation quantisation ("Humming wird angekuendigt", section
+ * "End-to-End-Inferenzleistung": tokenwise FP8 activations for W4A8).
+ * For each row m of x (fp32 [M][K]): s[m] = max_k |x| / 448 in fp32 (1 for an
+ * all-zero row); q[m][k] = E4M3(x / s[m]), fp32 division, round to nearest
+ * even, saturating at +-448.  out_dtype must be HQ_DT_FP8_E4M3.
+ */
+hq_status hq_quantize_act(int32_t out_dtype, int64_t M, int64_t K, const float* x, void* q, float* s,
+                          hq_stream_t stream);
+
+/*
+ * MoE routing metadata ("Humming wird angekuendigt", section "WnA16": the
+ * Grouped path runs on expert-sorted tokens).  From topk_ids [T][top_k]:
+ *   expert_offsets [E+1]: exclusive prefix sum of per-expert pair counts
+ *   sorted_pairs   [T*top_k]: pair ids p = t*top_k + j stably sorted by expert
+ * workspace: hq_workspace_bytes of a MoE descriptor with the same T, top_k.
+ */
+hq_status hq_moe_align(int64_t T, int32_t top_k, int32_t num_experts, const int32_t* topk_ids,
+                       int32_t* expert_offsets, int32_t* sorted_pairs, void* workspace,
+                       size_t ws_bytes, hq_stream_t stream);
+
+/*
+ * Builds the Grouped activation matrix: A_sorted[i] = A[sorted_pairs[i] / top_k]
+ * for i < T*top_k; rows of K elements of `dtype` (BF16, FP16, FP8_E4M3, INT8).
+ */
+hq_status hq_moe_gather(int32_t dtype, int64_t T, int32_t top_k, int64_t K, const void* A,
+                        const int32_t* sorted_pairs, void* A_sorted, hq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQ_H */
