@@ -98,19 +98,16 @@ void repack_zero4(const LayerInfo& L, const uint32_t* z, uint64_t* out) {
 }
 
 void repack_e8m0(const LayerInfo& L, const uint8_t* s, uint8_t* out) {
-    const int64_t N = L.N, nst = L.Np / 16, nc = L.K / 128, c4n = (nc + 3) / 4, nb = L.K / 32;
+    const int64_t N = L.N, nst = L.Np / 16, nc = L.K / 128, nb = L.K / 32;
     for (int64_t e = 0; e < L.E; ++e) {
         const uint8_t* se = s + e * nb * N;
-        uint8_t* oe = out + (size_t)e * (size_t)(nst * c4n * 256);
+        uint8_t* oe = out + (size_t)e * (size_t)(nst * nc * 64);
         for (int64_t st = 0; st < nst; ++st)
-            for (int64_t c4 = 0; c4 < c4n; ++c4)
-                for (int lane = 0; lane < 64; ++lane)
-                    for (int b = 0; b < 4; ++b) {
-                        const int64_t n = st * 16 + (lane & 15), c = 4 * c4 + b;
-                        uint8_t v = 127;
-                        if (c < nc && n < N) v = se[(4 * c + (lane >> 4)) * N + n];
-                        oe[((st * c4n + c4) * 64 + lane) * 4 + b] = v;
-                    }
+            for (int64_t c = 0; c < nc; ++c)
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int64_t n = st * 16 + (lane & 15);
+                    oe[(st * nc + c) * 64 + lane] = n < N ? se[(4 * c + (lane >> 4)) * N + n] : (uint8_t)127;
+                }
     }
 }
 
@@ -133,7 +130,7 @@ void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s
         case Kind::W4A8_MX:
         case Kind::MOE_MX_BF16:
             *w = E * nst * (size_t)(L.K / 128) * 1024;
-            *s = E * nst * (size_t)((L.K / 128 + 3) / 4) * 256;
+            *s = E * nst * (size_t)(L.K / 128) * 64;
             break;
         case Kind::W8A8:
             *w = E * nst * (size_t)(L.K / 64) * 1024;

@@ -17,6 +17,7 @@
 // last workgroup to arrive sums the partial tiles in a fixed order.
 #include "hq_device.hpp"
 #include "hq_internal.h"
+#include "tile_gemm.hpp"
 
 namespace hq {
 
@@ -240,14 +241,33 @@ hipError_t launch_gemv(const DenseArgs& a, int64_t m0, int64_t Mslab) {
     }
 }
 
+template <Fmt F, int BM>
+hipError_t launch_tile(const DenseArgs& a) {
+    TileArgs p{};
+    p.A = a.A;
+    p.W = a.w;
+    p.S = a.s;
+    p.Z = a.z;
+    p.D = a.D;
+    p.M = (int)a.M;
+    p.N = (int)a.N;
+    p.K = (int)a.K;
+    p.Np = (int)a.Np;
+    p.ngroups = (int)(a.K / a.group_size);
+    p.gsteps = a.group_size / 128;
+    p.tiles_m = (int)cdiv(a.M, BM);
+    p.tiles_n = (int)cdiv(a.Np, 128);
+    hipLaunchKernelGGL((tile_gemm_kernel<F, BM, 128>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, a.stream, p);
+    return hipGetLastError();
+}
+
 template <bool BF16, bool ZP>
 hipError_t launch_all(const DenseArgs& a) {
-    for (int64_t m0 = 0; m0 < a.M; m0 += 64) {
-        const int64_t Ms = a.M - m0 < 64 ? a.M - m0 : 64;
-        hipError_t e = launch_gemv<BF16, ZP>(a, m0, Ms);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    if (a.M <= 64) return launch_gemv<BF16, ZP>(a, 0, a.M);
+    if constexpr (BF16) return launch_tile<Fmt::WNA16_BF16, 128>(a);
+    const int64_t tiles_n = cdiv(a.Np, 128);
+    if (cdiv(a.M, 256) * tiles_n >= 256) return launch_tile<Fmt::WNA16_F16, 256>(a);
+    return launch_tile<Fmt::WNA16_F16, 128>(a);
 }
 
 }  // namespace
@@ -255,10 +275,10 @@ hipError_t launch_all(const DenseArgs& a) {
 size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size) {
     (void)group_size;
     const int64_t Np = pad16(N);
-    const int64_t Ms = M < 64 ? M : 64;
-    GemvPlan p = plan_gemv(Ms, Np, K);
+    if (M > 64) return 0;  // the tiled kernel needs no workspace
+    GemvPlan p = plan_gemv(M, Np, K);
     if (p.splits <= 1) return 0;
-    return kCounterBytes + (size_t)p.splits * (size_t)Ms * (size_t)Np * sizeof(float);
+    return kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)Np * sizeof(float);
 }
 
 hipError_t wna16_launch(const DenseArgs& a, bool bf16, bool zp) {

@@ -183,9 +183,9 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *      INT8: [Np/16][K/64][64 lanes][16 B]; lane l holds column
  *      16*strip + (l & 15), k = 64*chunk + 16*(l >> 4) + j, j = 0..15.
  *   scale  16-bit group scales: [E][Np/16][K/group][16];
- *          E8M0: [E][Np/16][ceil(K/512)][64 lanes][4 B], byte b of lane l is
- *          the exponent of column 16*strip + (l & 15), K-block
- *          4*(4*c4 + b) + (l >> 4) (padding bytes are 127);
+ *          E8M0: [E][Np/16][K/128][64 lanes] bytes; lane l holds the
+ *          exponent of column 16*strip + (l & 15), K-block 4*chunk + (l >> 4)
+ *          (padding columns hold 127);
  *          PER_CHANNEL fp32: [Np]
  *   zp     [E][Np/16][K/group] uint64, column 16*strip + i in bits 4i..4i+3
  */
