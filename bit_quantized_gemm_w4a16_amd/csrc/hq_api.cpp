@@ -175,8 +175,12 @@ hq_status hq_workspace_bytes(const hq_layer_desc* desc, int64_t M_or_T, int32_t 
     if (st != HQ_OK) return st;
     if (!bytes) return set_error(HQ_ERR_INVALID_ARG, "bytes is NULL");
     if (M_or_T < 0 || M_or_T > (1LL << 30)) return set_error(HQ_ERR_INVALID_ARG, "M/T out of range");
-    (void)top_k;
-    *bytes = desc->num_experts ? 0 : dense_workspace(L, M_or_T);
+    if (desc->num_experts) {
+        if (top_k < 1 || top_k > desc->num_experts) return set_error(HQ_ERR_INVALID_ARG, "top_k out of range");
+        *bytes = moe_layout(M_or_T, top_k, desc->num_experts, true).bytes;  // Indexed needs the most
+    } else {
+        *bytes = dense_workspace(L, M_or_T);
+    }
     return ok();
 }
 
@@ -205,6 +209,9 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const flo
     if (!aligned16(A) || !aligned16(w) || !aligned16(s) || !aligned16(D) || (z && !aligned16(z)) ||
         (a_scale && !aligned16(a_scale)))
         return set_error(HQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    const int64_t ab = desc->a_dtype == HQ_DT_BF16 || desc->a_dtype == HQ_DT_FP16 ? 2 : 1;
+    if (M * L.K * ab >= (int64_t)1 << 32 || M * L.N >= (int64_t)1 << 31)
+        return set_error(HQ_ERR_UNSUPPORTED, "M*K activation bytes must stay below 4 GiB and M*N below 2^31");
     const size_t need = dense_workspace(L, M);
     if (need) {
         if (!workspace || ws_bytes < need)
@@ -214,7 +221,9 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const flo
     DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, a_scale, w, s, z, D, workspace, ws_bytes, (hipStream_t)stream};
     switch (L.kind) {
         case Kind::WNA16: return hip_status(wna16_launch(a, L.a_bf16, L.zp), "hq_gemm(W4A16)");
-        default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind is not built yet");
+        case Kind::W4A8_MX: return hip_status(w4a8_launch(a), "hq_gemm(W4A8-MXFP4)");
+        case Kind::W8A8: return hip_status(w8a8_launch(a, L.out_i32), "hq_gemm(W8A8)");
+        default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind runs through hq_moe_gemm");
     }
 }
 
@@ -222,32 +231,106 @@ hq_status hq_moe_gemm(const hq_layer_desc* desc, int32_t mode, int64_t T, int32_
                       const float* a_scale, const int32_t* topk_ids, const int32_t* expert_offsets,
                       const void* w, const void* s, const void* z, const void* s2, void* D,
                       void* workspace, size_t ws_bytes, hq_stream_t stream) {
-    (void)mode; (void)T; (void)top_k; (void)A; (void)a_scale; (void)topk_ids; (void)expert_offsets;
-    (void)w; (void)s; (void)z; (void)s2; (void)D; (void)workspace; (void)ws_bytes; (void)stream;
     LayerInfo L;
     hq_status st = describe(desc, &L);
     if (st != HQ_OK) return st;
-    return set_error(HQ_ERR_UNSUPPORTED, "MoE kernels are not built yet");
+    if (!desc->num_experts || L.kind != Kind::MOE_MX_BF16)
+        return set_error(HQ_ERR_INVALID_ARG, "hq_moe_gemm takes a MoE descriptor (num_experts > 0)");
+    if (mode != HQ_MOE_INDEXED && mode != HQ_MOE_GROUPED) return set_error(HQ_ERR_INVALID_ARG, "bad MoE mode %d", mode);
+    if (T < 0 || T > (1LL << 24)) return set_error(HQ_ERR_INVALID_ARG, "T=%lld out of range", (long long)T);
+    if (top_k < 1 || top_k > desc->num_experts) return set_error(HQ_ERR_INVALID_ARG, "top_k=%d out of range", top_k);
+    if (T == 0) return ok();
+    const bool indexed = mode == HQ_MOE_INDEXED;
+    if (!A || !w || !s || !D) return set_error(HQ_ERR_INVALID_ARG, "A, w, s and D are required");
+    if (a_scale || z || s2) return set_error(HQ_ERR_INVALID_ARG, "a_scale, z and s2 must be NULL for this format");
+    if (indexed && (!topk_ids || expert_offsets))
+        return set_error(HQ_ERR_INVALID_ARG, "INDEXED takes topk_ids and no expert_offsets");
+    if (!indexed && (topk_ids || !expert_offsets))
+        return set_error(HQ_ERR_INVALID_ARG, "GROUPED takes expert_offsets and no topk_ids");
+    const int64_t P = T * top_k;
+    const int64_t arows = indexed ? T : P;
+    if (arows * L.K * 2 >= (int64_t)1 << 32 || P * L.N >= (int64_t)1 << 31)
+        return set_error(HQ_ERR_UNSUPPORTED, "activation bytes must stay below 4 GiB and rows*N below 2^31");
+    if (!aligned16(A) || !aligned16(w) || !aligned16(s) || !aligned16(D) || (topk_ids && !aligned16(topk_ids)) ||
+        (expert_offsets && !aligned16(expert_offsets)))
+        return set_error(HQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+    const MoeLayout lay = moe_layout(T, top_k, desc->num_experts, indexed);
+    if (!workspace || ws_bytes < lay.bytes)
+        return set_error(HQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", lay.bytes,
+                         workspace ? ws_bytes : (size_t)0);
+    if (!aligned16(workspace)) return set_error(HQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    size_t wb, sb, zb, s2b;
+    LayerInfo one = L;
+    one.E = 1;
+    packed_sizes(one, &wb, &sb, &zb, &s2b);
+    MoeArgs a{};
+    a.T = T;
+    a.N = L.N;
+    a.K = L.K;
+    a.Np = L.Np;
+    a.top_k = top_k;
+    a.E = desc->num_experts;
+    a.indexed = indexed;
+    a.A = A;
+    a.topk_ids = topk_ids;
+    a.expert_offsets = expert_offsets;
+    a.w = w;
+    a.s = s;
+    a.D = D;
+    a.w_estride = (int64_t)wb;
+    a.s_estride = (int64_t)sb;
+    a.ws = workspace;
+    a.stream = (hipStream_t)stream;
+    return hip_status(moe_gemm_launch(a), indexed ? "hq_moe_gemm(INDEXED)" : "hq_moe_gemm(GROUPED)");
 }
 
 hq_status hq_quantize_act(int32_t out_dtype, int64_t M, int64_t K, const float* x, void* q, float* s,
                           hq_stream_t stream) {
-    (void)out_dtype; (void)M; (void)K; (void)x; (void)q; (void)s; (void)stream;
-    return set_error(HQ_ERR_UNSUPPORTED, "activation quantisation is not built yet");
+    if (out_dtype != HQ_DT_FP8_E4M3) return set_error(HQ_ERR_UNSUPPORTED, "only FP8_E4M3 activation codes are built");
+    if (M < 0 || K < 1 || M > (1LL << 30) || K > (1LL << 24)) return set_error(HQ_ERR_INVALID_ARG, "M/K out of range");
+    if (M == 0) return ok();
+    if (!x || !q || !s) return set_error(HQ_ERR_INVALID_ARG, "x, q and s are required");
+    if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return set_error(HQ_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    return hip_status(quant_e4m3_launch(M, K, x, (uint8_t*)q, s, (hipStream_t)stream), "hq_quantize_act");
 }
 
 hq_status hq_moe_align(int64_t T, int32_t top_k, int32_t num_experts, const int32_t* topk_ids,
                        int32_t* expert_offsets, int32_t* sorted_pairs, void* workspace, size_t ws_bytes,
                        hq_stream_t stream) {
-    (void)T; (void)top_k; (void)num_experts; (void)topk_ids; (void)expert_offsets; (void)sorted_pairs;
-    (void)workspace; (void)ws_bytes; (void)stream;
-    return set_error(HQ_ERR_UNSUPPORTED, "routing metadata is not built yet");
+    if (num_experts < 1 || num_experts > 4096) return set_error(HQ_ERR_INVALID_ARG, "num_experts out of range");
+    if (top_k < 1 || top_k > num_experts) return set_error(HQ_ERR_INVALID_ARG, "top_k out of range");
+    if (T < 0 || T > (1LL << 24)) return set_error(HQ_ERR_INVALID_ARG, "T out of range");
+    if (T == 0) return ok();
+    if (!topk_ids || !expert_offsets || !sorted_pairs) return set_error(HQ_ERR_INVALID_ARG, "pointers are required");
+    if (!aligned16(topk_ids) || !aligned16(expert_offsets) || !aligned16(sorted_pairs))
+        return set_error(HQ_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    const size_t need = moe_align_workspace(T, top_k, num_experts);
+    if (!workspace || ws_bytes < need)
+        return set_error(HQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (!aligned16(workspace)) return set_error(HQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    return hip_status(moe_align_launch(T, top_k, num_experts, topk_ids, expert_offsets, sorted_pairs, workspace,
+                                       nullptr, nullptr, (hipStream_t)stream),
+                      "hq_moe_align");
 }
 
 hq_status hq_moe_gather(int32_t dtype, int64_t T, int32_t top_k, int64_t K, const void* A,
                         const int32_t* sorted_pairs, void* A_sorted, hq_stream_t stream) {
-    (void)dtype; (void)T; (void)top_k; (void)K; (void)A; (void)sorted_pairs; (void)A_sorted; (void)stream;
-    return set_error(HQ_ERR_UNSUPPORTED, "gather is not built yet");
+    int64_t eb = 0;
+    switch (dtype) {
+        case HQ_DT_BF16:
+        case HQ_DT_FP16: eb = 2; break;
+        case HQ_DT_FP8_E4M3:
+        case HQ_DT_INT8: eb = 1; break;
+        default: return set_error(HQ_ERR_UNSUPPORTED, "gather dtype must be BF16, FP16, FP8_E4M3 or INT8");
+    }
+    if (T < 0 || top_k < 1 || K < 1 || T > (1LL << 24) || K > (1LL << 24)) return set_error(HQ_ERR_INVALID_ARG, "sizes out of range");
+    if (T == 0) return ok();
+    if ((K * eb) % 16) return set_error(HQ_ERR_UNSUPPORTED, "row bytes must be a multiple of 16");
+    if (!A || !sorted_pairs || !A_sorted) return set_error(HQ_ERR_INVALID_ARG, "pointers are required");
+    if (!aligned16(A) || !aligned16(sorted_pairs) || !aligned16(A_sorted))
+        return set_error(HQ_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    return hip_status(moe_gather_launch(A, sorted_pairs, T * top_k, top_k, K * eb, A_sorted, (hipStream_t)stream),
+                      "hq_moe_gather");
 }
 
 }  // extern "C"

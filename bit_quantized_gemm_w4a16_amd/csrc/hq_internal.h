@@ -39,6 +39,41 @@ struct DenseArgs {
 size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size);
 hipError_t wna16_launch(const DenseArgs& a, bool bf16, bool zp);
 
+// W4A8-MXFP4 and W8A8-INT8
+hipError_t w4a8_launch(const DenseArgs& a);
+hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32);
+
+// MoE
+struct MoeLayout {  // byte offsets into the MoE workspace
+    size_t hist, lrank, offsets, sorted, tiles, ntiles, bytes;
+    int64_t max_tiles;
+};
+MoeLayout moe_layout(int64_t T, int top_k, int E, bool indexed);
+size_t moe_align_workspace(int64_t T, int top_k, int E);
+
+struct MoeArgs {
+    int64_t T, N, K, Np;
+    int top_k, E;
+    bool indexed;
+    const void* A;
+    const int* topk_ids;
+    const int* expert_offsets;
+    const void* w;
+    const void* s;
+    void* D;
+    int64_t w_estride, s_estride;
+    void* ws;
+    hipStream_t stream;
+};
+hipError_t moe_gemm_launch(const MoeArgs& a);
+hipError_t moe_align_launch(int64_t T, int top_k, int E, const int* ids, int* offsets, int* sorted, void* ws,
+                            int* tiles, int* ntiles, hipStream_t st);
+hipError_t moe_gather_launch(const void* A, const int* sorted, int64_t P, int top_k, int64_t row_bytes, void* out,
+                             hipStream_t st);
+
+// activation quantisation (tokenwise E4M3)
+hipError_t quant_e4m3_launch(int64_t M, int64_t K, const float* x, uint8_t* q, float* s, hipStream_t st);
+
 // fill kernel used by hq_workspace_init
 hipError_t fill_zero_launch(void* p, size_t bytes, hipStream_t stream);
 

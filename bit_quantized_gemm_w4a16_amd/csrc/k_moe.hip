@@ -1,0 +1,268 @@
+// MoE: routing metadata, Grouped-path gather, and the expert GEMM launches.
+//
+// "Humming wird angekuendigt", section "WnA16": MoE runs on an Indexed path
+// (token rows gathered per expert by index) and a Grouped path (tokens sorted
+// by expert, contiguous per expert); the work per expert varies with the
+// routing.  Both paths here share one tiled MFMA kernel over a device-built
+// list of m-tiles (expert, first sorted row, row count): experts with many
+// tokens get many tiles, experts with none get none, and the grid is sized by
+// the host from an upper bound so no host synchronisation is needed.
+//
+// Routing metadata is a stable counting sort of the flattened pairs
+// p = t * top_k + j by expert id: per-chunk histograms and in-chunk ranks,
+// a per-expert scan over chunks, one workgroup for the expert offsets and the
+// m-tile list, then the scatter.
+#include "hq_device.hpp"
+#include "hq_internal.h"
+#include "tile_gemm.hpp"
+
+namespace hq {
+
+constexpr int kMoeChunk = 256;  // pairs per histogram chunk
+constexpr int kMoeBM = 128;     // rows per m-tile of the expert GEMM
+
+// ---- 1. per-chunk histogram + rank of each pair among equal ids before it ----
+// hist is expert-major: hist[e * C + c].
+__global__ __launch_bounds__(256) void moe_hist_kernel(const int* __restrict__ ids, int P, int E, int C,
+                                                       int* __restrict__ hist, int* __restrict__ lrank) {
+    extern __shared__ int sh[];  // [E] histogram, then [kMoeChunk] ids
+    int* h = sh;
+    int* cid = sh + E;
+    const int c = blockIdx.x, t = threadIdx.x, p = c * kMoeChunk + t;
+    for (int e = t; e < E; e += 256) h[e] = 0;
+    const int id = p < P ? ids[p] : -1;
+    cid[t] = id;
+    __syncthreads();
+    if (id >= 0 && id < E) {
+        int r = 0;
+        for (int j = 0; j < t; ++j) r += cid[j] == id;
+        lrank[p] = r;
+        atomicAdd(&h[id], 1);
+    }
+    __syncthreads();
+    for (int e = t; e < E; e += 256) hist[(int64_t)e * C + c] = h[e];
+}
+
+// ---- 2a. per expert (one wave): exclusive scan of its chunk counts, total ----
+__global__ __launch_bounds__(64) void moe_colscan_kernel(int* __restrict__ hist, int C, int* __restrict__ counts) {
+    const int e = blockIdx.x, l = threadIdx.x;
+    int* row = hist + (int64_t)e * C;
+    int carry = 0;
+    for (int c0 = 0; c0 < C; c0 += 64) {
+        const int v = c0 + l < C ? row[c0 + l] : 0;
+        int incl = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (l >= off) incl += o;
+        }
+        if (c0 + l < C) row[c0 + l] = carry + incl - v;
+        carry += __shfl(incl, 63, 64);
+    }
+    if (l == 0) counts[e] = carry;
+}
+
+// block-wide exclusive scan of v over 1024 threads
+__device__ int block_excl_scan_1024(int v, int* tmp) {
+    const int t = threadIdx.x;
+    tmp[t] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int add = t >= off ? tmp[t - off] : 0;
+        __syncthreads();
+        tmp[t] += add;
+        __syncthreads();
+    }
+    const int incl = tmp[t];
+    __syncthreads();
+    return incl - v;
+}
+
+// ---- 2b. expert offsets and the m-tile list (one workgroup) ----
+// Counts come from `counts` (Indexed) or from the caller's offsets (Grouped).
+// Caller-given offsets are clamped to [0, P] so malformed input can never
+// address rows outside A or D; at most max_tiles tiles are written.
+__global__ __launch_bounds__(1024) void moe_offsets_kernel(const int* __restrict__ counts, const int* __restrict__ given_off,
+                                                           int E, int P, int max_tiles, int* __restrict__ offsets,
+                                                           int* __restrict__ tiles, int* __restrict__ ntiles, int BM) {
+    __shared__ int tmp[1024];
+    __shared__ int carry[2];
+    const int t = threadIdx.x;
+    if (t == 0) carry[0] = carry[1] = 0;
+    __syncthreads();
+    for (int e0 = 0; e0 < E; e0 += 4096) {  // 4 experts per thread per round
+        int cnt[4], sum = 0, ntl[4], tsum = 0;
+        for (int k = 0; k < 4; ++k) {
+            const int e = e0 + 4 * t + k;
+            int c = 0;
+            if (e < E) {
+                if (counts) {
+                    c = counts[e];
+                } else {
+                    const int lo = min(max(given_off[e], 0), P), hi = min(max(given_off[e + 1], lo), P);
+                    c = hi - lo;
+                }
+            }
+            cnt[k] = c;
+            ntl[k] = (cnt[k] + BM - 1) / BM;
+            sum += cnt[k];
+            tsum += ntl[k];
+        }
+        const int c0 = carry[0], c1 = carry[1];
+        int run = c0 + block_excl_scan_1024(sum, tmp);
+        int trun = c1 + block_excl_scan_1024(tsum, tmp);
+        for (int k = 0; k < 4; ++k) {
+            const int e = e0 + 4 * t + k;
+            if (e < E) {
+                const int start = counts ? run : min(max(given_off[e], 0), P);
+                if (offsets) offsets[e] = start;
+                for (int q = 0; tiles && q < ntl[k] && trun + q < max_tiles; ++q) {
+                    tiles[3 * (trun + q)] = e;
+                    tiles[3 * (trun + q) + 1] = start + q * BM;
+                    tiles[3 * (trun + q) + 2] = min(BM, cnt[k] - q * BM);
+                }
+            }
+            run += cnt[k];
+            trun += ntl[k];
+        }
+        __syncthreads();
+        if (t == 1023) {
+            carry[0] = run;
+            carry[1] = trun;
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        if (offsets) offsets[E] = carry[0];
+        if (ntiles) *ntiles = min(carry[1], max_tiles);
+    }
+}
+
+// ---- 3. scatter: sorted[offset(id) + chunk base(id) + rank] = p ----
+__global__ __launch_bounds__(256) void moe_place_kernel(const int* __restrict__ ids, int P, int E, int C,
+                                                        const int* __restrict__ hist, const int* __restrict__ offsets,
+                                                        const int* __restrict__ lrank, int* __restrict__ sorted) {
+    const int c = blockIdx.x, p = c * kMoeChunk + threadIdx.x;
+    if (p >= P) return;
+    const int id = ids[p];
+    if (id < 0 || id >= E) return;
+    sorted[offsets[id] + hist[(int64_t)id * C + c] + lrank[p]] = p;
+}
+
+// ---- gather for the Grouped path: out[i] = A[sorted[i] / top_k] ----
+__global__ __launch_bounds__(256) void moe_gather_kernel(const char* __restrict__ A, const int* __restrict__ sorted,
+                                                         int P, int top_k, int row_bytes, char* __restrict__ out) {
+    const int units = row_bytes / 16;
+    const int64_t total = (int64_t)P * units;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int r = (int)(i / units), u = (int)(i % units);
+        const int src = min(max(sorted[r], 0), P - 1) / top_k;  // clamped: never outside A
+        ((v4u*)(out + (int64_t)r * row_bytes))[u] = ((const v4u*)(A + (int64_t)src * row_bytes))[u];
+    }
+}
+
+// -------------------------------------------------------------------------
+// host side
+// -------------------------------------------------------------------------
+
+namespace {
+size_t al16(size_t b) { return (b + 15) / 16 * 16; }
+}  // namespace
+
+MoeLayout moe_layout(int64_t T, int top_k, int E, bool indexed) {
+    MoeLayout L{};
+    const int64_t P = T * top_k;
+    const int64_t max_tiles = cdiv(P, kMoeBM) + (E < P ? E : P);
+    size_t o = 0;
+    L.hist = o;  // hist + lrank + counts (the align scratch)
+    o += indexed ? moe_align_workspace(T, top_k, E) : 0;
+    L.offsets = o;
+    o += indexed ? al16((size_t)(E + 1) * 4) : 0;
+    L.sorted = o;
+    o += indexed ? al16((size_t)P * 4) : 0;
+    L.tiles = o;
+    o += al16((size_t)(max_tiles > 0 ? max_tiles : 1) * 12);
+    L.ntiles = o;
+    o += 16;
+    L.bytes = o;
+    L.max_tiles = max_tiles;
+    return L;
+}
+
+size_t moe_align_workspace(int64_t T, int top_k, int E) {
+    const int64_t P = T * top_k, C = cdiv(P, kMoeChunk);
+    return al16((size_t)(C * E) * 4) + al16((size_t)P * 4) + al16((size_t)E * 4);
+}
+
+hipError_t moe_align_launch(int64_t T, int top_k, int E, const int* ids, int* offsets, int* sorted, void* ws,
+                            int* tiles, int* ntiles, hipStream_t st) {
+    const int P = (int)(T * top_k), C = (int)cdiv(P, kMoeChunk);
+    int* hist = (int*)ws;
+    int* lrank = (int*)((char*)ws + al16((size_t)C * E * 4));
+    int* counts = (int*)((char*)lrank + al16((size_t)P * 4));
+    hipLaunchKernelGGL(moe_hist_kernel, dim3(C), dim3(256), (size_t)(E + kMoeChunk) * 4, st, ids, P, E, C, hist, lrank);
+    hipLaunchKernelGGL(moe_colscan_kernel, dim3(E), dim3(64), 0, st, hist, C, counts);
+    const int max_tiles = (int)(cdiv(P, kMoeBM) + (E < P ? E : P));
+    hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, st, (const int*)counts, (const int*)nullptr, E, P,
+                       max_tiles, offsets, tiles, ntiles, kMoeBM);
+    hipLaunchKernelGGL(moe_place_kernel, dim3(C), dim3(256), 0, st, ids, P, E, C, (const int*)hist,
+                       (const int*)offsets, (const int*)lrank, sorted);
+    return hipGetLastError();
+}
+
+hipError_t moe_gather_launch(const void* A, const int* sorted, int64_t P, int top_k, int64_t row_bytes, void* out,
+                             hipStream_t st) {
+    const int64_t units = P * (row_bytes / 16);
+    int64_t blocks = cdiv(units, 256);
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) return hipSuccess;
+    hipLaunchKernelGGL(moe_gather_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const char*)A, sorted, (int)P,
+                       top_k, (int)row_bytes, (char*)out);
+    return hipGetLastError();
+}
+
+hipError_t moe_gemm_launch(const MoeArgs& a) {
+    const int64_t P = a.T * a.top_k;
+    MoeLayout L = moe_layout(a.T, a.top_k, a.E, a.indexed);
+    char* ws = (char*)a.ws;
+    int* tiles = (int*)(ws + L.tiles);
+    int* ntiles = (int*)(ws + L.ntiles);
+    const int* sorted = nullptr;
+    hipError_t e;
+    if (a.indexed) {
+        int* offsets = (int*)(ws + L.offsets);
+        int* srt = (int*)(ws + L.sorted);
+        e = moe_align_launch(a.T, a.top_k, a.E, a.topk_ids, offsets, srt, ws + L.hist, tiles, ntiles, a.stream);
+        if (e != hipSuccess) return e;
+        sorted = srt;
+    } else {
+        hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, (const int*)nullptr,
+                           a.expert_offsets, a.E, (int)P, (int)L.max_tiles, (int*)nullptr, tiles, ntiles, kMoeBM);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    TileArgs p{};
+    p.A = a.A;
+    p.W = a.w;
+    p.S = a.s;
+    p.D = a.D;
+    p.N = (int)a.N;
+    p.K = (int)a.K;
+    p.Np = (int)a.Np;
+    p.M = (int)P;
+    p.ngroups = 1;
+    p.gsteps = 1;
+    p.w_estride = a.w_estride;
+    p.s_estride = a.s_estride;
+    p.tiles_m = (int)L.max_tiles;
+    p.tiles_n = (int)cdiv(a.Np, 128);
+    p.tile_info = tiles;
+    p.ntiles = ntiles;
+    p.sorted = sorted;
+    p.top_k = a.top_k;
+    hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeBM, 128>), dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(256),
+                       0, a.stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace hq

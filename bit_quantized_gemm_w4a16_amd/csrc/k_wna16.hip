@@ -8,13 +8,10 @@
 // weights laid out so that one 16-byte load per lane is one MFMA B fragment
 // for four consecutive K steps.
 //
-// Small M (M <= 64): a GEMV-like schedule.  Each workgroup owns one 16-column
-// strip; its waves split K; every wave issues all of its weight loads first
-// (the data is streamed once from HBM), then decodes and multiplies.  The
+// Small M (M <= 64): a GEMV-like schedule (see the skinny kernel below).  The
 // group scale is applied to the fp32 accumulator once per 128-K chunk, so the
 // dequantised operand (q - z, an integer in [-15, 15]) is exact in both bf16
-// and fp16.  Waves reduce through LDS; when K is split across workgroups the
-// last workgroup to arrive sums the partial tiles in a fixed order.
+// and fp16.  Large M: the LDS-tiled MFMA template in tile_gemm.hpp.
 #include "hq_device.hpp"
 #include "hq_internal.h"
 #include "tile_gemm.hpp"
@@ -54,133 +51,260 @@ __device__ __forceinline__ Frag8 deq4_bf16_biased(uint32_t w) {
 
 // -------------------------------------------------------------------------
 // small-M kernel
+//
+// Workgroup = 4 waves covering NS strips (16 columns each) and one K slice.
+// Waves split the workgroup as WS strip-columns x WK K-parts; each wave owns
+// SPW strips.  Every wave first issues all of its packed-weight loads into
+// registers (the HBM stream), then the workgroup copies the A slice, the
+// slice's group scales and zero-points into LDS with direct-to-LDS loads; one
+// wait, one barrier, then decode + MFMA with A fragments read from LDS.  The
+// K-parts reduce through LDS; K slices (split-K) through the workspace, where
+// the last workgroup to arrive sums the partial tiles in slice order.
 // -------------------------------------------------------------------------
 
-constexpr int kGemvMaxWaves = 8;
+constexpr int kSkinnyLds = 150 * 1024;
 
-template <bool BF16, bool ZP, int MT, int KC>
-__global__ __launch_bounds__(64 * kGemvMaxWaves) void wna16_gemv_kernel(
-    const uint16_t* __restrict__ A, int M, int K, const v4u* __restrict__ W,
-    const uint16_t* __restrict__ S, const uint64_t* __restrict__ Z, int nc, int ngroups,
-    int gchunks, uint16_t* __restrict__ D, int N, int Np, float* __restrict__ part,
-    unsigned* __restrict__ counters, int splits) {
-    __shared__ float red[kGemvMaxWaves * MT * 256];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, WK = blockDim.x >> 6;
-    const int strip = blockIdx.x, split = blockIdx.y;
-    const int TW = WK * splits, gw = split * WK + wave;
-    const int c_begin = (int)((int64_t)gw * nc / TW), c_end = (int)((int64_t)(gw + 1) * nc / TW);
+__device__ __forceinline__ void lds_dma16(const void* g, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+}
+
+struct SkinnyArgs {
+    const uint16_t* A;
+    const v4u* W;
+    const uint16_t* S;
+    const uint32_t* Z;   // packed zero-points as 32-bit words (two per strip-group)
+    uint16_t* D;
+    float* part;
+    unsigned* counters;
+    int M, K, N, Np, nc, ngroups, gchunks, splits;
+    int NS, WS;          // strips per workgroup, wave strip-columns (WK = 4 / WS)
+    int a_off, s_off, z_off, gslab_max;  // LDS layout (bytes / groups)
+};
+
+template <bool BF16, bool ZP, int MT, int SPW, int CPW>
+__global__ __launch_bounds__(256) void wna16_skinny_kernel(SkinnyArgs p) {
+    __shared__ __attribute__((aligned(1024))) char lds[kSkinnyLds];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, quad = lane >> 4;
+    const int WS = p.WS, WK = 4 / WS;
+    const int ws = wave % WS, wk = wave / WS;
+    const int nstrips = p.Np / 16;
+    const int strip_base = blockIdx.x * p.NS;
+    const int split = blockIdx.y;
+    // K slice of the workgroup, in 128-K chunks, and of this wave
+    const int c0 = (int)((int64_t)split * p.nc / p.splits), c1 = (int)((int64_t)(split + 1) * p.nc / p.splits);
+    const int cw0 = c0 + (c1 - c0) * wk / WK, cw1 = c0 + (c1 - c0) * (wk + 1) / WK;
+    const int g0 = c0 / p.gchunks, gslab = (c1 - 1) / p.gchunks - g0 + 1;
+    const int U = (c1 - c0) * 16;  // 16-byte units per A row in LDS
 
-    v4f acc[MT];
+    // ---- 1. the wave's packed weights: all loads in flight at once ----
+    v4u w[SPW][CPW];
+    int wstrip[SPW];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < SPW; ++sp) {
+        wstrip[sp] = strip_base + ws * SPW + sp;
+        const int st = wstrip[sp] < nstrips ? wstrip[sp] : nstrips - 1;
+        const v4u* Wst = p.W + (size_t)st * p.nc * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
+            if (cw0 + i < cw1) w[sp][i] = ld_nt(Wst + (size_t)(cw0 + i) * 64);
+    }
 
-    const v4u* Wst = W + (size_t)strip * nc * 64 + lane;
-    const uint16_t* Sst = S + (size_t)strip * ngroups * 16 + col;
-    for (int cb = c_begin; cb < c_end; cb += KC) {
-        v4u w[KC];
+    // ---- 2. A slice, scales and zero-points -> LDS (direct loads) ----
+    {
+        const int slots = p.M * U;
+        const char* Abase = (const char*)p.A + (size_t)c0 * 256;
+        for (int ib = wave * 64; ib < slots; ib += 256) {
+            const int s = ib + lane;
+            if (s < slots) {
+                const int row = s / U, pos = s % U;
+                const int unit = pos ^ (row & 15);
+                lds_dma16(Abase + (size_t)row * p.K * 2 + unit * 16, lds + p.a_off + ib * 16);
+            }
+        }
+        const int sunits = p.NS * gslab * 2;  // 32 bytes of scales per (strip, group)
+        for (int ib = wave * 64; ib < sunits; ib += 256) {
+            const int s = ib + lane;
+            if (s < sunits) {
+                const int j = s / (gslab * 2), u = s % (gslab * 2);
+                const int st = strip_base + j < nstrips ? strip_base + j : nstrips - 1;
+                lds_dma16((const char*)p.S + ((size_t)st * p.ngroups + g0) * 32 + u * 16, lds + p.s_off + ib * 16);
+            }
+        }
+        if constexpr (ZP) {
+            const int zwords = p.NS * gslab * 2;  // two 32-bit words per (strip, group)
+            for (int ib = wave * 64; ib < zwords; ib += 256) {
+                const int s = ib + lane;
+                if (s < zwords) {
+                    const int j = s / (gslab * 2), u = s % (gslab * 2);
+                    const int st = strip_base + j < nstrips ? strip_base + j : nstrips - 1;
+                    lds_dma4(p.Z + ((size_t)st * p.ngroups + g0) * 2 + u, lds + p.z_off + ib * 4);
+                }
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // ---- 3. decode + MFMA, group scale on the fp32 accumulator ----
+    v4f acc[SPW][MT];
 #pragma unroll
-        for (int i = 0; i < KC; ++i)
-            if (cb + i < c_end) w[i] = ld_nt(Wst + (size_t)(cb + i) * 64);
+    for (int sp = 0; sp < SPW; ++sp)
 #pragma unroll
-        for (int i = 0; i < KC; ++i) {
+        for (int mt = 0; mt < MT; ++mt) acc[sp][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    const char* lA = lds + p.a_off;
+    const uint16_t* lS = (const uint16_t*)(lds + p.s_off);
+    const uint32_t* lZ = (const uint32_t*)(lds + p.z_off);
+    Frag8 ones;
+    ones.u = v4u{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+
+    for (int cb = cw0; cb < cw1; cb += CPW) {
+        if (cb != cw0) {  // K longer than one register batch: fetch the next batch
+#pragma unroll
+            for (int sp = 0; sp < SPW; ++sp) {
+                const int st = wstrip[sp] < nstrips ? wstrip[sp] : nstrips - 1;
+                const v4u* Wst = p.W + (size_t)st * p.nc * 64 + lane;
+#pragma unroll
+                for (int i = 0; i < CPW; ++i)
+                    if (cb + i < cw1) w[sp][i] = ld_nt(Wst + (size_t)(cb + i) * 64);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
             const int c = cb + i;
-            if (c >= c_end) break;
-            const int g = c / gchunks;
-            const float sc = bits16_to_f32<BF16>(Sst[(size_t)g * 16]);
-            uint32_t z = 8;
-            if constexpr (ZP) z = (uint32_t)(Z[(size_t)strip * ngroups + g] >> (4 * col)) & 15u;
+            if (c >= cw1) break;
+            // A fragments of this chunk (rows >= M read row M-1; their outputs are dropped)
             Frag8 af[MT][4];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int row = mt * 16 + col;
-                const uint16_t* ap = A + (size_t)row * K + (size_t)c * 128 + quad * 32;
+                int row = mt * 16 + col;
+                row = row < p.M ? row : p.M - 1;
+                const char* ar = lA + (size_t)row * U * 16;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    if (row < M) af[mt][t].u = ld16(ap + 8 * t);
-                    else af[mt][t].u = v4u{0u, 0u, 0u, 0u};
+                    const int unit = (c - c0) * 16 + 4 * quad + t;
+                    af[mt][t].u = *(const v4u*)(ar + ((unit ^ (row & 15)) * 16));
                 }
             }
-            v4f gacc[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) gacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
-            Frag8 bc;
-            uint32_t nbias2 = 0;
+            const int g = c / p.gchunks - g0;
+            v4f rs[MT];
             if constexpr (BF16) {
-                const uint32_t nb = 0xC300u | z;  // bf16 bits of -(128 + z)
-                bc.u = v4u{nb | (nb << 16), nb | (nb << 16), nb | (nb << 16), nb | (nb << 16)};
-            } else {
-                const uint32_t nb = 0xE400u | z;  // fp16 bits of -(1024 + z)
-                nbias2 = nb | (nb << 16);
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                uint32_t word = w[i][t];
-                if constexpr (!ZP) word ^= 0x88888888u;  // two's complement -> offset binary
-                Frag8 b;
-                if constexpr (BF16) b = deq4_bf16_biased(word);
-                else b = deq4_f16(word, nbias2);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    gacc[mt] = mfma16<BF16>(af[mt][t], b, gacc[mt]);
-                    if constexpr (BF16) gacc[mt] = mfma16<BF16>(af[mt][t], bc, gacc[mt]);
+                    rs[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) rs[mt] = mfma16<true>(af[mt][t], ones, rs[mt]);
                 }
             }
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] += sc * gacc[mt];
+            for (int sp = 0; sp < SPW; ++sp) {
+                const int j = ws * SPW + sp;
+                const float sc = bits16_to_f32<BF16>(lS[(j * gslab + g) * 16 + col]);
+                uint32_t z = 8;
+                if constexpr (ZP) z = (lZ[(j * gslab + g) * 2 + (col >> 3)] >> (4 * (col & 7))) & 15u;
+                v4f gacc[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) gacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+                const uint32_t nbz = 0xE400u | z;  // fp16 bits of -(1024 + z)
+                const uint32_t nbias2 = nbz | (nbz << 16);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    uint32_t word = w[sp][i][t];
+                    if constexpr (!ZP) word ^= 0x88888888u;  // two's complement -> offset binary
+                    Frag8 b;
+                    if constexpr (BF16) b = deq4_bf16_biased(word);
+                    else b = deq4_f16(word, nbias2);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) gacc[mt] = mfma16<BF16>(af[mt][t], b, gacc[mt]);
+                }
+                if constexpr (BF16) {
+                    const float zc = (float)(128u + z);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[sp][mt] += sc * (gacc[mt] - zc * rs[mt]);
+                } else {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[sp][mt] += sc * gacc[mt];
+                }
+            }
         }
     }
 
+    // ---- 4. reduce the K-parts of the workgroup through LDS ----
     if (WK > 1) {
+        __syncthreads();  // the A slice is no longer needed
+        float* red = (float*)lds;
+        if (wk > 0) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int sp = 0; sp < SPW; ++sp)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[((wave * MT + mt) * 4 + r) * 64 + lane] = acc[mt][r];
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        red[((((wk - 1) * WS + ws) * SPW + sp) * MT * 4 + mt * 4 + r) * 64 + lane] = acc[sp][mt][r];
+        }
         __syncthreads();
-        if (wave != 0) return;
-        for (int w2 = 1; w2 < WK; ++w2)
+        if (wk == 0)
+            for (int k2 = 1; k2 < WK; ++k2)
+#pragma unroll
+            for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                            acc[sp][mt][r] += red[((((k2 - 1) * WS + ws) * SPW + sp) * MT * 4 + mt * 4 + r) * 64 + lane];
+    }
+    // waves of K-part 0 own the results; the others stay alive for the barriers below
+    const bool owner = wk == 0;
+
+    // ---- 5. output: lane (col, quad) holds rows mt*16 + 4*quad + r of its strip's column col ----
+    if (p.splits == 1) {
+        if (!owner) return;
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp) {
+            const int n = wstrip[sp] * 16 + col;
+            if (wstrip[sp] >= nstrips || n >= p.N) continue;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mt][r] += red[((w2 * MT + mt) * 4 + r) * 64 + lane];
+                for (int r = 0; r < 4; ++r) {
+                    const int m = mt * 16 + quad * 4 + r;
+                    if (m < p.M) p.D[(size_t)m * p.N + n] = f32_to_16<BF16>(acc[sp][mt][r]);
+                }
+        }
+        return;
     }
-
-    // lane (col, quad) holds rows mt*16 + 4*quad + r of column strip*16 + col
-    const int n = strip * 16 + col;
-    if (splits == 1) {
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        if (!owner || wstrip[sp] >= nstrips) continue;
+        const int n = wstrip[sp] * 16 + col;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = mt * 16 + quad * 4 + r;
-                if (m < M && n < N) D[(size_t)m * N + n] = f32_to_16<BF16>(acc[mt][r]);
+                if (m < p.M) p.part[((size_t)split * p.M + m) * p.Np + n] = acc[sp][mt][r];
             }
-        return;
     }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = mt * 16 + quad * 4 + r;
-            if (m < M) part[((size_t)split * M + m) * Np + n] = acc[mt][r];
-        }
     __threadfence();
-    unsigned prev = 0;
-    if (lane == 0) prev = atomicAdd(&counters[strip], 1u);
-    prev = __shfl(prev, 0);
-    if (prev != (unsigned)(splits - 1)) return;
+    __syncthreads();  // every wave of this workgroup has published its partials
+    __shared__ unsigned last;
+    if (tid == 0) last = atomicAdd(&p.counters[blockIdx.x], 1u) == (unsigned)(p.splits - 1);
+    __syncthreads();
+    if (!last) return;
     __threadfence();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = mt * 16 + quad * 4 + r;
-            if (m >= M) continue;
-            float v = 0.f;
-            for (int s = 0; s < splits; ++s) v += part[((size_t)s * M + m) * Np + n];
-            if (n < N) D[(size_t)m * N + n] = f32_to_16<BF16>(v);
-        }
-    if (lane == 0) counters[strip] = 0u;
+    // the last workgroup of this strip group sums every slice in order
+    const int ncols = p.NS * 16;
+    for (int e = tid; e < p.M * ncols; e += 256) {
+        const int m = e / ncols, n = strip_base * 16 + e % ncols;
+        if (n >= p.N) continue;
+        float v = 0.f;
+        for (int sl = 0; sl < p.splits; ++sl) v += p.part[((size_t)sl * p.M + m) * p.Np + n];
+        p.D[(size_t)m * p.N + n] = f32_to_16<BF16>(v);
+    }
+    if (tid == 0) p.counters[blockIdx.x] = 0u;
 }
 
 // -------------------------------------------------------------------------
@@ -189,55 +313,94 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void wna16_gemv_kernel(
 
 namespace {
 
-struct GemvPlan {
-    int WK, splits, KC, MT;
+struct SkinnyPlan {
+    int NS, WS, SPW, splits, MT, CPW;
+    int a_off, s_off, z_off;
+    int64_t groups_x;
 };
 
-GemvPlan plan_gemv(int64_t M, int64_t Np, int64_t K) {
-    const int64_t nstrips = Np / 16, nc = K / 128;
-    int64_t target = 2048 / nstrips;  // waves per strip for ~8 waves per CU
-    if (target < 1) target = 1;
-    if (target > nc) target = nc;
-    GemvPlan p;
-    p.WK = (int)(target < kGemvMaxWaves ? target : kGemvMaxWaves);
-    p.splits = (int)cdiv(target, p.WK);
-    if (nstrips > kMaxCounters) p.splits = 1;
-    const int64_t per = cdiv(nc, (int64_t)p.WK * p.splits);
-    p.KC = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
+SkinnyPlan plan_skinny(int64_t M, int64_t Np, int64_t K, int G) {
+    const int64_t nstrips = Np / 16, nc = K / 128, gch = G / 128;
+    SkinnyPlan p{};
+    // strips per workgroup grow with M so the A slice is re-read ~nstrips/NS times
+    p.NS = M <= 8 ? 1 : M <= 16 ? 2 : M <= 32 ? 4 : 8;
+    while (p.NS > 1 && p.NS > nstrips) p.NS /= 2;
+    p.SPW = p.NS <= 4 ? 1 : p.NS / 4;
+    p.WS = p.NS / p.SPW;  // 1, 2 or 4 wave strip-columns
+    const int WK = 4 / p.WS;
+    p.groups_x = cdiv(nstrips, p.NS);
+    // K slices: enough workgroups to cover the chip, A slice within the LDS budget
+    int64_t S = cdiv(256, p.groups_x);
+    auto lds_need = [&](int64_t s) {
+        const int64_t cmax = cdiv(nc, s);
+        const int64_t gmax = cmax / gch + 2;
+        const int64_t a = ((M * cmax * 256 + 1023) / 1024) * 1024;
+        const int64_t sc = ((p.NS * gmax * 32 + 1023) / 1024) * 1024;
+        const int64_t z = ((p.NS * gmax * 8 + 1023) / 1024) * 1024;
+        return a + sc + z;
+    };
+    while (S < nc / WK && lds_need(S) > kSkinnyLds) ++S;
+    if (S > nc / WK) S = nc / WK > 0 ? nc / WK : 1;
+    if (S < 1) S = 1;
+    if (p.groups_x > kMaxCounters) S = 1;
+    p.splits = (int)S;
+    const int64_t cmax = cdiv(nc, S), gmax = cmax / gch + 2;
+    p.a_off = 0;
+    p.s_off = (int)(((M * cmax * 256 + 1023) / 1024) * 1024);
+    p.z_off = p.s_off + (int)(((p.NS * gmax * 32 + 1023) / 1024) * 1024);
     p.MT = (int)cdiv(M < 1 ? 1 : M, 16);
+    const int64_t per = cdiv(cmax, WK);
+    p.CPW = p.SPW == 1 ? 16 : 8;
+    (void)per;
     return p;
 }
 
-template <bool BF16, bool ZP, int MT>
-hipError_t launch_mt(const GemvPlan& p, dim3 grid, dim3 block, const DenseArgs& a, int64_t m0,
-                     int64_t Mslab, float* part, unsigned* counters) {
-    const uint16_t* A = (const uint16_t*)a.A + m0 * a.K;
-    uint16_t* D = (uint16_t*)a.D + m0 * a.N;
-    const int nc = (int)(a.K / 128), ngroups = (int)(a.K / a.group_size), gchunks = a.group_size / 128;
-#define HQ_GEMV_ARGS                                                                                  \
-    A, (int)Mslab, (int)a.K, (const v4u*)a.w, (const uint16_t*)a.s, (const uint64_t*)a.z, nc, ngroups, \
-        gchunks, D, (int)a.N, (int)a.Np, part, counters, p.splits
-    switch (p.KC) {
-        case 1: hipLaunchKernelGGL((wna16_gemv_kernel<BF16, ZP, MT, 1>), grid, block, 0, a.stream, HQ_GEMV_ARGS); break;
-        case 2: hipLaunchKernelGGL((wna16_gemv_kernel<BF16, ZP, MT, 2>), grid, block, 0, a.stream, HQ_GEMV_ARGS); break;
-        case 4: hipLaunchKernelGGL((wna16_gemv_kernel<BF16, ZP, MT, 4>), grid, block, 0, a.stream, HQ_GEMV_ARGS); break;
-        default: hipLaunchKernelGGL((wna16_gemv_kernel<BF16, ZP, MT, 8>), grid, block, 0, a.stream, HQ_GEMV_ARGS); break;
-    }
-#undef HQ_GEMV_ARGS
+template <bool BF16, bool ZP, int MT, int SPW>
+hipError_t launch_skinny_mt(const SkinnyPlan& pl, const SkinnyArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)pl.groups_x, (unsigned)pl.splits), block(256);
+    hipLaunchKernelGGL((wna16_skinny_kernel<BF16, ZP, MT, SPW, SPW == 1 ? 16 : 8>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
 template <bool BF16, bool ZP>
-hipError_t launch_gemv(const DenseArgs& a, int64_t m0, int64_t Mslab) {
-    GemvPlan p = plan_gemv(Mslab, a.Np, a.K);
-    dim3 grid((unsigned)(a.Np / 16), (unsigned)p.splits), block(64 * p.WK);
-    unsigned* counters = (unsigned*)a.ws;
-    float* part = a.ws ? (float*)((char*)a.ws + kCounterBytes) : nullptr;
-    switch (p.MT) {
-        case 1: return launch_mt<BF16, ZP, 1>(p, grid, block, a, m0, Mslab, part, counters);
-        case 2: return launch_mt<BF16, ZP, 2>(p, grid, block, a, m0, Mslab, part, counters);
-        case 3: return launch_mt<BF16, ZP, 3>(p, grid, block, a, m0, Mslab, part, counters);
-        default: return launch_mt<BF16, ZP, 4>(p, grid, block, a, m0, Mslab, part, counters);
+hipError_t launch_skinny(const DenseArgs& a) {
+    SkinnyPlan pl = plan_skinny(a.M, a.Np, a.K, a.group_size);
+    if (pl.z_off + ((pl.NS * (cdiv(a.K / 128, pl.splits) / (a.group_size / 128) + 2) * 8 + 1023) / 1024) * 1024 > kSkinnyLds)
+        return hipErrorInvalidValue;  // shape beyond the LDS plan (validated on the host side)
+    SkinnyArgs s{};
+    s.A = (const uint16_t*)a.A;
+    s.W = (const v4u*)a.w;
+    s.S = (const uint16_t*)a.s;
+    s.Z = (const uint32_t*)a.z;
+    s.D = (uint16_t*)a.D;
+    s.counters = (unsigned*)a.ws;
+    s.part = a.ws ? (float*)((char*)a.ws + kCounterBytes) : nullptr;
+    s.M = (int)a.M;
+    s.K = (int)a.K;
+    s.N = (int)a.N;
+    s.Np = (int)a.Np;
+    s.nc = (int)(a.K / 128);
+    s.ngroups = (int)(a.K / a.group_size);
+    s.gchunks = a.group_size / 128;
+    s.splits = pl.splits;
+    s.NS = pl.NS;
+    s.WS = pl.WS;
+    s.a_off = pl.a_off;
+    s.s_off = pl.s_off;
+    s.z_off = pl.z_off;
+    if (pl.SPW == 2) {
+        switch (pl.MT) {
+            case 1: return launch_skinny_mt<BF16, ZP, 1, 2>(pl, s, a.stream);
+            case 2: return launch_skinny_mt<BF16, ZP, 2, 2>(pl, s, a.stream);
+            case 3: return launch_skinny_mt<BF16, ZP, 3, 2>(pl, s, a.stream);
+            default: return launch_skinny_mt<BF16, ZP, 4, 2>(pl, s, a.stream);
+        }
+    }
+    switch (pl.MT) {
+        case 1: return launch_skinny_mt<BF16, ZP, 1, 1>(pl, s, a.stream);
+        case 2: return launch_skinny_mt<BF16, ZP, 2, 1>(pl, s, a.stream);
+        case 3: return launch_skinny_mt<BF16, ZP, 3, 1>(pl, s, a.stream);
+        default: return launch_skinny_mt<BF16, ZP, 4, 1>(pl, s, a.stream);
     }
 }
 
@@ -263,7 +426,7 @@ hipError_t launch_tile(const DenseArgs& a) {
 
 template <bool BF16, bool ZP>
 hipError_t launch_all(const DenseArgs& a) {
-    if (a.M <= 64) return launch_gemv<BF16, ZP>(a, 0, a.M);
+    if (a.M <= 64) return launch_skinny<BF16, ZP>(a);
     if constexpr (BF16) return launch_tile<Fmt::WNA16_BF16, 128>(a);
     const int64_t tiles_n = cdiv(a.Np, 128);
     if (cdiv(a.M, 256) * tiles_n >= 256) return launch_tile<Fmt::WNA16_F16, 256>(a);
@@ -273,10 +436,9 @@ hipError_t launch_all(const DenseArgs& a) {
 }  // namespace
 
 size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size) {
-    (void)group_size;
-    const int64_t Np = pad16(N);
     if (M > 64) return 0;  // the tiled kernel needs no workspace
-    GemvPlan p = plan_gemv(M, Np, K);
+    const int64_t Np = pad16(N);
+    SkinnyPlan p = plan_skinny(M, Np, K, group_size);
     if (p.splits <= 1) return 0;
     return kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)Np * sizeof(float);
 }
