@@ -14,9 +14,12 @@ successive calls rotate through them, so every call streams its weights from
 HBM, as in the pages' cold-L2 protocol ("Humming wird angekuendigt", section
 "Leistung").
 
-Timing: HIP events on the stream the library launches on bracket every call;
-the step wall time is bracketed by torch.cuda.synchronize().  `value` is the
-sweep's algorithmic TFLOP/s: total flops of one step / step wall time.
+Timing: the calls are captured into HIP graphs, so host launch overhead does
+not starve the GPU.  Per M: a graph of back-to-back calls (one per weight
+copy) is replayed between HIP events on the capturing stream.  Per step: a
+graph of the whole sweep is replayed, K replays bracketed by
+torch.cuda.synchronize(); `value` = total algorithmic flops of one step /
+step wall time.
 """
 from __future__ import annotations
 
@@ -92,9 +95,8 @@ class DenseW4A16:
     def kernel_of(self, M):
         return "gemv" if M <= 64 else "tile"
 
-    def call(self, M):
-        w, s, z = self.copies[self.i % len(self.copies)]
-        self.i += 1
+    def call(self, M, copy):
+        w, s, z = self.copies[copy]
         hq.hq_gemm(self.desc, M, self.A, None, w, s, z, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
 
     def cpu_baseline(self, budget_s=15.0):
@@ -123,29 +125,58 @@ def _cores():
 
 # ---------------------------------------------------------------------------
 
-def run(work, sweep, steps, warmup):
-    stream = torch.cuda.current_stream()
-    # warmup
-    for _ in range(warmup):
-        for M in sweep:
-            work.call(M)
+def _capture(fn):
+    """Capture fn() (a sequence of hq calls on the current stream) into a HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                      # eager run on the capture stream (allocator warm-up)
     torch.cuda.synchronize()
-    per = {M: [] for M in sweep}
-    evs = []
+    with torch.cuda.graph(g, stream=side):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def run(work, sweep, steps, warmup):
+    """Per-M timing from graphs of R back-to-back calls (each on its own cold weight copy),
+    and the step timing from graphs of whole sweeps (one weight copy per call)."""
+    ncopy = len(work.copies)
+    per = {}
+    for M in sweep:
+        def calls(M=M):
+            for r in range(ncopy):
+                work.call(M, r)
+        g = _capture(calls)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 3
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per[M] = [e0.elapsed_time(e1) * 1e-3 / (reps * ncopy)]
+        del g
+    # sweep graphs: graph j uses copies j*len(sweep) + i (mod ncopy), so no copy repeats within ncopy calls
+    nsw = max(1, ncopy // len(sweep))
+    graphs = []
+    for j in range(nsw):
+        def sweep_calls(j=j):
+            for i, M in enumerate(sweep):
+                work.call(M, (j * len(sweep) + i) % ncopy)
+        graphs.append(_capture(sweep_calls))
+    for w in range(warmup):
+        graphs[w % nsw].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        for M in sweep:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            work.call(M)
-            e1.record(stream)
-            evs.append((M, e0, e1))
+    for k in range(steps):
+        graphs[k % nsw].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for M, e0, e1 in evs:
-        per[M].append(e0.elapsed_time(e1) * 1e-3)
     return wall, per
 
 

@@ -58,8 +58,8 @@ __device__ __forceinline__ Frag8 deq4_bf16_biased(uint32_t w) {
 // registers (the HBM stream), then the workgroup copies the A slice, the
 // slice's group scales and zero-points into LDS with direct-to-LDS loads; one
 // wait, one barrier, then decode + MFMA with A fragments read from LDS.  The
-// K-parts reduce through LDS; K slices (split-K) through the workspace, where
-// the last workgroup to arrive sums the partial tiles in slice order.
+// K-parts reduce through LDS; K slices (split-K) write fp32 partial tiles to
+// the workspace and a finalize kernel sums them in slice order.
 // -------------------------------------------------------------------------
 
 constexpr int kSkinnyLds = 150 * 1024;
@@ -78,7 +78,6 @@ struct SkinnyArgs {
     const uint32_t* Z;   // packed zero-points as 32-bit words (two per strip-group)
     uint16_t* D;
     float* part;
-    unsigned* counters;
     int M, K, N, Np, nc, ngroups, gchunks, splits;
     int NS, WS;          // strips per workgroup, wave strip-columns (WK = 4 / WS)
     int a_off, s_off, z_off, gslab_max;  // LDS layout (bytes / groups)
@@ -100,20 +99,7 @@ __global__ __launch_bounds__(256) void wna16_skinny_kernel(SkinnyArgs p) {
     const int g0 = c0 / p.gchunks, gslab = (c1 - 1) / p.gchunks - g0 + 1;
     const int U = (c1 - c0) * 16;  // 16-byte units per A row in LDS
 
-    // ---- 1. the wave's packed weights: all loads in flight at once ----
-    v4u w[SPW][CPW];
-    int wstrip[SPW];
-#pragma unroll
-    for (int sp = 0; sp < SPW; ++sp) {
-        wstrip[sp] = strip_base + ws * SPW + sp;
-        const int st = wstrip[sp] < nstrips ? wstrip[sp] : nstrips - 1;
-        const v4u* Wst = p.W + (size_t)st * p.nc * 64 + lane;
-#pragma unroll
-        for (int i = 0; i < CPW; ++i)
-            if (cw0 + i < cw1) w[sp][i] = ld_nt(Wst + (size_t)(cw0 + i) * 64);
-    }
-
-    // ---- 2. A slice, scales and zero-points -> LDS (direct loads) ----
+    // ---- 1. A slice, scales and zero-points -> LDS (direct loads, issued first) ----
     {
         const int slots = p.M * U;
         const char* Abase = (const char*)p.A + (size_t)c0 * 256;
@@ -146,7 +132,24 @@ __global__ __launch_bounds__(256) void wna16_skinny_kernel(SkinnyArgs p) {
             }
         }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // ---- 2. the wave's packed weights: CPW loads per strip, all in flight at once.
+    //         Indices past the wave's range repeat its last chunk (never used); a wave
+    //         with an empty range (more K-parts than chunks) re-reads the slice's first
+    //         chunk, so every load stays inside the strip. ----
+    const int wlast = cw1 > cw0 ? cw1 - 1 : c0;
+    v4u w[SPW][CPW];
+    int wstrip[SPW];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        wstrip[sp] = strip_base + ws * SPW + sp;
+        const int st = wstrip[sp] < nstrips ? wstrip[sp] : nstrips - 1;
+        const v4u* Wst = p.W + (size_t)st * p.nc * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) w[sp][i] = ld_nt(Wst + (size_t)min(cw0 + i, wlast) * 64);
+    }
+    // wait for this wave's LDS copies (issued before the SPW*CPW weight loads), then for everyone's
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SPW * CPW) : "memory");
     __syncthreads();
 
     // ---- 3. decode + MFMA, group scale on the fp32 accumulator ----
@@ -168,8 +171,7 @@ __global__ __launch_bounds__(256) void wna16_skinny_kernel(SkinnyArgs p) {
                 const int st = wstrip[sp] < nstrips ? wstrip[sp] : nstrips - 1;
                 const v4u* Wst = p.W + (size_t)st * p.nc * 64 + lane;
 #pragma unroll
-                for (int i = 0; i < CPW; ++i)
-                    if (cb + i < cw1) w[sp][i] = ld_nt(Wst + (size_t)(cb + i) * 64);
+                for (int i = 0; i < CPW; ++i) w[sp][i] = ld_nt(Wst + (size_t)min(cb + i, cw1 - 1) * 64);
             }
         }
 #pragma unroll
@@ -288,23 +290,20 @@ __global__ __launch_bounds__(256) void wna16_skinny_kernel(SkinnyArgs p) {
                 if (m < p.M) p.part[((size_t)split * p.M + m) * p.Np + n] = acc[sp][mt][r];
             }
     }
-    __threadfence();
-    __syncthreads();  // every wave of this workgroup has published its partials
-    __shared__ unsigned last;
-    if (tid == 0) last = atomicAdd(&p.counters[blockIdx.x], 1u) == (unsigned)(p.splits - 1);
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    // the last workgroup of this strip group sums every slice in order
-    const int ncols = p.NS * 16;
-    for (int e = tid; e < p.M * ncols; e += 256) {
-        const int m = e / ncols, n = strip_base * 16 + e % ncols;
-        if (n >= p.N) continue;
+}
+
+// Split-K finalize: D[m][n] = sum over slices s = 0..S-1 (in order) of part[s][m][n].
+template <bool BF16>
+__global__ __launch_bounds__(256) void splitk_finalize_kernel(const float* __restrict__ part, int S, int M, int N, int Np,
+                                                              uint16_t* __restrict__ D) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int m = (int)(e / N), n = (int)(e % N);
+        const float* pp = part + (size_t)m * Np + n;
         float v = 0.f;
-        for (int sl = 0; sl < p.splits; ++sl) v += p.part[((size_t)sl * p.M + m) * p.Np + n];
-        p.D[(size_t)m * p.N + n] = f32_to_16<BF16>(v);
+        for (int sl = 0; sl < S; ++sl) v += pp[(size_t)sl * M * Np];
+        D[e] = f32_to_16<BF16>(v);
     }
-    if (tid == 0) p.counters[blockIdx.x] = 0u;
 }
 
 // -------------------------------------------------------------------------
@@ -342,24 +341,43 @@ SkinnyPlan plan_skinny(int64_t M, int64_t Np, int64_t K, int G) {
     while (S < nc / WK && lds_need(S) > kSkinnyLds) ++S;
     if (S > nc / WK) S = nc / WK > 0 ? nc / WK : 1;
     if (S < 1) S = 1;
-    if (p.groups_x > kMaxCounters) S = 1;
     p.splits = (int)S;
     const int64_t cmax = cdiv(nc, S), gmax = cmax / gch + 2;
     p.a_off = 0;
     p.s_off = (int)(((M * cmax * 256 + 1023) / 1024) * 1024);
     p.z_off = p.s_off + (int)(((p.NS * gmax * 32 + 1023) / 1024) * 1024);
     p.MT = (int)cdiv(M < 1 ? 1 : M, 16);
+    // weight loads per wave and strip: the smallest instantiated batch that covers the wave's chunks
     const int64_t per = cdiv(cmax, WK);
-    p.CPW = p.SPW == 1 ? 16 : 8;
-    (void)per;
+    if (p.SPW == 1) p.CPW = per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : per <= 14 ? 14 : 16;
+    else p.CPW = per <= 4 ? 4 : per <= 7 ? 7 : 8;
     return p;
+}
+
+template <bool BF16, bool ZP, int MT, int SPW, int CPW>
+hipError_t launch_skinny_k(const SkinnyPlan& pl, const SkinnyArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)pl.groups_x, (unsigned)pl.splits), block(256);
+    hipLaunchKernelGGL((wna16_skinny_kernel<BF16, ZP, MT, SPW, CPW>), grid, block, 0, st, a);
+    return hipGetLastError();
 }
 
 template <bool BF16, bool ZP, int MT, int SPW>
 hipError_t launch_skinny_mt(const SkinnyPlan& pl, const SkinnyArgs& a, hipStream_t st) {
-    dim3 grid((unsigned)pl.groups_x, (unsigned)pl.splits), block(256);
-    hipLaunchKernelGGL((wna16_skinny_kernel<BF16, ZP, MT, SPW, SPW == 1 ? 16 : 8>), grid, block, 0, st, a);
-    return hipGetLastError();
+    if constexpr (SPW == 1) {
+        switch (pl.CPW) {
+            case 2: return launch_skinny_k<BF16, ZP, MT, 1, 2>(pl, a, st);
+            case 4: return launch_skinny_k<BF16, ZP, MT, 1, 4>(pl, a, st);
+            case 8: return launch_skinny_k<BF16, ZP, MT, 1, 8>(pl, a, st);
+            case 14: return launch_skinny_k<BF16, ZP, MT, 1, 14>(pl, a, st);
+            default: return launch_skinny_k<BF16, ZP, MT, 1, 16>(pl, a, st);
+        }
+    } else {
+        switch (pl.CPW) {
+            case 4: return launch_skinny_k<BF16, ZP, MT, 2, 4>(pl, a, st);
+            case 7: return launch_skinny_k<BF16, ZP, MT, 2, 7>(pl, a, st);
+            default: return launch_skinny_k<BF16, ZP, MT, 2, 8>(pl, a, st);
+        }
+    }
 }
 
 template <bool BF16, bool ZP>
@@ -373,8 +391,7 @@ hipError_t launch_skinny(const DenseArgs& a) {
     s.S = (const uint16_t*)a.s;
     s.Z = (const uint32_t*)a.z;
     s.D = (uint16_t*)a.D;
-    s.counters = (unsigned*)a.ws;
-    s.part = a.ws ? (float*)((char*)a.ws + kCounterBytes) : nullptr;
+    s.part = (float*)a.ws;
     s.M = (int)a.M;
     s.K = (int)a.K;
     s.N = (int)a.N;
@@ -388,20 +405,28 @@ hipError_t launch_skinny(const DenseArgs& a) {
     s.a_off = pl.a_off;
     s.s_off = pl.s_off;
     s.z_off = pl.z_off;
+    hipError_t e;
     if (pl.SPW == 2) {
         switch (pl.MT) {
-            case 1: return launch_skinny_mt<BF16, ZP, 1, 2>(pl, s, a.stream);
-            case 2: return launch_skinny_mt<BF16, ZP, 2, 2>(pl, s, a.stream);
-            case 3: return launch_skinny_mt<BF16, ZP, 3, 2>(pl, s, a.stream);
-            default: return launch_skinny_mt<BF16, ZP, 4, 2>(pl, s, a.stream);
+            case 1: e = launch_skinny_mt<BF16, ZP, 1, 2>(pl, s, a.stream); break;
+            case 2: e = launch_skinny_mt<BF16, ZP, 2, 2>(pl, s, a.stream); break;
+            case 3: e = launch_skinny_mt<BF16, ZP, 3, 2>(pl, s, a.stream); break;
+            default: e = launch_skinny_mt<BF16, ZP, 4, 2>(pl, s, a.stream); break;
+        }
+    } else {
+        switch (pl.MT) {
+            case 1: e = launch_skinny_mt<BF16, ZP, 1, 1>(pl, s, a.stream); break;
+            case 2: e = launch_skinny_mt<BF16, ZP, 2, 1>(pl, s, a.stream); break;
+            case 3: e = launch_skinny_mt<BF16, ZP, 3, 1>(pl, s, a.stream); break;
+            default: e = launch_skinny_mt<BF16, ZP, 4, 1>(pl, s, a.stream); break;
         }
     }
-    switch (pl.MT) {
-        case 1: return launch_skinny_mt<BF16, ZP, 1, 1>(pl, s, a.stream);
-        case 2: return launch_skinny_mt<BF16, ZP, 2, 1>(pl, s, a.stream);
-        case 3: return launch_skinny_mt<BF16, ZP, 3, 1>(pl, s, a.stream);
-        default: return launch_skinny_mt<BF16, ZP, 4, 1>(pl, s, a.stream);
-    }
+    if (e != hipSuccess || pl.splits == 1) return e;
+    int64_t blocks = cdiv(a.M * a.N, 256);
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL((splitk_finalize_kernel<BF16>), dim3((unsigned)blocks), dim3(256), 0, a.stream, (const float*)s.part,
+                       pl.splits, (int)a.M, (int)a.N, (int)a.Np, (uint16_t*)a.D);
+    return hipGetLastError();
 }
 
 template <Fmt F, int BM>
@@ -440,7 +465,7 @@ size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size) {
     const int64_t Np = pad16(N);
     SkinnyPlan p = plan_skinny(M, Np, K, group_size);
     if (p.splits <= 1) return 0;
-    return kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)Np * sizeof(float);
+    return (size_t)p.splits * (size_t)M * (size_t)Np * sizeof(float);
 }
 
 hipError_t wna16_launch(const DenseArgs& a, bool bf16, bool zp) {
