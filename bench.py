@@ -2,11 +2,12 @@
 """Benchmark of the hq quantized GEMM on one MI355X.
 
 A step is one pass of the hot path over the workload's M sweep: for every
-M in {1, 2, 4, ..., 8192} one hq_gemm call (host dispatch -> HIP kernels ->
+M in {1, 2, 4, ..., 8192} one library call (host dispatch -> HIP kernels ->
 output) on inputs already resident in HBM.  The default workload is the
 dense W4A16 asymmetric layer (fp16 activations, UINT4 weights with UINT4
-zero-points and fp16 scales per 128 K, N=4096, K=7168).  Other workloads
-(--config c1|c3|c4|c5) print their own line.
+zero-points and fp16 scales per 128 K, N=4096, K=7168), the configuration
+the metric is quoted on.  --config c1|c3|c4|c5|all measures the other
+workloads (one JSON line each).
 
 Cold cache: the packed weights are replicated into enough device copies
 (> 512 MiB in total, more than the 256 MiB Infinity Cache plus every L2) and
@@ -43,6 +44,7 @@ PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK = {"fp16": 2.5e15, "bf16": 2.5e15, "fp8": 5.0e15, "int8": 5.0e15}
 SWEEP = [1 << i for i in range(14)]
 COLD_BYTES = 512 << 20
+METRIC = "quant GEMM TFLOP/s + HBM GB/s vs roofline, M=1..8192, W4A16/W4A8/MoE"
 
 
 def log(msg):
@@ -53,74 +55,224 @@ def dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1).copy()).to("cuda")
 
 
+def _cores():
+    omp = os.environ.get("OMP_NUM_THREADS")
+    n = len(os.sched_getaffinity(0))
+    return min(n, int(omp)) if omp and omp.isdigit() else n
+
+
+def _timed_oracle(fn, nrows_for, budget_s):
+    """Time fn(rows) on a row sample sized to ~budget_s of CPU work."""
+    t0 = time.perf_counter()
+    fn(nrows_for(2))
+    t1 = max(time.perf_counter() - t0, 1e-3)
+    n = max(2, int(budget_s / t1 * 2))
+    rows = nrows_for(n)
+    t0 = time.perf_counter()
+    fn(rows)
+    return len(rows), time.perf_counter() - t0
+
+
+def _copies(tensors, nbytes, minimum=2):
+    n = max(minimum, -(-COLD_BYTES // max(nbytes, 1)))
+    return [tuple(None if t is None else t.clone() for t in tensors) for _ in range(n)]
+
+
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
 
 class DenseW4A16:
-    """Dense W4A16 asymmetric: fp16 A, UINT4 codes + UINT4 zero-points, fp16 scales, G=128."""
-    name = "dense_w4a16_zp_fp16_N4096_K7168"
-    dtype = "fp16"
+    """Dense W4A16 (UINT4 + zero-points fp16, or symmetric INT4 bf16), group 128."""
 
-    def __init__(self, N=4096, K=7168, G=128, Mmax=8192, bf16=False, zp=True, sym_cfg=False):
+    def __init__(self, N=4096, K=7168, G=128, Mmax=8192, bf16=False, zp=True, sweep=SWEEP, name=None):
         self.N, self.K, self.G, self.Mmax = N, K, G, Mmax
-        self.bf16, self.zp = bf16, zp
+        self.bf16, self.zp, self.sweep = bf16, zp, sweep
+        self.dtype = "bf16" if bf16 else "fp16"
+        self.name = name or f"dense_w4a16_{'zp' if zp else 'sym'}_{self.dtype}_N{N}_K{K}"
         t = torch.bfloat16 if bf16 else torch.float16
         log(f"[bench] generating {self.name}")
-        if zp:
-            d = syn.w4a16_zp(0, Mmax, N, K, G, t)
-        else:
-            d = syn.w4a16_sym(0, Mmax, N, K, G, t)
+        d = syn.w4a16_zp(0, Mmax, N, K, G, t) if zp else syn.w4a16_sym(0, Mmax, N, K, G, t, cfg=syn.C1)
         self.host = d
         self.desc = hq.desc_w4a16(N, K, G, bf16=bf16, zp=zp)
         wp, sp, zpk = hq.hq_repack(self.desc, d["q"], d["s"], d.get("z") if zp else None)
         self.wbytes = wp.size + sp.size + (zpk.size if zpk is not None else 0)
-        ncopy = max(2, -(-COLD_BYTES // self.wbytes))
-        w0, s0 = dev(wp), dev(sp)
-        z0 = dev(zpk) if zp else None
-        self.copies = [(w0.clone(), s0.clone(), None if z0 is None else z0.clone()) for _ in range(ncopy)]
+        self.copies = _copies((dev(wp), dev(sp), dev(zpk) if zp else None), self.wbytes)
         self.A = dev(d["A"])
         self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
-        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in SWEEP if m <= Mmax)
+        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in sweep)
         self.ws = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
-        self.i = 0
 
     def flops(self, M):
         return 2.0 * M * self.N * self.K
 
     def bytes(self, M):
-        # packed weights + scales + zeros (static) + A + D
         return self.wbytes + M * self.K * 2 + M * self.N * 2
 
     def kernel_of(self, M):
-        return "gemv" if M <= 64 else "tile"
+        return ("wna16_skinny_kernel (W4A16, M<=64)", "hbm") if M <= 64 else \
+               (f"tile_gemm_kernel (W4A16 {self.dtype}, M>64)", "mfma")
 
-    def call(self, M, copy):
-        w, s, z = self.copies[copy]
+    def call(self, M, c):
+        w, s, z = self.copies[c]
         hq.hq_gemm(self.desc, M, self.A, None, w, s, z, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
 
-    def cpu_baseline(self, budget_s=15.0):
+    def cpu_baseline(self, budget_s=12.0):
         import oracle
         d = self.host
-        rows = np.arange(2)
-        t0 = time.perf_counter()
-        oracle.gemm_wna16(d["A"], d["q"], d["s"], d.get("z"), N=self.N, K=self.K, G=self.G,
-                          a_bf16=self.bf16, w_signed=not self.zp, rows=rows)
-        t1 = time.perf_counter() - t0
-        nrows = int(max(2, min(self.Mmax, budget_s / max(t1, 1e-3) * 2)))
-        rows = np.arange(nrows)
-        t0 = time.perf_counter()
-        oracle.gemm_wna16(d["A"], d["q"], d["s"], d.get("z"), N=self.N, K=self.K, G=self.G,
-                          a_bf16=self.bf16, w_signed=not self.zp, rows=rows)
-        dt = time.perf_counter() - t0
-        return dict(value=self.flops(nrows) / dt / 1e12, unit="TFLOP/s", cores=_cores(), kind="oracle",
-                    sample=f"{nrows} output rows x N={self.N} x K={self.K} (fp64 accumulation), {dt:.1f} s")
+        f = lambda rows: oracle.gemm_wna16(d["A"], d["q"], d["s"], d.get("z"), N=self.N, K=self.K, G=self.G,
+                                           a_bf16=self.bf16, w_signed=not self.zp, rows=rows)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, self.Mmax)), budget_s)
+        return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(), kind="oracle",
+                    sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
 
 
-def _cores():
-    omp = os.environ.get("OMP_NUM_THREADS")
-    n = len(os.sched_getaffinity(0))
-    return min(n, int(omp)) if omp and omp.isdigit() else n
+class DenseW4A8:
+    """Dense W4A8-MXFP4: tokenwise e4m3 activations (quantised on the GPU, untimed)."""
+
+    def __init__(self, N=7168, K=4096, Mmax=8192, sweep=SWEEP):
+        self.N, self.K, self.Mmax, self.sweep = N, K, Mmax, sweep
+        self.dtype = "fp8"
+        self.name = f"dense_w4a8_mxfp4_N{N}_K{K}"
+        log(f"[bench] generating {self.name}")
+        d = syn.w4a8_mxfp4(0, Mmax, N, K)
+        self.host = d
+        self.desc = hq.desc_w4a8_mxfp4(N, K)
+        wp, ep, _ = hq.hq_repack(self.desc, d["q"], d["e"])
+        self.wbytes = wp.size + ep.size
+        self.copies = _copies((dev(wp), dev(ep)), self.wbytes)
+        x = dev(d["A0"])
+        self.A = torch.empty(Mmax * K, dtype=torch.uint8, device="cuda")
+        self.s_a = torch.empty(Mmax, dtype=torch.float32, device="cuda")
+        hq.hq_quantize_act(hq.HQ_DT_FP8_E4M3, Mmax, K, x, self.A, self.s_a)
+        torch.cuda.synchronize()
+        del x
+        self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+
+    def flops(self, M):
+        return 2.0 * M * self.N * self.K
+
+    def bytes(self, M):
+        return self.wbytes + M * self.K + 4 * M + M * self.N * 2
+
+    def kernel_of(self, M):
+        return ("tile_gemm_kernel (W4A8-MXFP4)", "mfma" if M >= 256 else "hbm")
+
+    def call(self, M, c):
+        w, e = self.copies[c]
+        hq.hq_gemm(self.desc, M, self.A, self.s_a, w, e, None, self.D)
+
+    def cpu_baseline(self, budget_s=12.0):
+        import oracle
+        d = self.host
+        qa, s_a = oracle.quant_act_e4m3(d["A0"][:64])
+        f = lambda rows: oracle.gemm_w4a8_mxfp4(qa, s_a, d["q"], d["e"], N=self.N, K=self.K, rows=rows)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, 64)), budget_s)
+        return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(), kind="oracle",
+                    sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
+
+
+class DenseW8A8:
+    """Dense W8A8 INT8 with per-token x per-channel epilogue, bf16 output."""
+
+    def __init__(self, N=18432, K=7168, Mmax=8192, sweep=SWEEP):
+        self.N, self.K, self.Mmax, self.sweep = N, K, Mmax, sweep
+        self.dtype = "int8"
+        self.name = f"dense_w8a8_int8_N{N}_K{K}"
+        log(f"[bench] generating {self.name}")
+        d = syn.w8a8_int8(0, Mmax, N, K)
+        self.host = d
+        self.desc = hq.desc_w8a8(N, K)
+        wp, sp, _ = hq.hq_repack(self.desc, d["w"], d["s_w"])
+        self.wbytes = wp.size + sp.size
+        self.copies = _copies((dev(wp), dev(sp)), self.wbytes)
+        self.A = dev(d["a"])
+        self.s_a = dev(d["s_a"])
+        self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+
+    def flops(self, M):
+        return 2.0 * M * self.N * self.K
+
+    def bytes(self, M):
+        return self.wbytes + M * self.K + 4 * M + M * self.N * 2
+
+    def kernel_of(self, M):
+        return ("tile_gemm_kernel (W8A8-INT8)", "mfma" if M >= 512 else "hbm")
+
+    def call(self, M, c):
+        w, s = self.copies[c]
+        hq.hq_gemm(self.desc, M, self.A, self.s_a, w, s, None, self.D)
+
+    def cpu_baseline(self, budget_s=12.0):
+        import oracle
+        d = self.host
+        f = lambda rows: oracle.gemm_w8a8(d["a"], d["s_a"], d["w"], d["s_w"], rows=rows)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, self.Mmax)), budget_s)
+        return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TOP/s", cores=_cores(), kind="oracle",
+                    sample=f"{n} output rows x N={self.N} x K={self.K}, exact int64 accumulation, {dt:.1f} s")
+
+
+class MoEMXFP4:
+    """MoE W4A16-MXFP4 gate+up: E=256, top-8, N=4096, K=7168, Zipf(1.1) routing; Indexed path
+    (each call = routing metadata + expert GEMM)."""
+
+    def __init__(self, E=256, top_k=8, N=4096, K=7168, Tmax=8192, sweep=SWEEP, mode="indexed"):
+        self.E, self.top_k, self.N, self.K, self.Tmax, self.sweep = E, top_k, N, K, Tmax, sweep
+        self.mode = mode
+        self.dtype = "bf16"
+        self.name = f"moe_w4a16_mxfp4_{mode}_E{E}_top{top_k}_N{N}_K{K}"
+        log(f"[bench] generating {self.name} (all {E} experts)")
+        d = syn.moe_mxfp4(0, Tmax, E, top_k, N, K)
+        self.host = d
+        self.desc = hq.desc_moe_mxfp4(E, N, K)
+        wp, ep, _ = hq.hq_repack(self.desc, d["q"], d["e"])
+        self.ebytes = (wp.size + ep.size) // E
+        n = 3                                     # 3 x 3.8 GB: > 256 MiB between reuses at every T
+        w0, e0 = dev(wp), dev(ep)
+        self.copies = [(w0, e0)] + [(w0.clone(), e0.clone()) for _ in range(n - 1)]
+        del wp, ep
+        self.ids = dev(d["ids"].astype(np.int32))
+        self.A = dev(d["A"])
+        self.D = torch.empty(Tmax * top_k * N * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = hq.hq_workspace_bytes(self.desc, Tmax, top_k)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        flat = d["ids"]
+        self.active = {T: len(np.unique(flat[:T])) for T in sweep}
+
+    def flops(self, T):
+        return 2.0 * T * self.top_k * self.N * self.K
+
+    def bytes(self, T):
+        return self.active[T] * self.ebytes + T * self.K * 2 + T * self.top_k * (self.N * 2 + 4)
+
+    def kernel_of(self, T):
+        return ("tile_gemm_kernel (MoE MXFP4 bf16)", "mfma" if T >= 4096 else "hbm")
+
+    def call(self, T, c):
+        w, e = self.copies[c]
+        hq.hq_moe_gemm(self.desc, hq.HQ_MOE_INDEXED, T, self.top_k, self.A, None, self.ids, None, w, e, None, self.D,
+                       self.ws, self.ws_bytes)
+
+    def cpu_baseline(self, budget_s=12.0):
+        import oracle
+        d = self.host
+        ids = d["ids"][:64]
+        sub_e = sorted(set(int(e) for e in ids.reshape(-1)))
+        f = lambda pairs: oracle.moe_mxfp4_bf16(d["A"][:64], ids, d["q"], d["e"], N=self.N, K=self.K, pairs=pairs)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, 64 * self.top_k)), budget_s)
+        return dict(value=round(2.0 * n * self.N * self.K / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(),
+                    kind="oracle", sample=f"{n} (token, expert) pairs of 64 tokens x N={self.N} x K={self.K} "
+                                          f"({len(sub_e)} experts touched), fp64 accumulation, {dt:.1f} s")
+
+
+WORKLOADS = {
+    "c1": lambda: DenseW4A16(N=1024, K=1024, Mmax=16, bf16=True, zp=False, sweep=[16],
+                             name="dense_w4a16_sym_bf16_M16_N1024_K1024"),
+    "c2": lambda: DenseW4A16(),
+    "c3": lambda: DenseW4A8(),
+    "c4": lambda: DenseW8A8(),
+    "c5": lambda: MoEMXFP4(),
+}
 
 
 # ---------------------------------------------------------------------------
@@ -131,7 +283,7 @@ def _capture(fn):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        fn()                      # eager run on the capture stream (allocator warm-up)
+        fn()                      # eager run on the capture stream
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=side):
         fn()
@@ -139,9 +291,10 @@ def _capture(fn):
     return g
 
 
-def run(work, sweep, steps, warmup):
-    """Per-M timing from graphs of R back-to-back calls (each on its own cold weight copy),
-    and the step timing from graphs of whole sweeps (one weight copy per call)."""
+def run(work, steps, warmup):
+    """Per-M timing from graphs of back-to-back calls (each on its own cold weight copy),
+    and the step timing from graphs of whole sweeps (rotating copies)."""
+    sweep = work.sweep
     ncopy = len(work.copies)
     per = {}
     for M in sweep:
@@ -159,9 +312,8 @@ def run(work, sweep, steps, warmup):
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        per[M] = [e0.elapsed_time(e1) * 1e-3 / (reps * ncopy)]
+        per[M] = e0.elapsed_time(e1) * 1e-3 / (reps * ncopy)
         del g
-    # sweep graphs: graph j uses copies j*len(sweep) + i (mod ncopy), so no copy repeats within ncopy calls
     nsw = max(1, ncopy // len(sweep))
     graphs = []
     for j in range(nsw):
@@ -180,57 +332,40 @@ def run(work, sweep, steps, warmup):
     return wall, per
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="c2")
-    ap.add_argument("--sweep", default=None, help="comma-separated M values (default 1..8192 powers of 2)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.set_device(0)
-    sweep = [int(x) for x in args.sweep.split(",")] if args.sweep else SWEEP
-    if args.config != "c2":
-        raise SystemExit(f"unknown --config {args.config}")
-    work = DenseW4A16()
-    wall, per = run(work, sweep, args.steps, args.warmup)
+def report(work, args, wall, per):
     ms_per_step = wall / args.steps * 1e3
-    flops_step = sum(work.flops(M) for M in sweep)
-    table = []
-    kern = {}
-    for M in sweep:
-        t = statistics.median(per[M])
+    flops_step = sum(work.flops(M) for M in work.sweep)
+    peak = PEAK[work.dtype]
+    table, kern = [], {}
+    for M in work.sweep:
+        t = per[M]
         F, B = work.flops(M), work.bytes(M)
-        peak = PEAK[work.dtype]
         table.append(dict(M=M, us=round(t * 1e6, 2), tflops=round(F / t / 1e12, 2), gbps=round(B / t / 1e9, 1),
                           hbm_frac=round(B / t / PEAK_HBM, 3), mfma_frac=round(F / t / peak, 3),
                           roofline_frac=round(max(B / PEAK_HBM, F / peak) / t, 3)))
-        k = work.kernel_of(M)
-        kern.setdefault(k, [0.0, 0.0, 0.0, 0])
-        kern[k][0] += F * len(per[M])
-        kern[k][1] += B * len(per[M])
-        kern[k][2] += sum(per[M])
-        kern[k][3] += len(per[M])
-    dom = max(kern, key=lambda k: kern[k][2])
-    F_tot, B_tot, t_tot, n = kern[dom]
-    if dom == "tile":
-        roof = dict(bound="mfma", achieved=round(F_tot / t_tot / 1e12, 1), peak=PEAK[work.dtype] / 1e12,
-                    unit="TFLOP/s", frac=round(F_tot / t_tot / PEAK[work.dtype], 4), traffic=None,
-                    kernel="tile_gemm_kernel (W4A16 fp16, M>=128)", launches=n, avg_us=round(t_tot / n * 1e6, 2))
+        name, bound = work.kernel_of(M)
+        k = kern.setdefault(name, dict(F=0.0, B=0.0, t=0.0, n=0, bounds={}))
+        k["F"] += F
+        k["B"] += B
+        k["t"] += t
+        k["n"] += 1
+        k["bounds"][bound] = k["bounds"].get(bound, 0.0) + t
+    dom = max(kern, key=lambda n: kern[n]["t"])
+    k = kern[dom]
+    bound = max(k["bounds"], key=k["bounds"].get)
+    if bound == "mfma":
+        roof = dict(bound="mfma", achieved=round(k["F"] / k["t"] / 1e12, 1), peak=peak / 1e12,
+                    unit="TFLOP/s" if work.dtype != "int8" else "TOP/s", frac=round(k["F"] / k["t"] / peak, 4))
     else:
-        roof = dict(bound="hbm", achieved=round(B_tot / t_tot / 1e9, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
-                    frac=round(B_tot / t_tot / PEAK_HBM, 4), traffic=None,
-                    kernel="wna16_gemv_kernel (M<=64)", launches=n, avg_us=round(t_tot / n * 1e6, 2))
+        roof = dict(bound="hbm", achieved=round(k["B"] / k["t"] / 1e9, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
+                    frac=round(k["B"] / k["t"] / PEAK_HBM, 4))
+    roof.update(traffic=None, kernel=dom, launches_per_step=k["n"], avg_us=round(k["t"] / k["n"] * 1e6, 2),
+                per_unit="flops 2*M*N*K per launch" if bound == "mfma" else "algorithmic bytes per launch")
     cpu = None if args.no_cpu_baseline else work.cpu_baseline()
-    line = {
-        "metric": "quant GEMM TFLOP/s + HBM GB/s vs roofline, M=1..8192, W4A16/W4A8/MoE",
+    return {
+        "metric": METRIC,
         "value": round(flops_step / (ms_per_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
+        "unit": "TFLOP/s" if work.dtype != "int8" else "TOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -240,13 +375,42 @@ def main():
         "vs_baseline": None,
         "dtype": work.dtype,
         "data": "synthetic",
-        "config": {"workload": work.name, "M_sweep": sweep, "N": work.N, "K": work.K, "group_size": work.G,
+        "config": {"workload": work.name, "M_sweep": work.sweep, "N": work.N, "K": work.K,
                    "cold_weight_copies": len(work.copies)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_M": table,
     }
-    print(json.dumps(line), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="c2", help="c1|c2|c3|c4|c5|all (default c2)")
+    ap.add_argument("--sweep", default=None, help="comma-separated M values (default 1..8192 powers of 2)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    names = list(WORKLOADS) if args.config == "all" else [args.config]
+    for nm in names:
+        if nm not in WORKLOADS:
+            raise SystemExit(f"unknown --config {nm}")
+        work = WORKLOADS[nm]()
+        if args.sweep and nm != "c1":
+            work.sweep = [int(x) for x in args.sweep.split(",")]
+            if hasattr(work, "active"):
+                flat = work.host["ids"]
+                work.active = {T: len(np.unique(flat[:T])) for T in work.sweep}
+        wall, per = run(work, args.steps, args.warmup)
+        print(json.dumps(report(work, args, wall, per)), flush=True)
+        del work
+        torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":
