@@ -148,6 +148,8 @@ class DenseW4A8:
         torch.cuda.synchronize()
         del x
         self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in sweep)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
     def flops(self, M):
         return 2.0 * M * self.N * self.K
@@ -160,7 +162,7 @@ class DenseW4A8:
 
     def call(self, M, c):
         w, e = self.copies[c]
-        hq.hq_gemm(self.desc, M, self.A, self.s_a, w, e, None, self.D)
+        hq.hq_gemm(self.desc, M, self.A, self.s_a, w, e, None, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
 
     def cpu_baseline(self, budget_s=12.0):
         import oracle
@@ -189,6 +191,8 @@ class DenseW8A8:
         self.A = dev(d["a"])
         self.s_a = dev(d["s_a"])
         self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in sweep)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
     def flops(self, M):
         return 2.0 * M * self.N * self.K
@@ -201,7 +205,7 @@ class DenseW8A8:
 
     def call(self, M, c):
         w, s = self.copies[c]
-        hq.hq_gemm(self.desc, M, self.A, self.s_a, w, s, None, self.D)
+        hq.hq_gemm(self.desc, M, self.A, self.s_a, w, s, None, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
 
     def cpu_baseline(self, budget_s=12.0):
         import oracle

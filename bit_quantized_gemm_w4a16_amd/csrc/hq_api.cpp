@@ -107,7 +107,9 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
 
 static size_t dense_workspace(const LayerInfo& L, int64_t M) {
     switch (L.kind) {
-        case Kind::WNA16: return wna16_workspace(M, L.N, L.K, (int)L.G);
+        case Kind::WNA16: return wna16_workspace(M, L.N, L.K, (int)L.G, L.a_bf16);
+        case Kind::W4A8_MX:
+        case Kind::W8A8: return w8bit_workspace(M, L.N, L.K);
         default: return 0;
     }
 }

@@ -54,6 +54,23 @@ __device__ __forceinline__ float bits16_to_f32(uint16_t v) {
     else return (float)__builtin_bit_cast(_Float16, v);
 }
 
+// Buffer-resource loads: base and size live in scalar registers, each lane
+// supplies a 32-bit offset and a wave-uniform offset goes in an SGPR, so a
+// staged load costs one VGPR of address instead of two.  A lane offset at or
+// beyond `bytes` reads zeros instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // word 3 = 0x00020000: raw (untyped) 32-bit data format, as the gfx9 ISA requires for range checks
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <bool NT = false>
+__device__ __forceinline__ v4u buf16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? 2 : 0));
+}
+__device__ __forceinline__ uint64_t buf8(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
 // 16-byte global loads: a non-temporal hint for data read exactly once.
 __device__ __forceinline__ v4u ld_nt(const v4u* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ v4u ld16(const void* p) { return *(const v4u*)p; }

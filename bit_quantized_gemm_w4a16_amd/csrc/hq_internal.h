@@ -36,10 +36,11 @@ struct DenseArgs {
 };
 
 // W4A16 (INT4 / UINT4+zp; bf16 / fp16 activations)
-size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size);
+size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size, bool bf16);
 hipError_t wna16_launch(const DenseArgs& a, bool bf16, bool zp);
 
-// W4A8-MXFP4 and W8A8-INT8
+// W4A8-MXFP4 and W8A8-INT8 (split-K workspace for mid M)
+size_t w8bit_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t w4a8_launch(const DenseArgs& a);
 hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32);
 

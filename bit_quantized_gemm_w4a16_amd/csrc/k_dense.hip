@@ -18,7 +18,7 @@ namespace hq {
 
 namespace {
 
-template <Fmt F, int BM>
+template <Fmt F>
 hipError_t launch(const DenseArgs& a, int raw_i32) {
     TileArgs p{};
     p.A = a.A;
@@ -26,30 +26,27 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
     p.W = a.w;
     p.S = a.s;
     p.D = a.D;
+    p.part = a.ws;
     p.M = (int)a.M;
+    p.a_rows = (int)a.M;
     p.N = (int)a.N;
     p.K = (int)a.K;
     p.Np = (int)a.Np;
     p.ngroups = 1;
     p.gsteps = 1;
     p.raw_i32 = raw_i32;
-    p.tiles_m = (int)cdiv(a.M, BM);
-    p.tiles_n = (int)cdiv(a.Np, 128);
-    hipLaunchKernelGGL((tile_gemm_kernel<F, BM, 128>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, a.stream, p);
-    return hipGetLastError();
-}
-
-template <Fmt F>
-hipError_t launch_any(const DenseArgs& a, int raw_i32) {
-    const int64_t tiles_n = cdiv(a.Np, 128);
-    if (cdiv(a.M, 256) * tiles_n >= 256) return launch<F, 256>(a, raw_i32);
-    return launch<F, 128>(a, raw_i32);
+    return launch_dense_plan<F>(plan_tile(a.M, a.Np, a.K, has_big_tile(F)), p, a.stream);
 }
 
 }  // namespace
 
-hipError_t w4a8_launch(const DenseArgs& a) { return launch_any<Fmt::W4A8_MX>(a, 0); }
+size_t w8bit_workspace(int64_t M, int64_t N, int64_t K) {
+    const int64_t Np = pad16(N);
+    return tile_workspace(plan_tile(M, Np, K, true), M, Np);  // both 8-bit-A formats have the 256-row tile
+}
 
-hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32) { return launch_any<Fmt::W8A8_I8>(a, raw_i32 ? 1 : 0); }
+hipError_t w4a8_launch(const DenseArgs& a) { return launch<Fmt::W4A8_MX>(a, 0); }
+
+hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32) { return launch<Fmt::W8A8_I8>(a, raw_i32 ? 1 : 0); }
 
 }  // namespace hq

@@ -250,18 +250,20 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     p.K = (int)a.K;
     p.Np = (int)a.Np;
     p.M = (int)P;
+    p.a_rows = (int)(a.indexed ? a.T : P);
     p.ngroups = 1;
     p.gsteps = 1;
     p.w_estride = a.w_estride;
     p.s_estride = a.s_estride;
     p.tiles_m = (int)L.max_tiles;
     p.tiles_n = (int)cdiv(a.Np, 128);
+    p.splits = 1;
     p.tile_info = tiles;
     p.ntiles = ntiles;
     p.sorted = sorted;
     p.top_k = a.top_k;
-    hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeBM, 128>), dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(256),
-                       0, a.stream, p);
+    hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeBM, 128, 2, 2, 2>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                       dim3(256), 0, a.stream, p);
     return hipGetLastError();
 }
 

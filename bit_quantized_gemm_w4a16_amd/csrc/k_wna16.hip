@@ -429,7 +429,7 @@ hipError_t launch_skinny(const DenseArgs& a) {
     return hipGetLastError();
 }
 
-template <Fmt F, int BM>
+template <Fmt F>
 hipError_t launch_tile(const DenseArgs& a) {
     TileArgs p{};
     p.A = a.A;
@@ -437,32 +437,29 @@ hipError_t launch_tile(const DenseArgs& a) {
     p.S = a.s;
     p.Z = a.z;
     p.D = a.D;
+    p.part = a.ws;
     p.M = (int)a.M;
+    p.a_rows = (int)a.M;
     p.N = (int)a.N;
     p.K = (int)a.K;
     p.Np = (int)a.Np;
     p.ngroups = (int)(a.K / a.group_size);
     p.gsteps = a.group_size / 128;
-    p.tiles_m = (int)cdiv(a.M, BM);
-    p.tiles_n = (int)cdiv(a.Np, 128);
-    hipLaunchKernelGGL((tile_gemm_kernel<F, BM, 128>), dim3(p.tiles_m * p.tiles_n), dim3(256), 0, a.stream, p);
-    return hipGetLastError();
+    return launch_dense_plan<F>(plan_tile(a.M, a.Np, a.K, has_big_tile(F)), p, a.stream);
 }
 
 template <bool BF16, bool ZP>
 hipError_t launch_all(const DenseArgs& a) {
     if (a.M <= 64) return launch_skinny<BF16, ZP>(a);
-    if constexpr (BF16) return launch_tile<Fmt::WNA16_BF16, 128>(a);
-    const int64_t tiles_n = cdiv(a.Np, 128);
-    if (cdiv(a.M, 256) * tiles_n >= 256) return launch_tile<Fmt::WNA16_F16, 256>(a);
-    return launch_tile<Fmt::WNA16_F16, 128>(a);
+    if constexpr (BF16) return launch_tile<Fmt::WNA16_BF16>(a);
+    return launch_tile<Fmt::WNA16_F16>(a);
 }
 
 }  // namespace
 
-size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size) {
-    if (M > 64) return 0;  // the tiled kernel needs no workspace
+size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size, bool bf16) {
     const int64_t Np = pad16(N);
+    if (M > 64) return tile_workspace(plan_tile(M, Np, K, has_big_tile(bf16 ? Fmt::WNA16_BF16 : Fmt::WNA16_F16)), M, Np);
     SkinnyPlan p = plan_skinny(M, Np, K, group_size);
     if (p.splits <= 1) return 0;
     return (size_t)p.splits * (size_t)M * (size_t)Np * sizeof(float);

@@ -1,13 +1,15 @@
 // LDS-tiled MFMA GEMM template for gfx950, shared by every weight format.
 //
-// One workgroup (4 waves, 2 x 2) computes a BM x BN tile of D.  Each K step
-// covers 128 input features: the A tile (BM rows x 128 K, 16- or 8-bit) and
-// the packed weight tile (BN/16 strips x one K step) are fetched with 16-byte
-// global loads into registers while step s-1 computes, then written to the
-// other half of a double-buffered LDS stage, so the copy of step s+1 overlaps
-// the MFMAs of step s.  A rows are XOR-swizzled in LDS so that the 16 rows a
-// fragment read touches fall in distinct banks.  The packed weight chunk of a
-// strip is, lane for lane, the MFMA B fragment, so it is copied unchanged.
+// One workgroup of WM x WN waves computes a BM x BN tile of D (optionally
+// over one K slice of a split-K launch).  Each K step covers 128 input
+// features: the A tile (BM rows x 128 K, 16- or 8-bit), the packed weight tile
+// (BN/16 strips x one step) and the step's scales are fetched with 16-byte
+// global loads two steps ahead into registers (two register sets), written to
+// one of two LDS stages one step ahead, and consumed from LDS.  So the loads
+// of step s+2 are in flight while step s computes.  A rows are XOR-swizzled in
+// LDS with a row permutation measured to be bank-conflict free on gfx950 for
+// the fragment reads below.  The packed weight chunk of a strip is, lane for
+// lane, the MFMA B fragment, so it is copied unchanged.
 //
 // Formats (the decode runs in registers between the LDS read and the MFMA):
 //   WNA16_F16   fp16 A; INT4/UINT4 -> (q - z) * s folded into the fp16 operand
@@ -18,6 +20,8 @@
 //   W8A8_I8     int8 x int8 -> int32 (exact), per-token x per-channel epilogue
 //   MOE_MX      bf16 A x e2m1 B converted to bf16 with the E8M0 scale (exact)
 #pragma once
+
+#include <type_traits>
 
 #include "hq_device.hpp"
 
@@ -40,10 +44,12 @@ struct TileArgs {
     const void* S;          // packed scales (expert 0)
     const void* Z;          // packed zero-points (WNA16 + UINT4)
     void* D;                // output, row-major [rows][N]
+    void* part;             // split-K partial tiles [splits][M][Np] (fp32 / int32), or null
     int64_t w_estride, s_estride;  // bytes between experts' packed W / scales
     int M, N, K, Np;
+    int a_rows;             // rows of A (bounds the buffer loads; A bytes < 2^32)
     int ngroups, gsteps;    // WNA16: K / G and G / 128
-    int tiles_m, tiles_n;
+    int tiles_m, tiles_n, splits;
     int raw_i32;            // W8A8: store int32 accumulators
     // MoE (tiles_m is an upper bound; the real count is *ntiles)
     const int* tile_info;   // per m-tile: expert, first sorted row, row count
@@ -52,8 +58,9 @@ struct TileArgs {
     int top_k;
 };
 
+// A-tile swizzle: the 16-byte unit u of row r is stored at u ^ swz(r).
 __device__ __forceinline__ int swz(int row, int units) {
-    return units == 16 ? (row & 15) : ((row >> 1) & 7);
+    return units == 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((row >> 1) & 7);
 }
 
 // fp16 (q - z) * s for eight codes of one pair-ordered word.
@@ -92,12 +99,13 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     return __uint_as_float(e == 0 ? 0x00400000u : e == 255u ? 0x7FC00000u : (e << 23));
 }
 
-template <Fmt F, int BM, int BN>
-__global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
+template <Fmt F, int BM, int BN, int WM, int WN, int PD>
+__global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) {
     using T = FmtTraits<F>;
     using Acc = typename T::Acc;
     constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
     constexpr bool MX = F == Fmt::W4A8_MX || F == Fmt::MOE_MX;
+    constexpr int NTH = 64 * WM * WN;
     constexpr int AB = T::AB, BK = 128;
     constexpr int AROW = BK * AB, AUNITS = AROW / 16;
     constexpr int A_STAGE = BM * AROW;
@@ -107,25 +115,26 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
     // MXFP4 one E8M0 byte per lane per strip; INT8 none (per-channel, epilogue)
     constexpr int SC_Z = NSTRIP * 32;                     // zero-point words start (WNA16)
     constexpr int SC_STAGE = WNA16 ? NSTRIP * 48 : MX ? NSTRIP * 64 : 0;
-    constexpr int SC_UNITS = SC_STAGE / 16;              // 16-byte units (WNA16: 2 scale + 1 zero per strip)
+    constexpr int SC_UNITS = SC_STAGE / 16;
     constexpr int STAGE = A_STAGE + B_STAGE + SC_STAGE;
-    constexpr int NIA = A_STAGE / 4096;  // 16-byte loads per lane per stage (A)
-    constexpr int NIB = B_STAGE / 4096;  // (B)
-    constexpr int MT = BM / 32, NT = BN / 32;  // 16x16 tiles per wave (2 x 2 waves)
-    static_assert(A_STAGE % 4096 == 0 && B_STAGE % 4096 == 0, "stage must split evenly over 4 waves");
-    static_assert(SC_UNITS <= 256, "one scale unit per thread at most");
+    constexpr int NIA = A_STAGE / 16 / NTH;  // 16-byte loads per thread per step (A)
+    constexpr int NIB = B_STAGE / 16 / NTH;  // (B)
+    constexpr int MT = BM / WM / 16, NT = BN / WN / 16;  // 16x16 tiles per wave
+    static_assert(A_STAGE % (16 * NTH) == 0 && B_STAGE % (16 * NTH) == 0, "stage must split evenly over threads");
+    static_assert(SC_UNITS <= NTH, "one scale unit per thread at most");
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
     __shared__ int rowinfo[2 * BM];  // [0,BM): A row per local row; [BM,2BM): D row (-1 = none)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int col = lane & 15, quad = lane >> 4;
 
-    // ---- tile coordinates: XCD-aware remap, then grouped raster along M ----
-    int bid = blockIdx.x;
-    const int nb = gridDim.x;
-    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    // ---- tile coordinates: K slice, XCD-aware remap, grouped raster along M ----
+    const int ntile = p.tiles_m * p.tiles_n;
+    int bid = blockIdx.x % ntile;
+    const int split = blockIdx.x / ntile;
+    if ((ntile & 7) == 0) bid = (bid & 7) * (ntile >> 3) + (bid >> 3);
     constexpr int GROUP_M = 4;
     const int tiles_n = p.tiles_n;
     const int group_size = GROUP_M * tiles_n;
@@ -143,7 +152,7 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
         mrows = p.tile_info[3 * pid_m + 2];
         Wbase += (int64_t)e * p.w_estride;
         Sbase += (int64_t)e * p.s_estride;
-        for (int r = tid; r < BM; r += 256) {
+        for (int r = tid; r < BM; r += NTH) {
             const int rr = r < mrows ? r : mrows - 1;
             const int pos = first + rr;
             const int pair = p.sorted ? p.sorted[pos] : pos;
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
         }
     } else {
         mrows = min(BM, p.M - m0);
-        for (int r = tid; r < BM; r += 256) {
+        for (int r = tid; r < BM; r += NTH) {
             rowinfo[r] = m0 + (r < mrows ? r : mrows - 1);
             rowinfo[BM + r] = r < mrows ? m0 + r : -1;
         }
@@ -160,70 +169,79 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
     __syncthreads();
 
     const int K = p.K, nsteps = K / BK;
+    const int k0 = (int)((int64_t)split * nsteps / p.splits), k1 = (int)((int64_t)(split + 1) * nsteps / p.splits);
     const int strip0 = pid_n * NSTRIP, nstrips_total = p.Np / 16;
     auto clamp_strip = [&](int s) { return s < nstrips_total ? s : nstrips_total - 1; };
 
-    // per-lane source offsets of the staged loads (fixed across K steps)
+    // buffer resources (base + size; wave-uniform K-step offsets go in SGPRs)
+    const uint32_t nstr = (uint32_t)(p.Np / 16);
+    const rsrc_t rA = make_rsrc(p.A, (uint32_t)p.a_rows * (uint32_t)K * AB);
+    const rsrc_t rW = make_rsrc(Wbase, nstr * (uint32_t)nsteps * T::BSTRIP);
+    const rsrc_t rS = make_rsrc(Sbase, WNA16 ? nstr * (uint32_t)p.ngroups * 32u : MX ? nstr * (uint32_t)nsteps * 64u : 0u);
+    const rsrc_t rZ = make_rsrc(p.Z, WNA16 && p.Z ? nstr * (uint32_t)p.ngroups * 8u : 0u);
+
+    // per-thread byte offsets of the staged loads (fixed across K steps)
     uint32_t aoff[NIA];
 #pragma unroll
     for (int i = 0; i < NIA; ++i) {
-        const int s = (wave * NIA + i) * 64 + lane;
+        const int s = i * NTH + tid;
         const int row = s / AUNITS, pos = s % AUNITS;
         const int unit = pos ^ swz(row, AUNITS);
-        aoff[i] = (uint32_t)((int64_t)rowinfo[row] * K * AB + unit * 16);
+        aoff[i] = (uint32_t)rowinfo[row] * (uint32_t)(K * AB) + unit * 16;
     }
-    const char* Abase = (const char*)p.A;
-    int64_t boff[NIB];
+    uint32_t boff[NIB];
 #pragma unroll
     for (int i = 0; i < NIB; ++i) {
-        const int s = (wave * NIB + i) * 64 + lane;
+        const int s = i * NTH + tid;
         constexpr int UPS = T::BSTRIP / 16;
         const int strip = clamp_strip(strip0 + s / UPS);
-        boff[i] = ((int64_t)strip * nsteps) * T::BSTRIP + (s % UPS) * 16;
+        boff[i] = (uint32_t)strip * (uint32_t)nsteps * T::BSTRIP + (s % UPS) * 16;
     }
-    // scale unit of this thread (tid < SC_UNITS): strip and part
-    const int sc_strip = clamp_strip(strip0 + (WNA16 ? (tid < 2 * NSTRIP ? tid / 2 : tid - 2 * NSTRIP) : tid / 4));
+    const uint32_t sc_strip = (uint32_t)clamp_strip(strip0 + (WNA16 ? (tid < 2 * NSTRIP ? tid / 2 : tid - 2 * NSTRIP) : tid / 4));
+    const uint32_t soff = WNA16 ? (tid < 2 * NSTRIP ? sc_strip * p.ngroups * 32u + (tid & 1) * 16u : sc_strip * p.ngroups * 8u)
+                                : sc_strip * (uint32_t)nsteps * 64u + (tid & 3) * 16u;
 
-    // global -> registers (issued early, in flight during the MFMAs) ...
-    v4u ra[NIA], rb[NIB], rs;
-    auto gload = [&](int ks) {
-        const char* ga = Abase + (int64_t)ks * AROW;
+    // PD register sets: the loads of step s+PD fly while step s computes
+    static_assert(PD == 1 || PD == 2, "prefetch depth is one or two steps");
+    v4u ra[PD][NIA], rb[PD][NIB], rs[PD];
+    auto gload = [&](int ks, auto setc) {
+        constexpr int st = decltype(setc)::value % PD;
 #pragma unroll
-        for (int i = 0; i < NIA; ++i) ra[i] = *(const v4u*)(ga + aoff[i]);
-        const char* gb = Wbase + (int64_t)ks * T::BSTRIP;
+        for (int i = 0; i < NIA; ++i) ra[st][i] = buf16(rA, aoff[i], (uint32_t)ks * AROW);
 #pragma unroll
-        for (int i = 0; i < NIB; ++i) rb[i] = __builtin_nontemporal_load((const v4u*)(gb + boff[i]));
+        for (int i = 0; i < NIB; ++i) rb[st][i] = buf16<true>(rW, boff[i], (uint32_t)ks * T::BSTRIP);
         if constexpr (WNA16) {
-            const int g = ks / p.gsteps;
+            const uint32_t g = (uint32_t)(ks / p.gsteps);
             if (tid < 2 * NSTRIP) {
-                rs = *(const v4u*)(Sbase + (((int64_t)sc_strip * p.ngroups + g) * 16 + (tid & 1) * 8) * 2);
+                rs[st] = buf16(rS, soff, g * 32u);
             } else if (tid < 3 * NSTRIP) {
-                rs = v4u{0x88888888u, 0x88888888u, 0u, 0u};
+                rs[st] = v4u{0x88888888u, 0x88888888u, 0u, 0u};
                 if (p.Z) {
-                    const uint32_t* zp = (const uint32_t*)p.Z + ((int64_t)sc_strip * p.ngroups + g) * 2;
-                    rs[0] = zp[0];
-                    rs[1] = zp[1];
+                    const uint64_t z = buf8(rZ, soff, g * 8u);
+                    rs[st][0] = (uint32_t)z;
+                    rs[st][1] = (uint32_t)(z >> 32);
                 }
             }
         } else if constexpr (MX) {
-            if (tid < SC_UNITS) rs = *(const v4u*)(Sbase + ((int64_t)sc_strip * nsteps + ks) * 64 + (tid & 3) * 16);
+            if (tid < SC_UNITS) rs[st] = buf16(rS, soff, (uint32_t)ks * 64u);
         }
     };
-    // ... registers -> LDS stage (slot s of this lane: wave-major, 64 lanes per 1 KB)
-    auto swrite = [&](int stage) {
+    auto swrite = [&](int stage, auto setc) {
+        constexpr int st = decltype(setc)::value % PD;
         char* sA = smem + stage * STAGE;
         char* sB = sA + A_STAGE;
 #pragma unroll
-        for (int i = 0; i < NIA; ++i) *(v4u*)(sA + ((wave * NIA + i) * 64 + lane) * 16) = ra[i];
+        for (int i = 0; i < NIA; ++i) *(v4u*)(sA + (i * NTH + tid) * 16) = ra[st][i];
 #pragma unroll
-        for (int i = 0; i < NIB; ++i) *(v4u*)(sB + ((wave * NIB + i) * 64 + lane) * 16) = rb[i];
+        for (int i = 0; i < NIB; ++i) *(v4u*)(sB + (i * NTH + tid) * 16) = rb[st][i];
         if constexpr (SC_STAGE > 0) {
             char* sS = sB + B_STAGE;
             if constexpr (WNA16) {
-                if (tid < 2 * NSTRIP) *(v4u*)(sS + tid * 16) = rs;
-                else if (tid < 3 * NSTRIP) *(uint64_t*)(sS + SC_Z + (tid - 2 * NSTRIP) * 8) = ((uint64_t)rs[1] << 32) | rs[0];
+                if (tid < 2 * NSTRIP) *(v4u*)(sS + tid * 16) = rs[st];
+                else if (tid < 3 * NSTRIP)
+                    *(uint64_t*)(sS + SC_Z + (tid - 2 * NSTRIP) * 8) = ((uint64_t)rs[st][1] << 32) | rs[st][0];
             } else {
-                if (tid < SC_UNITS) *(v4u*)(sS + tid * 16) = rs;
+                if (tid < SC_UNITS) *(v4u*)(sS + tid * 16) = rs[st];
             }
         }
     };
@@ -234,17 +252,10 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
-    gload(0);
-    swrite(0);
-    __syncthreads();
-
-    for (int ks = 0; ks < nsteps; ++ks) {
-        const int stage = ks & 1;
-        if (ks + 1 < nsteps) gload(ks + 1);
+    auto compute = [&](int stage) {
         const char* sA = smem + stage * STAGE;
         const char* sB = sA + A_STAGE;
         const char* sS = sB + B_STAGE;
-
         // this wave's packed weight words: one 16-byte read per strip (per 64-K half for INT8)
         v4u bw[NT][T::BSTRIP / 1024];
 #pragma unroll
@@ -275,12 +286,14 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
                 }
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
-                    const int row = wm * (BM / 2) + i * 16 + col;
+                    const int row = wm * (BM / WM) + i * 16 + col;
                     Frag8 a;
                     a.u = *(const v4u*)(sA + row * AROW + (((4 * quad + t) ^ swz(row, AUNITS)) * 16));
 #pragma unroll
                     for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<false>(a, b[j], acc[i][j]);
                 }
+                // keep one K sub-step's fragments live at a time (register budget of 8-wave tiles)
+                if constexpr (MT > 4) __builtin_amdgcn_sched_barrier(0);
             }
         } else if constexpr (F == Fmt::WNA16_BF16) {
             float sc[NT], zc[NT];
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
                 }
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
-                    const int row = wm * (BM / 2) + i * 16 + col;
+                    const int row = wm * (BM / WM) + i * 16 + col;
                     Frag8 a;
                     a.u = *(const v4u*)(sA + row * AROW + (((4 * quad + t) ^ swz(row, AUNITS)) * 16));
                     rsum[i] = mfma16<true>(a, ones, rsum[i]);
@@ -329,7 +342,7 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
             for (int j = 0; j < NT; ++j) bsc[j] = (int)((const uint8_t*)sS)[(wn * NT + j) * 64 + lane];
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
-                const int row = wm * (BM / 2) + i * 16 + col;
+                const int row = wm * (BM / WM) + i * 16 + col;
                 const int sw = swz(row, AUNITS);
                 const v4u lo = *(const v4u*)(sA + row * AROW + ((quad ^ sw) * 16));
                 const v4u hi = *(const v4u*)(sA + row * AROW + (((4 + quad) ^ sw) * 16));
@@ -345,7 +358,7 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
-                    const int row = wm * (BM / 2) + i * 16 + col;
+                    const int row = wm * (BM / WM) + i * 16 + col;
                     const v4u a = *(const v4u*)(sA + row * AROW + (((4 * h + quad) ^ swz(row, AUNITS)) * 16));
 #pragma unroll
                     for (int j = 0; j < NT; ++j)
@@ -362,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
                 for (int j = 0; j < NT; ++j) b[j] = fp4_to_bf16(bw[j][0][t], sf[j]);
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
-                    const int row = wm * (BM / 2) + i * 16 + col;
+                    const int row = wm * (BM / WM) + i * 16 + col;
                     Frag8 a;
                     a.u = *(const v4u*)(sA + row * AROW + (((4 * quad + t) ^ swz(row, AUNITS)) * 16));
 #pragma unroll
@@ -370,24 +383,54 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
                 }
             }
         }
-        // stage s+1 was last read in step s-1 (before the previous barrier)
-        if (ks + 1 < nsteps) swrite(stage ^ 1);
+    };
+
+    // ---- pipeline: LDS holds steps s and s+1; registers hold s+1 .. s+PD ----
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    if (k0 < k1) {
+        gload(k0, S0{});
+        if constexpr (PD == 2)
+            if (k0 + 1 < k1) gload(k0 + 1, S1{});
+        swrite(0, S0{});
+        __syncthreads();
+    }
+    for (int ks = k0; ks < k1; ks += 2) {
+        // step ks from stage 0
+        if (ks + PD < k1) gload(ks + PD, S0{});
+        compute(0);
+        if (ks + 1 < k1) swrite(1, S1{});
+        __syncthreads();
+        if (ks + 1 >= k1) break;
+        // step ks+1 from stage 1
+        if (ks + 1 + PD < k1) gload(ks + 1 + PD, S1{});
+        compute(1);
+        if (ks + 2 < k1) swrite(0, S0{});
         __syncthreads();
     }
 
     // ---- epilogue: lane (col, quad) holds rows 4*quad + r of column col in each 16x16 tile ----
+    const bool partial = p.splits > 1;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int lrow = wm * (BM / 2) + i * 16 + quad * 4 + r;
+            const int lrow = wm * (BM / WM) + i * 16 + quad * 4 + r;
             const int drow = rowinfo[BM + lrow];
             if (drow < 0) continue;
             float as = 1.f;
-            if constexpr (F == Fmt::W4A8_MX || F == Fmt::W8A8_I8) as = p.a_scale[rowinfo[lrow]];
+            if constexpr (F == Fmt::W4A8_MX || F == Fmt::W8A8_I8)
+                if (!partial) as = p.a_scale[rowinfo[lrow]];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const int n = (pid_n * NSTRIP + wn * NT + j) * 16 + col;
+                if (partial) {
+                    if (n >= p.Np) continue;
+                    const int64_t po = ((int64_t)split * p.M + drow) * p.Np + n;
+                    if constexpr (F == Fmt::W8A8_I8) ((int*)p.part)[po] = acc[i][j][r];
+                    else ((float*)p.part)[po] = acc[i][j][r];
+                    continue;
+                }
                 if (n >= p.N) continue;
                 const int64_t o = (int64_t)drow * p.N + n;
                 if constexpr (F == Fmt::WNA16_F16) {
@@ -402,6 +445,88 @@ __global__ __launch_bounds__(256, 1) void tile_gemm_kernel(TileArgs p) {
                 }
             }
         }
+}
+
+// Split-K finalize for the tiled kernel: sums the partial tiles in slice order
+// and applies the format's epilogue (dense formats only).
+template <Fmt F>
+__global__ __launch_bounds__(256) void tile_finalize_kernel(TileArgs p) {
+    const int64_t total = (int64_t)p.M * p.N;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int m = (int)(e / p.N), n = (int)(e % p.N);
+        const int64_t base = (int64_t)m * p.Np + n, stride = (int64_t)p.M * p.Np;
+        if constexpr (F == Fmt::W8A8_I8) {
+            int v = 0;
+            for (int s = 0; s < p.splits; ++s) v += ((const int*)p.part)[base + s * stride];
+            if (p.raw_i32) ((int*)p.D)[e] = v;
+            else ((uint16_t*)p.D)[e] = f32_to_bf16_bits((float)v * p.a_scale[m] * ((const float*)p.S)[n]);
+        } else {
+            float v = 0.f;
+            for (int s = 0; s < p.splits; ++s) v += ((const float*)p.part)[base + s * stride];
+            if constexpr (F == Fmt::WNA16_F16) ((uint16_t*)p.D)[e] = f32_to_16<false>(v);
+            else if constexpr (F == Fmt::W4A8_MX) ((uint16_t*)p.D)[e] = f32_to_bf16_bits(v * p.a_scale[m]);
+            else ((uint16_t*)p.D)[e] = f32_to_bf16_bits(v);
+        }
+    }
+}
+
+}  // namespace hq
+
+namespace hq {
+
+// ---- host-side plan shared by the dense launchers ----
+struct TilePlan {
+    int BM, splits;
+};
+
+// Large grids use 256 x 128 tiles on 8 waves; smaller ones 128 x 128 tiles on
+// 4 waves with K split across workgroups until the grid covers the chip.
+inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256) {
+    const int64_t tn = (Np + 127) / 128, nsteps = K / 128;
+    TilePlan pl{128, 1};
+    if (allow256 && ((M + 255) / 256) * tn >= 256) {
+        pl.BM = 256;
+        return pl;
+    }
+    const int64_t tiles = ((M + 127) / 128) * tn;
+    int64_t s = (256 + tiles - 1) / tiles;
+    if (s > 8) s = 8;
+    if (s > nsteps / 2) s = nsteps / 2;
+    pl.splits = (int)(s < 1 ? 1 : s);
+    return pl;
+}
+
+inline size_t tile_workspace(const TilePlan& pl, int64_t M, int64_t Np) {
+    return pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)Np * 4 : 0;
+}
+
+template <Fmt F, int BM, int BN, int WM, int WN, int PD>
+hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
+    p.tiles_m = (int)((p.M + BM - 1) / BM);
+    p.tiles_n = (int)((p.Np + BN - 1) / BN);
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.splits;
+    hipLaunchKernelGGL((tile_gemm_kernel<F, BM, BN, WM, WN, PD>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    int64_t blocks = ((int64_t)p.M * p.N + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL((tile_finalize_kernel<F>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+// Formats with a 256 x 128 variant on 8 waves that fits the 256-register
+// budget of two waves per SIMD without spilling (the 16-bit-A formats do not:
+// their dequantised fragments and 64 KB A stage need more).
+constexpr bool has_big_tile(Fmt F) { return F == Fmt::W4A8_MX || F == Fmt::W8A8_I8; }
+
+template <Fmt F>
+hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
+    p.splits = pl.splits;
+    if (pl.BM == 256) {
+        if constexpr (F == Fmt::W4A8_MX) return launch_tile_kernel<F, 256, 128, 2, 4, 1>(p, st);
+        if constexpr (F == Fmt::W8A8_I8) return launch_tile_kernel<F, 256, 128, 2, 4, 2>(p, st);
+    }
+    return launch_tile_kernel<F, 128, 128, 2, 2, 2>(p, st);
 }
 
 }  // namespace hq

@@ -7,7 +7,7 @@ import torch
 import oracle
 import synthetic as syn
 from bit_quantized_gemm_w4a16_amd import hq
-from gpu_util import GATE, dev, empty, gate_error, note, sample_rows, to_f64
+from gpu_util import GATE, dev, empty, gate_error, note, sample_rows, to_f64, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,8 @@ def run_w4a8(M, N, K, seed=0, data=None, rows=None):
     desc = hq.desc_w4a8_mxfp4(N, K)
     wp, sp, _ = hq.hq_repack(desc, d["q"], d["e"])
     D = empty(M * N * 2)
-    hq.hq_gemm(desc, M, dev(qa), dev(s_a), dev(wp), dev(sp), None, D)
+    ws, nb = workspace(desc, M)
+    hq.hq_gemm(desc, M, dev(qa), dev(s_a), dev(wp), dev(sp), None, D, ws, nb)
     torch.cuda.synchronize()
     Dh = to_f64(D[: M * N * 2].cpu().numpy().view(np.uint16).reshape(M, N), torch.bfloat16)
     r = sample_rows(M) if rows is None else rows
@@ -84,7 +85,8 @@ def run_w8a8(M, N, K, seed=0, raw=False, rows=None, data=None):
     desc = hq.desc_w8a8(N, K, raw_int32=raw)
     wp, sp, _ = hq.hq_repack(desc, d["w"], d["s_w"])
     D = empty(M * N * (4 if raw else 2))
-    hq.hq_gemm(desc, M, dev(d["a"]), dev(d["s_a"]), dev(wp), dev(sp), None, D)
+    ws, nb = workspace(desc, M)
+    hq.hq_gemm(desc, M, dev(d["a"]), dev(d["s_a"]), dev(wp), dev(sp), None, D, ws, nb)
     torch.cuda.synchronize()
     r = sample_rows(M) if rows is None else rows
     acc, O = oracle.gemm_w8a8(d["a"], d["s_a"], d["w"], d["s_w"], rows=r)
@@ -99,6 +101,17 @@ def run_w8a8(M, N, K, seed=0, raw=False, rows=None, data=None):
 def test_w8a8_raw_int32_bit_exact_small(M):
     got, acc = run_w8a8(M, 304, 640, seed=M, raw=True)
     np.testing.assert_array_equal(got.astype(np.int64), acc)
+
+
+def test_w8a8_split_k_needs_workspace():
+    """Shapes whose grid is split along K (partials summed by a finalize pass)
+    report a workspace; without it the call is rejected, not run."""
+    desc = hq.desc_w8a8(304, 640, raw_int32=True)
+    assert hq.hq_workspace_bytes(desc, 130) > 0
+    D = empty(130 * 304 * 4)
+    a, sa, w, s = empty(130 * 640), empty(130 * 4), empty(304 * 640), empty(304 * 4)
+    with pytest.raises(hq.HQError):
+        hq.hq_gemm(desc, 130, a, sa, w, s, None, D)
 
 
 @pytest.mark.parametrize("M", [1, 33, 200])
