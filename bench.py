@@ -295,17 +295,29 @@ def _capture(fn):
     return g
 
 
-def run(work, steps, warmup):
+class _Eager:
+    """Stand-in for a captured graph: replay() issues the calls directly (for
+    counter-collection runs, which need plain dispatches)."""
+
+    def __init__(self, fn):
+        self.fn = fn
+
+    def replay(self):
+        self.fn()
+
+
+def run(work, steps, warmup, eager=False):
     """Per-M timing from graphs of back-to-back calls (each on its own cold weight copy),
     and the step timing from graphs of whole sweeps (rotating copies)."""
     sweep = work.sweep
     ncopy = len(work.copies)
     per = {}
+    capture = _Eager if eager else _capture
     for M in sweep:
         def calls(M=M):
             for r in range(ncopy):
                 work.call(M, r)
-        g = _capture(calls)
+        g = capture(calls)
         g.replay()
         torch.cuda.synchronize()
         reps = 3
@@ -324,7 +336,7 @@ def run(work, steps, warmup):
         def sweep_calls(j=j):
             for i, M in enumerate(sweep):
                 work.call(M, (j * len(sweep) + i) % ncopy)
-        graphs.append(_capture(sweep_calls))
+        graphs.append(capture(sweep_calls))
     for w in range(warmup):
         graphs[w % nsw].replay()
     torch.cuda.synchronize()
@@ -334,6 +346,45 @@ def run(work, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, per
+
+
+KERNEL_SOURCES = ["tile_gemm.hpp", "k_wna16.hip", "k_dense.hip", "k_moe.hip", "hq_device.hpp"]
+
+
+def kernel_source_hash():
+    """Hash of the kernel sources; counter figures taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_quantized_gemm_w4a16_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload, M):
+    """HBM bytes per launch from the committed counter runs (profiles/traffic.json):
+    FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by the factor the same counter
+    gives on a plain device copy of known size.  None when absent or stale."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(workload)
+    if not rec or rec.get("M") != M or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_probe(nbytes, reps):
+    """A plain device-to-device copy of nbytes (read nbytes, write nbytes), reps times:
+    the reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def report(work, args, wall, per):
@@ -354,17 +405,23 @@ def report(work, args, wall, per):
         k["t"] += t
         k["n"] += 1
         k["bounds"][bound] = k["bounds"].get(bound, 0.0) + t
+    # Roofline of the dominant kernel, taken at the sweep's largest M, where one
+    # call is one launch of it: achieved = algorithmic flops (or bytes) of that
+    # launch / its average duration over back-to-back launches (HIP events on
+    # the launching stream).
     dom = max(kern, key=lambda n: kern[n]["t"])
-    k = kern[dom]
-    bound = max(k["bounds"], key=k["bounds"].get)
+    Mr = max(M for M in work.sweep if work.kernel_of(M)[0] == dom)
+    name, bound = work.kernel_of(Mr)
+    t, F, B = per[Mr], work.flops(Mr), work.bytes(Mr)
     if bound == "mfma":
-        roof = dict(bound="mfma", achieved=round(k["F"] / k["t"] / 1e12, 1), peak=peak / 1e12,
-                    unit="TFLOP/s" if work.dtype != "int8" else "TOP/s", frac=round(k["F"] / k["t"] / peak, 4))
+        roof = dict(bound="mfma", achieved=round(F / t / 1e12, 1), peak=peak / 1e12,
+                    unit="TFLOP/s" if work.dtype != "int8" else "TOP/s", frac=round(F / t / peak, 4))
     else:
-        roof = dict(bound="hbm", achieved=round(k["B"] / k["t"] / 1e9, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
-                    frac=round(k["B"] / k["t"] / PEAK_HBM, 4))
-    roof.update(traffic=None, kernel=dom, launches_per_step=k["n"], avg_us=round(k["t"] / k["n"] * 1e6, 2),
-                per_unit="flops 2*M*N*K per launch" if bound == "mfma" else "algorithmic bytes per launch")
+        roof = dict(bound="hbm", achieved=round(B / t / 1e9, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
+                    frac=round(B / t / PEAK_HBM, 4))
+    roof.update(traffic=_traffic(work.name, Mr), kernel=dom, M=Mr, avg_us=round(t * 1e6, 2),
+                algorithmic_flops=F, algorithmic_bytes=B,
+                per_unit="2*M*N*K flops per launch" if bound == "mfma" else "algorithmic bytes per launch")
     cpu = None if args.no_cpu_baseline else work.cpu_baseline()
     return {
         "metric": METRIC,
@@ -395,12 +452,19 @@ def main():
     ap.add_argument("--config", default="c2", help="c1|c2|c3|c4|c5|all (default c2)")
     ap.add_argument("--sweep", default=None, help="comma-separated M values (default 1..8192 powers of 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="issue calls directly instead of replaying HIP graphs "
+                    "(for counter-collection runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
     names = list(WORKLOADS) if args.config == "all" else [args.config]
     for nm in names:
         if nm not in WORKLOADS:
@@ -411,7 +475,7 @@ def main():
             if hasattr(work, "active"):
                 flat = work.host["ids"]
                 work.active = {T: len(np.unique(flat[:T])) for T in work.sweep}
-        wall, per = run(work, args.steps, args.warmup)
+        wall, per = run(work, args.steps, args.warmup, eager=args.eager)
         print(json.dumps(report(work, args, wall, per)), flush=True)
         del work
         torch.cuda.empty_cache()
