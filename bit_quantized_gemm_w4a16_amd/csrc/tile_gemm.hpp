@@ -121,9 +121,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     constexpr int NIB = B_STAGE / 16 / NTH;  // (B)
     constexpr int MT = BM / WM / 16, NT = BN / WN / 16;  // 16x16 tiles per wave
     static_assert(A_STAGE % (16 * NTH) == 0 && B_STAGE % (16 * NTH) == 0, "stage must split evenly over threads");
-    static_assert(SC_UNITS <= NTH, "one scale unit per thread at most");
+    static_assert(SC_UNITS <= 64, "scale units are fetched by wave 0");
+    static_assert(NTH >= 128, "zero-point words are fetched by wave 1");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    // Two LDS stages as distinct objects: the compiler can then tell a direct
+    // global->LDS load into one stage from fragment reads of the other and does
+    // not make the reads wait for the load.
+    __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
     __shared__ int rowinfo[2 * BM];  // [0,BM): A row per local row; [BM,2BM): D row (-1 = none)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -198,14 +203,46 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         boff[i] = (uint32_t)strip * (uint32_t)nsteps * T::BSTRIP + (s % UPS) * 16;
     }
     const uint32_t sc_strip = (uint32_t)clamp_strip(strip0 + (WNA16 ? (tid < 2 * NSTRIP ? tid / 2 : tid - 2 * NSTRIP) : tid / 4));
+    const uint32_t zoff = (uint32_t)clamp_strip(strip0 + ((tid - 64) >> 1)) * (uint32_t)p.ngroups * 8u + (tid & 1) * 4u;
     const uint32_t soff = WNA16 ? (tid < 2 * NSTRIP ? sc_strip * p.ngroups * 32u + (tid & 1) * 16u : sc_strip * p.ngroups * 8u)
                                 : sc_strip * (uint32_t)nsteps * 64u + (tid & 3) * 16u;
 
-    // PD register sets: the loads of step s+PD fly while step s computes
-    static_assert(PD == 1 || PD == 2, "prefetch depth is one or two steps");
-    v4u ra[PD][NIA], rb[PD][NIB], rs[PD];
+    auto stage_ptr = [&](auto stc) -> char* {
+        if constexpr (decltype(stc)::value == 0) return stage0;
+        else return stage1;
+    };
+
+    // PD = 0: loads go straight from HBM into the next LDS stage (no staging
+    // registers).  PD = 1, 2: register sets; the loads of step s+PD fly while
+    // step s computes.
+    static_assert(PD >= 0 && PD <= 2, "prefetch depth is zero (direct to LDS), one or two steps");
+    constexpr int NSET = PD > 0 ? PD : 1;
+    v4u ra[NSET][PD > 0 ? NIA : 1], rb[NSET][PD > 0 ? NIB : 1], rs[NSET];
+    auto dma = [&](int ks, auto stc) {
+        char* sA = stage_ptr(stc);
+        char* sB = sA + A_STAGE;
+        char* sS = sB + B_STAGE;
+        const int wbase = (tid & ~63) * 16;  // this wave's first 16-byte slot
+#pragma unroll
+        for (int i = 0; i < NIA; ++i)
+            dma16(rA, sA + i * NTH * 16 + wbase, aoff[i], (uint32_t)ks * AROW);
+#pragma unroll
+        for (int i = 0; i < NIB; ++i)
+            dma16_nt(rW, sB + i * NTH * 16 + wbase, boff[i], (uint32_t)ks * T::BSTRIP);
+        if constexpr (WNA16) {
+            const uint32_t g = (uint32_t)(ks / p.gsteps);
+            if (tid < 2 * NSTRIP) {
+                dma16(rS, sS, soff, g * 32u);
+            } else if (p.Z && tid >= 64 && tid < 64 + 2 * NSTRIP) {
+                // zero-point words: lane 2j + h of wave 1 fetches word h of strip j
+                dma4(rZ, sS + SC_Z, zoff, g * 8u);
+            }
+        } else if constexpr (MX) {
+            if (tid < SC_UNITS) dma16(rS, sS, soff, (uint32_t)ks * 64u);
+        }
+    };
     auto gload = [&](int ks, auto setc) {
-        constexpr int st = decltype(setc)::value % PD;
+        constexpr int st = decltype(setc)::value % NSET;
 #pragma unroll
         for (int i = 0; i < NIA; ++i) ra[st][i] = buf16(rA, aoff[i], (uint32_t)ks * AROW);
 #pragma unroll
@@ -226,9 +263,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
             if (tid < SC_UNITS) rs[st] = buf16(rS, soff, (uint32_t)ks * 64u);
         }
     };
-    auto swrite = [&](int stage, auto setc) {
-        constexpr int st = decltype(setc)::value % PD;
-        char* sA = smem + stage * STAGE;
+    auto swrite = [&](auto stc, auto setc) {
+        constexpr int st = decltype(setc)::value % NSET;
+        char* sA = stage_ptr(stc);
         char* sB = sA + A_STAGE;
 #pragma unroll
         for (int i = 0; i < NIA; ++i) *(v4u*)(sA + (i * NTH + tid) * 16) = ra[st][i];
@@ -252,8 +289,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
-    auto compute = [&](int stage) {
-        const char* sA = smem + stage * STAGE;
+    const uint32_t wx = p.Z ? 0u : 0x88888888u;  // symmetric INT4: two's complement -> offset binary
+    auto compute = [&](auto stc) {
+        const char* sA = stage_ptr(stc);
         const char* sB = sA + A_STAGE;
         const char* sS = sB + B_STAGE;
         // this wave's packed weight words: one 16-byte read per strip (per 64-K half for INT8)
@@ -270,7 +308,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
             for (int j = 0; j < NT; ++j) {
                 const int sl = wn * NT + j;
                 const uint32_t sc = ((const uint16_t*)sS)[sl * 16 + col];
-                const uint32_t z = (((const uint32_t*)(sS + SC_Z))[sl * 2 + (col >> 3)] >> (4 * (col & 7))) & 15u;
+                const uint32_t z = p.Z ? (((const uint32_t*)(sS + SC_Z))[sl * 2 + (col >> 3)] >> (4 * (col & 7))) & 15u : 8u;
                 s2[j] = sc | (sc << 16);
                 const uint32_t nbz = 0xE400u | z;
                 nb2[j] = nbz | (nbz << 16);
@@ -281,7 +319,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     uint32_t w = bw[j][0][t];
-                    if (!p.Z) w ^= 0x88888888u;
+                    w ^= wx;
                     b[j] = deq4_f16_scaled(w, nb2[j], s2[j]);
                 }
 #pragma unroll
@@ -301,7 +339,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
             for (int j = 0; j < NT; ++j) {
                 const int sl = wn * NT + j;
                 sc[j] = bits16_to_f32<true>(((const uint16_t*)sS)[sl * 16 + col]);
-                const uint32_t z = (((const uint32_t*)(sS + SC_Z))[sl * 2 + (col >> 3)] >> (4 * (col & 7))) & 15u;
+                const uint32_t z = p.Z ? (((const uint32_t*)(sS + SC_Z))[sl * 2 + (col >> 3)] >> (4 * (col & 7))) & 15u : 8u;
                 zc[j] = (float)(128u + z);
             }
             v4f st[MT][NT], rsum[MT];
@@ -319,7 +357,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     uint32_t w = bw[j][0][t];
-                    if (!p.Z) w ^= 0x88888888u;
+                    w ^= wx;
                     b[j] = deq4_bf16_offset(w);
                 }
 #pragma unroll
@@ -385,28 +423,50 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         }
     };
 
-    // ---- pipeline: LDS holds steps s and s+1; registers hold s+1 .. s+PD ----
+    // ---- pipeline: LDS holds steps s and s+1; registers (PD > 0) hold s+1 .. s+PD ----
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    if (k0 < k1) {
-        gload(k0, S0{});
-        if constexpr (PD == 2)
-            if (k0 + 1 < k1) gload(k0 + 1, S1{});
-        swrite(0, S0{});
-        __syncthreads();
-    }
-    for (int ks = k0; ks < k1; ks += 2) {
-        // step ks from stage 0
-        if (ks + PD < k1) gload(ks + PD, S0{});
-        compute(0);
-        if (ks + 1 < k1) swrite(1, S1{});
-        __syncthreads();
-        if (ks + 1 >= k1) break;
-        // step ks+1 from stage 1
-        if (ks + 1 + PD < k1) gload(ks + 1 + PD, S1{});
-        compute(1);
-        if (ks + 2 < k1) swrite(0, S0{});
-        __syncthreads();
+    if constexpr (PD == 0) {
+        if (k0 < k1) {
+            dma(k0, S0{});
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        // whole pairs of steps (one loop exit keeps the accumulators in place),
+        // then an odd last step; step ks is always in stage 0 at the loop top
+        int ks = k0;
+        for (; ks + 1 < k1; ks += 2) {
+            dma(ks + 1, S1{});
+            compute(S0{});
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (ks + 2 < k1) dma(ks + 2, S0{});
+            compute(S1{});
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        if (ks < k1) compute(S0{});
+    } else {
+        if (k0 < k1) {
+            gload(k0, S0{});
+            if constexpr (PD == 2)
+                if (k0 + 1 < k1) gload(k0 + 1, S1{});
+            swrite(S0{}, S0{});
+            __syncthreads();
+        }
+        for (int ks = k0; ks < k1; ks += 2) {
+            // step ks from stage 0
+            if (ks + PD < k1) gload(ks + PD, S0{});
+            compute(S0{});
+            if (ks + 1 < k1) swrite(S1{}, S1{});
+            __syncthreads();
+            if (ks + 1 >= k1) break;
+            // step ks+1 from stage 1
+            if (ks + 1 + PD < k1) gload(ks + 1 + PD, S1{});
+            compute(S1{});
+            if (ks + 2 < k1) swrite(S0{}, S0{});
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: lane (col, quad) holds rows 4*quad + r of column col in each 16x16 tile ----
@@ -514,17 +574,20 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Formats with a 256 x 128 variant on 8 waves that fits the 256-register
-// budget of two waves per SIMD without spilling (the 16-bit-A formats do not:
-// their dequantised fragments and 64 KB A stage need more).
-constexpr bool has_big_tile(Fmt F) { return F == Fmt::W4A8_MX || F == Fmt::W8A8_I8; }
+// Formats with a 256 x 128 tile.  4-bit formats: 4 waves of 128 x 64 each,
+// loads straight into LDS (no staging registers), one wave per SIMD, so each
+// dequantised weight fragment feeds 8 MFMAs.  INT8 (no dequant) runs faster
+// on 8 waves of 128 x 32 with two register-staged steps in flight.  bf16 A
+// has no 256-row variant (its row-sum MFMA needs a second accumulator set).
+constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16; }
 
 template <Fmt F>
 hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
     p.splits = pl.splits;
-    if (pl.BM == 256) {
-        if constexpr (F == Fmt::W4A8_MX) return launch_tile_kernel<F, 256, 128, 2, 4, 1>(p, st);
-        if constexpr (F == Fmt::W8A8_I8) return launch_tile_kernel<F, 256, 128, 2, 4, 2>(p, st);
+    if constexpr (F == Fmt::W8A8_I8) {
+        if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 2>(p, st);
+    } else if constexpr (has_big_tile(F)) {
+        if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 2, 0>(p, st);
     }
     return launch_tile_kernel<F, 128, 128, 2, 2, 2>(p, st);
 }
