@@ -99,7 +99,24 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     return __uint_as_float(e == 0 ? 0x00400000u : e == 255u ? 0x7FC00000u : (e << 23));
 }
 
-template <Fmt F, int BM, int BN, int WM, int WN, int PD>
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the direct-to-LDS pipelines.  Their only LDS writes are
+// the direct loads, whose completion each wave has already waited for with an
+// explicit vmcnt; __syncthreads() would add a release fence, which makes the
+// compiler wait for every load in flight (vmcnt(0)) and so drain the prefetch.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <Fmt F, int BM, int BN, int WM, int WN, int PD, int NSTAGE = 2>
 __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) {
     using T = FmtTraits<F>;
     using Acc = typename T::Acc;
@@ -127,8 +144,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     // Two LDS stages as distinct objects: the compiler can then tell a direct
     // global->LDS load into one stage from fragment reads of the other and does
     // not make the reads wait for the load.
+    static_assert(NSTAGE == 2 || (NSTAGE == 3 && PD == 0), "three stages only with direct-to-LDS loads");
     __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
     __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char stage2[NSTAGE == 3 ? STAGE : 16];
     __shared__ int rowinfo[2 * BM];  // [0,BM): A row per local row; [BM,2BM): D row (-1 = none)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -209,7 +228,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 
     auto stage_ptr = [&](auto stc) -> char* {
         if constexpr (decltype(stc)::value == 0) return stage0;
-        else return stage1;
+        else if constexpr (decltype(stc)::value == 1) return stage1;
+        else return stage2;
     };
 
     // PD = 0: loads go straight from HBM into the next LDS stage (no staging
@@ -218,17 +238,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     static_assert(PD >= 0 && PD <= 2, "prefetch depth is zero (direct to LDS), one or two steps");
     constexpr int NSET = PD > 0 ? PD : 1;
     v4u ra[NSET][PD > 0 ? NIA : 1], rb[NSET][PD > 0 ? NIB : 1], rs[NSET];
+    // Direct loads of one step into a stage.  The scale / zero-point loads are
+    // issued first, so after the NIA + NIB unconditional loads of a later step
+    // have been issued, vmcnt(NIA + NIB) means "this step has landed" in every wave.
+    const int wbase = __builtin_amdgcn_readfirstlane((tid & ~63) * 16);  // this wave's first 16-byte slot
     auto dma = [&](int ks, auto stc) {
         char* sA = stage_ptr(stc);
         char* sB = sA + A_STAGE;
         char* sS = sB + B_STAGE;
-        const int wbase = (tid & ~63) * 16;  // this wave's first 16-byte slot
-#pragma unroll
-        for (int i = 0; i < NIA; ++i)
-            dma16(rA, sA + i * NTH * 16 + wbase, aoff[i], (uint32_t)ks * AROW);
-#pragma unroll
-        for (int i = 0; i < NIB; ++i)
-            dma16_nt(rW, sB + i * NTH * 16 + wbase, boff[i], (uint32_t)ks * T::BSTRIP);
         if constexpr (WNA16) {
             const uint32_t g = (uint32_t)(ks / p.gsteps);
             if (tid < 2 * NSTRIP) {
@@ -240,6 +257,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         } else if constexpr (MX) {
             if (tid < SC_UNITS) dma16(rS, sS, soff, (uint32_t)ks * 64u);
         }
+#pragma unroll
+        for (int i = 0; i < NIA; ++i)
+            dma16(rA, sA + i * NTH * 16 + wbase, aoff[i], (uint32_t)ks * AROW);
+#pragma unroll
+        for (int i = 0; i < NIB; ++i)
+            dma16_nt(rW, sB + i * NTH * 16 + wbase, boff[i], (uint32_t)ks * T::BSTRIP);
     };
     auto gload = [&](int ks, auto setc) {
         constexpr int st = decltype(setc)::value % NSET;
@@ -426,11 +449,40 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     // ---- pipeline: LDS holds steps s and s+1; registers (PD > 0) hold s+1 .. s+PD ----
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    if constexpr (PD == 0) {
+    using S2 = std::integral_constant<int, 2>;
+    if constexpr (PD == 0 && NSTAGE == 3) {
+        // three stages: the loads of step q+2 fly while step q computes and q+1 lands
+        constexpr int NDMA = NIA + NIB;
+        if (k0 < k1) dma(k0, S0{});
+        if (k0 + 1 < k1) {
+            dma(k0 + 1, S1{});
+            wait_vmcnt<NDMA>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        lds_barrier();
+        // one step from stage X (holding step q); stage (X + 2) % 3 receives step q + 2
+        auto sub = [&](int q, auto xc) {
+            constexpr int X = decltype(xc)::value;
+            if (q + 2 < k1) dma(q + 2, std::integral_constant<int, (X + 2) % 3>{});
+            compute(xc);
+            if (q + 2 < k1) wait_vmcnt<NDMA>();
+            else wait_vmcnt<0>();
+            lds_barrier();
+        };
+        int ks = k0;
+        for (; ks + 3 <= k1; ks += 3) {
+            sub(ks, S0{});
+            sub(ks + 1, S1{});
+            sub(ks + 2, S2{});
+        }
+        if (ks < k1) sub(ks, S0{});
+        if (ks + 1 < k1) sub(ks + 1, S1{});
+    } else if constexpr (PD == 0) {
         if (k0 < k1) {
             dma(k0, S0{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
+            lds_barrier();
         }
         // whole pairs of steps (one loop exit keeps the accumulators in place),
         // then an odd last step; step ks is always in stage 0 at the loop top
@@ -439,11 +491,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
             dma(ks + 1, S1{});
             compute(S0{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
+            lds_barrier();
             if (ks + 2 < k1) dma(ks + 2, S0{});
             compute(S1{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
+            lds_barrier();
         }
         if (ks < k1) compute(S0{});
     } else {
@@ -560,12 +612,12 @@ inline size_t tile_workspace(const TilePlan& pl, int64_t M, int64_t Np) {
     return pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)Np * 4 : 0;
 }
 
-template <Fmt F, int BM, int BN, int WM, int WN, int PD>
+template <Fmt F, int BM, int BN, int WM, int WN, int PD, int NSTAGE = 2>
 hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.Np + BN - 1) / BN);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.splits;
-    hipLaunchKernelGGL((tile_gemm_kernel<F, BM, BN, WM, WN, PD>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, p);
+    hipLaunchKernelGGL((tile_gemm_kernel<F, BM, BN, WM, WN, PD, NSTAGE>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     int64_t blocks = ((int64_t)p.M * p.N + 255) / 256;
