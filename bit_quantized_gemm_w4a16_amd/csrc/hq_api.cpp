@@ -92,7 +92,7 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         if (d->w_scale_dtype != HQ_DT_FP32 || d->w_scale_gran != HQ_GRAN_PER_CHANNEL)
             return set_error(HQ_ERR_UNSUPPORTED, "W8A8 needs fp32 per-channel weight scales");
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "W8A8 takes no zero-points");
-        if (d->K % 64) return set_error(HQ_ERR_UNSUPPORTED, "W8A8 needs K %% 64 == 0 (K=%lld)", (long long)d->K);
+        if (d->K % 128) return set_error(HQ_ERR_UNSUPPORTED, "W8A8 needs K %% 128 == 0 (K=%lld)", (long long)d->K);
         if (d->out_dtype != HQ_DT_BF16 && d->out_dtype != HQ_DT_INT32)
             return set_error(HQ_ERR_UNSUPPORTED, "W8A8 outputs bf16 or raw int32");
         I.out_i32 = d->out_dtype == HQ_DT_INT32;
@@ -311,7 +311,7 @@ hq_status hq_moe_align(int64_t T, int32_t top_k, int32_t num_experts, const int3
         return set_error(HQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (!aligned16(workspace)) return set_error(HQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
     return hip_status(moe_align_launch(T, top_k, num_experts, topk_ids, expert_offsets, sorted_pairs, workspace,
-                                       nullptr, nullptr, (hipStream_t)stream),
+                                       (hipStream_t)stream),
                       "hq_moe_align");
 }
 

@@ -94,6 +94,15 @@ __device__ __forceinline__ uint64_t buf8(rsrc_t r, uint32_t voff, uint32_t soff)
     return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
+// Direct global -> LDS loads through a flat pointer (16 or 4 bytes per lane):
+// lane l writes lds_wave_base + l * size; the base must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(const void* g, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+}
+
 // 16-byte global loads: a non-temporal hint for data read exactly once.
 __device__ __forceinline__ v4u ld_nt(const v4u* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ v4u ld16(const void* p) { return *(const v4u*)p; }

@@ -12,7 +12,7 @@
 // fp32, or the raw int32 accumulators.
 #include "hq_device.hpp"
 #include "hq_internal.h"
-#include "tile_gemm.hpp"
+#include "skinny.hpp"
 
 namespace hq {
 
@@ -20,6 +20,24 @@ namespace {
 
 template <Fmt F>
 hipError_t launch(const DenseArgs& a, int raw_i32) {
+    if (a.M <= kSkinnyMaxM) {
+        SkinnyArgs s{};
+        s.A = a.A;
+        s.a_scale = a.a_scale;
+        s.W = a.w;
+        s.S = a.s;
+        s.D = a.D;
+        s.part = a.ws;
+        s.M = (int)a.M;
+        s.K = (int)a.K;
+        s.N = (int)a.N;
+        s.Np = (int)a.Np;
+        s.nc = (int)(a.K / 128);
+        s.ngroups = 1;
+        s.gchunks = 1;
+        s.raw_i32 = raw_i32;
+        return launch_skinny_dense<F>(plan_skinny(F, a.M, a.Np, a.K, 128), s, a.stream);
+    }
     TileArgs p{};
     p.A = a.A;
     p.a_scale = a.a_scale;
@@ -42,6 +60,11 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
 
 size_t w8bit_workspace(int64_t M, int64_t N, int64_t K) {
     const int64_t Np = pad16(N);
+    if (M <= kSkinnyMaxM) {  // the larger of the two formats' split plans
+        const size_t a = skinny_workspace(plan_skinny(Fmt::W4A8_MX, M, Np, K, 128), M, Np);
+        const size_t b = skinny_workspace(plan_skinny(Fmt::W8A8_I8, M, Np, K, 128), M, Np);
+        return a > b ? a : b;
+    }
     return tile_workspace(plan_tile(M, Np, K, true), M, Np);  // both 8-bit-A formats have the 256-row tile
 }
 

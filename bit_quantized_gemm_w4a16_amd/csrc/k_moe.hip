@@ -14,12 +14,20 @@
 // m-tile list, then the scatter.
 #include "hq_device.hpp"
 #include "hq_internal.h"
-#include "tile_gemm.hpp"
+#include "skinny.hpp"
 
 namespace hq {
 
 constexpr int kMoeChunk = 256;  // pairs per histogram chunk
-constexpr int kMoeBM = 128;     // rows per m-tile of the expert GEMM
+constexpr int kMoeBM = 128;     // rows per m-tile of the tiled expert GEMM
+// Experts are served in three tiers by their row count: up to kMoeSmallRows
+// rows on the weight-streaming kernel (one m-tile, its A rows in LDS for all
+// of K), up to kMoeMidMax rows on the tiled kernel with kMoeMidBM-row tiles,
+// and the rest on kMoeBM-row tiles, so no expert pads its rows more than ~2x.
+constexpr int kMoeSmallRows = 4;
+constexpr int kMoeSmallGridY = 32;  // workgroups per strip walking the tier-0 m-tiles
+constexpr int kMoeMidBM = 32;
+constexpr int kMoeMidMax = 64;
 
 // ---- 1. per-chunk histogram + rank of each pair among equal ids before it ----
 // hist is expert-major: hist[e * C + c].
@@ -78,20 +86,31 @@ __device__ int block_excl_scan_1024(int v, int* tmp) {
     return incl - v;
 }
 
-// ---- 2b. expert offsets and the m-tile list (one workgroup) ----
+// ---- 2b. expert offsets and the m-tile lists (one workgroup) ----
 // Counts come from `counts` (Indexed) or from the caller's offsets (Grouped).
 // Caller-given offsets are clamped to [0, P] so malformed input can never
-// address rows outside A or D; at most max_tiles tiles are written.
+// address rows outside A or D.  An expert with c rows goes to the first tier
+// with c <= upto: the tier's list gets ceil(c / bm) m-tiles of at most bm rows
+// (at most max_tiles entries per list).
+struct TileList {
+    int* tiles;   // per tile: expert, first sorted row, row count (null: no list)
+    int* ntiles;  // number of valid tiles
+    int max_tiles, bm, upto;
+};
+constexpr int kMoeTiers = 3;
+struct MoeTiers {
+    TileList t[kMoeTiers];
+};
+
 __global__ __launch_bounds__(1024) void moe_offsets_kernel(const int* __restrict__ counts, const int* __restrict__ given_off,
-                                                           int E, int P, int max_tiles, int* __restrict__ offsets,
-                                                           int* __restrict__ tiles, int* __restrict__ ntiles, int BM) {
+                                                           int E, int P, int* __restrict__ offsets, MoeTiers tiers) {
     __shared__ int tmp[1024];
-    __shared__ int carry[2];
+    __shared__ int carry[1 + kMoeTiers];
     const int t = threadIdx.x;
-    if (t == 0) carry[0] = carry[1] = 0;
+    if (t <= kMoeTiers) carry[t] = 0;
     __syncthreads();
     for (int e0 = 0; e0 < E; e0 += 4096) {  // 4 experts per thread per round
-        int cnt[4], sum = 0, ntl[4], tsum = 0;
+        int cnt[4], tier[4], ntl[4], sum = 0, tsum[kMoeTiers] = {0, 0, 0};
         for (int k = 0; k < 4; ++k) {
             const int e = e0 + 4 * t + k;
             int c = 0;
@@ -104,37 +123,51 @@ __global__ __launch_bounds__(1024) void moe_offsets_kernel(const int* __restrict
                 }
             }
             cnt[k] = c;
-            ntl[k] = (cnt[k] + BM - 1) / BM;
-            sum += cnt[k];
-            tsum += ntl[k];
+            int q = 0;
+            while (q < kMoeTiers - 1 && c > tiers.t[q].upto) ++q;
+            tier[k] = q;
+            ntl[k] = (c + tiers.t[q].bm - 1) / tiers.t[q].bm;
+            sum += c;
+#pragma unroll
+            for (int i = 0; i < kMoeTiers; ++i) tsum[i] += i == q ? ntl[k] : 0;
         }
-        const int c0 = carry[0], c1 = carry[1];
-        int run = c0 + block_excl_scan_1024(sum, tmp);
-        int trun = c1 + block_excl_scan_1024(tsum, tmp);
+        int run = carry[0] + block_excl_scan_1024(sum, tmp);
+        int trun[kMoeTiers];
+#pragma unroll
+        for (int i = 0; i < kMoeTiers; ++i) trun[i] = carry[1 + i] + block_excl_scan_1024(tsum[i], tmp);
         for (int k = 0; k < 4; ++k) {
             const int e = e0 + 4 * t + k;
             if (e < E) {
                 const int start = counts ? run : min(max(given_off[e], 0), P);
                 if (offsets) offsets[e] = start;
-                for (int q = 0; tiles && q < ntl[k] && trun + q < max_tiles; ++q) {
-                    tiles[3 * (trun + q)] = e;
-                    tiles[3 * (trun + q) + 1] = start + q * BM;
-                    tiles[3 * (trun + q) + 2] = min(BM, cnt[k] - q * BM);
+#pragma unroll
+                for (int i = 0; i < kMoeTiers; ++i) {
+                    const TileList& L = tiers.t[i];
+                    if (i != tier[k] || !L.tiles) continue;
+                    for (int q = 0; q < ntl[k] && trun[i] + q < L.max_tiles; ++q) {
+                        L.tiles[3 * (trun[i] + q)] = e;
+                        L.tiles[3 * (trun[i] + q) + 1] = start + q * L.bm;
+                        L.tiles[3 * (trun[i] + q) + 2] = min(L.bm, cnt[k] - q * L.bm);
+                    }
                 }
             }
             run += cnt[k];
-            trun += ntl[k];
+#pragma unroll
+            for (int i = 0; i < kMoeTiers; ++i) trun[i] += i == tier[k] ? ntl[k] : 0;
         }
         __syncthreads();
         if (t == 1023) {
             carry[0] = run;
-            carry[1] = trun;
+#pragma unroll
+            for (int i = 0; i < kMoeTiers; ++i) carry[1 + i] = trun[i];
         }
         __syncthreads();
     }
     if (t == 0) {
         if (offsets) offsets[E] = carry[0];
-        if (ntiles) *ntiles = min(carry[1], max_tiles);
+#pragma unroll
+        for (int i = 0; i < kMoeTiers; ++i)
+            if (tiers.t[i].ntiles) *tiers.t[i].ntiles = min(carry[1 + i], tiers.t[i].max_tiles);
     }
 }
 
@@ -169,10 +202,21 @@ namespace {
 size_t al16(size_t b) { return (b + 15) / 16 * 16; }
 }  // namespace
 
+// Upper bounds of the tier lists (the real lengths are known only on the device).
+static int64_t moe_max_tiles(int tier, int64_t P, int E) {
+    const int64_t ex = E < P ? E : P;  // experts that can hold a row
+    if (tier == 0) return ex;          // one m-tile of kMoeSmallRows per small expert
+    if (tier == 1) {                   // at most kMoeMidMax / kMoeMidBM tiles per mid expert
+        const int64_t a = cdiv(kMoeMidMax, kMoeMidBM) * ex, b = cdiv(P, kMoeMidBM) + ex;
+        return a < b ? a : b;
+    }
+    const int64_t big = P / (kMoeMidMax + 1);
+    return cdiv(P, kMoeBM) + (E < big ? E : big);
+}
+
 MoeLayout moe_layout(int64_t T, int top_k, int E, bool indexed) {
     MoeLayout L{};
     const int64_t P = T * top_k;
-    const int64_t max_tiles = cdiv(P, kMoeBM) + (E < P ? E : P);
     size_t o = 0;
     L.hist = o;  // hist + lrank + counts (the align scratch)
     o += indexed ? moe_align_workspace(T, top_k, E) : 0;
@@ -180,12 +224,14 @@ MoeLayout moe_layout(int64_t T, int top_k, int E, bool indexed) {
     o += indexed ? al16((size_t)(E + 1) * 4) : 0;
     L.sorted = o;
     o += indexed ? al16((size_t)P * 4) : 0;
-    L.tiles = o;
-    o += al16((size_t)(max_tiles > 0 ? max_tiles : 1) * 12);
-    L.ntiles = o;
+    for (int i = 0; i < 3; ++i) {
+        L.max_tier[i] = moe_max_tiles(i, P, E);
+        L.tiles_tier[i] = o;
+        o += al16((size_t)(L.max_tier[i] > 0 ? L.max_tier[i] : 1) * 12);
+    }
+    L.ntiles = o;  // one count per tier
     o += 16;
     L.bytes = o;
-    L.max_tiles = max_tiles;
     return L;
 }
 
@@ -195,16 +241,17 @@ size_t moe_align_workspace(int64_t T, int top_k, int E) {
 }
 
 hipError_t moe_align_launch(int64_t T, int top_k, int E, const int* ids, int* offsets, int* sorted, void* ws,
-                            int* tiles, int* ntiles, hipStream_t st) {
+                            hipStream_t st) {
     const int P = (int)(T * top_k), C = (int)cdiv(P, kMoeChunk);
     int* hist = (int*)ws;
     int* lrank = (int*)((char*)ws + al16((size_t)C * E * 4));
     int* counts = (int*)((char*)lrank + al16((size_t)P * 4));
     hipLaunchKernelGGL(moe_hist_kernel, dim3(C), dim3(256), (size_t)(E + kMoeChunk) * 4, st, ids, P, E, C, hist, lrank);
     hipLaunchKernelGGL(moe_colscan_kernel, dim3(E), dim3(64), 0, st, hist, C, counts);
-    const int max_tiles = (int)(cdiv(P, kMoeBM) + (E < P ? E : P));
+    MoeTiers none{};
+    for (int i = 0; i < kMoeTiers; ++i) none.t[i] = TileList{nullptr, nullptr, 0, 1, 0};
     hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, st, (const int*)counts, (const int*)nullptr, E, P,
-                       max_tiles, offsets, tiles, ntiles, kMoeBM);
+                       offsets, none);
     hipLaunchKernelGGL(moe_place_kernel, dim3(C), dim3(256), 0, st, ids, P, E, C, (const int*)hist,
                        (const int*)offsets, (const int*)lrank, sorted);
     return hipGetLastError();
@@ -221,26 +268,80 @@ hipError_t moe_gather_launch(const void* A, const int* sorted, int64_t P, int to
     return hipGetLastError();
 }
 
+// Experts with few rows (the common case below a few thousand tokens) run on
+// the weight-streaming kernel in m-tiles of kMoeSmallRows rows: their
+// weights are read once per m-tile without padding the tile to 128 rows.
+// Experts with more rows run on the tiled MFMA kernel.
 hipError_t moe_gemm_launch(const MoeArgs& a) {
     const int64_t P = a.T * a.top_k;
     MoeLayout L = moe_layout(a.T, a.top_k, a.E, a.indexed);
     char* ws = (char*)a.ws;
-    int* tiles = (int*)(ws + L.tiles);
     int* ntiles = (int*)(ws + L.ntiles);
+    int* tl[3];
+    for (int i = 0; i < 3; ++i) tl[i] = (int*)(ws + L.tiles_tier[i]);
     const int* sorted = nullptr;
+    const int* given = nullptr;
     hipError_t e;
     if (a.indexed) {
         int* offsets = (int*)(ws + L.offsets);
         int* srt = (int*)(ws + L.sorted);
-        e = moe_align_launch(a.T, a.top_k, a.E, a.topk_ids, offsets, srt, ws + L.hist, tiles, ntiles, a.stream);
+        e = moe_align_launch(a.T, a.top_k, a.E, a.topk_ids, offsets, srt, ws + L.hist, a.stream);
         if (e != hipSuccess) return e;
         sorted = srt;
+        given = offsets;  // the tile lists are built from the offsets just computed
     } else {
-        hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, (const int*)nullptr,
-                           a.expert_offsets, a.E, (int)P, (int)L.max_tiles, (int*)nullptr, tiles, ntiles, kMoeBM);
+        given = a.expert_offsets;
+    }
+    // The weight-streaming path holds a tile's A rows for all of K in LDS and a
+    // wave's quarter of K in registers; a larger K sends its experts to the mid tier.
+    const int nc = (int)(a.K / 128);
+    const int s_off = (int)(cdiv((int64_t)kMoeSmallRows * nc * 256, 1024) * 1024);
+    const int lds = s_off + (int)(cdiv((int64_t)nc * 64, 1024) * 1024);
+    const bool small_ok = cdiv(nc, 4) <= 16 && lds <= kSkinnyLds;
+    {
+        MoeTiers tiers{};
+        tiers.t[0] = TileList{tl[0], ntiles + 0, (int)L.max_tier[0], kMoeSmallRows, small_ok ? kMoeSmallRows : 0};
+        tiers.t[1] = TileList{tl[1], ntiles + 1, (int)L.max_tier[1], kMoeMidBM, kMoeMidMax};
+        tiers.t[2] = TileList{tl[2], ntiles + 2, (int)L.max_tier[2], kMoeBM, 1 << 30};
+        hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, (const int*)nullptr, given, a.E, (int)P,
+                           (int*)nullptr, tiers);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // tier 0 (at most kMoeSmallRows rows): weight-streaming kernel, persistent over its m-tiles
+    if (small_ok) {
+        SkinnyArgs s{};
+        s.A = a.A;
+        s.W = a.w;
+        s.S = a.s;
+        s.D = a.D;
+        s.w_estride = a.w_estride;
+        s.s_estride = a.s_estride;
+        s.M = (int)P;
+        s.K = (int)a.K;
+        s.N = (int)a.N;
+        s.Np = (int)a.Np;
+        s.nc = nc;
+        s.ngroups = 1;
+        s.gchunks = 1;
+        s.splits = 1;
+        s.cps = nc;
+        s.cpk = (int)cdiv(nc, 4);
+        s.NS = 1;
+        s.WS = 1;
+        s.a_off = 0;
+        s.s_off = s_off;
+        s.z_off = s_off;
+        s.tile_info = tl[0];
+        s.ntiles = ntiles + 0;
+        s.sorted = sorted;
+        s.top_k = a.top_k;
+        const int64_t gy = L.max_tier[0] < kMoeSmallGridY ? L.max_tier[0] : kMoeSmallGridY;
+        const dim3 grid((unsigned)(a.Np / 16), (unsigned)(gy > 0 ? gy : 1));
+        e = launch_skinny_cpw<Fmt::MOE_MX, 1, 1>(s.cpk <= 2 ? 2 : s.cpk <= 4 ? 4 : s.cpk <= 8 ? 8 : 16, grid, lds, s, a.stream);
+        if (e != hipSuccess) return e;
+    }
+    // tiers 1 and 2: tiled MFMA kernel over m-tiles of kMoeMidBM / kMoeBM rows
     TileArgs p{};
     p.A = a.A;
     p.W = a.w;
@@ -255,16 +356,28 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     p.gsteps = 1;
     p.w_estride = a.w_estride;
     p.s_estride = a.s_estride;
-    p.tiles_m = (int)L.max_tiles;
     p.tiles_n = (int)cdiv(a.Np, 128);
     p.splits = 1;
-    p.tile_info = tiles;
-    p.ntiles = ntiles;
     p.sorted = sorted;
     p.top_k = a.top_k;
-    hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeBM, 128, 2, 2, 2>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
-                       dim3(256), 0, a.stream, p);
-    return hipGetLastError();
+    p.tiles_m = (int)L.max_tier[1];
+    p.tile_info = tl[1];
+    p.ntiles = ntiles + 1;
+    if (p.tiles_m > 0) {
+        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeMidBM, 128, 2, 2, 2>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                           dim3(256), 0, a.stream, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    p.tiles_m = (int)L.max_tier[2];
+    p.tile_info = tl[2];
+    p.ntiles = ntiles + 2;
+    if (p.tiles_m > 0) {
+        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeBM, 128, 2, 2, 2>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                           dim3(256), 0, a.stream, p);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 }  // namespace hq

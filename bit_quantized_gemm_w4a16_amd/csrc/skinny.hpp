@@ -1,0 +1,607 @@
+// Small-M schedule for every weight format on gfx950: a GEMV-like stream of
+// the packed weights.
+//
+// The pages give the idea, not the code: at small batch the GEMM is bound by
+// the weight traffic, so the kernel must keep the memory system busy and split
+// the K dimension over the machine when the output alone gives too few
+// workgroups ("Humming wird angekuendigt", section "Tuning und JIT-Kompilierung
+// fuer jeden Workload", and the Stream-K option for small shapes in section
+// "Gemeinsam genutzte CUDA-Komponenten").  The schedule below is our own for
+// CDNA4.
+//
+// Workgroup = 4 waves over NS strips (16 output columns each) and one K slice
+// of 128-K chunks (one m-tile of an expert for MoE).  The waves split the
+// workgroup as WS strip-columns x WK K-parts; each wave owns SPW strips.
+//   1. The A rows of the slice and the slice's scales (group scales +
+//      zero-points, or E8M0 exponents) go to LDS with direct-to-LDS loads.
+//   2. Every wave issues all of its packed-weight loads (16 bytes per lane =
+//      one MFMA B fragment per load) in chunk order, so the whole weight
+//      stream of the chip is in flight at once.
+//   3. One wait for the LDS copies (they were issued first and memory
+//      returns in order), one barrier, then each chunk is decoded and fed to
+//      the MFMA as soon as its own load has landed.
+//   4. The K-parts of the workgroup reduce through LDS; K slices of a split
+//      launch write fp32 / int32 partial tiles that a finalize pass sums in
+//      slice order.  (A last-arriving-slice reduction inside the kernel needs a
+//      device-scope release of the partials, which writes back the L2 and was
+//      measured to cost far more than the extra launch.)
+//
+// Per format (one 128-K chunk of one strip):
+//   WNA16_F16/BF16  4 x v_mfma_f32_16x16x32_{f16,bf16}; the operand is the
+//                   exact integer (q - z) (fp16) or 128 + u with a row-sum
+//                   MFMA for the offset (bf16); the group scale multiplies the
+//                   fp32 partial of the chunk
+//   W4A8_MX         1 x v_mfma_scale_f32_16x16x128_f8f6f4 (fp8 A, fp4 B with
+//                   the E8M0 exponent as the B scale)
+//   W8A8_I8         2 x v_mfma_i32_16x16x64_i8 (exact int32)
+//   MOE_MX          4 x v_mfma_f32_16x16x32_bf16 after the exact
+//                   e2m1 x 2^(E-127) -> bf16 conversion
+#pragma once
+
+#include "tile_gemm.hpp"
+
+namespace hq {
+
+constexpr int kSkinnyLds = 150 * 1024;
+constexpr int64_t kSkinnyMaxM = 64;  // dense M handled by this schedule
+
+struct SkinnyArgs {
+    const void* A;          // activations [a_rows][K]
+    const float* a_scale;   // per-token fp32 (W4A8 / W8A8), by A row
+    const void* W;          // packed weights (expert 0 for MoE)
+    const void* S;          // packed group scales / E8M0 / per-channel fp32
+    const void* Z;          // packed zero-points (WNA16 with UINT4), or null
+    void* D;                // output [rows][N]
+    void* part;             // split-K partial tiles [splits][M][Np], or null
+    int64_t w_estride, s_estride;  // bytes between experts' packed W / scales
+    int M, K, N, Np;
+    int nc;                 // 128-K chunks in K
+    int ngroups, gchunks;   // WNA16: K / G and G / 128
+    int splits;
+    int cps, cpk;           // chunks per K slice, chunks per wave K-part (host-computed)
+    int NS, WS;             // strips per workgroup, wave strip-columns (WK = 4 / WS)
+    int a_off, s_off, z_off;  // LDS layout (bytes)
+    int raw_i32;            // W8A8: store the int32 accumulators
+    // MoE: blockIdx.y walks the m-tile list (expert, first sorted row, rows)
+    const int* tile_info;
+    const int* ntiles;
+    const int* sorted;      // Indexed: sorted pair ids; Grouped: null
+    int top_k;
+};
+
+template <Fmt F>
+struct SkinnyTraits {
+    static constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
+    static constexpr bool MX = F == Fmt::W4A8_MX || F == Fmt::MOE_MX;
+    static constexpr int AB = FmtTraits<F>::AB;        // bytes per activation
+    static constexpr int UPC = 8 * AB;                  // 16-byte A units per 128-K chunk and row
+    static constexpr int NB = FmtTraits<F>::BSTRIP / 1024;  // 16-byte weight loads per chunk and lane
+    static constexpr int MOE_ROWS = 8;                  // rows of a MoE m-tile on this path
+};
+
+// A unit u of LDS row r holds global unit u ^ skinny_swz(r): 16 consecutive
+// rows of a fragment read land in distinct bank groups.
+template <int UPC>
+__device__ __forceinline__ int skinny_swz(int row) {
+    return UPC == 16 ? (row & 15) : (row & 7);
+}
+
+// One work item: K slice `item` of a dense launch, or m-tile `item` of a MoE
+// launch.  Every thread of the workgroup calls it (it holds barriers).
+template <Fmt F, int MT, int SPW, int CPW>
+__device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char* lds, int* rowinfo) {
+    using Tr = SkinnyTraits<F>;
+    using Acc = typename FmtTraits<F>::Acc;
+    constexpr bool WNA16 = Tr::WNA16, MX = Tr::MX, MOE = F == Fmt::MOE_MX;
+    constexpr int AB = Tr::AB, UPC = Tr::UPC, NB = Tr::NB;
+    constexpr int ROWS = 16 * MT;
+    constexpr int NLOAD = SPW * CPW * NB;  // weight loads per wave and batch
+    static_assert(NLOAD < 64, "vmcnt counts at most 63 loads");
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, quad = lane >> 4;
+    const int WS = p.WS, wsh = WS >> 1, WK = 4 >> wsh;  // WS is 1, 2 or 4
+    const int ws = wave & (WS - 1), wk = wave >> wsh;
+    const int nstrips = p.Np / 16;
+    const int strip_base = blockIdx.x * p.NS;
+
+    // ---- m-tile (MoE) or K slice (dense) ----
+    const char* Wb = (const char*)p.W;
+    const char* Sb = (const char*)p.S;
+    int split = 0, rows = p.M, first = 0;
+    if constexpr (MOE) {
+        const int t = item;
+        const int e = p.tile_info[3 * t];
+        first = p.tile_info[3 * t + 1];
+        rows = p.tile_info[3 * t + 2];
+        Wb += (int64_t)e * p.w_estride;
+        Sb += (int64_t)e * p.s_estride;
+    } else {
+        split = item;
+    }
+    // K slice [c0, c1) and this wave's part [cw0, cw1), in 128-K chunks (no division on the device)
+    const int c0 = min(split * p.cps, p.nc), c1 = min(c0 + p.cps, p.nc);
+    const int cw0 = min(c0 + wk * p.cpk, c1), cw1 = min(cw0 + p.cpk, c1);
+    const int nsl = c1 - c0;   // chunks in the slice
+    const int U = nsl * UPC;   // A units per LDS row
+
+    // ---- local rows: A row and D row ----
+    if (tid < ROWS) {
+        const int r = tid, rr = r < rows ? r : rows - 1;
+        int arow = rr, drow = r < rows ? r : -1;
+        if constexpr (MOE) {
+            const int pos = first + rr;
+            const int pair = p.sorted ? p.sorted[pos] : pos;
+            arow = p.sorted ? pair / p.top_k : pos;
+            drow = r < rows ? pair : -1;
+        }
+        rowinfo[r] = arow;
+        rowinfo[ROWS + r] = drow;
+    }
+    __syncthreads();  // no weight load is in flight yet, so this drains nothing
+
+    // ---- 1. A slice and scales -> LDS (direct loads, issued before the weights) ----
+    {
+        const char* Abase = (const char*)p.A + (size_t)c0 * 128 * AB;
+        const int nblk = (U + 63) >> 6;  // 64-unit blocks per row
+        int r = 0, blk = wave;
+        while (r < rows && blk >= nblk) { blk -= nblk; ++r; }
+        while (r < rows) {
+            const int pos = blk * 64 + lane;
+            const char* arow = Abase + (size_t)rowinfo[r] * p.K * AB;
+            if (pos < U) lds_dma16(arow + ((pos ^ skinny_swz<UPC>(r)) * 16), lds + p.a_off + (r * U + blk * 64) * 16);
+            blk += 4;
+            while (r < rows && blk >= nblk) { blk -= nblk; ++r; }
+        }
+        if constexpr (WNA16) {
+            const int sg0 = c0 / p.gchunks, sgslab = (c1 - 1) / p.gchunks - sg0 + 1;
+            for (int j = 0; j < p.NS; ++j) {
+                const int st = strip_base + j < nstrips ? strip_base + j : nstrips - 1;
+                const char* sg = (const char*)Sb + ((size_t)st * p.ngroups + sg0) * 32;
+                const char* zg = (const char*)p.Z + ((size_t)st * p.ngroups + sg0) * 8;
+                for (int pos0 = wave * 64; pos0 < sgslab * 2; pos0 += 256) {
+                    const int pos = pos0 + lane;  // 16-byte scale units / 32-bit zero-point words
+                    if (pos < sgslab * 2) {
+                        lds_dma16(sg + pos * 16, lds + p.s_off + (j * sgslab * 2 + pos0) * 16);
+                        if (p.Z) lds_dma4(zg + pos * 4, lds + p.z_off + (j * sgslab * 2 + pos0) * 4);
+                    }
+                }
+            }
+        } else if constexpr (MX) {
+            for (int j = 0; j < p.NS; ++j) {
+                const int st = strip_base + j < nstrips ? strip_base + j : nstrips - 1;
+                for (int pos0 = wave * 64; pos0 < nsl * 4; pos0 += 256) {  // 64 bytes per chunk
+                    const int pos = pos0 + lane;
+                    if (pos < nsl * 4)
+                        lds_dma16((const char*)Sb + ((size_t)st * p.nc + c0) * 64 + pos * 16, lds + p.s_off + (j * nsl * 4 + pos0) * 16);
+                }
+            }
+        }
+    }
+
+    // ---- 2. the wave's packed weights, chunk-major, all in flight ----
+    // Chunks past the wave's range repeat its last chunk (never used); a wave
+    // with an empty range re-reads the slice's first chunk, so every load
+    // stays inside the strip.
+    const int wlast = cw1 > cw0 ? cw1 - 1 : c0;
+    int wstrip[SPW];
+    const v4u* wsrc[SPW];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        wstrip[sp] = strip_base + ws * SPW + sp;
+        const int st = wstrip[sp] < nstrips ? wstrip[sp] : nstrips - 1;
+        wsrc[sp] = (const v4u*)(Wb + (size_t)st * p.nc * FmtTraits<F>::BSTRIP) + lane;
+    }
+    v4u w[CPW][SPW][NB];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+            for (int h = 0; h < NB; ++h) w[i][sp][h] = ld_nt(wsrc[sp] + ((size_t)min(cw0 + i, wlast) * NB + h) * 64);
+        // keep the issue order = the consumption order, so each chunk waits only for its own loads
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // the LDS copies were issued before these NLOAD loads: once at most NLOAD
+    // loads are outstanding, this wave's copies have landed
+    wait_vmcnt<NLOAD>();
+    lds_barrier();
+
+    // ---- 3. decode + MFMA ----
+    Acc acc[SPW][MT];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[sp][mt] = Acc{0, 0, 0, 0};
+    const char* lA = lds + p.a_off;
+    int arow_l[MT];  // this lane's A row in LDS per m-tile (rows past the tile read its last row)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) arow_l[mt] = min(mt * 16 + col, rows - 1);
+    Frag8 ones;
+    ones.u = v4u{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const bool zsel = p.Z != nullptr;
+    const uint32_t wx = zsel ? 0u : 0x88888888u;  // symmetric INT4: two's complement -> offset binary
+    const uint32_t zmask = zsel ? 15u : 0u, zdef = zsel ? 0u : 8u;  // zero-point, or 8 for symmetric
+
+    // WNA16: group of the current chunk, relative to the slice's first group
+    const int g0 = WNA16 ? c0 / p.gchunks : 0, gslab = WNA16 ? (c1 - 1) / p.gchunks - g0 + 1 : 0;
+    int gcur = WNA16 ? cw0 / p.gchunks - g0 : 0, grem = WNA16 ? cw0 % p.gchunks : 0;
+    {  // the plan keeps a wave's K-part within one register batch (cpk <= CPW)
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            // Every wave runs all CPW chunk bodies without branches (branches let the
+            // compiler merge the bodies and lose the per-load waits); a chunk past the
+            // wave's part reads the slice's last chunk and contributes exactly zero.
+            const int c = cw0 + i;
+            const bool valid = c < cw1;
+            const int cl = min(c, c1 - 1) - c0;
+            if constexpr (WNA16) {
+                constexpr bool BF = F == Fmt::WNA16_BF16;
+                const int g = min(gcur, gslab - 1);
+                Frag8 af[MT][4];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int row = arow_l[mt];
+                    const char* ar = lA + (size_t)row * U * 16;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) af[mt][t].u = *(const v4u*)(ar + (((cl * 16 + 4 * quad + t) ^ skinny_swz<16>(row)) * 16));
+                }
+                v4f rs[MT];
+                if constexpr (BF) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        rs[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) rs[mt] = mfma16<true>(af[mt][t], ones, rs[mt]);
+                    }
+                }
+#pragma unroll
+                for (int sp = 0; sp < SPW; ++sp) {
+                    const int j = ws * SPW + sp;
+                    // LDS reads without branches (a branch here costs the per-load waits):
+                    // the zero-point word is read even without zero-points and then ignored
+                    const float sc0 = bits16_to_f32<BF>(((const uint16_t*)(lds + p.s_off))[(j * gslab + g) * 16 + col]);
+                    const uint32_t zw = ((const uint32_t*)(lds + p.z_off))[(j * gslab + g) * 2 + (col >> 3)];
+                    const float sc = valid ? sc0 : 0.f;
+                    const uint32_t z = ((zw >> (4 * (col & 7))) & zmask) | zdef;
+                    const uint32_t nbz = 0xE400u | z;  // fp16 bits of -(1024 + z)
+                    const uint32_t nbias2 = nbz | (nbz << 16);
+                    v4f gacc[MT];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) gacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t word = w[i][sp][0][t] ^ wx;
+                        Frag8 b;
+                        if constexpr (BF) b = deq4_bf16_offset(word);
+                        else b = deq4_f16_exact(word, nbias2);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) gacc[mt] = mfma16<BF>(af[mt][t], b, gacc[mt]);
+                    }
+                    if constexpr (BF) {
+                        const float zc = (float)(128u + z);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) acc[sp][mt] += sc * (gacc[mt] - zc * rs[mt]);
+                    } else {
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) acc[sp][mt] += sc * gacc[mt];
+                    }
+                }
+            } else if constexpr (F == Fmt::MOE_MX) {
+                Frag8 af[MT][4];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int row = arow_l[mt];
+                    const char* ar = lA + (size_t)row * U * 16;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) af[mt][t].u = *(const v4u*)(ar + (((cl * 16 + 4 * quad + t) ^ skinny_swz<16>(row)) * 16));
+                }
+#pragma unroll
+                for (int sp = 0; sp < SPW; ++sp) {
+                    const int j = ws * SPW + sp;
+                    const float sf0 = e8m0_to_f32(((const uint8_t*)(lds + p.s_off))[(j * nsl + cl) * 64 + lane]);
+                    const float sf = valid ? sf0 : 0.f;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const Frag8 b = fp4_to_bf16(w[i][sp][0][t], sf);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) acc[sp][mt] = mfma16<true>(af[mt][t], b, acc[sp][mt]);
+                    }
+                }
+            } else if constexpr (F == Fmt::W4A8_MX) {
+                v8i af[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int row = arow_l[mt];
+                    const char* ar = lA + (size_t)row * U * 16;
+                    const int sw = skinny_swz<8>(row);
+                    const v4u lo = *(const v4u*)(ar + (((cl * 8 + quad) ^ sw) * 16));
+                    const v4u hi = *(const v4u*)(ar + (((cl * 8 + 4 + quad) ^ sw) * 16));
+                    af[mt] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                }
+#pragma unroll
+                for (int sp = 0; sp < SPW; ++sp) {
+                    const int j = ws * SPW + sp;
+                    const int bsc = (int)((const uint8_t*)(lds + p.s_off))[(j * nsl + cl) * 64 + lane];
+                    const v4u bw = valid ? w[i][sp][0] : v4u{0u, 0u, 0u, 0u};  // e2m1 code 0 is +0
+                    const v8i b = v8i{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3], 0, 0, 0, 0};
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[sp][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], b, acc[sp][mt], 0, 4, 0, 0x7F, 0, bsc);
+                }
+            } else {  // W8A8_I8
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    v4i af[MT];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const int row = arow_l[mt];
+                        const char* ar = lA + (size_t)row * U * 16;
+                        af[mt] = *(const v4i*)(ar + (((cl * 8 + 4 * h + quad) ^ skinny_swz<8>(row)) * 16));
+                    }
+#pragma unroll
+                    for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            acc[sp][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], __builtin_bit_cast(v4i, valid ? w[i][sp][h] : v4u{0u, 0u, 0u, 0u}), acc[sp][mt], 0, 0, 0);
+                }
+            }
+            if constexpr (WNA16) {
+                if (++grem == p.gchunks) {
+                    grem = 0;
+                    ++gcur;
+                }
+            }
+        }
+    }
+
+    // ---- 4. reduce the K-parts of the workgroup through LDS ----
+    if (WK > 1) {
+        __syncthreads();  // every load has landed; the A slice is no longer needed
+        Acc* red = (Acc*)lds;
+        if (wk > 0) {
+#pragma unroll
+            for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) red[((((wk - 1) * WS + ws) * SPW + sp) * MT + mt) * 64 + lane] = acc[sp][mt];
+        }
+        __syncthreads();
+        if (wk == 0)
+            for (int k2 = 1; k2 < WK; ++k2)
+#pragma unroll
+                for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[sp][mt] += red[((((k2 - 1) * WS + ws) * SPW + sp) * MT + mt) * 64 + lane];
+    }
+    // ---- 5. split K: partial tile out (summed in slice order by the finalize pass) ----
+    if (p.splits > 1) {
+        if (wk == 0) {
+#pragma unroll
+            for (int sp = 0; sp < SPW; ++sp) {
+                if (wstrip[sp] >= nstrips) continue;
+                const int n = wstrip[sp] * 16 + col;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = mt * 16 + quad * 4 + r;
+                        if (m >= rows) continue;
+                        const int64_t po = ((int64_t)split * p.M + m) * p.Np + n;
+                        if constexpr (F == Fmt::W8A8_I8) ((int*)p.part)[po] = acc[sp][mt][r];
+                        else ((float*)p.part)[po] = acc[sp][mt][r];
+                    }
+            }
+        }
+        return;
+    }
+
+    // ---- 6. output (K-part 0): lane (col, quad) holds rows mt*16 + 4*quad + r of column col ----
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        const int n = wstrip[sp] * 16 + col;
+        if (wk != 0 || wstrip[sp] >= nstrips) continue;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = mt * 16 + quad * 4 + r;
+                if (m >= ROWS) continue;
+                const int drow = rowinfo[ROWS + m];
+                if (drow < 0) continue;
+                if (n >= p.N) continue;
+                const int64_t o = (int64_t)drow * p.N + n;
+                if constexpr (WNA16) {
+                    ((uint16_t*)p.D)[o] = f32_to_16<F == Fmt::WNA16_BF16>(acc[sp][mt][r]);
+                } else if constexpr (F == Fmt::W8A8_I8) {
+                    if (p.raw_i32) ((int*)p.D)[o] = acc[sp][mt][r];
+                    else ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)acc[sp][mt][r] * p.a_scale[rowinfo[m]] * ((const float*)Sb)[n]);
+                } else if constexpr (F == Fmt::W4A8_MX) {
+                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r] * p.a_scale[rowinfo[m]]);
+                } else {
+                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r]);
+                }
+            }
+    }
+}
+
+template <Fmt F, int MT, int SPW, int CPW>
+__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) char lds[];  // sized per launch (plan.lds_bytes)
+    __shared__ int rowinfo[2 * 16 * MT];  // [0,ROWS): A row of each local row; [ROWS,2ROWS): D row or -1
+    if constexpr (F == Fmt::MOE_MX) {
+        // persistent over the device-built m-tile list (its length is known only here)
+        const int nt = *p.ntiles;
+        for (int t = blockIdx.y; t < nt; t += gridDim.y) {
+            skinny_item<F, MT, SPW, CPW>(p, t, lds, rowinfo);
+            __syncthreads();  // the next tile reuses LDS
+        }
+    } else {
+        skinny_item<F, MT, SPW, CPW>(p, blockIdx.y, lds, rowinfo);
+    }
+}
+
+// ---- host-side plan ----
+
+struct SkinnyPlan {
+    int NS, WS, SPW, splits, MT, CPW;
+    int cps, cpk;   // chunks per slice, per wave K-part
+    int a_off, s_off, z_off;
+    int lds_bytes;  // dynamic LDS of one workgroup
+    int64_t groups_x;
+};
+
+inline int skinny_round_cpw(int64_t per, int spw) {
+    if (spw == 1) return per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
+    return per <= 2 ? 2 : per <= 4 ? 4 : 8;
+}
+
+// Bytes of LDS a slice of `cmax` chunks needs for `rows` A rows and NS strips.
+inline int64_t skinny_lds_need(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) {
+    const int ab = F == Fmt::W4A8_MX || F == Fmt::W8A8_I8 ? 1 : 2;
+    auto al = [](int64_t b) { return (b + 1023) / 1024 * 1024; };
+    const int64_t a = al(rows * cmax * 128 * ab);
+    int64_t s = 0, z = 0;
+    if (F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16) {
+        const int64_t gmax = cmax / gch + 2;
+        s = al(NS * gmax * 32);
+        z = al(NS * gmax * 8);
+    } else if (F == Fmt::W4A8_MX || F == Fmt::MOE_MX) {
+        s = al(NS * cmax * 64);
+    }
+    return a + s + z;
+}
+
+// Dense plan: strips per workgroup grow with M so the A slice is re-read about
+// nstrips / NS times; K slices until the grid covers the chip and the slice
+// fits in LDS.
+inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G) {
+    const int64_t nstrips = Np / 16, nc = K / 128;
+    const int gch = G >= 128 ? G / 128 : 1;
+    SkinnyPlan p{};
+    p.NS = M <= 8 ? 1 : M <= 16 ? 2 : M <= 32 ? 4 : 8;
+    while (p.NS > 1 && p.NS > nstrips) p.NS /= 2;
+    p.SPW = p.NS <= 4 ? 1 : p.NS / 4;
+    p.WS = p.NS / p.SPW;
+    const int WK = 4 / p.WS;
+    p.groups_x = cdiv(nstrips, p.NS);
+    int64_t S = cdiv(256, p.groups_x);
+    const int64_t smax = nc / WK > 0 ? nc / WK : 1;
+    const int nb = F == Fmt::W8A8_I8 ? 2 : 1;
+    const int64_t cap = p.SPW * 16 * nb < 64 ? 16 : 8;  // largest register batch instantiated
+    while (S < smax && (skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap)) ++S;
+    if (S > smax) S = smax;
+    p.splits = (int)(S < 1 ? 1 : S);
+    p.cps = (int)cdiv(nc, p.splits);
+    p.splits = (int)cdiv(nc, p.cps);  // no empty slice
+    p.cpk = (int)cdiv(p.cps, WK);
+    const int64_t cmax = p.cps;
+    const int ab = F == Fmt::W4A8_MX || F == Fmt::W8A8_I8 ? 1 : 2;
+    auto al = [](int64_t b) { return (b + 1023) / 1024 * 1024; };
+    p.a_off = 0;
+    p.s_off = (int)al(M * cmax * 128 * ab);
+    p.z_off = p.s_off + (int)al(p.NS * (cmax / gch + 2) * 32);
+    p.MT = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    p.CPW = skinny_round_cpw(p.cpk, p.SPW);
+    const int64_t need = skinny_lds_need(F, M, cmax, p.NS, gch);
+    const int64_t red = (int64_t)(WK - 1) * p.WS * p.SPW * p.MT * 1024;  // K-part reduction buffer
+    p.lds_bytes = (int)(need > red ? need : red);
+    return p;
+}
+
+// Split-K finalize: D = epilogue(sum over slices, in slice order); one thread
+// per pair of output columns of one row.
+template <Fmt F>
+__global__ __launch_bounds__(256) void skinny_finalize_kernel(SkinnyArgs p) {
+    const int m = blockIdx.y;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 2;
+    if (n >= p.N) return;
+    const int64_t stride = (int64_t)p.M * p.Np;
+    const int64_t base = (int64_t)m * p.Np + n;
+    const int64_t o = (int64_t)m * p.N + n;
+    const bool two = n + 1 < p.N;
+    if constexpr (F == Fmt::W8A8_I8) {
+        int v0 = 0, v1 = 0;
+        for (int s = 0; s < p.splits; ++s) {
+            const int2 v = *(const int2*)((const int*)p.part + base + s * stride);
+            v0 += v.x;
+            v1 += v.y;
+        }
+        if (p.raw_i32) {
+            ((int*)p.D)[o] = v0;
+            if (two) ((int*)p.D)[o + 1] = v1;
+        } else {
+            const float as = p.a_scale[m];
+            ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)v0 * as * ((const float*)p.S)[n]);
+            if (two) ((uint16_t*)p.D)[o + 1] = f32_to_bf16_bits((float)v1 * as * ((const float*)p.S)[n + 1]);
+        }
+    } else {
+        float v0 = 0.f, v1 = 0.f;
+        for (int s = 0; s < p.splits; ++s) {
+            const float2 v = *(const float2*)((const float*)p.part + base + s * stride);
+            v0 += v.x;
+            v1 += v.y;
+        }
+        if constexpr (F == Fmt::W4A8_MX) {
+            v0 *= p.a_scale[m];
+            v1 *= p.a_scale[m];
+        }
+        constexpr bool BF = F != Fmt::WNA16_F16;
+        ((uint16_t*)p.D)[o] = f32_to_16<BF>(v0);
+        if (two) ((uint16_t*)p.D)[o + 1] = f32_to_16<BF>(v1);
+    }
+}
+
+template <Fmt F, int MT, int SPW, int CPW>
+hipError_t launch_skinny_k(dim3 grid, int lds_bytes, const SkinnyArgs& a, hipStream_t st) {
+    // allow dynamic LDS beyond the 64 KB default, once per instantiation
+    static const hipError_t attr = hipFuncSetAttribute((const void*)skinny_kernel<F, MT, SPW, CPW>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLds);
+    if (attr != hipSuccess) return attr;
+    if (lds_bytes < 1024 || lds_bytes > kSkinnyLds) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((skinny_kernel<F, MT, SPW, CPW>), grid, dim3(256), (size_t)lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <Fmt F, int MT, int SPW>
+hipError_t launch_skinny_cpw(int cpw, dim3 grid, int lds_bytes, const SkinnyArgs& a, hipStream_t st) {
+    switch (cpw) {
+        case 2: return launch_skinny_k<F, MT, SPW, 2>(grid, lds_bytes, a, st);
+        case 4: return launch_skinny_k<F, MT, SPW, 4>(grid, lds_bytes, a, st);
+        case 8: return launch_skinny_k<F, MT, SPW, 8>(grid, lds_bytes, a, st);
+        default:
+            if constexpr (SPW * 16 * FmtTraits<F>::BSTRIP / 1024 < 64) return launch_skinny_k<F, MT, SPW, 16>(grid, lds_bytes, a, st);
+            else return launch_skinny_k<F, MT, SPW, 8>(grid, lds_bytes, a, st);
+    }
+}
+
+// Dense launch: skinny kernel, then the finalize pass when K is split.
+// Dense launch: the weight stream, then the finalize pass when K is split.
+template <Fmt F>
+hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t st) {
+    s.splits = pl.splits;
+    s.cps = pl.cps;
+    s.cpk = pl.cpk;
+    s.NS = pl.NS;
+    s.WS = pl.WS;
+    s.a_off = pl.a_off;
+    s.s_off = pl.s_off;
+    s.z_off = pl.z_off;
+    const dim3 grid((unsigned)pl.groups_x, (unsigned)pl.splits);
+    if (pl.cpk > pl.CPW) return hipErrorInvalidValue;  // K-part beyond one register batch (planned out)
+    hipError_t e;
+    if (pl.SPW == 2) e = launch_skinny_cpw<F, 4, 2>(pl.CPW, grid, pl.lds_bytes, s, st);
+    else if (pl.MT == 1) e = launch_skinny_cpw<F, 1, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
+    else if (pl.MT == 2) e = launch_skinny_cpw<F, 2, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
+    else e = launch_skinny_cpw<F, 4, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
+    if (e != hipSuccess || pl.splits == 1) return e;
+    const dim3 fgrid((unsigned)cdiv(cdiv(s.N, 2), 256), (unsigned)s.M);
+    hipLaunchKernelGGL((skinny_finalize_kernel<F>), fgrid, dim3(256), 0, st, s);
+    return hipGetLastError();
+}
+
+// Workspace of a split launch: the partial tiles.
+inline size_t skinny_workspace(const SkinnyPlan& pl, int64_t M, int64_t Np) {
+    return pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)Np * 4 : 0;
+}
+
+}  // namespace hq

@@ -63,19 +63,42 @@ __device__ __forceinline__ int swz(int row, int units) {
     return units == 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((row >> 1) & 7);
 }
 
-// fp16 (q - z) * s for eight codes of one pair-ordered word.
-__device__ __forceinline__ Frag8 deq4_f16_scaled(uint32_t w, uint32_t nbias2, uint32_t s2) {
-    const uint32_t m = 0x000F000Fu, c = 0x64006400u;
-    const v2h nb = __builtin_bit_cast(v2h, nbias2), sc = __builtin_bit_cast(v2h, s2);
+// v_and_or_b32 with every operand in a VGPR (a gfx9 VOP3 instruction takes no
+// literal, and the compiler otherwise splits it into an AND and an OR).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+    return r;
+}
+
+// fp16 (q - z) * s for eight codes of one pair-ordered word.  A nibble in bits
+// 0-3 of a half under exponent 0x6400 reads 1024 + u; a nibble in bits 4-7
+// under 0x5400 reads 64 + u (fp16 has 10 mantissa bits), so one shift serves
+// the upper two pairs.  nb_lo = -(1024 + z), nb_hi = -(64 + z) in both halves;
+// both differences are exact, one rounding comes from the scale.
+__device__ __forceinline__ Frag8 deq4_f16_scaled(uint32_t w, uint32_t nb_lo, uint32_t nb_hi, uint32_t s2) {
+    const uint32_t w8 = w >> 8;
+    const v2h lo = __builtin_bit_cast(v2h, nb_lo), hi = __builtin_bit_cast(v2h, nb_hi), sc = __builtin_bit_cast(v2h, s2);
     Frag8 f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        v2h x = __builtin_bit_cast(v2h, ((w >> (4 * s)) & m) | c) + nb;
-        f.u[s] = __builtin_bit_cast(uint32_t, x * sc);
-    }
+    f.u[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(v2h, and_or(w, 0x000F000Fu, 0x64006400u)) + lo) * sc);
+    f.u[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(v2h, and_or(w, 0x00F000F0u, 0x54005400u)) + hi) * sc);
+    f.u[2] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(v2h, and_or(w8, 0x000F000Fu, 0x64006400u)) + lo) * sc);
+    f.u[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(v2h, and_or(w8, 0x00F000F0u, 0x54005400u)) + hi) * sc);
     return f;
 }
 
+// fp16 u - z for eight codes of one pair-ordered word: (0x6400 | u) is
+// 1024 + u exactly, and one packed add of -(1024 + z) leaves u - z exactly.
+__device__ __forceinline__ Frag8 deq4_f16_exact(uint32_t w, uint32_t nbias2) {
+    const uint32_t m = 0x000F000Fu, c = 0x64006400u;
+    const v2h nb = __builtin_bit_cast(v2h, nbias2);
+    Frag8 f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f.u[s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, ((w >> (4 * s)) & m) | c) + nb);
+    return f;
+}
+
+// bf16 128 + u (exact) for eight codes of one pair-ordered word.
 __device__ __forceinline__ Frag8 deq4_bf16_offset(uint32_t w) {
     const uint32_t m = 0x000F000Fu, c = 0x43004300u;
     Frag8 f;
@@ -116,7 +139,7 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <Fmt F, int BM, int BN, int WM, int WN, int PD, int NSTAGE = 2>
+template <Fmt F, int BM, int BN, int WM, int WN, int PD, int NSTAGE = 2, bool BREG = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) {
     using T = FmtTraits<F>;
     using Acc = typename T::Acc;
@@ -128,12 +151,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     constexpr int A_STAGE = BM * AROW;
     constexpr int NSTRIP = BN / 16;
     constexpr int B_STAGE = NSTRIP * T::BSTRIP;
+    // BREG: each wave loads its own weight fragments straight into registers one
+    // step ahead (the packed chunk of a strip is, lane for lane, the B fragment),
+    // so LDS holds only A and the scales and the tile can be 256 columns wide.
+    static_assert(!BREG || (PD == 0 && NSTAGE == 2), "register-fed weights go with the two-stage direct-to-LDS pipeline");
+    constexpr int B_LDS = BREG ? 0 : B_STAGE;
     // per-step scale block: WNA16 16 fp16 scales + one zero-point word per strip;
     // MXFP4 one E8M0 byte per lane per strip; INT8 none (per-channel, epilogue)
     constexpr int SC_Z = NSTRIP * 32;                     // zero-point words start (WNA16)
     constexpr int SC_STAGE = WNA16 ? NSTRIP * 48 : MX ? NSTRIP * 64 : 0;
     constexpr int SC_UNITS = SC_STAGE / 16;
-    constexpr int STAGE = A_STAGE + B_STAGE + SC_STAGE;
+    constexpr int STAGE = A_STAGE + B_LDS + SC_STAGE;
     constexpr int NIA = A_STAGE / 16 / NTH;  // 16-byte loads per thread per step (A)
     constexpr int NIB = B_STAGE / 16 / NTH;  // (B)
     constexpr int MT = BM / WM / 16, NT = BN / WN / 16;  // 16x16 tiles per wave
@@ -204,15 +232,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     const rsrc_t rS = make_rsrc(Sbase, WNA16 ? nstr * (uint32_t)p.ngroups * 32u : MX ? nstr * (uint32_t)nsteps * 64u : 0u);
     const rsrc_t rZ = make_rsrc(p.Z, WNA16 && p.Z ? nstr * (uint32_t)p.ngroups * 8u : 0u);
 
-    // per-thread byte offsets of the staged loads (fixed across K steps)
-    uint32_t aoff[NIA];
+    // per-thread byte offsets of the staged loads (fixed across K steps).  Dense
+    // A rows are consecutive: one lane offset serves every load, load i adding
+    // a wave-uniform i * (NTH / AUNITS) rows (the swizzle repeats every 16 rows);
+    // rows past M fall outside the buffer resource and read zeros (their
+    // outputs are dropped).  MoE rows are gathered: one offset per load.
+    constexpr bool AFLAT = F != Fmt::MOE_MX && (NTH / AUNITS) % 16 == 0;
+    const uint32_t arow_stride = (uint32_t)(NTH / AUNITS) * (uint32_t)(K * AB);
+    uint32_t aoff[AFLAT ? 1 : NIA];
 #pragma unroll
-    for (int i = 0; i < NIA; ++i) {
+    for (int i = 0; i < (AFLAT ? 1 : NIA); ++i) {
         const int s = i * NTH + tid;
         const int row = s / AUNITS, pos = s % AUNITS;
         const int unit = pos ^ swz(row, AUNITS);
-        aoff[i] = (uint32_t)rowinfo[row] * (uint32_t)(K * AB) + unit * 16;
+        aoff[i] = (AFLAT ? (uint32_t)(m0 + row) : (uint32_t)rowinfo[row]) * (uint32_t)(K * AB) + unit * 16;
     }
+    auto a_voff = [&](int i) -> uint32_t { return AFLAT ? aoff[0] : aoff[i]; };
+    auto a_soff = [&](int i, int ks) -> uint32_t { return (AFLAT ? (uint32_t)i * arow_stride : 0u) + (uint32_t)ks * AROW; };
     uint32_t boff[NIB];
 #pragma unroll
     for (int i = 0; i < NIB; ++i) {
@@ -245,7 +281,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     auto dma = [&](int ks, auto stc) {
         char* sA = stage_ptr(stc);
         char* sB = sA + A_STAGE;
-        char* sS = sB + B_STAGE;
+        char* sS = sB + B_LDS;
         if constexpr (WNA16) {
             const uint32_t g = (uint32_t)(ks / p.gsteps);
             if (tid < 2 * NSTRIP) {
@@ -259,15 +295,35 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         }
 #pragma unroll
         for (int i = 0; i < NIA; ++i)
-            dma16(rA, sA + i * NTH * 16 + wbase, aoff[i], (uint32_t)ks * AROW);
+            dma16(rA, sA + i * NTH * 16 + wbase, a_voff(i), a_soff(i, ks));
+        if constexpr (!BREG) {
 #pragma unroll
-        for (int i = 0; i < NIB; ++i)
-            dma16_nt(rW, sB + i * NTH * 16 + wbase, boff[i], (uint32_t)ks * T::BSTRIP);
+            for (int i = 0; i < NIB; ++i)
+                dma16_nt(rW, sB + i * NTH * 16 + wbase, boff[i], (uint32_t)ks * T::BSTRIP);
+        }
+    };
+    // BREG: this wave's NT strips of one step into register slot `slc`
+    constexpr int NBH = T::BSTRIP / 1024;  // 16-byte fragments per strip and step (two for INT8)
+    v4u breg[2][BREG ? NT : 1][NBH];
+    uint32_t bro[BREG ? NT : 1];
+    if constexpr (BREG) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            bro[j] = (uint32_t)clamp_strip(strip0 + wn * NT + j) * (uint32_t)nsteps * T::BSTRIP + lane * 16;
+    }
+    auto bload = [&](int ks, auto slc) {
+        if constexpr (BREG) {
+            constexpr int sl = decltype(slc)::value;
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int h = 0; h < NBH; ++h) breg[sl][j][h] = buf16<true>(rW, bro[j] + h * 1024, (uint32_t)ks * T::BSTRIP);
+        }
     };
     auto gload = [&](int ks, auto setc) {
         constexpr int st = decltype(setc)::value % NSET;
 #pragma unroll
-        for (int i = 0; i < NIA; ++i) ra[st][i] = buf16(rA, aoff[i], (uint32_t)ks * AROW);
+        for (int i = 0; i < NIA; ++i) ra[st][i] = buf16(rA, a_voff(i), a_soff(i, ks));
 #pragma unroll
         for (int i = 0; i < NIB; ++i) rb[st][i] = buf16<true>(rW, boff[i], (uint32_t)ks * T::BSTRIP);
         if constexpr (WNA16) {
@@ -295,7 +351,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
         for (int i = 0; i < NIB; ++i) *(v4u*)(sB + (i * NTH + tid) * 16) = rb[st][i];
         if constexpr (SC_STAGE > 0) {
-            char* sS = sB + B_STAGE;
+            char* sS = sB + B_LDS;
             if constexpr (WNA16) {
                 if (tid < 2 * NSTRIP) *(v4u*)(sS + tid * 16) = rs[st];
                 else if (tid < 3 * NSTRIP)
@@ -313,28 +369,31 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         for (int j = 0; j < NT; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
     const uint32_t wx = p.Z ? 0u : 0x88888888u;  // symmetric INT4: two's complement -> offset binary
-    auto compute = [&](auto stc) {
+    auto compute = [&](auto stc, auto slc) {
         const char* sA = stage_ptr(stc);
         const char* sB = sA + A_STAGE;
-        const char* sS = sB + B_STAGE;
-        // this wave's packed weight words: one 16-byte read per strip (per 64-K half for INT8)
-        v4u bw[NT][T::BSTRIP / 1024];
+        const char* sS = sB + B_LDS;
+        // this wave's packed weight words: one 16-byte fragment per strip (per 64-K half for INT8)
+        v4u bw[NT][NBH];
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int h = 0; h < T::BSTRIP / 1024; ++h)
-                bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
+            for (int h = 0; h < NBH; ++h) {
+                if constexpr (BREG) bw[j][h] = breg[decltype(slc)::value][j][h];
+                else bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
+            }
 
         if constexpr (F == Fmt::WNA16_F16) {
-            uint32_t s2[NT], nb2[NT];
+            uint32_t s2[NT], nb2[NT], nh2[NT];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const int sl = wn * NT + j;
                 const uint32_t sc = ((const uint16_t*)sS)[sl * 16 + col];
                 const uint32_t z = p.Z ? (((const uint32_t*)(sS + SC_Z))[sl * 2 + (col >> 3)] >> (4 * (col & 7))) & 15u : 8u;
                 s2[j] = sc | (sc << 16);
-                const uint32_t nbz = 0xE400u | z;
+                const uint32_t nbz = 0xE400u | z, nhz = 0xD400u | (z << 4);  // -(1024 + z), -(64 + z)
                 nb2[j] = nbz | (nbz << 16);
+                nh2[j] = nhz | (nhz << 16);
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -343,7 +402,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
                 for (int j = 0; j < NT; ++j) {
                     uint32_t w = bw[j][0][t];
                     w ^= wx;
-                    b[j] = deq4_f16_scaled(w, nb2[j], s2[j]);
+                    b[j] = deq4_f16_scaled(w, nb2[j], nh2[j], s2[j]);
                 }
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
@@ -465,7 +524,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         auto sub = [&](int q, auto xc) {
             constexpr int X = decltype(xc)::value;
             if (q + 2 < k1) dma(q + 2, std::integral_constant<int, (X + 2) % 3>{});
-            compute(xc);
+            compute(xc, S0{});
             if (q + 2 < k1) wait_vmcnt<NDMA>();
             else wait_vmcnt<0>();
             lds_barrier();
@@ -478,6 +537,47 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         }
         if (ks < k1) sub(ks, S0{});
         if (ks + 1 < k1) sub(ks + 1, S1{});
+    } else if constexpr (PD == 0 && BREG) {
+        // A tiles through two LDS stages, weights through two register slots,
+        // both one step ahead.  Per step the loads go out as: scales (only in
+        // the waves that fetch them), A, weights.  With the next step in
+        // flight, "A of s+1 has landed" is vmcnt(NBL) and "weights of s have
+        // landed" is vmcnt(NIA + NBL), plus one in a wave that fetched scales.
+        constexpr int NBL = NT * NBH;
+        const bool sc_wave = WNA16 ? (wave == 0 || (p.Z && wave == 1)) : MX ? wave == 0 : false;
+        auto wait_b = [&]() {
+            if (sc_wave) wait_vmcnt<NIA + NBL + 1>();
+            else wait_vmcnt<NIA + NBL>();
+        };
+        if (k0 < k1) {
+            bload(k0, S0{});
+            dma(k0, S0{});
+            wait_vmcnt<0>();
+            lds_barrier();
+        }
+        int ks = k0;
+        for (; ks + 1 < k1; ks += 2) {
+            dma(ks + 1, S1{});
+            bload(ks + 1, S1{});
+            wait_b();  // weights of ks
+            compute(S0{}, S0{});
+            wait_vmcnt<NBL>();  // A of ks+1
+            lds_barrier();
+            if (ks + 2 < k1) {
+                dma(ks + 2, S0{});
+                bload(ks + 2, S0{});
+                wait_b();  // weights of ks+1
+            } else {
+                wait_vmcnt<0>();
+            }
+            compute(S1{}, S1{});
+            if (ks + 2 < k1) wait_vmcnt<NBL>();  // A of ks+2
+            lds_barrier();
+        }
+        if (ks < k1) {
+            wait_vmcnt<0>();  // weights of the odd last step
+            compute(S0{}, S0{});
+        }
     } else if constexpr (PD == 0) {
         if (k0 < k1) {
             dma(k0, S0{});
@@ -489,15 +589,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         int ks = k0;
         for (; ks + 1 < k1; ks += 2) {
             dma(ks + 1, S1{});
-            compute(S0{});
+            compute(S0{}, S0{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
             if (ks + 2 < k1) dma(ks + 2, S0{});
-            compute(S1{});
+            compute(S1{}, S0{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
         }
-        if (ks < k1) compute(S0{});
+        if (ks < k1) compute(S0{}, S0{});
     } else {
         if (k0 < k1) {
             gload(k0, S0{});
@@ -509,13 +609,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         for (int ks = k0; ks < k1; ks += 2) {
             // step ks from stage 0
             if (ks + PD < k1) gload(ks + PD, S0{});
-            compute(S0{});
+            compute(S0{}, S0{});
             if (ks + 1 < k1) swrite(S1{}, S1{});
             __syncthreads();
             if (ks + 1 >= k1) break;
             // step ks+1 from stage 1
             if (ks + 1 + PD < k1) gload(ks + 1 + PD, S1{});
-            compute(S1{});
+            compute(S1{}, S0{});
             if (ks + 2 < k1) swrite(S0{}, S0{});
             __syncthreads();
         }
@@ -626,11 +726,11 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Formats with a 256 x 128 tile.  4-bit formats: 4 waves of 128 x 64 each,
-// loads straight into LDS (no staging registers), one wave per SIMD, so each
-// dequantised weight fragment feeds 8 MFMAs.  INT8 (no dequant) runs faster
-// on 8 waves of 128 x 32 with two register-staged steps in flight.  bf16 A
-// has no 256-row variant (its row-sum MFMA needs a second accumulator set).
+// Formats with a 256 x 128 tile.  4-bit formats: 8 waves of 128 x 32 each
+// (two per SIMD, so one wave's LDS reads and dequantisation overlap the other's
+// MFMAs), loads straight into LDS (no staging registers).  INT8 (no dequant):
+// 8 waves of 128 x 32 with two register-staged steps in flight.  bf16 A has no
+// 256-row variant (its row-sum MFMA needs a second accumulator set).
 constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16; }
 
 template <Fmt F>
@@ -639,7 +739,7 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
     if constexpr (F == Fmt::W8A8_I8) {
         if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 2>(p, st);
     } else if constexpr (has_big_tile(F)) {
-        if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 2, 0>(p, st);
+        if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
     }
     return launch_tile_kernel<F, 128, 128, 2, 2, 2>(p, st);
 }

@@ -114,7 +114,7 @@ typedef enum hq_moe_mode {
  *   INT8      INT8       FP32, PER_CHANNEL             NONE    PER_TOKEN BF16|INT32
  *   BF16      FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MoE)
  * Group sizes for 16-bit scales: a multiple of 128 that divides K.
- * K: a multiple of 128 (4-bit weights) or of 64 (INT8).  N: any value >= 1.
+ * K: a multiple of 128 (every format).  N: any value >= 1.
  * out_dtype INT32 returns the raw INT8 x INT8 accumulators (bit-exact).
  */
 typedef struct hq_layer_desc {
