@@ -62,15 +62,18 @@ def _cores():
 
 
 def _timed_oracle(fn, nrows_for, budget_s):
-    """Time fn(rows) on a row sample sized to ~budget_s of CPU work."""
-    t0 = time.perf_counter()
-    fn(nrows_for(2))
-    t1 = max(time.perf_counter() - t0, 1e-3)
-    n = max(2, int(budget_s / t1 * 2))
-    rows = nrows_for(n)
-    t0 = time.perf_counter()
-    fn(rows)
-    return len(rows), time.perf_counter() - t0
+    """Time fn(rows) on a row sample of about budget_s of CPU work: the sample
+    doubles until one run takes at least budget_s / 2 (the oracle's cost per
+    row grows once its output leaves the caches, so no linear extrapolation)."""
+    n = 2
+    while True:
+        rows = nrows_for(n)
+        t0 = time.perf_counter()
+        fn(rows)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 2 or len(nrows_for(2 * n)) == len(rows):
+            return len(rows), dt
+        n *= 2
 
 
 def _copies(tensors, nbytes, minimum=2):
@@ -110,14 +113,15 @@ class DenseW4A16:
         return self.wbytes + M * self.K * 2 + M * self.N * 2
 
     def kernel_of(self, M):
-        return ("wna16_skinny_kernel (W4A16, M<=64)", "hbm") if M <= 64 else \
-               (f"tile_gemm_kernel (W4A16 {self.dtype}, M>64)", "mfma")
+        if M <= 64:
+            return (f"skinny_kernel<WNA16_{self.dtype.upper()}> (M<=64)", "hbm")
+        return (f"tile_gemm_kernel<WNA16_{self.dtype.upper()}> (M>64)", "mfma" if M >= 128 else "hbm")
 
     def call(self, M, c):
         w, s, z = self.copies[c]
         hq.hq_gemm(self.desc, M, self.A, None, w, s, z, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
 
-    def cpu_baseline(self, budget_s=12.0):
+    def cpu_baseline(self, budget_s=16.0):
         import oracle
         d = self.host
         f = lambda rows: oracle.gemm_wna16(d["A"], d["q"], d["s"], d.get("z"), N=self.N, K=self.K, G=self.G,
@@ -158,13 +162,15 @@ class DenseW4A8:
         return self.wbytes + M * self.K + 4 * M + M * self.N * 2
 
     def kernel_of(self, M):
-        return ("tile_gemm_kernel (W4A8-MXFP4)", "mfma" if M >= 256 else "hbm")
+        if M <= 64:
+            return ("skinny_kernel<W4A8_MX> (M<=64)", "hbm")
+        return ("tile_gemm_kernel<W4A8_MX> (M>64)", "mfma" if M >= 256 else "hbm")
 
     def call(self, M, c):
         w, e = self.copies[c]
         hq.hq_gemm(self.desc, M, self.A, self.s_a, w, e, None, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
 
-    def cpu_baseline(self, budget_s=12.0):
+    def cpu_baseline(self, budget_s=16.0):
         import oracle
         d = self.host
         qa, s_a = oracle.quant_act_e4m3(d["A0"][:64])
@@ -201,13 +207,15 @@ class DenseW8A8:
         return self.wbytes + M * self.K + 4 * M + M * self.N * 2
 
     def kernel_of(self, M):
-        return ("tile_gemm_kernel (W8A8-INT8)", "mfma" if M >= 512 else "hbm")
+        if M <= 64:
+            return ("skinny_kernel<W8A8_I8> (M<=64)", "hbm")
+        return ("tile_gemm_kernel<W8A8_I8> (M>64)", "mfma" if M >= 512 else "hbm")
 
     def call(self, M, c):
         w, s = self.copies[c]
         hq.hq_gemm(self.desc, M, self.A, self.s_a, w, s, None, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
 
-    def cpu_baseline(self, budget_s=12.0):
+    def cpu_baseline(self, budget_s=16.0):
         import oracle
         d = self.host
         f = lambda rows: oracle.gemm_w8a8(d["a"], d["s_a"], d["w"], d["s_w"], rows=rows)
@@ -250,14 +258,14 @@ class MoEMXFP4:
         return self.active[T] * self.ebytes + T * self.K * 2 + T * self.top_k * (self.N * 2 + 4)
 
     def kernel_of(self, T):
-        return ("tile_gemm_kernel (MoE MXFP4 bf16)", "mfma" if T >= 4096 else "hbm")
+        return ("moe: routing + skinny_kernel<MOE_MX> + tile_gemm_kernel<MOE_MX> tiers", "mfma" if T >= 4096 else "hbm")
 
     def call(self, T, c):
         w, e = self.copies[c]
         hq.hq_moe_gemm(self.desc, hq.HQ_MOE_INDEXED, T, self.top_k, self.A, None, self.ids, None, w, e, None, self.D,
                        self.ws, self.ws_bytes)
 
-    def cpu_baseline(self, budget_s=12.0):
+    def cpu_baseline(self, budget_s=16.0):
         import oracle
         d = self.host
         ids = d["ids"][:64]
@@ -348,7 +356,7 @@ def run(work, steps, warmup, eager=False):
     return wall, per
 
 
-KERNEL_SOURCES = ["tile_gemm.hpp", "k_wna16.hip", "k_dense.hip", "k_moe.hip", "hq_device.hpp"]
+KERNEL_SOURCES = ["tile_gemm.hpp", "skinny.hpp", "k_wna16.hip", "k_dense.hip", "k_moe.hip", "hq_device.hpp"]
 
 
 def kernel_source_hash():

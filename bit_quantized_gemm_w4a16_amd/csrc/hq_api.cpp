@@ -311,7 +311,7 @@ hq_status hq_moe_align(int64_t T, int32_t top_k, int32_t num_experts, const int3
         return set_error(HQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (!aligned16(workspace)) return set_error(HQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
     return hip_status(moe_align_launch(T, top_k, num_experts, topk_ids, expert_offsets, sorted_pairs, workspace,
-                                       (hipStream_t)stream),
+                                       nullptr, (hipStream_t)stream),
                       "hq_moe_align");
 }
 

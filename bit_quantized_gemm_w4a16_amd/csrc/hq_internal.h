@@ -46,8 +46,8 @@ hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32);
 
 // MoE
 struct MoeLayout {  // byte offsets into the MoE workspace
-    size_t hist, lrank, offsets, sorted, tiles_tier[3], ntiles, bytes;
-    int64_t max_tier[3];  // bounds of the per-tier m-tile lists (small / mid / large experts)
+    size_t hist, lrank, offsets, sorted, tiles_tier[4], ntiles, bytes;
+    int64_t max_tier[4];  // bounds of the per-tier m-tile lists (by expert row count)
 };
 MoeLayout moe_layout(int64_t T, int top_k, int E, bool indexed);
 size_t moe_align_workspace(int64_t T, int top_k, int E);
@@ -67,8 +67,9 @@ struct MoeArgs {
     hipStream_t stream;
 };
 hipError_t moe_gemm_launch(const MoeArgs& a);
+struct MoeTiers;
 hipError_t moe_align_launch(int64_t T, int top_k, int E, const int* ids, int* offsets, int* sorted, void* ws,
-                            hipStream_t st);
+                            const MoeTiers* tiers, hipStream_t st);
 hipError_t moe_gather_launch(const void* A, const int* sorted, int64_t P, int top_k, int64_t row_bytes, void* out,
                              hipStream_t st);
 

@@ -20,14 +20,19 @@ namespace hq {
 
 constexpr int kMoeChunk = 256;  // pairs per histogram chunk
 constexpr int kMoeBM = 128;     // rows per m-tile of the tiled expert GEMM
-// Experts are served in three tiers by their row count: up to kMoeSmallRows
+// Experts are served in four tiers by their row count: up to kMoeSmallRows
 // rows on the weight-streaming kernel (one m-tile, its A rows in LDS for all
 // of K), up to kMoeMidMax rows on the tiled kernel with kMoeMidBM-row tiles,
-// and the rest on kMoeBM-row tiles, so no expert pads its rows more than ~2x.
+// up to kMoeBigMax on kMoeBM-row tiles and the rest on kMoeHugeBM-row tiles,
+// so no expert pads its rows more than ~2x and the busiest ones get the most
+// efficient tile.
 constexpr int kMoeSmallRows = 4;
+constexpr int kMoeAllSmallP = 64;  // at most this many pairs: every expert on the streaming path
 constexpr int kMoeSmallGridY = 32;  // workgroups per strip walking the tier-0 m-tiles
 constexpr int kMoeMidBM = 32;
 constexpr int kMoeMidMax = 64;
+constexpr int kMoeBigMax = 256;  // up to this many rows: kMoeBM-row tiles; beyond: kMoeHugeBM
+constexpr int kMoeHugeBM = 256;
 
 // ---- 1. per-chunk histogram + rank of each pair among equal ids before it ----
 // hist is expert-major: hist[e * C + c].
@@ -70,20 +75,31 @@ __global__ __launch_bounds__(64) void moe_colscan_kernel(int* __restrict__ hist,
     if (l == 0) counts[e] = carry;
 }
 
-// block-wide exclusive scan of v over 1024 threads
-__device__ int block_excl_scan_1024(int v, int* tmp) {
-    const int t = threadIdx.x;
-    tmp[t] = v;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int add = t >= off ? tmp[t - off] : 0;
-        __syncthreads();
-        tmp[t] += add;
-        __syncthreads();
+// Block-wide exclusive scans of N values per thread over 1024 threads: a
+// shuffle scan inside each wave, then the 16 wave totals through LDS
+// (tmp holds 16 * N ints); two barriers for all N values.
+template <int N>
+__device__ void block_excl_scan_1024(int (&v)[N], int* tmp) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int incl[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        incl[i] = v[i];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl[i], off, 64);
+            if (lane >= off) incl[i] += o;
+        }
+        if (lane == 63) tmp[wave * N + i] = incl[i];
     }
-    const int incl = tmp[t];
     __syncthreads();
-    return incl - v;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += tmp[w * N + i];
+        v[i] = before + incl[i] - v[i];
+    }
+    __syncthreads();
 }
 
 // ---- 2b. expert offsets and the m-tile lists (one workgroup) ----
@@ -97,20 +113,22 @@ struct TileList {
     int* ntiles;  // number of valid tiles
     int max_tiles, bm, upto;
 };
-constexpr int kMoeTiers = 3;
+constexpr int kMoeTiers = 4;
 struct MoeTiers {
     TileList t[kMoeTiers];
 };
 
-__global__ __launch_bounds__(1024) void moe_offsets_kernel(const int* __restrict__ counts, const int* __restrict__ given_off,
-                                                           int E, int P, int* __restrict__ offsets, MoeTiers tiers) {
-    __shared__ int tmp[1024];
-    __shared__ int carry[1 + kMoeTiers];
+// Expert offsets and tier lists from per-expert counts (`counts`, global or
+// LDS) or from caller-given offsets; one workgroup of 1024 threads.  The
+// offsets also go to `off_lds` when it is not null.
+__device__ void moe_offsets_and_tiers(const int* counts, const int* __restrict__ given_off, int E, int P,
+                                      int* __restrict__ offsets, int* off_lds, const MoeTiers& tiers, int* tmp,
+                                      int* carry) {
     const int t = threadIdx.x;
     if (t <= kMoeTiers) carry[t] = 0;
     __syncthreads();
     for (int e0 = 0; e0 < E; e0 += 4096) {  // 4 experts per thread per round
-        int cnt[4], tier[4], ntl[4], sum = 0, tsum[kMoeTiers] = {0, 0, 0};
+        int cnt[4], tier[4], ntl[4], sum = 0, tsum[kMoeTiers] = {};
         for (int k = 0; k < 4; ++k) {
             const int e = e0 + 4 * t + k;
             int c = 0;
@@ -123,23 +141,36 @@ __global__ __launch_bounds__(1024) void moe_offsets_kernel(const int* __restrict
                 }
             }
             cnt[k] = c;
-            int q = 0;
-            while (q < kMoeTiers - 1 && c > tiers.t[q].upto) ++q;
+            // first tier with c <= upto (static indices only: a dynamic index into
+            // the kernel-argument struct would copy it to scratch memory)
+            int q = kMoeTiers - 1, bm = tiers.t[kMoeTiers - 1].bm;
+#pragma unroll
+            for (int i = kMoeTiers - 2; i >= 0; --i)
+                if (c <= tiers.t[i].upto) {
+                    q = i;
+                    bm = tiers.t[i].bm;
+                }
             tier[k] = q;
-            ntl[k] = (c + tiers.t[q].bm - 1) / tiers.t[q].bm;
+            ntl[k] = (c + bm - 1) / bm;
             sum += c;
 #pragma unroll
             for (int i = 0; i < kMoeTiers; ++i) tsum[i] += i == q ? ntl[k] : 0;
         }
-        int run = carry[0] + block_excl_scan_1024(sum, tmp);
+        int sc[1 + kMoeTiers];
+        sc[0] = sum;
+#pragma unroll
+        for (int i = 0; i < kMoeTiers; ++i) sc[1 + i] = tsum[i];
+        block_excl_scan_1024(sc, tmp);
+        int run = carry[0] + sc[0];
         int trun[kMoeTiers];
 #pragma unroll
-        for (int i = 0; i < kMoeTiers; ++i) trun[i] = carry[1 + i] + block_excl_scan_1024(tsum[i], tmp);
+        for (int i = 0; i < kMoeTiers; ++i) trun[i] = carry[1 + i] + sc[1 + i];
         for (int k = 0; k < 4; ++k) {
             const int e = e0 + 4 * t + k;
             if (e < E) {
                 const int start = counts ? run : min(max(given_off[e], 0), P);
                 if (offsets) offsets[e] = start;
+                if (off_lds) off_lds[e] = start;
 #pragma unroll
                 for (int i = 0; i < kMoeTiers; ++i) {
                     const TileList& L = tiers.t[i];
@@ -168,6 +199,41 @@ __global__ __launch_bounds__(1024) void moe_offsets_kernel(const int* __restrict
 #pragma unroll
         for (int i = 0; i < kMoeTiers; ++i)
             if (tiers.t[i].ntiles) *tiers.t[i].ntiles = min(carry[1 + i], tiers.t[i].max_tiles);
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(1024) void moe_offsets_kernel(const int* __restrict__ counts, const int* __restrict__ given_off,
+                                                           int E, int P, int* __restrict__ offsets, MoeTiers tiers) {
+    __shared__ int tmp[1024];
+    __shared__ int carry[1 + kMoeTiers];
+    moe_offsets_and_tiers(counts, given_off, E, P, offsets, nullptr, tiers, tmp, carry);
+}
+
+// ---- routing of at most 1024 pairs in one workgroup: counts, offsets, tier
+// lists and the stable placement (rank = equal ids before the pair) ----
+constexpr int kMoeSmallP = 1024;
+__global__ __launch_bounds__(1024) void moe_route_small_kernel(const int* __restrict__ ids, int P, int E,
+                                                               int* __restrict__ offsets, int* __restrict__ sorted,
+                                                               MoeTiers tiers) {
+    __shared__ int cnt[4096];
+    __shared__ int off[4096];
+    __shared__ int cid[kMoeSmallP];
+    __shared__ int tmp[1024];
+    __shared__ int carry[1 + kMoeTiers];
+    const int t = threadIdx.x;
+    for (int e = t; e < E; e += 1024) cnt[e] = 0;
+    const int id = t < P ? ids[t] : -1;
+    const bool ok = id >= 0 && id < E;
+    cid[t] = ok ? id : -1;
+    __syncthreads();
+    if (ok) atomicAdd(&cnt[id], 1);
+    __syncthreads();
+    moe_offsets_and_tiers(cnt, nullptr, E, P, offsets, off, tiers, tmp, carry);
+    if (ok) {
+        int r = 0;
+        for (int j = 0; j < t; ++j) r += cid[j] == id;
+        sorted[off[id] + r] = t;
     }
 }
 
@@ -205,13 +271,19 @@ size_t al16(size_t b) { return (b + 15) / 16 * 16; }
 // Upper bounds of the tier lists (the real lengths are known only on the device).
 static int64_t moe_max_tiles(int tier, int64_t P, int E) {
     const int64_t ex = E < P ? E : P;  // experts that can hold a row
-    if (tier == 0) return ex;          // one m-tile of kMoeSmallRows per small expert
+    if (tier == 0)                     // one 4-row m-tile per small expert; all pairs when P is tiny
+        return P <= kMoeAllSmallP ? cdiv(P, kMoeSmallRows) + ex : ex;
     if (tier == 1) {                   // at most kMoeMidMax / kMoeMidBM tiles per mid expert
         const int64_t a = cdiv(kMoeMidMax, kMoeMidBM) * ex, b = cdiv(P, kMoeMidBM) + ex;
         return a < b ? a : b;
     }
-    const int64_t big = P / (kMoeMidMax + 1);
-    return cdiv(P, kMoeBM) + (E < big ? E : big);
+    if (tier == 2) {                   // experts with kMoeMidMax < rows <= kMoeBigMax
+        const int64_t n = P / (kMoeMidMax + 1), ne = E < n ? E : n;
+        const int64_t a = cdiv(kMoeBigMax, kMoeBM) * ne, b = cdiv(P, kMoeBM) + ne;
+        return a < b ? a : b;
+    }
+    const int64_t n = P / (kMoeBigMax + 1);
+    return cdiv(P, kMoeHugeBM) + (E < n ? E : n);
 }
 
 MoeLayout moe_layout(int64_t T, int top_k, int E, bool indexed) {
@@ -224,7 +296,7 @@ MoeLayout moe_layout(int64_t T, int top_k, int E, bool indexed) {
     o += indexed ? al16((size_t)(E + 1) * 4) : 0;
     L.sorted = o;
     o += indexed ? al16((size_t)P * 4) : 0;
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < 4; ++i) {
         L.max_tier[i] = moe_max_tiles(i, P, E);
         L.tiles_tier[i] = o;
         o += al16((size_t)(L.max_tier[i] > 0 ? L.max_tier[i] : 1) * 12);
@@ -241,17 +313,22 @@ size_t moe_align_workspace(int64_t T, int top_k, int E) {
 }
 
 hipError_t moe_align_launch(int64_t T, int top_k, int E, const int* ids, int* offsets, int* sorted, void* ws,
-                            hipStream_t st) {
+                            const MoeTiers* tiers, hipStream_t st) {
     const int P = (int)(T * top_k), C = (int)cdiv(P, kMoeChunk);
+    MoeTiers none{};
+    for (int i = 0; i < kMoeTiers; ++i) none.t[i] = TileList{nullptr, nullptr, 0, 1, 0};
+    const MoeTiers& tl = tiers ? *tiers : none;
+    if (P <= kMoeSmallP && E <= 4096) {  // one launch for the whole routing
+        hipLaunchKernelGGL(moe_route_small_kernel, dim3(1), dim3(1024), 0, st, ids, P, E, offsets, sorted, tl);
+        return hipGetLastError();
+    }
     int* hist = (int*)ws;
     int* lrank = (int*)((char*)ws + al16((size_t)C * E * 4));
     int* counts = (int*)((char*)lrank + al16((size_t)P * 4));
     hipLaunchKernelGGL(moe_hist_kernel, dim3(C), dim3(256), (size_t)(E + kMoeChunk) * 4, st, ids, P, E, C, hist, lrank);
     hipLaunchKernelGGL(moe_colscan_kernel, dim3(E), dim3(64), 0, st, hist, C, counts);
-    MoeTiers none{};
-    for (int i = 0; i < kMoeTiers; ++i) none.t[i] = TileList{nullptr, nullptr, 0, 1, 0};
     hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, st, (const int*)counts, (const int*)nullptr, E, P,
-                       offsets, none);
+                       offsets, tl);
     hipLaunchKernelGGL(moe_place_kernel, dim3(C), dim3(256), 0, st, ids, P, E, C, (const int*)hist,
                        (const int*)offsets, (const int*)lrank, sorted);
     return hipGetLastError();
@@ -277,34 +354,34 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     MoeLayout L = moe_layout(a.T, a.top_k, a.E, a.indexed);
     char* ws = (char*)a.ws;
     int* ntiles = (int*)(ws + L.ntiles);
-    int* tl[3];
-    for (int i = 0; i < 3; ++i) tl[i] = (int*)(ws + L.tiles_tier[i]);
-    const int* sorted = nullptr;
-    const int* given = nullptr;
-    hipError_t e;
-    if (a.indexed) {
-        int* offsets = (int*)(ws + L.offsets);
-        int* srt = (int*)(ws + L.sorted);
-        e = moe_align_launch(a.T, a.top_k, a.E, a.topk_ids, offsets, srt, ws + L.hist, a.stream);
-        if (e != hipSuccess) return e;
-        sorted = srt;
-        given = offsets;  // the tile lists are built from the offsets just computed
-    } else {
-        given = a.expert_offsets;
-    }
+    int* tl[4];
+    for (int i = 0; i < 4; ++i) tl[i] = (int*)(ws + L.tiles_tier[i]);
     // The weight-streaming path holds a tile's A rows for all of K in LDS and a
     // wave's quarter of K in registers; a larger K sends its experts to the mid tier.
     const int nc = (int)(a.K / 128);
     const int s_off = (int)(cdiv((int64_t)kMoeSmallRows * nc * 256, 1024) * 1024);
     const int lds = s_off + (int)(cdiv((int64_t)nc * 64, 1024) * 1024);
     const bool small_ok = cdiv(nc, 4) <= 16 && lds <= kSkinnyLds;
-    {
-        MoeTiers tiers{};
-        tiers.t[0] = TileList{tl[0], ntiles + 0, (int)L.max_tier[0], kMoeSmallRows, small_ok ? kMoeSmallRows : 0};
-        tiers.t[1] = TileList{tl[1], ntiles + 1, (int)L.max_tier[1], kMoeMidBM, kMoeMidMax};
-        tiers.t[2] = TileList{tl[2], ntiles + 2, (int)L.max_tier[2], kMoeBM, 1 << 30};
-        hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, (const int*)nullptr, given, a.E, (int)P,
-                           (int*)nullptr, tiers);
+    // With few pairs in total no expert can fill a tile: every expert takes the
+    // streaming path (several 4-row m-tiles if it must) and no tiled launch is made.
+    const bool all_small = small_ok && P <= kMoeAllSmallP;
+    MoeTiers tiers{};
+    tiers.t[0] = TileList{tl[0], ntiles + 0, (int)L.max_tier[0], kMoeSmallRows,
+                          all_small ? (1 << 30) : small_ok ? kMoeSmallRows : 0};
+    tiers.t[1] = TileList{tl[1], ntiles + 1, (int)L.max_tier[1], kMoeMidBM, kMoeMidMax};
+    tiers.t[2] = TileList{tl[2], ntiles + 2, (int)L.max_tier[2], kMoeBM, kMoeBigMax};
+    tiers.t[3] = TileList{tl[3], ntiles + 3, (int)L.max_tier[3], kMoeHugeBM, 1 << 30};
+    const int* sorted = nullptr;
+    hipError_t e;
+    if (a.indexed) {  // routing builds the tier lists from the counts
+        int* offsets = (int*)(ws + L.offsets);
+        int* srt = (int*)(ws + L.sorted);
+        e = moe_align_launch(a.T, a.top_k, a.E, a.topk_ids, offsets, srt, ws + L.hist, &tiers, a.stream);
+        if (e != hipSuccess) return e;
+        sorted = srt;
+    } else {  // Grouped: tier lists from the caller's offsets
+        hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, (const int*)nullptr, a.expert_offsets,
+                           a.E, (int)P, (int*)nullptr, tiers);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -360,12 +437,13 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     p.splits = 1;
     p.sorted = sorted;
     p.top_k = a.top_k;
+    if (all_small) return hipSuccess;
     p.tiles_m = (int)L.max_tier[1];
     p.tile_info = tl[1];
     p.ntiles = ntiles + 1;
     if (p.tiles_m > 0) {
-        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeMidBM, 128, 2, 2, 2>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
-                           dim3(256), 0, a.stream, p);
+        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeMidBM, 128, 2, 4, 0>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                           dim3(512), 0, a.stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -373,8 +451,17 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     p.tile_info = tl[2];
     p.ntiles = ntiles + 2;
     if (p.tiles_m > 0) {
-        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeBM, 128, 2, 2, 2>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
-                           dim3(256), 0, a.stream, p);
+        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeBM, 128, 2, 4, 0>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                           dim3(512), 0, a.stream, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    p.tiles_m = (int)L.max_tier[3];
+    p.tile_info = tl[3];
+    p.ntiles = ntiles + 3;
+    if (p.tiles_m > 0) {
+        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeHugeBM, 128, 2, 4, 0>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                           dim3(512), 0, a.stream, p);
         e = hipGetLastError();
     }
     return e;

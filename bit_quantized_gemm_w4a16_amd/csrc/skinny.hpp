@@ -27,10 +27,11 @@
 //      measured to cost far more than the extra launch.)
 //
 // Per format (one 128-K chunk of one strip):
-//   WNA16_F16/BF16  4 x v_mfma_f32_16x16x32_{f16,bf16}; the operand is the
-//                   exact integer (q - z) (fp16) or 128 + u with a row-sum
-//                   MFMA for the offset (bf16); the group scale multiplies the
-//                   fp32 partial of the chunk
+//   WNA16_F16       4 x v_mfma_f32_16x16x32_f16 on the exact integer (q - z);
+//                   the group scale multiplies the fp32 partial of the chunk
+//   WNA16_BF16      4 x v_mfma_f32_16x16x32_bf16 on the exact 128 + u, the
+//                   -(128 + z) offset from a row-sum MFMA and the group scale
+//                   on the fp32 partial of the chunk
 //   W4A8_MX         1 x v_mfma_scale_f32_16x16x128_f8f6f4 (fp8 A, fp4 B with
 //                   the E8M0 exponent as the B scale)
 //   W8A8_I8         2 x v_mfma_i32_16x16x64_i8 (exact int32)
@@ -208,11 +209,15 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
     lds_barrier();
 
     // ---- 3. decode + MFMA ----
-    Acc acc[SPW][MT];
+    // two independent accumulator sets (alternating by K sub-step or chunk) so
+    // consecutive MFMAs do not wait on each other; summed before the reduction
+    Acc acc2[2][SPW][MT];
 #pragma unroll
-    for (int sp = 0; sp < SPW; ++sp)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[sp][mt] = Acc{0, 0, 0, 0};
+        for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc2[q][sp][mt] = Acc{0, 0, 0, 0};
     const char* lA = lds + p.a_off;
     int arow_l[MT];  // this lane's A row in LDS per m-tile (rows past the tile read its last row)
 #pragma unroll
@@ -223,12 +228,60 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
     const uint32_t wx = zsel ? 0u : 0x88888888u;  // symmetric INT4: two's complement -> offset binary
     const uint32_t zmask = zsel ? 15u : 0u, zdef = zsel ? 0u : 8u;  // zero-point, or 8 for symmetric
 
-    // WNA16: group of the current chunk, relative to the slice's first group
+    // WNA16: group of each chunk, relative to the slice's first group
     const int g0 = WNA16 ? c0 / p.gchunks : 0, gslab = WNA16 ? (c1 - 1) / p.gchunks - g0 + 1 : 0;
-    int gcur = WNA16 ? cw0 / p.gchunks - g0 : 0, grem = WNA16 ? cw0 % p.gchunks : 0;
+    int gi[CPW];
+    {
+        int gcur = WNA16 ? cw0 / p.gchunks - g0 : 0, grem = WNA16 ? cw0 % p.gchunks : 0;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            gi[i] = min(gcur, gslab - 1);
+            if (++grem == p.gchunks) {
+                grem = 0;
+                ++gcur;
+            }
+        }
+    }
+    // 16-bit A formats: the LDS operands of chunk i+1 (A fragments, the strip's
+    // scale and zero-point word, or its E8M0 byte) are read while chunk i computes
+    constexpr bool A16 = AB == 2;
+    Frag8 afb[2][A16 ? MT : 1][4];
+    uint32_t sbb[2][SPW], zwb[2][SPW];
+    auto lds_operands = [&](int i, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        const int cl = min(cw0 + i, c1 - 1) - c0;
+        if constexpr (A16) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row = arow_l[mt];
+                const char* ar = lA + (size_t)row * U * 16;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) afb[S][mt][t].u = *(const v4u*)(ar + (((cl * 16 + 4 * quad + t) ^ skinny_swz<16>(row)) * 16));
+            }
+        }
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp) {
+            const int j = ws * SPW + sp;
+            if constexpr (WNA16) {
+                sbb[S][sp] = ((const uint16_t*)(lds + p.s_off))[(j * gslab + gi[i]) * 16 + col];
+                zwb[S][sp] = ((const uint32_t*)(lds + p.z_off))[(j * gslab + gi[i]) * 2 + (col >> 3)];
+            } else if constexpr (F == Fmt::MOE_MX) {
+                sbb[S][sp] = ((const uint8_t*)(lds + p.s_off))[(j * nsl + cl) * 64 + lane];
+            }
+        }
+    };
+    using Z0 = std::integral_constant<int, 0>;
+    using Z1 = std::integral_constant<int, 1>;
+    if constexpr (A16) lds_operands(0, Z0{});
     {  // the plan keeps a wave's K-part within one register batch (cpk <= CPW)
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
+            if constexpr (A16) {
+                if (i + 1 < CPW) {
+                    if (i & 1) lds_operands(i + 1, Z0{});
+                    else lds_operands(i + 1, Z1{});
+                }
+            }
             // Every wave runs all CPW chunk bodies without branches (branches let the
             // compiler merge the bodies and lose the per-load waits); a chunk past the
             // wave's part reads the slice's last chunk and contributes exactly zero.
@@ -237,15 +290,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
             const int cl = min(c, c1 - 1) - c0;
             if constexpr (WNA16) {
                 constexpr bool BF = F == Fmt::WNA16_BF16;
-                const int g = min(gcur, gslab - 1);
-                Frag8 af[MT][4];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const int row = arow_l[mt];
-                    const char* ar = lA + (size_t)row * U * 16;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) af[mt][t].u = *(const v4u*)(ar + (((cl * 16 + 4 * quad + t) ^ skinny_swz<16>(row)) * 16));
-                }
+                const Frag8(&af)[MT][4] = afb[i & 1];
                 v4f rs[MT];
                 if constexpr (BF) {
 #pragma unroll
@@ -257,55 +302,58 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
                 }
 #pragma unroll
                 for (int sp = 0; sp < SPW; ++sp) {
-                    const int j = ws * SPW + sp;
-                    // LDS reads without branches (a branch here costs the per-load waits):
-                    // the zero-point word is read even without zero-points and then ignored
-                    const float sc0 = bits16_to_f32<BF>(((const uint16_t*)(lds + p.s_off))[(j * gslab + g) * 16 + col]);
-                    const uint32_t zw = ((const uint32_t*)(lds + p.z_off))[(j * gslab + g) * 2 + (col >> 3)];
-                    const float sc = valid ? sc0 : 0.f;
+                    // the zero-point word was read even without zero-points (no branch
+                    // around the LDS read: a branch here costs the per-load waits)
+                    const uint32_t sbits = sbb[i & 1][sp], zw = zwb[i & 1][sp];
                     const uint32_t z = ((zw >> (4 * (col & 7))) & zmask) | zdef;
-                    const uint32_t nbz = 0xE400u | z;  // fp16 bits of -(1024 + z)
-                    const uint32_t nbias2 = nbz | (nbz << 16);
-                    v4f gacc[MT];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) gacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const uint32_t word = w[i][sp][0][t] ^ wx;
-                        Frag8 b;
-                        if constexpr (BF) b = deq4_bf16_offset(word);
-                        else b = deq4_f16_exact(word, nbias2);
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) gacc[mt] = mfma16<BF>(af[mt][t], b, gacc[mt]);
-                    }
                     if constexpr (BF) {
+                        // bf16: operand 128 + u is exact; the group scale and the
+                        // -(128 + z) offset (a row-sum MFMA) act on the fp32 partial
+                        const float sc = valid ? bits16_to_f32<true>((uint16_t)sbits) : 0.f;
+                        v4f gacc[MT];
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) gacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const Frag8 b = deq4_bf16_offset(w[i][sp][0][t] ^ wx);
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt) gacc[mt] = mfma16<true>(af[mt][t], b, gacc[mt]);
+                        }
                         const float zc = (float)(128u + z);
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) acc[sp][mt] += sc * (gacc[mt] - zc * rs[mt]);
+                        for (int mt = 0; mt < MT; ++mt) acc2[0][sp][mt] += sc * (gacc[mt] - zc * rs[mt]);
                     } else {
+                        // fp16: the exact integer (q - z) as the operand, the group scale on
+                        // the fp32 partial of the chunk (fewer VALU per code than scaling
+                        // every operand, and exact)
+                        const float sc = valid ? bits16_to_f32<false>((uint16_t)sbits) : 0.f;
+                        const uint32_t nbz = 0xE400u | z, nhz = 0xD400u | (z << 4);  // -(1024 + z), -(64 + z)
+                        const uint32_t nb2 = nbz | (nbz << 16), nh2 = nhz | (nhz << 16);
+                        v4f gacc[2][MT];
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) acc[sp][mt] += sc * gacc[mt];
+                        for (int q = 0; q < 2; ++q)
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt) gacc[q][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const Frag8 b = deq4_f16_exact(w[i][sp][0][t] ^ wx, nb2, nh2);
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt) gacc[t & 1][mt] = mfma16<false>(af[mt][t], b, gacc[t & 1][mt]);
+                        }
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) acc2[i & 1][sp][mt] += sc * (gacc[0][mt] + gacc[1][mt]);
                     }
                 }
             } else if constexpr (F == Fmt::MOE_MX) {
-                Frag8 af[MT][4];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const int row = arow_l[mt];
-                    const char* ar = lA + (size_t)row * U * 16;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) af[mt][t].u = *(const v4u*)(ar + (((cl * 16 + 4 * quad + t) ^ skinny_swz<16>(row)) * 16));
-                }
+                const Frag8(&af)[MT][4] = afb[i & 1];
 #pragma unroll
                 for (int sp = 0; sp < SPW; ++sp) {
-                    const int j = ws * SPW + sp;
-                    const float sf0 = e8m0_to_f32(((const uint8_t*)(lds + p.s_off))[(j * nsl + cl) * 64 + lane]);
-                    const float sf = valid ? sf0 : 0.f;
+                    const float sf = valid ? e8m0_to_f32(sbb[i & 1][sp]) : 0.f;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const Frag8 b = fp4_to_bf16(w[i][sp][0][t], sf);
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) acc[sp][mt] = mfma16<true>(af[mt][t], b, acc[sp][mt]);
+                        for (int mt = 0; mt < MT; ++mt) acc2[t & 1][sp][mt] = mfma16<true>(af[mt][t], b, acc2[t & 1][sp][mt]);
                     }
                 }
             } else if constexpr (F == Fmt::W4A8_MX) {
@@ -327,7 +375,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
                     const v8i b = v8i{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3], 0, 0, 0, 0};
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        acc[sp][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], b, acc[sp][mt], 0, 4, 0, 0x7F, 0, bsc);
+                        acc2[i & 1][sp][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], b, acc2[i & 1][sp][mt], 0, 4, 0, 0x7F, 0, bsc);
                 }
             } else {  // W8A8_I8
 #pragma unroll
@@ -343,17 +391,17 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
                     for (int sp = 0; sp < SPW; ++sp)
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt)
-                            acc[sp][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], __builtin_bit_cast(v4i, valid ? w[i][sp][h] : v4u{0u, 0u, 0u, 0u}), acc[sp][mt], 0, 0, 0);
-                }
-            }
-            if constexpr (WNA16) {
-                if (++grem == p.gchunks) {
-                    grem = 0;
-                    ++gcur;
+                            acc2[h][sp][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], __builtin_bit_cast(v4i, valid ? w[i][sp][h] : v4u{0u, 0u, 0u, 0u}), acc2[h][sp][mt], 0, 0, 0);
                 }
             }
         }
     }
+
+    Acc acc[SPW][MT];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[sp][mt] = acc2[0][sp][mt] + acc2[1][sp][mt];
 
     // ---- 4. reduce the K-parts of the workgroup through LDS ----
     if (WK > 1) {

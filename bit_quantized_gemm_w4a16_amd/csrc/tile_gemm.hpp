@@ -3,13 +3,17 @@
 // One workgroup of WM x WN waves computes a BM x BN tile of D (optionally
 // over one K slice of a split-K launch).  Each K step covers 128 input
 // features: the A tile (BM rows x 128 K, 16- or 8-bit), the packed weight tile
-// (BN/16 strips x one step) and the step's scales are fetched with 16-byte
-// global loads two steps ahead into registers (two register sets), written to
-// one of two LDS stages one step ahead, and consumed from LDS.  So the loads
-// of step s+2 are in flight while step s computes.  A rows are XOR-swizzled in
-// LDS with a row permutation measured to be bank-conflict free on gfx950 for
-// the fragment reads below.  The packed weight chunk of a strip is, lane for
-// lane, the MFMA B fragment, so it is copied unchanged.
+// (BN/16 strips x one step) and the step's scales.  Two pipelines:
+//   PD = 0      16-byte direct HBM->LDS loads (buffer_load ... lds) of step s+1
+//               into the other of two LDS stages while step s computes; no
+//               staging registers (the 4-bit formats);
+//   PD = 1, 2   16-byte loads into PD register sets, written to the other LDS
+//               stage one step ahead (INT8, whose tiles are twice as large).
+// A rows are XOR-swizzled in LDS with a row permutation measured to be
+// bank-conflict free on gfx950 for the fragment reads below.  The packed
+// weight chunk of a strip is, lane for lane, the MFMA B fragment, so it is
+// copied unchanged.  Workgroups are remapped so that consecutive ids land on
+// one XCD's L2 and tiles sharing A rows run close together.
 //
 // Formats (the decode runs in registers between the LDS read and the MFMA):
 //   WNA16_F16   fp16 A; INT4/UINT4 -> (q - z) * s folded into the fp16 operand
@@ -87,14 +91,16 @@ __device__ __forceinline__ Frag8 deq4_f16_scaled(uint32_t w, uint32_t nb_lo, uin
     return f;
 }
 
-// fp16 u - z for eight codes of one pair-ordered word: (0x6400 | u) is
-// 1024 + u exactly, and one packed add of -(1024 + z) leaves u - z exactly.
-__device__ __forceinline__ Frag8 deq4_f16_exact(uint32_t w, uint32_t nbias2) {
-    const uint32_t m = 0x000F000Fu, c = 0x64006400u;
-    const v2h nb = __builtin_bit_cast(v2h, nbias2);
+// fp16 u - z (exact) for eight codes of one pair-ordered word: the unpack of
+// deq4_f16_scaled without the scale (9 VALU per 8 codes).
+__device__ __forceinline__ Frag8 deq4_f16_exact(uint32_t w, uint32_t nb_lo, uint32_t nb_hi) {
+    const uint32_t w8 = w >> 8;
+    const v2h lo = __builtin_bit_cast(v2h, nb_lo), hi = __builtin_bit_cast(v2h, nb_hi);
     Frag8 f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) f.u[s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, ((w >> (4 * s)) & m) | c) + nb);
+    f.u[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, and_or(w, 0x000F000Fu, 0x64006400u)) + lo);
+    f.u[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, and_or(w, 0x00F000F0u, 0x54005400u)) + hi);
+    f.u[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, and_or(w8, 0x000F000Fu, 0x64006400u)) + lo);
+    f.u[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, and_or(w8, 0x00F000F0u, 0x54005400u)) + hi);
     return f;
 }
 
@@ -139,7 +145,7 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <Fmt F, int BM, int BN, int WM, int WN, int PD, int NSTAGE = 2, bool BREG = false>
+template <Fmt F, int BM, int BN, int WM, int WN, int PD>
 __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) {
     using T = FmtTraits<F>;
     using Acc = typename T::Acc;
@@ -151,17 +157,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     constexpr int A_STAGE = BM * AROW;
     constexpr int NSTRIP = BN / 16;
     constexpr int B_STAGE = NSTRIP * T::BSTRIP;
-    // BREG: each wave loads its own weight fragments straight into registers one
-    // step ahead (the packed chunk of a strip is, lane for lane, the B fragment),
-    // so LDS holds only A and the scales and the tile can be 256 columns wide.
-    static_assert(!BREG || (PD == 0 && NSTAGE == 2), "register-fed weights go with the two-stage direct-to-LDS pipeline");
-    constexpr int B_LDS = BREG ? 0 : B_STAGE;
     // per-step scale block: WNA16 16 fp16 scales + one zero-point word per strip;
     // MXFP4 one E8M0 byte per lane per strip; INT8 none (per-channel, epilogue)
     constexpr int SC_Z = NSTRIP * 32;                     // zero-point words start (WNA16)
     constexpr int SC_STAGE = WNA16 ? NSTRIP * 48 : MX ? NSTRIP * 64 : 0;
     constexpr int SC_UNITS = SC_STAGE / 16;
-    constexpr int STAGE = A_STAGE + B_LDS + SC_STAGE;
+    constexpr int STAGE = A_STAGE + B_STAGE + SC_STAGE;
     constexpr int NIA = A_STAGE / 16 / NTH;  // 16-byte loads per thread per step (A)
     constexpr int NIB = B_STAGE / 16 / NTH;  // (B)
     constexpr int MT = BM / WM / 16, NT = BN / WN / 16;  // 16x16 tiles per wave
@@ -172,10 +173,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     // Two LDS stages as distinct objects: the compiler can then tell a direct
     // global->LDS load into one stage from fragment reads of the other and does
     // not make the reads wait for the load.
-    static_assert(NSTAGE == 2 || (NSTAGE == 3 && PD == 0), "three stages only with direct-to-LDS loads");
     __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
     __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
-    __shared__ __attribute__((aligned(1024))) char stage2[NSTAGE == 3 ? STAGE : 16];
     __shared__ int rowinfo[2 * BM];  // [0,BM): A row per local row; [BM,2BM): D row (-1 = none)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -183,7 +182,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     const int col = lane & 15, quad = lane >> 4;
 
     // ---- tile coordinates: K slice, XCD-aware remap, grouped raster along M ----
-    const int ntile = p.tiles_m * p.tiles_n;
+    // MoE grids are sized by an upper bound of the m-tile count; the valid
+    // tiles take the lowest workgroup ids and the remap below spans only them,
+    // so every XCD gets its share of real work
+    int tiles_m = p.tiles_m;
+    if constexpr (F == Fmt::MOE_MX) {
+        tiles_m = min(*p.ntiles, p.tiles_m);
+        if ((int)blockIdx.x >= tiles_m * p.tiles_n) return;
+    }
+    const int ntile = tiles_m * p.tiles_n;
     int bid = blockIdx.x % ntile;
     const int split = blockIdx.x / ntile;
     if ((ntile & 7) == 0) bid = (bid & 7) * (ntile >> 3) + (bid >> 3);
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     const int tiles_n = p.tiles_n;
     const int group_size = GROUP_M * tiles_n;
     const int first_m = (bid / group_size) * GROUP_M;
-    const int gm = min(p.tiles_m - first_m, GROUP_M);
+    const int gm = min(tiles_m - first_m, GROUP_M);
     const int pid_m = first_m + (bid % group_size) % gm;
     const int pid_n = (bid % group_size) / gm;
 
@@ -199,7 +206,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     const char* Sbase = (const char*)p.S;
     int m0 = pid_m * BM, mrows = BM;
     if constexpr (F == Fmt::MOE_MX) {
-        if (pid_m >= *p.ntiles) return;
         const int e = p.tile_info[3 * pid_m], first = p.tile_info[3 * pid_m + 1];
         mrows = p.tile_info[3 * pid_m + 2];
         Wbase += (int64_t)e * p.w_estride;
@@ -264,8 +270,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 
     auto stage_ptr = [&](auto stc) -> char* {
         if constexpr (decltype(stc)::value == 0) return stage0;
-        else if constexpr (decltype(stc)::value == 1) return stage1;
-        else return stage2;
+        else return stage1;
     };
 
     // PD = 0: loads go straight from HBM into the next LDS stage (no staging
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     auto dma = [&](int ks, auto stc) {
         char* sA = stage_ptr(stc);
         char* sB = sA + A_STAGE;
-        char* sS = sB + B_LDS;
+        char* sS = sB + B_STAGE;
         if constexpr (WNA16) {
             const uint32_t g = (uint32_t)(ks / p.gsteps);
             if (tid < 2 * NSTRIP) {
@@ -296,29 +301,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
         for (int i = 0; i < NIA; ++i)
             dma16(rA, sA + i * NTH * 16 + wbase, a_voff(i), a_soff(i, ks));
-        if constexpr (!BREG) {
 #pragma unroll
-            for (int i = 0; i < NIB; ++i)
-                dma16_nt(rW, sB + i * NTH * 16 + wbase, boff[i], (uint32_t)ks * T::BSTRIP);
-        }
-    };
-    // BREG: this wave's NT strips of one step into register slot `slc`
-    constexpr int NBH = T::BSTRIP / 1024;  // 16-byte fragments per strip and step (two for INT8)
-    v4u breg[2][BREG ? NT : 1][NBH];
-    uint32_t bro[BREG ? NT : 1];
-    if constexpr (BREG) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-            bro[j] = (uint32_t)clamp_strip(strip0 + wn * NT + j) * (uint32_t)nsteps * T::BSTRIP + lane * 16;
-    }
-    auto bload = [&](int ks, auto slc) {
-        if constexpr (BREG) {
-            constexpr int sl = decltype(slc)::value;
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-#pragma unroll
-                for (int h = 0; h < NBH; ++h) breg[sl][j][h] = buf16<true>(rW, bro[j] + h * 1024, (uint32_t)ks * T::BSTRIP);
-        }
+        for (int i = 0; i < NIB; ++i)
+            dma16_nt(rW, sB + i * NTH * 16 + wbase, boff[i], (uint32_t)ks * T::BSTRIP);
     };
     auto gload = [&](int ks, auto setc) {
         constexpr int st = decltype(setc)::value % NSET;
@@ -351,7 +336,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
         for (int i = 0; i < NIB; ++i) *(v4u*)(sB + (i * NTH + tid) * 16) = rb[st][i];
         if constexpr (SC_STAGE > 0) {
-            char* sS = sB + B_LDS;
+            char* sS = sB + B_STAGE;
             if constexpr (WNA16) {
                 if (tid < 2 * NSTRIP) *(v4u*)(sS + tid * 16) = rs[st];
                 else if (tid < 3 * NSTRIP)
@@ -369,19 +354,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         for (int j = 0; j < NT; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
     const uint32_t wx = p.Z ? 0u : 0x88888888u;  // symmetric INT4: two's complement -> offset binary
-    auto compute = [&](auto stc, auto slc) {
+    constexpr int NBH = T::BSTRIP / 1024;  // 16-byte fragments per strip and step (two for INT8)
+    auto compute = [&](auto stc) {
         const char* sA = stage_ptr(stc);
         const char* sB = sA + A_STAGE;
-        const char* sS = sB + B_LDS;
+        const char* sS = sB + B_STAGE;
         // this wave's packed weight words: one 16-byte fragment per strip (per 64-K half for INT8)
         v4u bw[NT][NBH];
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int h = 0; h < NBH; ++h) {
-                if constexpr (BREG) bw[j][h] = breg[decltype(slc)::value][j][h];
-                else bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
-            }
+            for (int h = 0; h < NBH; ++h) bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
 
         if constexpr (F == Fmt::WNA16_F16) {
             uint32_t s2[NT], nb2[NT], nh2[NT];
@@ -508,77 +491,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     // ---- pipeline: LDS holds steps s and s+1; registers (PD > 0) hold s+1 .. s+PD ----
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    if constexpr (PD == 0 && NSTAGE == 3) {
-        // three stages: the loads of step q+2 fly while step q computes and q+1 lands
-        constexpr int NDMA = NIA + NIB;
-        if (k0 < k1) dma(k0, S0{});
-        if (k0 + 1 < k1) {
-            dma(k0 + 1, S1{});
-            wait_vmcnt<NDMA>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        lds_barrier();
-        // one step from stage X (holding step q); stage (X + 2) % 3 receives step q + 2
-        auto sub = [&](int q, auto xc) {
-            constexpr int X = decltype(xc)::value;
-            if (q + 2 < k1) dma(q + 2, std::integral_constant<int, (X + 2) % 3>{});
-            compute(xc, S0{});
-            if (q + 2 < k1) wait_vmcnt<NDMA>();
-            else wait_vmcnt<0>();
-            lds_barrier();
-        };
-        int ks = k0;
-        for (; ks + 3 <= k1; ks += 3) {
-            sub(ks, S0{});
-            sub(ks + 1, S1{});
-            sub(ks + 2, S2{});
-        }
-        if (ks < k1) sub(ks, S0{});
-        if (ks + 1 < k1) sub(ks + 1, S1{});
-    } else if constexpr (PD == 0 && BREG) {
-        // A tiles through two LDS stages, weights through two register slots,
-        // both one step ahead.  Per step the loads go out as: scales (only in
-        // the waves that fetch them), A, weights.  With the next step in
-        // flight, "A of s+1 has landed" is vmcnt(NBL) and "weights of s have
-        // landed" is vmcnt(NIA + NBL), plus one in a wave that fetched scales.
-        constexpr int NBL = NT * NBH;
-        const bool sc_wave = WNA16 ? (wave == 0 || (p.Z && wave == 1)) : MX ? wave == 0 : false;
-        auto wait_b = [&]() {
-            if (sc_wave) wait_vmcnt<NIA + NBL + 1>();
-            else wait_vmcnt<NIA + NBL>();
-        };
-        if (k0 < k1) {
-            bload(k0, S0{});
-            dma(k0, S0{});
-            wait_vmcnt<0>();
-            lds_barrier();
-        }
-        int ks = k0;
-        for (; ks + 1 < k1; ks += 2) {
-            dma(ks + 1, S1{});
-            bload(ks + 1, S1{});
-            wait_b();  // weights of ks
-            compute(S0{}, S0{});
-            wait_vmcnt<NBL>();  // A of ks+1
-            lds_barrier();
-            if (ks + 2 < k1) {
-                dma(ks + 2, S0{});
-                bload(ks + 2, S0{});
-                wait_b();  // weights of ks+1
-            } else {
-                wait_vmcnt<0>();
-            }
-            compute(S1{}, S1{});
-            if (ks + 2 < k1) wait_vmcnt<NBL>();  // A of ks+2
-            lds_barrier();
-        }
-        if (ks < k1) {
-            wait_vmcnt<0>();  // weights of the odd last step
-            compute(S0{}, S0{});
-        }
-    } else if constexpr (PD == 0) {
+    if constexpr (PD == 0) {
         if (k0 < k1) {
             dma(k0, S0{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -589,15 +502,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         int ks = k0;
         for (; ks + 1 < k1; ks += 2) {
             dma(ks + 1, S1{});
-            compute(S0{}, S0{});
+            compute(S0{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
             if (ks + 2 < k1) dma(ks + 2, S0{});
-            compute(S1{}, S0{});
+            compute(S1{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
         }
-        if (ks < k1) compute(S0{}, S0{});
+        if (ks < k1) compute(S0{});
     } else {
         if (k0 < k1) {
             gload(k0, S0{});
@@ -609,13 +522,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         for (int ks = k0; ks < k1; ks += 2) {
             // step ks from stage 0
             if (ks + PD < k1) gload(ks + PD, S0{});
-            compute(S0{}, S0{});
+            compute(S0{});
             if (ks + 1 < k1) swrite(S1{}, S1{});
             __syncthreads();
             if (ks + 1 >= k1) break;
             // step ks+1 from stage 1
             if (ks + 1 + PD < k1) gload(ks + 1 + PD, S1{});
-            compute(S1{}, S0{});
+            compute(S1{});
             if (ks + 2 < k1) swrite(S0{}, S0{});
             __syncthreads();
         }
@@ -660,25 +573,44 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 }
 
 // Split-K finalize for the tiled kernel: sums the partial tiles in slice order
-// and applies the format's epilogue (dense formats only).
+// and applies the format's epilogue (dense formats only); one thread per pair
+// of output columns of one row.
 template <Fmt F>
 __global__ __launch_bounds__(256) void tile_finalize_kernel(TileArgs p) {
-    const int64_t total = (int64_t)p.M * p.N;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-        const int m = (int)(e / p.N), n = (int)(e % p.N);
-        const int64_t base = (int64_t)m * p.Np + n, stride = (int64_t)p.M * p.Np;
-        if constexpr (F == Fmt::W8A8_I8) {
-            int v = 0;
-            for (int s = 0; s < p.splits; ++s) v += ((const int*)p.part)[base + s * stride];
-            if (p.raw_i32) ((int*)p.D)[e] = v;
-            else ((uint16_t*)p.D)[e] = f32_to_bf16_bits((float)v * p.a_scale[m] * ((const float*)p.S)[n]);
-        } else {
-            float v = 0.f;
-            for (int s = 0; s < p.splits; ++s) v += ((const float*)p.part)[base + s * stride];
-            if constexpr (F == Fmt::WNA16_F16) ((uint16_t*)p.D)[e] = f32_to_16<false>(v);
-            else if constexpr (F == Fmt::W4A8_MX) ((uint16_t*)p.D)[e] = f32_to_bf16_bits(v * p.a_scale[m]);
-            else ((uint16_t*)p.D)[e] = f32_to_bf16_bits(v);
+    const int m = blockIdx.y;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 2;
+    if (n >= p.N) return;
+    const int64_t stride = (int64_t)p.M * p.Np, base = (int64_t)m * p.Np + n, o = (int64_t)m * p.N + n;
+    const bool two = n + 1 < p.N;
+    if constexpr (F == Fmt::W8A8_I8) {
+        int v0 = 0, v1 = 0;
+        for (int s = 0; s < p.splits; ++s) {
+            const int2 v = *(const int2*)((const int*)p.part + base + s * stride);
+            v0 += v.x;
+            v1 += v.y;
         }
+        if (p.raw_i32) {
+            ((int*)p.D)[o] = v0;
+            if (two) ((int*)p.D)[o + 1] = v1;
+        } else {
+            const float as = p.a_scale[m];
+            ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)v0 * as * ((const float*)p.S)[n]);
+            if (two) ((uint16_t*)p.D)[o + 1] = f32_to_bf16_bits((float)v1 * as * ((const float*)p.S)[n + 1]);
+        }
+    } else {
+        float v0 = 0.f, v1 = 0.f;
+        for (int s = 0; s < p.splits; ++s) {
+            const float2 v = *(const float2*)((const float*)p.part + base + s * stride);
+            v0 += v.x;
+            v1 += v.y;
+        }
+        if constexpr (F == Fmt::W4A8_MX) {
+            v0 *= p.a_scale[m];
+            v1 *= p.a_scale[m];
+        }
+        constexpr bool BF = F != Fmt::WNA16_F16;
+        ((uint16_t*)p.D)[o] = f32_to_16<BF>(v0);
+        if (two) ((uint16_t*)p.D)[o + 1] = f32_to_16<BF>(v1);
     }
 }
 
@@ -712,25 +644,26 @@ inline size_t tile_workspace(const TilePlan& pl, int64_t M, int64_t Np) {
     return pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)Np * 4 : 0;
 }
 
-template <Fmt F, int BM, int BN, int WM, int WN, int PD, int NSTAGE = 2>
+template <Fmt F, int BM, int BN, int WM, int WN, int PD>
 hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.Np + BN - 1) / BN);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.splits;
-    hipLaunchKernelGGL((tile_gemm_kernel<F, BM, BN, WM, WN, PD, NSTAGE>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, p);
+    hipLaunchKernelGGL((tile_gemm_kernel<F, BM, BN, WM, WN, PD>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    int64_t blocks = ((int64_t)p.M * p.N + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL((tile_finalize_kernel<F>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+    const dim3 fgrid((unsigned)((p.N + 511) / 512), (unsigned)p.M);
+    hipLaunchKernelGGL((tile_finalize_kernel<F>), fgrid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
-// Formats with a 256 x 128 tile.  4-bit formats: 8 waves of 128 x 32 each
-// (two per SIMD, so one wave's LDS reads and dequantisation overlap the other's
-// MFMAs), loads straight into LDS (no staging registers).  INT8 (no dequant):
-// 8 waves of 128 x 32 with two register-staged steps in flight.  bf16 A has no
-// 256-row variant (its row-sum MFMA needs a second accumulator set).
+// Formats with a 256-row tile.  4-bit weights with 16-bit A: 256 x 128 on 8
+// waves of 128 x 32 (two per SIMD, so one wave's LDS reads and dequantisation
+// overlap the other's MFMAs), loads straight into LDS (no staging registers).
+// W4A8 (8-bit A, no dequantisation): 256 x 256 on 8 waves of 128 x 64, which
+// halves the A traffic per flop and still fits two LDS stages.  INT8: 256 x 128
+// on 8 waves with two register-staged steps in flight.  bf16 A has no 256-row
+// variant (its row-sum MFMA needs a second accumulator set).
 constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16; }
 
 template <Fmt F>
@@ -738,10 +671,14 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
     p.splits = pl.splits;
     if constexpr (F == Fmt::W8A8_I8) {
         if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 2>(p, st);
-    } else if constexpr (has_big_tile(F)) {
-        if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
+        return launch_tile_kernel<F, 128, 128, 2, 4, 2>(p, st);
+    } else {
+        if constexpr (F == Fmt::W4A8_MX)  // 8-bit A: a 256-column tile still fits two LDS stages
+            if (pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
+        if constexpr (has_big_tile(F))
+            if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
+        return launch_tile_kernel<F, 128, 128, 2, 4, 0>(p, st);
     }
-    return launch_tile_kernel<F, 128, 128, 2, 2, 2>(p, st);
 }
 
 }  // namespace hq
