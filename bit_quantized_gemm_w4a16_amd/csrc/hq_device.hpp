@@ -64,26 +64,30 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 typedef __attribute__((address_space(3))) void* lds_ptr;  // LDS destination of a direct global->LDS load
+typedef __attribute__((address_space(3))) char lds_char;
 
 // Direct HBM -> LDS loads (buffer_load ... lds) of 16 or 4 bytes per lane:
 // lane l of the wave writes lds + l * size; `lds` must be the same for the
-// whole wave.  The _nt form marks the data non-temporal.  The builtin exists
+// whole wave, and is an LDS-space pointer taken straight from the __shared__
+// array (through a generic pointer the compiler loses which array a load
+// writes, and then makes every later LDS read wait for it).  The _nt form
+// marks the data non-temporal.  The builtin exists
 // only in the device pass (the host pass rejects its operands, and inside a
 // kernel template that rejection silently drops the kernel's launch stub),
 // and its size operand must be a literal, hence one helper per size.
-__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ void dma16(rsrc_t r, lds_ptr lds, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
 #endif
 }
-__device__ __forceinline__ void dma16_nt(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ void dma16_nt(rsrc_t r, lds_ptr lds, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, voff, soff, 0, 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 2);
 #endif
 }
-__device__ __forceinline__ void dma4(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ void dma4(rsrc_t r, lds_ptr lds, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, soff, 0, 0);
 #endif
 }
 template <bool NT = false>
@@ -92,6 +96,15 @@ __device__ __forceinline__ v4u buf16(rsrc_t r, uint32_t voff, uint32_t soff) {
 }
 __device__ __forceinline__ uint64_t buf8(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf4(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf2(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf1(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
 
 // Direct global -> LDS loads through a flat pointer (16 or 4 bytes per lane):

@@ -9,6 +9,8 @@
 //               staging registers (the 4-bit formats);
 //   PD = 1, 2   16-byte loads into PD register sets, written to the other LDS
 //               stage one step ahead (INT8, whose tiles are twice as large).
+// The scale block of a step always travels through registers into an LDS
+// array of its own (see dma below).
 // A rows are XOR-swizzled in LDS with a row permutation measured to be
 // bank-conflict free on gfx950 for the fragment reads below.  The packed
 // weight chunk of a strip is, lane for lane, the MFMA B fragment, so it is
@@ -145,8 +147,21 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// This wave's LDS writes complete (lgkmcnt(0), other counters untouched), then
+// the workgroup barrier.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    lds_barrier();
+}
+
+// The 128- and 256-row tiles run one workgroup per CU (their LDS footprint
+// admits no second one): 8-wave tiles two waves per SIMD, so the compiler may
+// spend up to 256 VGPRs on fragments read ahead instead of aiming for a third
+// wave; 4-wave tiles one wave per SIMD with the whole 512-entry register file.
 template <Fmt F, int BM, int BN, int WM, int WN, int PD>
-__global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) {
+__global__ __launch_bounds__(64 * WM * WN, 1)
+__attribute__((amdgpu_waves_per_eu(1, BM < 128 ? 4 : WM * WN <= 4 ? 1 : 2)))
+void tile_gemm_kernel(TileArgs p) {
     using T = FmtTraits<F>;
     using Acc = typename T::Acc;
     constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
@@ -162,7 +177,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     constexpr int SC_Z = NSTRIP * 32;                     // zero-point words start (WNA16)
     constexpr int SC_STAGE = WNA16 ? NSTRIP * 48 : MX ? NSTRIP * 64 : 0;
     constexpr int SC_UNITS = SC_STAGE / 16;
-    constexpr int STAGE = A_STAGE + B_STAGE + SC_STAGE;
+    // a stage holds the A and weight tiles of one step; the step's scale block
+    // sits in an LDS array of its own (it is loaded through registers, and its
+    // reads take immediate offsets)
+    constexpr int SC_PAD = SC_STAGE > 0 ? (SC_STAGE + 15) / 16 * 16 : 16;
+    constexpr int STAGE = A_STAGE + B_STAGE;
+    constexpr int NST = 2;  // LDS stages
     constexpr int NIA = A_STAGE / 16 / NTH;  // 16-byte loads per thread per step (A)
     constexpr int NIB = B_STAGE / 16 / NTH;  // (B)
     constexpr int MT = BM / WM / 16, NT = BN / WN / 16;  // 16x16 tiles per wave
@@ -175,6 +195,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     // not make the reads wait for the load.
     __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
     __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+    __shared__ __attribute__((aligned(16))) char scst[NST][SC_PAD];
     __shared__ int rowinfo[2 * BM];  // [0,BM): A row per local row; [BM,2BM): D row (-1 = none)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -255,7 +276,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     }
     auto a_voff = [&](int i) -> uint32_t { return AFLAT ? aoff[0] : aoff[i]; };
     auto a_soff = [&](int i, int ks) -> uint32_t { return (AFLAT ? (uint32_t)i * arow_stride : 0u) + (uint32_t)ks * AROW; };
-    uint32_t boff[NIB];
+    uint32_t boff[NIB > 0 ? NIB : 1];
 #pragma unroll
     for (int i = 0; i < NIB; ++i) {
         const int s = i * NTH + tid;
@@ -264,40 +285,35 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         boff[i] = (uint32_t)strip * (uint32_t)nsteps * T::BSTRIP + (s % UPS) * 16;
     }
     const uint32_t sc_strip = (uint32_t)clamp_strip(strip0 + (WNA16 ? (tid < 2 * NSTRIP ? tid / 2 : tid - 2 * NSTRIP) : tid / 4));
-    const uint32_t zoff = (uint32_t)clamp_strip(strip0 + ((tid - 64) >> 1)) * (uint32_t)p.ngroups * 8u + (tid & 1) * 4u;
     const uint32_t soff = WNA16 ? (tid < 2 * NSTRIP ? sc_strip * p.ngroups * 32u + (tid & 1) * 16u : sc_strip * p.ngroups * 8u)
                                 : sc_strip * (uint32_t)nsteps * 64u + (tid & 3) * 16u;
 
+    auto stage_lds = [&](auto stc) -> lds_char* {
+        if constexpr (decltype(stc)::value == 0) return (lds_char*)stage0;
+        else return (lds_char*)stage1;
+    };
     auto stage_ptr = [&](auto stc) -> char* {
         if constexpr (decltype(stc)::value == 0) return stage0;
         else return stage1;
     };
+    auto sc_ptr = [&](auto stc) -> char* { return scst[decltype(stc)::value]; };
 
     // PD = 0: loads go straight from HBM into the next LDS stage (no staging
     // registers).  PD = 1, 2: register sets; the loads of step s+PD fly while
     // step s computes.
     static_assert(PD >= 0 && PD <= 2, "prefetch depth is zero (direct to LDS), one or two steps");
-    constexpr int NSET = PD > 0 ? PD : 1;
-    v4u ra[NSET][PD > 0 ? NIA : 1], rb[NSET][PD > 0 ? NIB : 1], rs[NSET];
-    // Direct loads of one step into a stage.  The scale / zero-point loads are
-    // issued first, so after the NIA + NIB unconditional loads of a later step
-    // have been issued, vmcnt(NIA + NIB) means "this step has landed" in every wave.
+    constexpr bool RSTAGE = PD == 1 || PD == 2;  // A and B staged through registers
+    constexpr int NSET = RSTAGE ? PD : 1;
+    v4u ra[NSET][RSTAGE ? NIA : 1], rb[NSET][RSTAGE ? NIB : 1], rs[NSET];
+    // Direct loads of one step's A and weight tiles into a stage (NIA + NIB
+    // unconditional loads per thread).  The scale block goes through registers
+    // (sc_load, then sc_write into its own LDS array once landed): the compiler
+    // cannot tell direct loads into the scale block of one stage from reads of
+    // another stage's, and would make every LDS read wait for them.
     const int wbase = __builtin_amdgcn_readfirstlane((tid & ~63) * 16);  // this wave's first 16-byte slot
     auto dma = [&](int ks, auto stc) {
-        char* sA = stage_ptr(stc);
-        char* sB = sA + A_STAGE;
-        char* sS = sB + B_STAGE;
-        if constexpr (WNA16) {
-            const uint32_t g = (uint32_t)(ks / p.gsteps);
-            if (tid < 2 * NSTRIP) {
-                dma16(rS, sS, soff, g * 32u);
-            } else if (p.Z && tid >= 64 && tid < 64 + 2 * NSTRIP) {
-                // zero-point words: lane 2j + h of wave 1 fetches word h of strip j
-                dma4(rZ, sS + SC_Z, zoff, g * 8u);
-            }
-        } else if constexpr (MX) {
-            if (tid < SC_UNITS) dma16(rS, sS, soff, (uint32_t)ks * 64u);
-        }
+        lds_char* sA = stage_lds(stc);
+        lds_char* sB = sA + A_STAGE;
 #pragma unroll
         for (int i = 0; i < NIA; ++i)
             dma16(rA, sA + i * NTH * 16 + wbase, a_voff(i), a_soff(i, ks));
@@ -305,38 +321,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         for (int i = 0; i < NIB; ++i)
             dma16_nt(rW, sB + i * NTH * 16 + wbase, boff[i], (uint32_t)ks * T::BSTRIP);
     };
-    auto gload = [&](int ks, auto setc) {
+    // the step's scale block: WNA16 threads [0, 2 NSTRIP) fetch 16 scale bytes
+    // each, threads [2 NSTRIP, 3 NSTRIP) a strip's zero-point word; MXFP4
+    // threads [0, SC_UNITS) 16 E8M0 bytes each
+    auto sc_load = [&](int ks, auto setc) {
         constexpr int st = decltype(setc)::value % NSET;
-#pragma unroll
-        for (int i = 0; i < NIA; ++i) ra[st][i] = buf16(rA, a_voff(i), a_soff(i, ks));
-#pragma unroll
-        for (int i = 0; i < NIB; ++i) rb[st][i] = buf16<true>(rW, boff[i], (uint32_t)ks * T::BSTRIP);
         if constexpr (WNA16) {
             const uint32_t g = (uint32_t)(ks / p.gsteps);
             if (tid < 2 * NSTRIP) {
                 rs[st] = buf16(rS, soff, g * 32u);
             } else if (tid < 3 * NSTRIP) {
-                rs[st] = v4u{0x88888888u, 0x88888888u, 0u, 0u};
-                if (p.Z) {
-                    const uint64_t z = buf8(rZ, soff, g * 8u);
-                    rs[st][0] = (uint32_t)z;
-                    rs[st][1] = (uint32_t)(z >> 32);
-                }
+                // unconditional, straight into the register set (a select after
+                // the load would make the wave wait for it at once); without
+                // zero-points the buffer range is empty and the load reads zeros,
+                // which the symmetric decode ignores
+                const uint64_t z = buf8(rZ, soff, g * 8u);
+                rs[st][0] = (uint32_t)z;
+                rs[st][1] = (uint32_t)(z >> 32);
             }
         } else if constexpr (MX) {
             if (tid < SC_UNITS) rs[st] = buf16(rS, soff, (uint32_t)ks * 64u);
         }
     };
-    auto swrite = [&](auto stc, auto setc) {
+    auto sc_write = [&](auto stc, auto setc) {
         constexpr int st = decltype(setc)::value % NSET;
-        char* sA = stage_ptr(stc);
-        char* sB = sA + A_STAGE;
-#pragma unroll
-        for (int i = 0; i < NIA; ++i) *(v4u*)(sA + (i * NTH + tid) * 16) = ra[st][i];
-#pragma unroll
-        for (int i = 0; i < NIB; ++i) *(v4u*)(sB + (i * NTH + tid) * 16) = rb[st][i];
+        char* sS = sc_ptr(stc);
         if constexpr (SC_STAGE > 0) {
-            char* sS = sB + B_STAGE;
             if constexpr (WNA16) {
                 if (tid < 2 * NSTRIP) *(v4u*)(sS + tid * 16) = rs[st];
                 else if (tid < 3 * NSTRIP)
@@ -346,6 +356,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
             }
         }
     };
+    auto gload = [&](int ks, auto setc) {
+        constexpr int st = decltype(setc)::value % NSET;
+#pragma unroll
+        for (int i = 0; i < NIA; ++i) ra[st][i] = buf16(rA, a_voff(i), a_soff(i, ks));
+#pragma unroll
+        for (int i = 0; i < NIB; ++i) rb[st][i] = buf16<true>(rW, boff[i], (uint32_t)ks * T::BSTRIP);
+        sc_load(ks, setc);
+    };
+    auto swrite = [&](auto stc, auto setc) {
+        constexpr int st = decltype(setc)::value % NSET;
+        char* sA = stage_ptr(stc);
+        char* sB = sA + A_STAGE;
+#pragma unroll
+        for (int i = 0; i < NIA; ++i) *(v4u*)(sA + (i * NTH + tid) * 16) = ra[st][i];
+#pragma unroll
+        for (int i = 0; i < NIB; ++i) *(v4u*)(sB + (i * NTH + tid) * 16) = rb[st][i];
+        sc_write(stc, setc);
+    };
 
     Acc acc[MT][NT];
 #pragma unroll
@@ -353,12 +381,28 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
+    // LDS offset of this lane's A fragment for K sub-step t of a 128-K step: the
+    // rows of a wave's 16-row tiles differ by multiples of 16, so the swizzle
+    // depends on the lane's column only and tile i adds i * 16 rows (an
+    // immediate offset)
+    uint32_t a_frag[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        a_frag[t] = (uint32_t)((wm * (BM / WM) + col) * AROW + (((4 * quad + t) ^ swz(col, AUNITS)) * 16));
     const uint32_t wx = p.Z ? 0u : 0x88888888u;  // symmetric INT4: two's complement -> offset binary
+    // scale block of a step: this lane's column in the wave's first strip
+    const uint32_t sc_lane = (uint32_t)(wn * NT * 32 + col * 2), z_lane = (uint32_t)(wn * NT * 8 + (col >> 3) * 4);
+    const uint32_t zshift = 4u * (uint32_t)(col & 7), zmask = p.Z ? 15u : 0u, zsym = p.Z ? 0u : 8u;
     constexpr int NBH = T::BSTRIP / 1024;  // 16-byte fragments per strip and step (two for INT8)
-    auto compute = [&](auto stc) {
+    // compute(stage, hook): hook(t) runs at the start of K sub-step t = 0..3,
+    // after the step's scale block has been read from LDS; the pipelines issue
+    // the next steps' loads there (all at t = 0: spreading them over the step
+    // measured slower)
+    auto nohook = [](int) {};
+    auto compute = [&](auto stc, auto hook) {
+        const char* sS = sc_ptr(stc);
         const char* sA = stage_ptr(stc);
         const char* sB = sA + A_STAGE;
-        const char* sS = sB + B_STAGE;
         // this wave's packed weight words: one 16-byte fragment per strip (per 64-K half for INT8)
         v4u bw[NT][NBH];
 #pragma unroll
@@ -367,12 +411,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
             for (int h = 0; h < NBH; ++h) bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
 
         if constexpr (F == Fmt::WNA16_F16) {
+            Frag8 afr[2][MT > 3 ? MT : 3];  // A fragments read ahead (software pipeline)
+            Frag8 bq[2][NT];                  // dequantised weights of two sub-steps
             uint32_t s2[NT], nb2[NT], nh2[NT];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                const int sl = wn * NT + j;
-                const uint32_t sc = ((const uint16_t*)sS)[sl * 16 + col];
-                const uint32_t z = p.Z ? (((const uint32_t*)(sS + SC_Z))[sl * 2 + (col >> 3)] >> (4 * (col & 7))) & 15u : 8u;
+                // one lane offset for every strip (strips are immediate offsets); the
+                // zero-point select is branch-free (symmetric INT4: z = 8)
+                const uint32_t sc = *(const uint16_t*)(sS + sc_lane + j * 32);
+                const uint32_t zw = *(const uint32_t*)(sS + SC_Z + z_lane + j * 8);
+                const uint32_t z = ((zw >> zshift) & zmask) | zsym;
                 s2[j] = sc | (sc << 16);
                 const uint32_t nbz = 0xE400u | z, nhz = 0xD400u | (z << 4);  // -(1024 + z), -(64 + z)
                 nb2[j] = nbz | (nbz << 16);
@@ -380,25 +428,69 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                Frag8 b[NT];
+                hook(t);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (NT >= 4) {
+                    // wide wave tiles: A fragments stream through a ring of three
+                    // registers sets, each read two fragments (eight MFMAs) ahead
+                    // of its use; the sub-step's weights are dequantised first
+                    constexpr int NQ = 4 * MT;
+                    if (t == 0) {
+                        afr[0][0].u = *(const v4u*)(sA + a_frag[0]);
+                        afr[0][1].u = *(const v4u*)(sA + a_frag[0] + 16 * AROW);
+                    }
+                    Frag8 b[NT];
 #pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    uint32_t w = bw[j][0][t];
-                    w ^= wx;
-                    b[j] = deq4_f16_scaled(w, nb2[j], nh2[j], s2[j]);
+                    for (int j = 0; j < NT; ++j) b[j] = deq4_f16_scaled(bw[j][0][t] ^ wx, nb2[j], nh2[j], s2[j]);
+#pragma unroll
+                    for (int i = 0; i < MT; ++i) {
+                        const int q = t * MT + i;
+                        if (q + 2 < NQ)
+                            afr[0][(q + 2) % 3].u = *(const v4u*)(sA + a_frag[(q + 2) / MT] + ((q + 2) % MT) * 16 * AROW);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<false>(afr[0][q % 3], b[j], acc[i][j]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else {
+                    // Software pipeline over the four K sub-steps: the A fragments
+                    // and dequantised weights of sub-step t + 1 are produced
+                    // between the MFMAs of sub-step t, so one wave's VALU and LDS
+                    // work fills the gaps of its own MFMA stream
+                    if (t == 0) {
+#pragma unroll
+                        for (int i = 0; i < MT; ++i) afr[0][i].u = *(const v4u*)(sA + a_frag[0] + i * 16 * AROW);
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) bq[0][j] = deq4_f16_scaled(bw[j][0][0] ^ wx, nb2[j], nh2[j], s2[j]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (t < 3) {
+#pragma unroll
+                        for (int i = 0; i < MT; ++i) afr[(t + 1) & 1][i].u = *(const v4u*)(sA + a_frag[t + 1] + i * 16 * AROW);
+#pragma unroll
+                        for (int j = 0; j < NT; ++j)
+                            bq[(t + 1) & 1][j] = deq4_f16_scaled(bw[j][0][t + 1] ^ wx, nb2[j], nh2[j], s2[j]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < MT; ++i)
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<false>(afr[t & 1][i], bq[t & 1][j], acc[i][j]);
+                    if (t < 3) {
+                        // per A fragment: its read, the MFMAs of one fragment of
+                        // this sub-step, a share of the next sub-step's dequant
+#pragma unroll
+                        for (int i = 0; i < MT; ++i) {
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // DS read
+                            __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);       // MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);        // VALU
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-#pragma unroll
-                for (int i = 0; i < MT; ++i) {
-                    const int row = wm * (BM / WM) + i * 16 + col;
-                    Frag8 a;
-                    a.u = *(const v4u*)(sA + row * AROW + (((4 * quad + t) ^ swz(row, AUNITS)) * 16));
-#pragma unroll
-                    for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<false>(a, b[j], acc[i][j]);
-                }
-                // keep one K sub-step's fragments live at a time (register budget of 8-wave tiles)
-                if constexpr (MT > 4) __builtin_amdgcn_sched_barrier(0);
             }
         } else if constexpr (F == Fmt::WNA16_BF16) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) hook(t);
             float sc[NT], zc[NT];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
@@ -440,6 +532,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
 #pragma unroll
                 for (int j = 0; j < NT; ++j) acc[i][j] += sc[j] * (st[i][j] - zc[j] * rsum[i]);
         } else if constexpr (F == Fmt::W4A8_MX) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) hook(t);
             int bsc[NT];
 #pragma unroll
             for (int j = 0; j < NT; ++j) bsc[j] = (int)((const uint8_t*)sS)[(wn * NT + j) * 64 + lane];
@@ -458,6 +552,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
             }
         } else if constexpr (F == Fmt::W8A8_I8) {
 #pragma unroll
+            for (int t = 0; t < 4; ++t) hook(t);
+#pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int i = 0; i < MT; ++i) {
@@ -468,6 +564,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
                         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a), __builtin_bit_cast(v4i, bw[j][h]), acc[i][j], 0, 0, 0);
                 }
         } else {  // MOE_MX
+#pragma unroll
+            for (int t = 0; t < 4; ++t) hook(t);
             float sf[NT];
 #pragma unroll
             for (int j = 0; j < NT; ++j) sf[j] = e8m0_to_f32(((const uint8_t*)sS)[(wn * NT + j) * 64 + lane]);
@@ -492,25 +590,41 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     if constexpr (PD == 0) {
+        // two stages: the A / weight tiles of step s+1 load while step s
+        // computes; the scale block of s+1 lands in registers and is written to
+        // its LDS array after the step's wait.  The builtin waits (unlike inline
+        // asm) tell the compiler which loads have landed, so it adds none of its
+        // own that would drain the prefetch.
         if (k0 < k1) {
+            sc_load(k0, S0{});
             dma(k0, S0{});
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();
+            wait_vmcnt<0>();
+            sc_write(S0{}, S0{});
+            lds_sync();
         }
         // whole pairs of steps (one loop exit keeps the accumulators in place),
         // then an odd last step; step ks is always in stage 0 at the loop top
         int ks = k0;
         for (; ks + 1 < k1; ks += 2) {
-            dma(ks + 1, S1{});
-            compute(S0{});
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();
-            if (ks + 2 < k1) dma(ks + 2, S0{});
-            compute(S1{});
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();
+            compute(S0{}, [&](int t) {
+                if (t != 0) return;
+                sc_load(ks + 1, S0{});
+                dma(ks + 1, S1{});
+            });
+            wait_vmcnt<0>();
+            sc_write(S1{}, S0{});
+            lds_sync();
+            const bool more = ks + 2 < k1;
+            compute(S1{}, [&](int t) {
+                if (!more || t != 0) return;
+                sc_load(ks + 2, S0{});
+                dma(ks + 2, S0{});
+            });
+            wait_vmcnt<0>();
+            if (more) sc_write(S0{}, S0{});
+            lds_sync();
         }
-        if (ks < k1) compute(S0{});
+        if (ks < k1) compute(S0{}, nohook);
     } else {
         if (k0 < k1) {
             gload(k0, S0{});
@@ -522,13 +636,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void tile_gemm_kernel(TileArgs p) 
         for (int ks = k0; ks < k1; ks += 2) {
             // step ks from stage 0
             if (ks + PD < k1) gload(ks + PD, S0{});
-            compute(S0{});
+            compute(S0{}, nohook);
             if (ks + 1 < k1) swrite(S1{}, S1{});
             __syncthreads();
             if (ks + 1 >= k1) break;
             // step ks+1 from stage 1
             if (ks + 1 + PD < k1) gload(ks + 1 + PD, S1{});
-            compute(S1{});
+            compute(S1{}, nohook);
             if (ks + 2 < k1) swrite(S0{}, S0{});
             __syncthreads();
         }
@@ -621,13 +735,19 @@ namespace hq {
 // ---- host-side plan shared by the dense launchers ----
 struct TilePlan {
     int BM, splits;
+    bool wide;  // 128 x 256 tiles on 8 waves of 128 x 32
 };
 
-// Large grids use 256 x 128 tiles on 8 waves; smaller ones 128 x 128 tiles on
-// 4 waves with K split across workgroups until the grid covers the chip.
-inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256) {
+// The largest grids use 128 x 256 tiles where the format has them, else
+// 256 x 128 tiles on 8 waves; smaller ones 128 x 128 tiles with K split across
+// workgroups until the grid covers the chip.
+inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256, bool allow_wide = false) {
     const int64_t tn = (Np + 127) / 128, nsteps = K / 128;
-    TilePlan pl{128, 1};
+    TilePlan pl{128, 1, false};
+    if (allow_wide && ((M + 127) / 128) * ((Np + 255) / 256) >= 256) {
+        pl.wide = true;
+        return pl;
+    }
     if (allow256 && ((M + 255) / 256) * tn >= 256) {
         pl.BM = 256;
         return pl;
@@ -665,6 +785,11 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
 // on 8 waves with two register-staged steps in flight.  bf16 A has no 256-row
 // variant (its row-sum MFMA needs a second accumulator set).
 constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16; }
+// fp16 A with 4-bit weights: 128 x 256 on 8 waves of 128 x 32 side by side,
+// so each weight strip is dequantised by one wave only (a 256 x 128 tile
+// dequantises it in two) and a step loads 48 KB instead of 80 KB (+6..12 % at
+// M = 2048..8192 over 256 x 128).
+constexpr bool has_wide_tile(Fmt F) { return F == Fmt::WNA16_F16; }
 
 template <Fmt F>
 hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
@@ -675,6 +800,8 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
     } else {
         if constexpr (F == Fmt::W4A8_MX)  // 8-bit A: a 256-column tile still fits two LDS stages
             if (pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
+        if constexpr (has_wide_tile(F))
+            if (pl.wide) return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
         if constexpr (has_big_tile(F))
             if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
         return launch_tile_kernel<F, 128, 128, 2, 4, 0>(p, st);

@@ -105,3 +105,19 @@ def test_workspace_reused_across_calls_and_sizes():
         Dh = to_f64(D[: M * N * 2].cpu().numpy().view(np.uint16).reshape(M, N), torch.float16)
         O = oracle.gemm_wna16(d["A"], d["q"], d["s"], d["z"], N=N, K=K, G=G, a_bf16=False, w_signed=False)
         check(Dh, O, False)
+
+
+@pytest.mark.parametrize("M", [1, 64, 1024, 4096, 8192])
+def test_dense_w4a16_zp_full_size(M):
+    """The dense W4A16 workload (UINT4 + zero-points, fp16, N=4096, K=7168, G=128)
+    in the launch configuration the benchmark times; sampled rows at large M."""
+    Dr, O = run_wna16(M, 4096, 7168, 128, bf16=False, zp=True, seed=0)
+    check(Dr, O, False)
+
+
+@pytest.mark.parametrize("M,N,K,zp", [(4000, 4100, 512, True), (4096, 4096, 1024, False), (1100, 16000, 256, True),
+                                      (8192, 2056, 384, True)])
+def test_wide_tiles_ragged(M, N, K, zp):
+    """Grids large enough for 256 x 256 tiles, with ragged last row and column tiles."""
+    Dr, O = run_wna16(M, N, K, 128, bf16=False, zp=zp, seed=M + N)
+    check(Dr, O, False)
