@@ -8,7 +8,13 @@
 //               into the other of two LDS stages while step s computes; no
 //               staging registers (the 4-bit formats);
 //   PD = 1, 2   16-byte loads into PD register sets, written to the other LDS
-//               stage one step ahead (INT8, whose tiles are twice as large).
+//               stage one step ahead (INT8, whose tiles are twice as large);
+//   PD = 3      as PD = 0 with two A stages but ONE weight stage: every wave
+//               copies its weight fragments of the step into registers first,
+//               so after one barrier the weight stage takes the next step's
+//               tile.  That leaves room for 256-row x 256-column tiles of
+//               8 waves of 256 x 32, whose dequantised weight fragment feeds
+//               16 MFMAs (8 in a 128-row wave).
 // The scale block of a step always travels through registers into an LDS
 // array of its own (see dma below).
 // A rows are XOR-swizzled in LDS with a row permutation measured to be
@@ -181,7 +187,8 @@ void tile_gemm_kernel(TileArgs p) {
     // sits in an LDS array of its own (it is loaded through registers, and its
     // reads take immediate offsets)
     constexpr int SC_PAD = SC_STAGE > 0 ? (SC_STAGE + 15) / 16 * 16 : 16;
-    constexpr int STAGE = A_STAGE + B_STAGE;
+    constexpr bool B1 = PD == 3;  // single weight stage
+    constexpr int STAGE = A_STAGE + (B1 ? 0 : B_STAGE);
     constexpr int NST = 2;  // LDS stages
     constexpr int NIA = A_STAGE / 16 / NTH;  // 16-byte loads per thread per step (A)
     constexpr int NIB = B_STAGE / 16 / NTH;  // (B)
@@ -195,6 +202,7 @@ void tile_gemm_kernel(TileArgs p) {
     // not make the reads wait for the load.
     __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
     __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char bstage[B1 ? B_STAGE : 16];
     __shared__ __attribute__((aligned(16))) char scst[NST][SC_PAD];
     __shared__ int rowinfo[2 * BM];  // [0,BM): A row per local row; [BM,2BM): D row (-1 = none)
 
@@ -301,7 +309,7 @@ void tile_gemm_kernel(TileArgs p) {
     // PD = 0: loads go straight from HBM into the next LDS stage (no staging
     // registers).  PD = 1, 2: register sets; the loads of step s+PD fly while
     // step s computes.
-    static_assert(PD >= 0 && PD <= 2, "prefetch depth is zero (direct to LDS), one or two steps");
+    static_assert(PD >= 0 && PD <= 3, "prefetch: direct to LDS, one or two register steps, single weight stage");
     constexpr bool RSTAGE = PD == 1 || PD == 2;  // A and B staged through registers
     constexpr int NSET = RSTAGE ? PD : 1;
     v4u ra[NSET][RSTAGE ? NIA : 1], rb[NSET][RSTAGE ? NIB : 1], rs[NSET];
@@ -311,15 +319,21 @@ void tile_gemm_kernel(TileArgs p) {
     // cannot tell direct loads into the scale block of one stage from reads of
     // another stage's, and would make every LDS read wait for them.
     const int wbase = __builtin_amdgcn_readfirstlane((tid & ~63) * 16);  // this wave's first 16-byte slot
-    auto dma = [&](int ks, auto stc) {
+    auto dma_a = [&](int ks, auto stc) {
         lds_char* sA = stage_lds(stc);
-        lds_char* sB = sA + A_STAGE;
 #pragma unroll
         for (int i = 0; i < NIA; ++i)
             dma16(rA, sA + i * NTH * 16 + wbase, a_voff(i), a_soff(i, ks));
+    };
+    auto dma_b = [&](int ks, auto stc) {
+        lds_char* sB = B1 ? (lds_char*)bstage : stage_lds(stc) + A_STAGE;
 #pragma unroll
         for (int i = 0; i < NIB; ++i)
             dma16_nt(rW, sB + i * NTH * 16 + wbase, boff[i], (uint32_t)ks * T::BSTRIP);
+    };
+    auto dma = [&](int ks, auto stc) {
+        dma_a(ks, stc);
+        dma_b(ks, stc);
     };
     // the step's scale block: WNA16 threads [0, 2 NSTRIP) fetch 16 scale bytes
     // each, threads [2 NSTRIP, 3 NSTRIP) a strip's zero-point word; MXFP4
@@ -402,7 +416,7 @@ void tile_gemm_kernel(TileArgs p) {
     auto compute = [&](auto stc, auto hook) {
         const char* sS = sc_ptr(stc);
         const char* sA = stage_ptr(stc);
-        const char* sB = sA + A_STAGE;
+        const char* sB = B1 ? bstage : sA + A_STAGE;
         // this wave's packed weight words: one 16-byte fragment per strip (per 64-K half for INT8)
         v4u bw[NT][NBH];
 #pragma unroll
@@ -411,7 +425,9 @@ void tile_gemm_kernel(TileArgs p) {
             for (int h = 0; h < NBH; ++h) bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
 
         if constexpr (F == Fmt::WNA16_F16) {
-            Frag8 afr[2][MT > 3 ? MT : 3];  // A fragments read ahead (software pipeline)
+            // A fragments read ahead (software pipeline): a whole sub-step, or
+            // a ring of three for tall / wide wave tiles
+            Frag8 afr[(NT >= 4 || MT > 8) ? 1 : 2][(NT >= 4 || MT > 8) ? 3 : MT];
             Frag8 bq[2][NT];                  // dequantised weights of two sub-steps
             uint32_t s2[NT], nb2[NT], nh2[NT];
 #pragma unroll
@@ -430,26 +446,28 @@ void tile_gemm_kernel(TileArgs p) {
             for (int t = 0; t < 4; ++t) {
                 hook(t);
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (NT >= 4) {
-                    // wide wave tiles: A fragments stream through a ring of three
-                    // registers sets, each read two fragments (eight MFMAs) ahead
-                    // of its use; the sub-step's weights are dequantised first
+                if constexpr (NT >= 4 || MT > 8) {
+                    // tall or wide wave tiles: A fragments stream through a ring of
+                    // three register sets, each read two fragments ahead of its
+                    // MFMAs; the weights of sub-step t + 1 are dequantised one
+                    // strip per A fragment between the MFMAs of sub-step t
                     constexpr int NQ = 4 * MT;
                     if (t == 0) {
                         afr[0][0].u = *(const v4u*)(sA + a_frag[0]);
                         afr[0][1].u = *(const v4u*)(sA + a_frag[0] + 16 * AROW);
-                    }
-                    Frag8 b[NT];
 #pragma unroll
-                    for (int j = 0; j < NT; ++j) b[j] = deq4_f16_scaled(bw[j][0][t] ^ wx, nb2[j], nh2[j], s2[j]);
+                        for (int j = 0; j < NT; ++j) bq[0][j] = deq4_f16_scaled(bw[j][0][0] ^ wx, nb2[j], nh2[j], s2[j]);
+                    }
 #pragma unroll
                     for (int i = 0; i < MT; ++i) {
                         const int q = t * MT + i;
                         if (q + 2 < NQ)
                             afr[0][(q + 2) % 3].u = *(const v4u*)(sA + a_frag[(q + 2) / MT] + ((q + 2) % MT) * 16 * AROW);
+                        if (t < 3 && i < NT)
+                            bq[(t + 1) & 1][i] = deq4_f16_scaled(bw[i][0][t + 1] ^ wx, nb2[i], nh2[i], s2[i]);
                         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<false>(afr[0][q % 3], b[j], acc[i][j]);
+                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<false>(afr[0][q % 3], bq[t & 1][j], acc[i][j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 } else {
@@ -625,6 +643,39 @@ void tile_gemm_kernel(TileArgs p) {
             lds_sync();
         }
         if (ks < k1) compute(S0{}, nohook);
+    } else if constexpr (PD == 3) {
+        // as PD = 0; the single weight stage is refilled once every wave holds
+        // its fragments of the current step (the barrier in the hook at t = 0)
+        if (k0 < k1) {
+            sc_load(k0, S0{});
+            dma(k0, S0{});
+            wait_vmcnt<0>();
+            sc_write(S0{}, S0{});
+            lds_sync();
+        }
+        int ks = k0;
+        for (; ks + 1 < k1; ks += 2) {
+            compute(S0{}, [&](int t) {
+                if (t != 0) return;
+                lds_sync();
+                sc_load(ks + 1, S0{});
+                dma(ks + 1, S1{});
+            });
+            wait_vmcnt<0>();
+            sc_write(S1{}, S0{});
+            lds_sync();
+            const bool more = ks + 2 < k1;
+            compute(S1{}, [&](int t) {
+                if (!more || t != 0) return;
+                lds_sync();
+                sc_load(ks + 2, S0{});
+                dma(ks + 2, S0{});
+            });
+            wait_vmcnt<0>();
+            if (more) sc_write(S0{}, S0{});
+            lds_sync();
+        }
+        if (ks < k1) compute(S0{}, nohook);
     } else {
         if (k0 < k1) {
             gload(k0, S0{});
@@ -735,16 +786,21 @@ namespace hq {
 // ---- host-side plan shared by the dense launchers ----
 struct TilePlan {
     int BM, splits;
-    bool wide;  // 128 x 256 tiles on 8 waves of 128 x 32
+    bool wide;  // 256-column tiles: 256 x 256 if BM == 256, else 128 x 256
 };
 
-// The largest grids use 128 x 256 tiles where the format has them, else
-// 256 x 128 tiles on 8 waves; smaller ones 128 x 128 tiles with K split across
-// workgroups until the grid covers the chip.
+// The largest grids use 256-column tiles where the format has them (256 x 256,
+// else 128 x 256), then 256 x 128 tiles on 8 waves; smaller ones 128 x 128
+// tiles with K split across workgroups until the grid covers the chip.
 inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256, bool allow_wide = false) {
-    const int64_t tn = (Np + 127) / 128, nsteps = K / 128;
+    const int64_t tn = (Np + 127) / 128, nsteps = K / 128, tn2 = (Np + 255) / 256;
     TilePlan pl{128, 1, false};
-    if (allow_wide && ((M + 127) / 128) * ((Np + 255) / 256) >= 256) {
+    if (allow_wide && ((M + 255) / 256) * tn2 >= 256) {
+        pl.BM = 256;
+        pl.wide = true;
+        return pl;
+    }
+    if (allow_wide && ((M + 127) / 128) * tn2 >= 256) {
         pl.wide = true;
         return pl;
     }
@@ -785,10 +841,11 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
 // on 8 waves with two register-staged steps in flight.  bf16 A has no 256-row
 // variant (its row-sum MFMA needs a second accumulator set).
 constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16; }
-// fp16 A with 4-bit weights: 128 x 256 on 8 waves of 128 x 32 side by side,
-// so each weight strip is dequantised by one wave only (a 256 x 128 tile
-// dequantises it in two) and a step loads 48 KB instead of 80 KB (+6..12 % at
-// M = 2048..8192 over 256 x 128).
+// fp16 A with 4-bit weights: 8 waves side by side, each dequantising its own
+// weight strips once: 256 x 256 tiles of 256 x 32 waves with a single weight
+// stage (each dequantised fragment feeds 16 MFMAs; 13 % faster than 128 x 256
+// at M = 8192), or 128 x 256 tiles of 128 x 32 waves where 256 x 256 would not
+// cover the chip (a K step loads 48 KB instead of the 80 KB of 256 x 128).
 constexpr bool has_wide_tile(Fmt F) { return F == Fmt::WNA16_F16; }
 
 template <Fmt F>
@@ -800,8 +857,10 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
     } else {
         if constexpr (F == Fmt::W4A8_MX)  // 8-bit A: a 256-column tile still fits two LDS stages
             if (pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
-        if constexpr (has_wide_tile(F))
+        if constexpr (has_wide_tile(F)) {
+            if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
             if (pl.wide) return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
+        }
         if constexpr (has_big_tile(F))
             if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
         return launch_tile_kernel<F, 128, 128, 2, 4, 0>(p, st);

@@ -116,8 +116,9 @@ def test_dense_w4a16_zp_full_size(M):
 
 
 @pytest.mark.parametrize("M,N,K,zp", [(4000, 4100, 512, True), (4096, 4096, 1024, False), (1100, 16000, 256, True),
-                                      (8192, 2056, 384, True)])
+                                      (8192, 2056, 384, True), (2000, 4100, 384, True), (2048, 4096, 512, False)])
 def test_wide_tiles_ragged(M, N, K, zp):
-    """Grids large enough for 256 x 256 tiles, with ragged last row and column tiles."""
+    """Grids large enough for 256-column tiles (256 x 256 from about 256 tiles of
+    that size, else 128 x 256), with ragged last row and column tiles."""
     Dr, O = run_wna16(M, N, K, 128, bf16=False, zp=zp, seed=M + N)
     check(Dr, O, False)
