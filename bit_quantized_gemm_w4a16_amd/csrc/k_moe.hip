@@ -447,11 +447,15 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // experts with more than kMoeMidMax rows: 256-column tiles of 8 waves side by
+    // side (each wave decodes its weight strips once; the 256-row tile keeps one
+    // weight LDS stage and feeds each decoded fragment to 16 MFMAs)
+    p.tiles_n = (int)cdiv(a.Np, 256);
     p.tiles_m = (int)L.max_tier[2];
     p.tile_info = tl[2];
     p.ntiles = ntiles + 2;
     if (p.tiles_m > 0) {
-        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeBM, 128, 2, 4, 0>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeBM, 256, 1, 8, 0>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
                            dim3(512), 0, a.stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -460,7 +464,7 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     p.tile_info = tl[3];
     p.ntiles = ntiles + 3;
     if (p.tiles_m > 0) {
-        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeHugeBM, 128, 2, 4, 0>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeHugeBM, 256, 1, 8, 3>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
                            dim3(512), 0, a.stream, p);
         e = hipGetLastError();
     }

@@ -424,24 +424,37 @@ void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
             for (int h = 0; h < NBH; ++h) bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
 
-        if constexpr (F == Fmt::WNA16_F16) {
+        if constexpr (F == Fmt::WNA16_F16 || F == Fmt::MOE_MX) {
+            // 16-bit A with 4-bit weights decoded into the operand: fp16 (q - z) * s,
+            // or MXFP4 e2m1 x 2^(E-127) -> bf16 (exact)
+            constexpr bool MOE = F == Fmt::MOE_MX;
             // A fragments read ahead (software pipeline): a whole sub-step, or
             // a ring of three for tall / wide wave tiles
             Frag8 afr[(NT >= 4 || MT > 8) ? 1 : 2][(NT >= 4 || MT > 8) ? 3 : MT];
-            Frag8 bq[2][NT];                  // dequantised weights of two sub-steps
+            Frag8 bq[2][NT];                  // decoded weights of two sub-steps
             uint32_t s2[NT], nb2[NT], nh2[NT];
+            float sf[NT];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                // one lane offset for every strip (strips are immediate offsets); the
-                // zero-point select is branch-free (symmetric INT4: z = 8)
-                const uint32_t sc = *(const uint16_t*)(sS + sc_lane + j * 32);
-                const uint32_t zw = *(const uint32_t*)(sS + SC_Z + z_lane + j * 8);
-                const uint32_t z = ((zw >> zshift) & zmask) | zsym;
-                s2[j] = sc | (sc << 16);
-                const uint32_t nbz = 0xE400u | z, nhz = 0xD400u | (z << 4);  // -(1024 + z), -(64 + z)
-                nb2[j] = nbz | (nbz << 16);
-                nh2[j] = nhz | (nhz << 16);
+                if constexpr (MOE) {
+                    sf[j] = e8m0_to_f32(((const uint8_t*)sS)[(wn * NT + j) * 64 + lane]);
+                } else {
+                    // one lane offset for every strip (strips are immediate offsets); the
+                    // zero-point select is branch-free (symmetric INT4: z = 8)
+                    const uint32_t sc = *(const uint16_t*)(sS + sc_lane + j * 32);
+                    const uint32_t zw = *(const uint32_t*)(sS + SC_Z + z_lane + j * 8);
+                    const uint32_t z = ((zw >> zshift) & zmask) | zsym;
+                    s2[j] = sc | (sc << 16);
+                    const uint32_t nbz = 0xE400u | z, nhz = 0xD400u | (z << 4);  // -(1024 + z), -(64 + z)
+                    nb2[j] = nbz | (nbz << 16);
+                    nh2[j] = nhz | (nhz << 16);
+                }
             }
+            // weight operand of strip j for K sub-step t
+            auto mkb = [&](int j, int tt) -> Frag8 {
+                if constexpr (MOE) return fp4_to_bf16(bw[j][0][tt], sf[j]);
+                else return deq4_f16_scaled(bw[j][0][tt] ^ wx, nb2[j], nh2[j], s2[j]);
+            };
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 hook(t);
@@ -456,7 +469,7 @@ void tile_gemm_kernel(TileArgs p) {
                         afr[0][0].u = *(const v4u*)(sA + a_frag[0]);
                         afr[0][1].u = *(const v4u*)(sA + a_frag[0] + 16 * AROW);
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) bq[0][j] = deq4_f16_scaled(bw[j][0][0] ^ wx, nb2[j], nh2[j], s2[j]);
+                        for (int j = 0; j < NT; ++j) bq[0][j] = mkb(j, 0);
                     }
 #pragma unroll
                     for (int i = 0; i < MT; ++i) {
@@ -464,10 +477,10 @@ void tile_gemm_kernel(TileArgs p) {
                         if (q + 2 < NQ)
                             afr[0][(q + 2) % 3].u = *(const v4u*)(sA + a_frag[(q + 2) / MT] + ((q + 2) % MT) * 16 * AROW);
                         if (t < 3 && i < NT)
-                            bq[(t + 1) & 1][i] = deq4_f16_scaled(bw[i][0][t + 1] ^ wx, nb2[i], nh2[i], s2[i]);
+                            bq[(t + 1) & 1][i] = mkb(i, t + 1);
                         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<false>(afr[0][q % 3], bq[t & 1][j], acc[i][j]);
+                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<MOE>(afr[0][q % 3], bq[t & 1][j], acc[i][j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 } else {
@@ -479,7 +492,7 @@ void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
                         for (int i = 0; i < MT; ++i) afr[0][i].u = *(const v4u*)(sA + a_frag[0] + i * 16 * AROW);
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) bq[0][j] = deq4_f16_scaled(bw[j][0][0] ^ wx, nb2[j], nh2[j], s2[j]);
+                        for (int j = 0; j < NT; ++j) bq[0][j] = mkb(j, 0);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     if (t < 3) {
@@ -487,12 +500,12 @@ void tile_gemm_kernel(TileArgs p) {
                         for (int i = 0; i < MT; ++i) afr[(t + 1) & 1][i].u = *(const v4u*)(sA + a_frag[t + 1] + i * 16 * AROW);
 #pragma unroll
                         for (int j = 0; j < NT; ++j)
-                            bq[(t + 1) & 1][j] = deq4_f16_scaled(bw[j][0][t + 1] ^ wx, nb2[j], nh2[j], s2[j]);
+                            bq[(t + 1) & 1][j] = mkb(j, t + 1);
                     }
 #pragma unroll
                     for (int i = 0; i < MT; ++i)
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<false>(afr[t & 1][i], bq[t & 1][j], acc[i][j]);
+                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<MOE>(afr[t & 1][i], bq[t & 1][j], acc[i][j]);
                     if (t < 3) {
                         // per A fragment: its read, the MFMAs of one fragment of
                         // this sub-step, a share of the next sub-step's dequant
@@ -581,26 +594,6 @@ void tile_gemm_kernel(TileArgs p) {
                     for (int j = 0; j < NT; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a), __builtin_bit_cast(v4i, bw[j][h]), acc[i][j], 0, 0, 0);
                 }
-        } else {  // MOE_MX
-#pragma unroll
-            for (int t = 0; t < 4; ++t) hook(t);
-            float sf[NT];
-#pragma unroll
-            for (int j = 0; j < NT; ++j) sf[j] = e8m0_to_f32(((const uint8_t*)sS)[(wn * NT + j) * 64 + lane]);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                Frag8 b[NT];
-#pragma unroll
-                for (int j = 0; j < NT; ++j) b[j] = fp4_to_bf16(bw[j][0][t], sf[j]);
-#pragma unroll
-                for (int i = 0; i < MT; ++i) {
-                    const int row = wm * (BM / WM) + i * 16 + col;
-                    Frag8 a;
-                    a.u = *(const v4u*)(sA + row * AROW + (((4 * quad + t) ^ swz(row, AUNITS)) * 16));
-#pragma unroll
-                    for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<true>(a, b[j], acc[i][j]);
-                }
-            }
         }
     };
 
