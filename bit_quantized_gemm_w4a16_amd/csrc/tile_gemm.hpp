@@ -785,15 +785,15 @@ struct TilePlan {
 // The largest grids use 256-column tiles where the format has them (256 x 256,
 // else 128 x 256), then 256 x 128 tiles on 8 waves; smaller ones 128 x 128
 // tiles with K split across workgroups until the grid covers the chip.
-inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256, bool allow_wide = false) {
+inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256, bool wide256 = false, bool wide128 = false) {
     const int64_t tn = (Np + 127) / 128, nsteps = K / 128, tn2 = (Np + 255) / 256;
     TilePlan pl{128, 1, false};
-    if (allow_wide && ((M + 255) / 256) * tn2 >= 256) {
+    if (wide256 && ((M + 255) / 256) * tn2 >= 256) {
         pl.BM = 256;
         pl.wide = true;
         return pl;
     }
-    if (allow_wide && ((M + 127) / 128) * tn2 >= 256) {
+    if (wide128 && ((M + 127) / 128) * tn2 >= 256) {
         pl.wide = true;
         return pl;
     }
@@ -830,9 +830,8 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
 // waves of 128 x 32 (two per SIMD, so one wave's LDS reads and dequantisation
 // overlap the other's MFMAs), loads straight into LDS (no staging registers).
 // W4A8 (8-bit A, no dequantisation): 256 x 256 on 8 waves of 128 x 64, which
-// halves the A traffic per flop and still fits two LDS stages.  INT8: 256 x 128
-// on 8 waves with two register-staged steps in flight.  bf16 A has no 256-row
-// variant (its row-sum MFMA needs a second accumulator set).
+// halves the A traffic per flop and still fits two LDS stages.  bf16 A has no
+// 256-row variant (its row-sum MFMA needs a second accumulator set).
 constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16; }
 // fp16 A with 4-bit weights: 8 waves side by side, each dequantising its own
 // weight strips once: 256 x 256 tiles of 256 x 32 waves with a single weight
@@ -840,12 +839,17 @@ constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16; }
 // at M = 8192), or 128 x 256 tiles of 128 x 32 waves where 256 x 256 would not
 // cover the chip (a K step loads 48 KB instead of the 80 KB of 256 x 128).
 constexpr bool has_wide_tile(Fmt F) { return F == Fmt::WNA16_F16; }
+// INT8: 256 x 256 on 8 waves of 128 x 64, direct loads into two full stages
+// (M = 8192: 1126 us vs 1569 us for 256 x 128 with register-staged loads); the
+// 256 x 128 tile also loads directly (1498 us).
+constexpr bool has_wide256_tile(Fmt F) { return F == Fmt::WNA16_F16 || F == Fmt::W8A8_I8; }
 
 template <Fmt F>
 hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
     p.splits = pl.splits;
     if constexpr (F == Fmt::W8A8_I8) {
-        if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 2>(p, st);
+        if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
+        if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
         return launch_tile_kernel<F, 128, 128, 2, 4, 2>(p, st);
     } else {
         if constexpr (F == Fmt::W4A8_MX)  // 8-bit A: a 256-column tile still fits two LDS stages

@@ -139,3 +139,11 @@ def test_w8a8_full_size(M):
     np.testing.assert_array_equal(got.astype(np.int64), acc)
     got, O = run_w8a8(M, 18432, 7168, seed=0)
     assert gate_error(got, O) <= 8e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(1100, 16400, 256), (600, 11000, 384)])
+def test_w8a8_raw_int32_big_tiles_ragged(M, N, K):
+    """Grids of 256 x 256 (first shape) and 256 x 128 (second) INT8 tiles with
+    ragged last row and column tiles: raw int32 accumulators bit-exact."""
+    got, acc = run_w8a8(M, N, K, seed=M, raw=True)
+    np.testing.assert_array_equal(got.astype(np.int64), acc)
