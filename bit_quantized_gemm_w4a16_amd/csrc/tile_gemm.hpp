@@ -284,14 +284,15 @@ void tile_gemm_kernel(TileArgs p) {
     }
     auto a_voff = [&](int i) -> uint32_t { return AFLAT ? aoff[0] : aoff[i]; };
     auto a_soff = [&](int i, int ks) -> uint32_t { return (AFLAT ? (uint32_t)i * arow_stride : 0u) + (uint32_t)ks * AROW; };
-    uint32_t boff[NIB > 0 ? NIB : 1];
-#pragma unroll
-    for (int i = 0; i < NIB; ++i) {
-        const int s = i * NTH + tid;
-        constexpr int UPS = T::BSTRIP / 16;
-        const int strip = clamp_strip(strip0 + s / UPS);
-        boff[i] = (uint32_t)strip * (uint32_t)nsteps * T::BSTRIP + (s % UPS) * 16;
-    }
+    // weight loads: one lane offset, load i adding i * NTH / UPS strips as a
+    // wave-uniform offset.  Strips past the packed width (a ragged last column
+    // tile) fall outside the buffer resource and read zeros: the range check
+    // covers the scalar offset too (checked on gfx950), and those columns are
+    // never stored.
+    constexpr int UPS = T::BSTRIP / 16;  // 16-byte units per strip and step
+    static_assert(NTH % UPS == 0, "a load instruction covers whole strips");
+    const uint32_t boff0 = (uint32_t)(strip0 + tid / UPS) * (uint32_t)nsteps * T::BSTRIP + (uint32_t)(tid % UPS) * 16u;
+    const uint32_t bstride = (uint32_t)(NTH / UPS) * (uint32_t)nsteps * T::BSTRIP;
     const uint32_t sc_strip = (uint32_t)clamp_strip(strip0 + (WNA16 ? (tid < 2 * NSTRIP ? tid / 2 : tid - 2 * NSTRIP) : tid / 4));
     const uint32_t soff = WNA16 ? (tid < 2 * NSTRIP ? sc_strip * p.ngroups * 32u + (tid & 1) * 16u : sc_strip * p.ngroups * 8u)
                                 : sc_strip * (uint32_t)nsteps * 64u + (tid & 3) * 16u;
@@ -329,7 +330,7 @@ void tile_gemm_kernel(TileArgs p) {
         lds_char* sB = B1 ? (lds_char*)bstage : stage_lds(stc) + A_STAGE;
 #pragma unroll
         for (int i = 0; i < NIB; ++i)
-            dma16_nt(rW, sB + i * NTH * 16 + wbase, boff[i], (uint32_t)ks * T::BSTRIP);
+            dma16_nt(rW, sB + i * NTH * 16 + wbase, boff0, (uint32_t)i * bstride + (uint32_t)ks * T::BSTRIP);
     };
     auto dma = [&](int ks, auto stc) {
         dma_a(ks, stc);
@@ -375,7 +376,7 @@ void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
         for (int i = 0; i < NIA; ++i) ra[st][i] = buf16(rA, a_voff(i), a_soff(i, ks));
 #pragma unroll
-        for (int i = 0; i < NIB; ++i) rb[st][i] = buf16<true>(rW, boff[i], (uint32_t)ks * T::BSTRIP);
+        for (int i = 0; i < NIB; ++i) rb[st][i] = buf16<true>(rW, boff0, (uint32_t)i * bstride + (uint32_t)ks * T::BSTRIP);
         sc_load(ks, setc);
     };
     auto swrite = [&](auto stc, auto setc) {
@@ -582,18 +583,32 @@ void tile_gemm_kernel(TileArgs p) {
                 }
             }
         } else if constexpr (F == Fmt::W8A8_I8) {
+            // A fragment (h, i): 16 bytes per lane, unit 4h + quad of the lane's row
+            // (rows of a wave's tiles differ by multiples of 16, so the swizzle
+            // depends on the lane's column only), streamed through a ring of four,
+            // three fragments ahead of its MFMAs
+            const int sw8 = swz(col, AUNITS);
+            const uint32_t a_h[2] = {(uint32_t)((wm * (BM / WM) + col) * AROW + ((quad ^ sw8) * 16)),
+                                     (uint32_t)((wm * (BM / WM) + col) * AROW + (((4 + quad) ^ sw8) * 16))};
+            constexpr int NQ = 2 * MT;
+            auto rdA = [&](int q) -> v4u { return *(const v4u*)(sA + a_h[q / MT] + (q % MT) * 16 * AROW); };
+            v4u ar[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) hook(t);
+            for (int q = 0; q < 3 && q < NQ; ++q) ar[q] = rdA(q);
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int q = 0; q < NQ; ++q) {
+                const int h = q / MT, i = q % MT;
+                if (q == 0) {
 #pragma unroll
-                for (int i = 0; i < MT; ++i) {
-                    const int row = wm * (BM / WM) + i * 16 + col;
-                    const v4u a = *(const v4u*)(sA + row * AROW + (((4 * h + quad) ^ swz(row, AUNITS)) * 16));
-#pragma unroll
-                    for (int j = 0; j < NT; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a), __builtin_bit_cast(v4i, bw[j][h]), acc[i][j], 0, 0, 0);
+                    for (int t = 0; t < 4; ++t) hook(t);
                 }
+                if (q + 3 < NQ) ar[(q + 3) % 4] = rdA(q + 3);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, ar[q % 4]), __builtin_bit_cast(v4i, bw[j][h]), acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
