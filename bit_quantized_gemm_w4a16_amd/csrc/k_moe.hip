@@ -345,26 +345,89 @@ hipError_t moe_gather_launch(const void* A, const int* sorted, int64_t P, int to
     return hipGetLastError();
 }
 
+// Weight-streaming launch of the MoE kernel: each m-tile's A rows (at most
+// `rows`) sit in LDS for all of K, with the tile's E8M0 block; at least the
+// K-part reduction buffer (3 waves x 16 x 16 fp32).
+static int moe_small_lds(int rows, int nc) {
+    const int s_off = (int)(cdiv((int64_t)rows * nc * 256, 1024) * 1024);
+    const int lds = s_off + (int)(cdiv((int64_t)nc * 64, 1024) * 1024);
+    return lds > 3 * 1024 ? lds : 3 * 1024;
+}
+
+static SkinnyArgs moe_skinny_args(const MoeArgs& a, int64_t P, int nc, int rows) {
+    SkinnyArgs s{};
+    s.A = a.A;
+    s.W = a.w;
+    s.S = a.s;
+    s.D = a.D;
+    s.w_estride = a.w_estride;
+    s.s_estride = a.s_estride;
+    s.M = (int)P;
+    s.K = (int)a.K;
+    s.N = (int)a.N;
+    s.Np = (int)a.Np;
+    s.nc = nc;
+    s.ngroups = 1;
+    s.gchunks = 1;
+    s.splits = 1;
+    s.cps = nc;
+    s.cpk = (int)cdiv(nc, 4);
+    s.NS = 1;
+    s.WS = 1;
+    s.a_off = 0;
+    s.s_off = (int)(cdiv((int64_t)rows * nc * 256, 1024) * 1024);
+    s.z_off = s.s_off;
+    s.top_k = a.top_k;
+    return s;
+}
+
+static hipError_t moe_skinny_launch(const SkinnyArgs& s, int lds, int64_t gy, hipStream_t st) {
+    const dim3 grid((unsigned)(s.Np / 16), (unsigned)(gy > 0 ? gy : 1));
+    return launch_skinny_cpw<Fmt::MOE_MX, 1, 1>(s.cpk <= 2 ? 2 : s.cpk <= 4 ? 4 : s.cpk <= 8 ? 8 : 16, grid, lds, s, st);
+}
+
+// Fewer than kMoeSmallRows tokens (so at most kMoeAllSmallP pairs): one launch
+// of the weight-streaming kernel, whose workgroups each build the m-tile list
+// from the ids or offsets (no routing pass).  A token picks an expert at most
+// once, so an expert has at most T rows: tiles of T rows cover each expert
+// once and the A rows held in LDS shrink with T, which leaves room for more
+// workgroups per CU.  (Tiles never exceed T rows whatever the ids, so repeated
+// ids only cost extra tiles.)  From kMoeSmallRows tokens on, the LDS no longer
+// shrinks and a routing pass of its own measured faster than every workgroup
+// building the list.
+static_assert(kMoeAllSmallP <= kRouteMaxP, "the in-kernel routing handles one pair per lane");
+static hipError_t moe_all_small_launch(const MoeArgs& a, int64_t P, int nc) {
+    const int cap = (int)a.T;
+    SkinnyArgs s = moe_skinny_args(a, P, nc, cap);
+    s.route_ids = a.indexed ? a.topk_ids : nullptr;
+    s.route_off = a.indexed ? nullptr : a.expert_offsets;
+    s.route_P = (int)P;
+    s.route_E = a.E;
+    s.route_cap = cap;
+    // every tile holds a row, so at most P tiles
+    return moe_skinny_launch(s, moe_small_lds(cap, nc), P < kMoeSmallGridY ? P : kMoeSmallGridY, a.stream);
+}
+
 // Experts with few rows (the common case below a few thousand tokens) run on
 // the weight-streaming kernel in m-tiles of kMoeSmallRows rows: their
 // weights are read once per m-tile without padding the tile to 128 rows.
 // Experts with more rows run on the tiled MFMA kernel.
 hipError_t moe_gemm_launch(const MoeArgs& a) {
     const int64_t P = a.T * a.top_k;
+    // The weight-streaming path holds a tile's A rows for all of K in LDS and a
+    // wave's quarter of K in registers; a larger K sends its experts to the mid tier.
+    const int nc = (int)(a.K / 128);
+    const int lds = moe_small_lds(kMoeSmallRows, nc);
+    const bool small_ok = cdiv(nc, 4) <= 16 && lds <= kSkinnyLds;
+    // With few pairs in total no expert can fill a tile: every expert takes the
+    // streaming path (several m-tiles if it must) and no tiled launch is made.
+    const bool all_small = small_ok && P <= kMoeAllSmallP;
+    if (all_small && a.T < kMoeSmallRows) return moe_all_small_launch(a, P, nc);
     MoeLayout L = moe_layout(a.T, a.top_k, a.E, a.indexed);
     char* ws = (char*)a.ws;
     int* ntiles = (int*)(ws + L.ntiles);
     int* tl[4];
     for (int i = 0; i < 4; ++i) tl[i] = (int*)(ws + L.tiles_tier[i]);
-    // The weight-streaming path holds a tile's A rows for all of K in LDS and a
-    // wave's quarter of K in registers; a larger K sends its experts to the mid tier.
-    const int nc = (int)(a.K / 128);
-    const int s_off = (int)(cdiv((int64_t)kMoeSmallRows * nc * 256, 1024) * 1024);
-    const int lds = s_off + (int)(cdiv((int64_t)nc * 64, 1024) * 1024);
-    const bool small_ok = cdiv(nc, 4) <= 16 && lds <= kSkinnyLds;
-    // With few pairs in total no expert can fill a tile: every expert takes the
-    // streaming path (several 4-row m-tiles if it must) and no tiled launch is made.
-    const bool all_small = small_ok && P <= kMoeAllSmallP;
     MoeTiers tiers{};
     tiers.t[0] = TileList{tl[0], ntiles + 0, (int)L.max_tier[0], kMoeSmallRows,
                           all_small ? (1 << 30) : small_ok ? kMoeSmallRows : 0};
@@ -387,35 +450,11 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     }
     // tier 0 (at most kMoeSmallRows rows): weight-streaming kernel, persistent over its m-tiles
     if (small_ok) {
-        SkinnyArgs s{};
-        s.A = a.A;
-        s.W = a.w;
-        s.S = a.s;
-        s.D = a.D;
-        s.w_estride = a.w_estride;
-        s.s_estride = a.s_estride;
-        s.M = (int)P;
-        s.K = (int)a.K;
-        s.N = (int)a.N;
-        s.Np = (int)a.Np;
-        s.nc = nc;
-        s.ngroups = 1;
-        s.gchunks = 1;
-        s.splits = 1;
-        s.cps = nc;
-        s.cpk = (int)cdiv(nc, 4);
-        s.NS = 1;
-        s.WS = 1;
-        s.a_off = 0;
-        s.s_off = s_off;
-        s.z_off = s_off;
+        SkinnyArgs s = moe_skinny_args(a, P, nc, kMoeSmallRows);
         s.tile_info = tl[0];
         s.ntiles = ntiles + 0;
         s.sorted = sorted;
-        s.top_k = a.top_k;
-        const int64_t gy = L.max_tier[0] < kMoeSmallGridY ? L.max_tier[0] : kMoeSmallGridY;
-        const dim3 grid((unsigned)(a.Np / 16), (unsigned)(gy > 0 ? gy : 1));
-        e = launch_skinny_cpw<Fmt::MOE_MX, 1, 1>(s.cpk <= 2 ? 2 : s.cpk <= 4 ? 4 : s.cpk <= 8 ? 8 : 16, grid, lds, s, a.stream);
+        e = moe_skinny_launch(s, lds, L.max_tier[0] < kMoeSmallGridY ? L.max_tier[0] : kMoeSmallGridY, a.stream);
         if (e != hipSuccess) return e;
     }
     // tiers 1 and 2: tiled MFMA kernel over m-tiles of kMoeMidBM / kMoeBM rows

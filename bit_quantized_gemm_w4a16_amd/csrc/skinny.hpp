@@ -68,7 +68,14 @@ struct SkinnyArgs {
     const int* ntiles;
     const int* sorted;      // Indexed: sorted pair ids; Grouped: null
     int top_k;
+    // MoE with at most kRouteMaxP pairs: instead of tile_info / ntiles / sorted,
+    // every workgroup derives the m-tile list itself from the top-k ids
+    // (Indexed) or the expert offsets (Grouped), in tiles of at most route_cap rows
+    const int* route_ids;
+    const int* route_off;
+    int route_P, route_E, route_cap;
 };
+constexpr int kRouteMaxP = 64;  // one pair (or sorted row) per lane of a wave
 
 template <Fmt F>
 struct SkinnyTraits {
@@ -90,7 +97,8 @@ __device__ __forceinline__ int skinny_swz(int row) {
 // One work item: K slice `item` of a dense launch, or m-tile `item` of a MoE
 // launch.  Every thread of the workgroup calls it (it holds barriers).
 template <Fmt F, int MT, int SPW, int CPW>
-__device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char* lds, int* rowinfo) {
+__device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char* lds, int* rowinfo,
+                                            const int* tile_info, const int* sorted) {
     using Tr = SkinnyTraits<F>;
     using Acc = typename FmtTraits<F>::Acc;
     constexpr bool WNA16 = Tr::WNA16, MX = Tr::MX, MOE = F == Fmt::MOE_MX;
@@ -112,9 +120,9 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
     int split = 0, rows = p.M, first = 0;
     if constexpr (MOE) {
         const int t = item;
-        const int e = p.tile_info[3 * t];
-        first = p.tile_info[3 * t + 1];
-        rows = p.tile_info[3 * t + 2];
+        const int e = tile_info[3 * t];
+        first = tile_info[3 * t + 1];
+        rows = tile_info[3 * t + 2];
         Wb += (int64_t)e * p.w_estride;
         Sb += (int64_t)e * p.s_estride;
     } else {
@@ -132,8 +140,8 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
         int arow = rr, drow = r < rows ? r : -1;
         if constexpr (MOE) {
             const int pos = first + rr;
-            const int pair = p.sorted ? p.sorted[pos] : pos;
-            arow = p.sorted ? pair / p.top_k : pos;
+            const int pair = sorted ? sorted[pos] : pos;
+            arow = sorted ? pair / p.top_k : pos;
             drow = r < rows ? pair : -1;
         }
         rowinfo[r] = arow;
@@ -472,19 +480,101 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
     }
 }
 
+// The m-tile list of a MoE launch with at most kRouteMaxP pairs, built by
+// every workgroup in LDS (one launch less than a routing pass of its own).
+// Rows of the expert-sorted order carry their expert (or -1), their rank
+// among the expert's rows and the expert's row count; a tile starts at every
+// row whose rank is a multiple of route_cap and holds the next
+// min(route_cap, count - rank) rows.  Indexed: pairs are sorted stably by
+// expert (rank = equal ids before the pair), ids outside [0, E) are dropped.
+// Grouped: row i belongs to the expert whose clamped offset range holds it.
+// Returns the tile count (at most kRouteMaxP: every tile holds a row).  All
+// threads of the workgroup call it.
+__device__ __forceinline__ int moe_route_inline(const SkinnyArgs& p, int* tile, int* srt, int* rexp, int* rrank,
+                                                int* key, int* ntl) {
+    const int tid = threadIdx.x, P = p.route_P, E = p.route_E, cap = p.route_cap;
+    int id = -1;
+    if (p.route_ids && tid < P) {
+        const int v = p.route_ids[tid];
+        id = v >= 0 && v < E ? v : -1;
+    }
+    if (tid < kRouteMaxP) {
+        rexp[tid] = -1;
+        key[tid] = id;  // the pair's expert, read back by every pair below
+    }
+    __syncthreads();
+    if (p.route_ids) {
+        if (id >= 0) {
+            int pos = 0, rank = 0, cnt = 0;
+            for (int j = 0; j < P; ++j) {
+                const int v = key[j];
+                pos += (v >= 0 && (v < id || (v == id && j < tid))) ? 1 : 0;
+                rank += (v == id && j < tid) ? 1 : 0;
+                cnt += v == id ? 1 : 0;
+            }
+            srt[pos] = tid;
+            rexp[pos] = id;
+            rrank[pos] = rank | (cnt << 8);  // rank and count (both at most kRouteMaxP)
+        }
+    } else {
+        for (int e = tid; e < E; e += blockDim.x) {
+            const int lo = min(max(p.route_off[e], 0), P), hi = min(max(p.route_off[e + 1], lo), P);
+            for (int i = lo; i < hi; ++i) rexp[i] = e;  // overlapping ranges (malformed offsets): one owner wins
+        }
+    }
+    __syncthreads();
+    if (tid < kRouteMaxP) {  // wave 0: lane = row of the sorted order
+        const int i = tid;
+        const int e = i < P ? rexp[i] : -1;
+        int rank = 0, cnt = 0;
+        if (e >= 0) {
+            if (p.route_ids) {
+                rank = rrank[i] & 255;
+                cnt = rrank[i] >> 8;
+            } else {
+                const int lo = min(max(p.route_off[e], 0), P), hi = min(max(p.route_off[e + 1], lo), P);
+                rank = i - lo;
+                cnt = hi - lo;
+            }
+        }
+        const bool start = e >= 0 && rank % cap == 0;
+        const unsigned long long bal = __ballot(start);
+        const int t = __popcll(bal & ((1ull << i) - 1ull));
+        if (start) {
+            tile[3 * t] = e;
+            tile[3 * t + 1] = i;
+            tile[3 * t + 2] = min(cap, cnt - rank);
+        }
+        if (i == 0) *ntl = __popcll(bal);
+    }
+    __syncthreads();
+    return *ntl;
+}
+
 template <Fmt F, int MT, int SPW, int CPW>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];  // sized per launch (plan.lds_bytes)
     __shared__ int rowinfo[2 * 16 * MT];  // [0,ROWS): A row of each local row; [ROWS,2ROWS): D row or -1
     if constexpr (F == Fmt::MOE_MX) {
-        // persistent over the device-built m-tile list (its length is known only here)
-        const int nt = *p.ntiles;
+        // persistent over the m-tile list (its length is known only here)
+        const int* tinfo = p.tile_info;
+        const int* srt = p.sorted;
+        int nt;
+        if (p.route_ids || p.route_off) {
+            __shared__ int rt_tile[3 * kRouteMaxP], rt_srt[kRouteMaxP], rt_exp[kRouteMaxP], rt_rank[kRouteMaxP],
+                rt_tmp[kRouteMaxP], rt_n;
+            nt = moe_route_inline(p, rt_tile, rt_srt, rt_exp, rt_rank, rt_tmp, &rt_n);
+            tinfo = rt_tile;
+            srt = p.route_ids ? rt_srt : nullptr;
+        } else {
+            nt = *p.ntiles;
+        }
         for (int t = blockIdx.y; t < nt; t += gridDim.y) {
-            skinny_item<F, MT, SPW, CPW>(p, t, lds, rowinfo);
+            skinny_item<F, MT, SPW, CPW>(p, t, lds, rowinfo, tinfo, srt);
             __syncthreads();  // the next tile reuses LDS
         }
     } else {
-        skinny_item<F, MT, SPW, CPW>(p, blockIdx.y, lds, rowinfo);
+        skinny_item<F, MT, SPW, CPW>(p, blockIdx.y, lds, rowinfo, nullptr, nullptr);
     }
 }
 

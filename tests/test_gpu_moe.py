@@ -87,9 +87,18 @@ def check(out):
         assert err <= min(GATE, 8e-3), (mode, err)
 
 
-@pytest.mark.parametrize("T", [1, 2, 5, 33, 300])
+@pytest.mark.parametrize("T", [1, 2, 5, 32, 33, 300])
 def test_moe_small(T):
     check(run_moe(T, 8, 2, 272, 512, seed=T))
+
+
+@pytest.mark.parametrize("T,E,top_k", [(1, 64, 64), (2, 3, 2), (3, 40, 8), (16, 4, 4), (64, 3, 1)])
+def test_moe_small_pair_counts(T, E, top_k):
+    """At most 64 pairs.  Below 4 tokens the streaming kernel builds its tile
+    list itself: 64 one-row tiles (the list's limit), two-row tiles, three-row
+    tiles.  From 4 tokens on, every expert still takes the streaming kernel,
+    several 4-row tiles per busy expert."""
+    check(run_moe(T, E, top_k, 160, 256, seed=T + E))
 
 
 def test_moe_one_hot_expert_and_empty_experts():
@@ -110,7 +119,7 @@ def test_moe_single_expert_top1_equals_dense():
     check(run_moe(T, E, 1, N, K, seed=9))
 
 
-@pytest.mark.parametrize("T", [1, 64, 8192])
+@pytest.mark.parametrize("T", [1, 8, 64, 8192])
 def test_moe_full_size_sampled(T):
     """The MoE workload: E=256, top-8, N=4096, K=7168, Zipf(1.1) routing; sampled pairs."""
     E, top_k, N, K = 256, 8, 4096, 7168
