@@ -14,7 +14,7 @@
 // m-tile list, then the scatter.
 #include "hq_device.hpp"
 #include "hq_internal.h"
-#include "skinny.hpp"
+#include "moe_stream.hpp"
 
 namespace hq {
 
@@ -28,7 +28,7 @@ constexpr int kMoeBM = 128;     // rows per m-tile of the tiled expert GEMM
 // efficient tile.
 constexpr int kMoeSmallRows = 4;
 constexpr int kMoeAllSmallP = 64;  // at most this many pairs: every expert on the streaming path
-constexpr int kMoeSmallGridY = 32;  // workgroups per strip walking the tier-0 m-tiles
+constexpr int kMoeSmallGridY = 32;  // workgroup rows walking the tier-0 m-tiles
 constexpr int kMoeMidBM = 32;
 constexpr int kMoeMidMax = 64;
 constexpr int kMoeBigMax = 256;  // up to this many rows: kMoeBM-row tiles; beyond: kMoeHugeBM
@@ -345,45 +345,21 @@ hipError_t moe_gather_launch(const void* A, const int* sorted, int64_t P, int to
     return hipGetLastError();
 }
 
-// Weight-streaming launch of the MoE kernel: each m-tile's A rows (at most
-// `rows`) sit in LDS for all of K, with the tile's E8M0 block; at least the
-// K-part reduction buffer (3 waves x 16 x 16 fp32).
-static int moe_small_lds(int rows, int nc) {
-    const int s_off = (int)(cdiv((int64_t)rows * nc * 256, 1024) * 1024);
-    const int lds = s_off + (int)(cdiv((int64_t)nc * 64, 1024) * 1024);
-    return lds > 3 * 1024 ? lds : 3 * 1024;
-}
-
-static SkinnyArgs moe_skinny_args(const MoeArgs& a, int64_t P, int nc, int rows) {
-    SkinnyArgs s{};
+// Arguments of the MoE weight-streaming kernel.
+static MoeStreamArgs moe_stream_args(const MoeArgs& a, int nc) {
+    MoeStreamArgs s{};
     s.A = a.A;
     s.W = a.w;
     s.S = a.s;
     s.D = a.D;
     s.w_estride = a.w_estride;
     s.s_estride = a.s_estride;
-    s.M = (int)P;
     s.K = (int)a.K;
     s.N = (int)a.N;
     s.Np = (int)a.Np;
     s.nc = nc;
-    s.ngroups = 1;
-    s.gchunks = 1;
-    s.splits = 1;
-    s.cps = nc;
-    s.cpk = (int)cdiv(nc, 4);
-    s.NS = 1;
-    s.WS = 1;
-    s.a_off = 0;
-    s.s_off = (int)(cdiv((int64_t)rows * nc * 256, 1024) * 1024);
-    s.z_off = s.s_off;
     s.top_k = a.top_k;
     return s;
-}
-
-static hipError_t moe_skinny_launch(const SkinnyArgs& s, int lds, int64_t gy, hipStream_t st) {
-    const dim3 grid((unsigned)(s.Np / 16), (unsigned)(gy > 0 ? gy : 1));
-    return launch_skinny_cpw<Fmt::MOE_MX, 1, 1>(s.cpk <= 2 ? 2 : s.cpk <= 4 ? 4 : s.cpk <= 8 ? 8 : 16, grid, lds, s, st);
 }
 
 // Fewer than kMoeSmallRows tokens (so at most kMoeAllSmallP pairs): one launch
@@ -398,14 +374,14 @@ static hipError_t moe_skinny_launch(const SkinnyArgs& s, int lds, int64_t gy, hi
 static_assert(kMoeAllSmallP <= kRouteMaxP, "the in-kernel routing handles one pair per lane");
 static hipError_t moe_all_small_launch(const MoeArgs& a, int64_t P, int nc) {
     const int cap = (int)a.T;
-    SkinnyArgs s = moe_skinny_args(a, P, nc, cap);
+    MoeStreamArgs s = moe_stream_args(a, nc);
     s.route_ids = a.indexed ? a.topk_ids : nullptr;
     s.route_off = a.indexed ? nullptr : a.expert_offsets;
     s.route_P = (int)P;
     s.route_E = a.E;
     s.route_cap = cap;
     // every tile holds a row, so at most P tiles
-    return moe_skinny_launch(s, moe_small_lds(cap, nc), P < kMoeSmallGridY ? P : kMoeSmallGridY, a.stream);
+    return launch_moe_stream(s, cap, P < kMoeSmallGridY ? P : kMoeSmallGridY, a.stream);
 }
 
 // Experts with few rows (the common case below a few thousand tokens) run on
@@ -414,11 +390,10 @@ static hipError_t moe_all_small_launch(const MoeArgs& a, int64_t P, int nc) {
 // Experts with more rows run on the tiled MFMA kernel.
 hipError_t moe_gemm_launch(const MoeArgs& a) {
     const int64_t P = a.T * a.top_k;
-    // The weight-streaming path holds a tile's A rows for all of K in LDS and a
-    // wave's quarter of K in registers; a larger K sends its experts to the mid tier.
+    // The weight-streaming path holds a tile's A rows for all of K in LDS; a
+    // larger K sends its experts to the mid tier.
     const int nc = (int)(a.K / 128);
-    const int lds = moe_small_lds(kMoeSmallRows, nc);
-    const bool small_ok = cdiv(nc, 4) <= 16 && lds <= kSkinnyLds;
+    const bool small_ok = moe_stream_fits(nc) && (int64_t)kMoeSmallRows * nc * 256 <= kSkinnyLds;
     // With few pairs in total no expert can fill a tile: every expert takes the
     // streaming path (several m-tiles if it must) and no tiled launch is made.
     const bool all_small = small_ok && P <= kMoeAllSmallP;
@@ -450,11 +425,12 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     }
     // tier 0 (at most kMoeSmallRows rows): weight-streaming kernel, persistent over its m-tiles
     if (small_ok) {
-        SkinnyArgs s = moe_skinny_args(a, P, nc, kMoeSmallRows);
+        MoeStreamArgs s = moe_stream_args(a, nc);
         s.tile_info = tl[0];
         s.ntiles = ntiles + 0;
         s.sorted = sorted;
-        e = moe_skinny_launch(s, lds, L.max_tier[0] < kMoeSmallGridY ? L.max_tier[0] : kMoeSmallGridY, a.stream);
+        e = launch_moe_stream(s, kMoeSmallRows, L.max_tier[0] < kMoeSmallGridY ? L.max_tier[0] : kMoeSmallGridY,
+                              a.stream);
         if (e != hipSuccess) return e;
     }
     // tiers 1 and 2: tiled MFMA kernel over m-tiles of kMoeMidBM / kMoeBM rows

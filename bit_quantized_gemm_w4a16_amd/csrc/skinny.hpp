@@ -10,7 +10,7 @@
 // CDNA4.
 //
 // Workgroup = 4 waves over NS strips (16 output columns each) and one K slice
-// of 128-K chunks (one m-tile of an expert for MoE).  The waves split the
+// of 128-K chunks.  The waves split the
 // workgroup as WS strip-columns x WK K-parts; each wave owns SPW strips.
 //   1. The A rows of the slice and the slice's scales (group scales +
 //      zero-points, or E8M0 exponents) go to LDS with direct-to-LDS loads.
@@ -35,8 +35,6 @@
 //   W4A8_MX         1 x v_mfma_scale_f32_16x16x128_f8f6f4 (fp8 A, fp4 B with
 //                   the E8M0 exponent as the B scale)
 //   W8A8_I8         2 x v_mfma_i32_16x16x64_i8 (exact int32)
-//   MOE_MX          4 x v_mfma_f32_16x16x32_bf16 after the exact
-//                   e2m1 x 2^(E-127) -> bf16 conversion
 #pragma once
 
 #include "tile_gemm.hpp"
@@ -49,12 +47,11 @@ constexpr int64_t kSkinnyMaxM = 64;  // dense M handled by this schedule
 struct SkinnyArgs {
     const void* A;          // activations [a_rows][K]
     const float* a_scale;   // per-token fp32 (W4A8 / W8A8), by A row
-    const void* W;          // packed weights (expert 0 for MoE)
+    const void* W;          // packed weights
     const void* S;          // packed group scales / E8M0 / per-channel fp32
     const void* Z;          // packed zero-points (WNA16 with UINT4), or null
     void* D;                // output [rows][N]
     void* part;             // split-K partial tiles [splits][M][Np], or null
-    int64_t w_estride, s_estride;  // bytes between experts' packed W / scales
     int M, K, N, Np;
     int nc;                 // 128-K chunks in K
     int ngroups, gchunks;   // WNA16: K / G and G / 128
@@ -63,28 +60,15 @@ struct SkinnyArgs {
     int NS, WS;             // strips per workgroup, wave strip-columns (WK = 4 / WS)
     int a_off, s_off, z_off;  // LDS layout (bytes)
     int raw_i32;            // W8A8: store the int32 accumulators
-    // MoE: blockIdx.y walks the m-tile list (expert, first sorted row, rows)
-    const int* tile_info;
-    const int* ntiles;
-    const int* sorted;      // Indexed: sorted pair ids; Grouped: null
-    int top_k;
-    // MoE with at most kRouteMaxP pairs: instead of tile_info / ntiles / sorted,
-    // every workgroup derives the m-tile list itself from the top-k ids
-    // (Indexed) or the expert offsets (Grouped), in tiles of at most route_cap rows
-    const int* route_ids;
-    const int* route_off;
-    int route_P, route_E, route_cap;
 };
-constexpr int kRouteMaxP = 64;  // one pair (or sorted row) per lane of a wave
 
 template <Fmt F>
 struct SkinnyTraits {
     static constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
-    static constexpr bool MX = F == Fmt::W4A8_MX || F == Fmt::MOE_MX;
+    static constexpr bool MX = F == Fmt::W4A8_MX;
     static constexpr int AB = FmtTraits<F>::AB;        // bytes per activation
     static constexpr int UPC = 8 * AB;                  // 16-byte A units per 128-K chunk and row
     static constexpr int NB = FmtTraits<F>::BSTRIP / 1024;  // 16-byte weight loads per chunk and lane
-    static constexpr int MOE_ROWS = 8;                  // rows of a MoE m-tile on this path
 };
 
 // A unit u of LDS row r holds global unit u ^ skinny_swz(r): 16 consecutive
@@ -94,14 +78,14 @@ __device__ __forceinline__ int skinny_swz(int row) {
     return UPC == 16 ? (row & 15) : (row & 7);
 }
 
-// One work item: K slice `item` of a dense launch, or m-tile `item` of a MoE
-// launch.  Every thread of the workgroup calls it (it holds barriers).
+// One work item: K slice `split` of the launch.  Every thread of the
+// workgroup calls it (it holds barriers).
 template <Fmt F, int MT, int SPW, int CPW>
-__device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char* lds, int* rowinfo,
-                                            const int* tile_info, const int* sorted) {
+__device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char* lds, int* rowinfo) {
     using Tr = SkinnyTraits<F>;
     using Acc = typename FmtTraits<F>::Acc;
-    constexpr bool WNA16 = Tr::WNA16, MX = Tr::MX, MOE = F == Fmt::MOE_MX;
+    static_assert(F != Fmt::MOE_MX, "MoE experts stream through moe_stream_kernel");
+    constexpr bool WNA16 = Tr::WNA16, MX = Tr::MX;
     constexpr int AB = Tr::AB, UPC = Tr::UPC, NB = Tr::NB;
     constexpr int ROWS = 16 * MT;
     constexpr int NLOAD = SPW * CPW * NB;  // weight loads per wave and batch
@@ -114,20 +98,9 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
     const int nstrips = p.Np / 16;
     const int strip_base = blockIdx.x * p.NS;
 
-    // ---- m-tile (MoE) or K slice (dense) ----
     const char* Wb = (const char*)p.W;
     const char* Sb = (const char*)p.S;
-    int split = 0, rows = p.M, first = 0;
-    if constexpr (MOE) {
-        const int t = item;
-        const int e = tile_info[3 * t];
-        first = tile_info[3 * t + 1];
-        rows = tile_info[3 * t + 2];
-        Wb += (int64_t)e * p.w_estride;
-        Sb += (int64_t)e * p.s_estride;
-    } else {
-        split = item;
-    }
+    const int rows = p.M;
     // K slice [c0, c1) and this wave's part [cw0, cw1), in 128-K chunks (no division on the device)
     const int c0 = min(split * p.cps, p.nc), c1 = min(c0 + p.cps, p.nc);
     const int cw0 = min(c0 + wk * p.cpk, c1), cw1 = min(cw0 + p.cpk, c1);
@@ -136,16 +109,9 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
 
     // ---- local rows: A row and D row ----
     if (tid < ROWS) {
-        const int r = tid, rr = r < rows ? r : rows - 1;
-        int arow = rr, drow = r < rows ? r : -1;
-        if constexpr (MOE) {
-            const int pos = first + rr;
-            const int pair = sorted ? sorted[pos] : pos;
-            arow = sorted ? pair / p.top_k : pos;
-            drow = r < rows ? pair : -1;
-        }
-        rowinfo[r] = arow;
-        rowinfo[ROWS + r] = drow;
+        const int r = tid;
+        rowinfo[r] = r < rows ? r : rows - 1;
+        rowinfo[ROWS + r] = r < rows ? r : -1;
     }
     __syncthreads();  // no weight load is in flight yet, so this drains nothing
 
@@ -273,8 +239,6 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
             if constexpr (WNA16) {
                 sbb[S][sp] = ((const uint16_t*)(lds + p.s_off))[(j * gslab + gi[i]) * 16 + col];
                 zwb[S][sp] = ((const uint32_t*)(lds + p.z_off))[(j * gslab + gi[i]) * 2 + (col >> 3)];
-            } else if constexpr (F == Fmt::MOE_MX) {
-                sbb[S][sp] = ((const uint8_t*)(lds + p.s_off))[(j * nsl + cl) * 64 + lane];
             }
         }
     };
@@ -350,18 +314,6 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
                         }
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt) acc2[i & 1][sp][mt] += sc * (gacc[0][mt] + gacc[1][mt]);
-                    }
-                }
-            } else if constexpr (F == Fmt::MOE_MX) {
-                const Frag8(&af)[MT][4] = afb[i & 1];
-#pragma unroll
-                for (int sp = 0; sp < SPW; ++sp) {
-                    const float sf = valid ? e8m0_to_f32(sbb[i & 1][sp]) : 0.f;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const Frag8 b = fp4_to_bf16(w[i][sp][0][t], sf);
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) acc2[t & 1][sp][mt] = mfma16<true>(af[mt][t], b, acc2[t & 1][sp][mt]);
                     }
                 }
             } else if constexpr (F == Fmt::W4A8_MX) {
@@ -480,102 +432,11 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int item, char*
     }
 }
 
-// The m-tile list of a MoE launch with at most kRouteMaxP pairs, built by
-// every workgroup in LDS (one launch less than a routing pass of its own).
-// Rows of the expert-sorted order carry their expert (or -1), their rank
-// among the expert's rows and the expert's row count; a tile starts at every
-// row whose rank is a multiple of route_cap and holds the next
-// min(route_cap, count - rank) rows.  Indexed: pairs are sorted stably by
-// expert (rank = equal ids before the pair), ids outside [0, E) are dropped.
-// Grouped: row i belongs to the expert whose clamped offset range holds it.
-// Returns the tile count (at most kRouteMaxP: every tile holds a row).  All
-// threads of the workgroup call it.
-__device__ __forceinline__ int moe_route_inline(const SkinnyArgs& p, int* tile, int* srt, int* rexp, int* rrank,
-                                                int* key, int* ntl) {
-    const int tid = threadIdx.x, P = p.route_P, E = p.route_E, cap = p.route_cap;
-    int id = -1;
-    if (p.route_ids && tid < P) {
-        const int v = p.route_ids[tid];
-        id = v >= 0 && v < E ? v : -1;
-    }
-    if (tid < kRouteMaxP) {
-        rexp[tid] = -1;
-        key[tid] = id;  // the pair's expert, read back by every pair below
-    }
-    __syncthreads();
-    if (p.route_ids) {
-        if (id >= 0) {
-            int pos = 0, rank = 0, cnt = 0;
-            for (int j = 0; j < P; ++j) {
-                const int v = key[j];
-                pos += (v >= 0 && (v < id || (v == id && j < tid))) ? 1 : 0;
-                rank += (v == id && j < tid) ? 1 : 0;
-                cnt += v == id ? 1 : 0;
-            }
-            srt[pos] = tid;
-            rexp[pos] = id;
-            rrank[pos] = rank | (cnt << 8);  // rank and count (both at most kRouteMaxP)
-        }
-    } else {
-        for (int e = tid; e < E; e += blockDim.x) {
-            const int lo = min(max(p.route_off[e], 0), P), hi = min(max(p.route_off[e + 1], lo), P);
-            for (int i = lo; i < hi; ++i) rexp[i] = e;  // overlapping ranges (malformed offsets): one owner wins
-        }
-    }
-    __syncthreads();
-    if (tid < kRouteMaxP) {  // wave 0: lane = row of the sorted order
-        const int i = tid;
-        const int e = i < P ? rexp[i] : -1;
-        int rank = 0, cnt = 0;
-        if (e >= 0) {
-            if (p.route_ids) {
-                rank = rrank[i] & 255;
-                cnt = rrank[i] >> 8;
-            } else {
-                const int lo = min(max(p.route_off[e], 0), P), hi = min(max(p.route_off[e + 1], lo), P);
-                rank = i - lo;
-                cnt = hi - lo;
-            }
-        }
-        const bool start = e >= 0 && rank % cap == 0;
-        const unsigned long long bal = __ballot(start);
-        const int t = __popcll(bal & ((1ull << i) - 1ull));
-        if (start) {
-            tile[3 * t] = e;
-            tile[3 * t + 1] = i;
-            tile[3 * t + 2] = min(cap, cnt - rank);
-        }
-        if (i == 0) *ntl = __popcll(bal);
-    }
-    __syncthreads();
-    return *ntl;
-}
-
 template <Fmt F, int MT, int SPW, int CPW>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];  // sized per launch (plan.lds_bytes)
     __shared__ int rowinfo[2 * 16 * MT];  // [0,ROWS): A row of each local row; [ROWS,2ROWS): D row or -1
-    if constexpr (F == Fmt::MOE_MX) {
-        // persistent over the m-tile list (its length is known only here)
-        const int* tinfo = p.tile_info;
-        const int* srt = p.sorted;
-        int nt;
-        if (p.route_ids || p.route_off) {
-            __shared__ int rt_tile[3 * kRouteMaxP], rt_srt[kRouteMaxP], rt_exp[kRouteMaxP], rt_rank[kRouteMaxP],
-                rt_tmp[kRouteMaxP], rt_n;
-            nt = moe_route_inline(p, rt_tile, rt_srt, rt_exp, rt_rank, rt_tmp, &rt_n);
-            tinfo = rt_tile;
-            srt = p.route_ids ? rt_srt : nullptr;
-        } else {
-            nt = *p.ntiles;
-        }
-        for (int t = blockIdx.y; t < nt; t += gridDim.y) {
-            skinny_item<F, MT, SPW, CPW>(p, t, lds, rowinfo, tinfo, srt);
-            __syncthreads();  // the next tile reuses LDS
-        }
-    } else {
-        skinny_item<F, MT, SPW, CPW>(p, blockIdx.y, lds, rowinfo, nullptr, nullptr);
-    }
+    skinny_item<F, MT, SPW, CPW>(p, blockIdx.y, lds, rowinfo);
 }
 
 // ---- host-side plan ----
@@ -603,7 +464,7 @@ inline int64_t skinny_lds_need(Fmt F, int64_t rows, int64_t cmax, int NS, int gc
         const int64_t gmax = cmax / gch + 2;
         s = al(NS * gmax * 32);
         z = al(NS * gmax * 8);
-    } else if (F == Fmt::W4A8_MX || F == Fmt::MOE_MX) {
+    } else if (F == Fmt::W4A8_MX) {
         s = al(NS * cmax * 64);
     }
     return a + s + z;
