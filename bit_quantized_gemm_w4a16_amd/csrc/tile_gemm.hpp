@@ -189,7 +189,8 @@ void tile_gemm_kernel(TileArgs p) {
     constexpr int SC_PAD = SC_STAGE > 0 ? (SC_STAGE + 15) / 16 * 16 : 16;
     constexpr bool B1 = PD == 3;  // single weight stage
     constexpr int STAGE = A_STAGE + (B1 ? 0 : B_STAGE);
-    constexpr int NST = 2;  // LDS stages
+    constexpr int NST = PD == 4 ? 4 : 2;  // LDS stages
+    static_assert(PD != 4 || F == Fmt::W8A8_I8, "the four-stage ring has no scale block (INT8)");
     constexpr int NIA = A_STAGE / 16 / NTH;  // 16-byte loads per thread per step (A)
     constexpr int NIB = B_STAGE / 16 / NTH;  // (B)
     constexpr int MT = BM / WM / 16, NT = BN / WN / 16;  // 16x16 tiles per wave
@@ -202,6 +203,8 @@ void tile_gemm_kernel(TileArgs p) {
     // not make the reads wait for the load.
     __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
     __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char stage2[PD == 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char stage3[PD == 4 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) char bstage[B1 ? B_STAGE : 16];
     __shared__ __attribute__((aligned(16))) char scst[NST][SC_PAD];
     __shared__ int rowinfo[2 * BM];  // [0,BM): A row per local row; [BM,2BM): D row (-1 = none)
@@ -298,19 +301,25 @@ void tile_gemm_kernel(TileArgs p) {
                                 : sc_strip * (uint32_t)nsteps * 64u + (tid & 3) * 16u;
 
     auto stage_lds = [&](auto stc) -> lds_char* {
-        if constexpr (decltype(stc)::value == 0) return (lds_char*)stage0;
-        else return (lds_char*)stage1;
+        constexpr int S = decltype(stc)::value;
+        if constexpr (S == 0) return (lds_char*)stage0;
+        else if constexpr (S == 1) return (lds_char*)stage1;
+        else if constexpr (S == 2) return (lds_char*)stage2;
+        else return (lds_char*)stage3;
     };
     auto stage_ptr = [&](auto stc) -> char* {
-        if constexpr (decltype(stc)::value == 0) return stage0;
-        else return stage1;
+        constexpr int S = decltype(stc)::value;
+        if constexpr (S == 0) return stage0;
+        else if constexpr (S == 1) return stage1;
+        else if constexpr (S == 2) return stage2;
+        else return stage3;
     };
     auto sc_ptr = [&](auto stc) -> char* { return scst[decltype(stc)::value]; };
 
     // PD = 0: loads go straight from HBM into the next LDS stage (no staging
     // registers).  PD = 1, 2: register sets; the loads of step s+PD fly while
     // step s computes.
-    static_assert(PD >= 0 && PD <= 3, "prefetch: direct to LDS, one or two register steps, single weight stage");
+    static_assert(PD >= 0 && PD <= 4, "prefetch: direct to LDS, one or two register steps, single weight stage, four-stage ring");
     constexpr bool RSTAGE = PD == 1 || PD == 2;  // A and B staged through registers
     constexpr int NSET = RSTAGE ? PD : 1;
     v4u ra[NSET][RSTAGE ? NIA : 1], rb[NSET][RSTAGE ? NIB : 1], rs[NSET];
@@ -651,6 +660,33 @@ void tile_gemm_kernel(TileArgs p) {
             lds_sync();
         }
         if (ks < k1) compute(S0{}, nohook);
+    } else if constexpr (PD == 4) {
+        // four stages: the loads of steps s+1..s+3 fly while step s computes
+        // (INT8 tiles at mid M, whose steps are short next to the load
+        // latency).  Unrolled by the stage count, with an unconditional refill:
+        // steps past the slice load bytes that are never computed (other
+        // rows' data or zeros, always inside the buffer resources), so every
+        // point of the loop has the same loads outstanding on every path and
+        // the explicit waits hold for the compiler too.
+        constexpr int NL = NIA + NIB;  // direct loads per thread and step
+        using S2 = std::integral_constant<int, 2>;
+        using S3 = std::integral_constant<int, 3>;
+        dma(k0, S0{});
+        dma(k0 + 1, S1{});
+        dma(k0 + 2, S2{});
+        auto step = [&](int s, auto cur, auto refill) {
+            wait_vmcnt<2 * NL>();  // step s has landed (s+1, s+2 may fly)
+            lds_barrier();         // ... for every wave, which are all done with step s-1's stage
+            dma(s + 3, refill);
+            if (s < k1) compute(cur, nohook);
+        };
+        for (int ks = k0; ks < k1; ks += 4) {
+            step(ks, S0{}, S3{});
+            step(ks + 1, S1{}, S0{});
+            step(ks + 2, S2{}, S1{});
+            step(ks + 3, S3{}, S2{});
+        }
+        wait_vmcnt<0>();  // the three steps past the loop (never computed)
     } else if constexpr (PD == 3) {
         // as PD = 0; the single weight stage is refilled once every wave holds
         // its fragments of the current step (the barrier in the hook at t = 0)
@@ -865,7 +901,7 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
     if constexpr (F == Fmt::W8A8_I8) {
         if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
         if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
-        return launch_tile_kernel<F, 128, 128, 2, 4, 2>(p, st);
+        return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
     } else {
         if constexpr (F == Fmt::W4A8_MX)  // 8-bit A: a 256-column tile still fits two LDS stages
             if (pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
