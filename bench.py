@@ -356,7 +356,7 @@ def run(work, steps, warmup, eager=False):
     return wall, per
 
 
-KERNEL_SOURCES = ["tile_gemm.hpp", "skinny.hpp", "k_wna16.hip", "k_dense.hip", "k_moe.hip", "hq_device.hpp"]
+KERNEL_SOURCES = ["tile_gemm.hpp", "skinny.hpp", "moe_stream.hpp", "k_wna16.hip", "k_dense.hip", "k_moe.hip", "hq_device.hpp"]
 
 
 def kernel_source_hash():

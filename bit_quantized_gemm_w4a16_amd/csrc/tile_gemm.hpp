@@ -189,8 +189,11 @@ void tile_gemm_kernel(TileArgs p) {
     constexpr int SC_PAD = SC_STAGE > 0 ? (SC_STAGE + 15) / 16 * 16 : 16;
     constexpr bool B1 = PD == 3;  // single weight stage
     constexpr int STAGE = A_STAGE + (B1 ? 0 : B_STAGE);
-    constexpr int NST = PD == 4 ? 4 : 2;  // LDS stages
-    static_assert(PD != 4 || F == Fmt::W8A8_I8, "the four-stage ring has no scale block (INT8)");
+    // LDS stages: a ring of four where they fit, else three (PD = 4), else two
+    constexpr int NRING = 4 * STAGE <= 150 * 1024 ? 4 : 3;
+    constexpr int NST = PD == 4 ? NRING : 2;
+    static_assert(PD != 4 || F == Fmt::W8A8_I8, "the stage ring has no scale block (INT8)");
+    static_assert(PD != 4 || 3 * STAGE <= 150 * 1024, "a ring needs three stages");
     constexpr int NIA = A_STAGE / 16 / NTH;  // 16-byte loads per thread per step (A)
     constexpr int NIB = B_STAGE / 16 / NTH;  // (B)
     constexpr int MT = BM / WM / 16, NT = BN / WN / 16;  // 16x16 tiles per wave
@@ -203,8 +206,8 @@ void tile_gemm_kernel(TileArgs p) {
     // not make the reads wait for the load.
     __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
     __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
-    __shared__ __attribute__((aligned(1024))) char stage2[PD == 4 ? STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) char stage3[PD == 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char stage2[NST > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char stage3[NST > 3 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) char bstage[B1 ? B_STAGE : 16];
     __shared__ __attribute__((aligned(16))) char scst[NST][SC_PAD];
     __shared__ int rowinfo[2 * BM];  // [0,BM): A row per local row; [BM,2BM): D row (-1 = none)
@@ -319,7 +322,7 @@ void tile_gemm_kernel(TileArgs p) {
     // PD = 0: loads go straight from HBM into the next LDS stage (no staging
     // registers).  PD = 1, 2: register sets; the loads of step s+PD fly while
     // step s computes.
-    static_assert(PD >= 0 && PD <= 4, "prefetch: direct to LDS, one or two register steps, single weight stage, four-stage ring");
+    static_assert(PD >= 0 && PD <= 4, "prefetch: direct to LDS, one or two register steps, single weight stage, stage ring");
     constexpr bool RSTAGE = PD == 1 || PD == 2;  // A and B staged through registers
     constexpr int NSET = RSTAGE ? PD : 1;
     v4u ra[NSET][RSTAGE ? NIA : 1], rb[NSET][RSTAGE ? NIB : 1], rs[NSET];
@@ -661,32 +664,39 @@ void tile_gemm_kernel(TileArgs p) {
         }
         if (ks < k1) compute(S0{}, nohook);
     } else if constexpr (PD == 4) {
-        // four stages: the loads of steps s+1..s+3 fly while step s computes
-        // (INT8 tiles at mid M, whose steps are short next to the load
-        // latency).  Unrolled by the stage count, with an unconditional refill:
-        // steps past the slice load bytes that are never computed (other
-        // rows' data or zeros, always inside the buffer resources), so every
-        // point of the loop has the same loads outstanding on every path and
-        // the explicit waits hold for the compiler too.
+        // a ring of NST = 3 or 4 stages: the loads of steps s+1 .. s+NST-1 fly
+        // while step s computes (INT8 tiles at mid M, whose steps are short
+        // next to the load latency).  Unrolled by the stage count, with an
+        // unconditional refill: steps past the slice load bytes that are never
+        // computed (other rows' data or zeros, always inside the buffer
+        // resources), so every point of the loop has the same loads
+        // outstanding on every path and the explicit waits hold for the
+        // compiler too.
         constexpr int NL = NIA + NIB;  // direct loads per thread and step
         using S2 = std::integral_constant<int, 2>;
         using S3 = std::integral_constant<int, 3>;
         dma(k0, S0{});
         dma(k0 + 1, S1{});
-        dma(k0 + 2, S2{});
+        if constexpr (NST == 4) dma(k0 + 2, S2{});
         auto step = [&](int s, auto cur, auto refill) {
-            wait_vmcnt<2 * NL>();  // step s has landed (s+1, s+2 may fly)
-            lds_barrier();         // ... for every wave, which are all done with step s-1's stage
-            dma(s + 3, refill);
+            wait_vmcnt<(NST - 2) * NL>();  // step s has landed (the later ones may fly)
+            lds_barrier();                 // ... for every wave, which are all done with step s-1's stage
+            dma(s + NST - 1, refill);
             if (s < k1) compute(cur, nohook);
         };
-        for (int ks = k0; ks < k1; ks += 4) {
-            step(ks, S0{}, S3{});
-            step(ks + 1, S1{}, S0{});
-            step(ks + 2, S2{}, S1{});
-            step(ks + 3, S3{}, S2{});
+        for (int ks = k0; ks < k1; ks += NST) {
+            if constexpr (NST == 4) {
+                step(ks, S0{}, S3{});
+                step(ks + 1, S1{}, S0{});
+                step(ks + 2, S2{}, S1{});
+                step(ks + 3, S3{}, S2{});
+            } else {
+                step(ks, S0{}, S2{});
+                step(ks + 1, S1{}, S0{});
+                step(ks + 2, S2{}, S1{});
+            }
         }
-        wait_vmcnt<0>();  // the three steps past the loop (never computed)
+        wait_vmcnt<0>();  // the steps past the loop (never computed)
     } else if constexpr (PD == 3) {
         // as PD = 0; the single weight stage is refilled once every wave holds
         // its fragments of the current step (the barrier in the hook at t = 0)
@@ -900,7 +910,7 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
     p.splits = pl.splits;
     if constexpr (F == Fmt::W8A8_I8) {
         if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
-        if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
+        if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 4>(p, st);
         return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
     } else {
         if constexpr (F == Fmt::W4A8_MX)  // 8-bit A: a 256-column tile still fits two LDS stages
