@@ -53,7 +53,8 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
     p.ngroups = 1;
     p.gsteps = 1;
     p.raw_i32 = raw_i32;
-    return launch_dense_plan<F>(plan_tile(a.M, a.Np, a.K, has_big_tile(F), has_wide256_tile(F), has_wide_tile(F)), p, a.stream);
+    const TilePlan pl = plan_tile(a.M, a.Np, a.K, has_big_tile(F), has_wide256_tile(F), has_wide_tile(F), wide256_min_tiles(F));
+    return launch_dense_plan<F>(pl, p, a.stream);
 }
 
 }  // namespace

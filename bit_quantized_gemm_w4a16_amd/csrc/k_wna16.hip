@@ -60,7 +60,8 @@ hipError_t launch_tile(const DenseArgs& a) {
     p.Np = (int)a.Np;
     p.ngroups = (int)(a.K / a.group_size);
     p.gsteps = a.group_size / 128;
-    return launch_dense_plan<F>(plan_tile(a.M, a.Np, a.K, has_big_tile(F), has_wide256_tile(F), has_wide_tile(F)), p, a.stream);
+    const TilePlan pl = plan_tile(a.M, a.Np, a.K, has_big_tile(F), has_wide256_tile(F), has_wide_tile(F), wide256_min_tiles(F));
+    return launch_dense_plan<F>(pl, p, a.stream);
 }
 
 template <Fmt F>
@@ -74,7 +75,8 @@ hipError_t launch_all(const DenseArgs& a) {
 size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size, bool bf16) {
     const int64_t Np = pad16(N);
     const Fmt F = bf16 ? Fmt::WNA16_BF16 : Fmt::WNA16_F16;
-    if (M > kSkinnyMaxM) return tile_workspace(plan_tile(M, Np, K, has_big_tile(F), has_wide256_tile(F), has_wide_tile(F)), M, Np);
+    if (M > kSkinnyMaxM)
+        return tile_workspace(plan_tile(M, Np, K, has_big_tile(F), has_wide256_tile(F), has_wide_tile(F), wide256_min_tiles(F)), M, Np);
     return skinny_workspace(plan_skinny(F, M, Np, K, group_size), M, Np);
 }
 

@@ -846,10 +846,11 @@ struct TilePlan {
 // The largest grids use 256-column tiles where the format has them (256 x 256,
 // else 128 x 256), then 256 x 128 tiles on 8 waves; smaller ones 128 x 128
 // tiles with K split across workgroups until the grid covers the chip.
-inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256, bool wide256 = false, bool wide128 = false) {
+inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256, bool wide256 = false, bool wide128 = false,
+                          int64_t wide256_min = 256) {
     const int64_t tn = (Np + 127) / 128, nsteps = K / 128, tn2 = (Np + 255) / 256;
     TilePlan pl{128, 1, false};
-    if (wide256 && ((M + 255) / 256) * tn2 >= 256) {
+    if (wide256 && ((M + 255) / 256) * tn2 >= wide256_min) {
         pl.BM = 256;
         pl.wide = true;
         return pl;
@@ -904,6 +905,10 @@ constexpr bool has_wide_tile(Fmt F) { return F == Fmt::WNA16_F16; }
 // (M = 8192: 1126 us vs 1569 us for 256 x 128 with register-staged loads); the
 // 256 x 128 tile also loads directly (1498 us).
 constexpr bool has_wide256_tile(Fmt F) { return F == Fmt::WNA16_F16 || F == Fmt::W8A8_I8; }
+// 256x256 tiles from this many on: INT8 keeps the 256x128 three-stage ring
+// until the wide tiles fill two rounds of the chip (measured: the ring is
+// faster at M=1024 and level at M=2048 for N=18432, K=7168)
+constexpr int64_t wide256_min_tiles(Fmt F) { return F == Fmt::W8A8_I8 ? 512 : 256; }
 
 template <Fmt F>
 hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
