@@ -192,7 +192,6 @@ void tile_gemm_kernel(TileArgs p) {
     // LDS stages: a ring of four where they fit, else three (PD = 4), else two
     constexpr int NRING = 4 * STAGE <= 150 * 1024 ? 4 : 3;
     constexpr int NST = PD == 4 ? NRING : 2;
-    static_assert(PD != 4 || F == Fmt::W8A8_I8, "the stage ring has no scale block (INT8)");
     static_assert(PD != 4 || 3 * STAGE <= 150 * 1024, "a ring needs three stages");
     constexpr int NIA = A_STAGE / 16 / NTH;  // 16-byte loads per thread per step (A)
     constexpr int NIB = B_STAGE / 16 / NTH;  // (B)
@@ -324,7 +323,7 @@ void tile_gemm_kernel(TileArgs p) {
     // step s computes.
     static_assert(PD >= 0 && PD <= 4, "prefetch: direct to LDS, one or two register steps, single weight stage, stage ring");
     constexpr bool RSTAGE = PD == 1 || PD == 2;  // A and B staged through registers
-    constexpr int NSET = RSTAGE ? PD : 1;
+    constexpr int NSET = RSTAGE ? PD : PD == 4 ? NST : 1;  // register sets (the ring: one scale block per stage)
     v4u ra[NSET][RSTAGE ? NIA : 1], rb[NSET][RSTAGE ? NIB : 1], rs[NSET];
     // Direct loads of one step's A and weight tiles into a stage (NIA + NIB
     // unconditional loads per thread).  The scale block goes through registers
@@ -666,22 +665,37 @@ void tile_gemm_kernel(TileArgs p) {
     } else if constexpr (PD == 4) {
         // a ring of NST = 3 or 4 stages: the loads of steps s+1 .. s+NST-1 fly
         // while step s computes (INT8 tiles at mid M, whose steps are short
-        // next to the load latency).  Unrolled by the stage count, with an
+        // next to the load latency; W4A8 256x256 tiles, whose loads take
+        // longer than one step of MFMAs).  Unrolled by the stage count, with an
         // unconditional refill: steps past the slice load bytes that are never
         // computed (other rows' data or zeros, always inside the buffer
         // resources), so every point of the loop has the same loads
         // outstanding on every path and the explicit waits hold for the
         // compiler too.
+        // A step's scale block (4-bit formats) comes with its loads into the
+        // stage's register set and goes to the stage's LDS array once landed.
+        // The block's fetching threads issue one load more per step than the
+        // others; counting only the tile loads makes their wait stricter, never
+        // looser.
         constexpr int NL = NIA + NIB;  // direct loads per thread and step
         using S2 = std::integral_constant<int, 2>;
         using S3 = std::integral_constant<int, 3>;
-        dma(k0, S0{});
-        dma(k0 + 1, S1{});
-        if constexpr (NST == 4) dma(k0 + 2, S2{});
+        auto fetch = [&](int s, auto stc) {
+            sc_load(s, stc);
+            dma(s, stc);
+        };
+        fetch(k0, S0{});
+        fetch(k0 + 1, S1{});
+        if constexpr (NST == 4) fetch(k0 + 2, S2{});
         auto step = [&](int s, auto cur, auto refill) {
             wait_vmcnt<(NST - 2) * NL>();  // step s has landed (the later ones may fly)
-            lds_barrier();                 // ... for every wave, which are all done with step s-1's stage
-            dma(s + NST - 1, refill);
+            if constexpr (SC_STAGE > 0) {
+                sc_write(cur, cur);
+                lds_sync();  // the scale block written, and every wave done with step s-1's stage
+            } else {
+                lds_barrier();  // every wave's loads of step s landed, and every wave done with step s-1's stage
+            }
+            fetch(s + NST - 1, refill);
             if (s < k1) compute(cur, nohook);
         };
         for (int ks = k0; ks < k1; ks += NST) {
@@ -919,7 +933,7 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
         return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
     } else {
         if constexpr (F == Fmt::W4A8_MX)  // 8-bit A: a 256-column tile still fits two LDS stages
-            if (pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
+            if (pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 4>(p, st);
         if constexpr (has_wide_tile(F)) {
             if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
             if (pl.wide) return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
