@@ -258,7 +258,7 @@ class MoEMXFP4:
         return self.active[T] * self.ebytes + T * self.K * 2 + T * self.top_k * (self.N * 2 + 4)
 
     def kernel_of(self, T):
-        return ("moe: routing + skinny_kernel<MOE_MX> + tile_gemm_kernel<MOE_MX> tiers", "mfma" if T >= 4096 else "hbm")
+        return ("moe: routing + moe_stream_kernel + tile_gemm_kernel<MOE_MX> tiers", "mfma" if T >= 4096 else "hbm")
 
     def call(self, T, c):
         w, e = self.copies[c]
