@@ -12,14 +12,15 @@
 // Workgroup = 4 waves over NS strips (16 output columns each) and one K slice
 // of 128-K chunks.  The waves split the
 // workgroup as WS strip-columns x WK K-parts; each wave owns SPW strips.
-//   1. The A rows of the slice and the slice's scales (group scales +
-//      zero-points, or E8M0 exponents) go to LDS with direct-to-LDS loads.
-//   2. Every wave issues all of its packed-weight loads (16 bytes per lane =
-//      one MFMA B fragment per load) in chunk order, so the whole weight
-//      stream of the chip is in flight at once.
-//   3. One wait for the LDS copies (they were issued first and memory
-//      returns in order), one barrier, then each chunk is decoded and fed to
-//      the MFMA as soon as its own load has landed.
+//   1. Every wave issues the first half of its packed-weight loads (16 bytes
+//      per lane = one MFMA B fragment per load), in chunk order.
+//   2. The A rows of the slice and the slice's scales (group scales +
+//      zero-points, or E8M0 exponents) go to LDS with direct-to-LDS loads,
+//      then the second half of the weight loads: the whole weight stream of
+//      the chip is in flight at once, the weights (the long pole) first.
+//   3. One wait for the LDS copies (memory returns in order, so the first
+//      half of the weights has landed too), one barrier, then each chunk is
+//      decoded and fed to the MFMA as soon as its own load has landed.
 //   4. The K-parts of the workgroup reduce through LDS; K slices of a split
 //      launch write fp32 / int32 partial tiles that a finalize pass sums in
 //      slice order.  (A last-arriving-slice reduction inside the kernel needs a
@@ -81,7 +82,7 @@ __device__ __forceinline__ int skinny_swz(int row) {
 // One work item: K slice `split` of the launch.  Every thread of the
 // workgroup calls it (it holds barriers).
 template <Fmt F, int MT, int SPW, int CPW>
-__device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char* lds, int* rowinfo) {
+__device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char* lds) {
     using Tr = SkinnyTraits<F>;
     using Acc = typename FmtTraits<F>::Acc;
     static_assert(F != Fmt::MOE_MX, "MoE experts stream through moe_stream_kernel");
@@ -107,15 +108,34 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     const int nsl = c1 - c0;   // chunks in the slice
     const int U = nsl * UPC;   // A units per LDS row
 
-    // ---- local rows: A row and D row ----
-    if (tid < ROWS) {
-        const int r = tid;
-        rowinfo[r] = r < rows ? r : rows - 1;
-        rowinfo[ROWS + r] = r < rows ? r : -1;
+    // ---- the wave's packed weights, chunk-major, all in flight ----
+    // Chunks past the wave's range repeat its last chunk (never used); a wave
+    // with an empty range re-reads the slice's first chunk, so every load
+    // stays inside the strip.  The first CH chunks go out before the A slice
+    // and scales (the weights are the long pole), the rest after them.
+    const int wlast = cw1 > cw0 ? cw1 - 1 : c0;
+    int wstrip[SPW];
+    const v4u* wsrc[SPW];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        wstrip[sp] = strip_base + ws * SPW + sp;
+        const int st = wstrip[sp] < nstrips ? wstrip[sp] : nstrips - 1;
+        wsrc[sp] = (const v4u*)(Wb + (size_t)st * p.nc * FmtTraits<F>::BSTRIP) + lane;
     }
-    __syncthreads();  // no weight load is in flight yet, so this drains nothing
+    v4u w[CPW][SPW][NB];
+    constexpr int CH = CPW / 2;
+    auto issue_w = [&](int i) {
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+            for (int h = 0; h < NB; ++h) w[i][sp][h] = ld_nt(wsrc[sp] + ((size_t)min(cw0 + i, wlast) * NB + h) * 64);
+        // keep the issue order = the consumption order, so each chunk waits only for its own loads
+        __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int i = 0; i < CH; ++i) issue_w(i);
 
-    // ---- 1. A slice and scales -> LDS (direct loads, issued before the weights) ----
+    // ---- A slice and scales -> LDS (direct loads, issued between the two halves of the weights) ----
     {
         const char* Abase = (const char*)p.A + (size_t)c0 * 128 * AB;
         const int nblk = (U + 63) >> 6;  // 64-unit blocks per row
@@ -123,7 +143,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
         while (r < rows && blk >= nblk) { blk -= nblk; ++r; }
         while (r < rows) {
             const int pos = blk * 64 + lane;
-            const char* arow = Abase + (size_t)rowinfo[r] * p.K * AB;
+            const char* arow = Abase + (size_t)r * p.K * AB;
             if (pos < U) lds_dma16(arow + ((pos ^ skinny_swz<UPC>(r)) * 16), lds + p.a_off + (r * U + blk * 64) * 16);
             blk += 4;
             while (r < rows && blk >= nblk) { blk -= nblk; ++r; }
@@ -154,32 +174,12 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
         }
     }
 
-    // ---- 2. the wave's packed weights, chunk-major, all in flight ----
-    // Chunks past the wave's range repeat its last chunk (never used); a wave
-    // with an empty range re-reads the slice's first chunk, so every load
-    // stays inside the strip.
-    const int wlast = cw1 > cw0 ? cw1 - 1 : c0;
-    int wstrip[SPW];
-    const v4u* wsrc[SPW];
 #pragma unroll
-    for (int sp = 0; sp < SPW; ++sp) {
-        wstrip[sp] = strip_base + ws * SPW + sp;
-        const int st = wstrip[sp] < nstrips ? wstrip[sp] : nstrips - 1;
-        wsrc[sp] = (const v4u*)(Wb + (size_t)st * p.nc * FmtTraits<F>::BSTRIP) + lane;
-    }
-    v4u w[CPW][SPW][NB];
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-#pragma unroll
-        for (int sp = 0; sp < SPW; ++sp)
-#pragma unroll
-            for (int h = 0; h < NB; ++h) w[i][sp][h] = ld_nt(wsrc[sp] + ((size_t)min(cw0 + i, wlast) * NB + h) * 64);
-        // keep the issue order = the consumption order, so each chunk waits only for its own loads
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    // the LDS copies were issued before these NLOAD loads: once at most NLOAD
-    // loads are outstanding, this wave's copies have landed
-    wait_vmcnt<NLOAD>();
+    for (int i = CH; i < CPW; ++i) issue_w(i);
+    // the LDS copies were issued before the last (CPW - CH) chunks' loads: once
+    // at most that many loads are outstanding, this wave's copies (and its
+    // first CH chunks) have landed
+    wait_vmcnt<SPW * (CPW - CH) * NB>();
     lds_barrier();
 
     // ---- 3. decode + MFMA ----
@@ -414,17 +414,17 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
             for (int r = 0; r < 4; ++r) {
                 const int m = mt * 16 + quad * 4 + r;
                 if (m >= ROWS) continue;
-                const int drow = rowinfo[ROWS + m];
-                if (drow < 0) continue;
+                if (m >= rows) continue;
+                const int drow = m;
                 if (n >= p.N) continue;
                 const int64_t o = (int64_t)drow * p.N + n;
                 if constexpr (WNA16) {
                     ((uint16_t*)p.D)[o] = f32_to_16<F == Fmt::WNA16_BF16>(acc[sp][mt][r]);
                 } else if constexpr (F == Fmt::W8A8_I8) {
                     if (p.raw_i32) ((int*)p.D)[o] = acc[sp][mt][r];
-                    else ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)acc[sp][mt][r] * p.a_scale[rowinfo[m]] * ((const float*)Sb)[n]);
+                    else ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)acc[sp][mt][r] * p.a_scale[m] * ((const float*)Sb)[n]);
                 } else if constexpr (F == Fmt::W4A8_MX) {
-                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r] * p.a_scale[rowinfo[m]]);
+                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r] * p.a_scale[m]);
                 } else {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r]);
                 }
@@ -435,8 +435,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
 template <Fmt F, int MT, int SPW, int CPW>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];  // sized per launch (plan.lds_bytes)
-    __shared__ int rowinfo[2 * 16 * MT];  // [0,ROWS): A row of each local row; [ROWS,2ROWS): D row or -1
-    skinny_item<F, MT, SPW, CPW>(p, blockIdx.y, lds, rowinfo);
+    skinny_item<F, MT, SPW, CPW>(p, blockIdx.y, lds);
 }
 
 // ---- host-side plan ----
