@@ -71,6 +71,16 @@ def test_w4a8_ragged_n_and_extremes():
     assert gate_error(Dr, O) <= 8e-3
 
 
+@pytest.mark.parametrize("M,N,K", [(1100, 7200, 128), (1100, 7168, 640)])
+def test_w4a8_big_tiles_ragged(M, N, K):
+    """256 x 256 W4A8 tiles on the three-stage ring with ragged last row and
+    column tiles: one K step (the ring's prologue fetches steps past the slice,
+    never computed) and five steps (not a multiple of the ring)."""
+    Dr, O = run_w4a8(M, N, K, seed=M + K, rows=np.arange(M))
+    err = gate_error(Dr, O)
+    assert err <= min(GATE, 8e-3), err
+
+
 @pytest.mark.parametrize("M", [1, 16, 256, 2048, 8192])
 def test_w4a8_full_size(M):
     """The dense W4A8-MXFP4 workload: N=7168, K=4096 (sampled rows at large M)."""
@@ -141,9 +151,10 @@ def test_w8a8_full_size(M):
     assert gate_error(got, O) <= 8e-3
 
 
-@pytest.mark.parametrize("M,N,K", [(1100, 16400, 256), (600, 11000, 384)])
+@pytest.mark.parametrize("M,N,K", [(2100, 16400, 256), (600, 11000, 384), (600, 11000, 128)])
 def test_w8a8_raw_int32_big_tiles_ragged(M, N, K):
-    """Grids of 256 x 256 (first shape) and 256 x 128 (second) INT8 tiles with
-    ragged last row and column tiles: raw int32 accumulators bit-exact."""
+    """Grids of 256 x 256 (first shape) and 256 x 128 (the others, a three-stage
+    ring: three steps, and one step whose ring fetches run past the slice) INT8
+    tiles with ragged last row and column tiles: raw int32 accumulators bit-exact."""
     got, acc = run_w8a8(M, N, K, seed=M, raw=True)
     np.testing.assert_array_equal(got.astype(np.int64), acc)
