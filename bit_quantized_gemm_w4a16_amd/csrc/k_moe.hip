@@ -448,7 +448,7 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     p.gsteps = 1;
     p.w_estride = a.w_estride;
     p.s_estride = a.s_estride;
-    p.tiles_n = (int)cdiv(a.Np, 128);
+    p.tiles_n = (int)cdiv(a.Np, 256);
     p.splits = 1;
     p.sorted = sorted;
     p.top_k = a.top_k;
@@ -457,7 +457,7 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     p.tile_info = tl[1];
     p.ntiles = ntiles + 1;
     if (p.tiles_m > 0) {
-        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeMidBM, 128, 2, 4, 0>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+        hipLaunchKernelGGL((tile_gemm_kernel<Fmt::MOE_MX, kMoeMidBM, 256, 1, 8, 0>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
                            dim3(512), 0, a.stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -465,7 +465,6 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     // experts with more than kMoeMidMax rows: 256-column tiles of 8 waves side by
     // side (each wave decodes its weight strips once; the 256-row tile keeps one
     // weight LDS stage and feeds each decoded fragment to 16 MFMAs)
-    p.tiles_n = (int)cdiv(a.Np, 256);
     p.tiles_m = (int)L.max_tier[2];
     p.tile_info = tl[2];
     p.ntiles = ntiles + 2;
