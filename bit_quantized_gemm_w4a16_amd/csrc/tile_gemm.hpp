@@ -932,8 +932,21 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
         if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 4>(p, st);
         return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
     } else {
-        if constexpr (F == Fmt::W4A8_MX)  // 8-bit A: a 256-column tile still fits two LDS stages
+        if constexpr (F == Fmt::W4A8_MX) {
+            // 8-bit A: a 256-column tile on a three-stage ring
             if (pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 4>(p, st);
+            // mid M: a 128 x 128 step is 8 MFMAs per wave, short next to the load
+            // latency.  While the tiles fit one workgroup per CU, a four-stage ring
+            // (96 KB) with the K split rounded down to keep one round beats two
+            // workgroups per CU on two stages (fewer slices, so the partials and
+            // the finalize pass shrink or vanish too)
+            const int64_t tiles = ((p.M + 127) / 128) * ((p.Np + 127) / 128);
+            if (tiles <= 256) {
+                const int64_t s = 256 / tiles;
+                p.splits = (int)(s < 1 ? 1 : s < pl.splits ? s : pl.splits);
+                return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
+            }
+        }
         if constexpr (has_wide_tile(F)) {
             if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
             if (pl.wide) return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
