@@ -930,6 +930,18 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
     if constexpr (F == Fmt::W8A8_I8) {
         if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
         if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 4>(p, st);
+        // the rings run one workgroup per CU: keep the grid to one round, with
+        // 256-row tiles where 128-row ones would need two, and the K split
+        // rounded down
+        const int64_t tiles = ((p.M + 127) / 128) * ((p.Np + 127) / 128);
+        if (tiles > 256 && ((p.M + 255) / 256) * ((p.Np + 127) / 128) <= 256) {
+            p.splits = 1;
+            return launch_tile_kernel<F, 256, 128, 2, 4, 4>(p, st);
+        }
+        if (tiles <= 256) {
+            const int64_t s = 256 / tiles;
+            p.splits = (int)(s < 1 ? 1 : s < pl.splits ? s : pl.splits);
+        }
         return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
     } else {
         if constexpr (F == Fmt::W4A8_MX) {
