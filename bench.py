@@ -6,8 +6,9 @@ M in {1, 2, 4, ..., 8192} one library call (host dispatch -> HIP kernels ->
 output) on inputs already resident in HBM.  The default workload is the
 dense W4A16 asymmetric layer (fp16 activations, UINT4 weights with UINT4
 zero-points and fp16 scales per 128 K, N=4096, K=7168), the configuration
-the metric is quoted on.  --config c1|c3|c4|c5|all measures the other
-workloads (one JSON line each).
+the metric is quoted on.  --config c1|c3|c4|c5|c5l|all measures the other
+workloads (one JSON line each); c5l is the whole MoE layer the pages time
+(gate-up GEMM, SwiGLU, down-projection GEMM).
 
 Cold cache: the packed weights are replicated into enough device copies
 (> 512 MiB in total, more than the 256 MiB Infinity Cache plus every L2) and
@@ -277,6 +278,56 @@ class MoEMXFP4:
                                           f"({len(sub_e)} experts touched), fp64 accumulation, {dt:.1f} s")
 
 
+class MoELayerMXFP4(MoEMXFP4):
+    """The MoE layer the pages time (gate-up + down): gate-up W4A16-MXFP4 (N=4096, K=7168,
+    Indexed), SwiGLU, down projection (N=7168, K=2048, Indexed with one row per pair),
+    E=256, top-8, Zipf(1.1) routing; each call = the three steps with their routing."""
+
+    def __init__(self, N2=7168):
+        super().__init__()
+        self.N2, self.I = N2, self.N // 2
+        self.name = f"moe_layer_w4a16_mxfp4_E{self.E}_top{self.top_k}_N{self.N}_K{self.K}_down_N{N2}_K{self.I}"
+        log(f"[bench] generating the down projection (all {self.E} experts)")
+        d2 = syn.moe_mxfp4(1, 1, self.E, 1, N2, self.I)
+        self.desc2 = hq.desc_moe_mxfp4(self.E, N2, self.I)
+        wp, ep, _ = hq.hq_repack(self.desc2, d2["q"], d2["e"])
+        self.ebytes2 = (wp.size + ep.size) // self.E
+        w0, e0 = dev(wp), dev(ep)
+        self.copies2 = [(w0, e0)] + [(w0.clone(), e0.clone()) for _ in range(len(self.copies) - 1)]
+        del wp, ep, d2
+        P = self.Tmax * self.top_k
+        self.flat = dev(self.host["ids"].reshape(-1).astype(np.int32))
+        self.H = torch.empty(P * self.I * 2, dtype=torch.uint8, device="cuda")
+        self.D2 = torch.empty(P * N2 * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = max(self.ws_bytes, hq.hq_workspace_bytes(self.desc2, P, 1))
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def flops(self, T):
+        return 2.0 * T * self.top_k * (self.N * self.K + self.N2 * self.I)
+
+    def bytes(self, T):
+        P = T * self.top_k
+        return (self.active[T] * (self.ebytes + self.ebytes2) + T * self.K * 2 + P * (self.N * 2 + 4) * 2
+                + P * self.I * 2 * 2 + P * self.N2 * 2)
+
+    def kernel_of(self, T):
+        return ("moe layer: gate-up + silu_mul + down (routing, moe_stream_kernel, tile_gemm_kernel<MOE_MX> tiers)",
+                "mfma" if T >= 4096 else "hbm")
+
+    def call(self, T, c):
+        super().call(T, c)
+        P = T * self.top_k
+        hq.hq_silu_mul(hq.HQ_DT_BF16, P, self.I, self.D, self.H)
+        w, e = self.copies2[c]
+        hq.hq_moe_gemm(self.desc2, hq.HQ_MOE_INDEXED, P, 1, self.H, None, self.flat, None, w, e, None, self.D2,
+                       self.ws, self.ws_bytes)
+
+    def cpu_baseline(self, budget_s=16.0):
+        b = super().cpu_baseline(budget_s)
+        b["sample"] = "gate-up projection only: " + b["sample"]
+        return b
+
+
 WORKLOADS = {
     "c1": lambda: DenseW4A16(N=1024, K=1024, Mmax=16, bf16=True, zp=False, sweep=[16],
                              name="dense_w4a16_sym_bf16_M16_N1024_K1024"),
@@ -284,6 +335,7 @@ WORKLOADS = {
     "c3": lambda: DenseW4A8(),
     "c4": lambda: DenseW8A8(),
     "c5": lambda: MoEMXFP4(),
+    "c5l": lambda: MoELayerMXFP4(),
 }
 
 
@@ -457,7 +509,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="c2", help="c1|c2|c3|c4|c5|all (default c2)")
+    ap.add_argument("--config", default="c2", help="c1|c2|c3|c4|c5|c5l|all (default c2; c5l = MoE gate-up + SwiGLU + down)")
     ap.add_argument("--sweep", default=None, help="comma-separated M values (default 1..8192 powers of 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="issue calls directly instead of replaying HIP graphs "

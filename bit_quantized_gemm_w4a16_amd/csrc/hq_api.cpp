@@ -296,6 +296,16 @@ hq_status hq_quantize_act(int32_t out_dtype, int64_t M, int64_t K, const float* 
     return hip_status(quant_e4m3_launch(M, K, x, (uint8_t*)q, s, (hipStream_t)stream), "hq_quantize_act");
 }
 
+hq_status hq_silu_mul(int32_t dtype, int64_t rows, int64_t I, const void* gate_up, void* out, hq_stream_t stream) {
+    if (dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "only BF16 rows are built");
+    if (rows < 0 || rows > (1LL << 30) || I < 8 || I > (1LL << 24) || I % 8)
+        return set_error(HQ_ERR_INVALID_ARG, "rows/I out of range (I a multiple of 8)");
+    if (rows == 0) return ok();
+    if (!gate_up || !out) return set_error(HQ_ERR_INVALID_ARG, "gate_up and out are required");
+    if (!aligned16(gate_up) || !aligned16(out)) return set_error(HQ_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    return hip_status(silu_mul_launch(rows, I, gate_up, out, (hipStream_t)stream), "hq_silu_mul");
+}
+
 hq_status hq_moe_align(int64_t T, int32_t top_k, int32_t num_experts, const int32_t* topk_ids,
                        int32_t* expert_offsets, int32_t* sorted_pairs, void* workspace, size_t ws_bytes,
                        hq_stream_t stream) {

@@ -75,6 +75,7 @@ hipError_t moe_gather_launch(const void* A, const int* sorted, int64_t P, int to
 
 // activation quantisation (tokenwise E4M3)
 hipError_t quant_e4m3_launch(int64_t M, int64_t K, const float* x, uint8_t* q, float* s, hipStream_t st);
+hipError_t silu_mul_launch(int64_t rows, int64_t I, const void* in, void* out, hipStream_t st);
 
 // fill kernel used by hq_workspace_init
 hipError_t fill_zero_launch(void* p, size_t bytes, hipStream_t stream);

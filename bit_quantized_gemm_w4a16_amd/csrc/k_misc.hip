@@ -59,3 +59,44 @@ hipError_t quant_e4m3_launch(int64_t M, int64_t K, const float* x, uint8_t* q, f
 }
 
 }  // namespace hq
+
+namespace hq {
+
+// SwiGLU between the MoE projections: out[r][i] = bf16(silu(g) * u) with
+// g = in[r][i], u = in[r][I + i], computed in fp32 (exact bf16 -> fp32 inputs)
+// and rounded once to nearest even.  silu(g) = g / (1 + e^-g), evaluated as
+// g / (1 + t) for g >= 0 and g t / (1 + t) for g < 0 with t = e^-|g| <= 1: the
+// plain form overflows e^-g for g below about -88.7 and returns 0 where the
+// result is still a normal bf16.  One thread per 8 outputs (16-byte loads of
+// gate and up, one 16-byte store); HBM-bound.
+__global__ __launch_bounds__(256) void silu_mul_kernel(const v4u* __restrict__ in, int64_t rows, int I8,
+                                                       v4u* __restrict__ out) {
+    const int64_t total = rows * I8;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / I8, c = i - r * I8;
+        const v4u g = in[r * 2 * I8 + c], u = in[r * 2 * I8 + I8 + c];
+        v4u o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float g0 = __uint_as_float(g[k] << 16), g1 = __uint_as_float(g[k] & 0xFFFF0000u);
+            const float u0 = __uint_as_float(u[k] << 16), u1 = __uint_as_float(u[k] & 0xFFFF0000u);
+            const float t0 = expf(-fabsf(g0)), t1 = expf(-fabsf(g1));
+            const float y0 = (g0 >= 0.f ? g0 : g0 * t0) / (1.0f + t0) * u0;
+            const float y1 = (g1 >= 0.f ? g1 : g1 * t1) / (1.0f + t1) * u1;
+            o[k] = (uint32_t)f32_to_bf16_bits(y0) | ((uint32_t)f32_to_bf16_bits(y1) << 16);
+        }
+        out[i] = o;
+    }
+}
+
+hipError_t silu_mul_launch(int64_t rows, int64_t I, const void* in, void* out, hipStream_t st) {
+    const int64_t total = rows * (I / 8);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks < 1) return hipSuccess;
+    hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const v4u*)in, rows, (int)(I / 8),
+                       (v4u*)out);
+    return hipGetLastError();
+}
+
+}  // namespace hq

@@ -64,6 +64,7 @@ _SIGS = {
     "hq_quantize_act": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, _P, _P, _P, _P]),
     "hq_moe_align": (C.c_int, [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]),
     "hq_moe_gather": (C.c_int, [C.c_int32, C.c_int64, C.c_int32, C.c_int64, _P, _P, _P, _P]),
+    "hq_silu_mul": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, _P, _P, _P]),
 }
 
 
@@ -209,3 +210,7 @@ def hq_moe_align(T, top_k, num_experts, topk_ids, expert_offsets, sorted_pairs, 
 def hq_moe_gather(dtype, T, top_k, K, A, sorted_pairs, A_sorted, stream=None) -> None:
     _check(lib().hq_moe_gather(dtype, T, top_k, K, _dp(A), _dp(sorted_pairs), _dp(A_sorted), _stream(stream)),
            "hq_moe_gather")
+
+
+def hq_silu_mul(dtype, rows, I, gate_up, out, stream=None) -> None:
+    _check(lib().hq_silu_mul(dtype, rows, I, _dp(gate_up), _dp(out), _stream(stream)), "hq_silu_mul")

@@ -253,6 +253,22 @@ hq_status hq_quantize_act(int32_t out_dtype, int64_t M, int64_t K, const float* 
                           hq_stream_t stream);
 
 /*
+ * SwiGLU between the MoE gate-up and down projections ("Humming wird
+ * angekuendigt", section "Leistung": the MoE figures add the gate-up and down
+ * GEMMs; the activation between them is the plain SiLU(gate) * up of a fused
+ * gate+up output, gate in the first half of each row).
+ *   gate_up  device bf16 [rows][2I]: row r = gate[r][0..I) | up[r][0..I)
+ *   out      device bf16 [rows][I]: bf16(silu(gate) * up), fp32 arithmetic with
+ *            silu(g) = g / (1 + e^-g) (evaluated without overflow for large
+ *            negative g), rounded once to nearest even
+ * dtype must be HQ_DT_BF16; I a multiple of 8; pointers 16-byte aligned; the
+ * two buffers must not overlap.  rows == 0 returns HQ_OK.  The output feeds the
+ * down projection as hq_moe_gemm INDEXED with T = rows, top_k = 1 and the
+ * flattened top-k ids (each row its own token), or GROUPED on sorted rows.
+ */
+hq_status hq_silu_mul(int32_t dtype, int64_t rows, int64_t I, const void* gate_up, void* out, hq_stream_t stream);
+
+/*
  * MoE routing metadata ("Humming wird angekuendigt", section "WnA16": the
  * Grouped path runs on expert-sorted tokens).  From topk_ids [T][top_k]:
  *   expert_offsets [E+1]: exclusive prefix sum of per-expert pair counts

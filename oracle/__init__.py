@@ -65,6 +65,10 @@ def lib():
         L.hq_oracle_gemm_w8a8.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p, p]
         L.hq_oracle_moe_route.restype = C.c_int
         L.hq_oracle_moe_route.argtypes = [i64, i64, i64, p, p, p, p]
+        L.hq_oracle_bf16_encode.restype = C.c_uint16
+        L.hq_oracle_bf16_encode.argtypes = [d]
+        L.hq_oracle_silu_mul_bf16.restype = None
+        L.hq_oracle_silu_mul_bf16.argtypes = [i64, i64, p, p]
         L.hq_oracle_moe_mxfp4_bf16.restype = C.c_int
         L.hq_oracle_moe_mxfp4_bf16.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, i64, p]
         _lib = L
@@ -166,6 +170,23 @@ def gemm_w8a8(a, s_a, w, s_w, *, rows=None):
     if rc:
         raise ValueError(f"oracle gemm_w8a8 failed ({rc})")
     return acc, out
+
+
+def bf16_encode(x: float) -> int:
+    """bf16 bits of x, round to nearest even."""
+    return int(lib().hq_oracle_bf16_encode(float(x)))
+
+
+def silu_mul_bf16(x: np.ndarray) -> np.ndarray:
+    """SwiGLU between the MoE projections ("Humming wird angekuendigt", section
+    "Leistung"): x [rows][2I] bf16 bits (gate | up) -> bf16 bits [rows][I] of
+    silu(gate) * up in double, rounded once to nearest even."""
+    rows, two_i = x.shape
+    I = two_i // 2
+    src = _c(x, np.uint16)
+    out = np.empty((rows, I), dtype=np.uint16)
+    lib().hq_oracle_silu_mul_bf16(rows, I, _ptr(src), _ptr(out))
+    return out
 
 
 def moe_route(ids: np.ndarray, E: int):

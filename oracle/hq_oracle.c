@@ -252,6 +252,47 @@ int hq_oracle_moe_route(int64_t T, int64_t top_k, int64_t E, const int32_t* ids,
     return 0;
 }
 
+/* bf16 bits of x rounded to nearest, ties to even (overflow -> inf, NaN -> quiet
+ * NaN).  Exact: |x| / q with q the bf16 quantum of x's binade (2^(E-7), or
+ * 2^-133 below the normal range) is a power-of-two scaling, nearbyint rounds
+ * it to an integer under the default round-to-nearest-even mode, and r * q is
+ * representable in bf16, hence in float, whose top 16 bits are its encoding. */
+static uint16_t bf16_rne(double x)
+{
+    if (x != x) return 0x7FC0;
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                       /* a = m * 2^e, m in [0.5, 1): binade exponent e - 1 */
+    const int E = e - 1 < -126 ? -126 : e - 1;
+    const int qexp = e - 1 < -126 ? -133 : E - 7;
+    const double r = nearbyint(ldexp(a, -qexp));
+    const double v = ldexp(r, qexp);
+    if (v > 3.3895313892515355e38) return sign | 0x7F80;   /* beyond the largest bf16 */
+    const float f = (float)v;
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    return sign | (uint16_t)(bits >> 16);
+}
+
+uint16_t hq_oracle_bf16_encode(double x) { return bf16_rne(x); }
+
+/* The activation between the MoE gate-up and down projections ("Humming wird
+ * angekuendigt", section "Leistung": the MoE figures add the gate-up and down
+ * GEMMs; the pages name no activation, and the plain reading of a fused gate+up
+ * output is SiLU(gate) * up with the gate in the first half of each row).
+ * in [rows][2I] bf16 bits; out[r][i] = bf16_rne(silu(g) * u), g = in[r][i],
+ * u = in[r][I + i], silu(g) = g / (1 + e^-g), all in double. */
+void hq_oracle_silu_mul_bf16(int64_t rows, int64_t I, const uint16_t* in, uint16_t* out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t i = 0; i < I; ++i) {
+            const double g = hq_oracle_bf16(in[r * 2 * I + i]), u = hq_oracle_bf16(in[r * 2 * I + I + i]);
+            out[r * I + i] = bf16_rne(g / (1.0 + exp(-g)) * u);
+        }
+}
+
 /* MoE W4A16-MXFP4 (bf16 tokens): for each requested pair p (t = p / top_k),
  * out[i][:] = A[t][:] x W_real[ids[p]] with W_real as in the W4A8-MXFP4 entry.
  * q is expert-stacked [E][K/8][N], e8 is [E][K/32][N]. Each expert's weights

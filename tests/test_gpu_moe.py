@@ -135,3 +135,102 @@ def test_moe_full_size_sampled(T):
     note(f"moe full T={T}: generating {len(needed)} experts")
     d = syn.moe_mxfp4(0, T, E, top_k, N, K, experts=needed)
     check(run_moe(T, E, top_k, N, K, data=d, pairs=pairs))
+
+
+# ---------------------------------------------------------------------------
+# the MoE down projection: SwiGLU between the projections, then the expert GEMM
+# on the activated rows (Indexed with one row per pair)
+# ---------------------------------------------------------------------------
+
+def ordered16(bits):
+    """bf16 bits -> integers ordered like the values (adjacent values differ by 1)."""
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def gpu_silu_mul(x_bits):
+    rows, two_i = x_bits.shape
+    out = empty(rows * two_i)
+    hq.hq_silu_mul(hq.HQ_DT_BF16, rows, two_i // 2, dev(x_bits), out)
+    torch.cuda.synchronize()
+    return out[: rows * two_i].cpu().numpy().view(np.uint16).reshape(rows, two_i // 2)
+
+
+def check_silu(got, x_bits):
+    """fp32 arithmetic vs the fp64 oracle: at most one bf16 step where the result is a
+    normal bf16; below 2^-126 (where fp32 itself runs out of precision) within 2^-126."""
+    want = oracle.silu_mul_bf16(x_bits)
+    gv, wv = to_f64(got, torch.bfloat16), to_f64(want, torch.bfloat16)
+    steps = np.abs(ordered16(got) - ordered16(want))
+    normal = np.abs(wv) >= 2.0 ** -126
+    bad = (normal & (steps > 1)) | (~normal & (np.abs(gv - wv) > 2.0 ** -126))
+    if bad.any():
+        r, i = np.argwhere(bad)[0]
+        I = got.shape[1]
+        g, u = to_f64(x_bits[r:r + 1, [i, I + i]], torch.bfloat16)[0]
+        raise AssertionError(f"row {r} col {i}: gate {g!r} up {u!r} got {gv[r, i]!r} want {wv[r, i]!r}")
+    assert (steps > 0).mean() <= 0.01, (steps > 0).mean()
+
+
+@pytest.mark.parametrize("rows,I", [(1, 8), (7, 2048), (300, 136)])
+# gates below about -88.7 overflow e^-g in fp32 (-89.5 x 53.5 must still give -6.5e-36)
+def test_silu_mul_matches_oracle(rows, I):
+    note(f"silu_mul rows={rows} I={I}")
+    x = syn._to16(syn.normal_rows(rows, 5, 9, rows, 2 * I, sigma=3.0), torch.bfloat16)
+    x[0, :8] = syn._to16(np.array([0.0, -0.0, 1e-30, -1e-30, 40.0, -80.0, -89.5, -120.0], np.float32), torch.bfloat16)
+    check_silu(gpu_silu_mul(x), x)
+
+
+def test_silu_mul_rejects_bad_shapes():
+    x = empty(64)
+    with pytest.raises(hq.HQError):
+        hq.hq_silu_mul(hq.HQ_DT_BF16, 1, 12, x, x)          # I not a multiple of 8
+    with pytest.raises(hq.HQError):
+        hq.hq_silu_mul(hq.HQ_DT_FP16, 1, 8, x, x)            # bf16 only
+
+
+def run_layer(T, E, top_k, I, K1, N2, seed=0, pairs=None, experts=None):
+    """Gate-up (N = 2I, K = K1) -> SwiGLU -> down (N = N2, K = I), all through the C ABI;
+    the activation and the down projection are each checked against the oracle on the
+    GPU's own input to that step."""
+    d1 = syn.moe_mxfp4(seed, T, E, top_k, 2 * I, K1, experts=experts)
+    d2 = syn.moe_mxfp4(seed + 1, 1, E, 1, N2, I, experts=experts)
+    ids = d1["ids"]
+    P = T * top_k
+    pr = np.arange(P) if pairs is None else np.asarray(pairs)
+    note(f"moe layer T={T} E={E} top_k={top_k} I={I} K1={K1} N2={N2}")
+    desc1, desc2 = hq.desc_moe_mxfp4(E, 2 * I, K1), hq.desc_moe_mxfp4(E, N2, I)
+    w1, s1, _ = hq.hq_repack(desc1, d1["q"], d1["e"])
+    w2, s2, _ = hq.hq_repack(desc2, d2["q"], d2["e"])
+    nb = max(hq.hq_workspace_bytes(desc1, T, top_k), hq.hq_workspace_bytes(desc2, P, 1))
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    D1, H, D2 = empty(P * 2 * I * 2), empty(P * I * 2), empty(P * N2 * 2)
+    hq.hq_moe_gemm(desc1, hq.HQ_MOE_INDEXED, T, top_k, dev(d1["A"]), None, i32(ids), None, dev(w1), dev(s1), None,
+                   D1, ws, nb)
+    hq.hq_silu_mul(hq.HQ_DT_BF16, P, I, D1, H)
+    flat = ids.reshape(P, 1)
+    hq.hq_moe_gemm(desc2, hq.HQ_MOE_INDEXED, P, 1, H, None, i32(flat), None, dev(w2), dev(s2), None, D2, ws, nb)
+    torch.cuda.synchronize()
+    d1_bits = D1[: P * 2 * I * 2].cpu().numpy().view(np.uint16).reshape(P, 2 * I)
+    h_bits = H[: P * I * 2].cpu().numpy().view(np.uint16).reshape(P, I)
+    check_silu(h_bits[pr], d1_bits[pr])
+    O = oracle.moe_mxfp4_bf16(h_bits, flat, d2["q"], d2["e"], N=N2, K=I, pairs=pr)
+    Dh = to_f64(D2[: P * N2 * 2].cpu().numpy().view(np.uint16).reshape(P, N2), torch.bfloat16)
+    err = gate_error(Dh[pr], O)
+    assert np.all(np.isfinite(Dh[pr]))
+    assert err <= min(GATE, 8e-3), err
+
+
+@pytest.mark.parametrize("T", [3, 33, 300])
+def test_moe_down_projection_small(T):
+    """Both streaming paths (in-kernel routing below 4 rows, routed tier-0) and the tiled tiers."""
+    run_layer(T, 8, 2, 128, 256, 384, seed=T)
+
+
+def test_moe_down_projection_full_size():
+    """The MoE layer at its real shape: gate-up N=4096 K=7168, down N=7168 K=2048, E=256 top-8."""
+    T, E, top_k = 8, 256, 8
+    ids = syn.zipf_topk(0, syn.C5, T, E, top_k)
+    needed = sorted(set(int(e) for e in ids.reshape(-1)))
+    pairs = np.arange(0, T * top_k, 3)
+    run_layer(T, E, top_k, 2048, 7168, 7168, seed=0, pairs=pairs, experts=needed)

@@ -368,3 +368,52 @@ def test_moe_pairs_are_per_expert_dense_and_indexed_grouped_agree():
     _, _, perm = oracle.moe_route(d["ids"], E)
     grouped = oracle.moe_mxfp4_bf16(d["A"], d["ids"], d["q"], d["e"], N=N, K=K, pairs=perm)
     np.testing.assert_array_equal(grouped, full[perm])
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU between the MoE projections: bf16 rounding and silu
+# ---------------------------------------------------------------------------
+
+def test_bf16_encode_special_cases():
+    cases = {
+        1.0: 0x3F80, -2.5: 0xC020, 0.0: 0x0000,
+        1 + 2 ** -8: 0x3F80,                 # halfway between 1 and 1 + 2^-7: to the even 1
+        1 + 3 * 2 ** -8: 0x3F82,             # halfway between 1 + 2^-7 and 1 + 2^-6: to the even upper
+        2.0 ** -133: 0x0001,                 # smallest subnormal
+        2.0 ** -134: 0x0000,                 # halfway between 0 and it: to the even 0
+        1.5 * 2.0 ** -134: 0x0001,
+        (2 - 2 ** -7) * 2.0 ** 127: 0x7F7F,  # largest finite
+        3.4e38: 0x7F80,                      # rounds past it: inf
+    }
+    for x, bits in cases.items():
+        assert oracle.bf16_encode(x) == bits, (x, hex(oracle.bf16_encode(x)))
+    assert oracle.bf16_encode(-0.0) == 0x8000            # (a separate key: -0.0 == 0.0 in a dict)
+    assert oracle.bf16_encode(float("nan")) & 0x7FC0 == 0x7FC0
+
+
+def test_bf16_encode_matches_torch_on_float32():
+    """On float32 inputs (normal, subnormal, huge) the encoder equals torch's RNE cast."""
+    rng = np.random.default_rng(11)
+    f = np.concatenate([rng.standard_normal(20000).astype(np.float32) * np.float32(3),
+                        (rng.standard_normal(5000) * 1e-39).astype(np.float32),
+                        (rng.standard_normal(5000) * 1e38).astype(np.float32)])
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_encode(float(v)) for v in f], dtype=np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_silu_mul_matches_independent_formula():
+    """silu(g) * u with silu written as g (1 + tanh(g / 2)) / 2, gate = first half of
+    each row, up = second half, rounded once: any swap of the halves, row-stride
+    slip or dropped factor fails here."""
+    rows, I = 5, 24
+    bits = syn._to16(syn.normal_rows(4, 1, 9, rows, 2 * I, sigma=3.0), torch.bfloat16)
+    bits[0, :4] = syn._to16(np.array([0.0, -0.0, 30.0, -30.0], np.float32), torch.bfloat16)
+    x = torch16(bits, torch.bfloat16)
+    got = oracle.silu_mul_bf16(bits)
+    for r in range(rows):
+        for i in range(I):
+            g, u = x[r, i], x[r, I + i]
+            want = oracle.bf16_encode(g * (1.0 + math.tanh(g / 2.0)) / 2.0 * u)
+            assert got[r, i] == want, (r, i, g, u)
+    assert got[0, 0] in (0, 0x8000) and got[0, 1] in (0, 0x8000)   # silu(+-0) * u is a zero
