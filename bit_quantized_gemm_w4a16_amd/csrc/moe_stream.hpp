@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void moe_stream_kernel(MoeStreamArgs p) {
 // `gy` workgroup rows walk the tiles, and enough workgroup columns that the
 // chip holds about four workgroups per CU, each wave taking at least one strip.
 // The strip's batches come from the smallest instantiated CB x NB that covers
-// K (K=7168: 7 x 8 exactly).
+// K (K=7168: 7 x 8 exactly; K=2048: 8 x 2).
 inline bool moe_stream_fits(int nc) { return nc <= 8 * 16; }
 
 template <int CB, int NB>
@@ -310,6 +310,7 @@ inline hipError_t launch_moe_stream(const MoeStreamArgs& s, int rows_max, int64_
     const dim3 grid((unsigned)gx, (unsigned)gy);
     const int nc = s.nc;
     if (nc <= 8) return launch_moe_stream_k<4, 2>(s, (size_t)lds, grid, st);
+    if (nc <= 16) return launch_moe_stream_k<8, 2>(s, (size_t)lds, grid, st);  // K = 2048 (down projection)
     if (nc <= 32) return launch_moe_stream_k<8, 4>(s, (size_t)lds, grid, st);
     if (nc <= 56) return launch_moe_stream_k<7, 8>(s, (size_t)lds, grid, st);
     if (nc <= 64) return launch_moe_stream_k<8, 8>(s, (size_t)lds, grid, st);
