@@ -271,8 +271,8 @@ size_t al16(size_t b) { return (b + 15) / 16 * 16; }
 // Upper bounds of the tier lists (the real lengths are known only on the device).
 static int64_t moe_max_tiles(int tier, int64_t P, int E) {
     const int64_t ex = E < P ? E : P;  // experts that can hold a row
-    if (tier == 0)                     // one 4-row m-tile per small expert; all pairs when P is tiny
-        return P <= kMoeAllSmallP ? cdiv(P, kMoeSmallRows) + ex : ex;
+    if (tier == 0)                     // one m-tile of at most kMoeSmallRows rows per small expert
+        return ex;
     if (tier == 1) {                   // at most kMoeMidMax / kMoeMidBM tiles per mid expert
         const int64_t a = cdiv(kMoeMidMax, kMoeMidBM) * ex, b = cdiv(P, kMoeMidBM) + ex;
         return a < b ? a : b;
@@ -362,18 +362,18 @@ static MoeStreamArgs moe_stream_args(const MoeArgs& a, int nc) {
     return s;
 }
 
-// Fewer than kMoeSmallRows tokens (so at most kMoeAllSmallP pairs): one launch
-// of the weight-streaming kernel, whose workgroups each build the m-tile list
-// from the ids or offsets (no routing pass).  A token picks an expert at most
-// once, so an expert has at most T rows: tiles of T rows cover each expert
-// once and the A rows held in LDS shrink with T, which leaves room for more
-// workgroups per CU.  (Tiles never exceed T rows whatever the ids, so repeated
-// ids only cost extra tiles.)  From kMoeSmallRows tokens on, the LDS no longer
-// shrinks and a routing pass of its own measured faster than every workgroup
-// building the list.
+// At most kMoeAllSmallP pairs: one launch of the weight-streaming kernel, whose
+// workgroups each build the m-tile list from the ids or offsets (no routing
+// pass; measured faster than a routing launch of its own at every such size).
+// A token picks an expert at most once, so an expert has at most T rows: tiles
+// of min(T, kMoeSmallRows) rows cover each expert in as few tiles as the
+// streaming kernel's row limit allows, and below kMoeSmallRows tokens the A
+// rows held in LDS shrink with T, which leaves room for more workgroups per
+// CU.  (Tiles never exceed that many rows whatever the ids, so repeated ids
+// only cost extra tiles.)
 static_assert(kMoeAllSmallP <= kRouteMaxP, "the in-kernel routing handles one pair per lane");
 static hipError_t moe_all_small_launch(const MoeArgs& a, int64_t P, int nc) {
-    const int cap = (int)a.T;
+    const int cap = (int)(a.T < kMoeSmallRows ? a.T : kMoeSmallRows);
     MoeStreamArgs s = moe_stream_args(a, nc);
     s.route_ids = a.indexed ? a.topk_ids : nullptr;
     s.route_off = a.indexed ? nullptr : a.expert_offsets;
@@ -397,15 +397,14 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     // With few pairs in total no expert can fill a tile: every expert takes the
     // streaming path (several m-tiles if it must) and no tiled launch is made.
     const bool all_small = small_ok && P <= kMoeAllSmallP;
-    if (all_small && a.T < kMoeSmallRows) return moe_all_small_launch(a, P, nc);
+    if (all_small) return moe_all_small_launch(a, P, nc);
     MoeLayout L = moe_layout(a.T, a.top_k, a.E, a.indexed);
     char* ws = (char*)a.ws;
     int* ntiles = (int*)(ws + L.ntiles);
     int* tl[4];
     for (int i = 0; i < 4; ++i) tl[i] = (int*)(ws + L.tiles_tier[i]);
     MoeTiers tiers{};
-    tiers.t[0] = TileList{tl[0], ntiles + 0, (int)L.max_tier[0], kMoeSmallRows,
-                          all_small ? (1 << 30) : small_ok ? kMoeSmallRows : 0};
+    tiers.t[0] = TileList{tl[0], ntiles + 0, (int)L.max_tier[0], kMoeSmallRows, small_ok ? kMoeSmallRows : 0};
     tiers.t[1] = TileList{tl[1], ntiles + 1, (int)L.max_tier[1], kMoeMidBM, kMoeMidMax};
     tiers.t[2] = TileList{tl[2], ntiles + 2, (int)L.max_tier[2], kMoeBM, kMoeBigMax};
     tiers.t[3] = TileList{tl[3], ntiles + 3, (int)L.max_tier[3], kMoeHugeBM, 1 << 30};
@@ -452,7 +451,6 @@ hipError_t moe_gemm_launch(const MoeArgs& a) {
     p.splits = 1;
     p.sorted = sorted;
     p.top_k = a.top_k;
-    if (all_small) return hipSuccess;
     p.tiles_m = (int)L.max_tier[1];
     p.tile_info = tl[1];
     p.ntiles = ntiles + 1;

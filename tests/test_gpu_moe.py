@@ -94,10 +94,10 @@ def test_moe_small(T):
 
 @pytest.mark.parametrize("T,E,top_k", [(1, 64, 64), (2, 3, 2), (3, 40, 8), (16, 4, 4), (64, 3, 1)])
 def test_moe_small_pair_counts(T, E, top_k):
-    """At most 64 pairs.  Below 4 tokens the streaming kernel builds its tile
-    list itself: 64 one-row tiles (the list's limit), two-row tiles, three-row
-    tiles.  From 4 tokens on, every expert still takes the streaming kernel,
-    several 4-row tiles per busy expert."""
+    """At most 64 pairs: the streaming kernel builds its tile list itself, in
+    tiles of min(T, 4) rows: 64 one-row tiles (the list's limit), two-row
+    tiles, three-row tiles, and from 4 tokens on several 4-row tiles per busy
+    expert."""
     check(run_moe(T, E, top_k, 160, 256, seed=T + E))
 
 
