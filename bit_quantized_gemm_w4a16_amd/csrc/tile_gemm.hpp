@@ -929,7 +929,12 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
     p.splits = pl.splits;
     if constexpr (F == Fmt::W8A8_I8) {
         if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
-        if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 4>(p, st);
+        if (pl.BM == 256) {
+            // where 256 x 128 ring tiles need two rounds and 256 x 256 tiles fit one
+            if (((p.M + 255) / 256) * ((p.Np + 127) / 128) > 256 && ((p.M + 255) / 256) * ((p.Np + 255) / 256) <= 256)
+                return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
+            return launch_tile_kernel<F, 256, 128, 2, 4, 4>(p, st);
+        }
         // the rings run one workgroup per CU: keep the grid to one round, with
         // 256-row tiles where 128-row ones would need two, and the K split
         // rounded down
