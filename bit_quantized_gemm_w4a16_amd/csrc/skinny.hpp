@@ -449,7 +449,8 @@ struct SkinnyPlan {
 };
 
 inline int skinny_round_cpw(int64_t per, int spw) {
-    if (spw == 1) return per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
+    // 14: a wave's quarter of K = 7168 exactly (16 would add two dead loads per wave)
+    if (spw == 1) return per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : per == 14 ? 14 : 16;
     return per <= 2 ? 2 : per <= 4 ? 4 : 8;
 }
 
@@ -566,6 +567,9 @@ hipError_t launch_skinny_cpw(int cpw, dim3 grid, int lds_bytes, const SkinnyArgs
         case 2: return launch_skinny_k<F, MT, SPW, 2>(grid, lds_bytes, a, st);
         case 4: return launch_skinny_k<F, MT, SPW, 4>(grid, lds_bytes, a, st);
         case 8: return launch_skinny_k<F, MT, SPW, 8>(grid, lds_bytes, a, st);
+        case 14:
+            if constexpr (SPW == 1) return launch_skinny_k<F, MT, SPW, 14>(grid, lds_bytes, a, st);
+            else return hipErrorInvalidValue;
         default:
             if constexpr (SPW * 16 * FmtTraits<F>::BSTRIP / 1024 < 64) return launch_skinny_k<F, MT, SPW, 16>(grid, lds_bytes, a, st);
             else return launch_skinny_k<F, MT, SPW, 8>(grid, lds_bytes, a, st);
