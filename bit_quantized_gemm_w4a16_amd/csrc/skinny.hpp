@@ -483,7 +483,9 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G) {
     p.WS = p.NS / p.SPW;
     const int WK = 4 / p.WS;
     p.groups_x = cdiv(nstrips, p.NS);
-    int64_t S = cdiv(256, p.groups_x);
+    // a K split costs partial tiles and a finalize launch (~3 us): only when the
+    // strips alone leave a quarter of the chip idle (or the slice must shrink)
+    int64_t S = p.groups_x >= 192 ? 1 : cdiv(256, p.groups_x);
     const int64_t smax = nc / WK > 0 ? nc / WK : 1;
     const int nb = F == Fmt::W8A8_I8 ? 2 : 1;
     const int64_t cap = p.SPW * 16 * nb < 64 ? 16 : 8;  // largest register batch instantiated
