@@ -478,6 +478,9 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G) {
     const int gch = G >= 128 ? G / 128 : 1;
     SkinnyPlan p{};
     p.NS = M <= 8 ? 1 : M <= 16 ? 2 : M <= 32 ? 4 : 8;
+    // W4A8 at M <= 32: two strips per workgroup keep 224 workgroups at N = 7168
+    // and the whole 8-bit A slice in LDS, so no K split (and no finalize pass)
+    if (F == Fmt::W4A8_MX && M <= 32 && M * (K / 128) * 128 + 2 * (K / 128) * 64 <= kSkinnyLds) p.NS = M <= 8 ? 1 : 2;
     while (p.NS > 1 && p.NS > nstrips) p.NS /= 2;
     p.SPW = p.NS <= 4 ? 1 : p.NS / 4;
     p.WS = p.NS / p.SPW;

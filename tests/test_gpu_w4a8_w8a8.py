@@ -51,7 +51,7 @@ def run_w4a8(M, N, K, seed=0, data=None, rows=None):
     return Dh[r], O
 
 
-@pytest.mark.parametrize("M", [1, 3, 16, 64, 100, 257])
+@pytest.mark.parametrize("M", [1, 3, 16, 24, 32, 64, 100, 257])
 def test_w4a8_small_shapes(M):
     Dr, O = run_w4a8(M, 272, 512, seed=M)
     err = gate_error(Dr, O)
