@@ -81,7 +81,7 @@ def test_w4a8_big_tiles_ragged(M, N, K):
     assert err <= min(GATE, 8e-3), err
 
 
-@pytest.mark.parametrize("M", [1, 16, 256, 2048, 8192])
+@pytest.mark.parametrize("M", [1, 16, 32, 256, 2048, 8192])
 def test_w4a8_full_size(M):
     """The dense W4A8-MXFP4 workload: N=7168, K=4096 (sampled rows at large M)."""
     Dr, O = run_w4a8(M, 7168, 4096, seed=0)
