@@ -3,15 +3,18 @@
 // "Humming wird angekuendigt", section "WnA16": MoE runs on an Indexed path
 // (token rows gathered per expert by index) and a Grouped path (tokens sorted
 // by expert, contiguous per expert); the work per expert varies with the
-// routing.  Both paths here share one tiled MFMA kernel over a device-built
-// list of m-tiles (expert, first sorted row, row count): experts with many
-// tokens get many tiles, experts with none get none, and the grid is sized by
+// routing.  Both paths share one schedule over device-built lists of m-tiles
+// (expert, first sorted row, row count), one list per tier of experts by row
+// count: the weight-streaming kernel (moe_stream.hpp) for experts with a few
+// rows, tiled MFMA kernels of growing height for the rest.  Experts with many
+// tokens get many tiles, experts with none get none, and each grid is sized by
 // the host from an upper bound so no host synchronisation is needed.
 //
 // Routing metadata is a stable counting sort of the flattened pairs
 // p = t * top_k + j by expert id: per-chunk histograms and in-chunk ranks,
 // a per-expert scan over chunks, one workgroup for the expert offsets and the
-// m-tile list, then the scatter.
+// m-tile lists, then the scatter (one workgroup does it all up to 1024 pairs;
+// up to 64 pairs the streaming kernel's workgroups build their list in LDS).
 #include "hq_device.hpp"
 #include "hq_internal.h"
 #include "moe_stream.hpp"
