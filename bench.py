@@ -6,9 +6,10 @@ M in {1, 2, 4, ..., 8192} one library call (host dispatch -> HIP kernels ->
 output) on inputs already resident in HBM.  The default workload is the
 dense W4A16 asymmetric layer (fp16 activations, UINT4 weights with UINT4
 zero-points and fp16 scales per 128 K, N=4096, K=7168), the configuration
-the metric is quoted on.  --config c1|c3|c4|c5|c5l|all measures the other
-workloads (one JSON line each); c5l is the whole MoE layer the pages time
-(gate-up GEMM, SwiGLU, down-projection GEMM).
+the metric is quoted on.  --config c1|c3|c4|c5|c5g|c5l|all measures the other
+workloads (one JSON line each); c5 is the MoE gate-up on the Indexed path, c5g
+the same on the Grouped path, c5l the whole MoE layer the pages time (gate-up
+GEMM, SwiGLU, down-projection GEMM).
 
 Cold cache: the packed weights are replicated into enough device copies
 (> 512 MiB in total, more than the 256 MiB Infinity Cache plus every L2) and
@@ -278,6 +279,39 @@ class MoEMXFP4:
                                           f"({len(sub_e)} experts touched), fp64 accumulation, {dt:.1f} s")
 
 
+class MoEGroupedMXFP4(MoEMXFP4):
+    """The same MoE gate+up on the Grouped path: tokens already sorted by expert
+    (the Grouped path's input).  The expert offsets and the sorted rows are built
+    once per T with the library's own routing and gather (hq_moe_align,
+    hq_moe_gather) before timing; each timed call is the expert GEMM alone."""
+
+    def __init__(self):
+        super().__init__(mode="grouped")
+        E, k, K = self.E, self.top_k, self.K
+        self.rows = {}
+        for T in self.sweep:
+            P = T * k
+            offs = torch.empty(E + 4, dtype=torch.int32, device="cuda")
+            srt = torch.empty(max(P, 4), dtype=torch.int32, device="cuda")
+            nb = hq.hq_workspace_bytes(self.desc, T, k)
+            ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+            hq.hq_moe_align(T, k, E, self.ids, offs, srt, ws, nb)
+            As = torch.empty(P * K * 2, dtype=torch.uint8, device="cuda")
+            hq.hq_moe_gather(hq.HQ_DT_BF16, T, k, K, self.A, srt, As)
+            self.rows[T] = (As, offs)
+        torch.cuda.synchronize()
+
+    def bytes(self, T):
+        P = T * self.top_k
+        return self.active[T] * self.ebytes + P * self.K * 2 + P * self.N * 2 + (self.E + 1) * 4
+
+    def call(self, T, c):
+        w, e = self.copies[c]
+        As, offs = self.rows[T]
+        hq.hq_moe_gemm(self.desc, hq.HQ_MOE_GROUPED, T, self.top_k, As, None, None, offs, w, e, None, self.D,
+                       self.ws, self.ws_bytes)
+
+
 class MoELayerMXFP4(MoEMXFP4):
     """The MoE layer the pages time (gate-up + down): gate-up W4A16-MXFP4 (N=4096, K=7168,
     Indexed), SwiGLU, down projection (N=7168, K=2048, Indexed with one row per pair),
@@ -335,6 +369,7 @@ WORKLOADS = {
     "c3": lambda: DenseW4A8(),
     "c4": lambda: DenseW8A8(),
     "c5": lambda: MoEMXFP4(),
+    "c5g": lambda: MoEGroupedMXFP4(),
     "c5l": lambda: MoELayerMXFP4(),
 }
 
@@ -513,7 +548,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="c2", help="c1|c2|c3|c4|c5|c5l|all (default c2; c5l = MoE gate-up + SwiGLU + down)")
+    ap.add_argument("--config", default="c2", help="c1|c2|c3|c4|c5|c5g|c5l|all (default c2; c5g = MoE on the Grouped path, c5l = MoE gate-up + SwiGLU + down)")
     ap.add_argument("--sweep", default=None, help="comma-separated M values (default 1..8192 powers of 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="issue calls directly instead of replaying HIP graphs "
