@@ -114,6 +114,20 @@ def test_moe_one_hot_expert_and_empty_experts():
     check(run_moe(T, E, top_k, N, K, data=d))
 
 
+def test_moe_every_small_row_count():
+    """Experts holding 0..12 rows in one routed call (78 pairs, above the
+    in-kernel routing limit): up to 4 rows they take the streaming kernel, from
+    5 rows the 32-row tiled tier."""
+    E, N, K = 13, 256, 384
+    counts = np.arange(E)
+    T = int(counts.sum())
+    d = syn.moe_mxfp4(21, T, E, 1, N, K)
+    ids = np.repeat(np.arange(E), counts)
+    np.random.default_rng(21).shuffle(ids)
+    d["ids"] = ids.reshape(T, 1).astype(d["ids"].dtype)
+    check(run_moe(T, E, 1, N, K, data=d))
+
+
 def test_moe_single_expert_top1_equals_dense():
     T, E, N, K = 65, 1, 256, 384
     check(run_moe(T, E, 1, N, K, seed=9))
