@@ -172,6 +172,32 @@ class DenseW4A8:
         w, e = self.copies[c]
         hq.hq_gemm(self.desc, M, self.A, self.s_a, w, e, None, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
 
+    def aux(self, reps=20):
+        """The activation quantisation before the GEMM (outside the timed
+        sweep): fp32 [Mmax][K] in, e4m3 codes + one fp32 scale per row out,
+        timed alone with HIP events on the launching stream; two input copies
+        used in turn (268 MB together) so that no call finds its input in the
+        Infinity Cache."""
+        xs = [dev(self.host["A0"]) for _ in range(2)]
+        q = torch.empty_like(self.A)
+        s = torch.empty_like(self.s_a)
+        f = lambda i: hq.hq_quantize_act(hq.HQ_DT_FP8_E4M3, self.Mmax, self.K, xs[i % 2], q, s)
+        for i in range(4):
+            f(i)
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for i in range(reps):
+            f(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        B = self.Mmax * self.K * 5 + 4 * self.Mmax
+        del xs, q, s
+        return {"act_quant": dict(kernel="quant_e4m3_rows_kernel", M=self.Mmax, K=self.K, us=round(t * 1e6, 2),
+                                  algorithmic_bytes=B, gbps=round(B / t / 1e9, 1),
+                                  hbm_frac=round(B / t / PEAK_HBM, 3))}
+
     def cpu_baseline(self, budget_s=16.0):
         import oracle
         d = self.host
@@ -540,6 +566,7 @@ def report(work, args, wall, per):
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_M": table,
+        **({"aux": work.aux()} if hasattr(work, "aux") else {}),
     }
 
 

@@ -53,8 +53,66 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(const float* __restrict
     }
 }
 
+// The same quantisation for rows whose length K is a multiple of 4 and at
+// most 1024 * NV: each thread holds NV groups of 4 consecutive elements in
+// registers (16-byte loads, x read once), the row maximum is reduced across
+// the wave by shuffles and across the 4 waves through LDS, and each group's
+// four codes leave as one coalesced 32-bit store.  Same arithmetic as above,
+// so both kernels give identical codes and scales.
+template <int NV>
+__global__ __launch_bounds__(256) void quant_e4m3_rows_kernel(const float4* __restrict__ x, int K4,
+                                                              uint32_t* __restrict__ q, float* __restrict__ s) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float4* xr = x + row * K4;
+    float4 v[NV];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = j * 256 + (int)threadIdx.x;
+        v[j] = i < K4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (threadIdx.x == 0) s[row] = sc;
+    uint32_t* qr = q + row * K4;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = j * 256 + (int)threadIdx.x;
+        if (i < K4) {
+            const float a = fminf(fmaxf(v[j].x / sc, -448.f), 448.f);
+            const float b = fminf(fmaxf(v[j].y / sc, -448.f), 448.f);
+            const float c = fminf(fmaxf(v[j].z / sc, -448.f), 448.f);
+            const float d = fminf(fmaxf(v[j].w / sc, -448.f), 448.f);
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);  // bytes 0, 1
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, pk, true);      // bytes 2, 3
+            qr[i] = (uint32_t)pk;
+        }
+    }
+}
+
 hipError_t quant_e4m3_launch(int64_t M, int64_t K, const float* x, uint8_t* q, float* s, hipStream_t st) {
-    hipLaunchKernelGGL(quant_e4m3_kernel, dim3((unsigned)M), dim3(256), 0, st, x, (int)K, q, s);
+    const dim3 grid((unsigned)M), blk(256);
+    if (K % 4 == 0 && K <= 8192) {  // x and q are 16-byte aligned: 16-byte rows of x, 4-byte rows of q
+        const int K4 = (int)(K / 4), nv = (K4 + 255) / 256;
+        const float4* xv = (const float4*)x;
+        uint32_t* qv = (uint32_t*)q;
+        if (nv <= 1)
+            hipLaunchKernelGGL(quant_e4m3_rows_kernel<1>, grid, blk, 0, st, xv, K4, qv, s);
+        else if (nv <= 2)
+            hipLaunchKernelGGL(quant_e4m3_rows_kernel<2>, grid, blk, 0, st, xv, K4, qv, s);
+        else if (nv <= 4)
+            hipLaunchKernelGGL(quant_e4m3_rows_kernel<4>, grid, blk, 0, st, xv, K4, qv, s);
+        else
+            hipLaunchKernelGGL(quant_e4m3_rows_kernel<8>, grid, blk, 0, st, xv, K4, qv, s);
+    } else {
+        hipLaunchKernelGGL(quant_e4m3_kernel, grid, blk, 0, st, x, (int)K, q, s);
+    }
     return hipGetLastError();
 }
 

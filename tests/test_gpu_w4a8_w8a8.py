@@ -22,7 +22,10 @@ def gpu_quant(A0):
     return q[: M * K].cpu().numpy().reshape(M, K), s[:M].cpu().numpy()
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (5, 4096), (64, 1000), (300, 4096)])
+# K a multiple of 4 up to 8192: the register-held row kernel (1, 2, 4 and 8
+# float4 per thread, with ragged tails); other K: the generic kernel.
+@pytest.mark.parametrize("M,K", [(1, 4), (1, 128), (5, 4096), (64, 1000), (300, 4096), (9, 2052), (2, 8192),
+                                 (7, 1001), (3, 10000), (4, 8196)])
 def test_quantize_act_bit_exact(M, K):
     note(f"quant_e4m3 M={M} K={K}")
     A0 = syn.normal_rows(3, 3, syn.T_A, M, K)
