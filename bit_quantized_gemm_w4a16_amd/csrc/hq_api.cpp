@@ -31,6 +31,23 @@ hq_status set_error(hq_status st, const char* fmt, ...) {
     return st;
 }
 
+namespace {
+thread_local PlanRecorder* g_plan = nullptr;
+}
+
+PlanRecorder* plan_recorder() { return g_plan; }
+
+void plan_record(const char* fmt, ...) {
+    PlanRecorder* r = g_plan;
+    if (!r || r->used + 1 >= r->len) return;
+    if (r->used) r->buf[r->used++] = ';';
+    va_list ap;
+    va_start(ap, fmt);
+    const int n = vsnprintf(r->buf + r->used, r->len - r->used, fmt, ap);
+    va_end(ap);
+    if (n > 0) r->used += (size_t)n < r->len - r->used ? (size_t)n : r->len - r->used - 1;
+}
+
 static hq_status ok() {
     g_err[0] = 0;
     return HQ_OK;
@@ -100,7 +117,16 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
     } else {
         return set_error(HQ_ERR_UNSUPPORTED, "unsupported activation/weight dtype pair (%d, %d)", a, w);
     }
-    if (I.Np / 16 > kMaxCounters) return set_error(HQ_ERR_UNSUPPORTED, "N too large");
+    {
+        // the kernels address one expert's packed tensors with 32-bit buffer offsets
+        LayerInfo one = I;
+        one.E = 1;
+        size_t wb, sb, zb, s2b;
+        packed_sizes(one, &wb, &sb, &zb, &s2b);
+        if (wb >= ((size_t)1 << 32) || sb >= ((size_t)1 << 32))
+            return set_error(HQ_ERR_UNSUPPORTED, "one expert's packed weights or scales reach 4 GiB (N=%lld K=%lld)",
+                             (long long)d->N, (long long)d->K);
+    }
     *L = I;
     return HQ_OK;
 }
@@ -117,6 +143,15 @@ static size_t dense_workspace(const LayerInfo& L, int64_t M) {
 static hq_status hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();
     return set_error(HQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
+    switch (L.kind) {
+        case Kind::WNA16: return hip_status(wna16_launch(a, L.a_bf16, L.zp), "hq_gemm(W4A16)");
+        case Kind::W4A8_MX: return hip_status(w4a8_launch(a), "hq_gemm(W4A8-MXFP4)");
+        case Kind::W8A8: return hip_status(w8a8_launch(a, L.out_i32), "hq_gemm(W8A8)");
+        default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind runs through hq_moe_gemm");
+    }
 }
 
 }  // namespace hq
@@ -221,12 +256,25 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const flo
         if (!aligned16(workspace)) return set_error(HQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
     }
     DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, a_scale, w, s, z, D, workspace, ws_bytes, (hipStream_t)stream};
-    switch (L.kind) {
-        case Kind::WNA16: return hip_status(wna16_launch(a, L.a_bf16, L.zp), "hq_gemm(W4A16)");
-        case Kind::W4A8_MX: return hip_status(w4a8_launch(a), "hq_gemm(W4A8-MXFP4)");
-        case Kind::W8A8: return hip_status(w8a8_launch(a, L.out_i32), "hq_gemm(W8A8)");
-        default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind runs through hq_moe_gemm");
-    }
+    return dense_launch(L, a);
+}
+
+hq_status hq_gemm_plan(const hq_layer_desc* desc, int64_t M, char* buf, size_t len) {
+    LayerInfo L;
+    hq_status st = describe(desc, &L);
+    if (st != HQ_OK) return st;
+    if (desc->num_experts) return set_error(HQ_ERR_INVALID_ARG, "hq_gemm_plan takes a dense descriptor (num_experts == 0)");
+    if (M < 0 || M > (1LL << 30)) return set_error(HQ_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+    if (!buf || len < 2) return set_error(HQ_ERR_INVALID_ARG, "buf must hold at least 2 bytes");
+    buf[0] = 0;
+    if (M == 0) return ok();
+    PlanRecorder rec{buf, len, 0};
+    g_plan = &rec;
+    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+    st = dense_launch(L, a);
+    g_plan = nullptr;
+    buf[rec.used < len ? rec.used : len - 1] = 0;
+    return st;
 }
 
 hq_status hq_moe_gemm(const hq_layer_desc* desc, int32_t mode, int64_t T, int32_t top_k, const void* A,
@@ -312,6 +360,7 @@ hq_status hq_moe_align(int64_t T, int32_t top_k, int32_t num_experts, const int3
     if (num_experts < 1 || num_experts > 4096) return set_error(HQ_ERR_INVALID_ARG, "num_experts out of range");
     if (top_k < 1 || top_k > num_experts) return set_error(HQ_ERR_INVALID_ARG, "top_k out of range");
     if (T < 0 || T > (1LL << 24)) return set_error(HQ_ERR_INVALID_ARG, "T out of range");
+    if (T * top_k >= (1LL << 31)) return set_error(HQ_ERR_UNSUPPORTED, "T*top_k must stay below 2^31");
     if (T == 0) return ok();
     if (!topk_ids || !expert_offsets || !sorted_pairs) return set_error(HQ_ERR_INVALID_ARG, "pointers are required");
     if (!aligned16(topk_ids) || !aligned16(expert_offsets) || !aligned16(sorted_pairs))
@@ -335,7 +384,9 @@ hq_status hq_moe_gather(int32_t dtype, int64_t T, int32_t top_k, int64_t K, cons
         case HQ_DT_INT8: eb = 1; break;
         default: return set_error(HQ_ERR_UNSUPPORTED, "gather dtype must be BF16, FP16, FP8_E4M3 or INT8");
     }
-    if (T < 0 || top_k < 1 || K < 1 || T > (1LL << 24) || K > (1LL << 24)) return set_error(HQ_ERR_INVALID_ARG, "sizes out of range");
+    if (T < 0 || top_k < 1 || K < 1 || T > (1LL << 24) || K > (1LL << 24) || top_k > 4096)
+        return set_error(HQ_ERR_INVALID_ARG, "sizes out of range");
+    if (T * top_k >= (1LL << 31)) return set_error(HQ_ERR_UNSUPPORTED, "T*top_k must stay below 2^31");
     if (T == 0) return ok();
     if ((K * eb) % 16) return set_error(HQ_ERR_UNSUPPORTED, "row bytes must be a multiple of 16");
     if (!A || !sorted_pairs || !A_sorted) return set_error(HQ_ERR_INVALID_ARG, "pointers are required");

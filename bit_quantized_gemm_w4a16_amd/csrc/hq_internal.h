@@ -15,11 +15,16 @@ namespace hq {
 inline int64_t pad16(int64_t n) { return (n + 15) / 16 * 16; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Workspace carve-up shared by every dense split-K launch:
-//   [0, kCounterBytes)       uint32 arrival counters, one per output tile
-//   [kCounterBytes, ...)     fp32 / int32 partial tiles
-constexpr size_t kCounterBytes = 64 * 1024;
-constexpr int kMaxCounters = (int)(kCounterBytes / 4);
+// Launch planning without launching: while a PlanRecorder is active on the
+// calling thread, the dense launchers append the name, grid and split of each
+// kernel they would enqueue to it and return hipSuccess without any HIP call
+// (hq_gemm_plan).  The same code path chooses the kernels in both modes.
+struct PlanRecorder {
+    char* buf;
+    size_t len, used;
+};
+PlanRecorder* plan_recorder();                     // the active recorder of this thread, or null
+void plan_record(const char* fmt, ...);            // appends one launch (no-op without a recorder)
 
 struct DenseArgs {
     int64_t M, N, K, Np;

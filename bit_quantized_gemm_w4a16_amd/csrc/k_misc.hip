@@ -27,6 +27,14 @@ namespace hq {
 // an all-zero row), q = E4M3(x / s)
 // with round-to-nearest-even; |x / s| is clamped to 448 first, which equals
 // saturating rounding since every quotient lies within rounding of +-448.
+// Non-finite input: NaN elements take no part in the maximum (fmaxf returns
+// the other operand) and encode as 0x7F, the E4M3 NaN; an infinite element
+// makes s infinite, so finite elements of its row encode as +-0 and the
+// infinite ones (Inf / Inf) as NaN.
+__device__ __forceinline__ uint32_t e4m3_nan_fix(uint32_t codes, int byte, float v) {
+    return v != v ? (codes & ~(0xFFu << (8 * byte))) | (0x7Fu << (8 * byte)) : codes;
+}
+
 __global__ __launch_bounds__(256) void quant_e4m3_kernel(const float* __restrict__ x, int K,
                                                          uint8_t* __restrict__ q, float* __restrict__ s) {
     __shared__ float red[256];
@@ -45,9 +53,10 @@ __global__ __launch_bounds__(256) void quant_e4m3_kernel(const float* __restrict
     if (threadIdx.x == 0) s[row] = sc;
     uint8_t* qr = q + row * K;
     for (int k = 2 * threadIdx.x; k < K; k += 512) {
-        const float a = fminf(fmaxf(xr[k] / sc, -448.f), 448.f);
-        const float b = k + 1 < K ? fminf(fmaxf(xr[k + 1] / sc, -448.f), 448.f) : 0.f;
-        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        const float va = xr[k] / sc, vb = k + 1 < K ? xr[k + 1] / sc : 0.f;
+        const float a = fminf(fmaxf(va, -448.f), 448.f);
+        const float b = fminf(fmaxf(vb, -448.f), 448.f);
+        const uint32_t pk = e4m3_nan_fix(e4m3_nan_fix((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false), 0, va), 1, vb);
         qr[k] = (uint8_t)(pk & 0xFF);
         if (k + 1 < K) qr[k + 1] = (uint8_t)((pk >> 8) & 0xFF);
     }
@@ -85,13 +94,19 @@ __global__ __launch_bounds__(256) void quant_e4m3_rows_kernel(const float4* __re
     for (int j = 0; j < NV; ++j) {
         const int i = j * 256 + (int)threadIdx.x;
         if (i < K4) {
-            const float a = fminf(fmaxf(v[j].x / sc, -448.f), 448.f);
-            const float b = fminf(fmaxf(v[j].y / sc, -448.f), 448.f);
-            const float c = fminf(fmaxf(v[j].z / sc, -448.f), 448.f);
-            const float d = fminf(fmaxf(v[j].w / sc, -448.f), 448.f);
+            const float va = v[j].x / sc, vb = v[j].y / sc, vc = v[j].z / sc, vd = v[j].w / sc;
+            const float a = fminf(fmaxf(va, -448.f), 448.f);
+            const float b = fminf(fmaxf(vb, -448.f), 448.f);
+            const float c = fminf(fmaxf(vc, -448.f), 448.f);
+            const float d = fminf(fmaxf(vd, -448.f), 448.f);
             int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);  // bytes 0, 1
             pk = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, pk, true);      // bytes 2, 3
-            qr[i] = (uint32_t)pk;
+            uint32_t u = (uint32_t)pk;
+            u = e4m3_nan_fix(u, 0, va);
+            u = e4m3_nan_fix(u, 1, vb);
+            u = e4m3_nan_fix(u, 2, vc);
+            u = e4m3_nan_fix(u, 3, vd);
+            qr[i] = u;
         }
     }
 }

@@ -557,6 +557,10 @@ __global__ __launch_bounds__(256) void skinny_finalize_kernel(SkinnyArgs p) {
 
 template <Fmt F, int MT, int SPW, int CPW>
 hipError_t launch_skinny_k(dim3 grid, int lds_bytes, const SkinnyArgs& a, hipStream_t st) {
+    if (plan_recorder()) {
+        plan_record("skinny_kernel<%s,%d,%d,%d> grid=%ux%u splits=%d", fmt_name(F), MT, SPW, CPW, grid.x, grid.y, a.splits);
+        return hipSuccess;
+    }
     // allow dynamic LDS beyond the 64 KB default, once per instantiation
     static const hipError_t attr = hipFuncSetAttribute((const void*)skinny_kernel<F, MT, SPW, CPW>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLds);
@@ -581,7 +585,6 @@ hipError_t launch_skinny_cpw(int cpw, dim3 grid, int lds_bytes, const SkinnyArgs
     }
 }
 
-// Dense launch: skinny kernel, then the finalize pass when K is split.
 // Dense launch: the weight stream, then the finalize pass when K is split.
 template <Fmt F>
 hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t st) {
@@ -602,6 +605,10 @@ hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t s
     else e = launch_skinny_cpw<F, 4, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
     if (e != hipSuccess || pl.splits == 1) return e;
     const dim3 fgrid((unsigned)cdiv(cdiv(s.N, 2), 256), (unsigned)s.M);
+    if (plan_recorder()) {
+        plan_record("skinny_finalize_kernel<%s>", fmt_name(F));
+        return hipSuccess;
+    }
     hipLaunchKernelGGL((skinny_finalize_kernel<F>), fgrid, dim3(256), 0, st, s);
     return hipGetLastError();
 }

@@ -36,10 +36,16 @@
 #include <type_traits>
 
 #include "hq_device.hpp"
+#include "hq_internal.h"
 
 namespace hq {
 
 enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX };
+
+constexpr const char* fmt_name(Fmt F) {
+    return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
+         : F == Fmt::W8A8_I8 ? "W8A8_I8" : "MOE_MX";
+}
 
 template <Fmt F> struct FmtTraits;
 template <> struct FmtTraits<Fmt::WNA16_F16> { static constexpr int AB = 2, BSTRIP = 1024; using Acc = v4f; };
@@ -894,6 +900,12 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.Np + BN - 1) / BN);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.splits;
+    if (plan_recorder()) {
+        plan_record("tile_gemm_kernel<%s,%d,%d,%d,%d,%d> grid=%lld splits=%d", fmt_name(F), BM, BN, WM, WN, PD,
+                    (long long)grid, p.splits);
+        if (p.splits > 1) plan_record("tile_finalize_kernel<%s>", fmt_name(F));
+        return hipSuccess;
+    }
     hipLaunchKernelGGL((tile_gemm_kernel<F, BM, BN, WM, WN, PD>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;

@@ -59,6 +59,7 @@ _SIGS = {
     "hq_workspace_bytes": (C.c_int, [_P, C.c_int64, C.c_int32, _P]),
     "hq_workspace_init": (C.c_int, [_P, C.c_size_t, _P]),
     "hq_gemm": (C.c_int, [_P, C.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "hq_gemm_plan": (C.c_int, [_P, C.c_int64, C.c_char_p, C.c_size_t]),
     "hq_moe_gemm": (C.c_int, [_P, C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               C.c_size_t, _P]),
     "hq_quantize_act": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, _P, _P, _P, _P]),
@@ -188,6 +189,14 @@ def hq_workspace_init(workspace, nbytes: int, stream=None) -> None:
 def hq_gemm(desc, M, A, a_scale, w, s, z, D, workspace=None, ws_bytes=0, stream=None) -> None:
     _check(lib().hq_gemm(C.byref(desc), M, _dp(A), _dp(a_scale), _dp(w), _dp(s), _dp(z), None, _dp(D),
                          _dp(workspace), ws_bytes, _stream(stream)), "hq_gemm")
+
+
+def hq_gemm_plan(desc, M) -> list:
+    """The kernel launches hq_gemm would enqueue for (desc, M), one string each (host only)."""
+    buf = C.create_string_buffer(4096)
+    _check(lib().hq_gemm_plan(C.byref(desc), M, buf, len(buf)), "hq_gemm_plan")
+    txt = buf.value.decode()
+    return txt.split(";") if txt else []
 
 
 def hq_moe_gemm(desc, mode, T, top_k, A, a_scale, topk_ids, expert_offsets, w, s, z, D, workspace=None,

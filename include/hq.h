@@ -36,9 +36,10 @@
  *    hipStream_t passed as void*; NULL is the default stream).  Device-side
  *    faults surface at the caller's next synchronisation.
  *  - Device pointers must be 16-byte aligned (HQ_ERR_ALIGNMENT otherwise).
- *  - A workspace is needed only where hq_workspace_bytes() says so; it must
- *    be zero-filled once before its first use (hq_workspace_init) and is left
- *    ready for reuse by every call.  Two calls that share a workspace must not
+ *  - A workspace is needed only where hq_workspace_bytes() says so (split-K
+ *    partial tiles, MoE routing metadata).  Every kernel writes what it later
+ *    reads within the same call, so its contents need no initialisation and
+ *    are meaningless between calls.  Two calls that share a workspace must not
  *    run concurrently.
  *  - Thread safety: the library holds no mutable global state besides a
  *    per-device property cache filled once.
@@ -202,7 +203,9 @@ hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale,
  */
 hq_status hq_workspace_bytes(const hq_layer_desc* desc, int64_t M_or_T, int32_t top_k, size_t* bytes);
 
-/* Zero-fills a workspace on `stream` with a fill kernel (graph-capturable). */
+/* Zero-fills a workspace on `stream` with a fill kernel (graph-capturable).
+ * Never required by the GEMMs (they initialise what they read); kept for
+ * callers that want deterministic workspace contents. */
 hq_status hq_workspace_init(void* workspace, size_t bytes, hq_stream_t stream);
 
 /* ---------------------------------------------------------------------- */
@@ -221,6 +224,17 @@ hq_status hq_workspace_init(void* workspace, size_t bytes, hq_stream_t stream);
 hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const float* a_scale,
                   const void* w, const void* s, const void* z, const void* s2, void* D,
                   void* workspace, size_t ws_bytes, hq_stream_t stream);
+
+/*
+ * Host only, no HIP call: the kernel launches hq_gemm would enqueue for this
+ * dense descriptor and M, written to buf (NUL-terminated, truncated to len)
+ * as ';'-separated "kernel<template arguments> grid=... splits=..." items.
+ * The same code path picks the kernels in hq_gemm ("Humming wird
+ * angekuendigt", section "Tuning und JIT-Kompilierung fuer jeden Workload":
+ * one prepared configuration per range of input sizes, chosen at run time).
+ * M == 0 writes "" (no launch).
+ */
+hq_status hq_gemm_plan(const hq_layer_desc* desc, int64_t M, char* buf, size_t len);
 
 /*
  * MoE GEMM over top_k experts per token (expert-stacked packed weights).

@@ -1,0 +1,67 @@
+"""Dense GEMM shapes of the GPU parity suite, in one place.
+
+The GPU tests parametrize over these lists, and the host-only coverage test
+(tests/test_plan_coverage.py) asks the library's planner (hq_gemm_plan) which
+kernels each of them launches, to check that every kernel configuration the
+benchmark sweeps time is reached by at least one parity case.  No torch here.
+"""
+from __future__ import annotations
+
+# the benchmark's M sweep: 1, 2, 4, ..., 8192
+SWEEP = [1 << i for i in range(14)]
+
+# the dense workloads at their real shapes
+C2 = dict(N=4096, K=7168, G=128)          # W4A16 UINT4 + zero-points, fp16
+C3 = dict(N=7168, K=4096)                 # W4A8-MXFP4
+C4 = dict(N=18432, K=7168)                # W8A8 INT8
+
+# ---- W4A16: (M, N, K, G, bf16, zp) ----
+WNA16_SMALL_M = [1, 2, 3, 5, 8, 15, 16, 17, 24, 31, 33, 48, 63, 64]
+WNA16_SMALL = [(M, 272, 1024, 128, bf, zp) for M in WNA16_SMALL_M
+               for bf, zp in ((True, False), (False, True), (True, True), (False, False))]
+WNA16_LARGER = [(M, 384, 768, 128, False, True) for M in (65, 100, 128, 200, 300)]
+WNA16_SHAPES = [(M, N, K, G, False, True) for N, K, G in ((1000, 512, 128), (24, 128, 128), (512, 2048, 256),
+                                                          (1024, 7168, 128), (48, 1024, 1024))
+                for M in (1, 9, 40)]
+# skinny two-m-tile batches (17..32 rows) at a K whose quarter is 14 chunks
+WNA16_SKINNY_K7168 = [(24, 304, 7168, 128, bf, True) for bf in (False, True)]
+WNA16_WIDE = [(4000, 4100, 512, 128, False, True), (4096, 4096, 1024, 128, False, False),
+              (1100, 16000, 256, 128, False, True), (8192, 2056, 384, 128, False, True),
+              (2000, 4100, 384, 128, False, True), (2048, 4096, 512, 128, False, False)]
+# bf16 activations above the small-M schedule (the 128 x 128 tile with the row-sum MFMA)
+WNA16_BF16_LARGE = [(M, N, 7168, 128, True, zp) for M, N in ((65, 4096), (300, 4100), (2048, 4096))
+                    for zp in (False, True)]
+WNA16_C2_SWEEP = [(M, C2["N"], C2["K"], C2["G"], False, True) for M in SWEEP]
+
+# ---- W4A8-MXFP4: (M, N, K) ----
+W4A8_SMALL = [(M, 272, 512) for M in (1, 3, 16, 24, 32, 64, 100, 257)]
+W4A8_BIG = [(1100, 7200, 128), (1100, 7168, 640)]
+# the two-stage 128 x 128 tile (grids of more than 256 such tiles below the 256 x 256 threshold)
+W4A8_MID = [(1024, 7168, 256), (1000, 7000, 384)]
+W4A8_C3_SWEEP = [(M, C3["N"], C3["K"]) for M in SWEEP]
+
+# ---- W8A8-INT8: (M, N, K) ----
+W8A8_SMALL_RAW = [(M, 304, 640) for M in (1, 7, 24, 64, 130)]
+W8A8_SMALL_BF16 = [(M, 304, 640) for M in (1, 33, 200)]
+# skinny two-m-tile batches at K = 7168 (14-chunk register batches)
+W8A8_SKINNY_K7168 = [(M, 304, 7168) for M in (20, 32)]
+W8A8_BIG_RAW = [(2100, 16400, 256), (600, 11000, 384), (600, 11000, 128)]
+# the 256 x 128 stage ring: from the 128-row branch (M <= 1024, > 256 tiles of 128 x 128)
+# and from the 256-row branch (>= 256 tiles of 256 x 128 that 256 x 256 would not halve into one round)
+W8A8_RING = [(200, 20000, 384), (1024, 18432, 256), (256, 18432, 640)]
+W8A8_C4_SWEEP = [(M, C4["N"], C4["K"]) for M in SWEEP]
+
+
+def all_dense_cases():
+    """(format, M, N, K, G, flags) for every dense GPU case, flags a dict."""
+    out = []
+    for M, N, K, G, bf, zp in (WNA16_SMALL + WNA16_LARGER + WNA16_SHAPES + WNA16_SKINNY_K7168 + WNA16_WIDE
+                               + WNA16_BF16_LARGE + WNA16_C2_SWEEP + [(16, 1024, 1024, 128, True, False)]):
+        out.append(("wna16", M, N, K, G, dict(bf16=bf, zp=zp)))
+    for M, N, K in W4A8_SMALL + W4A8_BIG + W4A8_MID + W4A8_C3_SWEEP + [(20, 1000, 1024)]:
+        out.append(("w4a8", M, N, K, 32, {}))
+    for M, N, K in W8A8_SMALL_RAW + W8A8_SKINNY_K7168 + W8A8_BIG_RAW + W8A8_RING + W8A8_C4_SWEEP + [(8, 64, 7168)]:
+        out.append(("w8a8", M, N, K, K, dict(raw=True)))
+    for M, N, K in W8A8_SMALL_BF16 + W8A8_C4_SWEEP:
+        out.append(("w8a8", M, N, K, K, dict(raw=False)))
+    return out

@@ -63,3 +63,13 @@ def sample_rows(M: int, seed: int = 0, tile: int = 128, extra: int = 64) -> np.n
         rows.add(min(M, t0 + tile) - 1)
     rows.update(np.random.default_rng([seed, M]).choice(M, size=min(extra, M), replace=False).tolist())
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def sweep_rows(M: int, seed: int = 1, extra: int = 12) -> np.ndarray:
+    """Rows to compare at full-size sweep points: every row up to M = 8, else the
+    first two, the last two and `extra` seeded random rows."""
+    if M <= 8:
+        return np.arange(M)
+    rows = {0, 1, M - 2, M - 1}
+    rows.update(np.random.default_rng([seed, M]).choice(M, size=min(extra, M), replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)

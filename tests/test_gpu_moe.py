@@ -133,18 +133,32 @@ def test_moe_single_expert_top1_equals_dense():
     check(run_moe(T, E, 1, N, K, seed=9))
 
 
-@pytest.mark.parametrize("T", [1, 8, 64, 8192])
+def moe_sample_pairs(ids, E, tile_rows=256, extra=24, seed=1):
+    """Pairs to compare at full size: every active expert's first and last pair,
+    the first and last row of every m-tile of the busiest expert (in the sorted
+    order the kernels tile), and `extra` seeded random pairs."""
+    T, top_k = ids.shape
+    P = T * top_k
+    counts, offsets, perm = oracle.moe_route(ids, E)
+    pick = set(np.random.default_rng([T, seed]).choice(P, size=min(P, extra), replace=False).tolist())
+    for e in np.flatnonzero(counts):
+        pick.add(int(perm[offsets[e]]))
+        pick.add(int(perm[offsets[e + 1] - 1]))
+    top = int(counts.argmax())
+    for r0 in range(0, int(counts[top]), tile_rows):
+        pick.add(int(perm[offsets[top] + r0]))
+        pick.add(int(perm[offsets[top] + min(r0 + tile_rows, int(counts[top])) - 1]))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 2048, 8192])
 def test_moe_full_size_sampled(T):
-    """The MoE workload: E=256, top-8, N=4096, K=7168, Zipf(1.1) routing; sampled pairs."""
+    """The MoE workload: E=256, top-8, N=4096, K=7168, Zipf(1.1) routing; sampled
+    pairs covering every active expert and every tile of the busiest one."""
     E, top_k, N, K = 256, 8, 4096, 7168
     ids = syn.zipf_topk(0, syn.C5, T, E, top_k)
-    P = T * top_k
-    rng = np.random.default_rng([T, 1])
     flat = ids.reshape(-1)
-    top = np.bincount(flat, minlength=E).argmax()
-    pick = list(rng.choice(P, size=min(P, 24), replace=False))
-    pick += list(np.flatnonzero(flat == top)[[0, -1]])     # first and last row of the busiest expert
-    pairs = np.array(sorted(set(int(p) for p in pick)))
+    pairs = moe_sample_pairs(ids, E)
     needed = sorted(set(int(e) for e in flat))             # experts any token uses (the kernel reads these)
     note(f"moe full T={T}: generating {len(needed)} experts")
     d = syn.moe_mxfp4(0, T, E, top_k, N, K, experts=needed)

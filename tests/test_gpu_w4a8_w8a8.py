@@ -7,7 +7,8 @@ import torch
 import oracle
 import synthetic as syn
 from bit_quantized_gemm_w4a16_amd import hq
-from gpu_util import GATE, dev, empty, gate_error, note, sample_rows, to_f64, workspace
+import cases
+from gpu_util import GATE, dev, empty, gate_error, note, sample_rows, sweep_rows, to_f64, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -20,6 +21,26 @@ def gpu_quant(A0):
     hq.hq_quantize_act(hq.HQ_DT_FP8_E4M3, M, K, x, q, s)
     torch.cuda.synchronize()
     return q[: M * K].cpu().numpy().reshape(M, K), s[:M].cpu().numpy()
+
+
+@pytest.mark.parametrize("K", [4096, 1001])
+def test_quantize_act_non_finite_rows(K):
+    """NaN elements are left out of the row maximum and encode as 0x7F (the E4M3
+    NaN); a row holding an infinity gets an infinite scale, its finite elements
+    encode as +-0 and its infinities (Inf / Inf) as NaN -- bit for bit as the oracle."""
+    note(f"quant_e4m3 non-finite K={K}")
+    A0 = syn.normal_rows(4, 3, syn.T_A, 6, K)
+    A0[0, 5] = np.nan
+    A0[1, :3] = [np.nan, -np.nan, 7.0]
+    A0[2, 17] = np.inf
+    A0[3, 0] = -np.inf
+    A0[3, 9] = np.nan
+    A0[4, :] = np.nan
+    q_o, s_o = oracle.quant_act_e4m3(A0)
+    assert q_o[0, 5] == 0x7F and q_o[2, 17] == 0x7F and np.isinf(s_o[2]) and s_o[4] == 1.0
+    q_g, s_g = gpu_quant(A0)
+    np.testing.assert_array_equal(s_g.view(np.uint32), s_o.view(np.uint32))
+    np.testing.assert_array_equal(q_g, q_o)
 
 
 # K a multiple of 4 up to 8192: the register-held row kernel (1, 2, 4 and 8
@@ -54,9 +75,9 @@ def run_w4a8(M, N, K, seed=0, data=None, rows=None):
     return Dh[r], O
 
 
-@pytest.mark.parametrize("M", [1, 3, 16, 24, 32, 64, 100, 257])
-def test_w4a8_small_shapes(M):
-    Dr, O = run_w4a8(M, 272, 512, seed=M)
+@pytest.mark.parametrize("M,N,K", cases.W4A8_SMALL)
+def test_w4a8_small_shapes(M, N, K):
+    Dr, O = run_w4a8(M, N, K, seed=M)
     err = gate_error(Dr, O)
     assert err <= min(GATE, 8e-3), err
 
@@ -74,7 +95,16 @@ def test_w4a8_ragged_n_and_extremes():
     assert gate_error(Dr, O) <= 8e-3
 
 
-@pytest.mark.parametrize("M,N,K", [(1100, 7200, 128), (1100, 7168, 640)])
+@pytest.mark.parametrize("M,N,K", cases.W4A8_MID)
+def test_w4a8_two_stage_128_tiles(M, N, K):
+    """The two-stage 128 x 128 W4A8 tile (more than one round of 128 x 128 tiles,
+    too few for 256 x 256), with a ragged last column tile in the second shape."""
+    Dr, O = run_w4a8(M, N, K, seed=M + K, rows=sweep_rows(M))
+    err = gate_error(Dr, O)
+    assert err <= min(GATE, 8e-3), err
+
+
+@pytest.mark.parametrize("M,N,K", cases.W4A8_BIG)
 def test_w4a8_big_tiles_ragged(M, N, K):
     """256 x 256 W4A8 tiles on the three-stage ring with ragged last row and
     column tiles: one K step (the ring's prologue fetches steps past the slice,
@@ -84,10 +114,11 @@ def test_w4a8_big_tiles_ragged(M, N, K):
     assert err <= min(GATE, 8e-3), err
 
 
-@pytest.mark.parametrize("M", [1, 16, 32, 256, 2048, 8192])
-def test_w4a8_full_size(M):
-    """The dense W4A8-MXFP4 workload: N=7168, K=4096 (sampled rows at large M)."""
-    Dr, O = run_w4a8(M, 7168, 4096, seed=0)
+@pytest.mark.parametrize("M,N,K", cases.W4A8_C3_SWEEP)
+def test_w4a8_full_size(M, N, K):
+    """The dense W4A8-MXFP4 workload (N=7168, K=4096) at every M of the benchmark
+    sweep, in the launch configuration the benchmark times; sampled rows from M = 16 on."""
+    Dr, O = run_w4a8(M, N, K, seed=0, rows=sweep_rows(M))
     err = gate_error(Dr, O)
     assert err <= min(GATE, 8e-3), err
 
@@ -110,9 +141,9 @@ def run_w8a8(M, N, K, seed=0, raw=False, rows=None, data=None):
     return got, O
 
 
-@pytest.mark.parametrize("M", [1, 7, 64, 130])
-def test_w8a8_raw_int32_bit_exact_small(M):
-    got, acc = run_w8a8(M, 304, 640, seed=M, raw=True)
+@pytest.mark.parametrize("M,N,K", cases.W8A8_SMALL_RAW + cases.W8A8_SKINNY_K7168)
+def test_w8a8_raw_int32_bit_exact_small(M, N, K):
+    got, acc = run_w8a8(M, N, K, seed=M, raw=True)
     np.testing.assert_array_equal(got.astype(np.int64), acc)
 
 
@@ -127,9 +158,9 @@ def test_w8a8_split_k_needs_workspace():
         hq.hq_gemm(desc, 130, a, sa, w, s, None, D)
 
 
-@pytest.mark.parametrize("M", [1, 33, 200])
-def test_w8a8_bf16_small(M):
-    got, O = run_w8a8(M, 304, 640, seed=M)
+@pytest.mark.parametrize("M,N,K", cases.W8A8_SMALL_BF16)
+def test_w8a8_bf16_small(M, N, K):
+    got, O = run_w8a8(M, N, K, seed=M)
     assert gate_error(got, O) <= 8e-3
 
 
@@ -145,19 +176,30 @@ def test_w8a8_extreme_accumulators_exact():
     assert abs(int(acc[0, 0])) == 127 * 127 * K
 
 
-@pytest.mark.parametrize("M", [1, 64, 512, 8192])
-def test_w8a8_full_size(M):
-    """The dense W8A8 workload: N=18432, K=7168; raw int32 bit-exact and bf16 epilogue."""
-    got, acc = run_w8a8(M, 18432, 7168, seed=0, raw=True)
+@pytest.mark.parametrize("M,N,K", cases.W8A8_C4_SWEEP)
+def test_w8a8_full_size(M, N, K):
+    """The dense W8A8 workload (N=18432, K=7168) at every M of the benchmark sweep:
+    raw int32 bit-exact and the bf16 epilogue, sampled rows from M = 16 on."""
+    d = syn.w8a8_int8(0, M, N, K)
+    r = sweep_rows(M)
+    got, acc = run_w8a8(M, N, K, raw=True, rows=r, data=d)
     np.testing.assert_array_equal(got.astype(np.int64), acc)
-    got, O = run_w8a8(M, 18432, 7168, seed=0)
+    got, O = run_w8a8(M, N, K, rows=r, data=d)
     assert gate_error(got, O) <= 8e-3
 
 
-@pytest.mark.parametrize("M,N,K", [(2100, 16400, 256), (600, 11000, 384), (600, 11000, 128)])
+@pytest.mark.parametrize("M,N,K", cases.W8A8_BIG_RAW)
 def test_w8a8_raw_int32_big_tiles_ragged(M, N, K):
-    """Grids of 256 x 256 (first shape) and 256 x 128 (the others, a three-stage
-    ring: three steps, and one step whose ring fetches run past the slice) INT8
-    tiles with ragged last row and column tiles: raw int32 accumulators bit-exact."""
+    """Grids of 256 x 256 INT8 tiles (two stages) with ragged last row and column
+    tiles, at one, two and three K steps: raw int32 accumulators bit-exact."""
     got, acc = run_w8a8(M, N, K, seed=M, raw=True)
+    np.testing.assert_array_equal(got.astype(np.int64), acc)
+
+
+@pytest.mark.parametrize("M,N,K", cases.W8A8_RING)
+def test_w8a8_raw_int32_ring_tiles(M, N, K):
+    """The 256 x 128 INT8 tile on its three-stage ring, reached from the 128-row
+    branch (M = 200) and the 256-row branch (M = 1024, 256), with three, two and
+    five K steps and ragged last tiles: raw int32 accumulators bit-exact."""
+    got, acc = run_w8a8(M, N, K, seed=M, raw=True, rows=sweep_rows(M))
     np.testing.assert_array_equal(got.astype(np.int64), acc)

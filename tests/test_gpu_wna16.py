@@ -7,7 +7,8 @@ import torch
 import oracle
 import synthetic as syn
 from bit_quantized_gemm_w4a16_amd import hq
-from gpu_util import GATE, dev, empty, gate_error, note, sample_rows, to_f64, workspace
+import cases
+from gpu_util import GATE, dev, empty, gate_error, note, sample_rows, sweep_rows, to_f64, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -48,24 +49,31 @@ def test_c1_dense_w4a16_sym_bf16_m16():
     check(Dr, O, True)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 15, 16, 17, 31, 33, 48, 63, 64])
-@pytest.mark.parametrize("bf16,zp", [(True, False), (False, True), (True, True), (False, False)])
-def test_small_m_tiles_and_ragged_tail(M, bf16, zp):
-    Dr, O = run_wna16(M, 272, 1024, 128, bf16=bf16, zp=zp, seed=M)
+@pytest.mark.parametrize("M,N,K,G,bf16,zp", cases.WNA16_SMALL + cases.WNA16_SKINNY_K7168)
+def test_small_m_tiles_and_ragged_tail(M, N, K, G, bf16, zp):
+    Dr, O = run_wna16(M, N, K, G, bf16=bf16, zp=zp, seed=M)
     check(Dr, O, bf16)
 
 
-@pytest.mark.parametrize("M", [65, 100, 128, 200, 300])
-def test_larger_m(M):
-    Dr, O = run_wna16(M, 384, 768, 128, bf16=False, zp=True, seed=M)
-    check(Dr, O, False)
+@pytest.mark.parametrize("M,N,K,G,bf16,zp", cases.WNA16_LARGER)
+def test_larger_m(M, N, K, G, bf16, zp):
+    Dr, O = run_wna16(M, N, K, G, bf16=bf16, zp=zp, seed=M)
+    check(Dr, O, bf16)
 
 
-@pytest.mark.parametrize("N,K,G", [(1000, 512, 128), (24, 128, 128), (512, 2048, 256), (1024, 7168, 128), (48, 1024, 1024)])
-def test_shapes_groups_and_split_k(N, K, G):
-    for M in (1, 9, 40):
-        Dr, O = run_wna16(M, N, K, G, bf16=False, zp=True, seed=N + M)
-        check(Dr, O, False)
+@pytest.mark.parametrize("M,N,K,G,bf16,zp", cases.WNA16_SHAPES)
+def test_shapes_groups_and_split_k(M, N, K, G, bf16, zp):
+    Dr, O = run_wna16(M, N, K, G, bf16=bf16, zp=zp, seed=N + M)
+    check(Dr, O, bf16)
+
+
+@pytest.mark.parametrize("M,N,K,G,bf16,zp", cases.WNA16_BF16_LARGE)
+def test_bf16_above_small_m(M, N, K, G, bf16, zp):
+    """bf16 activations on the tiled path (operand 128 + u, the -(128 + z) offset
+    from a row-sum MFMA, the group scale on the fp32 partial), split and unsplit,
+    symmetric and zero-point, ragged N."""
+    Dr, O = run_wna16(M, N, K, G, bf16=bf16, zp=zp, seed=M + N, rows=sweep_rows(M))
+    check(Dr, O, bf16)
 
 
 def test_zero_point_equals_code_gives_exact_zero():
@@ -90,7 +98,8 @@ def test_extreme_codes():
 
 
 def test_workspace_reused_across_calls_and_sizes():
-    """Split-K counters are left at zero: back-to-back calls with one workspace agree with the oracle."""
+    """One workspace serves back-to-back calls of different M (split and unsplit):
+    each call writes the partial tiles it reads, so leftovers never leak in."""
     N, K, G = 1024, 7168, 128
     desc = hq.desc_w4a16(N, K, G, bf16=False, zp=True)
     nb = max(hq.hq_workspace_bytes(desc, m) for m in (1, 64))
@@ -107,18 +116,18 @@ def test_workspace_reused_across_calls_and_sizes():
         check(Dh, O, False)
 
 
-@pytest.mark.parametrize("M", [1, 64, 1024, 4096, 8192])
-def test_dense_w4a16_zp_full_size(M):
+@pytest.mark.parametrize("M,N,K,G,bf16,zp", cases.WNA16_C2_SWEEP)
+def test_dense_w4a16_zp_full_size(M, N, K, G, bf16, zp):
     """The dense W4A16 workload (UINT4 + zero-points, fp16, N=4096, K=7168, G=128)
-    in the launch configuration the benchmark times; sampled rows at large M."""
-    Dr, O = run_wna16(M, 4096, 7168, 128, bf16=False, zp=True, seed=0)
-    check(Dr, O, False)
+    at every M of the benchmark sweep, in the launch configuration the benchmark
+    times; sampled rows from M = 16 on."""
+    Dr, O = run_wna16(M, N, K, G, bf16=bf16, zp=zp, seed=0, rows=sweep_rows(M))
+    check(Dr, O, bf16)
 
 
-@pytest.mark.parametrize("M,N,K,zp", [(4000, 4100, 512, True), (4096, 4096, 1024, False), (1100, 16000, 256, True),
-                                      (8192, 2056, 384, True), (2000, 4100, 384, True), (2048, 4096, 512, False)])
-def test_wide_tiles_ragged(M, N, K, zp):
+@pytest.mark.parametrize("M,N,K,G,bf16,zp", cases.WNA16_WIDE)
+def test_wide_tiles_ragged(M, N, K, G, bf16, zp):
     """Grids large enough for 256-column tiles (256 x 256 from about 256 tiles of
     that size, else 128 x 256), with ragged last row and column tiles."""
-    Dr, O = run_wna16(M, N, K, 128, bf16=False, zp=zp, seed=M + N)
-    check(Dr, O, False)
+    Dr, O = run_wna16(M, N, K, G, bf16=bf16, zp=zp, seed=M + N)
+    check(Dr, O, bf16)

@@ -1,0 +1,72 @@
+"""Host-only check (no GPU) that the GPU parity suite reaches every kernel
+configuration the benchmark times.
+
+hq_gemm_plan runs the library's own dispatch without launching and names the
+kernels a call would enqueue.  For each dense workload of the benchmark and
+each M of its sweep, every launched kernel -- template arguments plus whether
+its K is split (partial tiles and a finalize pass) or not (direct epilogue) --
+must also be launched by at least one case of the GPU suite (tests/cases.py).
+"""
+import re
+
+import pytest
+
+import cases
+from bit_quantized_gemm_w4a16_amd import hq
+
+
+def desc_of(fmt, N, K, G, flags):
+    if fmt == "wna16":
+        return hq.desc_w4a16(N, K, G, bf16=flags["bf16"], zp=flags["zp"])
+    if fmt == "w4a8":
+        return hq.desc_w4a8_mxfp4(N, K)
+    return hq.desc_w8a8(N, K, raw_int32=flags["raw"])
+
+
+def keys(desc, M):
+    out = set()
+    for item in hq.hq_gemm_plan(desc, M):
+        name = item.split(" ")[0]
+        m = re.search(r"splits=(\d+)", item)
+        if m:
+            name += " split" if int(m.group(1)) > 1 else " direct"
+        out.add(name)
+    return out
+
+
+def covered():
+    cov = set()
+    for fmt, M, N, K, G, flags in cases.all_dense_cases():
+        cov |= keys(desc_of(fmt, N, K, G, flags), M)
+    return cov
+
+
+BENCH = {
+    "c2": ("wna16", cases.C2["N"], cases.C2["K"], cases.C2["G"], dict(bf16=False, zp=True)),
+    "c3": ("w4a8", cases.C3["N"], cases.C3["K"], 32, {}),
+    "c4": ("w8a8", cases.C4["N"], cases.C4["K"], cases.C4["K"], dict(raw=False)),
+    "c4raw": ("w8a8", cases.C4["N"], cases.C4["K"], cases.C4["K"], dict(raw=True)),
+}
+
+
+def test_plan_names_kernels_without_launching():
+    d = hq.desc_w4a16(4096, 7168, 128, bf16=False, zp=True)
+    assert hq.hq_gemm_plan(d, 0) == []
+    p1 = hq.hq_gemm_plan(d, 1)
+    assert len(p1) == 1 and p1[0].startswith("skinny_kernel<WNA16_F16,") and "splits=1" in p1[0]
+    p8k = hq.hq_gemm_plan(d, 8192)
+    assert len(p8k) == 1 and p8k[0].startswith("tile_gemm_kernel<WNA16_F16,")
+    with pytest.raises(hq.HQError):
+        hq.hq_gemm_plan(hq.desc_moe_mxfp4(8, 128, 128), 4)
+
+
+@pytest.mark.parametrize("cfg", sorted(BENCH))
+def test_every_bench_sweep_kernel_has_a_gpu_parity_case(cfg):
+    fmt, N, K, G, flags = BENCH[cfg]
+    d = desc_of(fmt, N, K, G, flags)
+    cov = covered()
+    missing = {}
+    for M in cases.SWEEP:
+        for k in keys(d, M) - cov:
+            missing.setdefault(k, []).append(M)
+    assert not missing, missing
