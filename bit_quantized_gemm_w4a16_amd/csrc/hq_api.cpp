@@ -37,9 +37,13 @@ thread_local PlanRecorder* g_plan = nullptr;
 
 PlanRecorder* plan_recorder() { return g_plan; }
 
+void plan_workspace(size_t bytes) {
+    if (g_plan && bytes > g_plan->ws) g_plan->ws = bytes;
+}
+
 void plan_record(const char* fmt, ...) {
     PlanRecorder* r = g_plan;
-    if (!r || r->used + 1 >= r->len) return;
+    if (!r || !r->buf || r->used + 1 >= r->len) return;
     if (r->used) r->buf[r->used++] = ';';
     va_list ap;
     va_start(ap, fmt);
@@ -131,15 +135,6 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
     return HQ_OK;
 }
 
-static size_t dense_workspace(const LayerInfo& L, int64_t M) {
-    switch (L.kind) {
-        case Kind::WNA16: return wna16_workspace(M, L.N, L.K, (int)L.G, L.a_bf16);
-        case Kind::W4A8_MX:
-        case Kind::W8A8: return w8bit_workspace(M, L.N, L.K);
-        default: return 0;
-    }
-}
-
 static hq_status hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();
     return set_error(HQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -152,6 +147,29 @@ static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
         case Kind::W8A8: return hip_status(w8a8_launch(a, L.out_i32), "hq_gemm(W8A8)");
         default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind runs through hq_moe_gemm");
     }
+}
+
+// Runs the dense dispatch in planning mode (no HIP call): fills buf (if any)
+// with the launches and returns the workspace they need in *ws.
+static hq_status dense_plan(const LayerInfo& L, int64_t M, char* buf, size_t len, size_t* ws) {
+    PlanRecorder rec{buf, len, 0, 0};
+    if (buf) buf[0] = 0;
+    if (M == 0) {
+        *ws = 0;
+        return HQ_OK;
+    }
+    g_plan = &rec;
+    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+    const hq_status st = dense_launch(L, a);
+    g_plan = nullptr;
+    if (buf) buf[rec.used < len ? rec.used : len - 1] = 0;
+    *ws = rec.ws;
+    return st;
+}
+
+static size_t dense_workspace(const LayerInfo& L, int64_t M) {
+    size_t ws = 0;
+    return dense_plan(L, M, nullptr, 0, &ws) == HQ_OK ? ws : 0;
 }
 
 }  // namespace hq
@@ -266,15 +284,9 @@ hq_status hq_gemm_plan(const hq_layer_desc* desc, int64_t M, char* buf, size_t l
     if (desc->num_experts) return set_error(HQ_ERR_INVALID_ARG, "hq_gemm_plan takes a dense descriptor (num_experts == 0)");
     if (M < 0 || M > (1LL << 30)) return set_error(HQ_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
     if (!buf || len < 2) return set_error(HQ_ERR_INVALID_ARG, "buf must hold at least 2 bytes");
-    buf[0] = 0;
-    if (M == 0) return ok();
-    PlanRecorder rec{buf, len, 0};
-    g_plan = &rec;
-    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
-    st = dense_launch(L, a);
-    g_plan = nullptr;
-    buf[rec.used < len ? rec.used : len - 1] = 0;
-    return st;
+    size_t ws = 0;
+    st = dense_plan(L, M, buf, len, &ws);
+    return st == HQ_OK ? ok() : st;
 }
 
 hq_status hq_moe_gemm(const hq_layer_desc* desc, int32_t mode, int64_t T, int32_t top_k, const void* A,

@@ -19,12 +19,17 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // calling thread, the dense launchers append the name, grid and split of each
 // kernel they would enqueue to it and return hipSuccess without any HIP call
 // (hq_gemm_plan).  The same code path chooses the kernels in both modes.
+// The launchers also report the workspace bytes their launches read and write,
+// so hq_workspace_bytes and the workspace check of hq_gemm follow the exact
+// plan the call will run.
 struct PlanRecorder {
-    char* buf;
+    char* buf;     // launch names (may be null: only the workspace is wanted)
     size_t len, used;
+    size_t ws;     // workspace bytes the planned launches need
 };
 PlanRecorder* plan_recorder();                     // the active recorder of this thread, or null
 void plan_record(const char* fmt, ...);            // appends one launch (no-op without a recorder)
+void plan_workspace(size_t bytes);                 // notes a workspace need (no-op without a recorder)
 
 struct DenseArgs {
     int64_t M, N, K, Np;
@@ -41,11 +46,9 @@ struct DenseArgs {
 };
 
 // W4A16 (INT4 / UINT4+zp; bf16 / fp16 activations)
-size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size, bool bf16);
 hipError_t wna16_launch(const DenseArgs& a, bool bf16, bool zp);
 
 // W4A8-MXFP4 and W8A8-INT8 (split-K workspace for mid M)
-size_t w8bit_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t w4a8_launch(const DenseArgs& a);
 hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32);
 

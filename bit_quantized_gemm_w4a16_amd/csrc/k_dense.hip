@@ -59,16 +59,6 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
 
 }  // namespace
 
-size_t w8bit_workspace(int64_t M, int64_t N, int64_t K) {
-    const int64_t Np = pad16(N);
-    if (M <= kSkinnyMaxM) {  // the larger of the two formats' split plans
-        const size_t a = skinny_workspace(plan_skinny(Fmt::W4A8_MX, M, Np, K, 128), M, Np);
-        const size_t b = skinny_workspace(plan_skinny(Fmt::W8A8_I8, M, Np, K, 128), M, Np);
-        return a > b ? a : b;
-    }
-    return tile_workspace(plan_tile(M, Np, K, true), M, Np);  // both 8-bit-A formats have the 256-row tile
-}
-
 hipError_t w4a8_launch(const DenseArgs& a) { return launch<Fmt::W4A8_MX>(a, 0); }
 
 hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32) { return launch<Fmt::W8A8_I8>(a, raw_i32 ? 1 : 0); }

@@ -72,14 +72,6 @@ hipError_t launch_all(const DenseArgs& a) {
 
 }  // namespace
 
-size_t wna16_workspace(int64_t M, int64_t N, int64_t K, int group_size, bool bf16) {
-    const int64_t Np = pad16(N);
-    const Fmt F = bf16 ? Fmt::WNA16_BF16 : Fmt::WNA16_F16;
-    if (M > kSkinnyMaxM)
-        return tile_workspace(plan_tile(M, Np, K, has_big_tile(F), has_wide256_tile(F), has_wide_tile(F), wide256_min_tiles(F)), M, Np);
-    return skinny_workspace(plan_skinny(F, M, Np, K, group_size), M, Np);
-}
-
 hipError_t wna16_launch(const DenseArgs& a, bool bf16, bool zp) {
     (void)zp;  // zero-points travel as a pointer (null for symmetric INT4)
     return bf16 ? launch_all<Fmt::WNA16_BF16>(a) : launch_all<Fmt::WNA16_F16>(a);

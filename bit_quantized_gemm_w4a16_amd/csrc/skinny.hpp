@@ -559,6 +559,7 @@ template <Fmt F, int MT, int SPW, int CPW>
 hipError_t launch_skinny_k(dim3 grid, int lds_bytes, const SkinnyArgs& a, hipStream_t st) {
     if (plan_recorder()) {
         plan_record("skinny_kernel<%s,%d,%d,%d> grid=%ux%u splits=%d", fmt_name(F), MT, SPW, CPW, grid.x, grid.y, a.splits);
+        if (a.splits > 1) plan_workspace((size_t)a.splits * (size_t)a.M * (size_t)a.Np * 4);
         return hipSuccess;
     }
     // allow dynamic LDS beyond the 64 KB default, once per instantiation
@@ -613,9 +614,5 @@ hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t s
     return hipGetLastError();
 }
 
-// Workspace of a split launch: the partial tiles.
-inline size_t skinny_workspace(const SkinnyPlan& pl, int64_t M, int64_t Np) {
-    return pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)Np * 4 : 0;
-}
 
 }  // namespace hq

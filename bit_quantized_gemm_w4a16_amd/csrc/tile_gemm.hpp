@@ -891,10 +891,6 @@ inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256, bool 
     return pl;
 }
 
-inline size_t tile_workspace(const TilePlan& pl, int64_t M, int64_t Np) {
-    return pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)Np * 4 : 0;
-}
-
 template <Fmt F, int BM, int BN, int WM, int WN, int PD>
 hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
     p.tiles_m = (int)((p.M + BM - 1) / BM);
@@ -903,7 +899,10 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
     if (plan_recorder()) {
         plan_record("tile_gemm_kernel<%s,%d,%d,%d,%d,%d> grid=%lld splits=%d", fmt_name(F), BM, BN, WM, WN, PD,
                     (long long)grid, p.splits);
-        if (p.splits > 1) plan_record("tile_finalize_kernel<%s>", fmt_name(F));
+        if (p.splits > 1) {
+            plan_record("tile_finalize_kernel<%s>", fmt_name(F));
+            plan_workspace((size_t)p.splits * (size_t)p.M * (size_t)p.Np * 4);
+        }
         return hipSuccess;
     }
     hipLaunchKernelGGL((tile_gemm_kernel<F, BM, BN, WM, WN, PD>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, p);

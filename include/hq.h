@@ -41,8 +41,8 @@
  *    reads within the same call, so its contents need no initialisation and
  *    are meaningless between calls.  Two calls that share a workspace must not
  *    run concurrently.
- *  - Thread safety: the library holds no mutable global state besides a
- *    per-device property cache filled once.
+ *  - Thread safety: the library holds no mutable global state besides
+ *    per-device caches filled once (kernel attributes).
  */
 #ifndef HQ_H
 #define HQ_H
