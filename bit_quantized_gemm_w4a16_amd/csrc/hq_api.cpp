@@ -7,9 +7,11 @@
 // ahead of time.  The host path does O(1) checks and no allocation, in the
 // spirit of the launch-overhead work in "Humming v0.1.0-0.1.4", section
 // "v0.1.1".
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "hq_common.h"
@@ -172,6 +174,53 @@ static size_t dense_workspace(const LayerInfo& L, int64_t M) {
     return dense_plan(L, M, nullptr, 0, &ws) == HQ_OK ? ws : 0;
 }
 
+// ---- scratch memory of the no-allocation entry point ----
+// One array in every device's copy of the code object, used by
+// hq_gemm_noalloc in place of a caller's workspace.  In host code the array's
+// name is only a stand-in: its device address is looked up once per device
+// (with that device current) and kept in scratch_dev[].
+static __device__ __align__(256) char scratch[HQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_dev[kMaxDevices];
+std::mutex scratch_mu;
+}  // namespace
+
+// Device address of `scratch` on the device that runs `stream`.
+static hq_status scratch_for_stream(hipStream_t stream, void** out) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return set_error(HQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    int dev = cur;
+    if (stream) {
+        hipDevice_t d = 0;
+        e = hipStreamGetDevice(stream, &d);
+        if (e != hipSuccess) return set_error(HQ_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return set_error(HQ_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+    void* p = scratch_dev[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(scratch_mu);
+        p = scratch_dev[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+                return set_error(HQ_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (dev != cur) {
+                const hipError_t e2 = hipSetDevice(cur);
+                if (e == hipSuccess) e = e2;
+            }
+            if (e != hipSuccess || !p)
+                return set_error(HQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+            scratch_dev[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return HQ_OK;
+}
+
 }  // namespace hq
 
 using namespace hq;
@@ -275,6 +324,26 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const flo
     }
     DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, a_scale, w, s, z, D, workspace, ws_bytes, (hipStream_t)stream};
     return dense_launch(L, a);
+}
+
+hq_status hq_gemm_noalloc(const hq_layer_desc* desc, int64_t M, const void* A, const float* a_scale,
+                          const void* w, const void* s, const void* z, const void* s2, void* D, hq_stream_t stream) {
+    LayerInfo L;
+    hq_status st = describe(desc, &L);
+    if (st != HQ_OK) return st;
+    if (desc->num_experts) return set_error(HQ_ERR_INVALID_ARG, "hq_gemm_noalloc takes a dense descriptor (num_experts == 0)");
+    if (M < 0 || M > (1LL << 30)) return set_error(HQ_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+    if (M == 0) return ok();
+    const size_t need = dense_workspace(L, M);
+    if (need > HQ_NOALLOC_SCRATCH_BYTES)
+        return set_error(HQ_ERR_WORKSPACE, "this call needs %zu bytes of scratch; hq_gemm_noalloc holds %zu (use hq_gemm "
+                         "with a workspace)", need, (size_t)HQ_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need) {
+        st = scratch_for_stream((hipStream_t)stream, &ws);
+        if (st != HQ_OK) return st;
+    }
+    return hq_gemm(desc, M, A, a_scale, w, s, z, s2, D, ws, need ? (size_t)HQ_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 hq_status hq_gemm_plan(const hq_layer_desc* desc, int64_t M, char* buf, size_t len) {

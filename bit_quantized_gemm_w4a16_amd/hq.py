@@ -60,6 +60,7 @@ _SIGS = {
     "hq_workspace_init": (C.c_int, [_P, C.c_size_t, _P]),
     "hq_gemm": (C.c_int, [_P, C.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "hq_gemm_plan": (C.c_int, [_P, C.c_int64, C.c_char_p, C.c_size_t]),
+    "hq_gemm_noalloc": (C.c_int, [_P, C.c_int64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hq_moe_gemm": (C.c_int, [_P, C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               C.c_size_t, _P]),
     "hq_quantize_act": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, _P, _P, _P, _P]),
@@ -189,6 +190,14 @@ def hq_workspace_init(workspace, nbytes: int, stream=None) -> None:
 def hq_gemm(desc, M, A, a_scale, w, s, z, D, workspace=None, ws_bytes=0, stream=None) -> None:
     _check(lib().hq_gemm(C.byref(desc), M, _dp(A), _dp(a_scale), _dp(w), _dp(s), _dp(z), None, _dp(D),
                          _dp(workspace), ws_bytes, _stream(stream)), "hq_gemm")
+
+
+HQ_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def hq_gemm_noalloc(desc, M, A, a_scale, w, s, z, D, stream=None) -> None:
+    _check(lib().hq_gemm_noalloc(C.byref(desc), M, _dp(A), _dp(a_scale), _dp(w), _dp(s), _dp(z), None, _dp(D),
+                                 _stream(stream)), "hq_gemm_noalloc")
 
 
 def hq_gemm_plan(desc, M) -> list:

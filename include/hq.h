@@ -42,7 +42,8 @@
  *    are meaningless between calls.  Two calls that share a workspace must not
  *    run concurrently.
  *  - Thread safety: the library holds no mutable global state besides
- *    per-device caches filled once (kernel attributes).
+ *    per-device caches filled once (kernel attributes, the device address of
+ *    hq_gemm_noalloc's scratch array).
  */
 #ifndef HQ_H
 #define HQ_H
@@ -224,6 +225,25 @@ hq_status hq_workspace_init(void* workspace, size_t bytes, hq_stream_t stream);
 hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const float* a_scale,
                   const void* w, const void* s, const void* z, const void* s2, void* D,
                   void* workspace, size_t ws_bytes, hq_stream_t stream);
+
+/*
+ * hq_gemm without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, kernels and results as hq_gemm;
+ * where that call's plan needs split-K partial tiles, they go to a scratch
+ * array of HQ_NOALLOC_SCRATCH_BYTES compiled into the library, one per GPU,
+ * held until the process ends.  Calls whose plan needs more scratch return
+ * HQ_ERR_WORKSPACE (hq_workspace_bytes() tells the need in advance).  Nothing
+ * is allocated: no hipMalloc/hipFree, no allocating library call.  The first
+ * call on a GPU looks up the array's device address once (hipGetSymbolAddress,
+ * with that GPU made current for the lookup).  Every call on one GPU shares
+ * its array, so calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller; the kernels write every
+ * scratch byte they read within the call, so nothing needs clearing.
+ */
+#define HQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+hq_status hq_gemm_noalloc(const hq_layer_desc* desc, int64_t M, const void* A, const float* a_scale,
+                          const void* w, const void* s, const void* z, const void* s2, void* D, hq_stream_t stream);
 
 /*
  * Host only, no HIP call: the kernel launches hq_gemm would enqueue for this
