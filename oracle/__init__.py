@@ -61,6 +61,12 @@ def lib():
         L.hq_oracle_gemm_wna16.argtypes = [i64, i64, i64, i64, C.c_int, p, C.c_int, p, p, p, p, i64, p]
         L.hq_oracle_gemm_w4a8_mxfp4.restype = C.c_int
         L.hq_oracle_gemm_w4a8_mxfp4.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
+        L.hq_oracle_e2m1_encode.restype = C.c_uint
+        L.hq_oracle_e2m1_encode.argtypes = [d]
+        L.hq_oracle_quant_act_mx.restype = C.c_int
+        L.hq_oracle_quant_act_mx.argtypes = [i64, i64, C.c_int, p, p, p]
+        L.hq_oracle_gemm_mx_mxfp4.restype = C.c_int
+        L.hq_oracle_gemm_mx_mxfp4.argtypes = [i64, i64, i64, C.c_int, p, p, p, p, p, i64, p]
         L.hq_oracle_gemm_w8a8.restype = C.c_int
         L.hq_oracle_gemm_w8a8.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p, p]
         L.hq_oracle_moe_route.restype = C.c_int
@@ -129,6 +135,26 @@ def quant_act_e4m3(x: np.ndarray):
     return q, s
 
 
+def e2m1_encode(x: float) -> int:
+    """E2M1 code of x: nearest, ties to even, saturating at +-6 (sign kept)."""
+    return int(lib().hq_oracle_e2m1_encode(float(x)))
+
+
+def quant_act_mx(x: np.ndarray, elem: str):
+    """MX activations (OCP MX v1.0, one E8M0 scale per 32 along K): elem 'e4m3'
+    -> (codes uint8 [M,K], scales uint8 [M,K/32]); elem 'e2m1' -> (codes
+    uint8 [M,K/2] two per byte, low nibble first, scales uint8 [M,K/32])."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    fp4 = elem == "e2m1"
+    assert fp4 or elem == "e4m3"
+    q = np.zeros((M, K // 2 if fp4 else K), dtype=np.uint8)
+    e = np.empty((M, K // 32), dtype=np.uint8)
+    if lib().hq_oracle_quant_act_mx(M, K, int(fp4), _ptr(x), _ptr(q), _ptr(e)):
+        raise ValueError("K must be a multiple of 32")
+    return q, e
+
+
 # GEMMs -----------------------------------------------------------------
 
 def gemm_wna16(A, q, s, z=None, *, N, K, G, a_bf16: bool, w_signed: bool, rows=None):
@@ -152,6 +178,19 @@ def gemm_w4a8_mxfp4(qa, s_a, q, e, *, N, K, rows=None):
                                          _ptr(_c(e, np.uint8)), _ptr(r), R, _ptr(out))
     if rc:
         raise ValueError(f"oracle gemm_w4a8_mxfp4 failed ({rc})")
+    return out
+
+
+def gemm_mx_mxfp4(qa, ea, q, e, *, N, K, a_elem: str, rows=None):
+    """MX activations (E4M3 or E2M1 codes + E8M0 per 32) x MXFP4 weights, fp64."""
+    qa = _c(qa, np.uint8)
+    M = qa.shape[0]
+    r, R = _rows(rows, M)
+    out = np.empty((R, N), dtype=np.float64)
+    rc = lib().hq_oracle_gemm_mx_mxfp4(M, N, K, int(a_elem == "e2m1"), _ptr(qa), _ptr(_c(ea, np.uint8)),
+                                       _ptr(_c(q, np.uint32)), _ptr(_c(e, np.uint8)), _ptr(r), R, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle gemm_mx_mxfp4 failed ({rc})")
     return out
 
 

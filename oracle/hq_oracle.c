@@ -141,6 +141,80 @@ void hq_oracle_quant_act_e4m3(int64_t M, int64_t K, const float* x, uint8_t* q, 
 }
 
 /* ------------------------------------------------------------------ */
+/* MX activation quantisation (OCP MX v1.0: one E8M0 scale per 32)      */
+/* ------------------------------------------------------------------ */
+
+/* Nearest E2M1 value to v, ties to the even mantissa bit, saturating at
+ * +-6; the sign of v is kept (so -0.0 and tiny negatives give code 8). */
+unsigned hq_oracle_e2m1_encode(double v)
+{
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    if (v != v) return 0u;
+    unsigned sign = signbit(v) ? 8u : 0u;
+    double a = fabs(v);
+    if (a >= 6.0) return sign | 7u;          /* saturation (also avoids distances lost to rounding) */
+    unsigned best = 0;
+    for (unsigned c = 1; c < 8; ++c) {
+        double dc = fabs(a - grid[c]), db = fabs(a - grid[best]);
+        if (dc < db || (dc == db && (c & 1u) == 0u)) best = c;
+    }
+    return sign | best;
+}
+
+/* One block of 32 values x[0..31] -> E8M0 exponent and element codes
+ * (elem 0: E4M3, codes one per byte; elem 1: E2M1, codes in code[0..31]).
+ * OCP MX v1.0, section 6.3: the shared exponent is floor(log2(max|x|))
+ * minus the largest exponent of the element format (E4M3: 8, since
+ * 448 = 1.75 * 2^8; E2M1: 2, since 6 = 1.5 * 2^2), as an E8M0 value
+ * clamped to 0..254 (0 for an all-zero block); each element is x / 2^(E-127)
+ * rounded to nearest-even and saturated.  A block holding a NaN or an
+ * infinity gets the NaN scale 0xFF and zero codes. */
+static unsigned mx_block(const float* x, int elem, unsigned* code)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) {
+        if (!isfinite(x[i])) {
+            for (int j = 0; j < 32; ++j) code[j] = 0;
+            return 0xFFu;
+        }
+        if (fabs((double)x[i]) > amax) amax = fabs((double)x[i]);
+    }
+    int E = 0;
+    if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex);                           /* amax = f * 2^ex, f in [0.5, 1) */
+        E = (ex - 1) - (elem ? 2 : 8) + 127;
+        if (E < 0) E = 0;
+        if (E > 254) E = 254;
+    }
+    for (int i = 0; i < 32; ++i) {
+        double v = ldexp((double)x[i], 127 - E);   /* exact power-of-two scaling */
+        code[i] = elem ? hq_oracle_e2m1_encode(v) : hq_oracle_e4m3_encode((float)v);
+    }
+    return (unsigned)E;
+}
+
+/* x fp32 [M][K] (K % 32 == 0) -> codes (E4M3: uint8 [M][K]; E2M1: uint8
+ * [M][K/2], element k in the low nibble of byte k/2 when k is even) and
+ * E8M0 scales uint8 [M][K/32]. */
+int hq_oracle_quant_act_mx(int64_t M, int64_t K, int elem, const float* x, uint8_t* q, uint8_t* e)
+{
+    if (K % 32 || (elem != 0 && elem != 1)) return 1;
+    unsigned code[32];
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < K / 32; ++b) {
+            e[m * (K / 32) + b] = (uint8_t)mx_block(x + m * K + b * 32, elem, code);
+            for (int i = 0; i < 32; ++i) {
+                int64_t k = b * 32 + i;
+                if (elem == 0) q[m * K + k] = (uint8_t)code[i];
+                else if ((k & 1) == 0) q[m * (K / 2) + k / 2] = (uint8_t)code[i];
+                else q[m * (K / 2) + k / 2] |= (uint8_t)(code[i] << 4);
+            }
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* dense GEMMs                                                          */
 /* ------------------------------------------------------------------ */
 
@@ -198,6 +272,38 @@ int hq_oracle_gemm_w4a8_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* qa
         }
         for (int64_t r = 0; r < R; ++r) out[r * N + n] *= (double)s_a[row_of(rows, r)];
     }
+    free(a);
+    return 0;
+}
+
+/* MX activations x MXFP4 weights (W4A4 with E2M1 activations, W4A8 with
+ * MXFP8 E4M3 activations): A_real[m][k] = dec(qa code) * 2^(ea[m][k/32]-127),
+ * W_real as in the W4A8-MXFP4 entry, D = A_real x W_real.
+ * a_elem 0: qa is E4M3 uint8 [M][K]; a_elem 1: qa is E2M1 uint8 [M][K/2]
+ * (element k in the low nibble of byte k/2 when k is even). */
+int hq_oracle_gemm_mx_mxfp4(int64_t M, int64_t N, int64_t K, int a_elem, const uint8_t* qa,
+                            const uint8_t* ea, const uint32_t* q, const uint8_t* e8,
+                            const int64_t* rows, int64_t nrows, double* out)
+{
+    if (K % 32 || (a_elem != 0 && a_elem != 1)) return 1;
+    int64_t R = rows ? nrows : M;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(R * K + 1));
+    if (!a) return 2;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t m = row_of(rows, r);
+        for (int64_t k = 0; k < K; ++k) {
+            double v = a_elem ? hq_oracle_e2m1((qa[m * (K / 2) + k / 2] >> (4 * (k & 1))) & 15u)
+                              : hq_oracle_e4m3(qa[m * K + k]);
+            a[r * K + k] = v * hq_oracle_e8m0(ea[m * (K / 32) + k / 32]);
+        }
+    }
+    memset(out, 0, sizeof(double) * (size_t)(R * N));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            double w = hq_oracle_e2m1(nib_along_k(q, N, k, n)) * hq_oracle_e8m0(e8[(k / 32) * N + n]);
+            for (int64_t r = 0; r < R; ++r) out[r * N + n] += a[r * K + k] * w;
+        }
     free(a);
     return 0;
 }

@@ -417,3 +417,147 @@ def test_silu_mul_matches_independent_formula():
             want = oracle.bf16_encode(g * (1.0 + math.tanh(g / 2.0)) / 2.0 * u)
             assert got[r, i] == want, (r, i, g, u)
     assert got[0, 0] in (0, 0x8000) and got[0, 1] in (0, 0x8000)   # silu(+-0) * u is a zero
+
+
+# ---------------------------------------------------------------------------
+# MX activations (OCP MX v1.0: E8M0 scale per 32 elements) and MX x MXFP4 GEMMs
+# ---------------------------------------------------------------------------
+
+def test_e2m1_encode_round_trip_ties_and_saturation():
+    for code, v in golden("e2m1_ocp_mx_v1.txt"):
+        assert oracle.e2m1_encode(v) == code, (code, v)
+    # midpoints between neighbours go to the even mantissa bit (code & 1 == 0)
+    for v, code in [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6),
+                    (-0.25, 8), (-0.75, 10), (-5.0, 14)]:
+        assert oracle.e2m1_encode(v) == code, (v, code)
+    for v in (6.0, 6.5, 7.0, 1e30):
+        assert oracle.e2m1_encode(v) == 7 and oracle.e2m1_encode(-v) == 15
+    assert oracle.e2m1_encode(-1e-30) == 8 and oracle.e2m1_encode(1e-30) == 0
+
+
+def test_e2m1_encode_is_nearest_and_monotone():
+    vals = np.array([E2M1_TABLE[c] for c in range(8)])
+    prev = -1
+    for v in np.linspace(0.0, 6.0, 2401):
+        c = oracle.e2m1_encode(float(v))
+        assert c >= prev
+        prev = c
+        assert abs(vals[c] - v) <= np.abs(vals - v).min() + 1e-15
+
+
+@pytest.mark.parametrize("elem,emax,lo,hi", [("e2m1", 2, 4.0, 6.0), ("e4m3", 8, 256.0, 448.0)])
+def test_quant_act_mx_scale_rule_and_error_bound(elem, emax, lo, hi):
+    x = syn.normal_rows(0, 9, syn.T_A, 17, 256) * np.float32(3.0)
+    x[4, 32:64] = 0.0                                     # an all-zero block
+    x[5, :32] *= np.float32(1e-30)                        # tiny block
+    q, e = oracle.quant_act_mx(x, elem)
+    dec = (lambda c: E2M1_TABLE[int(c)]) if elem == "e2m1" else oracle.e4m3
+    for m in range(x.shape[0]):
+        for b in range(8):
+            blk = x[m, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.abs(blk).max()
+            E = int(e[m, b])
+            codes = [(q[m, (32 * b + i) // 2] >> (4 * (i & 1))) & 15 if elem == "e2m1" else q[m, 32 * b + i]
+                     for i in range(32)]
+            if amax == 0:
+                assert E == 0 and all(c == 0 for c in codes)
+                continue
+            X = 2.0 ** (E - 127)
+            # the scale puts the block maximum in [2^emax, 2^(emax+1)) before rounding
+            assert 2.0 ** emax <= amax / X < 2.0 ** (emax + 1)
+            im = int(np.abs(blk).argmax())
+            assert lo <= abs(dec(codes[im])) <= hi
+            for i in range(32):
+                r = dec(codes[i]) * X
+                # nearest representable: within half the largest grid step (2 for e2m1 at 4..6,
+                # 32 for e4m3 at 256..448) times X, or saturated
+                step = (2.0 if elem == "e2m1" else 32.0) * X
+                assert abs(r - blk[i]) <= step / 2 + 1e-300 or abs(blk[i]) / X > hi
+
+
+def test_quant_act_mx_hand_worked_block_and_nibble_order():
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :6] = np.array([6.0, -3.0, 0.5, 0.25, 0.75, 5.0], dtype=np.float32) * np.float32(32.0)
+    q, e = oracle.quant_act_mx(x, "e2m1")
+    assert e[0, 0] == 127 + 7 - 2                        # amax 192: floor(log2) = 7, E2M1 emax 2
+    # codes: 6 -> 7, -3 -> 8|5, 0.5 -> 1, 0.25 -> 0 (tie to even), 0.75 -> 2 (tie to 1.0), 5 -> 6 (tie to 4)
+    assert list(q[0, :3]) == [7 | (13 << 4), 1 | (0 << 4), 2 | (6 << 4)]
+    assert not q[0, 3:].any()
+    q8, e8 = oracle.quant_act_mx(x, "e4m3")
+    assert e8[0, 0] == 127 + 7 - 8
+    ref = torch.from_numpy(np.ldexp(x.astype(np.float64), 127 - int(e8[0, 0])).astype(np.float32)).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(q8, ref.view(torch.uint8).numpy())
+
+
+def test_quant_act_mx_e4m3_matches_torch_cast_in_range_and_saturates():
+    x = syn.normal_rows(1, 9, syn.T_A, 9, 512)
+    q, e = oracle.quant_act_mx(x, "e4m3")
+    v = np.ldexp(x.astype(np.float64), 127 - np.repeat(e.astype(np.int64), 32, axis=1))
+    inr = np.abs(v) <= 448.0
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(q[inr], ref[inr])
+    assert np.all((q[~inr] & 0x7F) == 0x7E)             # beyond 448 saturates
+
+
+def test_quant_act_mx_non_finite_block_gets_nan_scale():
+    x = syn.normal_rows(2, 9, syn.T_A, 2, 64)
+    x[0, 3] = np.nan
+    x[1, 40] = -np.inf
+    for elem in ("e2m1", "e4m3"):
+        q, e = oracle.quant_act_mx(x, elem)
+        assert e[0, 0] == 0xFF and e[1, 1] == 0xFF and e[0, 1] != 0xFF and e[1, 0] != 0xFF
+        assert math.isnan(oracle.e8m0(int(e[0, 0])))
+
+
+def mx_a_decode(qa, ea, K, elem):
+    if elem == "e2m1":
+        codes = np.stack([qa & 15, qa >> 4], axis=-1).reshape(qa.shape[0], K).astype(np.int64)
+        v = e2m1_tab(codes)
+    else:
+        v = np.array([oracle.e4m3(c) for c in range(256)])[qa.astype(np.int64)]
+    return v * 2.0 ** (np.repeat(ea.astype(np.int64), 32, axis=1) - 127)
+
+
+@pytest.mark.parametrize("elem", ["e2m1", "e4m3"])
+def test_gemm_mx_mxfp4_exact_rational_tiny(elem):
+    M, N, K = 2, 16, 64
+    d = syn.w4a8_mxfp4(7, M, N, K)
+    qa, ea = oracle.quant_act_mx(d["A0"] * np.float32(50.0), elem)
+    got = oracle.gemm_mx_mxfp4(qa, ea, d["q"], d["e"], N=N, K=K, a_elem=elem)
+    a = mx_a_decode(qa, ea, K, elem)
+    codes = unpack_k(d["q"], K)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(a[m, k])) * Fraction(E2M1_TABLE[int(codes[k, n])]) * Fraction(2) ** (int(d["e"][k // 32, n]) - 127)
+            assert abs(got[m, n] - float(acc)) <= 1e-13 * max(abs(float(acc)), 1e-30)
+
+
+def test_gemm_mx_with_unit_scales_equals_tokenwise_w4a8():
+    """E4M3 activations whose MX scales are all 127 are the tokenwise W4A8 case with s_a = 1."""
+    M, N, K = 5, 48, 256
+    d = syn.w4a8_mxfp4(8, M, N, K)
+    qa, _ = oracle.quant_act_e4m3(d["A0"])
+    ones = np.ones(M, dtype=np.float32)
+    e127 = np.full((M, K // 32), 127, dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.gemm_mx_mxfp4(qa, e127, d["q"], d["e"], N=N, K=K, a_elem="e4m3"),
+                                  oracle.gemm_w4a8_mxfp4(qa, ones, d["q"], d["e"], N=N, K=K))
+
+
+@pytest.mark.parametrize("elem", ["e2m1", "e4m3"])
+def test_gemm_mx_block_scale_step_and_sign_flip(elem):
+    M, N, K = 3, 32, 256
+    d = syn.w4a8_mxfp4(9, M, N, K)
+    qa, ea = oracle.quant_act_mx(d["A0"], elem)
+    base = oracle.gemm_mx_mxfp4(qa, ea, d["q"], d["e"], N=N, K=K, a_elem=elem)
+    flip = qa ^ np.uint8(0x88 if elem == "e2m1" else 0x80)
+    np.testing.assert_array_equal(oracle.gemm_mx_mxfp4(flip, ea, d["q"], d["e"], N=N, K=K, a_elem=elem), -base)
+    e2 = ea.copy()
+    e2[1, 5] += 1                                          # row 1, K block [160, 192) doubles
+    moved = oracle.gemm_mx_mxfp4(qa, e2, d["q"], d["e"], N=N, K=K, a_elem=elem)
+    assert np.array_equal(moved[[0, 2]], base[[0, 2]])
+    a = mx_a_decode(qa, ea, K, elem)
+    w = e2m1_tab(unpack_k(d["q"], K)) * (2.0 ** (np.repeat(d["e"].astype(np.int64), 32, axis=0) - 127))
+    contrib = a[1, 160:192] @ w[160:192]
+    assert rel_err(moved[1] - base[1], contrib) < 1e-12
