@@ -91,6 +91,16 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
             return set_error(HQ_ERR_UNSUPPORTED, "zero-points: UINT4 codes need UINT4 zero-points, INT4 codes none");
         if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 takes no activation scale");
         if (d->out_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 output dtype must equal the activation dtype");
+    } else if (w == HQ_DT_FP4_E2M1 && (a == HQ_DT_FP8_E4M3 || a == HQ_DT_FP4_E2M1) && d->a_scale == HQ_ASCALE_MX_E8M0) {
+        I.kind = Kind::MXA_MX;
+        I.a_fp4 = a == HQ_DT_FP4_E2M1;
+        if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "MX activations are built for dense layers");
+        if (d->w_scale_dtype != HQ_DT_E8M0 || d->w_scale_gran != HQ_GRAN_PER_GROUP_K || d->group_size != 32)
+            return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 needs E8M0 scales per 32 K elements");
+        if (d->K % 128) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 needs K %% 128 == 0 (K=%lld)", (long long)d->K);
+        if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 takes no zero-points");
+        if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 paths output bf16");
+        I.G = 32;
     } else if (w == HQ_DT_FP4_E2M1 && (a == HQ_DT_FP8_E4M3 || a == HQ_DT_BF16)) {
         const bool moe = d->num_experts > 0;
         if (a == HQ_DT_FP8_E4M3) {
@@ -147,6 +157,7 @@ static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
         case Kind::WNA16: return hip_status(wna16_launch(a, L.a_bf16, L.zp), "hq_gemm(W4A16)");
         case Kind::W4A8_MX: return hip_status(w4a8_launch(a), "hq_gemm(W4A8-MXFP4)");
         case Kind::W8A8: return hip_status(w8a8_launch(a, L.out_i32), "hq_gemm(W8A8)");
+        case Kind::MXA_MX: return hip_status(mx_act_launch(a, L.a_fp4), L.a_fp4 ? "hq_gemm(W4A4-MXFP4)" : "hq_gemm(W4A8-MXFP8xMXFP4)");
         default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind runs through hq_moe_gemm");
     }
 }
@@ -161,7 +172,7 @@ static hq_status dense_plan(const LayerInfo& L, int64_t M, char* buf, size_t len
         return HQ_OK;
     }
     g_plan = &rec;
-    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
     const hq_status st = dense_launch(L, a);
     g_plan = nullptr;
     if (buf) buf[rec.used < len ? rec.used : len - 1] = 0;
@@ -295,7 +306,7 @@ hq_status hq_workspace_init(void* workspace, size_t bytes, hq_stream_t stream) {
     return hip_status(fill_zero_launch(workspace, bytes, (hipStream_t)stream), "hq_workspace_init");
 }
 
-hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const float* a_scale,
+hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const void* a_scale,
                   const void* w, const void* s, const void* z, const void* s2, void* D,
                   void* workspace, size_t ws_bytes, hq_stream_t stream) {
     LayerInfo L;
@@ -307,13 +318,13 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const flo
     if (!A || !w || !s || !D) return set_error(HQ_ERR_INVALID_ARG, "A, w, s and D are required");
     const bool need_z = L.kind == Kind::WNA16 && L.zp;
     if (need_z != (z != nullptr)) return set_error(HQ_ERR_INVALID_ARG, need_z ? "zero-points required" : "z must be NULL");
-    const bool need_as = desc->a_scale == HQ_ASCALE_PER_TOKEN_F32;
+    const bool need_as = desc->a_scale != HQ_ASCALE_NONE;
     if (need_as != (a_scale != nullptr)) return set_error(HQ_ERR_INVALID_ARG, need_as ? "a_scale required" : "a_scale must be NULL");
     if (s2) return set_error(HQ_ERR_INVALID_ARG, "s2 must be NULL");
     if (!aligned16(A) || !aligned16(w) || !aligned16(s) || !aligned16(D) || (z && !aligned16(z)) ||
         (a_scale && !aligned16(a_scale)))
         return set_error(HQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
-    const int64_t ab = desc->a_dtype == HQ_DT_BF16 || desc->a_dtype == HQ_DT_FP16 ? 2 : 1;
+    const int64_t ab = desc->a_dtype == HQ_DT_BF16 || desc->a_dtype == HQ_DT_FP16 ? 2 : 1;  // fp4: bounded by 1
     if (M * L.K * ab >= (int64_t)1 << 32 || M * L.N >= (int64_t)1 << 31)
         return set_error(HQ_ERR_UNSUPPORTED, "M*K activation bytes must stay below 4 GiB and M*N below 2^31");
     const size_t need = dense_workspace(L, M);
@@ -322,11 +333,13 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const flo
             return set_error(HQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? ws_bytes : (size_t)0);
         if (!aligned16(workspace)) return set_error(HQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
     }
-    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, a_scale, w, s, z, D, workspace, ws_bytes, (hipStream_t)stream};
+    const bool mx = desc->a_scale == HQ_ASCALE_MX_E8M0;
+    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, mx ? nullptr : (const float*)a_scale,
+                mx ? (const uint8_t*)a_scale : nullptr, w, s, z, D, workspace, ws_bytes, (hipStream_t)stream};
     return dense_launch(L, a);
 }
 
-hq_status hq_gemm_noalloc(const hq_layer_desc* desc, int64_t M, const void* A, const float* a_scale,
+hq_status hq_gemm_noalloc(const hq_layer_desc* desc, int64_t M, const void* A, const void* a_scale,
                           const void* w, const void* s, const void* z, const void* s2, void* D, hq_stream_t stream) {
     LayerInfo L;
     hq_status st = describe(desc, &L);
@@ -423,6 +436,20 @@ hq_status hq_quantize_act(int32_t out_dtype, int64_t M, int64_t K, const float* 
     if (!x || !q || !s) return set_error(HQ_ERR_INVALID_ARG, "x, q and s are required");
     if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return set_error(HQ_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
     return hip_status(quant_e4m3_launch(M, K, x, (uint8_t*)q, s, (hipStream_t)stream), "hq_quantize_act");
+}
+
+hq_status hq_quantize_act_mx(int32_t out_dtype, int64_t M, int64_t K, const float* x, void* q, void* e,
+                             hq_stream_t stream) {
+    if (out_dtype != HQ_DT_FP8_E4M3 && out_dtype != HQ_DT_FP4_E2M1)
+        return set_error(HQ_ERR_UNSUPPORTED, "MX activation codes are FP8_E4M3 or FP4_E2M1");
+    if (M < 0 || K < 32 || M > (1LL << 30) || K > (1LL << 24) || K % 32)
+        return set_error(HQ_ERR_INVALID_ARG, "M/K out of range (K a multiple of 32)");
+    if (M * K >= (1LL << 34)) return set_error(HQ_ERR_UNSUPPORTED, "M*K too large");
+    if (M == 0) return ok();
+    if (!x || !q || !e) return set_error(HQ_ERR_INVALID_ARG, "x, q and e are required");
+    if (!aligned16(x) || !aligned16(q) || !aligned16(e)) return set_error(HQ_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    return hip_status(quant_mx_launch(out_dtype == HQ_DT_FP4_E2M1, M, K, x, (uint8_t*)q, (uint8_t*)e, (hipStream_t)stream),
+                      "hq_quantize_act_mx");
 }
 
 hq_status hq_silu_mul(int32_t dtype, int64_t rows, int64_t I, const void* gate_up, void* out, hq_stream_t stream) {

@@ -16,6 +16,7 @@ enum class Kind {
     W4A8_MX,      // fp8-e4m3 A (per-token fp32 scale), e2m1 W, E8M0 per 32 K
     W8A8,         // int8 A (per-token fp32 scale), int8 W, fp32 per-channel
     MOE_MX_BF16,  // MoE: bf16 A, e2m1 W, E8M0 per 32 K
+    MXA_MX,       // MX activations (E4M3 or E2M1, E8M0 per 32 K) x e2m1 W, E8M0 per 32 K
 };
 
 struct LayerInfo {
@@ -24,6 +25,7 @@ struct LayerInfo {
     bool a_bf16;   // WNA16: activations (and scales, output) are bf16
     bool zp;       // WNA16: UINT4 codes with UINT4 zero-points
     bool out_i32;  // W8A8: raw int32 accumulators
+    bool a_fp4;    // MXA_MX: E2M1 activations (else E4M3)
 };
 
 // Validates a descriptor; fills `info` on success.  Sets the thread-local

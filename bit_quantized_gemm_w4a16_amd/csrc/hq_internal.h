@@ -35,7 +35,8 @@ struct DenseArgs {
     int64_t M, N, K, Np;
     int group_size;
     const void* A;
-    const float* a_scale;
+    const float* a_scale;   // per-token fp32 scales (W4A8 tokenwise, W8A8)
+    const uint8_t* a_e8;    // MX activation scales, E8M0 [M][K/32]
     const void* w;
     const void* s;
     const void* z;
@@ -51,6 +52,7 @@ hipError_t wna16_launch(const DenseArgs& a, bool bf16, bool zp);
 // W4A8-MXFP4 and W8A8-INT8 (split-K workspace for mid M)
 hipError_t w4a8_launch(const DenseArgs& a);
 hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32);
+hipError_t mx_act_launch(const DenseArgs& a, bool fp4_act);  // MX activations x MXFP4 weights
 
 // MoE
 struct MoeLayout {  // byte offsets into the MoE workspace
@@ -83,6 +85,7 @@ hipError_t moe_gather_launch(const void* A, const int* sorted, int64_t P, int to
 
 // activation quantisation (tokenwise E4M3)
 hipError_t quant_e4m3_launch(int64_t M, int64_t K, const float* x, uint8_t* q, float* s, hipStream_t st);
+hipError_t quant_mx_launch(bool fp4, int64_t M, int64_t K, const float* x, uint8_t* q, uint8_t* e, hipStream_t st);
 hipError_t silu_mul_launch(int64_t rows, int64_t I, const void* in, void* out, hipStream_t st);
 
 // fill kernel used by hq_workspace_init

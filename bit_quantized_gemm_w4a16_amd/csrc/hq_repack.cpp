@@ -128,6 +128,7 @@ void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s
             if (L.zp) *z = E * nst * (size_t)(L.K / L.G) * 8;
             break;
         case Kind::W4A8_MX:
+        case Kind::MXA_MX:
         case Kind::MOE_MX_BF16:
             *w = E * nst * (size_t)(L.K / 128) * 1024;
             *s = E * nst * (size_t)(L.K / 128) * 64;
@@ -148,6 +149,7 @@ void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z,
             if (L.zp) repack_zero4(L, (const uint32_t*)z, (uint64_t*)z_out);
             break;
         case Kind::W4A8_MX:
+        case Kind::MXA_MX:
         case Kind::MOE_MX_BF16:
             repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, false);
             repack_e8m0(L, (const uint8_t*)s, (uint8_t*)s_out);

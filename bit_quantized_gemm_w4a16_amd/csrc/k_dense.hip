@@ -7,6 +7,11 @@
 // that takes the e2m1 codes and the E8M0 exponents directly
 // (v_mfma_scale_f32_16x16x128_f8f6f4), so the weights are never dequantised.
 //
+// MX activations (same section, W4A4 and W4A8 on microscaling formats; section
+// "Auswahl von Aktivierungstypen" for MXFP8 activations): E4M3 or E2M1 codes
+// with one E8M0 scale per 32 K per row, fed with the weights' E8M0 scales to
+// the same scaled MFMA; no epilogue scale.
+//
 // W8A8-INT8 (same section, INT8 through integer MMA): int8 x int8 into exact
 // int32 accumulators (v_mfma_i32_16x16x64_i8), then acc * s_a[m] * s_w[n] in
 // fp32, or the raw int32 accumulators.
@@ -24,6 +29,7 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
         SkinnyArgs s{};
         s.A = a.A;
         s.a_scale = a.a_scale;
+        s.a_e8 = a.a_e8;
         s.W = a.w;
         s.S = a.s;
         s.D = a.D;
@@ -41,6 +47,7 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
     TileArgs p{};
     p.A = a.A;
     p.a_scale = a.a_scale;
+    p.a_e8 = a.a_e8;
     p.W = a.w;
     p.S = a.s;
     p.D = a.D;
@@ -62,5 +69,9 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
 hipError_t w4a8_launch(const DenseArgs& a) { return launch<Fmt::W4A8_MX>(a, 0); }
 
 hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32) { return launch<Fmt::W8A8_I8>(a, raw_i32 ? 1 : 0); }
+
+hipError_t mx_act_launch(const DenseArgs& a, bool fp4_act) {
+    return fp4_act ? launch<Fmt::W4A4_MX>(a, 0) : launch<Fmt::W4A8_MXA>(a, 0);
+}
 
 }  // namespace hq

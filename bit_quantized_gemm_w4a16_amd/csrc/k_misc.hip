@@ -135,6 +135,103 @@ hipError_t quant_e4m3_launch(int64_t M, int64_t K, const float* x, uint8_t* q, f
 
 namespace hq {
 
+// MX activation quantisation (OCP Microscaling Formats v1.0, section 6.3):
+// per row and block of 32 along K the shared exponent is floor(log2(amax))
+// minus the largest exponent of the element format (E4M3 8, E2M1 2), as an
+// E8M0 byte clamped to 0..254 (0 for an all-zero block, 0xFF -- NaN -- for a
+// block holding a NaN or an infinity, whose codes are then 0); each element
+// x * 2^(127 - E) (an exact power-of-two scaling) is rounded to nearest even
+// and saturated.  For normal amax, floor(log2(amax)) is its exponent field
+// minus 127.  One thread per 8 consecutive elements, 4 threads per block.
+//
+// E2M1 rounding: |v| is compared with the midpoints of the grid
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6; a midpoint itself goes to the neighbour with
+// the even mantissa bit, hence strict ">" at 0.25, 1.25, 2.5, 5 and ">=" at
+// 0.75, 1.75, 3.5.  The sign is that of x (so -0 and tiny negatives give 8).
+__device__ __forceinline__ uint32_t e2m1_code(float x, float v) {
+    const float a = fabsf(v);
+    const uint32_t mag = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                         (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+    return mag | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+template <bool FP4>
+__global__ __launch_bounds__(256) void quant_mx_kernel(const float4* __restrict__ x, int64_t ngroups, int K8,
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ e) {
+    constexpr int EMAX = FP4 ? 2 : 8;
+    for (int64_t g0 = (int64_t)blockIdx.x * 256; g0 < ngroups; g0 += (int64_t)gridDim.x * 256) {
+        const int64_t g = g0 + threadIdx.x;  // group of 8 elements; 4 consecutive groups form a block
+        const bool live = g < ngroups;
+        float v[8];
+        if (live) {
+            const float4 a = x[2 * g], b = x[2 * g + 1];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        }
+        float amax = 0.f;
+        uint32_t bad = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            bad |= (uint32_t)((__float_as_uint(v[i]) & 0x7F800000u) == 0x7F800000u);
+            amax = fmaxf(amax, fabsf(v[i]));
+        }
+        // the 4 groups of a block are lanes 4j..4j+3 of the wave (ngroups is a multiple of 4)
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        bad |= __shfl_xor(bad, 1);
+        bad |= __shfl_xor(bad, 2);
+        int E = 0;
+        if (bad) {
+            E = 255;
+        } else if (amax > 0.f) {
+            E = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - EMAX;
+            E = E < 0 ? 0 : E > 254 ? 254 : E;
+        }
+        if (!live) continue;
+        const int sh = 127 - (E == 255 ? 127 : E);
+        if constexpr (FP4) {
+            uint32_t w = 0;
+            if (E != 255) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w |= e2m1_code(v[i], ldexpf(v[i], sh)) << (4 * i);
+            }
+            ((uint32_t*)q)[g] = w;
+        } else {
+            uint32_t lo = 0, hi = 0;
+            if (E != 255) {
+                float c[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(ldexpf(v[i], sh), -448.f), 448.f);
+                lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+                lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], (int)lo, true);
+                hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+                hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], (int)hi, true);
+            }
+            ((uint2*)q)[g] = make_uint2(lo, hi);
+        }
+        if ((g & 3) == 0) e[g >> 2] = (uint8_t)E;
+        (void)K8;
+    }
+}
+
+hipError_t quant_mx_launch(bool fp4, int64_t M, int64_t K, const float* x, uint8_t* q, uint8_t* e, hipStream_t st) {
+    const int64_t ngroups = M * (K / 8);
+    int64_t blocks = (ngroups + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) return hipSuccess;
+    if (fp4)
+        hipLaunchKernelGGL(quant_mx_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, (const float4*)x, ngroups, (int)(K / 8), q, e);
+    else
+        hipLaunchKernelGGL(quant_mx_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, (const float4*)x, ngroups, (int)(K / 8), q, e);
+    return hipGetLastError();
+}
+
+}  // namespace hq
+
+namespace hq {
+
 // SwiGLU between the MoE projections: out[r][i] = bf16(silu(g) * u) with
 // g = in[r][i], u = in[r][I + i], computed in fp32 (exact bf16 -> fp32 inputs)
 // and rounded once to nearest even.  silu(g) = g / (1 + e^-g), evaluated as

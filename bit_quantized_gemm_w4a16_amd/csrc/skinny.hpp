@@ -35,6 +35,9 @@
 //                   on the fp32 partial of the chunk
 //   W4A8_MX         1 x v_mfma_scale_f32_16x16x128_f8f6f4 (fp8 A, fp4 B with
 //                   the E8M0 exponent as the B scale)
+//   W4A8_MXA        the same with the activations' own E8M0 block scales as
+//                   the A scale (MXFP8 activations; copied to LDS with the A slice)
+//   W4A4_MX         the same with fp4 e2m1 activations (MXFP4 x MXFP4)
 //   W8A8_I8         2 x v_mfma_i32_16x16x64_i8 (exact int32)
 #pragma once
 
@@ -48,6 +51,7 @@ constexpr int64_t kSkinnyMaxM = 64;  // dense M handled by this schedule
 struct SkinnyArgs {
     const void* A;          // activations [a_rows][K]
     const float* a_scale;   // per-token fp32 (W4A8 / W8A8), by A row
+    const uint8_t* a_e8;    // MX activation scales E8M0 [a_rows][K/32] (W4A8_MXA / W4A4_MX)
     const void* W;          // packed weights
     const void* S;          // packed group scales / E8M0 / per-channel fp32
     const void* Z;          // packed zero-points (WNA16 with UINT4), or null
@@ -59,16 +63,17 @@ struct SkinnyArgs {
     int splits;
     int cps, cpk;           // chunks per K slice, chunks per wave K-part (host-computed)
     int NS, WS;             // strips per workgroup, wave strip-columns (WK = 4 / WS)
-    int a_off, s_off, z_off;  // LDS layout (bytes)
+    int a_off, s_off, z_off;  // LDS layout (bytes); MX activation scales share z_off
     int raw_i32;            // W8A8: store the int32 accumulators
 };
 
 template <Fmt F>
 struct SkinnyTraits {
     static constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
-    static constexpr bool MX = F == Fmt::W4A8_MX;
-    static constexpr int AB = FmtTraits<F>::AB;        // bytes per activation
-    static constexpr int UPC = 8 * AB;                  // 16-byte A units per 128-K chunk and row
+    static constexpr bool MX = mx_mfma(F);               // E8M0 weight scales per 32 K
+    static constexpr bool MXA = mx_act(F);               // E8M0 activation scales per 32 K
+    static constexpr int AROW = FmtTraits<F>::AROW;      // bytes of a row per 128-K chunk
+    static constexpr int UPC = AROW / 16;                // 16-byte A units per 128-K chunk and row
     static constexpr int NB = FmtTraits<F>::BSTRIP / 1024;  // 16-byte weight loads per chunk and lane
 };
 
@@ -76,7 +81,7 @@ struct SkinnyTraits {
 // rows of a fragment read land in distinct bank groups.
 template <int UPC>
 __device__ __forceinline__ int skinny_swz(int row) {
-    return UPC == 16 ? (row & 15) : (row & 7);
+    return UPC == 16 ? (row & 15) : UPC == 8 ? (row & 7) : (row & 3);
 }
 
 // One work item: K slice `split` of the launch.  Every thread of the
@@ -86,8 +91,8 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     using Tr = SkinnyTraits<F>;
     using Acc = typename FmtTraits<F>::Acc;
     static_assert(F != Fmt::MOE_MX, "MoE experts stream through moe_stream_kernel");
-    constexpr bool WNA16 = Tr::WNA16, MX = Tr::MX;
-    constexpr int AB = Tr::AB, UPC = Tr::UPC, NB = Tr::NB;
+    constexpr bool WNA16 = Tr::WNA16, MX = Tr::MX, MXA = Tr::MXA;
+    constexpr int AROW = Tr::AROW, UPC = Tr::UPC, NB = Tr::NB;
     constexpr int ROWS = 16 * MT;
     constexpr int NLOAD = SPW * CPW * NB;  // weight loads per wave and batch
     static_assert(NLOAD < 64, "vmcnt counts at most 63 loads");
@@ -137,13 +142,13 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
 
     // ---- A slice and scales -> LDS (direct loads, issued between the two halves of the weights) ----
     {
-        const char* Abase = (const char*)p.A + (size_t)c0 * 128 * AB;
+        const char* Abase = (const char*)p.A + (size_t)c0 * AROW;
         const int nblk = (U + 63) >> 6;  // 64-unit blocks per row
         int r = 0, blk = wave;
         while (r < rows && blk >= nblk) { blk -= nblk; ++r; }
         while (r < rows) {
             const int pos = blk * 64 + lane;
-            const char* arow = Abase + (size_t)r * p.K * AB;
+            const char* arow = Abase + (size_t)r * (p.K / 128) * AROW;
             if (pos < U) lds_dma16(arow + ((pos ^ skinny_swz<UPC>(r)) * 16), lds + p.a_off + (r * U + blk * 64) * 16);
             blk += 4;
             while (r < rows && blk >= nblk) { blk -= nblk; ++r; }
@@ -169,6 +174,17 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     const int pos = pos0 + lane;
                     if (pos < nsl * 4)
                         lds_dma16((const char*)Sb + ((size_t)st * p.nc + c0) * 64 + pos * 16, lds + p.s_off + (j * nsl * 4 + pos0) * 16);
+                }
+            }
+            if constexpr (MXA) {
+                // the slice's activation scales: one 4-byte word (4 K blocks) per row and chunk, [row][nsl]
+                const int nw = rows * nsl;
+                for (int w0 = wave * 64; w0 < nw; w0 += 256) {
+                    const int w = w0 + lane;
+                    if (w < nw) {
+                        const int r = w / nsl, c = w - r * nsl;
+                        lds_dma4(p.a_e8 + (size_t)r * (p.K / 32) + (size_t)(c0 + c) * 4, lds + p.z_off + w0 * 4);
+                    }
                 }
             }
         }
@@ -218,7 +234,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     }
     // 16-bit A formats: the LDS operands of chunk i+1 (A fragments, the strip's
     // scale and zero-point word, or its E8M0 byte) are read while chunk i computes
-    constexpr bool A16 = AB == 2;
+    constexpr bool A16 = AROW == 256;
     Frag8 afb[2][A16 ? MT : 1][4];
     uint32_t sbb[2][SPW], zwb[2][SPW];
     auto lds_operands = [&](int i, auto slot) {
@@ -316,16 +332,24 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                         for (int mt = 0; mt < MT; ++mt) acc2[i & 1][sp][mt] += sc * (gacc[0][mt] + gacc[1][mt]);
                     }
                 }
-            } else if constexpr (F == Fmt::W4A8_MX) {
+            } else if constexpr (MX) {
                 v8i af[MT];
+                int asc[MT];
+                constexpr int CBSZ = F == Fmt::W4A4_MX ? 4 : 0;  // A operand: fp8 e4m3 or fp4 e2m1
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const int row = arow_l[mt];
                     const char* ar = lA + (size_t)row * U * 16;
-                    const int sw = skinny_swz<8>(row);
-                    const v4u lo = *(const v4u*)(ar + (((cl * 8 + quad) ^ sw) * 16));
-                    const v4u hi = *(const v4u*)(ar + (((cl * 8 + 4 + quad) ^ sw) * 16));
-                    af[mt] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    const int sw = skinny_swz<UPC>(row);
+                    const v4u lo = *(const v4u*)(ar + (((cl * UPC + quad) ^ sw) * 16));
+                    if constexpr (F == Fmt::W4A4_MX) {
+                        af[mt] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+                    } else {
+                        const v4u hi = *(const v4u*)(ar + (((cl * 8 + 4 + quad) ^ sw) * 16));
+                        af[mt] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    }
+                    // lane (row, quad) supplies the scale of its row's K block `quad` of the chunk
+                    asc[mt] = MXA ? (int)((const uint8_t*)(lds + p.z_off))[(row * nsl + cl) * 4 + quad] : 0x7F;
                 }
 #pragma unroll
                 for (int sp = 0; sp < SPW; ++sp) {
@@ -335,7 +359,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     const v8i b = v8i{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3], 0, 0, 0, 0};
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        acc2[i & 1][sp][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], b, acc2[i & 1][sp][mt], 0, 4, 0, 0x7F, 0, bsc);
+                        acc2[i & 1][sp][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], b, acc2[i & 1][sp][mt], CBSZ, 4, 0, asc[mt], 0, bsc);
                 }
             } else {  // W8A8_I8
 #pragma unroll
@@ -454,20 +478,36 @@ inline int skinny_round_cpw(int64_t per, int spw) {
     return per <= 2 ? 2 : per <= 4 ? 4 : 8;
 }
 
-// Bytes of LDS a slice of `cmax` chunks needs for `rows` A rows and NS strips.
-inline int64_t skinny_lds_need(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) {
-    const int ab = F == Fmt::W4A8_MX || F == Fmt::W8A8_I8 ? 1 : 2;
+// LDS layout of one slice of `cmax` chunks for `rows` A rows and NS strips:
+// the A rows, then the weight scales (16-bit group scales, or E8M0 bytes),
+// then the zero-point words (WNA16) or the activations' E8M0 words (MX
+// activations); each region 1 KB aligned.
+struct SkinnyLds {
+    int64_t a_off, s_off, z_off, bytes;
+};
+inline int skinny_arow(Fmt F) {
+    return F == Fmt::W4A4_MX ? 64 : (F == Fmt::W4A8_MX || F == Fmt::W4A8_MXA || F == Fmt::W8A8_I8) ? 128 : 256;
+}
+inline SkinnyLds skinny_lds(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) {
     auto al = [](int64_t b) { return (b + 1023) / 1024 * 1024; };
-    const int64_t a = al(rows * cmax * 128 * ab);
     int64_t s = 0, z = 0;
     if (F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16) {
         const int64_t gmax = cmax / gch + 2;
         s = al(NS * gmax * 32);
         z = al(NS * gmax * 8);
-    } else if (F == Fmt::W4A8_MX) {
+    } else if (mx_mfma(F)) {
         s = al(NS * cmax * 64);
+        if (mx_act(F)) z = al(rows * cmax * 4);
     }
-    return a + s + z;
+    SkinnyLds L;
+    L.a_off = 0;
+    L.s_off = al(rows * cmax * skinny_arow(F));
+    L.z_off = L.s_off + s;
+    L.bytes = L.z_off + z;
+    return L;
+}
+inline int64_t skinny_lds_need(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) {
+    return skinny_lds(F, rows, cmax, NS, gch).bytes;
 }
 
 // Dense plan: strips per workgroup grow with M so the A slice is re-read about
@@ -480,7 +520,7 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G) {
     p.NS = M <= 8 ? 1 : M <= 16 ? 2 : M <= 32 ? 4 : 8;
     // W4A8 at M <= 32: two strips per workgroup keep 224 workgroups at N = 7168
     // and the whole 8-bit A slice in LDS, so no K split (and no finalize pass)
-    if (F == Fmt::W4A8_MX && M <= 32 && M * (K / 128) * 128 + 2 * (K / 128) * 64 <= kSkinnyLds) p.NS = M <= 8 ? 1 : 2;
+    if (mx_mfma(F) && M <= 32 && skinny_lds_need(F, M, K / 128, 2, 1) <= kSkinnyLds) p.NS = M <= 8 ? 1 : 2;
     while (p.NS > 1 && p.NS > nstrips) p.NS /= 2;
     p.SPW = p.NS <= 4 ? 1 : p.NS / 4;
     p.WS = p.NS / p.SPW;
@@ -499,60 +539,16 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G) {
     p.splits = (int)cdiv(nc, p.cps);  // no empty slice
     p.cpk = (int)cdiv(p.cps, WK);
     const int64_t cmax = p.cps;
-    const int ab = F == Fmt::W4A8_MX || F == Fmt::W8A8_I8 ? 1 : 2;
-    auto al = [](int64_t b) { return (b + 1023) / 1024 * 1024; };
-    p.a_off = 0;
-    p.s_off = (int)al(M * cmax * 128 * ab);
-    p.z_off = p.s_off + (int)al(p.NS * (cmax / gch + 2) * 32);
+    const SkinnyLds L = skinny_lds(F, M, cmax, p.NS, gch);
+    p.a_off = (int)L.a_off;
+    p.s_off = (int)L.s_off;
+    p.z_off = (int)L.z_off;
     p.MT = M <= 16 ? 1 : M <= 32 ? 2 : 4;
     p.CPW = skinny_round_cpw(p.cpk, p.SPW);
-    const int64_t need = skinny_lds_need(F, M, cmax, p.NS, gch);
+    const int64_t need = L.bytes;
     const int64_t red = (int64_t)(WK - 1) * p.WS * p.SPW * p.MT * 1024;  // K-part reduction buffer
     p.lds_bytes = (int)(need > red ? need : red);
     return p;
-}
-
-// Split-K finalize: D = epilogue(sum over slices, in slice order); one thread
-// per pair of output columns of one row.
-template <Fmt F>
-__global__ __launch_bounds__(256) void skinny_finalize_kernel(SkinnyArgs p) {
-    const int m = blockIdx.y;
-    const int n = (blockIdx.x * 256 + threadIdx.x) * 2;
-    if (n >= p.N) return;
-    const int64_t stride = (int64_t)p.M * p.Np;
-    const int64_t base = (int64_t)m * p.Np + n;
-    const int64_t o = (int64_t)m * p.N + n;
-    const bool two = n + 1 < p.N;
-    if constexpr (F == Fmt::W8A8_I8) {
-        int v0 = 0, v1 = 0;
-        for (int s = 0; s < p.splits; ++s) {
-            const int2 v = *(const int2*)((const int*)p.part + base + s * stride);
-            v0 += v.x;
-            v1 += v.y;
-        }
-        if (p.raw_i32) {
-            ((int*)p.D)[o] = v0;
-            if (two) ((int*)p.D)[o + 1] = v1;
-        } else {
-            const float as = p.a_scale[m];
-            ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)v0 * as * ((const float*)p.S)[n]);
-            if (two) ((uint16_t*)p.D)[o + 1] = f32_to_bf16_bits((float)v1 * as * ((const float*)p.S)[n + 1]);
-        }
-    } else {
-        float v0 = 0.f, v1 = 0.f;
-        for (int s = 0; s < p.splits; ++s) {
-            const float2 v = *(const float2*)((const float*)p.part + base + s * stride);
-            v0 += v.x;
-            v1 += v.y;
-        }
-        if constexpr (F == Fmt::W4A8_MX) {
-            v0 *= p.a_scale[m];
-            v1 *= p.a_scale[m];
-        }
-        constexpr bool BF = F != Fmt::WNA16_F16;
-        ((uint16_t*)p.D)[o] = f32_to_16<BF>(v0);
-        if (two) ((uint16_t*)p.D)[o + 1] = f32_to_16<BF>(v1);
-    }
 }
 
 template <Fmt F, int MT, int SPW, int CPW>
@@ -605,13 +601,7 @@ hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t s
     else if (pl.MT == 2) e = launch_skinny_cpw<F, 2, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
     else e = launch_skinny_cpw<F, 4, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
     if (e != hipSuccess || pl.splits == 1) return e;
-    const dim3 fgrid((unsigned)cdiv(cdiv(s.N, 2), 256), (unsigned)s.M);
-    if (plan_recorder()) {
-        plan_record("skinny_finalize_kernel<%s>", fmt_name(F));
-        return hipSuccess;
-    }
-    hipLaunchKernelGGL((skinny_finalize_kernel<F>), fgrid, dim3(256), 0, st, s);
-    return hipGetLastError();
+    return launch_finalize<F>(FinalizeArgs{s.part, s.D, s.a_scale, (const float*)s.S, s.M, s.N, s.Np, s.splits, s.raw_i32}, st);
 }
 
 

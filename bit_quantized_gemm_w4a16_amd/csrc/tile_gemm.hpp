@@ -29,6 +29,11 @@
 //               row-sum MFMA, group scale applied to the fp32 accumulator
 //   W4A8_MX     fp8-e4m3 A x e2m1 B on the scaled MFMA (E8M0 B scale per
 //               32 K), per-token scale in the epilogue
+//   W4A8_MXA    fp8-e4m3 A with its own E8M0 scale per 32 K (MXFP8) x e2m1 B,
+//               both scales fed to the scaled MFMA (lane l's A scale applies
+//               to row l & 15 and K block l >> 4 of the instruction)
+//   W4A4_MX     fp4-e2m1 A with E8M0 per 32 K (MXFP4) x e2m1 B on the same
+//               scaled MFMA (A lane l holds row l & 15, K = 32 (l >> 4) + i)
 //   W8A8_I8     int8 x int8 -> int32 (exact), per-token x per-channel epilogue
 //   MOE_MX      bf16 A x e2m1 B converted to bf16 with the E8M0 scale (exact)
 #pragma once
@@ -40,24 +45,33 @@
 
 namespace hq {
 
-enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX };
+enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX };
 
 constexpr const char* fmt_name(Fmt F) {
     return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
-         : F == Fmt::W8A8_I8 ? "W8A8_I8" : "MOE_MX";
+         : F == Fmt::W8A8_I8 ? "W8A8_I8" : F == Fmt::MOE_MX ? "MOE_MX" : F == Fmt::W4A8_MXA ? "W4A8_MXA" : "W4A4_MX";
 }
+// Formats whose activations carry OCP MX scales (E8M0 per 32 K, [rows][K/32]).
+constexpr bool mx_act(Fmt F) { return F == Fmt::W4A8_MXA || F == Fmt::W4A4_MX; }
+// fp8 x fp4 or fp4 x fp4 on the scaled MFMA (B always e2m1 + E8M0).
+constexpr bool mx_mfma(Fmt F) { return F == Fmt::W4A8_MX || mx_act(F); }
 
+// AROW: bytes of one activation row per 128-K step; BSTRIP: packed weight
+// bytes per 16-column strip and step.
 template <Fmt F> struct FmtTraits;
-template <> struct FmtTraits<Fmt::WNA16_F16> { static constexpr int AB = 2, BSTRIP = 1024; using Acc = v4f; };
-template <> struct FmtTraits<Fmt::WNA16_BF16> { static constexpr int AB = 2, BSTRIP = 1024; using Acc = v4f; };
-template <> struct FmtTraits<Fmt::W4A8_MX> { static constexpr int AB = 1, BSTRIP = 1024; using Acc = v4f; };
-template <> struct FmtTraits<Fmt::W8A8_I8> { static constexpr int AB = 1, BSTRIP = 2048; using Acc = v4i; };
-template <> struct FmtTraits<Fmt::MOE_MX> { static constexpr int AB = 2, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::WNA16_F16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::WNA16_BF16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::W4A8_MX> { static constexpr int AROW = 128, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::W8A8_I8> { static constexpr int AROW = 128, BSTRIP = 2048; using Acc = v4i; };
+template <> struct FmtTraits<Fmt::MOE_MX> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::W4A8_MXA> { static constexpr int AROW = 128, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::W4A4_MX> { static constexpr int AROW = 64, BSTRIP = 1024; using Acc = v4f; };
 
 // Work description of one launch.  Dense launches leave the MoE fields null.
 struct TileArgs {
     const void* A;          // activations, row-major [rows][K]
     const float* a_scale;   // per-token fp32 (W4A8 / W8A8), indexed by A row
+    const uint8_t* a_e8;    // MX activation scales, E8M0 [rows][K/32] (W4A8_MXA / W4A4_MX)
     const void* W;          // packed weights (expert 0)
     const void* S;          // packed scales (expert 0)
     const void* Z;          // packed zero-points (WNA16 + UINT4)
@@ -76,9 +90,11 @@ struct TileArgs {
     int top_k;
 };
 
-// A-tile swizzle: the 16-byte unit u of row r is stored at u ^ swz(r).
+// A-tile swizzle: the 16-byte unit u of row r is stored at u ^ swz(r).  Rows
+// of 4 units (fp4 A, 64 bytes) need none: a wave's fragment read covers 1 KB
+// of consecutive bytes.
 __device__ __forceinline__ int swz(int row, int units) {
-    return units == 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((row >> 1) & 7);
+    return units == 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : units == 8 ? ((row >> 1) & 7) : 0;
 }
 
 // v_and_or_b32 with every operand in a VGPR (a gfx9 VOP3 instruction takes no
@@ -177,18 +193,20 @@ void tile_gemm_kernel(TileArgs p) {
     using T = FmtTraits<F>;
     using Acc = typename T::Acc;
     constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
-    constexpr bool MX = F == Fmt::W4A8_MX || F == Fmt::MOE_MX;
+    constexpr bool MX = mx_mfma(F) || F == Fmt::MOE_MX;  // E8M0 weight scales per 32 K
+    constexpr bool MXA = mx_act(F);
     constexpr int NTH = 64 * WM * WN;
-    constexpr int AB = T::AB, BK = 128;
-    constexpr int AROW = BK * AB, AUNITS = AROW / 16;
+    constexpr int BK = 128;
+    constexpr int AROW = T::AROW, AUNITS = AROW / 16;
     constexpr int A_STAGE = BM * AROW;
     constexpr int NSTRIP = BN / 16;
     constexpr int B_STAGE = NSTRIP * T::BSTRIP;
     // per-step scale block: WNA16 16 fp16 scales + one zero-point word per strip;
     // MXFP4 one E8M0 byte per lane per strip; INT8 none (per-channel, epilogue)
     constexpr int SC_Z = NSTRIP * 32;                     // zero-point words start (WNA16)
-    constexpr int SC_STAGE = WNA16 ? NSTRIP * 48 : MX ? NSTRIP * 64 : 0;
-    constexpr int SC_UNITS = SC_STAGE / 16;
+    constexpr int SC_B = WNA16 ? NSTRIP * 48 : MX ? NSTRIP * 64 : 0;
+    constexpr int SC_STAGE = SC_B + (MXA ? BM * 4 : 0);   // MX activations: one E8M0 word (4 K blocks) per row
+    constexpr int SC_UNITS = SC_B / 16;
     // a stage holds the A and weight tiles of one step; the step's scale block
     // sits in an LDS array of its own (it is loaded through registers, and its
     // reads take immediate offsets)
@@ -273,7 +291,9 @@ void tile_gemm_kernel(TileArgs p) {
 
     // buffer resources (base + size; wave-uniform K-step offsets go in SGPRs)
     const uint32_t nstr = (uint32_t)(p.Np / 16);
-    const rsrc_t rA = make_rsrc(p.A, (uint32_t)p.a_rows * (uint32_t)K * AB);
+    const uint32_t arow_bytes = (uint32_t)(K / BK) * AROW;  // bytes of one A row
+    const rsrc_t rA = make_rsrc(p.A, (uint32_t)p.a_rows * arow_bytes);
+    const rsrc_t rAS = make_rsrc(p.a_e8, MXA ? (uint32_t)p.a_rows * (uint32_t)(K / 32) : 0u);
     const rsrc_t rW = make_rsrc(Wbase, nstr * (uint32_t)nsteps * T::BSTRIP);
     const rsrc_t rS = make_rsrc(Sbase, WNA16 ? nstr * (uint32_t)p.ngroups * 32u : MX ? nstr * (uint32_t)nsteps * 64u : 0u);
     const rsrc_t rZ = make_rsrc(p.Z, WNA16 && p.Z ? nstr * (uint32_t)p.ngroups * 8u : 0u);
@@ -284,14 +304,14 @@ void tile_gemm_kernel(TileArgs p) {
     // rows past M fall outside the buffer resource and read zeros (their
     // outputs are dropped).  MoE rows are gathered: one offset per load.
     constexpr bool AFLAT = F != Fmt::MOE_MX && (NTH / AUNITS) % 16 == 0;
-    const uint32_t arow_stride = (uint32_t)(NTH / AUNITS) * (uint32_t)(K * AB);
+    const uint32_t arow_stride = (uint32_t)(NTH / AUNITS) * arow_bytes;
     uint32_t aoff[AFLAT ? 1 : NIA];
 #pragma unroll
     for (int i = 0; i < (AFLAT ? 1 : NIA); ++i) {
         const int s = i * NTH + tid;
         const int row = s / AUNITS, pos = s % AUNITS;
         const int unit = pos ^ swz(row, AUNITS);
-        aoff[i] = (AFLAT ? (uint32_t)(m0 + row) : (uint32_t)rowinfo[row]) * (uint32_t)(K * AB) + unit * 16;
+        aoff[i] = (AFLAT ? (uint32_t)(m0 + row) : (uint32_t)rowinfo[row]) * arow_bytes + unit * 16;
     }
     auto a_voff = [&](int i) -> uint32_t { return AFLAT ? aoff[0] : aoff[i]; };
     auto a_soff = [&](int i, int ks) -> uint32_t { return (AFLAT ? (uint32_t)i * arow_stride : 0u) + (uint32_t)ks * AROW; };
@@ -331,6 +351,8 @@ void tile_gemm_kernel(TileArgs p) {
     constexpr bool RSTAGE = PD == 1 || PD == 2;  // A and B staged through registers
     constexpr int NSET = RSTAGE ? PD : PD == 4 ? NST : 1;  // register sets (the ring: one scale block per stage)
     v4u ra[NSET][RSTAGE ? NIA : 1], rb[NSET][RSTAGE ? NIB : 1], rs[NSET];
+    uint32_t rsa[NSET];  // MX activations: this thread's row's E8M0 word of the step (threads < BM)
+    const uint32_t as_voff = (uint32_t)(m0 + (tid < BM ? tid : 0)) * (uint32_t)(K / 32);
     // Direct loads of one step's A and weight tiles into a stage (NIA + NIB
     // unconditional loads per thread).  The scale block goes through registers
     // (sc_load, then sc_write into its own LDS array once landed): the compiler
@@ -373,6 +395,9 @@ void tile_gemm_kernel(TileArgs p) {
             }
         } else if constexpr (MX) {
             if (tid < SC_UNITS) rs[st] = buf16(rS, soff, (uint32_t)ks * 64u);
+            // rows past M fall outside the buffer resource and read zeros (outputs dropped)
+            if constexpr (MXA)
+                if (tid < BM) rsa[st] = buf4(rAS, as_voff, (uint32_t)ks * 4u);
         }
     };
     auto sc_write = [&](auto stc, auto setc) {
@@ -385,6 +410,8 @@ void tile_gemm_kernel(TileArgs p) {
                     *(uint64_t*)(sS + SC_Z + (tid - 2 * NSTRIP) * 8) = ((uint64_t)rs[st][1] << 32) | rs[st][0];
             } else {
                 if (tid < SC_UNITS) *(v4u*)(sS + tid * 16) = rs[st];
+                if constexpr (MXA)
+                    if (tid < BM) *(uint32_t*)(sS + SC_B + tid * 4) = rsa[st];
             }
         }
     };
@@ -580,23 +607,30 @@ void tile_gemm_kernel(TileArgs p) {
             for (int i = 0; i < MT; ++i)
 #pragma unroll
                 for (int j = 0; j < NT; ++j) acc[i][j] += sc[j] * (st[i][j] - zc[j] * rsum[i]);
-        } else if constexpr (F == Fmt::W4A8_MX) {
+        } else if constexpr (mx_mfma(F)) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) hook(t);
             int bsc[NT];
 #pragma unroll
             for (int j = 0; j < NT; ++j) bsc[j] = (int)((const uint8_t*)sS)[(wn * NT + j) * 64 + lane];
+            constexpr int CBSZ = F == Fmt::W4A4_MX ? 4 : 0;  // A operand format: fp8 e4m3 or fp4 e2m1
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 const int row = wm * (BM / WM) + i * 16 + col;
                 const int sw = swz(row, AUNITS);
                 const v4u lo = *(const v4u*)(sA + row * AROW + ((quad ^ sw) * 16));
-                const v4u hi = *(const v4u*)(sA + row * AROW + (((4 + quad) ^ sw) * 16));
-                const v8i a = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                v8i a;
+                if constexpr (F == Fmt::W4A4_MX) {
+                    a = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
+                } else {
+                    const v4u hi = *(const v4u*)(sA + row * AROW + (((4 + quad) ^ sw) * 16));
+                    a = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                }
+                const int asc = MXA ? (int)((const uint8_t*)(sS + SC_B))[row * 4 + quad] : 0x7F;
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     const v8i b = v8i{(int)bw[j][0][0], (int)bw[j][0][1], (int)bw[j][0][2], (int)bw[j][0][3], 0, 0, 0, 0};
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i][j], 0, 4, 0, 0x7F, 0, bsc[j]);
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i][j], CBSZ, 4, 0, asc, 0, bsc[j]);
                 }
             }
         } else if constexpr (F == Fmt::W8A8_I8) {
@@ -811,46 +845,62 @@ void tile_gemm_kernel(TileArgs p) {
         }
 }
 
-// Split-K finalize for the tiled kernel: sums the partial tiles in slice order
-// and applies the format's epilogue (dense formats only); one thread per pair
-// of output columns of one row.
+// Split-K finalize shared by the dense launchers: sums the fp32 / int32
+// partial tiles [splits][M][Np] in slice order and applies the format's
+// epilogue.  One thread per 4 columns of one row; the loads of up to 8 slices
+// are issued together (independent 16-byte loads), then added in order.
+struct FinalizeArgs {
+    const void* part;
+    void* D;
+    const float* a_scale;  // per-token scale (W4A8 / W8A8)
+    const float* s_w;      // per-channel scale (W8A8)
+    int M, N, Np, splits, raw_i32;
+};
+
 template <Fmt F>
-__global__ __launch_bounds__(256) void tile_finalize_kernel(TileArgs p) {
+__global__ __launch_bounds__(256) void splitk_finalize_kernel(FinalizeArgs p) {
     const int m = blockIdx.y;
-    const int n = (blockIdx.x * 256 + threadIdx.x) * 2;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (n >= p.N) return;
     const int64_t stride = (int64_t)p.M * p.Np, base = (int64_t)m * p.Np + n, o = (int64_t)m * p.N + n;
-    const bool two = n + 1 < p.N;
-    if constexpr (F == Fmt::W8A8_I8) {
-        int v0 = 0, v1 = 0;
-        for (int s = 0; s < p.splits; ++s) {
-            const int2 v = *(const int2*)((const int*)p.part + base + s * stride);
-            v0 += v.x;
-            v1 += v.y;
-        }
+    constexpr bool I32 = F == Fmt::W8A8_I8;
+    using V = typename std::conditional<I32, v4i, v4f>::type;
+    const V* src = (const V*)((const char*)p.part + base * 4);
+    const int64_t vstride = stride / 4;  // Np is a multiple of 16
+    V acc = src[0];
+    for (int s0 = 1; s0 < p.splits; s0 += 8) {
+        V v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (s0 + j < p.splits) v[j] = src[(s0 + j) * vstride];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (s0 + j < p.splits) acc += v[j];
+    }
+    const int cnt = p.N - n < 4 ? p.N - n : 4;
+    if constexpr (I32) {
         if (p.raw_i32) {
-            ((int*)p.D)[o] = v0;
-            if (two) ((int*)p.D)[o + 1] = v1;
+            for (int j = 0; j < cnt; ++j) ((int*)p.D)[o + j] = acc[j];
         } else {
             const float as = p.a_scale[m];
-            ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)v0 * as * ((const float*)p.S)[n]);
-            if (two) ((uint16_t*)p.D)[o + 1] = f32_to_bf16_bits((float)v1 * as * ((const float*)p.S)[n + 1]);
+            for (int j = 0; j < cnt; ++j) ((uint16_t*)p.D)[o + j] = f32_to_bf16_bits((float)acc[j] * as * p.s_w[n + j]);
         }
     } else {
-        float v0 = 0.f, v1 = 0.f;
-        for (int s = 0; s < p.splits; ++s) {
-            const float2 v = *(const float2*)((const float*)p.part + base + s * stride);
-            v0 += v.x;
-            v1 += v.y;
-        }
-        if constexpr (F == Fmt::W4A8_MX) {
-            v0 *= p.a_scale[m];
-            v1 *= p.a_scale[m];
-        }
+        if constexpr (F == Fmt::W4A8_MX) acc *= p.a_scale[m];
         constexpr bool BF = F != Fmt::WNA16_F16;
-        ((uint16_t*)p.D)[o] = f32_to_16<BF>(v0);
-        if (two) ((uint16_t*)p.D)[o + 1] = f32_to_16<BF>(v1);
+        for (int j = 0; j < cnt; ++j) ((uint16_t*)p.D)[o + j] = f32_to_16<BF>(acc[j]);
     }
+}
+
+template <Fmt F>
+hipError_t launch_finalize(const FinalizeArgs& f, hipStream_t st) {
+    if (plan_recorder()) {
+        plan_record("splitk_finalize_kernel<%s>", fmt_name(F));
+        return hipSuccess;
+    }
+    const dim3 grid((unsigned)((f.N + 1023) / 1024), (unsigned)f.M);
+    hipLaunchKernelGGL((splitk_finalize_kernel<F>), grid, dim3(256), 0, st, f);
+    return hipGetLastError();
 }
 
 }  // namespace hq
@@ -899,18 +949,14 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
     if (plan_recorder()) {
         plan_record("tile_gemm_kernel<%s,%d,%d,%d,%d,%d> grid=%lld splits=%d", fmt_name(F), BM, BN, WM, WN, PD,
                     (long long)grid, p.splits);
-        if (p.splits > 1) {
-            plan_record("tile_finalize_kernel<%s>", fmt_name(F));
-            plan_workspace((size_t)p.splits * (size_t)p.M * (size_t)p.Np * 4);
-        }
-        return hipSuccess;
+        if (p.splits > 1) plan_workspace((size_t)p.splits * (size_t)p.M * (size_t)p.Np * 4);
+    } else {
+        hipLaunchKernelGGL((tile_gemm_kernel<F, BM, BN, WM, WN, PD>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((tile_gemm_kernel<F, BM, BN, WM, WN, PD>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splits == 1) return e;
-    const dim3 fgrid((unsigned)((p.N + 511) / 512), (unsigned)p.M);
-    hipLaunchKernelGGL((tile_finalize_kernel<F>), fgrid, dim3(256), 0, st, p);
-    return hipGetLastError();
+    if (p.splits == 1) return hipSuccess;
+    return launch_finalize<F>(FinalizeArgs{p.part, p.D, p.a_scale, (const float*)p.S, p.M, p.N, p.Np, p.splits, p.raw_i32}, st);
 }
 
 // Formats with a 256-row tile.  4-bit weights with 16-bit A: 256 x 128 on 8
@@ -960,8 +1006,8 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
         }
         return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
     } else {
-        if constexpr (F == Fmt::W4A8_MX) {
-            // 8-bit A: a 256-column tile on a three-stage ring
+        if constexpr (mx_mfma(F)) {
+            // 8-bit A: a 256-column tile on a three-stage ring (4-bit A: four stages)
             if (pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 4>(p, st);
             // mid M: a 128 x 128 step is 8 MFMAs per wave, short next to the load
             // latency.  While the tiles fit one workgroup per CU, a four-stage ring

@@ -91,7 +91,8 @@ typedef enum hq_scale_gran {
 
 typedef enum hq_ascale {
     HQ_ASCALE_NONE = 0,
-    HQ_ASCALE_PER_TOKEN_F32 = 1 /* fp32 a_scale[M], applied in the epilogue */
+    HQ_ASCALE_PER_TOKEN_F32 = 1, /* fp32 a_scale[M], applied in the epilogue              */
+    HQ_ASCALE_MX_E8M0 = 2        /* OCP MX: uint8 E8M0 a_scale[M][K/32], 2^(e-127) per 32 K */
 } hq_ascale;
 
 typedef enum hq_scale2 {
@@ -114,7 +115,11 @@ typedef enum hq_moe_mode {
  *   BF16|FP16 UINT4      same as a_dtype, PER_GROUP_K  UINT4   NONE      a_dtype
  *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    PER_TOKEN BF16
  *   INT8      INT8       FP32, PER_CHANNEL             NONE    PER_TOKEN BF16|INT32
+ *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    MX_E8M0   BF16   (MXFP8 x MXFP4)
+ *   FP4_E2M1  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    MX_E8M0   BF16   (W4A4 MXFP4)
  *   BF16      FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MoE)
+ * FP4_E2M1 activations are packed two per byte along K, element k in the low
+ * nibble of byte k/2 when k is even (rows of K/2 bytes).
  * Group sizes for 16-bit scales: a multiple of 128 that divides K.
  * K: a multiple of 128 (every format).  N: any value >= 1.
  * out_dtype INT32 returns the raw INT8 x INT8 accumulators (bit-exact).
@@ -215,14 +220,15 @@ hq_status hq_workspace_init(void* workspace, size_t bytes, hq_stream_t stream);
 
 /*
  * Dense D[M,N] = A[M,K] x dequant(W).
- *   A        device, [M][K] row-major, a_dtype
- *   a_scale  device fp32 [M] when a_scale == PER_TOKEN_F32, else NULL
+ *   A        device, [M][K] row-major, a_dtype (E2M1: [M][K/2] bytes)
+ *   a_scale  device; PER_TOKEN_F32: fp32 [M]; MX_E8M0: uint8 [M][K/32]
+ *            (E8M0 of row m, K block b); NONE: NULL
  *   w, s, z, s2  device, packed by hq_repack (unused ones NULL)
  *   D        device, [M][N] row-major, out_dtype
  * Floating outputs: fp32 accumulation, rounded once (RNE) to out_dtype.
  * M == 0 returns HQ_OK without launching.
  */
-hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const float* a_scale,
+hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const void* a_scale,
                   const void* w, const void* s, const void* z, const void* s2, void* D,
                   void* workspace, size_t ws_bytes, hq_stream_t stream);
 
@@ -242,7 +248,7 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const flo
  * scratch byte they read within the call, so nothing needs clearing.
  */
 #define HQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
-hq_status hq_gemm_noalloc(const hq_layer_desc* desc, int64_t M, const void* A, const float* a_scale,
+hq_status hq_gemm_noalloc(const hq_layer_desc* desc, int64_t M, const void* A, const void* a_scale,
                           const void* w, const void* s, const void* z, const void* s2, void* D, hq_stream_t stream);
 
 /*
@@ -285,6 +291,23 @@ hq_status hq_moe_gemm(const hq_layer_desc* desc, int32_t mode, int64_t T, int32_
  */
 hq_status hq_quantize_act(int32_t out_dtype, int64_t M, int64_t K, const float* x, void* q, float* s,
                           hq_stream_t stream);
+
+/*
+ * MX activation quantisation ("Humming wird angekuendigt", sections
+ * "W8A8 / W4A8 / W4A4" and "Auswahl von Aktivierungstypen": W4A4 on MXFP4
+ * and MXFP8 activations), OCP Microscaling Formats v1.0, section 6.3:
+ * for each row m of x (fp32 [M][K], K a multiple of 32) and block b of 32 along K:
+ *   e[m][b] = clamp(floor(log2(max|x|)) - emax, ...) as E8M0 (emax: E4M3 8,
+ *             E2M1 2), i.e. the exponent field of max|x| minus emax, clamped
+ *             to 0..254; 0 for an all-zero block; 0xFF (NaN) for a block
+ *             holding a NaN or an infinity (its codes are then 0)
+ *   q = x * 2^(127 - e) rounded to nearest even, saturated (E4M3 +-448,
+ *       E2M1 +-6); E4M3 codes one per byte [M][K]; E2M1 codes two per byte
+ *       [M][K/2], element k in the low nibble of byte k/2 when k is even.
+ * out_dtype HQ_DT_FP8_E4M3 or HQ_DT_FP4_E2M1; pointers 16-byte aligned.
+ */
+hq_status hq_quantize_act_mx(int32_t out_dtype, int64_t M, int64_t K, const float* x, void* q, void* e,
+                             hq_stream_t stream);
 
 /*
  * SwiGLU between the MoE gate-up and down projections ("Humming wird

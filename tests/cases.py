@@ -52,6 +52,13 @@ W8A8_RING = [(200, 20000, 384), (1024, 18432, 256), (256, 18432, 640)]
 W8A8_C4_SWEEP = [(M, C4["N"], C4["K"]) for M in SWEEP]
 
 
+# ---- MX activations x MXFP4 weights: (M, N, K), for E2M1 (W4A4) and E4M3 (MXFP8) activations ----
+MXA_SMALL = [(M, 272, 512) for M in (1, 3, 16, 24, 32, 64, 100, 257)]
+MXA_MID = [(1024, 7168, 256), (1000, 7000, 384)]
+MXA_BIG = [(1100, 7200, 128), (1100, 7168, 640)]
+MXA_SWEEP = [(M, C3["N"], C3["K"]) for M in SWEEP]
+
+
 def all_dense_cases():
     """(format, M, N, K, G, flags) for every dense GPU case, flags a dict."""
     out = []
@@ -64,4 +71,7 @@ def all_dense_cases():
         out.append(("w8a8", M, N, K, K, dict(raw=True)))
     for M, N, K in W8A8_SMALL_BF16 + W8A8_C4_SWEEP:
         out.append(("w8a8", M, N, K, K, dict(raw=False)))
+    for elem in ("e2m1", "e4m3"):
+        for M, N, K in MXA_SMALL + MXA_MID + MXA_BIG + MXA_SWEEP:
+            out.append(("mxa", M, N, K, 32, dict(elem=elem)))
     return out

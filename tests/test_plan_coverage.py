@@ -20,6 +20,8 @@ def desc_of(fmt, N, K, G, flags):
         return hq.desc_w4a16(N, K, G, bf16=flags["bf16"], zp=flags["zp"])
     if fmt == "w4a8":
         return hq.desc_w4a8_mxfp4(N, K)
+    if fmt == "mxa":
+        return hq.desc_mx_act_mxfp4(N, K, fp4_act=flags["elem"] == "e2m1")
     return hq.desc_w8a8(N, K, raw_int32=flags["raw"])
 
 
@@ -46,6 +48,8 @@ BENCH = {
     "c3": ("w4a8", cases.C3["N"], cases.C3["K"], 32, {}),
     "c4": ("w8a8", cases.C4["N"], cases.C4["K"], cases.C4["K"], dict(raw=False)),
     "c4raw": ("w8a8", cases.C4["N"], cases.C4["K"], cases.C4["K"], dict(raw=True)),
+    "w4a4": ("mxa", cases.C3["N"], cases.C3["K"], 32, dict(elem="e2m1")),
+    "w4a8mx": ("mxa", cases.C3["N"], cases.C3["K"], 32, dict(elem="e4m3")),
 }
 
 
