@@ -67,6 +67,10 @@ def lib():
         L.hq_oracle_quant_act_mx.argtypes = [i64, i64, C.c_int, p, p, p]
         L.hq_oracle_gemm_mx_mxfp4.restype = C.c_int
         L.hq_oracle_gemm_mx_mxfp4.argtypes = [i64, i64, i64, C.c_int, p, p, p, p, p, i64, p]
+        L.hq_oracle_quant_act_e4m3_blocks.restype = C.c_int
+        L.hq_oracle_quant_act_e4m3_blocks.argtypes = [i64, i64, i64, p, p, p]
+        L.hq_oracle_gemm_fp8_blockwise.restype = C.c_int
+        L.hq_oracle_gemm_fp8_blockwise.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
         L.hq_oracle_gemm_w8a8.restype = C.c_int
         L.hq_oracle_gemm_w8a8.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p, p]
         L.hq_oracle_moe_route.restype = C.c_int
@@ -135,6 +139,18 @@ def quant_act_e4m3(x: np.ndarray):
     return q, s
 
 
+def quant_act_e4m3_blocks(x: np.ndarray, block: int):
+    """E4M3 activations with one fp32 scale per (row, block of `block` along K):
+    returns (codes uint8 [M,K], scales fp32 [M,K/block]); block == K is tokenwise."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // block), dtype=np.float32)
+    if lib().hq_oracle_quant_act_e4m3_blocks(M, K, block, _ptr(x), _ptr(q), _ptr(s)):
+        raise ValueError("K must be a multiple of the block")
+    return q, s
+
+
 def e2m1_encode(x: float) -> int:
     """E2M1 code of x: nearest, ties to even, saturating at +-6 (sign kept)."""
     return int(lib().hq_oracle_e2m1_encode(float(x)))
@@ -191,6 +207,21 @@ def gemm_mx_mxfp4(qa, ea, q, e, *, N, K, a_elem: str, rows=None):
                                        _ptr(_c(q, np.uint32)), _ptr(_c(e, np.uint8)), _ptr(r), R, _ptr(out))
     if rc:
         raise ValueError(f"oracle gemm_mx_mxfp4 failed ({rc})")
+    return out
+
+
+def gemm_fp8_blockwise(qa, sa, w, sw, *, rows=None):
+    """FP8 W8A8 with blockwise scales (1 x 128 activation blocks, 128 x 128 weight blocks), fp64."""
+    qa = _c(qa, np.uint8)
+    w = _c(w, np.uint8)
+    M, K = qa.shape
+    N = w.shape[1]
+    r, R = _rows(rows, M)
+    out = np.empty((R, N), dtype=np.float64)
+    rc = lib().hq_oracle_gemm_fp8_blockwise(M, N, K, _ptr(qa), _ptr(_c(sa, np.float32)), _ptr(w),
+                                            _ptr(_c(sw, np.float32)), _ptr(r), R, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle gemm_fp8_blockwise failed ({rc})")
     return out
 
 

@@ -140,6 +140,29 @@ void hq_oracle_quant_act_e4m3(int64_t M, int64_t K, const float* x, uint8_t* q, 
     }
 }
 
+/* Per row m and block b of B consecutive elements along K (K % B == 0):
+ * s[m][b] = max |x| over the block / 448 in fp32 (1 for an all-zero block),
+ * q = E4M3_RNE_satfinite(x / s) with the division in fp32.  B == K is the
+ * tokenwise case above; B == 128 is the 1 x 128 activation blocks of FP8
+ * W8A8 with blockwise scales. */
+int hq_oracle_quant_act_e4m3_blocks(int64_t M, int64_t K, int64_t B, const float* x, uint8_t* q, float* s)
+{
+    if (B <= 0 || K % B) return 1;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < K / B; ++b) {
+            const float* xb = x + m * K + b * B;
+            float amax = 0.0f;
+            for (int64_t k = 0; k < B; ++k) {
+                float a = fabsf(xb[k]);
+                if (a > amax) amax = a;
+            }
+            float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+            s[m * (K / B) + b] = sc;
+            for (int64_t k = 0; k < B; ++k) q[m * K + b * B + k] = (uint8_t)hq_oracle_e4m3_encode(xb[k] / sc);
+        }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* MX activation quantisation (OCP MX v1.0: one E8M0 scale per 32)      */
 /* ------------------------------------------------------------------ */
@@ -303,6 +326,32 @@ int hq_oracle_gemm_mx_mxfp4(int64_t M, int64_t N, int64_t K, int a_elem, const u
         for (int64_t k = 0; k < K; ++k) {
             double w = hq_oracle_e2m1(nib_along_k(q, N, k, n)) * hq_oracle_e8m0(e8[(k / 32) * N + n]);
             for (int64_t r = 0; r < R; ++r) out[r * N + n] += a[r * K + k] * w;
+        }
+    free(a);
+    return 0;
+}
+
+/* FP8 W8A8 with blockwise scales: A_real[m][k] = e4m3(qa[m][k]) * sa[m][k/128],
+ * W_real[k][n] = e4m3(w[k][n]) * sw[k/128][n/128], D = A_real x W_real.
+ * qa uint8 [M][K], sa fp32 [M][K/128], w uint8 [K][N], sw fp32 [K/128][ceil(N/128)]. */
+int hq_oracle_gemm_fp8_blockwise(int64_t M, int64_t N, int64_t K, const uint8_t* qa, const float* sa,
+                                 const uint8_t* w, const float* sw, const int64_t* rows, int64_t nrows,
+                                 double* out)
+{
+    if (K % 128) return 1;
+    int64_t R = rows ? nrows : M, nbn = (N + 127) / 128;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(R * K + 1));
+    if (!a) return 2;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t m = row_of(rows, r);
+        for (int64_t k = 0; k < K; ++k) a[r * K + k] = hq_oracle_e4m3(qa[m * K + k]) * (double)sa[m * (K / 128) + k / 128];
+    }
+    memset(out, 0, sizeof(double) * (size_t)(R * N));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            double wv = hq_oracle_e4m3(w[k * N + n]) * (double)sw[(k / 128) * nbn + n / 128];
+            for (int64_t r = 0; r < R; ++r) out[r * N + n] += a[r * K + k] * wv;
         }
     free(a);
     return 0;

@@ -168,6 +168,27 @@ def w8a8_int8(seed, M, N, K, cfg=C4):
     )
 
 
+C6 = 6  # FP8 W8A8 with blockwise scales
+
+
+def fp8_codes(seed, cfg, tensor, shape) -> np.ndarray:
+    """E4M3 codes drawn uniformly over the finite codes (0x7F / 0xFF, the NaNs, excluded)."""
+    c = _rng(seed, cfg, tensor).integers(0, 254, size=shape, dtype=np.int64)
+    c = c + (c >= 0x7F) # skip 0x7F
+    return c.astype(np.uint8)
+
+
+def w8a8_fp8_blockwise(seed, M, N, K, cfg=C6):
+    """FP8 W8A8 with blockwise scales: fp32 activations (quantised per 1 x 128 block
+    by the consumer), E4M3 weight codes [K, N] uniform over the finite codes, fp32
+    weight scales |N(0, 0.01)| + 1e-4 per 128 x 128 block [K/128, ceil(N/128)]."""
+    return dict(
+        A0=normal_rows(seed, cfg, T_A, M, K),
+        w=fp8_codes(seed, cfg, T_Q, (K, N)),
+        s_w=abs_normal_scales(seed, cfg, T_SW, (K // 128, (N + 127) // 128), 0.01, 1e-4, torch.float32),
+    )
+
+
 def moe_expert_mxfp4(seed, e, N, K, cfg=C5):
     """One expert's MXFP4 weights (codes + E8M0), drawn from the expert's own stream."""
     return (random_words(seed, cfg, T_Q, (K // 8, N), e),

@@ -561,3 +561,62 @@ def test_gemm_mx_block_scale_step_and_sign_flip(elem):
     w = e2m1_tab(unpack_k(d["q"], K)) * (2.0 ** (np.repeat(d["e"].astype(np.int64), 32, axis=0) - 127))
     contrib = a[1, 160:192] @ w[160:192]
     assert rel_err(moved[1] - base[1], contrib) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# FP8 W8A8 with blockwise scales (1 x 128 activation blocks, 128 x 128 weight blocks)
+# ---------------------------------------------------------------------------
+
+E4M3_LUT = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_quant_act_e4m3_blocks_reduces_to_tokenwise_and_per_block():
+    x = syn.normal_rows(3, 10, syn.T_A, 9, 512)
+    x[2, 128:256] = 0.0
+    q1, s1 = oracle.quant_act_e4m3_blocks(x, 512)
+    qt, st = oracle.quant_act_e4m3(x)
+    np.testing.assert_array_equal(q1, qt)
+    np.testing.assert_array_equal(s1[:, 0], st)
+    q, s = oracle.quant_act_e4m3_blocks(x, 128)
+    for b in range(4):                                    # each block is its own tokenwise problem
+        qb, sb = oracle.quant_act_e4m3(x[:, 128 * b:128 * b + 128])
+        np.testing.assert_array_equal(q[:, 128 * b:128 * b + 128], qb)
+        np.testing.assert_array_equal(s[:, b], sb)
+    assert s[2, 1] == 1.0 and not q[2, 128:256].any()
+
+
+def test_gemm_fp8_blockwise_matches_decoded_matmul_and_exact_rational():
+    M, N, K = 5, 200, 384
+    d = syn.w8a8_fp8_blockwise(1, M, N, K)
+    qa, sa = oracle.quant_act_e4m3_blocks(d["A0"], 128)
+    got = oracle.gemm_fp8_blockwise(qa, sa, d["w"], d["s_w"])
+    a = E4M3_LUT[qa] * np.repeat(sa.astype(np.float64), 128, axis=1)
+    w = E4M3_LUT[d["w"]] * np.repeat(np.repeat(d["s_w"].astype(np.float64), 128, axis=0), 128, axis=1)[:, :N]
+    assert rel_err(got, a @ w) < 1e-13
+    for m, n in [(0, 0), (4, 199), (2, 128), (3, 127)]:
+        acc = Fraction(0)
+        for k in range(K):
+            acc += (Fraction(float(E4M3_LUT[qa[m, k]])) * Fraction(float(sa[m, k // 128]))
+                    * Fraction(float(E4M3_LUT[d["w"][k, n]])) * Fraction(float(d["s_w"][k // 128, n // 128])))
+        assert abs(got[m, n] - float(acc)) <= 1e-13 * max(abs(float(acc)), 1e-30)
+
+
+def test_gemm_fp8_blockwise_scale_indexing():
+    """Doubling one activation block scale doubles exactly that row's K block; doubling
+    one weight block scale doubles exactly that K block of those 128 columns."""
+    M, N, K = 3, 256, 384
+    d = syn.w8a8_fp8_blockwise(2, M, N, K)
+    qa, sa = oracle.quant_act_e4m3_blocks(d["A0"], 128)
+    base = oracle.gemm_fp8_blockwise(qa, sa, d["w"], d["s_w"])
+    a = E4M3_LUT[qa] * np.repeat(sa.astype(np.float64), 128, axis=1)
+    w = E4M3_LUT[d["w"]] * np.repeat(np.repeat(d["s_w"].astype(np.float64), 128, axis=0), 128, axis=1)[:, :N]
+    sa2 = sa.copy()
+    sa2[1, 2] *= 2
+    got = oracle.gemm_fp8_blockwise(qa, sa2, d["w"], d["s_w"])
+    assert np.array_equal(got[[0, 2]], base[[0, 2]])
+    assert rel_err(got[1] - base[1], a[1, 256:384] @ w[256:384]) < 1e-12
+    sw2 = d["s_w"].copy()
+    sw2[0, 1] *= 2
+    got = oracle.gemm_fp8_blockwise(qa, sa, d["w"], sw2)
+    assert np.array_equal(got[:, :128], base[:, :128])
+    assert rel_err(got[:, 128:] - base[:, 128:], a[:, :128] @ w[:128, 128:]) < 1e-12
