@@ -118,6 +118,17 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 takes no zero-points");
         if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 paths output bf16");
         I.G = 32;
+    } else if (a == HQ_DT_FP8_E4M3 && w == HQ_DT_FP8_E4M3) {
+        I.kind = Kind::FP8_BLOCK;
+        if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "blockwise FP8 is built for dense layers");
+        if (d->a_scale != HQ_ASCALE_PER_BLOCK128_F32)
+            return set_error(HQ_ERR_UNSUPPORTED, "FP8 W8A8 needs fp32 activation scales per 128-K block");
+        if (d->w_scale_dtype != HQ_DT_FP32 || d->w_scale_gran != HQ_GRAN_BLOCK_128x128)
+            return set_error(HQ_ERR_UNSUPPORTED, "FP8 W8A8 needs fp32 weight scales per 128 x 128 block");
+        if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "FP8 W8A8 takes no zero-points");
+        if (d->K % 128) return set_error(HQ_ERR_UNSUPPORTED, "FP8 W8A8 needs K %% 128 == 0 (K=%lld)", (long long)d->K);
+        if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "FP8 W8A8 outputs bf16");
+        I.G = 128;
     } else if (a == HQ_DT_INT8 && w == HQ_DT_INT8) {
         I.kind = Kind::W8A8;
         if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "W8A8 is dense-only");
@@ -158,6 +169,7 @@ static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
         case Kind::W4A8_MX: return hip_status(w4a8_launch(a), "hq_gemm(W4A8-MXFP4)");
         case Kind::W8A8: return hip_status(w8a8_launch(a, L.out_i32), "hq_gemm(W8A8)");
         case Kind::MXA_MX: return hip_status(mx_act_launch(a, L.a_fp4), L.a_fp4 ? "hq_gemm(W4A4-MXFP4)" : "hq_gemm(W4A8-MXFP8xMXFP4)");
+        case Kind::FP8_BLOCK: return hip_status(fp8_block_launch(a), "hq_gemm(FP8-blockwise)");
         default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind runs through hq_moe_gemm");
     }
 }
@@ -172,7 +184,12 @@ static hq_status dense_plan(const LayerInfo& L, int64_t M, char* buf, size_t len
         return HQ_OK;
     }
     g_plan = &rec;
-    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+    DenseArgs a{};  // shapes only: the planning run touches no pointer
+    a.M = M;
+    a.N = L.N;
+    a.K = L.K;
+    a.Np = L.Np;
+    a.group_size = (int)L.G;
     const hq_status st = dense_launch(L, a);
     g_plan = nullptr;
     if (buf) buf[rec.used < len ? rec.used : len - 1] = 0;
@@ -333,9 +350,10 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const voi
             return set_error(HQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? ws_bytes : (size_t)0);
         if (!aligned16(workspace)) return set_error(HQ_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
     }
-    const bool mx = desc->a_scale == HQ_ASCALE_MX_E8M0;
-    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, mx ? nullptr : (const float*)a_scale,
-                mx ? (const uint8_t*)a_scale : nullptr, w, s, z, D, workspace, ws_bytes, (hipStream_t)stream};
+    const bool mx = desc->a_scale == HQ_ASCALE_MX_E8M0, blk = desc->a_scale == HQ_ASCALE_PER_BLOCK128_F32;
+    DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, mx || blk ? nullptr : (const float*)a_scale,
+                mx ? (const uint8_t*)a_scale : nullptr, blk ? (const float*)a_scale : nullptr,
+                w, s, z, D, workspace, ws_bytes, (hipStream_t)stream};
     return dense_launch(L, a);
 }
 
@@ -450,6 +468,21 @@ hq_status hq_quantize_act_mx(int32_t out_dtype, int64_t M, int64_t K, const floa
     if (!aligned16(x) || !aligned16(q) || !aligned16(e)) return set_error(HQ_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
     return hip_status(quant_mx_launch(out_dtype == HQ_DT_FP4_E2M1, M, K, x, (uint8_t*)q, (uint8_t*)e, (hipStream_t)stream),
                       "hq_quantize_act_mx");
+}
+
+hq_status hq_quantize_act_blocks(int32_t out_dtype, int64_t M, int64_t K, int64_t block, const float* x, void* q,
+                                 float* s, hq_stream_t stream) {
+    if (out_dtype != HQ_DT_FP8_E4M3) return set_error(HQ_ERR_UNSUPPORTED, "only FP8_E4M3 activation codes are built");
+    if (M < 0 || K < 1 || block < 1 || M > (1LL << 30) || K > (1LL << 24) || K % block)
+        return set_error(HQ_ERR_INVALID_ARG, "M/K/block out of range (K a multiple of block)");
+    if (M * (K / block) >= (1LL << 31)) return set_error(HQ_ERR_UNSUPPORTED, "too many blocks");
+    if (M == 0) return ok();
+    if (!x || !q || !s) return set_error(HQ_ERR_INVALID_ARG, "x, q and s are required");
+    if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return set_error(HQ_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    if ((block * 4) % 16 && K != block) return set_error(HQ_ERR_UNSUPPORTED, "block must be a multiple of 4 (or K)");
+    // every block is its own row of a tokenwise problem: rows of `block` consecutive elements
+    return hip_status(quant_e4m3_launch(M * (K / block), block, x, (uint8_t*)q, s, (hipStream_t)stream),
+                      "hq_quantize_act_blocks");
 }
 
 hq_status hq_silu_mul(int32_t dtype, int64_t rows, int64_t I, const void* gate_up, void* out, hq_stream_t stream) {

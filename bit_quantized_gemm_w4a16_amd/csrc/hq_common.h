@@ -17,6 +17,7 @@ enum class Kind {
     W8A8,         // int8 A (per-token fp32 scale), int8 W, fp32 per-channel
     MOE_MX_BF16,  // MoE: bf16 A, e2m1 W, E8M0 per 32 K
     MXA_MX,       // MX activations (E4M3 or E2M1, E8M0 per 32 K) x e2m1 W, E8M0 per 32 K
+    FP8_BLOCK,    // fp8-e4m3 A (fp32 per row and 128-K block) x fp8-e4m3 W (fp32 per 128 x 128 block)
 };
 
 struct LayerInfo {

@@ -37,6 +37,7 @@ struct DenseArgs {
     const void* A;
     const float* a_scale;   // per-token fp32 scales (W4A8 tokenwise, W8A8)
     const uint8_t* a_e8;    // MX activation scales, E8M0 [M][K/32]
+    const float* a_blk;     // blockwise fp8 activation scales, fp32 [M][K/128]
     const void* w;
     const void* s;
     const void* z;
@@ -53,6 +54,7 @@ hipError_t wna16_launch(const DenseArgs& a, bool bf16, bool zp);
 hipError_t w4a8_launch(const DenseArgs& a);
 hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32);
 hipError_t mx_act_launch(const DenseArgs& a, bool fp4_act);  // MX activations x MXFP4 weights
+hipError_t fp8_block_launch(const DenseArgs& a);              // FP8 W8A8 with blockwise scales
 
 // MoE
 struct MoeLayout {  // byte offsets into the MoE workspace

@@ -137,6 +137,10 @@ void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s
             *w = E * nst * (size_t)(L.K / 64) * 1024;
             *s = E * (size_t)L.Np * 4;
             break;
+        case Kind::FP8_BLOCK:
+            *w = E * nst * (size_t)(L.K / 64) * 1024;
+            *s = E * (size_t)(L.K / 128) * (size_t)((L.N + 127) / 128) * 4;
+            break;
     }
 }
 
@@ -157,6 +161,12 @@ void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z,
         case Kind::W8A8:
             repack_int8(L, (const int8_t*)w, (int8_t*)w_out);
             repack_chan32(L, (const float*)s, (float*)s_out);
+            break;
+        case Kind::FP8_BLOCK:
+            // E4M3 codes take the INT8 byte layout (code 0 = +0 in the padding); the
+            // 128 x 128 block scales keep their logical [K/128][ceil(N/128)] order
+            repack_int8(L, (const int8_t*)w, (int8_t*)w_out);
+            std::memcpy(s_out, s, (size_t)(L.K / 128) * (size_t)((L.N + 127) / 128) * 4 * (size_t)L.E);
             break;
     }
 }

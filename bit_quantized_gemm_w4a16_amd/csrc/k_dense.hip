@@ -12,6 +12,11 @@
 // with one E8M0 scale per 32 K per row, fed with the weights' E8M0 scales to
 // the same scaled MFMA; no epilogue scale.
 //
+// FP8 W8A8 with blockwise scales (same section: the Hopper-era FP8 path with
+// blockwise scaling; "Humming v0.1.0-0.1.4" for the per-K-block activation
+// scale indexing): fp8 x fp8 on the scaled MFMA per 128-K block, the partial
+// scaled by the row's block scale times the 128 x 128 weight block scale.
+//
 // W8A8-INT8 (same section, INT8 through integer MMA): int8 x int8 into exact
 // int32 accumulators (v_mfma_i32_16x16x64_i8), then acc * s_a[m] * s_w[n] in
 // fp32, or the raw int32 accumulators.
@@ -30,6 +35,7 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
         s.A = a.A;
         s.a_scale = a.a_scale;
         s.a_e8 = a.a_e8;
+        s.a_blk = a.a_blk;
         s.W = a.w;
         s.S = a.s;
         s.D = a.D;
@@ -48,6 +54,7 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
     p.A = a.A;
     p.a_scale = a.a_scale;
     p.a_e8 = a.a_e8;
+    p.a_blk = a.a_blk;
     p.W = a.w;
     p.S = a.s;
     p.D = a.D;
@@ -69,6 +76,8 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
 hipError_t w4a8_launch(const DenseArgs& a) { return launch<Fmt::W4A8_MX>(a, 0); }
 
 hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32) { return launch<Fmt::W8A8_I8>(a, raw_i32 ? 1 : 0); }
+
+hipError_t fp8_block_launch(const DenseArgs& a) { return launch<Fmt::W8A8_F8B>(a, 0); }
 
 hipError_t mx_act_launch(const DenseArgs& a, bool fp4_act) {
     return fp4_act ? launch<Fmt::W4A4_MX>(a, 0) : launch<Fmt::W4A8_MXA>(a, 0);

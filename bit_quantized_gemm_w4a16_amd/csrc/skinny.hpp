@@ -39,6 +39,9 @@
 //                   the A scale (MXFP8 activations; copied to LDS with the A slice)
 //   W4A4_MX         the same with fp4 e2m1 activations (MXFP4 x MXFP4)
 //   W8A8_I8         2 x v_mfma_i32_16x16x64_i8 (exact int32)
+//   W8A8_F8B        1 x the scaled MFMA on fp8 x fp8 per chunk (one 128-K scale
+//                   block), its partial scaled by the row's activation block
+//                   scale times the strip's weight block scale (both in LDS)
 #pragma once
 
 #include "tile_gemm.hpp"
@@ -52,6 +55,7 @@ struct SkinnyArgs {
     const void* A;          // activations [a_rows][K]
     const float* a_scale;   // per-token fp32 (W4A8 / W8A8), by A row
     const uint8_t* a_e8;    // MX activation scales E8M0 [a_rows][K/32] (W4A8_MXA / W4A4_MX)
+    const float* a_blk;     // activation scales per row and 128-K block [a_rows][K/128] (W8A8_F8B)
     const void* W;          // packed weights
     const void* S;          // packed group scales / E8M0 / per-channel fp32
     const void* Z;          // packed zero-points (WNA16 with UINT4), or null
@@ -152,6 +156,27 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
             if (pos < U) lds_dma16(arow + ((pos ^ skinny_swz<UPC>(r)) * 16), lds + p.a_off + (r * U + blk * 64) * 16);
             blk += 4;
             while (r < rows && blk >= nblk) { blk -= nblk; ++r; }
+        }
+        if constexpr (F == Fmt::W8A8_F8B) {
+            // weight block scales [strip j][chunk] at s_off (strip j's 128-column block is
+            // its strip index / 8); activation scales [chunk][row, 16-row aligned] at z_off
+            const int nbn = (p.Np + 127) / 128, R16 = (rows + 15) & ~15;
+            const float* swg = (const float*)Sb;
+            for (int w0 = wave * 64; w0 < p.NS * nsl; w0 += 256) {
+                const int w = w0 + lane;
+                if (w < p.NS * nsl) {
+                    const int j = w / nsl, c = w - j * nsl;
+                    const int st = strip_base + j < nstrips ? strip_base + j : nstrips - 1;
+                    lds_dma4(swg + (size_t)(c0 + c) * nbn + st / 8, lds + p.s_off + w0 * 4);
+                }
+            }
+            for (int w0 = wave * 64; w0 < nsl * R16; w0 += 256) {
+                const int w = w0 + lane;
+                if (w < nsl * R16) {
+                    const int c = w / R16, r = w - c * R16;
+                    lds_dma4(p.a_blk + (size_t)(r < rows ? r : rows - 1) * (p.K / 128) + c0 + c, lds + p.z_off + w0 * 4);
+                }
+            }
         }
         if constexpr (WNA16) {
             const int sg0 = c0 / p.gchunks, sgslab = (c1 - 1) / p.gchunks - sg0 + 1;
@@ -361,6 +386,32 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     for (int mt = 0; mt < MT; ++mt)
                         acc2[i & 1][sp][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], b, acc2[i & 1][sp][mt], CBSZ, 4, 0, asc[mt], 0, bsc);
                 }
+            } else if constexpr (F == Fmt::W8A8_F8B) {
+                const int R16 = (rows + 15) & ~15;
+                v8i af[MT];
+                v4f sa4[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int row = arow_l[mt];
+                    const char* ar = lA + (size_t)row * U * 16;
+                    const int sw = skinny_swz<8>(row);
+                    const v4u lo = *(const v4u*)(ar + (((cl * 8 + quad) ^ sw) * 16));
+                    const v4u hi = *(const v4u*)(ar + (((cl * 8 + 4 + quad) ^ sw) * 16));
+                    af[mt] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    // this lane's output rows mt * 16 + 4 quad .. + 3 (clamped rows are dropped on store)
+                    sa4[mt] = *(const v4f*)(lds + p.z_off + (cl * R16 + (mt * 16 + 4 * quad < R16 ? mt * 16 + 4 * quad : R16 - 4)) * 4);
+                }
+#pragma unroll
+                for (int sp = 0; sp < SPW; ++sp) {
+                    const float swv = ((const float*)(lds + p.s_off))[(ws * SPW + sp) * nsl + cl];
+                    const v4u w0 = valid ? w[i][sp][0] : v4u{0u, 0u, 0u, 0u}, w1 = valid ? w[i][sp][1] : v4u{0u, 0u, 0u, 0u};
+                    const v8i b = v8i{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0x7F, 0, 0x7F);
+                        acc2[i & 1][sp][mt] += part * (sa4[mt] * swv);
+                    }
+                }
             } else {  // W8A8_I8
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -486,7 +537,7 @@ struct SkinnyLds {
     int64_t a_off, s_off, z_off, bytes;
 };
 inline int skinny_arow(Fmt F) {
-    return F == Fmt::W4A4_MX ? 64 : (F == Fmt::W4A8_MX || F == Fmt::W4A8_MXA || F == Fmt::W8A8_I8) ? 128 : 256;
+    return F == Fmt::W4A4_MX ? 64 : (F == Fmt::W4A8_MX || F == Fmt::W4A8_MXA || F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B) ? 128 : 256;
 }
 inline SkinnyLds skinny_lds(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) {
     auto al = [](int64_t b) { return (b + 1023) / 1024 * 1024; };
@@ -498,6 +549,9 @@ inline SkinnyLds skinny_lds(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) 
     } else if (mx_mfma(F)) {
         s = al(NS * cmax * 64);
         if (mx_act(F)) z = al(rows * cmax * 4);
+    } else if (F == Fmt::W8A8_F8B) {
+        s = al(NS * cmax * 4);
+        z = al(((rows + 15) / 16 * 16) * cmax * 4);
     }
     SkinnyLds L;
     L.a_off = 0;
@@ -530,7 +584,7 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G) {
     // strips alone leave a quarter of the chip idle (or the slice must shrink)
     int64_t S = p.groups_x >= 192 ? 1 : cdiv(256, p.groups_x);
     const int64_t smax = nc / WK > 0 ? nc / WK : 1;
-    const int nb = F == Fmt::W8A8_I8 ? 2 : 1;
+    const int nb = (F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B) ? 2 : 1;  // 16-byte weight loads per chunk
     const int64_t cap = p.SPW * 16 * nb < 64 ? 16 : 8;  // largest register batch instantiated
     while (S < smax && (skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap)) ++S;
     if (S > smax) S = smax;

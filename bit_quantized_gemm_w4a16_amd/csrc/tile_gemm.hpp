@@ -34,6 +34,10 @@
 //               to row l & 15 and K block l >> 4 of the instruction)
 //   W4A4_MX     fp4-e2m1 A with E8M0 per 32 K (MXFP4) x e2m1 B on the same
 //               scaled MFMA (A lane l holds row l & 15, K = 32 (l >> 4) + i)
+//   W8A8_F8B    fp8-e4m3 A (fp32 scale per row and 128-K block) x fp8-e4m3 B
+//               (fp32 scale per 128 x 128 block, INT8 packing): each 128-K
+//               step's fp8 MFMA partial is scaled by sa[row] * sw and added
+//               to the fp32 accumulator
 //   W8A8_I8     int8 x int8 -> int32 (exact), per-token x per-channel epilogue
 //   MOE_MX      bf16 A x e2m1 B converted to bf16 with the E8M0 scale (exact)
 #pragma once
@@ -45,11 +49,12 @@
 
 namespace hq {
 
-enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX };
+enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B };
 
 constexpr const char* fmt_name(Fmt F) {
     return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
-         : F == Fmt::W8A8_I8 ? "W8A8_I8" : F == Fmt::MOE_MX ? "MOE_MX" : F == Fmt::W4A8_MXA ? "W4A8_MXA" : "W4A4_MX";
+         : F == Fmt::W8A8_I8 ? "W8A8_I8" : F == Fmt::MOE_MX ? "MOE_MX" : F == Fmt::W4A8_MXA ? "W4A8_MXA"
+         : F == Fmt::W4A4_MX ? "W4A4_MX" : "W8A8_F8B";
 }
 // Formats whose activations carry OCP MX scales (E8M0 per 32 K, [rows][K/32]).
 constexpr bool mx_act(Fmt F) { return F == Fmt::W4A8_MXA || F == Fmt::W4A4_MX; }
@@ -66,12 +71,14 @@ template <> struct FmtTraits<Fmt::W8A8_I8> { static constexpr int AROW = 128, BS
 template <> struct FmtTraits<Fmt::MOE_MX> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::W4A8_MXA> { static constexpr int AROW = 128, BSTRIP = 1024; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::W4A4_MX> { static constexpr int AROW = 64, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::W8A8_F8B> { static constexpr int AROW = 128, BSTRIP = 2048; using Acc = v4f; };
 
 // Work description of one launch.  Dense launches leave the MoE fields null.
 struct TileArgs {
     const void* A;          // activations, row-major [rows][K]
     const float* a_scale;   // per-token fp32 (W4A8 / W8A8), indexed by A row
     const uint8_t* a_e8;    // MX activation scales, E8M0 [rows][K/32] (W4A8_MXA / W4A4_MX)
+    const float* a_blk;     // fp32 activation scales per row and 128-K block [rows][K/128] (W8A8_F8B)
     const void* W;          // packed weights (expert 0)
     const void* S;          // packed scales (expert 0)
     const void* Z;          // packed zero-points (WNA16 + UINT4)
@@ -195,6 +202,8 @@ void tile_gemm_kernel(TileArgs p) {
     constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
     constexpr bool MX = mx_mfma(F) || F == Fmt::MOE_MX;  // E8M0 weight scales per 32 K
     constexpr bool MXA = mx_act(F);
+    constexpr bool F8B = F == Fmt::W8A8_F8B;
+    static_assert(!F8B || BN == 128, "blockwise fp8: one 128-column weight block per tile");
     constexpr int NTH = 64 * WM * WN;
     constexpr int BK = 128;
     constexpr int AROW = T::AROW, AUNITS = AROW / 16;
@@ -205,7 +214,9 @@ void tile_gemm_kernel(TileArgs p) {
     // MXFP4 one E8M0 byte per lane per strip; INT8 none (per-channel, epilogue)
     constexpr int SC_Z = NSTRIP * 32;                     // zero-point words start (WNA16)
     constexpr int SC_B = WNA16 ? NSTRIP * 48 : MX ? NSTRIP * 64 : 0;
-    constexpr int SC_STAGE = SC_B + (MXA ? BM * 4 : 0);   // MX activations: one E8M0 word (4 K blocks) per row
+    // MX activations: one E8M0 word (4 K blocks) per row; blockwise fp8: one fp32
+    // activation scale per row, then the tile's weight block scale
+    constexpr int SC_STAGE = SC_B + (MXA ? BM * 4 : 0) + (F8B ? BM * 4 + 16 : 0);
     constexpr int SC_UNITS = SC_B / 16;
     // a stage holds the A and weight tiles of one step; the step's scale block
     // sits in an LDS array of its own (it is loaded through registers, and its
@@ -293,9 +304,12 @@ void tile_gemm_kernel(TileArgs p) {
     const uint32_t nstr = (uint32_t)(p.Np / 16);
     const uint32_t arow_bytes = (uint32_t)(K / BK) * AROW;  // bytes of one A row
     const rsrc_t rA = make_rsrc(p.A, (uint32_t)p.a_rows * arow_bytes);
-    const rsrc_t rAS = make_rsrc(p.a_e8, MXA ? (uint32_t)p.a_rows * (uint32_t)(K / 32) : 0u);
+    const rsrc_t rAS = MXA ? make_rsrc(p.a_e8, (uint32_t)p.a_rows * (uint32_t)(K / 32))
+                     : make_rsrc(p.a_blk, F8B ? (uint32_t)p.a_rows * (uint32_t)(K / 128) * 4u : 0u);
     const rsrc_t rW = make_rsrc(Wbase, nstr * (uint32_t)nsteps * T::BSTRIP);
-    const rsrc_t rS = make_rsrc(Sbase, WNA16 ? nstr * (uint32_t)p.ngroups * 32u : MX ? nstr * (uint32_t)nsteps * 64u : 0u);
+    const uint32_t nbn = (uint32_t)((p.Np + 127) / 128);  // weight column blocks (blockwise fp8)
+    const rsrc_t rS = make_rsrc(Sbase, WNA16 ? nstr * (uint32_t)p.ngroups * 32u : MX ? nstr * (uint32_t)nsteps * 64u
+                                       : F8B ? (uint32_t)nsteps * nbn * 4u : 0u);
     const rsrc_t rZ = make_rsrc(p.Z, WNA16 && p.Z ? nstr * (uint32_t)p.ngroups * 8u : 0u);
 
     // per-thread byte offsets of the staged loads (fixed across K steps).  Dense
@@ -352,7 +366,7 @@ void tile_gemm_kernel(TileArgs p) {
     constexpr int NSET = RSTAGE ? PD : PD == 4 ? NST : 1;  // register sets (the ring: one scale block per stage)
     v4u ra[NSET][RSTAGE ? NIA : 1], rb[NSET][RSTAGE ? NIB : 1], rs[NSET];
     uint32_t rsa[NSET];  // MX activations: this thread's row's E8M0 word of the step (threads < BM)
-    const uint32_t as_voff = (uint32_t)(m0 + (tid < BM ? tid : 0)) * (uint32_t)(K / 32);
+    const uint32_t as_voff = (uint32_t)(m0 + (tid < BM ? tid : 0)) * (uint32_t)(F8B ? (K / 128) * 4 : K / 32);
     // Direct loads of one step's A and weight tiles into a stage (NIA + NIB
     // unconditional loads per thread).  The scale block goes through registers
     // (sc_load, then sc_write into its own LDS array once landed): the compiler
@@ -398,6 +412,9 @@ void tile_gemm_kernel(TileArgs p) {
             // rows past M fall outside the buffer resource and read zeros (outputs dropped)
             if constexpr (MXA)
                 if (tid < BM) rsa[st] = buf4(rAS, as_voff, (uint32_t)ks * 4u);
+        } else if constexpr (F8B) {
+            if (tid < BM) rsa[st] = buf4(rAS, as_voff, (uint32_t)ks * 4u);
+            else if (tid == BM) rsa[st] = buf4(rS, 0u, ((uint32_t)ks * nbn + (uint32_t)(strip0 / 8)) * 4u);
         }
     };
     auto sc_write = [&](auto stc, auto setc) {
@@ -408,6 +425,8 @@ void tile_gemm_kernel(TileArgs p) {
                 if (tid < 2 * NSTRIP) *(v4u*)(sS + tid * 16) = rs[st];
                 else if (tid < 3 * NSTRIP)
                     *(uint64_t*)(sS + SC_Z + (tid - 2 * NSTRIP) * 8) = ((uint64_t)rs[st][1] << 32) | rs[st][0];
+            } else if constexpr (F8B) {
+                if (tid <= BM) *(uint32_t*)(sS + tid * 4) = rsa[st];
             } else {
                 if (tid < SC_UNITS) *(v4u*)(sS + tid * 16) = rs[st];
                 if constexpr (MXA)
@@ -631,6 +650,30 @@ void tile_gemm_kernel(TileArgs p) {
                 for (int j = 0; j < NT; ++j) {
                     const v8i b = v8i{(int)bw[j][0][0], (int)bw[j][0][1], (int)bw[j][0][2], (int)bw[j][0][3], 0, 0, 0, 0};
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i][j], CBSZ, 4, 0, asc, 0, bsc[j]);
+                }
+            }
+        } else if constexpr (F8B) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) hook(t);
+            // one fp8 x fp8 MFMA per 16 x 16 tile covers the whole 128-K step (A bytes
+            // 0-15: K 16 quad + [0,16), bytes 16-31: K 64 + 16 quad + [0,16); the INT8
+            // weight packing holds the same K in its two 64-K halves)
+            const float swv = ((const float*)sS)[BM];
+            const int sw8 = swz(col, AUNITS);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int row = wm * (BM / WM) + i * 16 + col;
+                const v4u lo = *(const v4u*)(sA + row * AROW + ((quad ^ sw8) * 16));
+                const v4u hi = *(const v4u*)(sA + row * AROW + (((4 + quad) ^ sw8) * 16));
+                const v8i a = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                // this lane's output rows 4 quad .. 4 quad + 3 of tile i
+                const v4f sa4 = *(const v4f*)(sS + (wm * (BM / WM) + i * 16 + 4 * quad) * 4) * swv;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const v8i b = v8i{(int)bw[j][0][0], (int)bw[j][0][1], (int)bw[j][0][2], (int)bw[j][0][3],
+                                      (int)bw[j][1][0], (int)bw[j][1][1], (int)bw[j][1][2], (int)bw[j][1][3]};
+                    const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0x7F, 0, 0x7F);
+                    acc[i][j] += part * sa4;
                 }
             }
         } else if constexpr (F == Fmt::W8A8_I8) {
@@ -1006,6 +1049,20 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
         }
         return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
     } else {
+        if constexpr (F == Fmt::W8A8_F8B) {
+            // 128-column tiles (one weight scale block) on stage rings, one round of
+            // the chip: 256 rows where that fills it, else 128 rows with K split
+            if (((p.M + 255) / 256) * ((p.Np + 127) / 128) >= 256) {
+                p.splits = 1;
+                return launch_tile_kernel<F, 256, 128, 2, 4, 4>(p, st);
+            }
+            const int64_t tiles = ((p.M + 127) / 128) * ((p.Np + 127) / 128), nsteps = p.K / 128;
+            int64_t s = tiles < 256 ? 256 / tiles : 1;
+            if (s > 8) s = 8;
+            if (s > nsteps / 2) s = nsteps / 2;
+            p.splits = (int)(s < 1 ? 1 : s);
+            return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
+        }
         if constexpr (mx_mfma(F)) {
             // 8-bit A: a 256-column tile on a three-stage ring (4-bit A: four stages)
             if (pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 4>(p, st);

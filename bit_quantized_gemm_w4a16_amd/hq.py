@@ -23,8 +23,8 @@ HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_ALIGNMENT, HQ_ERR_WORKSPAC
 # hq_dtype
 (HQ_DT_NONE, HQ_DT_BF16, HQ_DT_FP16, HQ_DT_FP32, HQ_DT_FP8_E4M3, HQ_DT_INT8, HQ_DT_INT4, HQ_DT_UINT4,
  HQ_DT_FP4_E2M1, HQ_DT_E8M0, HQ_DT_INT32) = range(11)
-HQ_GRAN_NONE, HQ_GRAN_PER_GROUP_K, HQ_GRAN_PER_CHANNEL = range(3)
-HQ_ASCALE_NONE, HQ_ASCALE_PER_TOKEN_F32, HQ_ASCALE_MX_E8M0 = range(3)
+HQ_GRAN_NONE, HQ_GRAN_PER_GROUP_K, HQ_GRAN_PER_CHANNEL, HQ_GRAN_BLOCK_128x128 = range(4)
+HQ_ASCALE_NONE, HQ_ASCALE_PER_TOKEN_F32, HQ_ASCALE_MX_E8M0, HQ_ASCALE_PER_BLOCK128_F32 = range(4)
 HQ_S2_NONE = 0
 HQ_MOE_INDEXED, HQ_MOE_GROUPED = 1, 2
 
@@ -65,6 +65,7 @@ _SIGS = {
                               C.c_size_t, _P]),
     "hq_quantize_act": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, _P, _P, _P, _P]),
     "hq_quantize_act_mx": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, _P, _P, _P, _P]),
+    "hq_quantize_act_blocks": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, C.c_int64, _P, _P, _P, _P]),
     "hq_moe_align": (C.c_int, [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]),
     "hq_moe_gather": (C.c_int, [C.c_int32, C.c_int64, C.c_int32, C.c_int64, _P, _P, _P, _P]),
     "hq_silu_mul": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, _P, _P, _P]),
@@ -143,6 +144,13 @@ def desc_mx_act_mxfp4(N, K, fp4_act: bool) -> hq_layer_desc:
     """MX activations (E2M1 for W4A4, E4M3 for MXFP8 x MXFP4), E8M0 per 32 K, x MXFP4 weights."""
     return make_desc(N, K, HQ_DT_FP4_E2M1 if fp4_act else HQ_DT_FP8_E4M3, HQ_DT_FP4_E2M1, HQ_DT_E8M0,
                      HQ_GRAN_PER_GROUP_K, 32, HQ_DT_BF16, a_scale=HQ_ASCALE_MX_E8M0)
+
+
+def desc_fp8_blockwise(N, K) -> hq_layer_desc:
+    """FP8 W8A8 with blockwise scales: E4M3 activations with fp32 scales per 128-K block,
+    E4M3 weights with fp32 scales per 128 x 128 block, bf16 output."""
+    return make_desc(N, K, HQ_DT_FP8_E4M3, HQ_DT_FP8_E4M3, HQ_DT_FP32, HQ_GRAN_BLOCK_128x128, 128, HQ_DT_BF16,
+                     a_scale=HQ_ASCALE_PER_BLOCK128_F32)
 
 
 def desc_w8a8(N, K, raw_int32=False) -> hq_layer_desc:
@@ -224,6 +232,11 @@ def hq_moe_gemm(desc, mode, T, top_k, A, a_scale, topk_ids, expert_offsets, w, s
 
 def hq_quantize_act(out_dtype, M, K, x, q, s, stream=None) -> None:
     _check(lib().hq_quantize_act(out_dtype, M, K, _dp(x), _dp(q), _dp(s), _stream(stream)), "hq_quantize_act")
+
+
+def hq_quantize_act_blocks(out_dtype, M, K, block, x, q, s, stream=None) -> None:
+    _check(lib().hq_quantize_act_blocks(out_dtype, M, K, block, _dp(x), _dp(q), _dp(s), _stream(stream)),
+           "hq_quantize_act_blocks")
 
 
 def hq_quantize_act_mx(out_dtype, M, K, x, q, e, stream=None) -> None:

@@ -86,13 +86,15 @@ typedef enum hq_dtype {
 typedef enum hq_scale_gran {
     HQ_GRAN_NONE = 0,
     HQ_GRAN_PER_GROUP_K = 1, /* one scale per (group of group_size along K, column) */
-    HQ_GRAN_PER_CHANNEL = 2  /* one scale per output column                         */
+    HQ_GRAN_PER_CHANNEL = 2, /* one scale per output column                         */
+    HQ_GRAN_BLOCK_128x128 = 3 /* one scale per 128 x 128 block: [K/128][ceil(N/128)] */
 } hq_scale_gran;
 
 typedef enum hq_ascale {
     HQ_ASCALE_NONE = 0,
     HQ_ASCALE_PER_TOKEN_F32 = 1, /* fp32 a_scale[M], applied in the epilogue              */
-    HQ_ASCALE_MX_E8M0 = 2        /* OCP MX: uint8 E8M0 a_scale[M][K/32], 2^(e-127) per 32 K */
+    HQ_ASCALE_MX_E8M0 = 2,       /* OCP MX: uint8 E8M0 a_scale[M][K/32], 2^(e-127) per 32 K */
+    HQ_ASCALE_PER_BLOCK128_F32 = 3 /* fp32 a_scale[M][K/128], one per row and 128-K block   */
 } hq_ascale;
 
 typedef enum hq_scale2 {
@@ -117,6 +119,7 @@ typedef enum hq_moe_mode {
  *   INT8      INT8       FP32, PER_CHANNEL             NONE    PER_TOKEN BF16|INT32
  *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    MX_E8M0   BF16   (MXFP8 x MXFP4)
  *   FP4_E2M1  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    MX_E8M0   BF16   (W4A4 MXFP4)
+ *   FP8_E4M3  FP8_E4M3   FP32, BLOCK_128x128           NONE    PER_BLOCK128 BF16 (FP8 blockwise)
  *   BF16      FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MoE)
  * FP4_E2M1 activations are packed two per byte along K, element k in the low
  * nibble of byte k/2 when k is even (rows of K/2 bytes).
@@ -171,9 +174,9 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *
  * Logical inputs (per expert, experts stacked along a leading axis):
  *   w  4-bit codes: uint32 [K/8][N]; code k = 8j+i of column n in bits
- *      4i..4i+3 of word [j][n]            INT8: int8 [K][N]
+ *      4i..4i+3 of word [j][n]            INT8 / FP8_E4M3: one byte [K][N]
  *   scale  [K/group][N] in w_scale_dtype (16-bit raw bits, uint8 for E8M0);
- *          PER_CHANNEL fp32: [N]
+ *          PER_CHANNEL fp32: [N]; BLOCK_128x128 fp32: [K/128][ceil(N/128)]
  *   zp     UINT4: uint32 [K/group][ceil(N/8)]; column n = 8j+i in bits
  *          4i..4i+3 of word [g][j]
  *   scale2 must be NULL (no second-level scale kernels yet)
@@ -187,13 +190,13 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *      natural order (j in nibble j%8); INT4/UINT4 codes are in pair order
  *      (nibble p holds j%8 = {0,2,4,6,1,3,5,7}[p]) so that one shift+mask
  *      yields two consecutive codes in the two 16-bit halves.
- *      INT8: [Np/16][K/64][64 lanes][16 B]; lane l holds column
+ *      INT8 and FP8_E4M3: [Np/16][K/64][64 lanes][16 B]; lane l holds column
  *      16*strip + (l & 15), k = 64*chunk + 16*(l >> 4) + j, j = 0..15.
  *   scale  16-bit group scales: [E][Np/16][K/group][16];
  *          E8M0: [E][Np/16][K/128][64 lanes] bytes; lane l holds the
  *          exponent of column 16*strip + (l & 15), K-block 4*chunk + (l >> 4)
  *          (padding columns hold 127);
- *          PER_CHANNEL fp32: [Np]
+ *          PER_CHANNEL fp32: [Np]; BLOCK_128x128 fp32: unchanged [K/128][ceil(N/128)]
  *   zp     [E][Np/16][K/group] uint64, column 16*strip + i in bits 4i..4i+3
  */
 hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale, const void* zp,
@@ -222,7 +225,8 @@ hq_status hq_workspace_init(void* workspace, size_t bytes, hq_stream_t stream);
  * Dense D[M,N] = A[M,K] x dequant(W).
  *   A        device, [M][K] row-major, a_dtype (E2M1: [M][K/2] bytes)
  *   a_scale  device; PER_TOKEN_F32: fp32 [M]; MX_E8M0: uint8 [M][K/32]
- *            (E8M0 of row m, K block b); NONE: NULL
+ *            (E8M0 of row m, K block b); PER_BLOCK128_F32: fp32 [M][K/128];
+ *            NONE: NULL
  *   w, s, z, s2  device, packed by hq_repack (unused ones NULL)
  *   D        device, [M][N] row-major, out_dtype
  * Floating outputs: fp32 accumulation, rounded once (RNE) to out_dtype.
@@ -291,6 +295,20 @@ hq_status hq_moe_gemm(const hq_layer_desc* desc, int32_t mode, int64_t T, int32_
  */
 hq_status hq_quantize_act(int32_t out_dtype, int64_t M, int64_t K, const float* x, void* q, float* s,
                           hq_stream_t stream);
+
+/*
+ * Activation quantisation to E4M3 with one fp32 scale per row and block of
+ * `block` consecutive elements along K ("Humming wird angekuendigt", section
+ * "W8A8 / W4A8 / W4A4": FP8 W8A8 with blockwise scaling; block 128 gives the
+ * 1 x 128 activation blocks of that path, block K the tokenwise case of
+ * hq_quantize_act).  Per block: s = max |x| / 448 in fp32 (1 for an all-zero
+ * block), q = E4M3(x / s) with fp32 division, round to nearest even,
+ * saturating at +-448; NaN and infinity as in hq_quantize_act.
+ *   x fp32 [M][K], q [M][K], s fp32 [M][K/block]; K a multiple of block,
+ *   block a multiple of 4 unless it equals K; pointers 16-byte aligned.
+ */
+hq_status hq_quantize_act_blocks(int32_t out_dtype, int64_t M, int64_t K, int64_t block, const float* x, void* q,
+                                 float* s, hq_stream_t stream);
 
 /*
  * MX activation quantisation ("Humming wird angekuendigt", sections

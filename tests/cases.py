@@ -59,6 +59,12 @@ MXA_BIG = [(1100, 7200, 128), (1100, 7168, 640)]
 MXA_SWEEP = [(M, C3["N"], C3["K"]) for M in SWEEP]
 
 
+# ---- FP8 W8A8 with blockwise scales: (M, N, K) ----
+FP8B_SMALL = [(M, 304, 640) for M in (1, 3, 16, 24, 33, 64, 100, 200)] + [(M, 300, 7168) for M in (1, 20, 64)]
+FP8B_TILES = [(1100, 7200, 384), (600, 4000, 1280), (2100, 16400, 256)]
+FP8B_SWEEP = [(M, 7168, 7168) for M in SWEEP]
+
+
 def all_dense_cases():
     """(format, M, N, K, G, flags) for every dense GPU case, flags a dict."""
     out = []
@@ -74,4 +80,6 @@ def all_dense_cases():
     for elem in ("e2m1", "e4m3"):
         for M, N, K in MXA_SMALL + MXA_MID + MXA_BIG + MXA_SWEEP:
             out.append(("mxa", M, N, K, 32, dict(elem=elem)))
+    for M, N, K in FP8B_SMALL + FP8B_TILES + FP8B_SWEEP:
+        out.append(("fp8b", M, N, K, 128, {}))
     return out

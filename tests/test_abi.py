@@ -65,6 +65,36 @@ def test_descriptor_validation():
     assert "dtype" in hq.lib().hq_last_error().decode()
 
 
+def test_descriptor_validation_low_precision_variants():
+    """W4A4 / MXFP8 activations (E8M0 per 32 K) and FP8 W8A8 with blockwise scales."""
+    assert status_of(hq.hq_desc_validate, hq.desc_mx_act_mxfp4(7168, 4096, fp4_act=True)) == hq.HQ_OK
+    assert status_of(hq.hq_desc_validate, hq.desc_mx_act_mxfp4(7168, 4096, fp4_act=False)) == hq.HQ_OK
+    assert status_of(hq.hq_desc_validate, hq.desc_mx_act_mxfp4(7168, 4000, fp4_act=True)) == hq.HQ_ERR_UNSUPPORTED
+    d = hq.desc_mx_act_mxfp4(256, 256, fp4_act=True)
+    d.a_scale = hq.HQ_ASCALE_PER_TOKEN_F32                  # fp4 activations need MX scales
+    assert status_of(hq.hq_desc_validate, d) == hq.HQ_ERR_UNSUPPORTED
+    d = hq.desc_mx_act_mxfp4(256, 256, fp4_act=True)
+    d.num_experts = 4
+    assert status_of(hq.hq_desc_validate, d) == hq.HQ_ERR_UNSUPPORTED
+    assert status_of(hq.hq_desc_validate, hq.desc_fp8_blockwise(7168, 7168)) == hq.HQ_OK
+    assert status_of(hq.hq_desc_validate, hq.desc_fp8_blockwise(7168, 7000)) == hq.HQ_ERR_UNSUPPORTED
+    d = hq.desc_fp8_blockwise(256, 256)
+    d.w_scale_gran = hq.HQ_GRAN_PER_CHANNEL
+    assert status_of(hq.hq_desc_validate, d) == hq.HQ_ERR_UNSUPPORTED
+    d = hq.desc_fp8_blockwise(256, 256)
+    d.a_scale = hq.HQ_ASCALE_PER_TOKEN_F32
+    assert status_of(hq.hq_desc_validate, d) == hq.HQ_ERR_UNSUPPORTED
+
+
+def test_fp8_blockwise_repack_keeps_int8_layout_and_block_scales():
+    N, K = 300, 256
+    d = syn.w8a8_fp8_blockwise(0, 1, N, K)
+    wp, sp, _ = hq.hq_repack(hq.desc_fp8_blockwise(N, K), d["w"], d["s_w"])
+    wi, _, _ = hq.hq_repack(hq.desc_w8a8(N, K), d["w"].view(np.int8), np.ones(N, np.float32))
+    np.testing.assert_array_equal(wp, wi)
+    np.testing.assert_array_equal(sp.view(np.float32).reshape(K // 128, 3), d["s_w"])
+
+
 def test_gemm_error_paths_return_before_any_hip_call():
     d = hq.desc_w4a16(1024, 7168, zp=True, bf16=False)
     A = w = s = z = D = 0x10000

@@ -22,6 +22,8 @@ def desc_of(fmt, N, K, G, flags):
         return hq.desc_w4a8_mxfp4(N, K)
     if fmt == "mxa":
         return hq.desc_mx_act_mxfp4(N, K, fp4_act=flags["elem"] == "e2m1")
+    if fmt == "fp8b":
+        return hq.desc_fp8_blockwise(N, K)
     return hq.desc_w8a8(N, K, raw_int32=flags["raw"])
 
 
@@ -50,6 +52,7 @@ BENCH = {
     "c4raw": ("w8a8", cases.C4["N"], cases.C4["K"], cases.C4["K"], dict(raw=True)),
     "w4a4": ("mxa", cases.C3["N"], cases.C3["K"], 32, dict(elem="e2m1")),
     "w4a8mx": ("mxa", cases.C3["N"], cases.C3["K"], 32, dict(elem="e4m3")),
+    "fp8b": ("fp8b", 7168, 7168, 128, {}),
 }
 
 
