@@ -71,6 +71,8 @@ def lib():
         L.hq_oracle_quant_act_e4m3_blocks.argtypes = [i64, i64, i64, p, p, p]
         L.hq_oracle_gemm_fp8_blockwise.restype = C.c_int
         L.hq_oracle_gemm_fp8_blockwise.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
+        L.hq_oracle_gemm_fp4_a16.restype = C.c_int
+        L.hq_oracle_gemm_fp4_a16.argtypes = [i64, i64, i64, C.c_int, p, p, C.c_int, p, p, p, i64, p]
         L.hq_oracle_gemm_w8a8.restype = C.c_int
         L.hq_oracle_gemm_w8a8.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p, p]
         L.hq_oracle_moe_route.restype = C.c_int
@@ -207,6 +209,21 @@ def gemm_mx_mxfp4(qa, ea, q, e, *, N, K, a_elem: str, rows=None):
                                        _ptr(_c(q, np.uint32)), _ptr(_c(e, np.uint8)), _ptr(r), R, _ptr(out))
     if rc:
         raise ValueError(f"oracle gemm_mx_mxfp4 failed ({rc})")
+    return out
+
+
+def gemm_fp4_a16(A, q, scales, *, N, K, a_bf16: bool, nvfp4: bool, s2=None, rows=None):
+    """FP4 (e2m1) weights with 16-bit activations: MXFP4 (E8M0 per 32 K) or NVFP4
+    (E4M3 per 16 K, times the per-tensor fp32 second-level scale s2), fp64."""
+    A = _c(A, np.uint16)
+    M = A.shape[0]
+    r, R = _rows(rows, M)
+    out = np.empty((R, N), dtype=np.float64)
+    s2a = None if s2 is None else np.array([s2], dtype=np.float32)
+    rc = lib().hq_oracle_gemm_fp4_a16(M, N, K, int(a_bf16), _ptr(A), _ptr(_c(q, np.uint32)), int(nvfp4),
+                                      _ptr(_c(scales, np.uint8)), _ptr(s2a), _ptr(r), R, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle gemm_fp4_a16 failed ({rc})")
     return out
 
 

@@ -331,6 +331,35 @@ int hq_oracle_gemm_mx_mxfp4(int64_t M, int64_t N, int64_t K, int a_elem, const u
     return 0;
 }
 
+/* FP4 weights with 16-bit activations (WnA16, FP4): W_real[k][n] =
+ * e2m1(q) * scale * s2, where scale_kind 0 (MXFP4) is an E8M0 byte per 32 K
+ * (scales uint8 [K/32][N]) and scale_kind 1 (NVFP4) an E4M3 byte per 16 K
+ * (scales uint8 [K/16][N]); s2 is the second-level fp32 scale per tensor
+ * (NULL: 1).  A is bf16 (a_bf16 = 1) or fp16 raw bits [M][K]; D = A x W_real. */
+int hq_oracle_gemm_fp4_a16(int64_t M, int64_t N, int64_t K, int a_bf16, const uint16_t* A, const uint32_t* q,
+                           int scale_kind, const uint8_t* scales, const float* s2,
+                           const int64_t* rows, int64_t nrows, double* out)
+{
+    const int64_t G = scale_kind ? 16 : 32;
+    if (K % G || (scale_kind != 0 && scale_kind != 1)) return 1;
+    int64_t R = rows ? nrows : M;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(R * K + 1));
+    if (!a) return 2;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k) a[r * K + k] = act16(a_bf16, A[row_of(rows, r) * K + k]);
+    const double t2 = s2 ? (double)s2[0] : 1.0;
+    memset(out, 0, sizeof(double) * (size_t)(R * N));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t sc = scales[(k / G) * N + n];
+            double w = hq_oracle_e2m1(nib_along_k(q, N, k, n)) * (scale_kind ? hq_oracle_e4m3(sc) : hq_oracle_e8m0(sc)) * t2;
+            for (int64_t r = 0; r < R; ++r) out[r * N + n] += a[r * K + k] * w;
+        }
+    free(a);
+    return 0;
+}
+
 /* FP8 W8A8 with blockwise scales: A_real[m][k] = e4m3(qa[m][k]) * sa[m][k/128],
  * W_real[k][n] = e4m3(w[k][n]) * sw[k/128][n/128], D = A_real x W_real.
  * qa uint8 [M][K], sa fp32 [M][K/128], w uint8 [K][N], sw fp32 [K/128][ceil(N/128)]. */

@@ -189,6 +189,23 @@ def w8a8_fp8_blockwise(seed, M, N, K, cfg=C6):
     )
 
 
+C7 = 7  # FP4 weights with 16-bit activations (MXFP4 / NVFP4 WnA16)
+
+
+def w4a16_fp4(seed, M, N, K, nvfp4: bool, dtype=torch.bfloat16, cfg=C7):
+    """FP4 WnA16: N(0,1) activations rounded to bf16/fp16, e2m1 codes uniform over all 16,
+    MXFP4: E8M0 exponents in [118, 127] per 32 K; NVFP4: E4M3 scales per 16 K drawn as
+    |N(0, 0.1)| + 0.01 rounded to E4M3 (torch's cast) and a per-tensor fp32 scale."""
+    out = dict(A=activations(seed, cfg, M, K, dtype), q=random_words(seed, cfg, T_Q, (K // 8, N)))
+    if nvfp4:
+        v = np.abs(_rng(seed, cfg, T_S).standard_normal((K // 16, N), dtype=np.float32)) * np.float32(0.1) + np.float32(0.01)
+        out["s"] = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+        out["s2"] = float(np.float32(np.abs(_rng(seed, cfg, T_Z).standard_normal()) * 0.5 + 0.25))
+    else:
+        out["s"] = e8m0_exponents(seed, cfg, (K // 32, N))
+    return out
+
+
 def moe_expert_mxfp4(seed, e, N, K, cfg=C5):
     """One expert's MXFP4 weights (codes + E8M0), drawn from the expert's own stream."""
     return (random_words(seed, cfg, T_Q, (K // 8, N), e),

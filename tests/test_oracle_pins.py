@@ -620,3 +620,49 @@ def test_gemm_fp8_blockwise_scale_indexing():
     got = oracle.gemm_fp8_blockwise(qa, sa, d["w"], sw2)
     assert np.array_equal(got[:, :128], base[:, :128])
     assert rel_err(got[:, 128:] - base[:, 128:], a[:, :128] @ w[:128, 128:]) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# FP4 weights with 16-bit activations: MXFP4 and NVFP4 (second-level scale)
+# ---------------------------------------------------------------------------
+
+def test_fp4_a16_mxfp4_equals_single_expert_moe():
+    """Dense MXFP4 with bf16 activations is the MoE oracle with one expert and top-1."""
+    M, N, K = 6, 48, 256
+    d = syn.w4a16_fp4(0, M, N, K, nvfp4=False)
+    got = oracle.gemm_fp4_a16(d["A"], d["q"], d["s"], N=N, K=K, a_bf16=True, nvfp4=False)
+    moe = oracle.moe_mxfp4_bf16(d["A"], np.zeros((M, 1), np.int32), d["q"][None], d["s"][None], N=N, K=K)
+    np.testing.assert_array_equal(got, moe)
+
+
+def test_fp4_a16_nvfp4_exact_rational_and_second_level_scale():
+    M, N, K = 2, 16, 64
+    d = syn.w4a16_fp4(1, M, N, K, nvfp4=True)
+    got = oracle.gemm_fp4_a16(d["A"], d["q"], d["s"], N=N, K=K, a_bf16=True, nvfp4=True, s2=d["s2"])
+    a = torch16(d["A"], torch.bfloat16)
+    codes = unpack_k(d["q"], K)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += (Fraction(float(a[m, k])) * Fraction(E2M1_TABLE[int(codes[k, n])])
+                        * Fraction(float(E4M3_LUT[d["s"][k // 16, n]])) * Fraction(float(np.float32(d["s2"]))))
+            assert abs(got[m, n] - float(acc)) <= 1e-13 * max(abs(float(acc)), 1e-30)
+    base = oracle.gemm_fp4_a16(d["A"], d["q"], d["s"], N=N, K=K, a_bf16=True, nvfp4=True)
+    np.testing.assert_allclose(got, base * np.float64(np.float32(d["s2"])), rtol=1e-15)
+
+
+def test_fp4_a16_nvfp4_group_of_16_indexing():
+    """Changing one 16-K group scale changes exactly that group's contribution of that column."""
+    M, N, K = 3, 32, 128
+    d = syn.w4a16_fp4(2, M, N, K, nvfp4=True)
+    base = oracle.gemm_fp4_a16(d["A"], d["q"], d["s"], N=N, K=K, a_bf16=False, nvfp4=True)
+    s = d["s"].copy()
+    s[5, 7] = 0x38                                            # E4M3 1.0 for K in [80, 96), column 7
+    got = oracle.gemm_fp4_a16(d["A"], d["q"], s, N=N, K=K, a_bf16=False, nvfp4=True)
+    cols = [c for c in range(N) if c != 7]
+    assert np.array_equal(got[:, cols], base[:, cols])
+    a = torch16(d["A"], torch.float16)
+    w = e2m1_tab(unpack_k(d["q"], K))[80:96, 7]
+    delta = a[:, 80:96] @ w * (1.0 - E4M3_LUT[d["s"][5, 7]])
+    assert rel_err(got[:, 7] - base[:, 7], delta) < 1e-12
