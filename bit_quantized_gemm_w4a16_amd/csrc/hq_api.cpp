@@ -69,7 +69,8 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         return set_error(HQ_ERR_INVALID_ARG, "N=%lld K=%lld out of range [1, 2^24]", (long long)d->N, (long long)d->K);
     if (d->num_experts < 0 || d->num_experts > 4096)
         return set_error(HQ_ERR_INVALID_ARG, "num_experts=%d out of range [0, 4096]", d->num_experts);
-    if (d->scale2 != HQ_S2_NONE) return set_error(HQ_ERR_UNSUPPORTED, "second-level scales are not supported");
+    if (d->scale2 != HQ_S2_NONE && d->scale2 != HQ_S2_PER_TENSOR_F32)
+        return set_error(HQ_ERR_INVALID_ARG, "bad scale2 kind %d", d->scale2);
     LayerInfo I{};
     I.N = d->N;
     I.K = d->K;
@@ -101,6 +102,22 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 takes no zero-points");
         if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 paths output bf16");
         I.G = 32;
+    } else if (w == HQ_DT_FP4_E2M1 && a == HQ_DT_BF16 && !d->num_experts) {
+        I.kind = Kind::FP4_A16;
+        I.nv = d->w_scale_dtype == HQ_DT_FP8_E4M3;
+        if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x FP4 takes no activation scale");
+        if (I.nv) {
+            if (d->w_scale_gran != HQ_GRAN_PER_GROUP_K || d->group_size != 16)
+                return set_error(HQ_ERR_UNSUPPORTED, "NVFP4 needs E4M3 scales per 16 K elements");
+            if (d->scale2 != HQ_S2_PER_TENSOR_F32)
+                return set_error(HQ_ERR_UNSUPPORTED, "NVFP4 needs a per-tensor fp32 second-level scale");
+        } else if (d->w_scale_dtype != HQ_DT_E8M0 || d->w_scale_gran != HQ_GRAN_PER_GROUP_K || d->group_size != 32) {
+            return set_error(HQ_ERR_UNSUPPORTED, "FP4 weights need E8M0 scales per 32 K (MXFP4) or E4M3 per 16 K (NVFP4)");
+        }
+        if (d->K % 128) return set_error(HQ_ERR_UNSUPPORTED, "FP4 weights need K %% 128 == 0 (K=%lld)", (long long)d->K);
+        if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "FP4 weights take no zero-points");
+        if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x FP4 outputs bf16");
+        I.G = I.nv ? 16 : 32;
     } else if (w == HQ_DT_FP4_E2M1 && (a == HQ_DT_FP8_E4M3 || a == HQ_DT_BF16)) {
         const bool moe = d->num_experts > 0;
         if (a == HQ_DT_FP8_E4M3) {
@@ -144,6 +161,8 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
     } else {
         return set_error(HQ_ERR_UNSUPPORTED, "unsupported activation/weight dtype pair (%d, %d)", a, w);
     }
+    if (d->scale2 != HQ_S2_NONE && !(I.kind == Kind::FP4_A16 && I.nv))
+        return set_error(HQ_ERR_UNSUPPORTED, "second-level scales are built for NVFP4 weights only");
     {
         // the kernels address one expert's packed tensors with 32-bit buffer offsets
         LayerInfo one = I;
@@ -170,6 +189,7 @@ static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
         case Kind::W8A8: return hip_status(w8a8_launch(a, L.out_i32), "hq_gemm(W8A8)");
         case Kind::MXA_MX: return hip_status(mx_act_launch(a, L.a_fp4), L.a_fp4 ? "hq_gemm(W4A4-MXFP4)" : "hq_gemm(W4A8-MXFP8xMXFP4)");
         case Kind::FP8_BLOCK: return hip_status(fp8_block_launch(a), "hq_gemm(FP8-blockwise)");
+        case Kind::FP4_A16: return hip_status(fp4_a16_launch(a, L.nv), L.nv ? "hq_gemm(NVFP4-A16)" : "hq_gemm(MXFP4-A16)");
         default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind runs through hq_moe_gemm");
     }
 }
@@ -296,8 +316,10 @@ hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale,
     const bool need_z = L.kind == Kind::WNA16 && L.zp;
     if (need_z && (!zp || !z_out)) return set_error(HQ_ERR_INVALID_ARG, "zero-points are required for UINT4 weights");
     if (!need_z && (zp || z_out)) return set_error(HQ_ERR_INVALID_ARG, "zero-point buffers must be NULL for this format");
-    if (scale2 || s2_out) return set_error(HQ_ERR_INVALID_ARG, "second-level scale buffers must be NULL");
-    repack_all(L, w, scale, zp, w_out, s_out, z_out);
+    const bool need_s2 = desc->scale2 != HQ_S2_NONE;
+    if (need_s2 && (!scale2 || !s2_out)) return set_error(HQ_ERR_INVALID_ARG, "second-level scale buffers are required");
+    if (!need_s2 && (scale2 || s2_out)) return set_error(HQ_ERR_INVALID_ARG, "second-level scale buffers must be NULL");
+    repack_all(L, w, scale, zp, scale2, w_out, s_out, z_out, s2_out);
     return ok();
 }
 
@@ -337,7 +359,9 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const voi
     if (need_z != (z != nullptr)) return set_error(HQ_ERR_INVALID_ARG, need_z ? "zero-points required" : "z must be NULL");
     const bool need_as = desc->a_scale != HQ_ASCALE_NONE;
     if (need_as != (a_scale != nullptr)) return set_error(HQ_ERR_INVALID_ARG, need_as ? "a_scale required" : "a_scale must be NULL");
-    if (s2) return set_error(HQ_ERR_INVALID_ARG, "s2 must be NULL");
+    const bool need_s2 = desc->scale2 != HQ_S2_NONE;
+    if (need_s2 != (s2 != nullptr)) return set_error(HQ_ERR_INVALID_ARG, need_s2 ? "s2 required" : "s2 must be NULL");
+    if (s2 && ((uintptr_t)s2 & 3u)) return set_error(HQ_ERR_ALIGNMENT, "s2 must be 4-byte aligned");
     if (!aligned16(A) || !aligned16(w) || !aligned16(s) || !aligned16(D) || (z && !aligned16(z)) ||
         (a_scale && !aligned16(a_scale)))
         return set_error(HQ_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
@@ -353,7 +377,7 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const voi
     const bool mx = desc->a_scale == HQ_ASCALE_MX_E8M0, blk = desc->a_scale == HQ_ASCALE_PER_BLOCK128_F32;
     DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, mx || blk ? nullptr : (const float*)a_scale,
                 mx ? (const uint8_t*)a_scale : nullptr, blk ? (const float*)a_scale : nullptr,
-                w, s, z, D, workspace, ws_bytes, (hipStream_t)stream};
+                w, s, z, (const float*)s2, D, workspace, ws_bytes, (hipStream_t)stream};
     return dense_launch(L, a);
 }
 

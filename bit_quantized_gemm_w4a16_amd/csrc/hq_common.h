@@ -18,6 +18,7 @@ enum class Kind {
     MOE_MX_BF16,  // MoE: bf16 A, e2m1 W, E8M0 per 32 K
     MXA_MX,       // MX activations (E4M3 or E2M1, E8M0 per 32 K) x e2m1 W, E8M0 per 32 K
     FP8_BLOCK,    // fp8-e4m3 A (fp32 per row and 128-K block) x fp8-e4m3 W (fp32 per 128 x 128 block)
+    FP4_A16,      // bf16 A, e2m1 W with E8M0 per 32 K (MXFP4) or E4M3 per 16 K + fp32 per tensor (NVFP4)
 };
 
 struct LayerInfo {
@@ -27,6 +28,7 @@ struct LayerInfo {
     bool zp;       // WNA16: UINT4 codes with UINT4 zero-points
     bool out_i32;  // W8A8: raw int32 accumulators
     bool a_fp4;    // MXA_MX: E2M1 activations (else E4M3)
+    bool nv;       // FP4_A16: NVFP4 (E4M3 per 16 K, per-tensor second-level scale), else MXFP4
 };
 
 // Validates a descriptor; fills `info` on success.  Sets the thread-local
@@ -34,8 +36,8 @@ struct LayerInfo {
 hq_status describe(const hq_layer_desc* d, LayerInfo* info);
 
 void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s2);
-void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z, void* w_out,
-                void* s_out, void* z_out);
+void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z, const void* s2, void* w_out,
+                void* s_out, void* z_out, void* s2_out);
 
 hq_status set_error(hq_status st, const char* fmt, ...);
 

@@ -41,6 +41,7 @@ struct DenseArgs {
     const void* w;
     const void* s;
     const void* z;
+    const float* s2;        // second-level weight scale (NVFP4), fp32 [1]
     void* D;
     void* ws;
     size_t ws_bytes;
@@ -55,6 +56,7 @@ hipError_t w4a8_launch(const DenseArgs& a);
 hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32);
 hipError_t mx_act_launch(const DenseArgs& a, bool fp4_act);  // MX activations x MXFP4 weights
 hipError_t fp8_block_launch(const DenseArgs& a);              // FP8 W8A8 with blockwise scales
+hipError_t fp4_a16_launch(const DenseArgs& a, bool nv);       // bf16 A x MXFP4 / NVFP4 weights
 
 // MoE
 struct MoeLayout {  // byte offsets into the MoE workspace

@@ -111,6 +111,24 @@ void repack_e8m0(const LayerInfo& L, const uint8_t* s, uint8_t* out) {
     }
 }
 
+// NVFP4 group scales (E4M3 per 16 K): [E][Np/16][K/128][64 lanes][2 bytes]; lane
+// l holds column 16*strip + (l & 15), groups 8*chunk + 2*(l >> 4) + {0, 1}
+// (the two 16-K halves of the lane's 32 K); padding columns hold 0x38 (1.0).
+void repack_e4m3_g16(const LayerInfo& L, const uint8_t* s, uint8_t* out) {
+    const int64_t N = L.N, nst = L.Np / 16, nc = L.K / 128, ng = L.K / 16;
+    for (int64_t e = 0; e < L.E; ++e) {
+        const uint8_t* se = s + e * ng * N;
+        uint8_t* oe = out + (size_t)e * (size_t)(nst * nc * 128);
+        for (int64_t st = 0; st < nst; ++st)
+            for (int64_t c = 0; c < nc; ++c)
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int64_t n = st * 16 + (lane & 15);
+                    for (int h = 0; h < 2; ++h)
+                        oe[((st * nc + c) * 64 + lane) * 2 + h] = n < N ? se[(8 * c + 2 * (lane >> 4) + h) * N + n] : (uint8_t)0x38;
+                }
+    }
+}
+
 void repack_chan32(const LayerInfo& L, const float* s, float* out) {
     for (int64_t e = 0; e < L.E; ++e)
         for (int64_t n = 0; n < L.Np; ++n) out[e * L.Np + n] = n < L.N ? s[e * L.N + n] : 1.0f;
@@ -137,6 +155,11 @@ void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s
             *w = E * nst * (size_t)(L.K / 64) * 1024;
             *s = E * (size_t)L.Np * 4;
             break;
+        case Kind::FP4_A16:
+            *w = E * nst * (size_t)(L.K / 128) * 1024;
+            *s = E * nst * (size_t)(L.K / 128) * (L.nv ? 128 : 64);
+            if (L.nv) *s2 = E * 4;
+            break;
         case Kind::FP8_BLOCK:
             *w = E * nst * (size_t)(L.K / 64) * 1024;
             *s = E * (size_t)(L.K / 128) * (size_t)((L.N + 127) / 128) * 4;
@@ -144,8 +167,8 @@ void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s
     }
 }
 
-void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z, void* w_out,
-                void* s_out, void* z_out) {
+void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z, const void* s2, void* w_out,
+                void* s_out, void* z_out, void* s2_out) {
     switch (L.kind) {
         case Kind::WNA16:
             repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, true);
@@ -161,6 +184,12 @@ void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z,
         case Kind::W8A8:
             repack_int8(L, (const int8_t*)w, (int8_t*)w_out);
             repack_chan32(L, (const float*)s, (float*)s_out);
+            break;
+        case Kind::FP4_A16:
+            repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, false);
+            if (L.nv) repack_e4m3_g16(L, (const uint8_t*)s, (uint8_t*)s_out);
+            else repack_e8m0(L, (const uint8_t*)s, (uint8_t*)s_out);
+            if (L.nv) std::memcpy(s2_out, s2, (size_t)L.E * 4);
             break;
         case Kind::FP8_BLOCK:
             // E4M3 codes take the INT8 byte layout (code 0 = +0 in the padding); the

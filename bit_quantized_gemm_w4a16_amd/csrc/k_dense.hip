@@ -12,6 +12,11 @@
 // with one E8M0 scale per 32 K per row, fed with the weights' E8M0 scales to
 // the same scaled MFMA; no epilogue scale.
 //
+// FP4 weights with bf16 activations (section "WnA16": FP4 among the weight
+// formats; NVFP4 with its second-level scale, section "Eine einheitliche
+// Quantisierungsdarstellung"): e2m1 codes converted to bf16 with the lane's
+// E8M0 or E4M3 group scale (exact), bf16 MFMA, the per-tensor scale on the output.
+//
 // FP8 W8A8 with blockwise scales (same section: the Hopper-era FP8 path with
 // blockwise scaling; "Humming v0.1.0-0.1.4" for the per-K-block activation
 // scale indexing): fp8 x fp8 on the scaled MFMA per 128-K block, the partial
@@ -36,6 +41,7 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
         s.a_scale = a.a_scale;
         s.a_e8 = a.a_e8;
         s.a_blk = a.a_blk;
+        s.s2 = a.s2;
         s.W = a.w;
         s.S = a.s;
         s.D = a.D;
@@ -55,6 +61,7 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
     p.a_scale = a.a_scale;
     p.a_e8 = a.a_e8;
     p.a_blk = a.a_blk;
+    p.s2 = a.s2;
     p.W = a.w;
     p.S = a.s;
     p.D = a.D;
@@ -78,6 +85,10 @@ hipError_t w4a8_launch(const DenseArgs& a) { return launch<Fmt::W4A8_MX>(a, 0); 
 hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32) { return launch<Fmt::W8A8_I8>(a, raw_i32 ? 1 : 0); }
 
 hipError_t fp8_block_launch(const DenseArgs& a) { return launch<Fmt::W8A8_F8B>(a, 0); }
+
+hipError_t fp4_a16_launch(const DenseArgs& a, bool nv) {
+    return nv ? launch<Fmt::NVFP4_BF16>(a, 0) : launch<Fmt::MXFP4_BF16>(a, 0);
+}
 
 hipError_t mx_act_launch(const DenseArgs& a, bool fp4_act) {
     return fp4_act ? launch<Fmt::W4A4_MX>(a, 0) : launch<Fmt::W4A8_MXA>(a, 0);

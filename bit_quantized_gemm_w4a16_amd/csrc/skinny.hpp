@@ -39,6 +39,10 @@
 //                   the A scale (MXFP8 activations; copied to LDS with the A slice)
 //   W4A4_MX         the same with fp4 e2m1 activations (MXFP4 x MXFP4)
 //   W8A8_I8         2 x v_mfma_i32_16x16x64_i8 (exact int32)
+//   MXFP4_BF16      4 x v_mfma_f32_16x16x32_bf16 on e2m1 x 2^(E-127) converted
+//                   to bf16 (exact) with the lane's E8M0 byte
+//   NVFP4_BF16      the same with the lane's two E4M3 group scales (16 K each)
+//                   and the per-tensor fp32 second-level scale on the output
 //   W8A8_F8B        1 x the scaled MFMA on fp8 x fp8 per chunk (one 128-K scale
 //                   block), its partial scaled by the row's activation block
 //                   scale times the strip's weight block scale (both in LDS)
@@ -56,6 +60,7 @@ struct SkinnyArgs {
     const float* a_scale;   // per-token fp32 (W4A8 / W8A8), by A row
     const uint8_t* a_e8;    // MX activation scales E8M0 [a_rows][K/32] (W4A8_MXA / W4A4_MX)
     const float* a_blk;     // activation scales per row and 128-K block [a_rows][K/128] (W8A8_F8B)
+    const float* s2;        // per-tensor second-level weight scale, fp32 [1] (NVFP4_BF16)
     const void* W;          // packed weights
     const void* S;          // packed group scales / E8M0 / per-channel fp32
     const void* Z;          // packed zero-points (WNA16 with UINT4), or null
@@ -76,6 +81,8 @@ struct SkinnyTraits {
     static constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
     static constexpr bool MX = mx_mfma(F);               // E8M0 weight scales per 32 K
     static constexpr bool MXA = mx_act(F);               // E8M0 activation scales per 32 K
+    static constexpr bool FP4B = F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16;  // e2m1 -> bf16 operands
+    static constexpr int SB = F == Fmt::NVFP4_BF16 ? 128 : 64;  // scale bytes per strip and chunk
     static constexpr int AROW = FmtTraits<F>::AROW;      // bytes of a row per 128-K chunk
     static constexpr int UPC = AROW / 16;                // 16-byte A units per 128-K chunk and row
     static constexpr int NB = FmtTraits<F>::BSTRIP / 1024;  // 16-byte weight loads per chunk and lane
@@ -95,7 +102,8 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     using Tr = SkinnyTraits<F>;
     using Acc = typename FmtTraits<F>::Acc;
     static_assert(F != Fmt::MOE_MX, "MoE experts stream through moe_stream_kernel");
-    constexpr bool WNA16 = Tr::WNA16, MX = Tr::MX, MXA = Tr::MXA;
+    constexpr bool WNA16 = Tr::WNA16, MX = Tr::MX, MXA = Tr::MXA, FP4B = Tr::FP4B;
+    constexpr int SB = Tr::SB;
     constexpr int AROW = Tr::AROW, UPC = Tr::UPC, NB = Tr::NB;
     constexpr int ROWS = 16 * MT;
     constexpr int NLOAD = SPW * CPW * NB;  // weight loads per wave and batch
@@ -192,13 +200,14 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     }
                 }
             }
-        } else if constexpr (MX) {
+        } else if constexpr (MX || FP4B) {
+            constexpr int UPS = SB / 16;  // 16-byte scale units per chunk and strip
             for (int j = 0; j < p.NS; ++j) {
                 const int st = strip_base + j < nstrips ? strip_base + j : nstrips - 1;
-                for (int pos0 = wave * 64; pos0 < nsl * 4; pos0 += 256) {  // 64 bytes per chunk
+                for (int pos0 = wave * 64; pos0 < nsl * UPS; pos0 += 256) {  // SB bytes per chunk
                     const int pos = pos0 + lane;
-                    if (pos < nsl * 4)
-                        lds_dma16((const char*)Sb + ((size_t)st * p.nc + c0) * 64 + pos * 16, lds + p.s_off + (j * nsl * 4 + pos0) * 16);
+                    if (pos < nsl * UPS)
+                        lds_dma16((const char*)Sb + ((size_t)st * p.nc + c0) * SB + pos * 16, lds + p.s_off + (j * nsl * UPS + pos0) * 16);
                 }
             }
             if constexpr (MXA) {
@@ -357,6 +366,29 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                         for (int mt = 0; mt < MT; ++mt) acc2[i & 1][sp][mt] += sc * (gacc[0][mt] + gacc[1][mt]);
                     }
                 }
+            } else if constexpr (FP4B) {
+                // e2m1 x (2^(E-127) or E4M3 group scale) -> exact bf16 operands, bf16 MFMA
+                const Frag8(&af)[MT][4] = afb[i & 1];
+#pragma unroll
+                for (int sp = 0; sp < SPW; ++sp) {
+                    const int j = ws * SPW + sp;
+                    float sf0, sf1;
+                    if constexpr (F == Fmt::NVFP4_BF16) {
+                        const uint32_t two = ((const uint16_t*)(lds + p.s_off))[((j * nsl + cl) * SB) / 2 + lane];
+                        sf0 = __builtin_amdgcn_cvt_f32_fp8((int)two, 0);
+                        sf1 = __builtin_amdgcn_cvt_f32_fp8((int)two, 1);
+                    } else {
+                        sf0 = sf1 = e8m0_to_f32(((const uint8_t*)(lds + p.s_off))[(j * nsl + cl) * SB + lane]);
+                    }
+                    if (!valid) sf0 = sf1 = 0.f;  // a chunk past the wave's part contributes exactly zero
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const Frag8 b = F == Fmt::NVFP4_BF16 ? fp4_to_bf16_mul(w[i][sp][0][t], t < 2 ? sf0 : sf1)
+                                                             : fp4_to_bf16(w[i][sp][0][t], sf0);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) acc2[t & 1][sp][mt] = mfma16<true>(af[mt][t], b, acc2[t & 1][sp][mt]);
+                    }
+                }
             } else if constexpr (MX) {
                 v8i af[MT];
                 int asc[MT];
@@ -500,6 +532,8 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     else ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)acc[sp][mt][r] * p.a_scale[m] * ((const float*)Sb)[n]);
                 } else if constexpr (F == Fmt::W4A8_MX) {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r] * p.a_scale[m]);
+                } else if constexpr (F == Fmt::NVFP4_BF16) {
+                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r] * *p.s2);
                 } else {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r]);
                 }
@@ -549,6 +583,8 @@ inline SkinnyLds skinny_lds(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) 
     } else if (mx_mfma(F)) {
         s = al(NS * cmax * 64);
         if (mx_act(F)) z = al(rows * cmax * 4);
+    } else if (F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16) {
+        s = al(NS * cmax * (F == Fmt::NVFP4_BF16 ? 128 : 64));
     } else if (F == Fmt::W8A8_F8B) {
         s = al(NS * cmax * 4);
         z = al(((rows + 15) / 16 * 16) * cmax * 4);
@@ -655,7 +691,7 @@ hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t s
     else if (pl.MT == 2) e = launch_skinny_cpw<F, 2, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
     else e = launch_skinny_cpw<F, 4, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
     if (e != hipSuccess || pl.splits == 1) return e;
-    return launch_finalize<F>(FinalizeArgs{s.part, s.D, s.a_scale, (const float*)s.S, s.M, s.N, s.Np, s.splits, s.raw_i32}, st);
+    return launch_finalize<F>(FinalizeArgs{s.part, s.D, s.a_scale, (const float*)s.S, s.s2, s.M, s.N, s.Np, s.splits, s.raw_i32}, st);
 }
 
 

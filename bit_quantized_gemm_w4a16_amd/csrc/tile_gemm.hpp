@@ -40,6 +40,10 @@
 //               to the fp32 accumulator
 //   W8A8_I8     int8 x int8 -> int32 (exact), per-token x per-channel epilogue
 //   MOE_MX      bf16 A x e2m1 B converted to bf16 with the E8M0 scale (exact)
+//   MXFP4_BF16  the same decode for dense layers (FP4 WnA16)
+//   NVFP4_BF16  bf16 A x e2m1 B with an E4M3 scale per 16 K (e2m1 x e4m3 has
+//               at most 5 significant bits: the product is exact in bf16) and
+//               the per-tensor fp32 second-level scale in the epilogue
 #pragma once
 
 #include <type_traits>
@@ -49,12 +53,13 @@
 
 namespace hq {
 
-enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B };
+enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B, MXFP4_BF16, NVFP4_BF16 };
 
 constexpr const char* fmt_name(Fmt F) {
     return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
          : F == Fmt::W8A8_I8 ? "W8A8_I8" : F == Fmt::MOE_MX ? "MOE_MX" : F == Fmt::W4A8_MXA ? "W4A8_MXA"
-         : F == Fmt::W4A4_MX ? "W4A4_MX" : "W8A8_F8B";
+         : F == Fmt::W4A4_MX ? "W4A4_MX" : F == Fmt::W8A8_F8B ? "W8A8_F8B" : F == Fmt::MXFP4_BF16 ? "MXFP4_BF16"
+         : "NVFP4_BF16";
 }
 // Formats whose activations carry OCP MX scales (E8M0 per 32 K, [rows][K/32]).
 constexpr bool mx_act(Fmt F) { return F == Fmt::W4A8_MXA || F == Fmt::W4A4_MX; }
@@ -72,6 +77,10 @@ template <> struct FmtTraits<Fmt::MOE_MX> { static constexpr int AROW = 256, BST
 template <> struct FmtTraits<Fmt::W4A8_MXA> { static constexpr int AROW = 128, BSTRIP = 1024; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::W4A4_MX> { static constexpr int AROW = 64, BSTRIP = 1024; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::W8A8_F8B> { static constexpr int AROW = 128, BSTRIP = 2048; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::MXFP4_BF16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::NVFP4_BF16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
+// e2m1 weights converted to bf16 operands with a per-lane scale (bf16 MFMA)
+constexpr bool fp4_bf16(Fmt F) { return F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16; }
 
 // Work description of one launch.  Dense launches leave the MoE fields null.
 struct TileArgs {
@@ -79,6 +88,7 @@ struct TileArgs {
     const float* a_scale;   // per-token fp32 (W4A8 / W8A8), indexed by A row
     const uint8_t* a_e8;    // MX activation scales, E8M0 [rows][K/32] (W4A8_MXA / W4A4_MX)
     const float* a_blk;     // fp32 activation scales per row and 128-K block [rows][K/128] (W8A8_F8B)
+    const float* s2;        // second-level weight scale, fp32 [1] per tensor (NVFP4_BF16)
     const void* W;          // packed weights (expert 0)
     const void* S;          // packed scales (expert 0)
     const void* Z;          // packed zero-points (WNA16 + UINT4)
@@ -160,6 +170,21 @@ __device__ __forceinline__ Frag8 fp4_to_bf16(uint32_t w, float scale) {
     return f;
 }
 
+// e2m1 x s -> bf16 for a scale s that is not a power of two (an E4M3 group
+// scale): the scaled convert applies only the exponent of its scale operand, so
+// the codes are converted unscaled (exact) and each value is multiplied by s
+// in fp32; e2m1 x e4m3 has at most 5 significant bits, so the RNE conversion
+// back to bf16 is exact.
+__device__ __forceinline__ Frag8 fp4_to_bf16_mul(uint32_t w, float s) {
+    Frag8 f = fp4_to_bf16(w, 1.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(f.u[i] << 16) * s, hi = __uint_as_float(f.u[i] & 0xFFFF0000u) * s;
+        f.u[i] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    }
+    return f;
+}
+
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     e &= 0xFFu;
     return __uint_as_float(e == 0 ? 0x00400000u : e == 255u ? 0x7FC00000u : (e << 23));
@@ -200,7 +225,8 @@ void tile_gemm_kernel(TileArgs p) {
     using T = FmtTraits<F>;
     using Acc = typename T::Acc;
     constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
-    constexpr bool MX = mx_mfma(F) || F == Fmt::MOE_MX;  // E8M0 weight scales per 32 K
+    constexpr bool NV = F == Fmt::NVFP4_BF16;             // E4M3 weight scales per 16 K
+    constexpr bool MX = mx_mfma(F) || F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || NV;  // byte scales per lane
     constexpr bool MXA = mx_act(F);
     constexpr bool F8B = F == Fmt::W8A8_F8B;
     static_assert(!F8B || BN == 128, "blockwise fp8: one 128-column weight block per tile");
@@ -213,7 +239,7 @@ void tile_gemm_kernel(TileArgs p) {
     // per-step scale block: WNA16 16 fp16 scales + one zero-point word per strip;
     // MXFP4 one E8M0 byte per lane per strip; INT8 none (per-channel, epilogue)
     constexpr int SC_Z = NSTRIP * 32;                     // zero-point words start (WNA16)
-    constexpr int SC_B = WNA16 ? NSTRIP * 48 : MX ? NSTRIP * 64 : 0;
+    constexpr int SC_B = WNA16 ? NSTRIP * 48 : NV ? NSTRIP * 128 : MX ? NSTRIP * 64 : 0;
     // MX activations: one E8M0 word (4 K blocks) per row; blockwise fp8: one fp32
     // activation scale per row, then the tile's weight block scale
     constexpr int SC_STAGE = SC_B + (MXA ? BM * 4 : 0) + (F8B ? BM * 4 + 16 : 0);
@@ -232,7 +258,7 @@ void tile_gemm_kernel(TileArgs p) {
     constexpr int NIB = B_STAGE / 16 / NTH;  // (B)
     constexpr int MT = BM / WM / 16, NT = BN / WN / 16;  // 16x16 tiles per wave
     static_assert(A_STAGE % (16 * NTH) == 0 && B_STAGE % (16 * NTH) == 0, "stage must split evenly over threads");
-    static_assert(SC_UNITS <= 64, "scale units are fetched by wave 0");
+    static_assert(SC_UNITS <= NTH, "one 16-byte scale unit per fetching thread");
     static_assert(NTH >= 128, "zero-point words are fetched by wave 1");
 
     // Two LDS stages as distinct objects: the compiler can then tell a direct
@@ -308,7 +334,7 @@ void tile_gemm_kernel(TileArgs p) {
                      : make_rsrc(p.a_blk, F8B ? (uint32_t)p.a_rows * (uint32_t)(K / 128) * 4u : 0u);
     const rsrc_t rW = make_rsrc(Wbase, nstr * (uint32_t)nsteps * T::BSTRIP);
     const uint32_t nbn = (uint32_t)((p.Np + 127) / 128);  // weight column blocks (blockwise fp8)
-    const rsrc_t rS = make_rsrc(Sbase, WNA16 ? nstr * (uint32_t)p.ngroups * 32u : MX ? nstr * (uint32_t)nsteps * 64u
+    const rsrc_t rS = make_rsrc(Sbase, WNA16 ? nstr * (uint32_t)p.ngroups * 32u : MX ? nstr * (uint32_t)nsteps * (NV ? 128u : 64u)
                                        : F8B ? (uint32_t)nsteps * nbn * 4u : 0u);
     const rsrc_t rZ = make_rsrc(p.Z, WNA16 && p.Z ? nstr * (uint32_t)p.ngroups * 8u : 0u);
 
@@ -338,9 +364,13 @@ void tile_gemm_kernel(TileArgs p) {
     static_assert(NTH % UPS == 0, "a load instruction covers whole strips");
     const uint32_t boff0 = (uint32_t)(strip0 + tid / UPS) * (uint32_t)nsteps * T::BSTRIP + (uint32_t)(tid % UPS) * 16u;
     const uint32_t bstride = (uint32_t)(NTH / UPS) * (uint32_t)nsteps * T::BSTRIP;
-    const uint32_t sc_strip = (uint32_t)clamp_strip(strip0 + (WNA16 ? (tid < 2 * NSTRIP ? tid / 2 : tid - 2 * NSTRIP) : tid / 4));
+    // scale block fetchers: 16 bytes per thread; MXFP4 4 threads per strip (64 B),
+    // NVFP4 8 threads per strip (128 B: two E4M3 bytes per lane)
+    constexpr int SPT = NV ? 8 : 4;
+    constexpr uint32_t SBYTES = NV ? 128u : 64u;  // scale bytes per strip and step
+    const uint32_t sc_strip = (uint32_t)clamp_strip(strip0 + (WNA16 ? (tid < 2 * NSTRIP ? tid / 2 : tid - 2 * NSTRIP) : tid / SPT));
     const uint32_t soff = WNA16 ? (tid < 2 * NSTRIP ? sc_strip * p.ngroups * 32u + (tid & 1) * 16u : sc_strip * p.ngroups * 8u)
-                                : sc_strip * (uint32_t)nsteps * 64u + (tid & 3) * 16u;
+                                : sc_strip * (uint32_t)nsteps * SBYTES + (tid % SPT) * 16u;
 
     auto stage_lds = [&](auto stc) -> lds_char* {
         constexpr int S = decltype(stc)::value;
@@ -408,7 +438,7 @@ void tile_gemm_kernel(TileArgs p) {
                 rs[st][1] = (uint32_t)(z >> 32);
             }
         } else if constexpr (MX) {
-            if (tid < SC_UNITS) rs[st] = buf16(rS, soff, (uint32_t)ks * 64u);
+            if (tid < SC_UNITS) rs[st] = buf16(rS, soff, (uint32_t)ks * SBYTES);
             // rows past M fall outside the buffer resource and read zeros (outputs dropped)
             if constexpr (MXA)
                 if (tid < BM) rsa[st] = buf4(rAS, as_voff, (uint32_t)ks * 4u);
@@ -488,20 +518,25 @@ void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
             for (int h = 0; h < NBH; ++h) bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
 
-        if constexpr (F == Fmt::WNA16_F16 || F == Fmt::MOE_MX) {
+        if constexpr (F == Fmt::WNA16_F16 || fp4_bf16(F)) {
             // 16-bit A with 4-bit weights decoded into the operand: fp16 (q - z) * s,
-            // or MXFP4 e2m1 x 2^(E-127) -> bf16 (exact)
-            constexpr bool MOE = F == Fmt::MOE_MX;
+            // or e2m1 x (2^(E-127) or an E4M3 value) -> bf16 (exact)
+            constexpr bool MOE = fp4_bf16(F);
             // A fragments read ahead (software pipeline): a whole sub-step, or
             // a ring of three for tall / wide wave tiles
             Frag8 afr[(NT >= 4 || MT > 8) ? 1 : 2][(NT >= 4 || MT > 8) ? 3 : MT];
             Frag8 bq[2][NT];                  // decoded weights of two sub-steps
             uint32_t s2[NT], nb2[NT], nh2[NT];
-            float sf[NT];
+            float sf[NT][NV ? 2 : 1];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                if constexpr (MOE) {
-                    sf[j] = e8m0_to_f32(((const uint8_t*)sS)[(wn * NT + j) * 64 + lane]);
+                if constexpr (NV) {
+                    // this lane's 16-K groups 2 quad and 2 quad + 1 of the step (sub-steps 0-1, 2-3)
+                    const uint32_t two = *(const uint16_t*)(sS + (wn * NT + j) * 128 + lane * 2);
+                    sf[j][0] = __builtin_amdgcn_cvt_f32_fp8((int)two, 0);
+                    sf[j][1] = __builtin_amdgcn_cvt_f32_fp8((int)two, 1);
+                } else if constexpr (MOE) {
+                    sf[j][0] = e8m0_to_f32(((const uint8_t*)sS)[(wn * NT + j) * 64 + lane]);
                 } else {
                     // one lane offset for every strip (strips are immediate offsets); the
                     // zero-point select is branch-free (symmetric INT4: z = 8)
@@ -516,7 +551,8 @@ void tile_gemm_kernel(TileArgs p) {
             }
             // weight operand of strip j for K sub-step t
             auto mkb = [&](int j, int tt) -> Frag8 {
-                if constexpr (MOE) return fp4_to_bf16(bw[j][0][tt], sf[j]);
+                if constexpr (NV) return fp4_to_bf16_mul(bw[j][0][tt], sf[j][tt >> 1]);
+                else if constexpr (MOE) return fp4_to_bf16(bw[j][0][tt], sf[j][0]);
                 else return deq4_f16_scaled(bw[j][0][tt] ^ wx, nb2[j], nh2[j], s2[j]);
             };
 #pragma unroll
@@ -881,6 +917,8 @@ void tile_gemm_kernel(TileArgs p) {
                     else ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)acc[i][j][r] * as * ((const float*)Sbase)[n]);
                 } else if constexpr (F == Fmt::W4A8_MX) {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r] * as);
+                } else if constexpr (F == Fmt::NVFP4_BF16) {
+                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r] * *p.s2);
                 } else {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r]);
                 }
@@ -897,6 +935,7 @@ struct FinalizeArgs {
     void* D;
     const float* a_scale;  // per-token scale (W4A8 / W8A8)
     const float* s_w;      // per-channel scale (W8A8)
+    const float* s2;       // per-tensor second-level scale (NVFP4)
     int M, N, Np, splits, raw_i32;
 };
 
@@ -930,6 +969,7 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(FinalizeArgs p) {
         }
     } else {
         if constexpr (F == Fmt::W4A8_MX) acc *= p.a_scale[m];
+        if constexpr (F == Fmt::NVFP4_BF16) acc *= *p.s2;
         constexpr bool BF = F != Fmt::WNA16_F16;
         for (int j = 0; j < cnt; ++j) ((uint16_t*)p.D)[o + j] = f32_to_16<BF>(acc[j]);
     }
@@ -999,7 +1039,7 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     if (p.splits == 1) return hipSuccess;
-    return launch_finalize<F>(FinalizeArgs{p.part, p.D, p.a_scale, (const float*)p.S, p.M, p.N, p.Np, p.splits, p.raw_i32}, st);
+    return launch_finalize<F>(FinalizeArgs{p.part, p.D, p.a_scale, (const float*)p.S, p.s2, p.M, p.N, p.Np, p.splits, p.raw_i32}, st);
 }
 
 // Formats with a 256-row tile.  4-bit weights with 16-bit A: 256 x 128 on 8
@@ -1014,11 +1054,11 @@ constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16; }
 // stage (each dequantised fragment feeds 16 MFMAs; 13 % faster than 128 x 256
 // at M = 8192), or 128 x 256 tiles of 128 x 32 waves where 256 x 256 would not
 // cover the chip (a K step loads 48 KB instead of the 80 KB of 256 x 128).
-constexpr bool has_wide_tile(Fmt F) { return F == Fmt::WNA16_F16; }
+constexpr bool has_wide_tile(Fmt F) { return F == Fmt::WNA16_F16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16; }
 // INT8: 256 x 256 on 8 waves of 128 x 64, direct loads into two full stages
 // (M = 8192: 1126 us vs 1569 us for 256 x 128 with register-staged loads); the
 // 256 x 128 tile also loads directly (1498 us).
-constexpr bool has_wide256_tile(Fmt F) { return F == Fmt::WNA16_F16 || F == Fmt::W8A8_I8; }
+constexpr bool has_wide256_tile(Fmt F) { return has_wide_tile(F) || F == Fmt::W8A8_I8; }
 // 256x256 tiles from this many on: INT8 keeps the 256x128 three-stage ring
 // until the wide tiles fill two rounds of the chip (measured: the ring is
 // faster at M=1024 and level at M=2048 for N=18432, K=7168)

@@ -25,7 +25,7 @@ HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_ALIGNMENT, HQ_ERR_WORKSPAC
  HQ_DT_FP4_E2M1, HQ_DT_E8M0, HQ_DT_INT32) = range(11)
 HQ_GRAN_NONE, HQ_GRAN_PER_GROUP_K, HQ_GRAN_PER_CHANNEL, HQ_GRAN_BLOCK_128x128 = range(4)
 HQ_ASCALE_NONE, HQ_ASCALE_PER_TOKEN_F32, HQ_ASCALE_MX_E8M0, HQ_ASCALE_PER_BLOCK128_F32 = range(4)
-HQ_S2_NONE = 0
+HQ_S2_NONE, HQ_S2_PER_TENSOR_F32 = 0, 1
 HQ_MOE_INDEXED, HQ_MOE_GROUPED = 1, 2
 
 
@@ -153,6 +153,16 @@ def desc_fp8_blockwise(N, K) -> hq_layer_desc:
                      a_scale=HQ_ASCALE_PER_BLOCK128_F32)
 
 
+def desc_fp4_a16(N, K, nvfp4: bool) -> hq_layer_desc:
+    """bf16 activations x FP4 (e2m1) weights: MXFP4 (E8M0 per 32 K) or NVFP4 (E4M3 per
+    16 K and a per-tensor fp32 second-level scale)."""
+    d = make_desc(N, K, HQ_DT_BF16, HQ_DT_FP4_E2M1, HQ_DT_FP8_E4M3 if nvfp4 else HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K,
+                  16 if nvfp4 else 32, HQ_DT_BF16)
+    if nvfp4:
+        d.scale2 = HQ_S2_PER_TENSOR_F32
+    return d
+
+
 def desc_w8a8(N, K, raw_int32=False) -> hq_layer_desc:
     return make_desc(N, K, HQ_DT_INT8, HQ_DT_INT8, HQ_DT_FP32, HQ_GRAN_PER_CHANNEL, K,
                      HQ_DT_INT32 if raw_int32 else HQ_DT_BF16, a_scale=HQ_ASCALE_PER_TOKEN_F32)
@@ -178,18 +188,21 @@ def hq_repacked_bytes(desc: hq_layer_desc):
     return w.value, s.value, z.value, s2.value
 
 
-def hq_repack(desc: hq_layer_desc, w: np.ndarray, scale: np.ndarray, zp: np.ndarray | None = None):
-    """Host repack; returns the packed (w, s, z) as uint8 numpy arrays (z None if unused)."""
-    wb, sb, zb, _ = hq_repacked_bytes(desc)
+def hq_repack(desc: hq_layer_desc, w: np.ndarray, scale: np.ndarray, zp: np.ndarray | None = None, scale2=None):
+    """Host repack; returns the packed (w, s, z) as uint8 numpy arrays (z None if unused),
+    plus the packed second-level scale as a fourth item when `scale2` is given."""
+    wb, sb, zb, s2b = hq_repacked_bytes(desc)
     w = np.ascontiguousarray(w)
     scale = np.ascontiguousarray(scale)
     zp = None if zp is None else np.ascontiguousarray(zp)
+    s2 = None if scale2 is None else np.ascontiguousarray(np.atleast_1d(np.asarray(scale2, dtype=np.float32)))
     wo = np.empty(wb, dtype=np.uint8)
     so = np.empty(sb, dtype=np.uint8)
     zo = np.empty(zb, dtype=np.uint8) if zb else None
-    _check(lib().hq_repack(C.byref(desc), _dp(w), _dp(scale), _dp(zp), None, _dp(wo), _dp(so), _dp(zo), None),
+    s2o = np.empty(s2b, dtype=np.uint8) if s2b else None
+    _check(lib().hq_repack(C.byref(desc), _dp(w), _dp(scale), _dp(zp), _dp(s2), _dp(wo), _dp(so), _dp(zo), _dp(s2o)),
            "hq_repack")
-    return wo, so, zo
+    return (wo, so, zo) if scale2 is None else (wo, so, zo, s2o)
 
 
 def hq_workspace_bytes(desc: hq_layer_desc, M_or_T: int, top_k: int = 0) -> int:
@@ -202,8 +215,8 @@ def hq_workspace_init(workspace, nbytes: int, stream=None) -> None:
     _check(lib().hq_workspace_init(_dp(workspace), nbytes, _stream(stream)), "hq_workspace_init")
 
 
-def hq_gemm(desc, M, A, a_scale, w, s, z, D, workspace=None, ws_bytes=0, stream=None) -> None:
-    _check(lib().hq_gemm(C.byref(desc), M, _dp(A), _dp(a_scale), _dp(w), _dp(s), _dp(z), None, _dp(D),
+def hq_gemm(desc, M, A, a_scale, w, s, z, D, workspace=None, ws_bytes=0, stream=None, s2=None) -> None:
+    _check(lib().hq_gemm(C.byref(desc), M, _dp(A), _dp(a_scale), _dp(w), _dp(s), _dp(z), _dp(s2), _dp(D),
                          _dp(workspace), ws_bytes, _stream(stream)), "hq_gemm")
 
 

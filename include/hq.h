@@ -98,7 +98,8 @@ typedef enum hq_ascale {
 } hq_ascale;
 
 typedef enum hq_scale2 {
-    HQ_S2_NONE = 0 /* second-level scales: slot kept in the ABI, no kernel uses one yet */
+    HQ_S2_NONE = 0,
+    HQ_S2_PER_TENSOR_F32 = 1 /* one fp32 multiplier of the whole weight tensor (per expert) */
 } hq_scale2;
 
 typedef enum hq_moe_mode {
@@ -120,6 +121,9 @@ typedef enum hq_moe_mode {
  *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    MX_E8M0   BF16   (MXFP8 x MXFP4)
  *   FP4_E2M1  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    MX_E8M0   BF16   (W4A4 MXFP4)
  *   FP8_E4M3  FP8_E4M3   FP32, BLOCK_128x128           NONE    PER_BLOCK128 BF16 (FP8 blockwise)
+ *   BF16      FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (FP4 WnA16, MXFP4)
+ *   BF16      FP4_E2M1   FP8_E4M3, PER_GROUP_K, grp 16 NONE    NONE      BF16   (NVFP4; scale2
+ *                                                                               PER_TENSOR_F32)
  *   BF16      FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MoE)
  * FP4_E2M1 activations are packed two per byte along K, element k in the low
  * nibble of byte k/2 when k is even (rows of K/2 bytes).
@@ -179,7 +183,7 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *          PER_CHANNEL fp32: [N]; BLOCK_128x128 fp32: [K/128][ceil(N/128)]
  *   zp     UINT4: uint32 [K/group][ceil(N/8)]; column n = 8j+i in bits
  *          4i..4i+3 of word [g][j]
- *   scale2 must be NULL (no second-level scale kernels yet)
+ *   scale2 PER_TENSOR_F32: fp32 [E] (one per expert); otherwise NULL
  *
  * Packed outputs (N padded to Np = ceil(N/16)*16; padding decodes to 0 with
  * unit scale).  A "strip" is 16 consecutive columns; a lane is one of the 64
@@ -196,8 +200,12 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *          E8M0: [E][Np/16][K/128][64 lanes] bytes; lane l holds the
  *          exponent of column 16*strip + (l & 15), K-block 4*chunk + (l >> 4)
  *          (padding columns hold 127);
+ *          E4M3 per 16 K (NVFP4): [E][Np/16][K/128][64 lanes][2] bytes; lane l
+ *          holds column 16*strip + (l & 15), groups 8*chunk + 2*(l >> 4) + h
+ *          (padding columns hold 0x38 = 1.0);
  *          PER_CHANNEL fp32: [Np]; BLOCK_128x128 fp32: unchanged [K/128][ceil(N/128)]
  *   zp     [E][Np/16][K/group] uint64, column 16*strip + i in bits 4i..4i+3
+ *   scale2 fp32 [E], copied
  */
 hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale, const void* zp,
                     const void* scale2, void* w_out, void* s_out, void* z_out, void* s2_out);
@@ -227,7 +235,7 @@ hq_status hq_workspace_init(void* workspace, size_t bytes, hq_stream_t stream);
  *   a_scale  device; PER_TOKEN_F32: fp32 [M]; MX_E8M0: uint8 [M][K/32]
  *            (E8M0 of row m, K block b); PER_BLOCK128_F32: fp32 [M][K/128];
  *            NONE: NULL
- *   w, s, z, s2  device, packed by hq_repack (unused ones NULL)
+ *   w, s, z, s2  device, packed by hq_repack (unused ones NULL; s2 4-byte aligned)
  *   D        device, [M][N] row-major, out_dtype
  * Floating outputs: fp32 accumulation, rounded once (RNE) to out_dtype.
  * M == 0 returns HQ_OK without launching.

@@ -65,6 +65,12 @@ FP8B_TILES = [(1100, 7200, 384), (600, 4000, 1280), (2100, 16400, 256)]
 FP8B_SWEEP = [(M, 7168, 7168) for M in SWEEP]
 
 
+# ---- FP4 weights with bf16 activations (MXFP4 / NVFP4): (M, N, K) ----
+FP4A16_SMALL = [(M, 272, 1024) for M in (1, 3, 16, 24, 33, 64, 100, 300)] + [(M, 304, 7168) for M in (1, 20)]
+FP4A16_TILES = [(2000, 4100, 384), (4000, 4100, 512), (1100, 16000, 256)]
+FP4A16_SWEEP = [(M, C2["N"], C2["K"]) for M in SWEEP]
+
+
 def all_dense_cases():
     """(format, M, N, K, G, flags) for every dense GPU case, flags a dict."""
     out = []
@@ -82,4 +88,7 @@ def all_dense_cases():
             out.append(("mxa", M, N, K, 32, dict(elem=elem)))
     for M, N, K in FP8B_SMALL + FP8B_TILES + FP8B_SWEEP:
         out.append(("fp8b", M, N, K, 128, {}))
+    for kind in ("mxfp4", "nvfp4"):
+        for M, N, K in FP4A16_SMALL + FP4A16_TILES + FP4A16_SWEEP:
+            out.append(("fp4a16", M, N, K, 16 if kind == "nvfp4" else 32, dict(kind=kind)))
     return out

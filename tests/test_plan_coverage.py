@@ -24,6 +24,8 @@ def desc_of(fmt, N, K, G, flags):
         return hq.desc_mx_act_mxfp4(N, K, fp4_act=flags["elem"] == "e2m1")
     if fmt == "fp8b":
         return hq.desc_fp8_blockwise(N, K)
+    if fmt == "fp4a16":
+        return hq.desc_fp4_a16(N, K, nvfp4=flags["kind"] == "nvfp4")
     return hq.desc_w8a8(N, K, raw_int32=flags["raw"])
 
 
@@ -53,6 +55,8 @@ BENCH = {
     "w4a4": ("mxa", cases.C3["N"], cases.C3["K"], 32, dict(elem="e2m1")),
     "w4a8mx": ("mxa", cases.C3["N"], cases.C3["K"], 32, dict(elem="e4m3")),
     "fp8b": ("fp8b", 7168, 7168, 128, {}),
+    "mxfp4a16": ("fp4a16", 4096, 7168, 32, dict(kind="mxfp4")),
+    "nvfp4a16": ("fp4a16", 4096, 7168, 16, dict(kind="nvfp4")),
 }
 
 
