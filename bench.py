@@ -3,13 +3,15 @@
 
 A step is one pass of the hot path over the workload's M sweep: for every
 M in {1, 2, 4, ..., 8192} one library call (host dispatch -> HIP kernels ->
-output) on inputs already resident in HBM.  The default workload is the
+output) on inputs already resident in HBM.  The headline workload is the
 dense W4A16 asymmetric layer (fp16 activations, UINT4 weights with UINT4
 zero-points and fp16 scales per 128 K, N=4096, K=7168), the configuration
-the metric is quoted on.  --config c1|c3|c4|c5|c5g|c5l|all measures the other
-workloads (one JSON line each); c5 is the MoE gate-up on the Indexed path, c5g
-the same on the Grouped path, c5l the whole MoE layer the pages time (gate-up
-GEMM, SwiGLU, down-projection GEMM).
+the metric is quoted on; its line also carries, under "configs", the same
+measurement of every other workload (dense W4A8-MXFP4, W8A8-INT8, the MoE
+gate-up on the Indexed path with its routing timed apart, W4A4 MXFP4 x MXFP4,
+MXFP8 x MXFP4, FP8 W8A8 with blockwise scales, bf16 x MXFP4 and NVFP4 WnA16).
+--config NAME measures one workload alone (c5g: the MoE Grouped path, c5l:
+the whole MoE layer the pages time, gate-up + SwiGLU + down).
 
 Cold cache: the packed weights are replicated into enough device copies
 (> 512 MiB in total, more than the 256 MiB Infinity Cache plus every L2) and
@@ -19,10 +21,11 @@ HBM, as in the pages' cold-L2 protocol ("Humming wird angekuendigt", section
 
 Timing: the calls are captured into HIP graphs, so host launch overhead does
 not starve the GPU.  Per M: a graph of back-to-back calls (one per weight
-copy) is replayed between HIP events on the capturing stream.  Per step: a
-graph of the whole sweep is replayed, K replays bracketed by
-torch.cuda.synchronize(); `value` = total algorithmic flops of one step /
-step wall time.
+copy) is replayed several times, each replay between HIP events on the
+capturing stream; per-call time = replay time / calls, reported as the median
+with p10 / p90 over the replays.  Per step: a graph of the whole sweep is
+replayed, K replays bracketed by torch.cuda.synchronize(); `value` = total
+algorithmic flops of one step / step wall time.
 """
 from __future__ import annotations
 
@@ -43,7 +46,7 @@ import synthetic as syn  # noqa: E402
 from bit_quantized_gemm_w4a16_amd import hq  # noqa: E402
 
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
-PEAK = {"fp16": 2.5e15, "bf16": 2.5e15, "fp8": 5.0e15, "int8": 5.0e15}
+PEAK = {"fp16": 2.5e15, "bf16": 2.5e15, "fp8": 5.0e15, "int8": 5.0e15, "fp4": 10.1e15}
 SWEEP = [1 << i for i in range(14)]
 COLD_BYTES = 512 << 20
 METRIC = "quant GEMM TFLOP/s + HBM GB/s vs roofline, M=1..8192, W4A16/W4A8/MoE"
@@ -119,9 +122,9 @@ class DenseW4A16:
             return (f"skinny_kernel<WNA16_{self.dtype.upper()}> (M<=64)", "hbm")
         return (f"tile_gemm_kernel<WNA16_{self.dtype.upper()}> (M>64)", "mfma" if M >= 128 else "hbm")
 
-    def call(self, M, c):
+    def call(self, M, c, desc=None):
         w, s, z = self.copies[c]
-        hq.hq_gemm(self.desc, M, self.A, None, w, s, z, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
+        hq.hq_gemm(desc or self.desc, M, self.A, None, w, s, z, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
 
     def cpu_baseline(self, budget_s=16.0):
         import oracle
@@ -168,9 +171,10 @@ class DenseW4A8:
             return ("skinny_kernel<W4A8_MX> (M<=64)", "hbm")
         return ("tile_gemm_kernel<W4A8_MX> (M>64)", "mfma" if M >= 256 else "hbm")
 
-    def call(self, M, c):
+    def call(self, M, c, desc=None):
         w, e = self.copies[c]
-        hq.hq_gemm(self.desc, M, self.A, self.s_a, w, e, None, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
+        hq.hq_gemm(desc or self.desc, M, self.A, self.s_a, w, e, None, self.D, self.ws if self.ws_bytes else None,
+                   self.ws_bytes)
 
     def aux(self, reps=20):
         """The activation quantisation before the GEMM (outside the timed
@@ -239,9 +243,10 @@ class DenseW8A8:
             return ("skinny_kernel<W8A8_I8> (M<=64)", "hbm")
         return ("tile_gemm_kernel<W8A8_I8> (M>64)", "mfma" if M >= 512 else "hbm")
 
-    def call(self, M, c):
+    def call(self, M, c, desc=None):
         w, s = self.copies[c]
-        hq.hq_gemm(self.desc, M, self.A, self.s_a, w, s, None, self.D, self.ws if self.ws_bytes else None, self.ws_bytes)
+        hq.hq_gemm(desc or self.desc, M, self.A, self.s_a, w, s, None, self.D, self.ws if self.ws_bytes else None,
+                   self.ws_bytes)
 
     def cpu_baseline(self, budget_s=16.0):
         import oracle
@@ -292,6 +297,24 @@ class MoEMXFP4:
         w, e = self.copies[c]
         hq.hq_moe_gemm(self.desc, hq.HQ_MOE_INDEXED, T, self.top_k, self.A, None, self.ids, None, w, e, None, self.D,
                        self.ws, self.ws_bytes)
+
+    def routing_us(self, T):
+        """Median time of the routing step alone at T tokens (hq_moe_align: expert
+        counts, offsets and the pairs sorted by expert), which an Indexed call runs
+        before its expert GEMM -- except at T * top_k <= 64, where the streaming
+        kernel routes by itself (reported as 0)."""
+        P = T * self.top_k
+        if P <= 64:
+            return 0.0
+        offs = torch.empty(self.E + 4, dtype=torch.int32, device="cuda")
+        srt = torch.empty(max(P, 4), dtype=torch.int32, device="cuda")
+        nb = hq.hq_workspace_bytes(self.desc, T, self.top_k)
+        ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+
+        def calls():
+            for _ in range(16):
+                hq.hq_moe_align(T, self.top_k, self.E, self.ids, offs, srt, ws, nb)
+        return round(statistics.median(_graph_times(calls, 16, reps=3)) * 1e6, 2)
 
     def cpu_baseline(self, budget_s=16.0):
         import oracle
@@ -388,6 +411,161 @@ class MoELayerMXFP4(MoEMXFP4):
         return b
 
 
+class DenseMXAct:
+    """MX activations (OCP MX: E8M0 per 32 K; E2M1 for W4A4, E4M3 for MXFP8) x MXFP4
+    weights, N=7168, K=4096 (the W4A8 layer's shape); activations quantised on the
+    GPU once, untimed."""
+
+    def __init__(self, fp4_act: bool, N=7168, K=4096, Mmax=8192, sweep=SWEEP):
+        self.N, self.K, self.Mmax, self.sweep, self.fp4 = N, K, Mmax, sweep, fp4_act
+        self.dtype = "fp4" if fp4_act else "fp8"
+        self.name = f"dense_{'w4a4_mxfp4' if fp4_act else 'w4a8_mxfp8_mxfp4'}_N{N}_K{K}"
+        log(f"[bench] generating {self.name}")
+        d = syn.w4a8_mxfp4(0, Mmax, N, K)
+        self.host = d
+        self.desc = hq.desc_mx_act_mxfp4(N, K, fp4_act=fp4_act)
+        wp, ep, _ = hq.hq_repack(self.desc, d["q"], d["e"])
+        self.wbytes = wp.size + ep.size
+        self.copies = _copies((dev(wp), dev(ep)), self.wbytes)
+        x = dev(d["A0"])
+        self.abytes = K // 2 if fp4_act else K
+        self.A = torch.empty(Mmax * self.abytes, dtype=torch.uint8, device="cuda")
+        self.e = torch.empty(Mmax * K // 32, dtype=torch.uint8, device="cuda")
+        hq.hq_quantize_act_mx(hq.HQ_DT_FP4_E2M1 if fp4_act else hq.HQ_DT_FP8_E4M3, Mmax, K, x, self.A, self.e)
+        torch.cuda.synchronize()
+        del x
+        self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in sweep)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def flops(self, M):
+        return 2.0 * M * self.N * self.K
+
+    def bytes(self, M):
+        return self.wbytes + M * (self.abytes + self.K // 32) + M * self.N * 2
+
+    def kernel_of(self, M):
+        f = "W4A4_MX" if self.fp4 else "W4A8_MXA"
+        if M <= 64:
+            return (f"skinny_kernel<{f}> (M<=64)", "hbm")
+        return (f"tile_gemm_kernel<{f}> (M>64)", "mfma" if M >= 256 else "hbm")
+
+    def call(self, M, c, desc=None):
+        w, e = self.copies[c]
+        hq.hq_gemm(desc or self.desc, M, self.A, self.e, w, e, None, self.D, self.ws if self.ws_bytes else None,
+                   self.ws_bytes)
+
+    def cpu_baseline(self, budget_s=8.0):
+        import oracle
+        elem = "e2m1" if self.fp4 else "e4m3"
+        qa, ea = oracle.quant_act_mx(self.host["A0"][:64], elem)
+        f = lambda rows: oracle.gemm_mx_mxfp4(qa, ea, self.host["q"], self.host["e"], N=self.N, K=self.K,
+                                              a_elem=elem, rows=rows)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, 64)), budget_s)
+        return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(), kind="oracle",
+                    sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
+
+
+class DenseFP8Blockwise:
+    """FP8 W8A8 with blockwise scales (1x128 activation blocks quantised on the GPU
+    once, untimed; 128x128 weight blocks), N=K=7168 (a DeepSeek-class FP8 layer)."""
+
+    def __init__(self, N=7168, K=7168, Mmax=8192, sweep=SWEEP):
+        self.N, self.K, self.Mmax, self.sweep = N, K, Mmax, sweep
+        self.dtype = "fp8"
+        self.name = f"dense_w8a8_fp8_blockwise_N{N}_K{K}"
+        log(f"[bench] generating {self.name}")
+        d = syn.w8a8_fp8_blockwise(0, Mmax, N, K)
+        self.host = d
+        self.desc = hq.desc_fp8_blockwise(N, K)
+        wp, sp, _ = hq.hq_repack(self.desc, d["w"], d["s_w"])
+        self.wbytes = wp.size + sp.size
+        self.copies = _copies((dev(wp), dev(sp)), self.wbytes)
+        x = dev(d["A0"])
+        self.A = torch.empty(Mmax * K, dtype=torch.uint8, device="cuda")
+        self.s_a = torch.empty(Mmax * (K // 128), dtype=torch.float32, device="cuda")
+        hq.hq_quantize_act_blocks(hq.HQ_DT_FP8_E4M3, Mmax, K, 128, x, self.A, self.s_a)
+        torch.cuda.synchronize()
+        del x
+        self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in sweep)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def flops(self, M):
+        return 2.0 * M * self.N * self.K
+
+    def bytes(self, M):
+        return self.wbytes + M * self.K + M * (self.K // 128) * 4 + M * self.N * 2
+
+    def kernel_of(self, M):
+        if M <= 64:
+            return ("skinny_kernel<W8A8_F8B> (M<=64)", "hbm")
+        return ("tile_gemm_kernel<W8A8_F8B> (M>64)", "mfma" if M >= 512 else "hbm")
+
+    def call(self, M, c, desc=None):
+        w, s = self.copies[c]
+        hq.hq_gemm(desc or self.desc, M, self.A, self.s_a, w, s, None, self.D, self.ws if self.ws_bytes else None,
+                   self.ws_bytes)
+
+    def cpu_baseline(self, budget_s=8.0):
+        import oracle
+        qa, sa = oracle.quant_act_e4m3_blocks(self.host["A0"][:64], 128)
+        f = lambda rows: oracle.gemm_fp8_blockwise(qa, sa, self.host["w"], self.host["s_w"], rows=rows)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, 64)), budget_s)
+        return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(), kind="oracle",
+                    sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
+
+
+class DenseFP4A16:
+    """bf16 activations x FP4 weights (MXFP4: E8M0 per 32 K; NVFP4: E4M3 per 16 K and a
+    per-tensor second-level scale) at the dense W4A16 layer's shape, N=4096, K=7168."""
+
+    def __init__(self, nvfp4: bool, N=4096, K=7168, Mmax=8192, sweep=SWEEP):
+        self.N, self.K, self.Mmax, self.sweep, self.nv = N, K, Mmax, sweep, nvfp4
+        self.dtype = "bf16"
+        self.name = f"dense_w4a16_{'nvfp4' if nvfp4 else 'mxfp4'}_bf16_N{N}_K{K}"
+        log(f"[bench] generating {self.name}")
+        d = syn.w4a16_fp4(0, Mmax, N, K, nvfp4=nvfp4)
+        self.host = d
+        self.desc = hq.desc_fp4_a16(N, K, nvfp4)
+        if nvfp4:
+            wp, sp, _, s2 = hq.hq_repack(self.desc, d["q"], d["s"], None, d["s2"])
+        else:
+            (wp, sp, _), s2 = hq.hq_repack(self.desc, d["q"], d["s"]), None
+        self.wbytes = wp.size + sp.size + (s2.size if s2 is not None else 0)
+        self.copies = _copies((dev(wp), dev(sp), dev(s2) if s2 is not None else None), self.wbytes)
+        self.A = dev(d["A"])
+        self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in sweep)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def flops(self, M):
+        return 2.0 * M * self.N * self.K
+
+    def bytes(self, M):
+        return self.wbytes + M * self.K * 2 + M * self.N * 2
+
+    def kernel_of(self, M):
+        f = "NVFP4_BF16" if self.nv else "MXFP4_BF16"
+        if M <= 64:
+            return (f"skinny_kernel<{f}> (M<=64)", "hbm")
+        return (f"tile_gemm_kernel<{f}> (M>64)", "mfma" if M >= 128 else "hbm")
+
+    def call(self, M, c, desc=None):
+        w, s, s2 = self.copies[c]
+        hq.hq_gemm(desc or self.desc, M, self.A, None, w, s, None, self.D, self.ws if self.ws_bytes else None,
+                   self.ws_bytes, s2=s2)
+
+    def cpu_baseline(self, budget_s=8.0):
+        import oracle
+        d = self.host
+        f = lambda rows: oracle.gemm_fp4_a16(d["A"], d["q"], d["s"], N=self.N, K=self.K, a_bf16=True, nvfp4=self.nv,
+                                             s2=d.get("s2"), rows=rows)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, self.Mmax)), budget_s)
+        return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(), kind="oracle",
+                    sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
+
+
 WORKLOADS = {
     "c1": lambda: DenseW4A16(N=1024, K=1024, Mmax=16, bf16=True, zp=False, sweep=[16],
                              name="dense_w4a16_sym_bf16_M16_N1024_K1024"),
@@ -397,7 +575,14 @@ WORKLOADS = {
     "c5": lambda: MoEMXFP4(),
     "c5g": lambda: MoEGroupedMXFP4(),
     "c5l": lambda: MoELayerMXFP4(),
+    "w4a4": lambda: DenseMXAct(fp4_act=True),
+    "w4a8mx": lambda: DenseMXAct(fp4_act=False),
+    "fp8b": lambda: DenseFP8Blockwise(),
+    "mxfp4a16": lambda: DenseFP4A16(nvfp4=False),
+    "nvfp4a16": lambda: DenseFP4A16(nvfp4=True),
 }
+# the workloads the default run measures besides the headline one (c2)
+DEFAULT_EXTRA = ["c3", "c4", "c5", "w4a4", "w4a8mx", "fp8b", "mxfp4a16", "nvfp4a16"]
 
 
 # ---------------------------------------------------------------------------
@@ -427,32 +612,55 @@ class _Eager:
         self.fn()
 
 
-def run(work, steps, warmup, eager=False):
-    """Per-M timing from graphs of back-to-back calls (each on its own cold weight copy),
-    and the step timing from graphs of whole sweeps (rotating copies)."""
-    sweep = work.sweep
-    ncopy = len(work.copies)
-    per = {}
-    capture = _Eager if eager else _capture
-    for M in sweep:
-        def calls(M=M):
-            for r in range(ncopy):
-                work.call(M, r)
-        g = capture(calls)
-        g.replay()
-        torch.cuda.synchronize()
-        reps = 3
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+REPS = 7        # timed replays per M (median, p10, p90 over them)
+
+
+def _pct(xs, q):
+    return float(np.percentile(np.asarray(xs), q))
+
+
+def _graph_times(fn, ncalls, eager=False, reps=REPS):
+    """Per-call seconds of each of `reps` replays of a graph of fn() (ncalls calls);
+    HIP events on the replaying stream."""
+    g = (_Eager if eager else _capture)(fn)
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(reps):
         e0.record()
-        for _ in range(reps):
-            g.replay()
+        g.replay()
         e1.record()
         torch.cuda.synchronize()
-        per[M] = e0.elapsed_time(e1) * 1e-3 / (reps * ncopy)
-        del g
+        out.append(e0.elapsed_time(e1) * 1e-3 / ncalls)
+    del g
+    return out
+
+
+def time_calls(work, M, desc=None, eager=False, reps=REPS):
+    """Per-call seconds over `reps` replays of back-to-back calls at M, one call
+    per cold weight copy."""
+    ncopy = len(work.copies)
+
+    def calls():
+        for r in range(ncopy):
+            if desc is None:
+                work.call(M, r)
+            else:
+                work.call(M, r, desc)
+    return _graph_times(calls, ncopy, eager, reps)
+
+
+def run(work, steps, warmup, eager=False):
+    """Per-M timings (list of per-call seconds over the replays) and the wall time
+    of `steps` replays of the whole sweep (graphs of sweeps over rotating copies)."""
+    sweep = work.sweep
+    ncopy = len(work.copies)
+    per = {M: time_calls(work, M, eager=eager) for M in sweep}
     nsw = max(1, ncopy // len(sweep))
     graphs = []
+    capture = _Eager if eager else _capture
     for j in range(nsw):
         def sweep_calls(j=j):
             for i, M in enumerate(sweep):
@@ -467,6 +675,27 @@ def run(work, steps, warmup, eager=False):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, per
+
+
+def tune_table(work, log_fn=log):
+    """Autotune the workload's dense layer over its sweep: per M the fastest
+    tuning override (HQ_TUNE(path, splits)) and the library's own choice."""
+    from bit_quantized_gemm_w4a16_amd import autotune as at
+
+    def time_us(desc, M):
+        need = hq.hq_workspace_bytes(desc, M)
+        if need > work.ws.numel():
+            work.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        if need > work.ws_bytes:
+            work.ws_bytes = need
+        # the fastest of 5 replays: the candidates are compared on what they can do,
+        # not on the clock and queue noise of one replay
+        return min(time_calls(work, M, desc=desc, reps=5)) * 1e6
+
+    table = at.autotune(work.desc, work.sweep, time_us, verbose=log_fn)
+    return [dict(M=M, best_tune=t, best_plan=at.plan_name(work.desc, t, M), best_us=round(b, 2),
+                 library_plan=at.plan_name(work.desc, 0, M), library_us=round(base, 2),
+                 gain=round(base / b, 3)) for M, (t, b, base) in table.items()]
 
 
 # The sources the counted kernel (the dense W4A16 tile GEMM and its launch) is
@@ -512,62 +741,133 @@ def copy_probe(nbytes, reps):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def report(work, args, wall, per):
-    ms_per_step = wall / args.steps * 1e3
+def report(work, args, wall, per, cpu_budget=16.0):
+    ms_per_step = wall / args.steps * 1e3 if args.steps else None
     flops_step = sum(work.flops(M) for M in work.sweep)
     peak = PEAK[work.dtype]
     table, kern = [], {}
     for M in work.sweep:
-        t = per[M]
+        t = statistics.median(per[M])
         F, B = work.flops(M), work.bytes(M)
-        table.append(dict(M=M, us=round(t * 1e6, 2), tflops=round(F / t / 1e12, 2), gbps=round(B / t / 1e9, 1),
-                          hbm_frac=round(B / t / PEAK_HBM, 3), mfma_frac=round(F / t / peak, 3),
-                          roofline_frac=round(max(B / PEAK_HBM, F / peak) / t, 3)))
+        row = dict(M=M, us=round(t * 1e6, 2), us_p10=round(_pct(per[M], 10) * 1e6, 2),
+                   us_p90=round(_pct(per[M], 90) * 1e6, 2), tflops=round(F / t / 1e12, 2),
+                   gbps=round(B / t / 1e9, 1), hbm_frac=round(B / t / PEAK_HBM, 3),
+                   mfma_frac=round(F / t / peak, 3), roofline_frac=round(max(B / PEAK_HBM, F / peak) / t, 3))
+        if hasattr(work, "routing_us"):
+            row["routing_us"] = work.routing_us(M)
+        table.append(row)
         name, bound = work.kernel_of(M)
-        k = kern.setdefault(name, dict(F=0.0, B=0.0, t=0.0, n=0, bounds={}))
-        k["F"] += F
-        k["B"] += B
+        k = kern.setdefault(name, dict(t=0.0))
         k["t"] += t
-        k["n"] += 1
-        k["bounds"][bound] = k["bounds"].get(bound, 0.0) + t
     # Roofline of the dominant kernel, taken at the sweep's largest M, where one
     # call is one launch of it: achieved = algorithmic flops (or bytes) of that
-    # launch / its average duration over back-to-back launches (HIP events on
+    # launch / its median duration over back-to-back launches (HIP events on
     # the launching stream).
     dom = max(kern, key=lambda n: kern[n]["t"])
     Mr = max(M for M in work.sweep if work.kernel_of(M)[0] == dom)
     name, bound = work.kernel_of(Mr)
-    t, F, B = per[Mr], work.flops(Mr), work.bytes(Mr)
+    t, F, B = statistics.median(per[Mr]), work.flops(Mr), work.bytes(Mr)
+    unit = "TFLOP/s" if work.dtype != "int8" else "TOP/s"
     if bound == "mfma":
-        roof = dict(bound="mfma", achieved=round(F / t / 1e12, 1), peak=peak / 1e12,
-                    unit="TFLOP/s" if work.dtype != "int8" else "TOP/s", frac=round(F / t / peak, 4))
+        roof = dict(bound="mfma", achieved=round(F / t / 1e12, 1), peak=peak / 1e12, unit=unit,
+                    frac=round(F / t / peak, 4))
     else:
         roof = dict(bound="hbm", achieved=round(B / t / 1e9, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
                     frac=round(B / t / PEAK_HBM, 4))
     roof.update(traffic=_traffic(work.name, Mr), kernel=dom, M=Mr, avg_us=round(t * 1e6, 2),
                 algorithmic_flops=F, algorithmic_bytes=B,
                 per_unit="2*M*N*K flops per launch" if bound == "mfma" else "algorithmic bytes per launch")
-    cpu = None if args.no_cpu_baseline else work.cpu_baseline()
-    return {
+    cpu = None if args.no_cpu_baseline else work.cpu_baseline(cpu_budget)
+    cfg = {"workload": work.name, "M_sweep": work.sweep, "N": work.N, "K": work.K,
+           "cold_weight_copies": len(work.copies)}
+    if hasattr(work, "E"):
+        cfg.update(E=work.E, top_k=work.top_k)
+    out = {
         "metric": METRIC,
-        "value": round(flops_step / (ms_per_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s" if work.dtype != "int8" else "TOP/s",
+        "value": round(flops_step / (ms_per_step * 1e-3) / 1e12, 2) if ms_per_step else None,
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(ms_per_step, 4) if ms_per_step else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": work.dtype,
         "data": "synthetic",
-        "config": {"workload": work.name, "M_sweep": work.sweep, "N": work.N, "K": work.K,
-                   "cold_weight_copies": len(work.copies)},
+        "config": cfg,
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_M": table,
-        **({"aux": work.aux()} if hasattr(work, "aux") else {}),
     }
+    if hasattr(work, "aux"):
+        out["aux"] = work.aux()
+    return out
+
+
+def kernel_stats(csv_path, config, sweep=None, reps=REPS):
+    """Kernel-only time per M from a rocprofv3 kernel trace of
+    `bench.py --config <dense workload> --steps 0 --warmup 0 --no-cpu-baseline`.
+
+    The trace lists the dispatches in order; per M the run makes (2 + reps) x copies
+    calls (the capture's eager pass, the warm-up replay, the timed replays), each
+    launching the kernels hq_gemm_plan names.  Those are matched in order against
+    the trace (other kernels -- torch's, the setup's -- are skipped; a name that
+    does not match the plan aborts), and the kernel durations of each call are
+    summed.  Prints one JSON object: per M the median / p10 / p90 over calls."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    desc = _DRY[config]()
+    sweep = sweep or SWEEP
+    ncopy = _ncopies(desc)
+    seq = []
+    for M in sweep:
+        plan = [p.split("<")[0] for p in hq.hq_gemm_plan(desc, M)]
+        seq.append((M, plan, (2 + reps) * ncopy))
+    i, out = 0, []
+    for M, plan, ncalls in seq:
+        calls = []
+        for _ in range(ncalls):
+            t = 0.0
+            for k in plan:
+                while i < len(rows) and not _is_hq_kernel(rows[i]["Kernel_Name"]):
+                    i += 1
+                if i >= len(rows):
+                    raise SystemExit(f"trace ended before M={M}")
+                nm = rows[i]["Kernel_Name"]
+                base = nm.split("<")[0].replace("void ", "").strip()
+                if base != k:
+                    raise SystemExit(f"M={M}: expected {k}, trace has {nm}")
+                t += (int(rows[i]["End_Timestamp"]) - int(rows[i]["Start_Timestamp"])) * 1e-3
+                i += 1
+            calls.append(t)
+        timed = calls[2 * ncopy:]
+        out.append(dict(M=M, kernels=plan, calls=len(timed), median_us=round(_pct(timed, 50), 2),
+                        p10_us=round(_pct(timed, 10), 2), p90_us=round(_pct(timed, 90), 2)))
+    print(json.dumps({"workload": config, "copies": ncopy, "kernel_only_us": out}))
+
+
+def _is_hq_kernel(name):
+    return any(k in name for k in ("skinny_kernel", "tile_gemm_kernel", "splitk_finalize_kernel"))
+
+
+# descriptors of the dense workloads, for kernel_stats (no device memory needed)
+_DRY = {
+    "c2": lambda: hq.desc_w4a16(4096, 7168, 128, bf16=False, zp=True),
+    "c3": lambda: hq.desc_w4a8_mxfp4(7168, 4096),
+    "c4": lambda: hq.desc_w8a8(18432, 7168),
+    "w4a4": lambda: hq.desc_mx_act_mxfp4(7168, 4096, fp4_act=True),
+    "w4a8mx": lambda: hq.desc_mx_act_mxfp4(7168, 4096, fp4_act=False),
+    "fp8b": lambda: hq.desc_fp8_blockwise(7168, 7168),
+    "mxfp4a16": lambda: hq.desc_fp4_a16(4096, 7168, False),
+    "nvfp4a16": lambda: hq.desc_fp4_a16(4096, 7168, True),
+}
+
+
+def _ncopies(desc):
+    """The number of cold weight copies a workload makes (as _copies does)."""
+    return max(2, -(-COLD_BYTES // sum(hq.hq_repacked_bytes(desc))))
 
 
 def main():
@@ -575,36 +875,66 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="c2", help="c1|c2|c3|c4|c5|c5g|c5l|all (default c2; c5g = MoE on the Grouped path, c5l = MoE gate-up + SwiGLU + down)")
+    ap.add_argument("--config", default=None,
+                    help=f"one of {', '.join(WORKLOADS)} or all (default: c2 as the headline line, "
+                         f"with {', '.join(DEFAULT_EXTRA)} under its 'configs'; c5g = MoE on the Grouped path, "
+                         "c5l = MoE gate-up + SwiGLU + down)")
     ap.add_argument("--sweep", default=None, help="comma-separated M values (default 1..8192 powers of 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="issue calls directly instead of replaying HIP graphs "
                     "(for counter-collection runs)")
+    ap.add_argument("--autotune", action="store_true",
+                    help="also time every tuning override per M (dense workloads) and report the fastest")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--kernel-stats", default=None, metavar="CSV",
+                    help="no GPU: per-M kernel-only times from a rocprofv3 kernel trace of this script "
+                         "(--config <dense workload> --steps 0 --warmup 0)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    sweep = [int(x) for x in args.sweep.split(",")] if args.sweep else None
+    if args.kernel_stats:
+        kernel_stats(args.kernel_stats, args.config or "c2", sweep)
+        return
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(args.copy_probe, args.steps)
         return
-    names = list(WORKLOADS) if args.config == "all" else [args.config]
-    for nm in names:
+
+    def measure(nm, cpu_budget):
         if nm not in WORKLOADS:
             raise SystemExit(f"unknown --config {nm}")
         work = WORKLOADS[nm]()
-        if args.sweep and nm != "c1":
-            work.sweep = [int(x) for x in args.sweep.split(",")]
+        if sweep and nm != "c1":
+            work.sweep = sweep
             if hasattr(work, "active"):
                 flat = work.host["ids"]
                 work.active = {T: len(np.unique(flat[:T])) for T in work.sweep}
+        t0 = time.perf_counter()
         wall, per = run(work, args.steps, args.warmup, eager=args.eager)
-        print(json.dumps(report(work, args, wall, per)), flush=True)
+        rec = report(work, args, wall, per, cpu_budget)
+        if args.autotune and hasattr(work, "desc") and not hasattr(work, "E"):
+            rec["autotune"] = tune_table(work)
+        log(f"[bench] {nm}: {time.perf_counter() - t0:.1f} s")
         del work
         torch.cuda.empty_cache()
+        return rec
+
+    if args.config is None:
+        head = measure("c2", 16.0)
+        head["configs"] = {}
+        for nm in DEFAULT_EXTRA:
+            rec = measure(nm, 3.0)
+            head["configs"][nm] = {k: rec[k] for k in ("value", "unit", "ms_per_step", "dtype", "config", "roofline",
+                                                       "cpu_baseline", "per_M") + (("aux",) if "aux" in rec else ())}
+        print(json.dumps(head), flush=True)
+        return
+    names = list(WORKLOADS) if args.config == "all" else [args.config]
+    for nm in names:
+        print(json.dumps(measure(nm, 16.0)), flush=True)
 
 
 if __name__ == "__main__":

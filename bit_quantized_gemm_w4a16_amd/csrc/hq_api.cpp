@@ -63,8 +63,13 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
     if (!d) return set_error(HQ_ERR_INVALID_ARG, "descriptor is NULL");
     if (d->abi_version != HQ_ABI_VERSION)
         return set_error(HQ_ERR_ABI, "descriptor abi_version %d, library %d", d->abi_version, HQ_ABI_VERSION);
-    for (int i = 0; i < 3; ++i)
-        if (d->reserved[i]) return set_error(HQ_ERR_INVALID_ARG, "reserved fields must be zero");
+    if (d->reserved) return set_error(HQ_ERR_INVALID_ARG, "reserved fields must be zero");
+    if (d->flags & ~HQ_FLAG_BATCH_INVARIANT) return set_error(HQ_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
+    const int tune_path = d->tune & 0xFF, tune_splits = (d->tune >> 8) & 0xFFFF;
+    if (tune_path > HQ_TUNE_W256 || (d->tune >> 24) || (tune_path == 0 && tune_splits))
+        return set_error(HQ_ERR_INVALID_ARG, "bad tune value 0x%x", d->tune);
+    if ((d->flags || d->tune) && d->num_experts)
+        return set_error(HQ_ERR_UNSUPPORTED, "batch invariance and tuning overrides apply to dense layers");
     if (d->N < 1 || d->K < 1 || d->N > (1LL << 24) || d->K > (1LL << 24))
         return set_error(HQ_ERR_INVALID_ARG, "N=%lld K=%lld out of range [1, 2^24]", (long long)d->N, (long long)d->K);
     if (d->num_experts < 0 || d->num_experts > 4096)
@@ -72,6 +77,9 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
     if (d->scale2 != HQ_S2_NONE && d->scale2 != HQ_S2_PER_TENSOR_F32)
         return set_error(HQ_ERR_INVALID_ARG, "bad scale2 kind %d", d->scale2);
     LayerInfo I{};
+    I.invariant = (d->flags & HQ_FLAG_BATCH_INVARIANT) != 0;
+    I.tune_path = tune_path;
+    I.tune_splits = tune_splits;
     I.N = d->N;
     I.K = d->K;
     I.Np = pad16(d->N);
@@ -179,6 +187,8 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
 
 static hq_status hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();
+    if (e == hipErrorNotSupported)
+        return set_error(HQ_ERR_UNSUPPORTED, "%s: the tuning override does not apply to this layer and M", what);
     return set_error(HQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -210,6 +220,9 @@ static hq_status dense_plan(const LayerInfo& L, int64_t M, char* buf, size_t len
     a.K = L.K;
     a.Np = L.Np;
     a.group_size = (int)L.G;
+    a.invariant = L.invariant;
+    a.tune_path = L.tune_path;
+    a.tune_splits = L.tune_splits;
     const hq_status st = dense_launch(L, a);
     g_plan = nullptr;
     if (buf) buf[rec.used < len ? rec.used : len - 1] = 0;
@@ -377,7 +390,8 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const voi
     const bool mx = desc->a_scale == HQ_ASCALE_MX_E8M0, blk = desc->a_scale == HQ_ASCALE_PER_BLOCK128_F32;
     DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, mx || blk ? nullptr : (const float*)a_scale,
                 mx ? (const uint8_t*)a_scale : nullptr, blk ? (const float*)a_scale : nullptr,
-                w, s, z, (const float*)s2, D, workspace, ws_bytes, (hipStream_t)stream};
+                w, s, z, (const float*)s2, D, workspace, ws_bytes, (hipStream_t)stream,
+                L.invariant, L.tune_path, L.tune_splits};
     return dense_launch(L, a);
 }
 

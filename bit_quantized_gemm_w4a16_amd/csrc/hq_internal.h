@@ -46,6 +46,10 @@ struct DenseArgs {
     void* ws;
     size_t ws_bytes;
     hipStream_t stream;
+    // compute / tuning options from the descriptor
+    bool invariant;       // batch-invariant mode: results per row independent of M
+    int tune_path;        // 0: library's choice; else a TunePath override
+    int tune_splits;      // K slices of the override (0: the planner's)
 };
 
 // W4A16 (INT4 / UINT4+zp; bf16 / fp16 activations)

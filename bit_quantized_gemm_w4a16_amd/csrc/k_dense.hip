@@ -35,27 +35,24 @@ namespace {
 
 template <Fmt F>
 hipError_t launch(const DenseArgs& a, int raw_i32) {
-    if (a.M <= kSkinnyMaxM) {
-        SkinnyArgs s{};
-        s.A = a.A;
-        s.a_scale = a.a_scale;
-        s.a_e8 = a.a_e8;
-        s.a_blk = a.a_blk;
-        s.s2 = a.s2;
-        s.W = a.w;
-        s.S = a.s;
-        s.D = a.D;
-        s.part = a.ws;
-        s.M = (int)a.M;
-        s.K = (int)a.K;
-        s.N = (int)a.N;
-        s.Np = (int)a.Np;
-        s.nc = (int)(a.K / 128);
-        s.ngroups = 1;
-        s.gchunks = 1;
-        s.raw_i32 = raw_i32;
-        return launch_skinny_dense<F>(plan_skinny(F, a.M, a.Np, a.K, 128), s, a.stream);
-    }
+    SkinnyArgs s{};
+    s.A = a.A;
+    s.a_scale = a.a_scale;
+    s.a_e8 = a.a_e8;
+    s.a_blk = a.a_blk;
+    s.s2 = a.s2;
+    s.W = a.w;
+    s.S = a.s;
+    s.D = a.D;
+    s.part = a.ws;
+    s.M = (int)a.M;
+    s.K = (int)a.K;
+    s.N = (int)a.N;
+    s.Np = (int)a.Np;
+    s.nc = (int)(a.K / 128);
+    s.ngroups = 1;
+    s.gchunks = 1;
+    s.raw_i32 = raw_i32;
     TileArgs p{};
     p.A = a.A;
     p.a_scale = a.a_scale;
@@ -74,8 +71,7 @@ hipError_t launch(const DenseArgs& a, int raw_i32) {
     p.ngroups = 1;
     p.gsteps = 1;
     p.raw_i32 = raw_i32;
-    const TilePlan pl = plan_tile(a.M, a.Np, a.K, has_big_tile(F), has_wide256_tile(F), has_wide_tile(F), wide256_min_tiles(F));
-    return launch_dense_plan<F>(pl, p, a.stream);
+    return dense_dispatch<F>(a, s, p, 128);
 }
 
 }  // namespace

@@ -25,8 +25,7 @@ namespace hq {
 namespace {
 
 template <Fmt F>
-hipError_t launch_small(const DenseArgs& a) {
-    const SkinnyPlan pl = plan_skinny(F, a.M, a.Np, a.K, a.group_size);
+hipError_t launch_all(const DenseArgs& a) {
     SkinnyArgs s{};
     s.A = a.A;
     s.W = a.w;
@@ -41,11 +40,6 @@ hipError_t launch_small(const DenseArgs& a) {
     s.nc = (int)(a.K / 128);
     s.ngroups = (int)(a.K / a.group_size);
     s.gchunks = a.group_size / 128;
-    return launch_skinny_dense<F>(pl, s, a.stream);
-}
-
-template <Fmt F>
-hipError_t launch_tile(const DenseArgs& a) {
     TileArgs p{};
     p.A = a.A;
     p.W = a.w;
@@ -60,14 +54,7 @@ hipError_t launch_tile(const DenseArgs& a) {
     p.Np = (int)a.Np;
     p.ngroups = (int)(a.K / a.group_size);
     p.gsteps = a.group_size / 128;
-    const TilePlan pl = plan_tile(a.M, a.Np, a.K, has_big_tile(F), has_wide256_tile(F), has_wide_tile(F), wide256_min_tiles(F));
-    return launch_dense_plan<F>(pl, p, a.stream);
-}
-
-template <Fmt F>
-hipError_t launch_all(const DenseArgs& a) {
-    if (a.M <= kSkinnyMaxM) return launch_small<F>(a);
-    return launch_tile<F>(a);
+    return dense_dispatch<F>(a, s, p, a.group_size);
 }
 
 }  // namespace

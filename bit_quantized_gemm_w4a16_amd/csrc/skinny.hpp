@@ -550,6 +550,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
 // ---- host-side plan ----
 
 struct SkinnyPlan {
+    bool ok;        // false: a forced K split that the slice's LDS or register batch cannot take
     int NS, WS, SPW, splits, MT, CPW;
     int cps, cpk;   // chunks per slice, per wave K-part
     int a_off, s_off, z_off;
@@ -603,7 +604,7 @@ inline int64_t skinny_lds_need(Fmt F, int64_t rows, int64_t cmax, int NS, int gc
 // Dense plan: strips per workgroup grow with M so the A slice is re-read about
 // nstrips / NS times; K slices until the grid covers the chip and the slice
 // fits in LDS.
-inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G) {
+inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, int force_splits = 0) {
     const int64_t nstrips = Np / 16, nc = K / 128;
     const int gch = G >= 128 ? G / 128 : 1;
     SkinnyPlan p{};
@@ -624,6 +625,11 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G) {
     const int64_t cap = p.SPW * 16 * nb < 64 ? 16 : 8;  // largest register batch instantiated
     while (S < smax && (skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap)) ++S;
     if (S > smax) S = smax;
+    p.ok = true;
+    if (force_splits > 0) {  // tuning override: the slice must still fit LDS and one register batch
+        S = force_splits;
+        if (S > nc || skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap) p.ok = false;
+    }
     p.splits = (int)(S < 1 ? 1 : S);
     p.cps = (int)cdiv(nc, p.splits);
     p.splits = (int)cdiv(nc, p.cps);  // no empty slice
@@ -694,5 +700,29 @@ hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t s
     return launch_finalize<F>(FinalizeArgs{s.part, s.D, s.a_scale, (const float*)s.S, s.s2, s.M, s.N, s.Np, s.splits, s.raw_i32}, st);
 }
 
+
+// Dense dispatch shared by the format launchers: the small-M weight stream up
+// to kSkinnyMaxM rows, the tiled kernels above; a tuning override (TunePath and
+// K split) or batch-invariant mode (tiled kernels without K split at every M:
+// every tile shape of a format accumulates an output in the same order, so a
+// row's result does not depend on M) changes the choice.
+template <Fmt F>
+hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
+    const bool tile_forced = a.tune_path >= TUNE_T128;
+    if (!a.invariant && !tile_forced && (a.tune_path == TUNE_STREAM || a.M <= kSkinnyMaxM)) {
+        if (a.M > kSkinnyMaxM) return hipErrorNotSupported;
+        const SkinnyPlan pl = plan_skinny(F, a.M, a.Np, a.K, G, a.tune_splits);
+        if (!pl.ok) return hipErrorNotSupported;
+        return launch_skinny_dense<F>(pl, s, a.stream);
+    }
+    TilePlan pl = plan_tile(a.M, a.Np, a.K, has_big_tile(F), has_wide256_tile(F), has_wide_tile(F), wide256_min_tiles(F));
+    if (tile_forced) {
+        pl.forced = a.tune_path;
+        pl.splits = a.tune_splits;
+        if (pl.splits > a.K / 128) return hipErrorNotSupported;
+    }
+    if (a.invariant) p.max_splits = 1;
+    return launch_dense_plan<F>(pl, p, a.stream);
+}
 
 }  // namespace hq

@@ -99,6 +99,7 @@ struct TileArgs {
     int a_rows;             // rows of A (bounds the buffer loads; A bytes < 2^32)
     int ngroups, gsteps;    // WNA16: K / G and G / 128
     int tiles_m, tiles_n, splits;
+    int max_splits;         // upper bound on splits (0: none; 1 in batch-invariant mode)
     int raw_i32;            // W8A8: store int32 accumulators
     // MoE (tiles_m is an upper bound; the real count is *ntiles)
     const int* tile_info;   // per m-tile: expert, first sorted row, row count
@@ -994,7 +995,11 @@ namespace hq {
 struct TilePlan {
     int BM, splits;
     bool wide;  // 256-column tiles: 256 x 256 if BM == 256, else 128 x 256
+    int forced; // 0: the heuristic below; else a tuning override (TunePath) with `splits` K slices
 };
+
+// Tuning overrides of the kernel choice (the descriptor's tune field).
+enum TunePath { TUNE_AUTO = 0, TUNE_STREAM = 1, TUNE_T128 = 2, TUNE_T256 = 3, TUNE_W128 = 4, TUNE_W256 = 5 };
 
 // The largest grids use 256-column tiles where the format has them (256 x 256,
 // else 128 x 256), then 256 x 128 tiles on 8 waves; smaller ones 128 x 128
@@ -1002,7 +1007,7 @@ struct TilePlan {
 inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256, bool wide256 = false, bool wide128 = false,
                           int64_t wide256_min = 256) {
     const int64_t tn = (Np + 127) / 128, nsteps = K / 128, tn2 = (Np + 255) / 256;
-    TilePlan pl{128, 1, false};
+    TilePlan pl{128, 1, false, 0};
     if (wide256 && ((M + 255) / 256) * tn2 >= wide256_min) {
         pl.BM = 256;
         pl.wide = true;
@@ -1026,6 +1031,7 @@ inline TilePlan plan_tile(int64_t M, int64_t Np, int64_t K, bool allow256, bool 
 
 template <Fmt F, int BM, int BN, int WM, int WN, int PD>
 hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
+    if (p.max_splits > 0 && p.splits > p.max_splits) p.splits = p.max_splits;
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.Np + BN - 1) / BN);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.splits;
@@ -1064,8 +1070,36 @@ constexpr bool has_wide256_tile(Fmt F) { return has_wide_tile(F) || F == Fmt::W8
 // faster at M=1024 and level at M=2048 for N=18432, K=7168)
 constexpr int64_t wide256_min_tiles(Fmt F) { return F == Fmt::W8A8_I8 ? 512 : 256; }
 
+// A tuning override: the format's kernel of the requested class with the
+// requested K split (hipErrorNotSupported where the format has no such tile).
+template <Fmt F>
+hipError_t launch_forced(const TilePlan& pl, TileArgs p, hipStream_t st) {
+    p.splits = pl.splits < 1 ? 1 : pl.splits;
+    constexpr bool RING8 = F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B;  // tiles on stage rings
+    switch (pl.forced) {
+        case TUNE_T128:
+            if constexpr (RING8 || mx_mfma(F)) return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
+            else return launch_tile_kernel<F, 128, 128, 2, 4, 0>(p, st);
+        case TUNE_T256:
+            if constexpr (RING8) return launch_tile_kernel<F, 256, 128, 2, 4, 4>(p, st);
+            else if constexpr (mx_mfma(F)) return launch_tile_kernel<F, 256, 256, 2, 4, 4>(p, st);
+            else if constexpr (has_big_tile(F)) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
+            else return hipErrorNotSupported;
+        case TUNE_W128:
+            if constexpr (has_wide_tile(F)) return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
+            else return hipErrorNotSupported;
+        case TUNE_W256:
+            if constexpr (has_wide_tile(F)) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
+            else if constexpr (F == Fmt::W8A8_I8) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
+            else if constexpr (mx_mfma(F)) return launch_tile_kernel<F, 256, 256, 2, 4, 4>(p, st);
+            else return hipErrorNotSupported;
+        default: return hipErrorNotSupported;
+    }
+}
+
 template <Fmt F>
 hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
+    if (pl.forced) return launch_forced<F>(pl, p, st);
     p.splits = pl.splits;
     if constexpr (F == Fmt::W8A8_I8) {
         if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);

@@ -27,6 +27,12 @@ HQ_GRAN_NONE, HQ_GRAN_PER_GROUP_K, HQ_GRAN_PER_CHANNEL, HQ_GRAN_BLOCK_128x128 = 
 HQ_ASCALE_NONE, HQ_ASCALE_PER_TOKEN_F32, HQ_ASCALE_MX_E8M0, HQ_ASCALE_PER_BLOCK128_F32 = range(4)
 HQ_S2_NONE, HQ_S2_PER_TENSOR_F32 = 0, 1
 HQ_MOE_INDEXED, HQ_MOE_GROUPED = 1, 2
+HQ_FLAG_BATCH_INVARIANT = 1
+HQ_TUNE_STREAM, HQ_TUNE_T128, HQ_TUNE_T256, HQ_TUNE_W128, HQ_TUNE_W256 = 1, 2, 3, 4, 5
+
+
+def HQ_TUNE(path: int, splits: int = 0) -> int:
+    return int(path) | (int(splits) << 8)
 
 
 class HQError(RuntimeError):
@@ -42,7 +48,7 @@ class hq_layer_desc(C.Structure):
         ("a_dtype", C.c_int32), ("a_scale", C.c_int32), ("w_dtype", C.c_int32),
         ("w_scale_dtype", C.c_int32), ("w_scale_gran", C.c_int32), ("group_size", C.c_int32),
         ("zp_dtype", C.c_int32), ("scale2", C.c_int32), ("out_dtype", C.c_int32),
-        ("reserved", C.c_int32 * 3),
+        ("flags", C.c_int32), ("tune", C.c_int32), ("reserved", C.c_int32),
     ]
 
 

@@ -145,8 +145,41 @@ typedef struct hq_layer_desc {
     int32_t zp_dtype;       /* HQ_DT_NONE or HQ_DT_UINT4                       */
     int32_t scale2;         /* hq_scale2                                       */
     int32_t out_dtype;      /* hq_dtype of D                                   */
-    int32_t reserved[3];    /* must be zero                                    */
+    int32_t flags;          /* HQ_FLAG_* compute options (0: none)             */
+    int32_t tune;           /* 0: the library's kernel choice; HQ_TUNE(...)    */
+    int32_t reserved;       /* must be zero                                    */
 } hq_layer_desc;
+
+/*
+ * Compute options ("Humming wird angekuendigt", section "Tuning und
+ * JIT-Kompilierung fuer jeden Workload": the compute description carries
+ * options such as batch invariance).
+ *   HQ_FLAG_BATCH_INVARIANT  dense layers: every output row is computed in an
+ *       order that does not depend on M or on the other rows (tiled kernels
+ *       without a K split at every M), so a row gives bit-identical results
+ *       whatever batch it is part of.  Slower at small M.
+ */
+#define HQ_FLAG_BATCH_INVARIANT 1
+
+/*
+ * Tuning override of the kernel choice for dense layers (same section: the
+ * tuning description selects tile shape and pipeline; an autotuner times the
+ * candidates on the device, "Humming wird angekuendigt", section "Zukuenftige
+ * Plaene").  tune = HQ_TUNE(path, splits); splits = K slices (0: the
+ * planner's choice for the stream path, 1 for tiles).  Paths:
+ *   HQ_TUNE_STREAM  the small-M weight stream (M <= 64)
+ *   HQ_TUNE_T128    128 x 128 tiles          HQ_TUNE_T256  the 256-row tile
+ *   HQ_TUNE_W128    128 x 256 tiles          HQ_TUNE_W256  256 x 256 tiles
+ * A path the layer's format lacks, or a split the slice cannot take, returns
+ * HQ_ERR_UNSUPPORTED at the call.  hq_gemm_plan and hq_workspace_bytes follow
+ * the override.
+ */
+#define HQ_TUNE_STREAM 1
+#define HQ_TUNE_T128 2
+#define HQ_TUNE_T256 3
+#define HQ_TUNE_W128 4
+#define HQ_TUNE_W256 5
+#define HQ_TUNE(path, splits) ((int32_t)(path) | ((int32_t)(splits) << 8))
 
 /* ---------------------------------------------------------------------- */
 /* general                                                                 */

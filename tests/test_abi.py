@@ -46,8 +46,17 @@ def test_descriptor_validation():
     assert status_of(hq.hq_desc_validate, hq.desc_w4a16(1024, 1024, group_size=64)) == hq.HQ_ERR_UNSUPPORTED
     assert status_of(hq.hq_desc_validate, hq.desc_w4a16(0, 1024)) == hq.HQ_ERR_INVALID_ARG
     r = hq.desc_w4a16(64, 128)
-    r.reserved[1] = 3
+    r.reserved = 3
     assert status_of(hq.hq_desc_validate, r) == hq.HQ_ERR_INVALID_ARG
+    r = hq.desc_w4a16(64, 128)
+    r.flags = 4
+    assert status_of(hq.hq_desc_validate, r) == hq.HQ_ERR_INVALID_ARG
+    r = hq.desc_w4a16(64, 128)
+    r.tune = hq.HQ_TUNE(9, 1)
+    assert status_of(hq.hq_desc_validate, r) == hq.HQ_ERR_INVALID_ARG
+    r = hq.desc_moe_mxfp4(8, 128, 128)
+    r.flags = hq.HQ_FLAG_BATCH_INVARIANT
+    assert status_of(hq.hq_desc_validate, r) == hq.HQ_ERR_UNSUPPORTED
     mix = hq.desc_w4a16(64, 128)
     mix.w_scale_dtype = hq.HQ_DT_FP16                                                             # bf16 A, fp16 scales
     assert status_of(hq.hq_desc_validate, mix) == hq.HQ_ERR_UNSUPPORTED
