@@ -250,7 +250,13 @@ void tile_gemm_kernel(TileArgs p) {
     // reads take immediate offsets)
     constexpr int SC_PAD = SC_STAGE > 0 ? (SC_STAGE + 15) / 16 * 16 : 16;
     constexpr bool B1 = PD == 3;  // single weight stage
-    constexpr int STAGE = A_STAGE + (B1 ? 0 : B_STAGE);
+    // MX MFMA formats on the stage ring: the step's scale block (weight E8M0
+    // bytes, and the activations' E8M0 words) loads straight into its stage like
+    // the tiles.  Through registers it needs one register set per ring stage,
+    // which the 256 x 256 tiles cannot hold beside their accumulators (the
+    // compiler spills them, and every spill waits for all loads in flight).
+    constexpr bool SC_DMA = PD == 4 && mx_mfma(F);
+    constexpr int STAGE = A_STAGE + (B1 ? 0 : B_STAGE) + (SC_DMA ? SC_PAD : 0);
     // LDS stages: a ring of four where they fit, else three (PD = 4), else two
     constexpr int NRING = 4 * STAGE <= 150 * 1024 ? 4 : 3;
     constexpr int NST = PD == 4 ? NRING : 2;
@@ -270,7 +276,7 @@ void tile_gemm_kernel(TileArgs p) {
     __shared__ __attribute__((aligned(1024))) char stage2[NST > 2 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) char stage3[NST > 3 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) char bstage[B1 ? B_STAGE : 16];
-    __shared__ __attribute__((aligned(16))) char scst[NST][SC_PAD];
+    __shared__ __attribute__((aligned(16))) char scst[SC_DMA ? 1 : NST][SC_DMA ? 16 : SC_PAD];
     __shared__ int rowinfo[2 * BM];  // [0,BM): A row per local row; [BM,2BM): D row (-1 = none)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -387,7 +393,10 @@ void tile_gemm_kernel(TileArgs p) {
         else if constexpr (S == 2) return stage2;
         else return stage3;
     };
-    auto sc_ptr = [&](auto stc) -> char* { return scst[decltype(stc)::value]; };
+    auto sc_ptr = [&](auto stc) -> char* {
+        if constexpr (SC_DMA) return stage_ptr(stc) + A_STAGE + B_STAGE;
+        else return scst[decltype(stc)::value];
+    };
 
     // PD = 0: loads go straight from HBM into the next LDS stage (no staging
     // registers).  PD = 1, 2: register sets; the loads of step s+PD fly while
@@ -438,6 +447,12 @@ void tile_gemm_kernel(TileArgs p) {
                 rs[st][0] = (uint32_t)z;
                 rs[st][1] = (uint32_t)(z >> 32);
             }
+        } else if constexpr (SC_DMA) {
+            lds_char* sc = stage_lds(setc) + A_STAGE + B_STAGE;
+            if (tid < SC_UNITS) dma16(rS, sc + wbase, soff, (uint32_t)ks * SBYTES);
+            // one E8M0 word per row: lane l of wave w writes row 64 w + l
+            if constexpr (MXA)
+                if (tid < BM) dma4(rAS, sc + SC_B + wbase / 4, as_voff, (uint32_t)ks * 4u);
         } else if constexpr (MX) {
             if (tid < SC_UNITS) rs[st] = buf16(rS, soff, (uint32_t)ks * SBYTES);
             // rows past M fall outside the buffer resource and read zeros (outputs dropped)
@@ -451,7 +466,7 @@ void tile_gemm_kernel(TileArgs p) {
     auto sc_write = [&](auto stc, auto setc) {
         constexpr int st = decltype(setc)::value % NSET;
         char* sS = sc_ptr(stc);
-        if constexpr (SC_STAGE > 0) {
+        if constexpr (SC_STAGE > 0 && !SC_DMA) {
             if constexpr (WNA16) {
                 if (tid < 2 * NSTRIP) *(v4u*)(sS + tid * 16) = rs[st];
                 else if (tid < 3 * NSTRIP)
@@ -670,23 +685,58 @@ void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
             for (int j = 0; j < NT; ++j) bsc[j] = (int)((const uint8_t*)sS)[(wn * NT + j) * 64 + lane];
             constexpr int CBSZ = F == Fmt::W4A4_MX ? 4 : 0;  // A operand format: fp8 e4m3 or fp4 e2m1
-#pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                const int row = wm * (BM / WM) + i * 16 + col;
-                const int sw = swz(row, AUNITS);
-                const v4u lo = *(const v4u*)(sA + row * AROW + ((quad ^ sw) * 16));
-                v8i a;
+            // A fragment of m-tile i (and, for MX activations, its E8M0 scale
+            // byte).  The lane's row is r0 + 16 i; the swizzle depends on the
+            // row's low four bits only, so on the lane's column: the offsets of
+            // the m-tiles differ by constants (immediate offsets of the LDS reads
+            // instead of one address register per m-tile and stage)
+            const int r0 = wm * (BM / WM) + col;
+            const int swc = swz(col, AUNITS);
+            const int a_lo = r0 * AROW + ((quad ^ swc) * 16);
+            const int a_hi = r0 * AROW + (((4 + quad) ^ swc) * 16);
+            const uint32_t* a_sc = (const uint32_t*)(sS + SC_B + r0 * 4);
+            auto rdA = [&](int i, v8i& a, int& asc) {
+                const v4u lo = *(const v4u*)(sA + a_lo + i * 16 * AROW);
                 if constexpr (F == Fmt::W4A4_MX) {
                     a = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], 0, 0, 0, 0};
                 } else {
-                    const v4u hi = *(const v4u*)(sA + row * AROW + (((4 + quad) ^ sw) * 16));
+                    const v4u hi = *(const v4u*)(sA + a_hi + i * 16 * AROW);
                     a = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                 }
-                const int asc = MXA ? (int)((const uint8_t*)(sS + SC_B))[row * 4 + quad] : 0x7F;
+                // the row's E8M0 word of the step, byte `quad` (a whole-word read: the
+                // compiler waits for every load in flight before a byte read of
+                // a word that a direct load writes)
+                asc = MXA ? (int)((a_sc[i * 16] >> (8 * quad)) & 0xFFu) : 0x7F;
+            };
+            auto mm = [&](int i, const v8i& a, int asc) {
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     const v8i b = v8i{(int)bw[j][0][0], (int)bw[j][0][1], (int)bw[j][0][2], (int)bw[j][0][3], 0, 0, 0, 0};
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i][j], CBSZ, 4, 0, asc, 0, bsc[j]);
+                }
+            };
+            if constexpr (MT >= 8 && (MXA || F == Fmt::W4A4_MX)) {
+                // tall wave tiles with MX activations: the A fragments stream through
+                // two register sets, each read one m-tile ahead of its MFMAs (all of
+                // them in flight at once spill the 256-register budget of two waves
+                // per SIMD)
+                v8i ar[2];
+                int as[2];
+                rdA(0, ar[0], as[0]);
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    if (i + 1 < MT) rdA(i + 1, ar[(i + 1) & 1], as[(i + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mm(i, ar[i & 1], as[i & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    v8i a;
+                    int asc;
+                    rdA(i, a, asc);
+                    mm(i, a, asc);
                 }
             }
         } else if constexpr (F8B) {
@@ -792,11 +842,11 @@ void tile_gemm_kernel(TileArgs p) {
         // resources), so every point of the loop has the same loads
         // outstanding on every path and the explicit waits hold for the
         // compiler too.
-        // A step's scale block (4-bit formats) comes with its loads into the
-        // stage's register set and goes to the stage's LDS array once landed.
-        // The block's fetching threads issue one load more per step than the
-        // others; counting only the tile loads makes their wait stricter, never
-        // looser.
+        // A step's scale block comes with its loads: straight into the stage
+        // (MX MFMA formats), or into the stage's register set and on to the
+        // stage's LDS array once landed (blockwise fp8).  The block's fetching
+        // threads issue one or two loads more per step than the others;
+        // counting only the tile loads makes their wait stricter, never looser.
         constexpr int NL = NIA + NIB;  // direct loads per thread and step
         using S2 = std::integral_constant<int, 2>;
         using S3 = std::integral_constant<int, 3>;
@@ -809,7 +859,7 @@ void tile_gemm_kernel(TileArgs p) {
         if constexpr (NST == 4) fetch(k0 + 2, S2{});
         auto step = [&](int s, auto cur, auto refill) {
             wait_vmcnt<(NST - 2) * NL>();  // step s has landed (the later ones may fly)
-            if constexpr (SC_STAGE > 0) {
+            if constexpr (SC_STAGE > 0 && !SC_DMA) {
                 sc_write(cur, cur);
                 lds_sync();  // the scale block written, and every wave done with step s-1's stage
             } else {
