@@ -53,7 +53,14 @@
 namespace hq {
 
 constexpr int kSkinnyLds = 150 * 1024;
-constexpr int64_t kSkinnyMaxM = 64;  // dense M handled by this schedule
+constexpr int64_t kSkinnyMaxM = 64;  // dense M this schedule can take (tuning overrides)
+// The M up to which the library's own choice is this schedule.  8-bit A on
+// MFMAs that take whole 128-K steps: above 32 rows (INT8: 16) the tiled ring
+// with a K split is faster (at N=7168 K=4096, M=64: 15.4 against 19.2 us; INT8
+// at N=18432 K=7168, M=32: 32.9 against 35.7 us).
+constexpr int64_t skinny_max_m(Fmt F) {
+    return F == Fmt::W8A8_I8 ? 16 : (mx_mfma(F) || F == Fmt::W8A8_F8B) ? 32 : kSkinnyMaxM;
+}
 
 struct SkinnyArgs {
     const void* A;          // activations [a_rows][K]
@@ -619,7 +626,11 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
     p.groups_x = cdiv(nstrips, p.NS);
     // a K split costs partial tiles and a finalize launch (~3 us): only when the
     // strips alone leave a quarter of the chip idle (or the slice must shrink)
-    int64_t S = p.groups_x >= 192 ? 1 : cdiv(256, p.groups_x);
+    // 16-bit A at 9..16 rows (two strips per workgroup): two workgroups per CU
+    // (four slices at N=4096: 11.2 against 11.9 us with two)
+    const bool a16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16;
+    const int64_t target = a16 && p.NS == 2 ? 512 : 256;
+    int64_t S = p.groups_x >= 192 ? 1 : cdiv(target, p.groups_x);
     const int64_t smax = nc / WK > 0 ? nc / WK : 1;
     const int nb = (F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B) ? 2 : 1;  // 16-byte weight loads per chunk
     const int64_t cap = p.SPW * 16 * nb < 64 ? 16 : 8;  // largest register batch instantiated
@@ -709,7 +720,7 @@ hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t s
 template <Fmt F>
 hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
     const bool tile_forced = a.tune_path >= TUNE_T128;
-    if (!a.invariant && !tile_forced && (a.tune_path == TUNE_STREAM || a.M <= kSkinnyMaxM)) {
+    if (!a.invariant && !tile_forced && (a.tune_path == TUNE_STREAM || a.M <= skinny_max_m(F))) {
         if (a.M > kSkinnyMaxM) return hipErrorNotSupported;
         const SkinnyPlan pl = plan_skinny(F, a.M, a.Np, a.K, G, a.tune_splits);
         if (!pl.ok) return hipErrorNotSupported;

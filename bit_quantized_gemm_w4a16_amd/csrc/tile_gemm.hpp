@@ -1176,7 +1176,9 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
         if constexpr (F == Fmt::W8A8_F8B) {
             // 128-column tiles (one weight scale block) on stage rings, one round of
             // the chip: 256 rows where that fills it, else 128 rows with K split
-            if (((p.M + 255) / 256) * ((p.Np + 127) / 128) >= 256) {
+            // (from 192 such tiles: at M=1024 N=K=7168, 224 of them take 89.8 us,
+            // 448 tiles of 128 x 128 99.0 us)
+            if (((p.M + 255) / 256) * ((p.Np + 127) / 128) >= 192) {
                 p.splits = 1;
                 return launch_tile_kernel<F, 256, 128, 2, 4, 4>(p, st);
             }
@@ -1195,9 +1197,12 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
             // (96 KB) with the K split rounded down to keep one round beats two
             // workgroups per CU on two stages (fewer slices, so the partials and
             // the finalize pass shrink or vanish too)
+            // Above 64 rows the K split targets half the chip: a slice's MFMA
+            // work grows with M while its loads do not (N=7168 K=4096: M=128 on
+            // 2 slices 19.8 against 20.7 us on 4, M=256 unsplit 21.5 against 24.1)
             const int64_t tiles = ((p.M + 127) / 128) * ((p.Np + 127) / 128);
             if (tiles <= 256) {
-                const int64_t s = 256 / tiles;
+                const int64_t s = (p.M <= 64 ? 256 : 128) / tiles;
                 p.splits = (int)(s < 1 ? 1 : s < pl.splits ? s : pl.splits);
                 return launch_tile_kernel<F, 128, 128, 2, 4, 4>(p, st);
             }
@@ -1205,6 +1210,18 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
         if constexpr (has_wide_tile(F)) {
             if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
             if (pl.wide) return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
+            // from 512 rows, 128 x 256 tiles with the K split filling the chip
+            // beat 128 x 128 tiles (each wave dequantises its weights once instead
+            // of twice): N=4096 K=7168 fp16, M=512 45.6 against 49.2 us, M=1024
+            // 71.9 against 77.0; NVFP4 48.7 against 58.9 and 77.9 against 96.3
+            if (p.M >= 512) {
+                const int64_t tiles = ((p.M + 127) / 128) * ((p.Np + 255) / 256), nsteps = p.K / 128;
+                int64_t s = tiles < 256 ? 256 / tiles : 1;
+                if (s > 8) s = 8;
+                if (s > nsteps / 2) s = nsteps / 2;
+                p.splits = (int)(s < 1 ? 1 : s);
+                return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
+            }
         }
         if constexpr (has_big_tile(F))
             if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);

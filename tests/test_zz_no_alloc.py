@@ -30,11 +30,11 @@ def _w8a8_pair(M, N, K, d):
 
 
 def test_noalloc_w8a8_two_calls_bit_exact():
-    """W8A8 (N=18432, K=7168) at M=64 (7-way K split, 31.5 MiB of partials) and
+    """W8A8 (N=8192, K=7168) at M=128 (4-way K split, 16 MiB of partials) and
     then M=16 (2-way): raw int32 identical to hq_gemm and to the oracle."""
-    N, K = 18432, 7168
-    d = syn.w8a8_int8(0, 64, N, K)
-    for M in (64, 16):
+    N, K = 8192, 7168
+    d = syn.w8a8_int8(0, 128, N, K)
+    for M in (128, 16):
         note(f"noalloc w8a8 M={M} N={N} K={K}")
         ref, got = _w8a8_pair(M, N, K, d)
         np.testing.assert_array_equal(got, ref)
@@ -72,9 +72,9 @@ def test_noalloc_rejects_plans_beyond_the_scratch():
     """A plan needing more partial-tile bytes than the array holds is refused
     before any launch, with the need in the message."""
     N, K, M = 36864, 7168, 64
-    desc = hq.desc_w8a8(N, K, raw_int32=True)
+    desc = hq.desc_w4a16(N, K, 128, bf16=False, zp=True)
     assert hq.hq_workspace_bytes(desc, M) > hq.HQ_NOALLOC_SCRATCH_BYTES
-    a, sa, w, s, D = empty(M * K), empty(M * 4), empty(16), empty(N * 4), empty(M * N * 4)
+    a, w, s, z, D = empty(M * K * 2), empty(16), empty(16), empty(16), empty(M * N * 2)
     with pytest.raises(hq.HQError) as e:
-        hq.hq_gemm_noalloc(desc, M, a, sa, w, s, None, D)
+        hq.hq_gemm_noalloc(desc, M, a, None, w, s, z, D)
     assert e.value.status == hq.HQ_ERR_WORKSPACE and "scratch" in str(e.value)
