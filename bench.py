@@ -729,6 +729,44 @@ def _traffic(workload, M):
     return rec.get("hbm_bytes_per_launch")
 
 
+MEASURED = {}   # on-device peaks from the library's probes (filled by measure_peaks)
+
+
+def measure_peaks():
+    """The device's attainable HBM read rate and dense MFMA rate per type, from
+    the library's probes (hq_probe_stream, hq_probe_mfma), timed with HIP events:
+    what the kernels' rooflines are also set against, next to the published peaks."""
+    nbytes = 2 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hq.hq_probe_stream(src, nbytes, sink, 1)
+    reps = 8
+    e0.record()
+    hq.hq_probe_stream(src, nbytes, sink, reps)
+    e1.record()
+    torch.cuda.synchronize()
+    hbm = reps * nbytes / (e0.elapsed_time(e1) * 1e-3)
+    del src
+    out = {"hbm": hbm}
+    wgs, iters = 1024, 4000
+    fsink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    for name, dt in (("fp16", hq.HQ_DT_FP16), ("bf16", hq.HQ_DT_BF16), ("fp8", hq.HQ_DT_FP8_E4M3),
+                     ("fp4", hq.HQ_DT_FP4_E2M1), ("int8", hq.HQ_DT_INT8)):
+        hq.hq_probe_mfma(dt, wgs, 100, fsink)
+        e0.record()
+        flops = hq.hq_probe_mfma(dt, wgs, iters, fsink)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = flops / (e0.elapsed_time(e1) * 1e-3)
+    MEASURED.update(out)
+    spec = {"hbm": PEAK_HBM, **PEAK}
+    return {k: {"measured": round(v / (1e9 if k == "hbm" else 1e12), 1),
+                "unit": "GB/s" if k == "hbm" else ("TOP/s" if k == "int8" else "TFLOP/s"),
+                "spec": round(spec[k] / (1e9 if k == "hbm" else 1e12), 1), "frac_of_spec": round(v / spec[k], 3)}
+            for k, v in out.items()}
+
+
 def copy_probe(nbytes, reps):
     """A plain device-to-device copy of nbytes (read nbytes, write nbytes), reps times:
     the reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
@@ -774,6 +812,10 @@ def report(work, args, wall, per, cpu_budget=16.0):
     else:
         roof = dict(bound="hbm", achieved=round(B / t / 1e9, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
                     frac=round(B / t / PEAK_HBM, 4))
+    key = "hbm" if bound == "hbm" else work.dtype
+    if key in MEASURED:   # the same achieved rate against the probe-measured peak
+        roof.update(measured_peak=round(MEASURED[key] / (1e9 if key == "hbm" else 1e12), 1),
+                    frac_of_measured=round((B if key == "hbm" else F) / t / MEASURED[key], 4))
     roof.update(traffic=_traffic(work.name, Mr), kernel=dom, M=Mr, avg_us=round(t * 1e6, 2),
                 algorithmic_flops=F, algorithmic_bytes=B,
                 per_unit="2*M*N*K flops per launch" if bound == "mfma" else "algorithmic bytes per launch")
@@ -805,51 +847,95 @@ def report(work, args, wall, per, cpu_budget=16.0):
     return out
 
 
-def kernel_stats(csv_path, config, sweep=None, reps=REPS):
-    """Kernel-only time per M from a rocprofv3 kernel trace of
-    `bench.py --config <dense workload> --steps 0 --warmup 0 --no-cpu-baseline`.
-
-    The trace lists the dispatches in order; per M the run makes (2 + reps) x copies
-    calls (the capture's eager pass, the warm-up replay, the timed replays), each
-    launching the kernels hq_gemm_plan names.  Those are matched in order against
-    the trace (other kernels -- torch's, the setup's -- are skipped; a name that
-    does not match the plan aborts), and the kernel durations of each call are
-    summed.  Prints one JSON object: per M the median / p10 / p90 over calls."""
+def _dispatches(csv_path):
+    """The dispatches of a rocprofv3 kernel trace or counter collection (CSV), in
+    dispatch order: (kernel name, duration in us, {counter: value})."""
     import csv
-    rows = list(csv.DictReader(open(csv_path)))
-    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    by = {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            d = by.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"],
+                              (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3, {}])
+            if r.get("Counter_Name"):
+                d[2][r["Counter_Name"]] = float(r["Counter_Value"])
+    return [tuple(by[k]) for k in sorted(by)]
+
+
+def _base(name):
+    return name.split("<")[0].split("(")[0].replace("void ", "").strip().split("::")[-1]
+
+
+def _median_counters(ds):
+    keys = sorted({k for d in ds for k in d})
+    return {k: _pct([d.get(k, 0.0) for d in ds], 50) for k in keys}
+
+
+def kernel_stats(csv_path, config, sweep=None, reps=REPS, eager=False):
+    """Kernel-only time (and counters) per M from a rocprofv3 kernel trace or
+    counter collection of `bench.py --config <workload> --steps 0 --warmup 0
+    --no-cpu-baseline [--eager]`.
+
+    Dense workloads: the CSV lists the dispatches in order; per M the run makes
+    (2 + reps) x copies calls (graph capture's eager pass, the warm-up replay, the
+    timed replays; with --eager there is no capture pass), each launching the
+    kernels hq_gemm_plan names.  Those are matched in order against the CSV (other
+    kernels -- torch's, the setup's -- are skipped; a name that does not match the
+    plan aborts).  Per M: the summed kernel time of a call (median / p10 / p90 over
+    the timed calls), and per planned kernel its median duration and the median of
+    each collected counter.  MoE workloads (no plan): per kernel name over every
+    dispatch of the library's kernels.  Prints one JSON object."""
+    ds = _dispatches(csv_path)
+    if config not in _DRY:
+        groups = {}
+        for name, t, c in ds:
+            if not _is_torch_kernel(name):
+                groups.setdefault(_base(name), []).append((t, c))
+        out = {k: dict(dispatches=len(v), median_us=round(_pct([t for t, _ in v], 50), 2),
+                       p10_us=round(_pct([t for t, _ in v], 10), 2), p90_us=round(_pct([t for t, _ in v], 90), 2),
+                       counters=_median_counters([c for _, c in v])) for k, v in groups.items()}
+        print(json.dumps({"workload": config, "by_kernel": out}))
+        return
     desc = _DRY[config]()
     sweep = sweep or SWEEP
     ncopy = _ncopies(desc)
-    seq = []
-    for M in sweep:
-        plan = [p.split("<")[0] for p in hq.hq_gemm_plan(desc, M)]
-        seq.append((M, plan, (2 + reps) * ncopy))
+    untimed = (1 if eager else 2) * ncopy
     i, out = 0, []
-    for M, plan, ncalls in seq:
+    # the library's setup launches (activation quantisers) come before the sweep
+    first = _base(hq.hq_gemm_plan(desc, sweep[0])[0])
+    while i < len(ds) and _base(ds[i][0]) != first:
+        i += 1
+    if i == len(ds):
+        raise SystemExit(f"M={sweep[0]}: expected {first}, the trace has no such dispatch")
+    for M in sweep:
+        plan = hq.hq_gemm_plan(desc, M)
         calls = []
-        for _ in range(ncalls):
-            t = 0.0
-            for k in plan:
-                while i < len(rows) and not _is_hq_kernel(rows[i]["Kernel_Name"]):
+        for _ in range(untimed + reps * ncopy):
+            call = []
+            for item in plan:
+                k = _base(item)
+                while i < len(ds) and _is_torch_kernel(ds[i][0]):
                     i += 1
-                if i >= len(rows):
+                if i >= len(ds):
                     raise SystemExit(f"trace ended before M={M}")
-                nm = rows[i]["Kernel_Name"]
-                base = nm.split("<")[0].replace("void ", "").strip()
-                if base != k:
-                    raise SystemExit(f"M={M}: expected {k}, trace has {nm}")
-                t += (int(rows[i]["End_Timestamp"]) - int(rows[i]["Start_Timestamp"])) * 1e-3
+                if _base(ds[i][0]) != k:
+                    raise SystemExit(f"M={M}: expected {k}, trace has {ds[i][0]}")
+                call.append(ds[i])
                 i += 1
-            calls.append(t)
-        timed = calls[2 * ncopy:]
-        out.append(dict(M=M, kernels=plan, calls=len(timed), median_us=round(_pct(timed, 50), 2),
-                        p10_us=round(_pct(timed, 10), 2), p90_us=round(_pct(timed, 90), 2)))
+            calls.append(call)
+        timed = calls[untimed:]
+        tot = [sum(d[1] for d in c) for c in timed]
+        kern = []
+        for j, item in enumerate(plan):
+            ts = [c[j][1] for c in timed]
+            kern.append(dict(kernel=item, median_us=round(_pct(ts, 50), 2),
+                             counters=_median_counters([c[j][2] for c in timed])))
+        out.append(dict(M=M, calls=len(timed), median_us=round(_pct(tot, 50), 2), p10_us=round(_pct(tot, 10), 2),
+                        p90_us=round(_pct(tot, 90), 2), kernels=kern))
     print(json.dumps({"workload": config, "copies": ncopy, "kernel_only_us": out}))
 
 
-def _is_hq_kernel(name):
-    return any(k in name for k in ("skinny_kernel", "tile_gemm_kernel", "splitk_finalize_kernel"))
+def _is_torch_kernel(name):
+    return "at::native" in name or name.startswith("__amd_rocclr") or "at::" in name.split("(")[0]
 
 
 # descriptors of the dense workloads, for kernel_stats (no device memory needed)
@@ -885,6 +971,7 @@ def main():
                     "(for counter-collection runs)")
     ap.add_argument("--autotune", action="store_true",
                     help="also time every tuning override per M (dense workloads) and report the fastest")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the on-device peak probes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     ap.add_argument("--kernel-stats", default=None, metavar="CSV",
@@ -897,7 +984,7 @@ def main():
         sys.exit(2)
     sweep = [int(x) for x in args.sweep.split(",")] if args.sweep else None
     if args.kernel_stats:
-        kernel_stats(args.kernel_stats, args.config or "c2", sweep)
+        kernel_stats(args.kernel_stats, args.config or "c2", sweep, eager=args.eager)
         return
     torch.cuda.set_device(0)
     if args.copy_probe:
@@ -923,8 +1010,13 @@ def main():
         torch.cuda.empty_cache()
         return rec
 
+    peaks = None if args.no_peaks or args.eager else measure_peaks()
+    if peaks:
+        log("[bench] measured peaks " + json.dumps(peaks))
+
     if args.config is None:
         head = measure("c2", 16.0)
+        head["peaks"] = peaks
         head["configs"] = {}
         for nm in DEFAULT_EXTRA:
             rec = measure(nm, 3.0)
@@ -934,7 +1026,9 @@ def main():
         return
     names = list(WORKLOADS) if args.config == "all" else [args.config]
     for nm in names:
-        print(json.dumps(measure(nm, 16.0)), flush=True)
+        rec = measure(nm, 16.0)
+        rec["peaks"] = peaks
+        print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":

@@ -24,7 +24,17 @@ COMMON = [
     f"--offload-arch={ARCH}",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32) on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the weight-stream kernels scale each
+    # group's MFMA partial on the VALU, which otherwise copies every result out
+    # of the accumulator registers first (the M=64 W4A16 kernel: 1747 instead of
+    # 2218 instructions around its MFMAs, 270 instead of 326 VGPRs); the MFMA
+    # probe's independent chains need it too (in AGPRs the compiler shuffles
+    # half of them through copies every round)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
+
+
+EXTRA: dict = {}  # per-file flags
 
 
 def _hipcc() -> str:
@@ -33,7 +43,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -533,6 +533,25 @@ hq_status hq_silu_mul(int32_t dtype, int64_t rows, int64_t I, const void* gate_u
     return hip_status(silu_mul_launch(rows, I, gate_up, out, (hipStream_t)stream), "hq_silu_mul");
 }
 
+hq_status hq_probe_stream(const void* src, size_t bytes, void* sink, int32_t reps, hq_stream_t stream) {
+    if (bytes == 0 || bytes % 16 || reps < 1 || reps > 1000)
+        return set_error(HQ_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and reps 1..1000");
+    if (!src || !sink) return set_error(HQ_ERR_INVALID_ARG, "src and sink are required");
+    if (!aligned16(src) || !aligned16(sink)) return set_error(HQ_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+    return hip_status(probe_stream_launch(src, bytes, sink, reps, (hipStream_t)stream), "hq_probe_stream");
+}
+
+hq_status hq_probe_mfma(int32_t dtype, int64_t workgroups, int32_t iters, void* sink, hq_stream_t stream) {
+    if (dtype != HQ_DT_FP16 && dtype != HQ_DT_BF16 && dtype != HQ_DT_FP8_E4M3 && dtype != HQ_DT_FP4_E2M1 &&
+        dtype != HQ_DT_INT8)
+        return set_error(HQ_ERR_UNSUPPORTED, "dtype %d has no MFMA probe", dtype);
+    if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > 1000000)
+        return set_error(HQ_ERR_INVALID_ARG, "workgroups 1..65536 and iters 1..1000000");
+    if (!sink) return set_error(HQ_ERR_INVALID_ARG, "sink is required");
+    if (!aligned16(sink)) return set_error(HQ_ERR_ALIGNMENT, "sink must be 16-byte aligned");
+    return hip_status(probe_mfma_launch(dtype, workgroups, iters, sink, (hipStream_t)stream), "hq_probe_mfma");
+}
+
 hq_status hq_moe_align(int64_t T, int32_t top_k, int32_t num_experts, const int32_t* topk_ids,
                        int32_t* expert_offsets, int32_t* sorted_pairs, void* workspace, size_t ws_bytes,
                        hq_stream_t stream) {

@@ -96,6 +96,10 @@ hipError_t quant_e4m3_launch(int64_t M, int64_t K, const float* x, uint8_t* q, f
 hipError_t quant_mx_launch(bool fp4, int64_t M, int64_t K, const float* x, uint8_t* q, uint8_t* e, hipStream_t st);
 hipError_t silu_mul_launch(int64_t rows, int64_t I, const void* in, void* out, hipStream_t st);
 
+// measurement probes
+hipError_t probe_stream_launch(const void* src, size_t bytes, void* sink, int reps, hipStream_t st);
+hipError_t probe_mfma_launch(int dtype, int64_t workgroups, int iters, void* sink, hipStream_t st);
+
 // fill kernel used by hq_workspace_init
 hipError_t fill_zero_launch(void* p, size_t bytes, hipStream_t stream);
 

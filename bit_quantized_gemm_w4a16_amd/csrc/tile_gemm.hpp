@@ -1223,9 +1223,13 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
                 return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
             }
         }
-        if constexpr (has_big_tile(F))
-            if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
-        return launch_tile_kernel<F, 128, 128, 2, 4, 0>(p, st);
+        if constexpr (F == Fmt::W8A8_F8B) {
+            return hipErrorNotSupported;  // (returned above: no two-stage tiles are built for it)
+        } else {
+            if constexpr (has_big_tile(F))
+                if (pl.BM == 256) return launch_tile_kernel<F, 256, 128, 2, 4, 0>(p, st);
+            return launch_tile_kernel<F, 128, 128, 2, 4, 0>(p, st);
+        }
     }
 }
 

@@ -75,6 +75,8 @@ _SIGS = {
     "hq_moe_align": (C.c_int, [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]),
     "hq_moe_gather": (C.c_int, [C.c_int32, C.c_int64, C.c_int32, C.c_int64, _P, _P, _P, _P]),
     "hq_silu_mul": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, _P, _P, _P]),
+    "hq_probe_stream": (C.c_int, [_P, C.c_size_t, _P, C.c_int32, _P]),
+    "hq_probe_mfma": (C.c_int, [C.c_int32, C.c_int64, C.c_int32, _P, _P]),
 }
 
 
@@ -271,6 +273,22 @@ def hq_moe_align(T, top_k, num_experts, topk_ids, expert_offsets, sorted_pairs, 
 def hq_moe_gather(dtype, T, top_k, K, A, sorted_pairs, A_sorted, stream=None) -> None:
     _check(lib().hq_moe_gather(dtype, T, top_k, K, _dp(A), _dp(sorted_pairs), _dp(A_sorted), _stream(stream)),
            "hq_moe_gather")
+
+
+def hq_probe_stream(src, nbytes, sink, reps=1, stream=None) -> None:
+    """Read nbytes of src `reps` times (a measurement of the attainable HBM read rate)."""
+    _check(lib().hq_probe_stream(_dp(src), nbytes, _dp(sink), reps, _stream(stream)), "hq_probe_stream")
+
+
+# flops (int8: ops) of one MFMA of each probed type
+PROBE_MFMA_FLOPS = {HQ_DT_FP16: 16384, HQ_DT_BF16: 16384, HQ_DT_FP8_E4M3: 65536, HQ_DT_FP4_E2M1: 65536,
+                    HQ_DT_INT8: 32768}
+
+
+def hq_probe_mfma(dtype, workgroups, iters, sink, stream=None) -> float:
+    """Run the dense MFMA probe; returns the flops (int8: ops) the call performs."""
+    _check(lib().hq_probe_mfma(dtype, workgroups, iters, _dp(sink), _stream(stream)), "hq_probe_mfma")
+    return float(workgroups) * 4 * iters * 8 * PROBE_MFMA_FLOPS[dtype]
 
 
 def hq_silu_mul(dtype, rows, I, gate_up, out, stream=None) -> None:

@@ -402,6 +402,28 @@ hq_status hq_moe_align(int64_t T, int32_t top_k, int32_t num_experts, const int3
 hq_status hq_moe_gather(int32_t dtype, int64_t T, int32_t top_k, int64_t K, const void* A,
                         const int32_t* sorted_pairs, void* A_sorted, hq_stream_t stream);
 
+/*
+ * Measurement probes (not part of the GEMM path): what the device delivers, for
+ * setting kernel timings against measured as well as published peaks.
+ *
+ * hq_probe_stream: reads the `bytes` of device buffer src once per repetition
+ * (16-byte non-temporal loads, grid-stride, 4096 workgroups of 256 threads),
+ * `reps` times back to back on `stream`; nothing is written in practice (sink,
+ * 16 device bytes, is stored to only if the XOR of all loaded words takes one
+ * fixed value).  bytes a positive multiple of 16, src and sink 16-byte aligned,
+ * reps 1..1000.
+ *
+ * hq_probe_mfma: `workgroups` workgroups of 4 waves; each wave runs `iters`
+ * rounds of 8 independent MFMAs of the dense 16x16 instruction of `dtype` on
+ * register operands: HQ_DT_FP16 / HQ_DT_BF16 16x16x32 (16384 flops each),
+ * HQ_DT_FP8_E4M3 and HQ_DT_FP4_E2M1 16x16x128 (65536), HQ_DT_INT8 16x16x64
+ * (32768 ops); flops per call = workgroups * 4 * iters * 8 * that.  sink: device
+ * fp32 [workgroups * 256], written (one sum per thread).  workgroups 1..65536,
+ * iters 1..1000000.
+ */
+hq_status hq_probe_stream(const void* src, size_t bytes, void* sink, int32_t reps, hq_stream_t stream);
+hq_status hq_probe_mfma(int32_t dtype, int64_t workgroups, int32_t iters, void* sink, hq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

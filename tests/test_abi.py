@@ -237,3 +237,19 @@ def test_repack_rejects_bad_buffers():
     q = np.zeros((16, 16), np.uint32)
     s = np.zeros((1, 16), np.uint16)
     assert status_of(hq.hq_repack, d, q, s, None) == hq.HQ_ERR_INVALID_ARG
+
+
+def test_probe_argument_checks_need_no_gpu():
+    """The measurement probes reject bad arguments before any device call."""
+    with pytest.raises(hq.HQError) as e:
+        hq.hq_probe_stream(None, 100, None, 1, stream=0)        # not a multiple of 16
+    assert e.value.status == hq.HQ_ERR_INVALID_ARG
+    with pytest.raises(hq.HQError) as e:
+        hq.hq_probe_stream(None, 1024, None, 1, stream=0)       # no buffers
+    assert e.value.status == hq.HQ_ERR_INVALID_ARG
+    with pytest.raises(hq.HQError) as e:
+        hq.hq_probe_mfma(hq.HQ_DT_FP32, 1, 1, None, stream=0)   # no fp32 probe
+    assert e.value.status == hq.HQ_ERR_UNSUPPORTED
+    with pytest.raises(hq.HQError) as e:
+        hq.hq_probe_mfma(hq.HQ_DT_FP16, 0, 1, None, stream=0)
+    assert e.value.status == hq.HQ_ERR_INVALID_ARG
