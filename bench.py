@@ -698,15 +698,15 @@ def tune_table(work, log_fn=log):
                  gain=round(base / b, 3)) for M, (t, b, base) in table.items()]
 
 
-# The sources the counted kernel (the dense W4A16 tile GEMM and its launch) is
-# built from: counter figures taken on other versions of them are stale.
-KERNEL_SOURCES = ["bit_quantized_gemm_w4a16_amd/csrc/" + f for f in
-                  ("tile_gemm.hpp", "skinny.hpp", "hq_device.hpp", "hq_internal.h", "hq_common.h", "k_wna16.hip")]
-KERNEL_SOURCES.append("include/hq.h")
+# The library's sources: counter figures taken on other versions of them are stale.
+KERNEL_SOURCES = sorted("bit_quantized_gemm_w4a16_amd/csrc/" + f
+                        for f in os.listdir(os.path.join(ROOT, "bit_quantized_gemm_w4a16_amd", "csrc"))
+                        if f.endswith((".hip", ".hpp", ".h", ".cpp")))
+KERNEL_SOURCES += ["include/hq.h", "bit_quantized_gemm_w4a16_amd/build.py"]   # (the build flags shape the code too)
 
 
 def kernel_source_hash():
-    """Hash of the counted kernel's sources; counter figures taken on other sources are stale."""
+    """Hash of the library's sources; counter figures taken on other sources are stale."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -716,17 +716,19 @@ def kernel_source_hash():
 
 
 def _traffic(workload, M):
-    """HBM bytes per launch from the committed counter runs (profiles/traffic.json):
+    """HBM bytes at M from the committed counter runs (profiles/traffic.json):
     FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by the factor the same counter
-    gives on a plain device copy of known size.  None when absent or stale."""
+    gives on a plain device copy of known size; `kernel_bytes` for one launch of the
+    call's main kernel, `call_bytes` for all of the call's launches.  None when
+    absent or taken on other sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh).get(workload)
-    if not rec or rec.get("M") != M or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("per_M", {}).get(str(M))
 
 
 MEASURED = {}   # on-device peaks from the library's probes (filled by measure_peaks)
@@ -787,12 +789,16 @@ def report(work, args, wall, per, cpu_budget=16.0):
     for M in work.sweep:
         t = statistics.median(per[M])
         F, B = work.flops(M), work.bytes(M)
-        row = dict(M=M, us=round(t * 1e6, 2), us_p10=round(_pct(per[M], 10) * 1e6, 2),
+        row = dict(M=M, flops=F, bytes=B, us=round(t * 1e6, 2), us_p10=round(_pct(per[M], 10) * 1e6, 2),
                    us_p90=round(_pct(per[M], 90) * 1e6, 2), tflops=round(F / t / 1e12, 2),
                    gbps=round(B / t / 1e9, 1), hbm_frac=round(B / t / PEAK_HBM, 3),
                    mfma_frac=round(F / t / peak, 3), roofline_frac=round(max(B / PEAK_HBM, F / peak) / t, 3))
-        if hasattr(work, "routing_us"):
+        if hasattr(work, "routing_us") and not args.eager:   # (eager: counter runs, no extra launches)
             row["routing_us"] = work.routing_us(M)
+        tr = _traffic(work.name, M)
+        if tr:   # HBM bytes of the whole call from the counter runs, against the algorithmic bytes
+            row["traffic_bytes"] = tr["call_bytes"]
+            row["traffic_ratio"] = round(tr["call_bytes"] / B, 3)
         table.append(row)
         name, bound = work.kernel_of(M)
         k = kern.setdefault(name, dict(t=0.0))
@@ -816,7 +822,8 @@ def report(work, args, wall, per, cpu_budget=16.0):
     if key in MEASURED:   # the same achieved rate against the probe-measured peak
         roof.update(measured_peak=round(MEASURED[key] / (1e9 if key == "hbm" else 1e12), 1),
                     frac_of_measured=round((B if key == "hbm" else F) / t / MEASURED[key], 4))
-    roof.update(traffic=_traffic(work.name, Mr), kernel=dom, M=Mr, avg_us=round(t * 1e6, 2),
+    tr = _traffic(work.name, Mr)
+    roof.update(traffic=tr["kernel_bytes"] if tr else None, kernel=dom, M=Mr, avg_us=round(t * 1e6, 2),
                 algorithmic_flops=F, algorithmic_bytes=B,
                 per_unit="2*M*N*K flops per launch" if bound == "mfma" else "algorithmic bytes per launch")
     cpu = None if args.no_cpu_baseline else work.cpu_baseline(cpu_budget)
