@@ -23,6 +23,7 @@ def _write_trace(path, config, sweep, dur_of):
     ncopy = bench._ncopies(desc)
     rows, t, did = [], 1000, 1
     rows.append(("void at::native::fill_kernel<float>(int)", 5000))
+    rows.append(("void quant_mx_kernel<true>(QuantArgs)", 5000))
     for M in sweep:
         plan = hq.hq_gemm_plan(desc, M)
         for c in range((2 + bench.REPS) * ncopy):
@@ -56,12 +57,38 @@ def test_kernel_stats_attributes_dispatches_per_M(tmp_path):
                           "--sweep", "1,16,8192"], capture_output=True, text=True, check=True)
     rec = json.loads(out.stdout.strip().splitlines()[-1])
     by = {r["M"]: r for r in rec["kernel_only_us"]}
-    assert by[1]["kernels"] == ["skinny_kernel"]
-    assert by[16]["kernels"] == ["skinny_kernel", "splitk_finalize_kernel"]
+    assert [k["kernel"].split("<")[0] for k in by[1]["kernels"]] == ["skinny_kernel"]
     assert by[1]["calls"] == bench.REPS * ncopy_ref[0]
     # M=1: one kernel of 10 us + 1 ns + {0,10,20} ns; M=16: 10 + 3 us + 2*16 ns + ...
     assert 10.0 <= by[1]["p10_us"] <= by[1]["median_us"] <= by[1]["p90_us"] <= 10.03
     assert 13.03 <= by[16]["median_us"] <= 13.06
+    assert [k["kernel"].split("<")[0] for k in by[16]["kernels"]] == ["skinny_kernel", "splitk_finalize_kernel"]
+    assert 3.0 <= by[16]["kernels"][1]["median_us"] <= 3.03
+
+
+def test_kernel_stats_reads_counter_collections(tmp_path):
+    """A counter collection has one row per (dispatch, counter); --eager runs
+    have no capture pass."""
+    desc = bench._DRY["c3"]()
+    ncopy = bench._ncopies(desc)
+    p = tmp_path / "pmc.csv"
+    did, t = 1, 0
+    with open(p, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                    "End_Timestamp"])
+        for M in (1, 8192):
+            for c in range((1 + bench.REPS) * ncopy):
+                for item in hq.hq_gemm_plan(desc, M):
+                    for cn, cv in (("FETCH_SIZE", 100.0 * M), ("WRITE_SIZE", 7.0 + (c >= ncopy))):
+                        w.writerow([did, "void " + item.split(" ")[0] + "(TileArgs)", cn, cv, t, t + 2000])
+                    did += 1
+                    t += 3000
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--kernel-stats", str(p), "--config", "c3",
+                          "--sweep", "1,8192", "--eager"], capture_output=True, text=True, check=True)
+    rec = json.loads(out.stdout.strip().splitlines()[-1])
+    big = rec["kernel_only_us"][1]
+    assert big["M"] == 8192 and big["kernels"][0]["counters"] == {"FETCH_SIZE": 819200.0, "WRITE_SIZE": 8.0}
 
 
 def test_kernel_stats_rejects_a_trace_of_another_plan(tmp_path):
