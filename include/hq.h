@@ -6,7 +6,13 @@
  * for weight-only W4A16 (symmetric INT4, or UINT4 with zero-points; group
  * scales along K), W4A8 with MXFP4 weights (e2m1 codes, E8M0 scale per 32 K)
  * and tokenwise FP8-e4m3 activations, W8A8 INT8 with a per-token x
- * per-channel epilogue, and the MoE Indexed / Grouped variants.
+ * per-channel epilogue, and the MoE Indexed / Grouped variants; further
+ * W4A4 (MXFP4 x MXFP4) and MXFP8 x MXFP4 with the activations' own E8M0
+ * scales, FP8 W8A8 with blockwise scales (1 x 128 activation blocks, 128 x 128
+ * weight blocks), and 16-bit activations with FP4 weights (MXFP4, or NVFP4
+ * with E4M3 scales per 16 K and a per-tensor second-level scale).  A layer
+ * descriptor may ask for a batch-invariant reduction order or override the
+ * kernel choice (tuning); two probes measure the device's attainable peaks.
  *
  * Sources.  The operation and its parameters follow the Humming pages:
  *  - "Humming wird angekuendigt", section "Eine einheitliche
