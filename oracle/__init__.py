@@ -73,6 +73,8 @@ def lib():
         L.hq_oracle_gemm_fp8_blockwise.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
         L.hq_oracle_gemm_fp4_a16.restype = C.c_int
         L.hq_oracle_gemm_fp4_a16.argtypes = [i64, i64, i64, C.c_int, p, p, C.c_int, p, p, p, i64, p]
+        L.hq_oracle_gemm_mxint4_a16.restype = C.c_int
+        L.hq_oracle_gemm_mxint4_a16.argtypes = [i64, i64, i64, C.c_int, p, p, p, p, i64, p]
         L.hq_oracle_gemm_w8a8.restype = C.c_int
         L.hq_oracle_gemm_w8a8.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p, p]
         L.hq_oracle_moe_route.restype = C.c_int
@@ -224,6 +226,19 @@ def gemm_fp4_a16(A, q, scales, *, N, K, a_bf16: bool, nvfp4: bool, s2=None, rows
                                       _ptr(_c(scales, np.uint8)), _ptr(s2a), _ptr(r), R, _ptr(out))
     if rc:
         raise ValueError(f"oracle gemm_fp4_a16 failed ({rc})")
+    return out
+
+
+def gemm_mxint4_a16(A, q, e8, *, N, K, a_bf16: bool = True, rows=None):
+    """MXINT4 weights (two's-complement INT4, E8M0 per 32 K) with 16-bit activations, fp64."""
+    A = _c(A, np.uint16)
+    M = A.shape[0]
+    r, R = _rows(rows, M)
+    out = np.empty((R, N), dtype=np.float64)
+    rc = lib().hq_oracle_gemm_mxint4_a16(M, N, K, int(a_bf16), _ptr(A), _ptr(_c(q, np.uint32)),
+                                         _ptr(_c(e8, np.uint8)), _ptr(r), R, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle gemm_mxint4_a16 failed ({rc})")
     return out
 
 

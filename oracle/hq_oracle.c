@@ -360,6 +360,33 @@ int hq_oracle_gemm_fp4_a16(int64_t M, int64_t N, int64_t K, int a_bf16, const ui
     return 0;
 }
 
+/* MXINT4 weights with 16-bit activations: two's-complement INT4 codes (-8..7)
+ * with one E8M0 scale per 32 consecutive K of a column (the OCP MX integer
+ * element type MXINT4 under the MX block scale):
+ *   W_real[k][n] = int4(q[k][n]) * 2^(e8[k/32][n] - 127),  D = A x W_real (fp64).
+ * q uint32 [K/8][N] (4-bit layout above), e8 uint8 [K/32][N]. */
+int hq_oracle_gemm_mxint4_a16(int64_t M, int64_t N, int64_t K, int a_bf16, const uint16_t* A, const uint32_t* q,
+                              const uint8_t* e8, const int64_t* rows, int64_t nrows, double* out)
+{
+    if (K % 32) return 1;
+    int64_t R = rows ? nrows : M;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(R * K + 1));
+    if (!a) return 2;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k) a[r * K + k] = act16(a_bf16, A[row_of(rows, r) * K + k]);
+    memset(out, 0, sizeof(double) * (size_t)(R * N));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int code = (int)nib_along_k(q, N, k, n);
+            code = code >= 8 ? code - 16 : code;
+            double w = (double)code * hq_oracle_e8m0(e8[(k / 32) * N + n]);
+            for (int64_t r = 0; r < R; ++r) out[r * N + n] += a[r * K + k] * w;
+        }
+    free(a);
+    return 0;
+}
+
 /* FP8 W8A8 with blockwise scales: A_real[m][k] = e4m3(qa[m][k]) * sa[m][k/128],
  * W_real[k][n] = e4m3(w[k][n]) * sw[k/128][n/128], D = A_real x W_real.
  * qa uint8 [M][K], sa fp32 [M][K/128], w uint8 [K][N], sw fp32 [K/128][ceil(N/128)]. */

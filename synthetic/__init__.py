@@ -206,6 +206,16 @@ def w4a16_fp4(seed, M, N, K, nvfp4: bool, dtype=torch.bfloat16, cfg=C7):
     return out
 
 
+C8 = 8  # MXINT4 weights with 16-bit activations
+
+
+def w4a16_mxint4(seed, M, N, K, dtype=torch.bfloat16, cfg=C8):
+    """MXINT4 WnA16: N(0,1) activations rounded to bf16, INT4 codes uniform over all 16
+    (two's complement -8..7), E8M0 exponents in [118, 127] per 32 K."""
+    return dict(A=activations(seed, cfg, M, K, dtype), q=random_words(seed, cfg, T_Q, (K // 8, N)),
+                e=e8m0_exponents(seed, cfg, (K // 32, N)))
+
+
 def moe_expert_mxfp4(seed, e, N, K, cfg=C5):
     """One expert's MXFP4 weights (codes + E8M0), drawn from the expert's own stream."""
     return (random_words(seed, cfg, T_Q, (K // 8, N), e),

@@ -666,3 +666,60 @@ def test_fp4_a16_nvfp4_group_of_16_indexing():
     w = e2m1_tab(unpack_k(d["q"], K))[80:96, 7]
     delta = a[:, 80:96] @ w * (1.0 - E4M3_LUT[d["s"][5, 7]])
     assert rel_err(got[:, 7] - base[:, 7], delta) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# MXINT4 weights (two's-complement INT4, E8M0 per 32 K) with bf16 activations
+# ---------------------------------------------------------------------------
+
+def test_mxint4_a16_exact_rational():
+    M, N, K = 2, 16, 64
+    d = syn.w4a16_mxint4(0, M, N, K)
+    got = oracle.gemm_mxint4_a16(d["A"], d["q"], d["e"], N=N, K=K)
+    a = torch16(d["A"], torch.bfloat16)
+    codes = unpack_k(d["q"], K)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                c = int(codes[k, n])
+                c = c - 16 if c >= 8 else c
+                acc += Fraction(float(a[m, k])) * c * Fraction(2) ** (int(d["e"][k // 32, n]) - 127)
+            assert abs(got[m, n] - float(acc)) <= 1e-13 * max(abs(float(acc)), 1e-30)
+
+
+def test_mxint4_a16_unit_scales_equal_symmetric_w4a16():
+    """With every E8M0 exponent 127 (scale 1) MXINT4 is symmetric INT4 W4A16 with unit group scales."""
+    M, N, K = 5, 40, 256
+    d = syn.w4a16_mxint4(1, M, N, K)
+    e = np.full((K // 32, N), 127, np.uint8)
+    got = oracle.gemm_mxint4_a16(d["A"], d["q"], e, N=N, K=K)
+    ones = np.full((K // 128, N), 0x3F80, np.uint16)
+    ref = oracle.gemm_wna16(d["A"], d["q"], ones, None, N=N, K=K, G=128, a_bf16=True, w_signed=True)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_mxint4_a16_single_weight_and_block_step():
+    """A lone code 0x8 decodes to -8 at its (k, n); raising one block's exponent by one
+    doubles exactly that block's contribution of that column."""
+    M, N, K = 3, 16, 128
+    d = syn.w4a16_mxint4(2, M, N, K)
+    a = torch16(d["A"], torch.bfloat16).astype(np.float64)
+    q = np.zeros((K // 8, N), np.uint32)
+    k0, n0 = 37, 5
+    q[k0 // 8, n0] = np.uint32(0x8) << np.uint32(4 * (k0 % 8))
+    e = np.full((K // 32, N), 127, np.uint8)
+    got = oracle.gemm_mxint4_a16(d["A"], q, e, N=N, K=K)
+    want = np.zeros((M, N))
+    want[:, n0] = -8.0 * a[:, k0]
+    np.testing.assert_array_equal(got, want)
+    base = oracle.gemm_mxint4_a16(d["A"], d["q"], d["e"], N=N, K=K)
+    e2 = d["e"].copy()
+    e2[2, 7] += 1
+    moved = oracle.gemm_mxint4_a16(d["A"], d["q"], e2, N=N, K=K)
+    codes = unpack_k(d["q"], K).astype(np.int64)
+    codes = np.where(codes >= 8, codes - 16, codes)
+    blk = a[:, 64:96] @ (codes[64:96, 7] * 2.0 ** (int(d["e"][2, 7]) - 127))
+    np.testing.assert_allclose(moved[:, 7] - base[:, 7], blk, rtol=1e-12, atol=1e-12)
+    other = [n for n in range(N) if n != 7]
+    np.testing.assert_array_equal(moved[:, other], base[:, other])
