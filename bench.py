@@ -9,7 +9,7 @@ zero-points and fp16 scales per 128 K, N=4096, K=7168), the configuration
 the metric is quoted on; its line also carries, under "configs", the same
 measurement of every other workload (dense W4A8-MXFP4, W8A8-INT8, the MoE
 gate-up on the Indexed path with its routing timed apart, W4A4 MXFP4 x MXFP4,
-MXFP8 x MXFP4, FP8 W8A8 with blockwise scales, bf16 x MXFP4 and NVFP4 WnA16).
+MXFP8 x MXFP4, FP8 W8A8 with blockwise scales, bf16 x MXFP4, NVFP4 and MXINT4 WnA16).
 --config NAME measures one workload alone (c5g: the MoE Grouped path, c5l:
 the whole MoE layer the pages time, gate-up + SwiGLU + down).
 
@@ -566,6 +566,40 @@ class DenseFP4A16:
                     sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
 
 
+class DenseMXINT4A16(DenseFP4A16):
+    """bf16 activations x MXINT4 weights (two's-complement INT4, E8M0 per 32 K) at the
+    dense W4A16 layer's shape, N=4096, K=7168."""
+
+    def __init__(self, N=4096, K=7168, Mmax=8192, sweep=SWEEP):
+        self.N, self.K, self.Mmax, self.sweep, self.nv = N, K, Mmax, sweep, False
+        self.dtype = "bf16"
+        self.name = f"dense_w4a16_mxint4_bf16_N{N}_K{K}"
+        log(f"[bench] generating {self.name}")
+        d = syn.w4a16_mxint4(0, Mmax, N, K)
+        self.host = d
+        self.desc = hq.desc_mxint4_a16(N, K)
+        wp, sp, _ = hq.hq_repack(self.desc, d["q"], d["e"])
+        self.wbytes = wp.size + sp.size
+        self.copies = _copies((dev(wp), dev(sp), None), self.wbytes)
+        self.A = dev(d["A"])
+        self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in sweep)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def kernel_of(self, M):
+        if M <= 64:
+            return ("skinny_kernel<MXINT4_BF16> (M<=64)", "hbm")
+        return ("tile_gemm_kernel<MXINT4_BF16> (M>64)", "mfma" if M >= 128 else "hbm")
+
+    def cpu_baseline(self, budget_s=8.0):
+        import oracle
+        d = self.host
+        f = lambda rows: oracle.gemm_mxint4_a16(d["A"], d["q"], d["e"], N=self.N, K=self.K, rows=rows)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, self.Mmax)), budget_s)
+        return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(), kind="oracle",
+                    sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
+
+
 WORKLOADS = {
     "c1": lambda: DenseW4A16(N=1024, K=1024, Mmax=16, bf16=True, zp=False, sweep=[16],
                              name="dense_w4a16_sym_bf16_M16_N1024_K1024"),
@@ -580,9 +614,10 @@ WORKLOADS = {
     "fp8b": lambda: DenseFP8Blockwise(),
     "mxfp4a16": lambda: DenseFP4A16(nvfp4=False),
     "nvfp4a16": lambda: DenseFP4A16(nvfp4=True),
+    "mxint4a16": lambda: DenseMXINT4A16(),
 }
 # the workloads the default run measures besides the headline one (c2)
-DEFAULT_EXTRA = ["c3", "c4", "c5", "w4a4", "w4a8mx", "fp8b", "mxfp4a16", "nvfp4a16"]
+DEFAULT_EXTRA = ["c3", "c4", "c5", "w4a4", "w4a8mx", "fp8b", "mxfp4a16", "nvfp4a16", "mxint4a16"]
 
 
 # ---------------------------------------------------------------------------
@@ -955,6 +990,7 @@ _DRY = {
     "fp8b": lambda: hq.desc_fp8_blockwise(7168, 7168),
     "mxfp4a16": lambda: hq.desc_fp4_a16(4096, 7168, False),
     "nvfp4a16": lambda: hq.desc_fp4_a16(4096, 7168, True),
+    "mxint4a16": lambda: hq.desc_mxint4_a16(4096, 7168),
 }
 
 

@@ -86,7 +86,20 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
     I.E = d->num_experts ? d->num_experts : 1;
     I.G = d->group_size;
     const int a = d->a_dtype, w = d->w_dtype;
-    if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT4 || w == HQ_DT_UINT4)) {
+    if (w == HQ_DT_INT4 && a == HQ_DT_BF16 && d->w_scale_dtype == HQ_DT_E8M0) {
+        // MXINT4: two's-complement INT4 codes with one E8M0 scale per 32 K (the
+        // FP4 weight-only path with an integer decode)
+        I.kind = Kind::FP4_A16;
+        I.i4 = true;
+        if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 is dense-only");
+        if (d->w_scale_gran != HQ_GRAN_PER_GROUP_K || d->group_size != 32)
+            return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 needs E8M0 scales per 32 K elements");
+        if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x MXINT4 takes no activation scale");
+        if (d->K % 128) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 needs K %% 128 == 0 (K=%lld)", (long long)d->K);
+        if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 takes no zero-points");
+        if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x MXINT4 outputs bf16");
+        I.G = 32;
+    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT4 || w == HQ_DT_UINT4)) {
         I.kind = Kind::WNA16;
         I.a_bf16 = a == HQ_DT_BF16;
         I.zp = w == HQ_DT_UINT4;
@@ -199,7 +212,9 @@ static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
         case Kind::W8A8: return hip_status(w8a8_launch(a, L.out_i32), "hq_gemm(W8A8)");
         case Kind::MXA_MX: return hip_status(mx_act_launch(a, L.a_fp4), L.a_fp4 ? "hq_gemm(W4A4-MXFP4)" : "hq_gemm(W4A8-MXFP8xMXFP4)");
         case Kind::FP8_BLOCK: return hip_status(fp8_block_launch(a), "hq_gemm(FP8-blockwise)");
-        case Kind::FP4_A16: return hip_status(fp4_a16_launch(a, L.nv), L.nv ? "hq_gemm(NVFP4-A16)" : "hq_gemm(MXFP4-A16)");
+        case Kind::FP4_A16:
+            return hip_status(fp4_a16_launch(a, L.nv ? 1 : L.i4 ? 2 : 0),
+                              L.nv ? "hq_gemm(NVFP4-A16)" : L.i4 ? "hq_gemm(MXINT4-A16)" : "hq_gemm(MXFP4-A16)");
         default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind runs through hq_moe_gemm");
     }
 }

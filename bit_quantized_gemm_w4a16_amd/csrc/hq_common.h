@@ -29,6 +29,7 @@ struct LayerInfo {
     bool out_i32;  // W8A8: raw int32 accumulators
     bool a_fp4;    // MXA_MX: E2M1 activations (else E4M3)
     bool nv;       // FP4_A16: NVFP4 (E4M3 per 16 K, per-tensor second-level scale), else MXFP4
+    bool i4;       // FP4_A16: MXINT4 (two's-complement INT4 codes, E8M0 per 32 K) instead of e2m1
     bool invariant;        // HQ_FLAG_BATCH_INVARIANT
     int tune_path, tune_splits;  // HQ_TUNE override (0, 0: the library's choice)
 };

@@ -43,6 +43,8 @@
 //                   to bf16 (exact) with the lane's E8M0 byte
 //   NVFP4_BF16      the same with the lane's two E4M3 group scales (16 K each)
 //                   and the per-tensor fp32 second-level scale on the output
+//   MXINT4_BF16     the same with two's-complement INT4 codes: sign-extended,
+//                   scaled by 2^(E-127) in fp32 and rounded to bf16 (exact)
 //   W8A8_F8B        1 x the scaled MFMA on fp8 x fp8 per chunk (one 128-K scale
 //                   block), its partial scaled by the row's activation block
 //                   scale times the strip's weight block scale (both in LDS)
@@ -88,7 +90,7 @@ struct SkinnyTraits {
     static constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
     static constexpr bool MX = mx_mfma(F);               // E8M0 weight scales per 32 K
     static constexpr bool MXA = mx_act(F);               // E8M0 activation scales per 32 K
-    static constexpr bool FP4B = F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16;  // e2m1 -> bf16 operands
+    static constexpr bool FP4B = F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16;  // 4-bit -> bf16 operands
     static constexpr int SB = F == Fmt::NVFP4_BF16 ? 128 : 64;  // scale bytes per strip and chunk
     static constexpr int AROW = FmtTraits<F>::AROW;      // bytes of a row per 128-K chunk
     static constexpr int UPC = AROW / 16;                // 16-byte A units per 128-K chunk and row
@@ -390,8 +392,9 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     if (!valid) sf0 = sf1 = 0.f;  // a chunk past the wave's part contributes exactly zero
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const Frag8 b = F == Fmt::NVFP4_BF16 ? fp4_to_bf16_mul(w[i][sp][0][t], t < 2 ? sf0 : sf1)
-                                                             : fp4_to_bf16(w[i][sp][0][t], sf0);
+                        const Frag8 b = F == Fmt::NVFP4_BF16    ? fp4_to_bf16_mul(w[i][sp][0][t], t < 2 ? sf0 : sf1)
+                                        : F == Fmt::MXINT4_BF16 ? int4_to_bf16(w[i][sp][0][t], sf0)
+                                                                : fp4_to_bf16(w[i][sp][0][t], sf0);
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt) acc2[t & 1][sp][mt] = mfma16<true>(af[mt][t], b, acc2[t & 1][sp][mt]);
                     }
@@ -591,7 +594,7 @@ inline SkinnyLds skinny_lds(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) 
     } else if (mx_mfma(F)) {
         s = al(NS * cmax * 64);
         if (mx_act(F)) z = al(rows * cmax * 4);
-    } else if (F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16) {
+    } else if (F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16) {
         s = al(NS * cmax * (F == Fmt::NVFP4_BF16 ? 128 : 64));
     } else if (F == Fmt::W8A8_F8B) {
         s = al(NS * cmax * 4);
@@ -628,7 +631,8 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
     // strips alone leave a quarter of the chip idle (or the slice must shrink)
     // 16-bit A at 9..16 rows (two strips per workgroup): two workgroups per CU
     // (four slices at N=4096: 11.2 against 11.9 us with two)
-    const bool a16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16;
+    const bool a16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 ||
+                     F == Fmt::MXINT4_BF16;
     const int64_t target = a16 && p.NS == 2 ? 512 : 256;
     int64_t S = p.groups_x >= 192 ? 1 : cdiv(target, p.groups_x);
     const int64_t smax = nc / WK > 0 ? nc / WK : 1;

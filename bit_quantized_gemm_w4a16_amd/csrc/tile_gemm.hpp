@@ -44,6 +44,8 @@
 //   NVFP4_BF16  bf16 A x e2m1 B with an E4M3 scale per 16 K (e2m1 x e4m3 has
 //               at most 5 significant bits: the product is exact in bf16) and
 //               the per-tensor fp32 second-level scale in the epilogue
+//   MXINT4_BF16 bf16 A x two's-complement INT4 B with E8M0 per 32 K (MXINT4):
+//               q x 2^(E-127) in fp32, rounded to bf16 (exact: 3 significant bits)
 #pragma once
 
 #include <type_traits>
@@ -53,13 +55,14 @@
 
 namespace hq {
 
-enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B, MXFP4_BF16, NVFP4_BF16 };
+enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B, MXFP4_BF16, NVFP4_BF16,
+                 MXINT4_BF16 };
 
 constexpr const char* fmt_name(Fmt F) {
     return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
          : F == Fmt::W8A8_I8 ? "W8A8_I8" : F == Fmt::MOE_MX ? "MOE_MX" : F == Fmt::W4A8_MXA ? "W4A8_MXA"
          : F == Fmt::W4A4_MX ? "W4A4_MX" : F == Fmt::W8A8_F8B ? "W8A8_F8B" : F == Fmt::MXFP4_BF16 ? "MXFP4_BF16"
-         : "NVFP4_BF16";
+         : F == Fmt::NVFP4_BF16 ? "NVFP4_BF16" : "MXINT4_BF16";
 }
 // Formats whose activations carry OCP MX scales (E8M0 per 32 K, [rows][K/32]).
 constexpr bool mx_act(Fmt F) { return F == Fmt::W4A8_MXA || F == Fmt::W4A4_MX; }
@@ -79,8 +82,11 @@ template <> struct FmtTraits<Fmt::W4A4_MX> { static constexpr int AROW = 64, BST
 template <> struct FmtTraits<Fmt::W8A8_F8B> { static constexpr int AROW = 128, BSTRIP = 2048; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::MXFP4_BF16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::NVFP4_BF16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::MXINT4_BF16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
 // e2m1 weights converted to bf16 operands with a per-lane scale (bf16 MFMA)
-constexpr bool fp4_bf16(Fmt F) { return F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16; }
+constexpr bool fp4_bf16(Fmt F) {
+    return F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16;
+}
 
 // Work description of one launch.  Dense launches leave the MoE fields null.
 struct TileArgs {
@@ -186,6 +192,21 @@ __device__ __forceinline__ Frag8 fp4_to_bf16_mul(uint32_t w, float s) {
     return f;
 }
 
+// two's-complement INT4 x 2^(e-127) -> bf16, exact (at most 3 significant bits);
+// 8 natural-order codes of one word, in the element order of fp4_to_bf16
+__device__ __forceinline__ Frag8 int4_to_bf16(uint32_t w, float scale) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+    Frag8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int lo = (int)(w << (28 - 8 * i)) >> 28, hi = (int)(w << (24 - 8 * i)) >> 28;
+        const f2v v = f2v{(float)lo * scale, (float)hi * scale};
+        f.u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2v));
+    }
+    return f;
+}
+
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     e &= 0xFFu;
     return __uint_as_float(e == 0 ? 0x00400000u : e == 255u ? 0x7FC00000u : (e << 23));
@@ -227,7 +248,7 @@ void tile_gemm_kernel(TileArgs p) {
     using Acc = typename T::Acc;
     constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
     constexpr bool NV = F == Fmt::NVFP4_BF16;             // E4M3 weight scales per 16 K
-    constexpr bool MX = mx_mfma(F) || F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || NV;  // byte scales per lane
+    constexpr bool MX = mx_mfma(F) || F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::MXINT4_BF16 || NV;  // byte scales per lane
     constexpr bool MXA = mx_act(F);
     constexpr bool F8B = F == Fmt::W8A8_F8B;
     static_assert(!F8B || BN == 128, "blockwise fp8: one 128-column weight block per tile");
@@ -568,6 +589,7 @@ void tile_gemm_kernel(TileArgs p) {
             // weight operand of strip j for K sub-step t
             auto mkb = [&](int j, int tt) -> Frag8 {
                 if constexpr (NV) return fp4_to_bf16_mul(bw[j][0][tt], sf[j][tt >> 1]);
+                else if constexpr (F == Fmt::MXINT4_BF16) return int4_to_bf16(bw[j][0][tt], sf[j][0]);
                 else if constexpr (MOE) return fp4_to_bf16(bw[j][0][tt], sf[j][0]);
                 else return deq4_f16_scaled(bw[j][0][tt] ^ wx, nb2[j], nh2[j], s2[j]);
             };
@@ -1110,7 +1132,9 @@ constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16; }
 // stage (each dequantised fragment feeds 16 MFMAs; 13 % faster than 128 x 256
 // at M = 8192), or 128 x 256 tiles of 128 x 32 waves where 256 x 256 would not
 // cover the chip (a K step loads 48 KB instead of the 80 KB of 256 x 128).
-constexpr bool has_wide_tile(Fmt F) { return F == Fmt::WNA16_F16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16; }
+constexpr bool has_wide_tile(Fmt F) {
+    return F == Fmt::WNA16_F16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16;
+}
 // INT8: 256 x 256 on 8 waves of 128 x 64, direct loads into two full stages
 // (M = 8192: 1126 us vs 1569 us for 256 x 128 with register-staged loads); the
 // 256 x 128 tile also loads directly (1498 us).

@@ -171,6 +171,11 @@ def desc_fp4_a16(N, K, nvfp4: bool) -> hq_layer_desc:
     return d
 
 
+def desc_mxint4_a16(N, K) -> hq_layer_desc:
+    """bf16 activations x MXINT4 weights (two's-complement INT4, E8M0 scale per 32 K)."""
+    return make_desc(N, K, HQ_DT_BF16, HQ_DT_INT4, HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K, 32, HQ_DT_BF16)
+
+
 def desc_w8a8(N, K, raw_int32=False) -> hq_layer_desc:
     return make_desc(N, K, HQ_DT_INT8, HQ_DT_INT8, HQ_DT_FP32, HQ_GRAN_PER_CHANNEL, K,
                      HQ_DT_INT32 if raw_int32 else HQ_DT_BF16, a_scale=HQ_ASCALE_PER_TOKEN_F32)

@@ -71,6 +71,12 @@ FP4A16_TILES = [(2000, 4100, 384), (4000, 4100, 512), (1100, 16000, 256)]
 FP4A16_SWEEP = [(M, C2["N"], C2["K"]) for M in SWEEP]
 
 
+# ---- MXINT4 weights with bf16 activations: (M, N, K) ----
+MXINT4_SMALL = [(M, 272, 1024) for M in (1, 3, 16, 24, 33, 64, 100, 300)] + [(M, 304, 7168) for M in (1, 20)]
+MXINT4_TILES = [(2000, 4100, 384), (4000, 4100, 512), (1100, 16000, 256)]
+MXINT4_SWEEP = [(M, C2["N"], C2["K"]) for M in SWEEP]
+
+
 def all_dense_cases():
     """(format, M, N, K, G, flags) for every dense GPU case, flags a dict."""
     out = []
@@ -91,4 +97,6 @@ def all_dense_cases():
     for kind in ("mxfp4", "nvfp4"):
         for M, N, K in FP4A16_SMALL + FP4A16_TILES + FP4A16_SWEEP:
             out.append(("fp4a16", M, N, K, 16 if kind == "nvfp4" else 32, dict(kind=kind)))
+    for M, N, K in MXINT4_SMALL + MXINT4_TILES + MXINT4_SWEEP:
+        out.append(("mxint4", M, N, K, 32, {}))
     return out

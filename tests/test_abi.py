@@ -95,6 +95,27 @@ def test_descriptor_validation_low_precision_variants():
     assert status_of(hq.hq_desc_validate, d) == hq.HQ_ERR_UNSUPPORTED
 
 
+def test_descriptor_validation_mxint4():
+    """MXINT4 (INT4 codes, E8M0 per 32 K, bf16 activations): dense only, 32-K blocks,
+    no zero-points; INT4 with bf16 scales stays the symmetric W4A16 format."""
+    assert status_of(hq.hq_desc_validate, hq.desc_mxint4_a16(4096, 7168)) == hq.HQ_OK
+    assert status_of(hq.hq_desc_validate, hq.desc_mxint4_a16(4096, 7000)) == hq.HQ_ERR_UNSUPPORTED
+    for field, value in (("group_size", 16), ("num_experts", 4), ("zp_dtype", hq.HQ_DT_UINT4),
+                         ("a_scale", hq.HQ_ASCALE_PER_TOKEN_F32), ("out_dtype", hq.HQ_DT_FP16),
+                         ("scale2", hq.HQ_S2_PER_TENSOR_F32)):
+        d = hq.desc_mxint4_a16(256, 256)
+        setattr(d, field, value)
+        assert status_of(hq.hq_desc_validate, d) == hq.HQ_ERR_UNSUPPORTED, field
+    assert status_of(hq.hq_desc_validate, hq.desc_w4a16(256, 256, bf16=True, zp=False)) == hq.HQ_OK
+    # the packed layout is the MXFP4 one (natural nibble order, E8M0 per lane)
+    N, K = 40, 256
+    d = syn.w4a16_mxint4(0, 1, N, K)
+    wi, si, _ = hq.hq_repack(hq.desc_mxint4_a16(N, K), d["q"], d["e"])
+    wf, sf, _ = hq.hq_repack(hq.desc_fp4_a16(N, K, False), d["q"], d["e"])
+    np.testing.assert_array_equal(wi, wf)
+    np.testing.assert_array_equal(si, sf)
+
+
 def test_fp8_blockwise_repack_keeps_int8_layout_and_block_scales():
     N, K = 300, 256
     d = syn.w8a8_fp8_blockwise(0, 1, N, K)

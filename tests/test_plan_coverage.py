@@ -24,6 +24,8 @@ def desc_of(fmt, N, K, G, flags):
         return hq.desc_mx_act_mxfp4(N, K, fp4_act=flags["elem"] == "e2m1")
     if fmt == "fp8b":
         return hq.desc_fp8_blockwise(N, K)
+    if fmt == "mxint4":
+        return hq.desc_mxint4_a16(N, K)
     if fmt == "fp4a16":
         return hq.desc_fp4_a16(N, K, nvfp4=flags["kind"] == "nvfp4")
     return hq.desc_w8a8(N, K, raw_int32=flags["raw"])
@@ -57,6 +59,7 @@ BENCH = {
     "fp8b": ("fp8b", 7168, 7168, 128, {}),
     "mxfp4a16": ("fp4a16", 4096, 7168, 32, dict(kind="mxfp4")),
     "nvfp4a16": ("fp4a16", 4096, 7168, 16, dict(kind="nvfp4")),
+    "mxint4a16": ("mxint4", 4096, 7168, 32, {}),
 }
 
 
