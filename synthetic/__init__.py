@@ -216,6 +216,16 @@ def w4a16_mxint4(seed, M, N, K, dtype=torch.bfloat16, cfg=C8):
                 e=e8m0_exponents(seed, cfg, (K // 32, N)))
 
 
+C9 = 9  # INT8 weight-only (W8A16)
+
+
+def w8a16_int8(seed, M, N, K, dtype=torch.bfloat16, cfg=C9):
+    """INT8 weight-only: N(0,1) activations rounded to bf16/fp16, INT8 weights uniform
+    over the full two's-complement range [-128, 127], fp32 per-column scales |N(0,0.01)|+1e-4."""
+    return dict(A=activations(seed, cfg, M, K, dtype), w=int8_uniform(seed, cfg, T_Q, (K, N), lo=-128, hi=127),
+                s_w=abs_normal_scales(seed, cfg, T_SW, (N,), 0.01, 1e-4, torch.float32))
+
+
 def moe_expert_mxfp4(seed, e, N, K, cfg=C5):
     """One expert's MXFP4 weights (codes + E8M0), drawn from the expert's own stream."""
     return (random_words(seed, cfg, T_Q, (K // 8, N), e),

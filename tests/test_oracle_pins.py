@@ -723,3 +723,41 @@ def test_mxint4_a16_single_weight_and_block_step():
     np.testing.assert_allclose(moved[:, 7] - base[:, 7], blk, rtol=1e-12, atol=1e-12)
     other = [n for n in range(N) if n != 7]
     np.testing.assert_array_equal(moved[:, other], base[:, other])
+
+
+# ---------------------------------------------------------------------------
+# INT8 weight-only (W8A16): 16-bit activations x INT8 weights, per-column fp32 scale
+# ---------------------------------------------------------------------------
+
+def test_w8a16_integer_activations_equal_w8a8():
+    """With integer-valued activations in [-127, 127] and unit token scales, W8A16 is the
+    (exact, int64) W8A8 oracle: same sums, same per-column epilogue."""
+    M, N, K = 5, 24, 192
+    d = syn.w8a16_int8(0, M, N, K)
+    a8 = syn.int8_uniform(0, 99, 0, (M, K))
+    for bf in (True, False):
+        dt = torch.bfloat16 if bf else torch.float16
+        A = torch.from_numpy(a8.astype(np.float32)).to(dt).view(torch.int16).numpy().view(np.uint16)
+        got = oracle.gemm_w8a16(A, d["w"], d["s_w"], a_bf16=bf)
+        _, ref = oracle.gemm_w8a8(a8, np.ones(M, np.float32), d["w"], d["s_w"])
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_w8a16_exact_rational_and_column_scale():
+    M, N, K = 2, 8, 64
+    d = syn.w8a16_int8(1, M, N, K, torch.float16)
+    got = oracle.gemm_w8a16(d["A"], d["w"], d["s_w"], a_bf16=False)
+    a = torch16(d["A"], torch.float16)
+    for m in range(M):
+        for n in range(N):
+            acc = sum(Fraction(float(a[m, k])) * int(d["w"][k, n]) for k in range(K)) * Fraction(float(d["s_w"][n]))
+            assert abs(got[m, n] - float(acc)) <= 1e-13 * max(abs(float(acc)), 1e-30)
+    # -128 is a code like any other; a column's scale scales exactly that column
+    w = np.zeros((K, N), np.int8)
+    w[17, 3] = -128
+    s = np.ones(N, np.float32)
+    s[3] = 0.5
+    got = oracle.gemm_w8a16(d["A"], w, s, a_bf16=False)
+    want = np.zeros((M, N))
+    want[:, 3] = -64.0 * a[:, 17].astype(np.float64)
+    np.testing.assert_array_equal(got, want)
