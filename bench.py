@@ -9,7 +9,7 @@ zero-points and fp16 scales per 128 K, N=4096, K=7168), the configuration
 the metric is quoted on; its line also carries, under "configs", the same
 measurement of every other workload (dense W4A8-MXFP4, W8A8-INT8, the MoE
 gate-up on the Indexed path with its routing timed apart, W4A4 MXFP4 x MXFP4,
-MXFP8 x MXFP4, FP8 W8A8 with blockwise scales, bf16 x MXFP4, NVFP4 and MXINT4 WnA16).
+MXFP8 x MXFP4, FP8 W8A8 with blockwise scales, bf16 x MXFP4, NVFP4 and MXINT4 WnA16, INT8 weight-only).
 --config NAME measures one workload alone (c5g: the MoE Grouped path, c5l:
 the whole MoE layer the pages time, gate-up + SwiGLU + down).
 
@@ -600,6 +600,51 @@ class DenseMXINT4A16(DenseFP4A16):
                     sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
 
 
+class DenseW8A16:
+    """INT8 weight-only: bf16 activations x INT8 weights with fp32 per-channel scales at the
+    dense W4A16 layer's shape, N=4096, K=7168."""
+
+    def __init__(self, N=4096, K=7168, Mmax=8192, sweep=SWEEP):
+        self.N, self.K, self.Mmax, self.sweep = N, K, Mmax, sweep
+        self.dtype = "bf16"
+        self.name = f"dense_w8a16_int8_bf16_N{N}_K{K}"
+        log(f"[bench] generating {self.name}")
+        d = syn.w8a16_int8(0, Mmax, N, K)
+        self.host = d
+        self.desc = hq.desc_w8a16(N, K, bf16=True)
+        wp, sp, _ = hq.hq_repack(self.desc, d["w"], d["s_w"])
+        self.wbytes = wp.size + sp.size
+        self.copies = _copies((dev(wp), dev(sp)), self.wbytes)
+        self.A = dev(d["A"])
+        self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in sweep)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def flops(self, M):
+        return 2.0 * M * self.N * self.K
+
+    def bytes(self, M):
+        return self.wbytes + M * self.K * 2 + M * self.N * 2
+
+    def kernel_of(self, M):
+        if M <= 64:
+            return ("skinny_kernel<W8A16_BF16> (M<=64)", "hbm")
+        return ("tile_gemm_kernel<W8A16_BF16> (M>64)", "mfma" if M >= 256 else "hbm")
+
+    def call(self, M, c, desc=None):
+        w, s = self.copies[c]
+        hq.hq_gemm(desc or self.desc, M, self.A, None, w, s, None, self.D, self.ws if self.ws_bytes else None,
+                   self.ws_bytes)
+
+    def cpu_baseline(self, budget_s=8.0):
+        import oracle
+        d = self.host
+        f = lambda rows: oracle.gemm_w8a16(d["A"], d["w"], d["s_w"], a_bf16=True, rows=rows)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, self.Mmax)), budget_s)
+        return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(), kind="oracle",
+                    sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
+
+
 WORKLOADS = {
     "c1": lambda: DenseW4A16(N=1024, K=1024, Mmax=16, bf16=True, zp=False, sweep=[16],
                              name="dense_w4a16_sym_bf16_M16_N1024_K1024"),
@@ -615,9 +660,10 @@ WORKLOADS = {
     "mxfp4a16": lambda: DenseFP4A16(nvfp4=False),
     "nvfp4a16": lambda: DenseFP4A16(nvfp4=True),
     "mxint4a16": lambda: DenseMXINT4A16(),
+    "w8a16": lambda: DenseW8A16(),
 }
 # the workloads the default run measures besides the headline one (c2)
-DEFAULT_EXTRA = ["c3", "c4", "c5", "w4a4", "w4a8mx", "fp8b", "mxfp4a16", "nvfp4a16", "mxint4a16"]
+DEFAULT_EXTRA = ["c3", "c4", "c5", "w4a4", "w4a8mx", "fp8b", "mxfp4a16", "nvfp4a16", "mxint4a16", "w8a16"]
 
 
 # ---------------------------------------------------------------------------
@@ -991,6 +1037,7 @@ _DRY = {
     "mxfp4a16": lambda: hq.desc_fp4_a16(4096, 7168, False),
     "nvfp4a16": lambda: hq.desc_fp4_a16(4096, 7168, True),
     "mxint4a16": lambda: hq.desc_mxint4_a16(4096, 7168),
+    "w8a16": lambda: hq.desc_w8a16(4096, 7168, bf16=True),
 }
 
 

@@ -18,7 +18,9 @@ enum class Kind {
     MOE_MX_BF16,  // MoE: bf16 A, e2m1 W, E8M0 per 32 K
     MXA_MX,       // MX activations (E4M3 or E2M1, E8M0 per 32 K) x e2m1 W, E8M0 per 32 K
     FP8_BLOCK,    // fp8-e4m3 A (fp32 per row and 128-K block) x fp8-e4m3 W (fp32 per 128 x 128 block)
-    FP4_A16,      // bf16 A, e2m1 W with E8M0 per 32 K (MXFP4) or E4M3 per 16 K + fp32 per tensor (NVFP4)
+    FP4_A16,      // bf16 A, e2m1 W with E8M0 per 32 K (MXFP4) or E4M3 per 16 K + fp32 per tensor (NVFP4);
+                  // also INT4 W with E8M0 per 32 K (MXINT4)
+    W8A16,        // bf16/fp16 A, int8 W, fp32 per-channel
 };
 
 struct LayerInfo {

@@ -65,6 +65,27 @@ void repack_int8(const LayerInfo& L, const int8_t* w, int8_t* out) {
     }
 }
 
+// INT8 weight-only: [E][Np/16][K/128][2 halves][64 lanes][16 B]; lane l holds column
+// 16*strip + (l & 15) and, in half h, K = 128*chunk + 32*(l >> 4) + 16*h + j (a lane's
+// 32 consecutive K of the chunk, the K order of the 16-bit activation fragments).
+void repack_int8_k32(const LayerInfo& L, const int8_t* w, int8_t* out) {
+    const int64_t N = L.N, K = L.K, nst = L.Np / 16, nc = K / 128;
+    for (int64_t e = 0; e < L.E; ++e) {
+        const int8_t* we = w + e * K * N;
+        int8_t* oe = out + (size_t)e * (size_t)(nst * nc * 2048);
+        for (int64_t st = 0; st < nst; ++st)
+            for (int64_t c = 0; c < nc; ++c)
+                for (int h = 0; h < 2; ++h)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        const int64_t n = st * 16 + (lane & 15);
+                        for (int j = 0; j < 16; ++j) {
+                            const int64_t k = c * 128 + 32 * (lane >> 4) + 16 * h + j;
+                            oe[(((st * nc + c) * 2 + h) * 64 + lane) * 16 + j] = n < N ? we[k * N + n] : 0;
+                        }
+                    }
+    }
+}
+
 void repack_scale16(const LayerInfo& L, const uint16_t* s, uint16_t* out, uint16_t one) {
     const int64_t N = L.N, nst = L.Np / 16, ng = L.K / L.G;
     for (int64_t e = 0; e < L.E; ++e) {
@@ -155,6 +176,10 @@ void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s
             *w = E * nst * (size_t)(L.K / 64) * 1024;
             *s = E * (size_t)L.Np * 4;
             break;
+        case Kind::W8A16:
+            *w = E * nst * (size_t)(L.K / 128) * 2048;
+            *s = E * (size_t)L.Np * 4;
+            break;
         case Kind::FP4_A16:
             *w = E * nst * (size_t)(L.K / 128) * 1024;
             *s = E * nst * (size_t)(L.K / 128) * (L.nv ? 128 : 64);
@@ -183,6 +208,10 @@ void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z,
             break;
         case Kind::W8A8:
             repack_int8(L, (const int8_t*)w, (int8_t*)w_out);
+            repack_chan32(L, (const float*)s, (float*)s_out);
+            break;
+        case Kind::W8A16:
+            repack_int8_k32(L, (const int8_t*)w, (int8_t*)w_out);
             repack_chan32(L, (const float*)s, (float*)s_out);
             break;
         case Kind::FP4_A16:

@@ -82,6 +82,10 @@ hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32) { return launch<Fmt::W8
 
 hipError_t fp8_block_launch(const DenseArgs& a) { return launch<Fmt::W8A8_F8B>(a, 0); }
 
+hipError_t w8a16_launch(const DenseArgs& a, bool bf16) {
+    return bf16 ? launch<Fmt::W8A16_BF16>(a, 0) : launch<Fmt::W8A16_F16>(a, 0);
+}
+
 hipError_t fp4_a16_launch(const DenseArgs& a, int kind) {
     return kind == 1 ? launch<Fmt::NVFP4_BF16>(a, 0) : kind == 2 ? launch<Fmt::MXINT4_BF16>(a, 0)
                      : launch<Fmt::MXFP4_BF16>(a, 0);

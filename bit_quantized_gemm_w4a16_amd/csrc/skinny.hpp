@@ -45,6 +45,9 @@
 //                   and the per-tensor fp32 second-level scale on the output
 //   MXINT4_BF16     the same with two's-complement INT4 codes: sign-extended,
 //                   scaled by 2^(E-127) in fp32 and rounded to bf16 (exact)
+//   W8A16_F16/_BF16 4 x v_mfma_f32_16x16x32_{f16,bf16} on INT8 codes decoded to
+//                   exact 16-bit operands (two 16-byte loads per chunk and lane),
+//                   the per-channel fp32 scale in the epilogue
 //   W8A8_F8B        1 x the scaled MFMA on fp8 x fp8 per chunk (one 128-K scale
 //                   block), its partial scaled by the row's activation block
 //                   scale times the strip's weight block scale (both in LDS)
@@ -375,6 +378,21 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                         for (int mt = 0; mt < MT; ++mt) acc2[i & 1][sp][mt] += sc * (gacc[0][mt] + gacc[1][mt]);
                     }
                 }
+            } else if constexpr (w8a16(F)) {
+                // INT8 -> exact 16-bit operands (the per-channel scale is applied in the
+                // epilogue); a chunk past the wave's part multiplies zeros
+                constexpr bool BF = F == Fmt::W8A16_BF16;
+                const Frag8(&af)[MT][4] = afb[i & 1];
+#pragma unroll
+                for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        Frag8 b = deq8<BF>(w[i][sp][t >> 1], t & 1);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) b.u[e] = valid ? b.u[e] : 0u;
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) acc2[t & 1][sp][mt] = mfma16<BF>(af[mt][t], b, acc2[t & 1][sp][mt]);
+                    }
             } else if constexpr (FP4B) {
                 // e2m1 x (2^(E-127) or E4M3 group scale) -> exact bf16 operands, bf16 MFMA
                 const Frag8(&af)[MT][4] = afb[i & 1];
@@ -544,6 +562,8 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r] * p.a_scale[m]);
                 } else if constexpr (F == Fmt::NVFP4_BF16) {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r] * *p.s2);
+                } else if constexpr (w8a16(F)) {
+                    ((uint16_t*)p.D)[o] = f32_to_16<F == Fmt::W8A16_BF16>(acc[sp][mt][r] * ((const float*)Sb)[n]);
                 } else {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r]);
                 }
@@ -632,11 +652,11 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
     // 16-bit A at 9..16 rows (two strips per workgroup): two workgroups per CU
     // (four slices at N=4096: 11.2 against 11.9 us with two)
     const bool a16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 ||
-                     F == Fmt::MXINT4_BF16;
+                     F == Fmt::MXINT4_BF16 || w8a16(F);
     const int64_t target = a16 && p.NS == 2 ? 512 : 256;
     int64_t S = p.groups_x >= 192 ? 1 : cdiv(target, p.groups_x);
     const int64_t smax = nc / WK > 0 ? nc / WK : 1;
-    const int nb = (F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B) ? 2 : 1;  // 16-byte weight loads per chunk
+    const int nb = (F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B || w8a16(F)) ? 2 : 1;  // 16-byte weight loads per chunk
     const int64_t cap = p.SPW * 16 * nb < 64 ? 16 : 8;  // largest register batch instantiated
     while (S < smax && (skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap)) ++S;
     if (S > smax) S = smax;

@@ -46,6 +46,9 @@
 //               the per-tensor fp32 second-level scale in the epilogue
 //   MXINT4_BF16 bf16 A x two's-complement INT4 B with E8M0 per 32 K (MXINT4):
 //               q x 2^(E-127) in fp32, rounded to bf16 (exact: 3 significant bits)
+//   W8A16_*     fp16 / bf16 A x INT8 B (a lane's 32 consecutive K per chunk in two
+//               16-byte halves) decoded to exact 16-bit operands; per-channel fp32
+//               scale in the epilogue
 #pragma once
 
 #include <type_traits>
@@ -56,13 +59,14 @@
 namespace hq {
 
 enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B, MXFP4_BF16, NVFP4_BF16,
-                 MXINT4_BF16 };
+                 MXINT4_BF16, W8A16_F16, W8A16_BF16 };
 
 constexpr const char* fmt_name(Fmt F) {
     return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
          : F == Fmt::W8A8_I8 ? "W8A8_I8" : F == Fmt::MOE_MX ? "MOE_MX" : F == Fmt::W4A8_MXA ? "W4A8_MXA"
          : F == Fmt::W4A4_MX ? "W4A4_MX" : F == Fmt::W8A8_F8B ? "W8A8_F8B" : F == Fmt::MXFP4_BF16 ? "MXFP4_BF16"
-         : F == Fmt::NVFP4_BF16 ? "NVFP4_BF16" : "MXINT4_BF16";
+         : F == Fmt::NVFP4_BF16 ? "NVFP4_BF16" : F == Fmt::MXINT4_BF16 ? "MXINT4_BF16"
+         : F == Fmt::W8A16_F16 ? "W8A16_F16" : "W8A16_BF16";
 }
 // Formats whose activations carry OCP MX scales (E8M0 per 32 K, [rows][K/32]).
 constexpr bool mx_act(Fmt F) { return F == Fmt::W4A8_MXA || F == Fmt::W4A4_MX; }
@@ -83,6 +87,10 @@ template <> struct FmtTraits<Fmt::W8A8_F8B> { static constexpr int AROW = 128, B
 template <> struct FmtTraits<Fmt::MXFP4_BF16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::NVFP4_BF16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::MXINT4_BF16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
+// INT8 weight-only: a lane's 32 consecutive K of its column per 128-K chunk, as two 16-byte halves
+template <> struct FmtTraits<Fmt::W8A16_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::W8A16_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+constexpr bool w8a16(Fmt F) { return F == Fmt::W8A16_F16 || F == Fmt::W8A16_BF16; }
 // e2m1 weights converted to bf16 operands with a per-lane scale (bf16 MFMA)
 constexpr bool fp4_bf16(Fmt F) {
     return F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16;
@@ -205,6 +213,39 @@ __device__ __forceinline__ Frag8 int4_to_bf16(uint32_t w, float scale) {
         f.u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2v));
     }
     return f;
+}
+
+// INT8 -> fp16, exact: byte q + 128 placed under the exponent of 1024 (fp16 has 10
+// mantissa bits) reads 1024 + q + 128; adding -1152 leaves q.  8 codes, two words.
+__device__ __forceinline__ Frag8 deq8_f16(uint32_t w0, uint32_t w1) {
+    const v2h nb = __builtin_bit_cast(v2h, 0xE480E480u);  // -1152, -1152
+    const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+    Frag8 f;
+    f.u[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)) + nb);
+    f.u[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)) + nb);
+    f.u[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u)) + nb);
+    f.u[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)) + nb);
+    return f;
+}
+
+// INT8 -> bf16, exact (|q| <= 128 needs at most 8 significant bits).
+__device__ __forceinline__ Frag8 deq8_bf16(uint32_t w0, uint32_t w1) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+    Frag8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = i < 2 ? w0 : w1;
+        const int lo = (int)(w << (24 - 16 * (i & 1))) >> 24, hi = (int)(w << (16 - 16 * (i & 1))) >> 24;
+        f.u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2v{(float)lo, (float)hi}, b2v));
+    }
+    return f;
+}
+
+template <bool BF>
+__device__ __forceinline__ Frag8 deq8(const v4u& half, int pair) {
+    if constexpr (BF) return deq8_bf16(half[2 * pair], half[2 * pair + 1]);
+    else return deq8_f16(half[2 * pair], half[2 * pair + 1]);
 }
 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
@@ -555,10 +596,11 @@ void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
             for (int h = 0; h < NBH; ++h) bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
 
-        if constexpr (F == Fmt::WNA16_F16 || fp4_bf16(F)) {
+        if constexpr (F == Fmt::WNA16_F16 || fp4_bf16(F) || w8a16(F)) {
             // 16-bit A with 4-bit weights decoded into the operand: fp16 (q - z) * s,
             // or e2m1 x (2^(E-127) or an E4M3 value) -> bf16 (exact)
             constexpr bool MOE = fp4_bf16(F);
+            constexpr bool BFA = MOE || F == Fmt::W8A16_BF16;  // bf16 MFMA (else fp16)
             // A fragments read ahead (software pipeline): a whole sub-step, or
             // a ring of three for tall / wide wave tiles
             Frag8 afr[(NT >= 4 || MT > 8) ? 1 : 2][(NT >= 4 || MT > 8) ? 3 : MT];
@@ -574,6 +616,8 @@ void tile_gemm_kernel(TileArgs p) {
                     sf[j][1] = __builtin_amdgcn_cvt_f32_fp8((int)two, 1);
                 } else if constexpr (MOE) {
                     sf[j][0] = e8m0_to_f32(((const uint8_t*)sS)[(wn * NT + j) * 64 + lane]);
+                } else if constexpr (w8a16(F)) {
+                    // per-channel scale in the epilogue: nothing per step
                 } else {
                     // one lane offset for every strip (strips are immediate offsets); the
                     // zero-point select is branch-free (symmetric INT4: z = 8)
@@ -590,6 +634,7 @@ void tile_gemm_kernel(TileArgs p) {
             auto mkb = [&](int j, int tt) -> Frag8 {
                 if constexpr (NV) return fp4_to_bf16_mul(bw[j][0][tt], sf[j][tt >> 1]);
                 else if constexpr (F == Fmt::MXINT4_BF16) return int4_to_bf16(bw[j][0][tt], sf[j][0]);
+                else if constexpr (w8a16(F)) return deq8<F == Fmt::W8A16_BF16>(bw[j][tt >> 1], tt & 1);
                 else if constexpr (MOE) return fp4_to_bf16(bw[j][0][tt], sf[j][0]);
                 else return deq4_f16_scaled(bw[j][0][tt] ^ wx, nb2[j], nh2[j], s2[j]);
             };
@@ -618,7 +663,7 @@ void tile_gemm_kernel(TileArgs p) {
                             bq[(t + 1) & 1][i] = mkb(i, t + 1);
                         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<MOE>(afr[0][q % 3], bq[t & 1][j], acc[i][j]);
+                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<BFA>(afr[0][q % 3], bq[t & 1][j], acc[i][j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 } else {
@@ -643,7 +688,7 @@ void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
                     for (int i = 0; i < MT; ++i)
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<MOE>(afr[t & 1][i], bq[t & 1][j], acc[i][j]);
+                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<BFA>(afr[t & 1][i], bq[t & 1][j], acc[i][j]);
                     if (t < 3) {
                         // per A fragment: its read, the MFMAs of one fragment of
                         // this sub-step, a share of the next sub-step's dequant
@@ -992,6 +1037,8 @@ void tile_gemm_kernel(TileArgs p) {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r] * as);
                 } else if constexpr (F == Fmt::NVFP4_BF16) {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r] * *p.s2);
+                } else if constexpr (w8a16(F)) {
+                    ((uint16_t*)p.D)[o] = f32_to_16<F == Fmt::W8A16_BF16>(acc[i][j][r] * ((const float*)Sbase)[n]);
                 } else {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r]);
                 }
@@ -1043,7 +1090,8 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(FinalizeArgs p) {
     } else {
         if constexpr (F == Fmt::W4A8_MX) acc *= p.a_scale[m];
         if constexpr (F == Fmt::NVFP4_BF16) acc *= *p.s2;
-        constexpr bool BF = F != Fmt::WNA16_F16;
+        if constexpr (w8a16(F)) acc *= *(const v4f*)(p.s_w + n);  // (s_w padded to a multiple of 16)
+        constexpr bool BF = F != Fmt::WNA16_F16 && F != Fmt::W8A16_F16;
         for (int j = 0; j < cnt; ++j) ((uint16_t*)p.D)[o + j] = f32_to_16<BF>(acc[j]);
     }
 }
@@ -1126,19 +1174,20 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
 // W4A8 (8-bit A, no dequantisation): 256 x 256 on 8 waves of 128 x 64, which
 // halves the A traffic per flop and still fits two LDS stages.  bf16 A has no
 // 256-row variant (its row-sum MFMA needs a second accumulator set).
-constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16; }
+// INT8 weight-only: 256-row tiles do not fit two stages of its 2 KB weight strips
+constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16 && !w8a16(F); }
 // fp16 A with 4-bit weights: 8 waves side by side, each dequantising its own
 // weight strips once: 256 x 256 tiles of 256 x 32 waves with a single weight
 // stage (each dequantised fragment feeds 16 MFMAs; 13 % faster than 128 x 256
 // at M = 8192), or 128 x 256 tiles of 128 x 32 waves where 256 x 256 would not
 // cover the chip (a K step loads 48 KB instead of the 80 KB of 256 x 128).
 constexpr bool has_wide_tile(Fmt F) {
-    return F == Fmt::WNA16_F16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16;
+    return F == Fmt::WNA16_F16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || w8a16(F);
 }
 // INT8: 256 x 256 on 8 waves of 128 x 64, direct loads into two full stages
 // (M = 8192: 1126 us vs 1569 us for 256 x 128 with register-staged loads); the
 // 256 x 128 tile also loads directly (1498 us).
-constexpr bool has_wide256_tile(Fmt F) { return has_wide_tile(F) || F == Fmt::W8A8_I8; }
+constexpr bool has_wide256_tile(Fmt F) { return (has_wide_tile(F) && !w8a16(F)) || F == Fmt::W8A8_I8; }
 // 256x256 tiles from this many on: INT8 keeps the 256x128 three-stage ring
 // until the wide tiles fill two rounds of the chip (measured: the ring is
 // faster at M=1024 and level at M=2048 for N=18432, K=7168)
@@ -1163,7 +1212,7 @@ hipError_t launch_forced(const TilePlan& pl, TileArgs p, hipStream_t st) {
             if constexpr (has_wide_tile(F)) return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
             else return hipErrorNotSupported;
         case TUNE_W256:
-            if constexpr (has_wide_tile(F)) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
+            if constexpr (has_wide_tile(F) && !w8a16(F)) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
             else if constexpr (F == Fmt::W8A8_I8) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
             else if constexpr (mx_mfma(F)) return launch_tile_kernel<F, 256, 256, 2, 4, 4>(p, st);
             else return hipErrorNotSupported;
@@ -1232,7 +1281,8 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
             }
         }
         if constexpr (has_wide_tile(F)) {
-            if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
+            if constexpr (!w8a16(F))
+                if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
             if (pl.wide) return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
             // from 512 rows, 128 x 256 tiles with the K split filling the chip
             // beat 128 x 128 tiles (each wave dequantises its weights once instead

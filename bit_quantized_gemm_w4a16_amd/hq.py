@@ -176,6 +176,12 @@ def desc_mxint4_a16(N, K) -> hq_layer_desc:
     return make_desc(N, K, HQ_DT_BF16, HQ_DT_INT4, HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K, 32, HQ_DT_BF16)
 
 
+def desc_w8a16(N, K, bf16=True) -> hq_layer_desc:
+    """bf16 / fp16 activations x INT8 weights with fp32 per-channel scales (INT8 weight-only)."""
+    a = HQ_DT_BF16 if bf16 else HQ_DT_FP16
+    return make_desc(N, K, a, HQ_DT_INT8, HQ_DT_FP32, HQ_GRAN_PER_CHANNEL, K, a)
+
+
 def desc_w8a8(N, K, raw_int32=False) -> hq_layer_desc:
     return make_desc(N, K, HQ_DT_INT8, HQ_DT_INT8, HQ_DT_FP32, HQ_GRAN_PER_CHANNEL, K,
                      HQ_DT_INT32 if raw_int32 else HQ_DT_BF16, a_scale=HQ_ASCALE_PER_TOKEN_F32)

@@ -116,6 +116,35 @@ def test_descriptor_validation_mxint4():
     np.testing.assert_array_equal(si, sf)
 
 
+def test_descriptor_validation_and_layout_w8a16():
+    """INT8 weight-only: 16-bit activations, fp32 per-channel scales, dense only; the packed
+    layout gives each lane 32 consecutive K of its column per 128-K chunk (two 16-byte halves)."""
+    for bf in (True, False):
+        assert status_of(hq.hq_desc_validate, hq.desc_w8a16(4096, 7168, bf16=bf)) == hq.HQ_OK
+    assert status_of(hq.hq_desc_validate, hq.desc_w8a16(4096, 7000)) == hq.HQ_ERR_UNSUPPORTED
+    for field, value in (("w_scale_gran", hq.HQ_GRAN_PER_GROUP_K), ("num_experts", 2), ("zp_dtype", hq.HQ_DT_UINT4),
+                         ("a_scale", hq.HQ_ASCALE_PER_TOKEN_F32), ("out_dtype", hq.HQ_DT_INT32),
+                         ("w_scale_dtype", hq.HQ_DT_BF16)):
+        d = hq.desc_w8a16(256, 256)
+        setattr(d, field, value)
+        assert status_of(hq.hq_desc_validate, d) == hq.HQ_ERR_UNSUPPORTED, field
+    N, K = 40, 256
+    d = syn.w8a16_int8(0, 1, N, K)
+    wp, sp, _ = hq.hq_repack(hq.desc_w8a16(N, K), d["w"], d["s_w"])
+    Np = 48
+    got = wp.view(np.int8).reshape(Np // 16, K // 128, 2, 64, 16)
+    for st in range(Np // 16):
+        for c in range(K // 128):
+            for h in range(2):
+                for lane in range(64):
+                    n = 16 * st + (lane & 15)
+                    k = 128 * c + 32 * (lane >> 4) + 16 * h + np.arange(16)
+                    want = d["w"][k, n] if n < N else np.zeros(16, np.int8)
+                    np.testing.assert_array_equal(got[st, c, h, lane], want)
+    np.testing.assert_array_equal(sp.view(np.float32)[:N], d["s_w"])
+    np.testing.assert_array_equal(sp.view(np.float32)[N:], np.ones(Np - N, np.float32))
+
+
 def test_fp8_blockwise_repack_keeps_int8_layout_and_block_scales():
     N, K = 300, 256
     d = syn.w8a8_fp8_blockwise(0, 1, N, K)

@@ -24,6 +24,8 @@ def desc_of(fmt, N, K, G, flags):
         return hq.desc_mx_act_mxfp4(N, K, fp4_act=flags["elem"] == "e2m1")
     if fmt == "fp8b":
         return hq.desc_fp8_blockwise(N, K)
+    if fmt == "w8a16":
+        return hq.desc_w8a16(N, K, bf16=flags["bf16"])
     if fmt == "mxint4":
         return hq.desc_mxint4_a16(N, K)
     if fmt == "fp4a16":
@@ -60,6 +62,8 @@ BENCH = {
     "mxfp4a16": ("fp4a16", 4096, 7168, 32, dict(kind="mxfp4")),
     "nvfp4a16": ("fp4a16", 4096, 7168, 16, dict(kind="nvfp4")),
     "mxint4a16": ("mxint4", 4096, 7168, 32, {}),
+    "w8a16bf": ("w8a16", 4096, 7168, 7168, dict(bf16=True)),
+    "w8a16fp": ("w8a16", 4096, 7168, 7168, dict(bf16=False)),
 }
 
 
