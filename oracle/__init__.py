@@ -73,6 +73,8 @@ def lib():
         L.hq_oracle_gemm_fp8_blockwise.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
         L.hq_oracle_gemm_fp4_a16.restype = C.c_int
         L.hq_oracle_gemm_fp4_a16.argtypes = [i64, i64, i64, C.c_int, p, p, C.c_int, p, p, p, i64, p]
+        L.hq_oracle_gemm_fp8w_a16.restype = C.c_int
+        L.hq_oracle_gemm_fp8w_a16.argtypes = [i64, i64, i64, C.c_int, p, p, p, p, i64, p]
         L.hq_oracle_gemm_w8a16.restype = C.c_int
         L.hq_oracle_gemm_w8a16.argtypes = [i64, i64, i64, C.c_int, p, p, p, p, i64, p]
         L.hq_oracle_gemm_mxint4_a16.restype = C.c_int
@@ -256,6 +258,21 @@ def gemm_w8a16(A, w, s_w, *, a_bf16: bool, rows=None):
                                     _ptr(out))
     if rc:
         raise ValueError(f"oracle gemm_w8a16 failed ({rc})")
+    return out
+
+
+def gemm_fp8w_a16(A, w, s_w, *, a_bf16: bool, rows=None):
+    """FP8 weight-only: 16-bit activations x E4M3 weight codes [K][N], fp32 per-column scales, fp64."""
+    A = _c(A, np.uint16)
+    w = _c(w, np.uint8)
+    M, K = A.shape
+    N = w.shape[1]
+    r, R = _rows(rows, M)
+    out = np.empty((R, N), dtype=np.float64)
+    rc = lib().hq_oracle_gemm_fp8w_a16(M, N, K, int(a_bf16), _ptr(A), _ptr(w), _ptr(_c(s_w, np.float32)), _ptr(r),
+                                       R, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle gemm_fp8w_a16 failed ({rc})")
     return out
 
 

@@ -462,6 +462,30 @@ int hq_oracle_gemm_w8a16(int64_t M, int64_t N, int64_t K, int a_bf16, const uint
     return 0;
 }
 
+/* FP8 weight-only: E4M3 weights with one fp32 scale per output column and 16-bit
+ * activations:  D[m][n] = (sum_k A[m][k] * e4m3(w[k][n])) * s_w[n]   (fp64).
+ * A uint16 [M][K] (bf16 or fp16 bits), w uint8 [K][N] (E4M3 codes), s_w fp32 [N]. */
+int hq_oracle_gemm_fp8w_a16(int64_t M, int64_t N, int64_t K, int a_bf16, const uint16_t* A, const uint8_t* w,
+                            const float* s_w, const int64_t* rows, int64_t nrows, double* out)
+{
+    int64_t R = rows ? nrows : M;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(R * K + 1));
+    if (!a) return 2;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k) a[r * K + k] = act16(a_bf16, A[row_of(rows, r) * K + k]);
+    memset(out, 0, sizeof(double) * (size_t)(R * N));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            double wv = hq_oracle_e4m3(w[k * N + n]);
+            for (int64_t r = 0; r < R; ++r) out[r * N + n] += a[r * K + k] * wv;
+        }
+        for (int64_t r = 0; r < R; ++r) out[r * N + n] *= (double)s_w[n];
+    }
+    free(a);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* MoE                                                                   */
 /* ------------------------------------------------------------------ */

@@ -226,6 +226,16 @@ def w8a16_int8(seed, M, N, K, dtype=torch.bfloat16, cfg=C9):
                 s_w=abs_normal_scales(seed, cfg, T_SW, (N,), 0.01, 1e-4, torch.float32))
 
 
+C10 = 10  # FP8 weight-only
+
+
+def w8a16_fp8(seed, M, N, K, dtype=torch.bfloat16, cfg=C10):
+    """FP8 weight-only: N(0,1) activations rounded to bf16/fp16, E4M3 weight codes uniform
+    over the finite codes, fp32 per-column scales |N(0,0.01)|+1e-4."""
+    return dict(A=activations(seed, cfg, M, K, dtype), w=fp8_codes(seed, cfg, T_Q, (K, N)),
+                s_w=abs_normal_scales(seed, cfg, T_SW, (N,), 0.01, 1e-4, torch.float32))
+
+
 def moe_expert_mxfp4(seed, e, N, K, cfg=C5):
     """One expert's MXFP4 weights (codes + E8M0), drawn from the expert's own stream."""
     return (random_words(seed, cfg, T_Q, (K // 8, N), e),

@@ -761,3 +761,34 @@ def test_w8a16_exact_rational_and_column_scale():
     want = np.zeros((M, N))
     want[:, 3] = -64.0 * a[:, 17].astype(np.float64)
     np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# FP8 weight-only: 16-bit activations x E4M3 weights, per-column fp32 scale
+# ---------------------------------------------------------------------------
+
+def test_fp8w_a16_integer_codes_equal_w8a16():
+    """E4M3 codes of the integers -16..16 (every one exactly representable) give the
+    INT8 weight-only oracle's result on the same integers, bit for bit."""
+    M, N, K = 4, 24, 128
+    d = syn.w8a16_fp8(0, M, N, K)
+    ints = np.random.default_rng(5).integers(-16, 17, size=(K, N)).astype(np.int8)
+    codes = np.array([oracle.e4m3_encode(float(v)) for v in ints.reshape(-1)], np.uint8).reshape(K, N)
+    for bf in (True, False):
+        dt = torch.bfloat16 if bf else torch.float16
+        A = syn.w8a16_fp8(0, M, N, K, dt)["A"]
+        got = oracle.gemm_fp8w_a16(A, codes, d["s_w"], a_bf16=bf)
+        ref = oracle.gemm_w8a16(A, ints, d["s_w"], a_bf16=bf)
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_fp8w_a16_exact_rational():
+    M, N, K = 2, 8, 64
+    d = syn.w8a16_fp8(1, M, N, K)
+    got = oracle.gemm_fp8w_a16(d["A"], d["w"], d["s_w"], a_bf16=True)
+    a = torch16(d["A"], torch.bfloat16)
+    for m in range(M):
+        for n in range(N):
+            acc = sum(Fraction(float(a[m, k])) * Fraction(float(E4M3_LUT[d["w"][k, n]])) for k in range(K))
+            acc *= Fraction(float(d["s_w"][n]))
+            assert abs(got[m, n] - float(acc)) <= 1e-13 * max(abs(float(acc)), 1e-30)
