@@ -9,7 +9,7 @@ zero-points and fp16 scales per 128 K, N=4096, K=7168), the configuration
 the metric is quoted on; its line also carries, under "configs", the same
 measurement of every other workload (dense W4A8-MXFP4, W8A8-INT8, the MoE
 gate-up on the Indexed path with its routing timed apart, W4A4 MXFP4 x MXFP4,
-MXFP8 x MXFP4, FP8 W8A8 with blockwise scales, bf16 x MXFP4, NVFP4 and MXINT4 WnA16, INT8 weight-only).
+MXFP8 x MXFP4, FP8 W8A8 with blockwise scales, bf16 x MXFP4, NVFP4 and MXINT4 WnA16, INT8 and FP8 weight-only).
 --config NAME measures one workload alone (c5g: the MoE Grouped path, c5l:
 the whole MoE layer the pages time, gate-up + SwiGLU + down).
 
@@ -601,17 +601,17 @@ class DenseMXINT4A16(DenseFP4A16):
 
 
 class DenseW8A16:
-    """INT8 weight-only: bf16 activations x INT8 weights with fp32 per-channel scales at the
-    dense W4A16 layer's shape, N=4096, K=7168."""
+    """8-bit weight-only: bf16 activations x INT8 (or FP8-E4M3) weights with fp32 per-channel
+    scales at the dense W4A16 layer's shape, N=4096, K=7168."""
 
-    def __init__(self, N=4096, K=7168, Mmax=8192, sweep=SWEEP):
-        self.N, self.K, self.Mmax, self.sweep = N, K, Mmax, sweep
+    def __init__(self, fp8=False, N=4096, K=7168, Mmax=8192, sweep=SWEEP):
+        self.N, self.K, self.Mmax, self.sweep, self.fp8 = N, K, Mmax, sweep, fp8
         self.dtype = "bf16"
-        self.name = f"dense_w8a16_int8_bf16_N{N}_K{K}"
+        self.name = f"dense_w8a16_{'fp8' if fp8 else 'int8'}_bf16_N{N}_K{K}"
         log(f"[bench] generating {self.name}")
-        d = syn.w8a16_int8(0, Mmax, N, K)
+        d = (syn.w8a16_fp8 if fp8 else syn.w8a16_int8)(0, Mmax, N, K)
         self.host = d
-        self.desc = hq.desc_w8a16(N, K, bf16=True)
+        self.desc = (hq.desc_fp8w_a16 if fp8 else hq.desc_w8a16)(N, K, bf16=True)
         wp, sp, _ = hq.hq_repack(self.desc, d["w"], d["s_w"])
         self.wbytes = wp.size + sp.size
         self.copies = _copies((dev(wp), dev(sp)), self.wbytes)
@@ -627,9 +627,10 @@ class DenseW8A16:
         return self.wbytes + M * self.K * 2 + M * self.N * 2
 
     def kernel_of(self, M):
+        f = "F8W_BF16" if self.fp8 else "W8A16_BF16"
         if M <= 64:
-            return ("skinny_kernel<W8A16_BF16> (M<=64)", "hbm")
-        return ("tile_gemm_kernel<W8A16_BF16> (M>64)", "mfma" if M >= 256 else "hbm")
+            return (f"skinny_kernel<{f}> (M<=64)", "hbm")
+        return (f"tile_gemm_kernel<{f}> (M>64)", "mfma" if M >= 256 else "hbm")
 
     def call(self, M, c, desc=None):
         w, s = self.copies[c]
@@ -639,7 +640,8 @@ class DenseW8A16:
     def cpu_baseline(self, budget_s=8.0):
         import oracle
         d = self.host
-        f = lambda rows: oracle.gemm_w8a16(d["A"], d["w"], d["s_w"], a_bf16=True, rows=rows)
+        ref = oracle.gemm_fp8w_a16 if self.fp8 else oracle.gemm_w8a16
+        f = lambda rows: ref(d["A"], d["w"], d["s_w"], a_bf16=True, rows=rows)
         n, dt = _timed_oracle(f, lambda n: np.arange(min(n, self.Mmax)), budget_s)
         return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(), kind="oracle",
                     sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
@@ -661,9 +663,10 @@ WORKLOADS = {
     "nvfp4a16": lambda: DenseFP4A16(nvfp4=True),
     "mxint4a16": lambda: DenseMXINT4A16(),
     "w8a16": lambda: DenseW8A16(),
+    "fp8w": lambda: DenseW8A16(fp8=True),
 }
 # the workloads the default run measures besides the headline one (c2)
-DEFAULT_EXTRA = ["c3", "c4", "c5", "w4a4", "w4a8mx", "fp8b", "mxfp4a16", "nvfp4a16", "mxint4a16", "w8a16"]
+DEFAULT_EXTRA = ["c3", "c4", "c5", "w4a4", "w4a8mx", "fp8b", "mxfp4a16", "nvfp4a16", "mxint4a16", "w8a16", "fp8w"]
 
 
 # ---------------------------------------------------------------------------
@@ -1038,6 +1041,7 @@ _DRY = {
     "nvfp4a16": lambda: hq.desc_fp4_a16(4096, 7168, True),
     "mxint4a16": lambda: hq.desc_mxint4_a16(4096, 7168),
     "w8a16": lambda: hq.desc_w8a16(4096, 7168, bf16=True),
+    "fp8w": lambda: hq.desc_fp8w_a16(4096, 7168, bf16=True),
 }
 
 

@@ -179,9 +179,10 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
             return set_error(HQ_ERR_UNSUPPORTED, "W8A8 outputs bf16 or raw int32");
         I.out_i32 = d->out_dtype == HQ_DT_INT32;
         I.G = d->K;
-    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && w == HQ_DT_INT8) {
+    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT8 || w == HQ_DT_FP8_E4M3)) {
         I.kind = Kind::W8A16;
         I.a_bf16 = a == HQ_DT_BF16;
+        I.w_fp8 = w == HQ_DT_FP8_E4M3;
         if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "INT8 weight-only is dense-only");
         if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "INT8 weight-only takes no activation scale");
         if (d->w_scale_dtype != HQ_DT_FP32 || d->w_scale_gran != HQ_GRAN_PER_CHANNEL)
@@ -222,7 +223,8 @@ static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
         case Kind::WNA16: return hip_status(wna16_launch(a, L.a_bf16, L.zp), "hq_gemm(W4A16)");
         case Kind::W4A8_MX: return hip_status(w4a8_launch(a), "hq_gemm(W4A8-MXFP4)");
         case Kind::W8A8: return hip_status(w8a8_launch(a, L.out_i32), "hq_gemm(W8A8)");
-        case Kind::W8A16: return hip_status(w8a16_launch(a, L.a_bf16), "hq_gemm(W8A16)");
+        case Kind::W8A16:
+            return hip_status(w8a16_launch(a, L.a_bf16, L.w_fp8), L.w_fp8 ? "hq_gemm(FP8-weight-only)" : "hq_gemm(W8A16)");
         case Kind::MXA_MX: return hip_status(mx_act_launch(a, L.a_fp4), L.a_fp4 ? "hq_gemm(W4A4-MXFP4)" : "hq_gemm(W4A8-MXFP8xMXFP4)");
         case Kind::FP8_BLOCK: return hip_status(fp8_block_launch(a), "hq_gemm(FP8-blockwise)");
         case Kind::FP4_A16:

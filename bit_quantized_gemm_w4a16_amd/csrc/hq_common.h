@@ -20,7 +20,7 @@ enum class Kind {
     FP8_BLOCK,    // fp8-e4m3 A (fp32 per row and 128-K block) x fp8-e4m3 W (fp32 per 128 x 128 block)
     FP4_A16,      // bf16 A, e2m1 W with E8M0 per 32 K (MXFP4) or E4M3 per 16 K + fp32 per tensor (NVFP4);
                   // also INT4 W with E8M0 per 32 K (MXINT4)
-    W8A16,        // bf16/fp16 A, int8 W, fp32 per-channel
+    W8A16,        // bf16/fp16 A, int8 or fp8-e4m3 W, fp32 per-channel
 };
 
 struct LayerInfo {
@@ -32,6 +32,7 @@ struct LayerInfo {
     bool a_fp4;    // MXA_MX: E2M1 activations (else E4M3)
     bool nv;       // FP4_A16: NVFP4 (E4M3 per 16 K, per-tensor second-level scale), else MXFP4
     bool i4;       // FP4_A16: MXINT4 (two's-complement INT4 codes, E8M0 per 32 K) instead of e2m1
+    bool w_fp8;    // W8A16: E4M3 weight codes instead of INT8
     bool invariant;        // HQ_FLAG_BATCH_INVARIANT
     int tune_path, tune_splits;  // HQ_TUNE override (0, 0: the library's choice)
 };

@@ -60,7 +60,7 @@ hipError_t w4a8_launch(const DenseArgs& a);
 hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32);
 hipError_t mx_act_launch(const DenseArgs& a, bool fp4_act);  // MX activations x MXFP4 weights
 hipError_t fp8_block_launch(const DenseArgs& a);              // FP8 W8A8 with blockwise scales
-hipError_t w8a16_launch(const DenseArgs& a, bool bf16);        // bf16 / fp16 A x INT8 weights, per-channel scale
+hipError_t w8a16_launch(const DenseArgs& a, bool bf16, bool fp8);  // bf16 / fp16 A x INT8 / E4M3 weights, per-channel scale
 hipError_t fp4_a16_launch(const DenseArgs& a, int kind);      // bf16 A x MXFP4 (0) / NVFP4 (1) / MXINT4 (2)
 
 // MoE

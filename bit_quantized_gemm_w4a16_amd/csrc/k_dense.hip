@@ -82,7 +82,8 @@ hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32) { return launch<Fmt::W8
 
 hipError_t fp8_block_launch(const DenseArgs& a) { return launch<Fmt::W8A8_F8B>(a, 0); }
 
-hipError_t w8a16_launch(const DenseArgs& a, bool bf16) {
+hipError_t w8a16_launch(const DenseArgs& a, bool bf16, bool fp8) {
+    if (fp8) return bf16 ? launch<Fmt::F8W_BF16>(a, 0) : launch<Fmt::F8W_F16>(a, 0);
     return bf16 ? launch<Fmt::W8A16_BF16>(a, 0) : launch<Fmt::W8A16_F16>(a, 0);
 }
 

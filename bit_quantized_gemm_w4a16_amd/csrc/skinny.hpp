@@ -48,6 +48,7 @@
 //   W8A16_F16/_BF16 4 x v_mfma_f32_16x16x32_{f16,bf16} on INT8 codes decoded to
 //                   exact 16-bit operands (two 16-byte loads per chunk and lane),
 //                   the per-channel fp32 scale in the epilogue
+//   F8W_F16/_BF16   the same with E4M3 weight codes (FP8 weight-only)
 //   W8A8_F8B        1 x the scaled MFMA on fp8 x fp8 per chunk (one 128-K scale
 //                   block), its partial scaled by the row's activation block
 //                   scale times the strip's weight block scale (both in LDS)
@@ -381,13 +382,13 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
             } else if constexpr (w8a16(F)) {
                 // INT8 -> exact 16-bit operands (the per-channel scale is applied in the
                 // epilogue); a chunk past the wave's part multiplies zeros
-                constexpr bool BF = F == Fmt::W8A16_BF16;
+                constexpr bool BF = w8bf(F);
                 const Frag8(&af)[MT][4] = afb[i & 1];
 #pragma unroll
                 for (int sp = 0; sp < SPW; ++sp)
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        Frag8 b = deq8<BF>(w[i][sp][t >> 1], t & 1);
+                        Frag8 b = deq8<F>(w[i][sp][t >> 1], t & 1);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) b.u[e] = valid ? b.u[e] : 0u;
 #pragma unroll
@@ -563,7 +564,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                 } else if constexpr (F == Fmt::NVFP4_BF16) {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r] * *p.s2);
                 } else if constexpr (w8a16(F)) {
-                    ((uint16_t*)p.D)[o] = f32_to_16<F == Fmt::W8A16_BF16>(acc[sp][mt][r] * ((const float*)Sb)[n]);
+                    ((uint16_t*)p.D)[o] = f32_to_16<w8bf(F)>(acc[sp][mt][r] * ((const float*)Sb)[n]);
                 } else {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r]);
                 }

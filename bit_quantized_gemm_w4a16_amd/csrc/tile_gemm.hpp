@@ -49,6 +49,8 @@
 //   W8A16_*     fp16 / bf16 A x INT8 B (a lane's 32 consecutive K per chunk in two
 //               16-byte halves) decoded to exact 16-bit operands; per-channel fp32
 //               scale in the epilogue
+//   F8W_*       the same with E4M3 weight codes (FP8 weight-only), converted to
+//               the 16-bit operand type by the scaled converts (exact)
 #pragma once
 
 #include <type_traits>
@@ -59,14 +61,15 @@
 namespace hq {
 
 enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B, MXFP4_BF16, NVFP4_BF16,
-                 MXINT4_BF16, W8A16_F16, W8A16_BF16 };
+                 MXINT4_BF16, W8A16_F16, W8A16_BF16, F8W_F16, F8W_BF16 };
 
 constexpr const char* fmt_name(Fmt F) {
     return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
          : F == Fmt::W8A8_I8 ? "W8A8_I8" : F == Fmt::MOE_MX ? "MOE_MX" : F == Fmt::W4A8_MXA ? "W4A8_MXA"
          : F == Fmt::W4A4_MX ? "W4A4_MX" : F == Fmt::W8A8_F8B ? "W8A8_F8B" : F == Fmt::MXFP4_BF16 ? "MXFP4_BF16"
          : F == Fmt::NVFP4_BF16 ? "NVFP4_BF16" : F == Fmt::MXINT4_BF16 ? "MXINT4_BF16"
-         : F == Fmt::W8A16_F16 ? "W8A16_F16" : "W8A16_BF16";
+         : F == Fmt::W8A16_F16 ? "W8A16_F16" : F == Fmt::W8A16_BF16 ? "W8A16_BF16" : F == Fmt::F8W_F16 ? "F8W_F16"
+         : "F8W_BF16";
 }
 // Formats whose activations carry OCP MX scales (E8M0 per 32 K, [rows][K/32]).
 constexpr bool mx_act(Fmt F) { return F == Fmt::W4A8_MXA || F == Fmt::W4A4_MX; }
@@ -90,7 +93,12 @@ template <> struct FmtTraits<Fmt::MXINT4_BF16> { static constexpr int AROW = 256
 // INT8 weight-only: a lane's 32 consecutive K of its column per 128-K chunk, as two 16-byte halves
 template <> struct FmtTraits<Fmt::W8A16_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::W8A16_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
-constexpr bool w8a16(Fmt F) { return F == Fmt::W8A16_F16 || F == Fmt::W8A16_BF16; }
+template <> struct FmtTraits<Fmt::F8W_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::F8W_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+// 8-bit weight-only formats: INT8 or FP8 (E4M3) codes in the same layout, per-channel fp32 scale
+constexpr bool f8w(Fmt F) { return F == Fmt::F8W_F16 || F == Fmt::F8W_BF16; }
+constexpr bool w8a16(Fmt F) { return F == Fmt::W8A16_F16 || F == Fmt::W8A16_BF16 || f8w(F); }
+constexpr bool w8bf(Fmt F) { return F == Fmt::W8A16_BF16 || F == Fmt::F8W_BF16; }
 // e2m1 weights converted to bf16 operands with a per-lane scale (bf16 MFMA)
 constexpr bool fp4_bf16(Fmt F) {
     return F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16;
@@ -242,9 +250,31 @@ __device__ __forceinline__ Frag8 deq8_bf16(uint32_t w0, uint32_t w1) {
     return f;
 }
 
+// E4M3 -> bf16 / fp16, exact (4 significant bits, exponents 2^-9..2^8 inside both
+// formats' normal ranges): the scaled converts with a unit scale.
 template <bool BF>
+__device__ __forceinline__ Frag8 deq8_fp8(uint32_t w0, uint32_t w1) {
+    Frag8 f;
+    if constexpr (BF) {
+        f.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+        f.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+        f.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+        f.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+    } else {
+        f.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false));
+        f.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true));
+        f.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false));
+        f.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+    }
+    return f;
+}
+
+// 8 codes (one K sub-step) of a lane's 16-byte half: INT8 or E4M3
+template <Fmt F>
 __device__ __forceinline__ Frag8 deq8(const v4u& half, int pair) {
-    if constexpr (BF) return deq8_bf16(half[2 * pair], half[2 * pair + 1]);
+    constexpr bool BF = w8bf(F);
+    if constexpr (f8w(F)) return deq8_fp8<BF>(half[2 * pair], half[2 * pair + 1]);
+    else if constexpr (BF) return deq8_bf16(half[2 * pair], half[2 * pair + 1]);
     else return deq8_f16(half[2 * pair], half[2 * pair + 1]);
 }
 
@@ -600,7 +630,7 @@ void tile_gemm_kernel(TileArgs p) {
             // 16-bit A with 4-bit weights decoded into the operand: fp16 (q - z) * s,
             // or e2m1 x (2^(E-127) or an E4M3 value) -> bf16 (exact)
             constexpr bool MOE = fp4_bf16(F);
-            constexpr bool BFA = MOE || F == Fmt::W8A16_BF16;  // bf16 MFMA (else fp16)
+            constexpr bool BFA = MOE || w8bf(F);  // bf16 MFMA (else fp16)
             // A fragments read ahead (software pipeline): a whole sub-step, or
             // a ring of three for tall / wide wave tiles
             Frag8 afr[(NT >= 4 || MT > 8) ? 1 : 2][(NT >= 4 || MT > 8) ? 3 : MT];
@@ -634,7 +664,7 @@ void tile_gemm_kernel(TileArgs p) {
             auto mkb = [&](int j, int tt) -> Frag8 {
                 if constexpr (NV) return fp4_to_bf16_mul(bw[j][0][tt], sf[j][tt >> 1]);
                 else if constexpr (F == Fmt::MXINT4_BF16) return int4_to_bf16(bw[j][0][tt], sf[j][0]);
-                else if constexpr (w8a16(F)) return deq8<F == Fmt::W8A16_BF16>(bw[j][tt >> 1], tt & 1);
+                else if constexpr (w8a16(F)) return deq8<F>(bw[j][tt >> 1], tt & 1);
                 else if constexpr (MOE) return fp4_to_bf16(bw[j][0][tt], sf[j][0]);
                 else return deq4_f16_scaled(bw[j][0][tt] ^ wx, nb2[j], nh2[j], s2[j]);
             };
@@ -1038,7 +1068,7 @@ void tile_gemm_kernel(TileArgs p) {
                 } else if constexpr (F == Fmt::NVFP4_BF16) {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r] * *p.s2);
                 } else if constexpr (w8a16(F)) {
-                    ((uint16_t*)p.D)[o] = f32_to_16<F == Fmt::W8A16_BF16>(acc[i][j][r] * ((const float*)Sbase)[n]);
+                    ((uint16_t*)p.D)[o] = f32_to_16<w8bf(F)>(acc[i][j][r] * ((const float*)Sbase)[n]);
                 } else {
                     ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r]);
                 }
@@ -1091,7 +1121,7 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(FinalizeArgs p) {
         if constexpr (F == Fmt::W4A8_MX) acc *= p.a_scale[m];
         if constexpr (F == Fmt::NVFP4_BF16) acc *= *p.s2;
         if constexpr (w8a16(F)) acc *= *(const v4f*)(p.s_w + n);  // (s_w padded to a multiple of 16)
-        constexpr bool BF = F != Fmt::WNA16_F16 && F != Fmt::W8A16_F16;
+        constexpr bool BF = F != Fmt::WNA16_F16 && F != Fmt::W8A16_F16 && F != Fmt::F8W_F16;
         for (int j = 0; j < cnt; ++j) ((uint16_t*)p.D)[o + j] = f32_to_16<BF>(acc[j]);
     }
 }

@@ -182,6 +182,12 @@ def desc_w8a16(N, K, bf16=True) -> hq_layer_desc:
     return make_desc(N, K, a, HQ_DT_INT8, HQ_DT_FP32, HQ_GRAN_PER_CHANNEL, K, a)
 
 
+def desc_fp8w_a16(N, K, bf16=True) -> hq_layer_desc:
+    """bf16 / fp16 activations x FP8 (E4M3) weights with fp32 per-channel scales (FP8 weight-only)."""
+    a = HQ_DT_BF16 if bf16 else HQ_DT_FP16
+    return make_desc(N, K, a, HQ_DT_FP8_E4M3, HQ_DT_FP32, HQ_GRAN_PER_CHANNEL, K, a)
+
+
 def desc_w8a8(N, K, raw_int32=False) -> hq_layer_desc:
     return make_desc(N, K, HQ_DT_INT8, HQ_DT_INT8, HQ_DT_FP32, HQ_GRAN_PER_CHANNEL, K,
                      HQ_DT_INT32 if raw_int32 else HQ_DT_BF16, a_scale=HQ_ASCALE_PER_TOKEN_F32)

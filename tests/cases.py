@@ -77,7 +77,7 @@ MXINT4_TILES = [(2000, 4100, 384), (4000, 4100, 512), (1100, 16000, 256)]
 MXINT4_SWEEP = [(M, C2["N"], C2["K"]) for M in SWEEP]
 
 
-# ---- INT8 weight-only (bf16 / fp16 activations): (M, N, K) ----
+# ---- INT8 / FP8 weight-only (bf16 / fp16 activations): (M, N, K) ----
 W8A16_SMALL = [(M, 272, 1024) for M in (1, 3, 16, 24, 33, 64, 100, 300)] + [(M, 304, 7168) for M in (1, 20)]
 W8A16_TILES = [(2000, 4100, 384), (1100, 16000, 256), (700, 4100, 512)]
 W8A16_SWEEP = [(M, C2["N"], C2["K"]) for M in SWEEP]
@@ -105,7 +105,8 @@ def all_dense_cases():
             out.append(("fp4a16", M, N, K, 16 if kind == "nvfp4" else 32, dict(kind=kind)))
     for M, N, K in MXINT4_SMALL + MXINT4_TILES + MXINT4_SWEEP:
         out.append(("mxint4", M, N, K, 32, {}))
-    for dt in ("bf16", "fp16"):
-        for M, N, K in W8A16_SMALL + W8A16_TILES + W8A16_SWEEP:
-            out.append(("w8a16", M, N, K, K, dict(bf16=dt == "bf16")))
+    for wf in ("w8a16", "fp8w"):
+        for dt in ("bf16", "fp16"):
+            for M, N, K in W8A16_SMALL + W8A16_TILES + W8A16_SWEEP:
+                out.append((wf, M, N, K, K, dict(bf16=dt == "bf16")))
     return out

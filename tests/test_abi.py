@@ -145,6 +145,21 @@ def test_descriptor_validation_and_layout_w8a16():
     np.testing.assert_array_equal(sp.view(np.float32)[N:], np.ones(Np - N, np.float32))
 
 
+def test_fp8_weight_only_descriptor_and_layout():
+    """FP8 weight-only takes the INT8 weight-only layout byte for byte."""
+    for bf in (True, False):
+        assert status_of(hq.hq_desc_validate, hq.desc_fp8w_a16(4096, 7168, bf16=bf)) == hq.HQ_OK
+    d = hq.desc_fp8w_a16(256, 256)
+    d.w_scale_gran = hq.HQ_GRAN_BLOCK_128x128
+    assert status_of(hq.hq_desc_validate, d) == hq.HQ_ERR_UNSUPPORTED
+    N, K = 40, 256
+    d = syn.w8a16_fp8(0, 1, N, K)
+    wf, sf, _ = hq.hq_repack(hq.desc_fp8w_a16(N, K), d["w"], d["s_w"])
+    wi, si, _ = hq.hq_repack(hq.desc_w8a16(N, K), d["w"].view(np.int8), d["s_w"])
+    np.testing.assert_array_equal(wf, wi)
+    np.testing.assert_array_equal(sf, si)
+
+
 def test_fp8_blockwise_repack_keeps_int8_layout_and_block_scales():
     N, K = 300, 256
     d = syn.w8a8_fp8_blockwise(0, 1, N, K)

@@ -21,7 +21,7 @@ from gpu_util import GATE, dev, empty, gate_error, note, to_f64
 pytestmark = pytest.mark.gpu
 
 FORMATS = ["wna16_f16_zp", "wna16_bf16_sym", "w4a8_mxfp4", "w8a8_bf16", "w8a8_raw", "w4a4_mx", "mxfp8_mx",
-           "fp8_blockwise", "mxfp4_a16", "nvfp4_a16", "mxint4_a16", "w8a16_bf16", "w8a16_f16"]
+           "fp8_blockwise", "mxfp4_a16", "nvfp4_a16", "mxint4_a16", "w8a16_bf16", "w8a16_f16", "fp8w_bf16", "fp8w_f16"]
 
 
 class Layer:
@@ -70,14 +70,16 @@ class Layer:
             packed = hq.hq_repack(self.desc, d["w"], d["s_w"])
             A, sa, arow, srow = qa, s_a, K, (K // 128) * 4
             self.ref = lambda r: oracle.gemm_fp8_blockwise(qa, s_a, d["w"], d["s_w"], rows=r)
-        elif fmt.startswith("w8a16"):
+        elif fmt.startswith("w8a16") or fmt.startswith("fp8w"):
             bf = fmt.endswith("bf16")
+            fp8 = fmt.startswith("fp8w")
             self.out_dt = torch.bfloat16 if bf else torch.float16
-            d = syn.w8a16_int8(seed, M, N, K, self.out_dt)
-            self.desc = hq.desc_w8a16(N, K, bf16=bf)
+            d = (syn.w8a16_fp8 if fp8 else syn.w8a16_int8)(seed, M, N, K, self.out_dt)
+            self.desc = (hq.desc_fp8w_a16 if fp8 else hq.desc_w8a16)(N, K, bf16=bf)
             packed = hq.hq_repack(self.desc, d["w"], d["s_w"])
             A, sa, arow, srow = d["A"], None, K * 2, 0
-            self.ref = lambda r: oracle.gemm_w8a16(d["A"], d["w"], d["s_w"], a_bf16=bf, rows=r)
+            ref = oracle.gemm_fp8w_a16 if fp8 else oracle.gemm_w8a16
+            self.ref = lambda r: ref(d["A"], d["w"], d["s_w"], a_bf16=bf, rows=r)
         elif fmt == "mxint4_a16":
             d = syn.w4a16_mxint4(seed, M, N, K)
             self.desc = hq.desc_mxint4_a16(N, K)

@@ -26,6 +26,8 @@ def desc_of(fmt, N, K, G, flags):
         return hq.desc_fp8_blockwise(N, K)
     if fmt == "w8a16":
         return hq.desc_w8a16(N, K, bf16=flags["bf16"])
+    if fmt == "fp8w":
+        return hq.desc_fp8w_a16(N, K, bf16=flags["bf16"])
     if fmt == "mxint4":
         return hq.desc_mxint4_a16(N, K)
     if fmt == "fp4a16":
@@ -64,6 +66,8 @@ BENCH = {
     "mxint4a16": ("mxint4", 4096, 7168, 32, {}),
     "w8a16bf": ("w8a16", 4096, 7168, 7168, dict(bf16=True)),
     "w8a16fp": ("w8a16", 4096, 7168, 7168, dict(bf16=False)),
+    "fp8wbf": ("fp8w", 4096, 7168, 7168, dict(bf16=True)),
+    "fp8wfp": ("fp8w", 4096, 7168, 7168, dict(bf16=False)),
 }
 
 
