@@ -10,7 +10,8 @@
  * W4A4 (MXFP4 x MXFP4) and MXFP8 x MXFP4 with the activations' own E8M0
  * scales, FP8 W8A8 with blockwise scales (1 x 128 activation blocks, 128 x 128
  * weight blocks), and 16-bit activations with FP4 weights (MXFP4, or NVFP4
- * with E4M3 scales per 16 K and a per-tensor second-level scale).  A layer
+ * with E4M3 scales per 16 K and a per-tensor second-level scale), MXINT4
+ * weights, or INT8 / FP8-E4M3 weights with per-channel scales.  A layer
  * descriptor may ask for a batch-invariant reduction order or override the
  * kernel choice (tuning); two probes measure the device's attainable peaks.
  *
@@ -131,6 +132,9 @@ typedef enum hq_moe_mode {
  *   BF16      FP4_E2M1   FP8_E4M3, PER_GROUP_K, grp 16 NONE    NONE      BF16   (NVFP4; scale2
  *                                                                               PER_TENSOR_F32)
  *   BF16      FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MoE)
+ *   BF16      INT4       E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MXINT4)
+ *   BF16|FP16 INT8       FP32, PER_CHANNEL             NONE    NONE      a_dtype (INT8 weight-only)
+ *   BF16|FP16 FP8_E4M3   FP32, PER_CHANNEL             NONE    NONE      a_dtype (FP8 weight-only)
  * FP4_E2M1 activations are packed two per byte along K, element k in the low
  * nibble of byte k/2 when k is even (rows of K/2 bytes).
  * Group sizes for 16-bit scales: a multiple of 128 that divides K.
@@ -233,8 +237,12 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *      natural order (j in nibble j%8); INT4/UINT4 codes are in pair order
  *      (nibble p holds j%8 = {0,2,4,6,1,3,5,7}[p]) so that one shift+mask
  *      yields two consecutive codes in the two 16-bit halves.
- *      INT8 and FP8_E4M3: [Np/16][K/64][64 lanes][16 B]; lane l holds column
- *      16*strip + (l & 15), k = 64*chunk + 16*(l >> 4) + j, j = 0..15.
+ *      INT8 and FP8_E4M3 with 8-bit activations (W8A8, FP8 blockwise):
+ *      [Np/16][K/64][64 lanes][16 B]; lane l holds column 16*strip + (l & 15),
+ *      k = 64*chunk + 16*(l >> 4) + j, j = 0..15.
+ *      INT8 and FP8_E4M3 with 16-bit activations (weight-only):
+ *      [Np/16][K/128][2 halves][64 lanes][16 B]; lane l holds column
+ *      16*strip + (l & 15), k = 128*chunk + 32*(l >> 4) + 16*h + j, j = 0..15.
  *   scale  16-bit group scales: [E][Np/16][K/group][16];
  *          E8M0: [E][Np/16][K/128][64 lanes] bytes; lane l holds the
  *          exponent of column 16*strip + (l & 15), K-block 4*chunk + (l >> 4)
