@@ -14,7 +14,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhq.so")
+# HQ_LIB_PATH names another build of the same library (the host-sanitizer build)
+LIB_PATH = os.environ.get("HQ_LIB_PATH") or os.path.join(_HERE, "libhq.so")
 
 HQ_ABI_VERSION = 1
 

@@ -20,7 +20,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hq_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# HQ_ORACLE_LIB_PATH names another build of the oracle (the host-sanitizer build)
+_LIB = os.environ.get("HQ_ORACLE_LIB_PATH") or os.path.join(_HERE, "liboracle.so")
 
 
 def build(force: bool = True) -> str:
