@@ -9,8 +9,8 @@ benchmark candidate configurations on the target device to find better
 execution parameters per workload).
 
 Candidates are the tuning paths the layer's format has (small-M weight
-stream, 128 x 128 / 256-row / 128 x 256 / 256 x 256 tiles) with a range of K
-splits; ``hq_gemm_plan`` filters out the ones that do not apply.  Every timing
+stream on four waves, or on eight with direct A loads; 128 x 128 / 256-row /
+128 x 256 / 256 x 256 tiles) with a range of K splits; ``hq_gemm_plan`` filters out the ones that do not apply.  Every timing
 runs the library's own kernels through ``hq_gemm``; nothing is computed here.
 """
 from __future__ import annotations
@@ -35,6 +35,7 @@ def candidates(desc: hq.hq_layer_desc, M: int) -> List[int]:
     """Tuning values that apply to (desc, M): 0 (the library's own choice) first."""
     out = [0]
     tunes = [hq.HQ_TUNE(hq.HQ_TUNE_STREAM, s) for s in STREAM_SPLITS]
+    tunes.append(hq.HQ_TUNE(hq.HQ_TUNE_STREAM8, 0))
     for path, splits in TILE_SPLITS.items():
         tunes += [hq.HQ_TUNE(path, s) for s in splits]
     seen = {tuple(hq.hq_gemm_plan(desc, M))}

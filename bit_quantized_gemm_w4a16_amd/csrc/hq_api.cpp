@@ -66,12 +66,15 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
     if (d->reserved) return set_error(HQ_ERR_INVALID_ARG, "reserved fields must be zero");
     if (d->flags & ~HQ_FLAG_BATCH_INVARIANT) return set_error(HQ_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
     const int tune_path = d->tune & 0xFF, tune_splits = (d->tune >> 8) & 0xFFFF;
-    if (tune_path > HQ_TUNE_W256 || (d->tune >> 24) || (tune_path == 0 && tune_splits))
+    if (tune_path > HQ_TUNE_STREAM8 || (d->tune >> 24) || (tune_path == 0 && tune_splits))
         return set_error(HQ_ERR_INVALID_ARG, "bad tune value 0x%x", d->tune);
     if ((d->flags || d->tune) && d->num_experts)
         return set_error(HQ_ERR_UNSUPPORTED, "batch invariance and tuning overrides apply to dense layers");
-    if (d->N < 1 || d->K < 1 || d->N > (1LL << 24) || d->K > (1LL << 24))
-        return set_error(HQ_ERR_INVALID_ARG, "N=%lld K=%lld out of range [1, 2^24]", (long long)d->N, (long long)d->K);
+    // N <= 2^21: the tile epilogues address a tile's rows of the output (or of a
+    // partial tile) through one 32-bit buffer range (256 rows x N x 4 bytes)
+    if (d->N < 1 || d->K < 1 || d->N > (1LL << 21) || d->K > (1LL << 24))
+        return set_error(HQ_ERR_INVALID_ARG, "N=%lld K=%lld out of range (N in [1, 2^21], K in [1, 2^24])", (long long)d->N,
+                         (long long)d->K);
     if (d->num_experts < 0 || d->num_experts > 4096)
         return set_error(HQ_ERR_INVALID_ARG, "num_experts=%d out of range [0, 4096]", d->num_experts);
     if (d->scale2 != HQ_S2_NONE && d->scale2 != HQ_S2_PER_TENSOR_F32)

@@ -87,6 +87,7 @@ struct SkinnyArgs {
     int NS, WS;             // strips per workgroup, wave strip-columns (WK = 4 / WS)
     int a_off, s_off, z_off;  // LDS layout (bytes); MX activation scales share z_off
     int raw_i32;            // W8A8: store the int32 accumulators
+    int part_nt;            // partial tiles stored non-temporally (set by the launcher)
 };
 
 template <Fmt F>
@@ -110,7 +111,15 @@ __device__ __forceinline__ int skinny_swz(int row) {
 
 // One work item: K slice `split` of the launch.  Every thread of the
 // workgroup calls it (it holds barriers).
-template <Fmt F, int MT, int SPW, int CPW>
+//
+// NW = 4: the A slice goes to LDS, where the waves of different strips share it.
+// NW = 8 (16-bit A, one m-tile, one strip per workgroup, no K split): eight
+// waves each take an eighth of K and load their A fragments straight from
+// global memory into registers (the A rows are read by every workgroup and sit
+// in L2), all at once with the weights; no A slice in LDS, so K need not be
+// split to fit it (M = 9..16 otherwise splits K four ways and adds a finalize
+// launch).
+template <Fmt F, int MT, int SPW, int CPW, int NW>
 __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char* lds) {
     using Tr = SkinnyTraits<F>;
     using Acc = typename FmtTraits<F>::Acc;
@@ -121,10 +130,13 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     constexpr int ROWS = 16 * MT;
     constexpr int NLOAD = SPW * CPW * NB;  // weight loads per wave and batch
     static_assert(NLOAD < 64, "vmcnt counts at most 63 loads");
+    constexpr bool ADIR = NW == 8;  // A fragments straight from global memory
+    static_assert(NW == 4 || (ADIR && AROW == 256 && MT == 1 && SPW == 1), "direct A: 16-bit A, one m-tile and strip");
+    static_assert(!ADIR || NLOAD + CPW * MT * 4 + 4 < 64, "direct A: every load of a wave in flight at once");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, quad = lane >> 4;
-    const int WS = p.WS, wsh = WS >> 1, WK = 4 >> wsh;  // WS is 1, 2 or 4
+    const int WS = p.WS, wsh = WS >> 1, WK = NW >> wsh;  // WS is 1, 2 or 4 (1 with eight waves)
     const int ws = wave & (WS - 1), wk = wave >> wsh;
     const int nstrips = p.Np / 16;
     const int strip_base = blockIdx.x * p.NS;
@@ -171,11 +183,11 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
         const int nblk = (U + 63) >> 6;  // 64-unit blocks per row
         int r = 0, blk = wave;
         while (r < rows && blk >= nblk) { blk -= nblk; ++r; }
-        while (r < rows) {
+        while (!ADIR && r < rows) {
             const int pos = blk * 64 + lane;
             const char* arow = Abase + (size_t)r * (p.K / 128) * AROW;
             if (pos < U) lds_dma16(arow + ((pos ^ skinny_swz<UPC>(r)) * 16), lds + p.a_off + (r * U + blk * 64) * 16);
-            blk += 4;
+            blk += NW;
             while (r < rows && blk >= nblk) { blk -= nblk; ++r; }
         }
         if constexpr (F == Fmt::W8A8_F8B) {
@@ -183,7 +195,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
             // its strip index / 8); activation scales [chunk][row, 16-row aligned] at z_off
             const int nbn = (p.Np + 127) / 128, R16 = (rows + 15) & ~15;
             const float* swg = (const float*)Sb;
-            for (int w0 = wave * 64; w0 < p.NS * nsl; w0 += 256) {
+            for (int w0 = wave * 64; w0 < p.NS * nsl; w0 += 64 * NW) {
                 const int w = w0 + lane;
                 if (w < p.NS * nsl) {
                     const int j = w / nsl, c = w - j * nsl;
@@ -191,7 +203,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     lds_dma4(swg + (size_t)(c0 + c) * nbn + st / 8, lds + p.s_off + w0 * 4);
                 }
             }
-            for (int w0 = wave * 64; w0 < nsl * R16; w0 += 256) {
+            for (int w0 = wave * 64; w0 < nsl * R16; w0 += 64 * NW) {
                 const int w = w0 + lane;
                 if (w < nsl * R16) {
                     const int c = w / R16, r = w - c * R16;
@@ -205,7 +217,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                 const int st = strip_base + j < nstrips ? strip_base + j : nstrips - 1;
                 const char* sg = (const char*)Sb + ((size_t)st * p.ngroups + sg0) * 32;
                 const char* zg = (const char*)p.Z + ((size_t)st * p.ngroups + sg0) * 8;
-                for (int pos0 = wave * 64; pos0 < sgslab * 2; pos0 += 256) {
+                for (int pos0 = wave * 64; pos0 < sgslab * 2; pos0 += 64 * NW) {
                     const int pos = pos0 + lane;  // 16-byte scale units / 32-bit zero-point words
                     if (pos < sgslab * 2) {
                         lds_dma16(sg + pos * 16, lds + p.s_off + (j * sgslab * 2 + pos0) * 16);
@@ -217,7 +229,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
             constexpr int UPS = SB / 16;  // 16-byte scale units per chunk and strip
             for (int j = 0; j < p.NS; ++j) {
                 const int st = strip_base + j < nstrips ? strip_base + j : nstrips - 1;
-                for (int pos0 = wave * 64; pos0 < nsl * UPS; pos0 += 256) {  // SB bytes per chunk
+                for (int pos0 = wave * 64; pos0 < nsl * UPS; pos0 += 64 * NW) {  // SB bytes per chunk
                     const int pos = pos0 + lane;
                     if (pos < nsl * UPS)
                         lds_dma16((const char*)Sb + ((size_t)st * p.nc + c0) * SB + pos * 16, lds + p.s_off + (j * nsl * UPS + pos0) * 16);
@@ -226,7 +238,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
             if constexpr (MXA) {
                 // the slice's activation scales: one 4-byte word (4 K blocks) per row and chunk, [row][nsl]
                 const int nw = rows * nsl;
-                for (int w0 = wave * 64; w0 < nw; w0 += 256) {
+                for (int w0 = wave * 64; w0 < nw; w0 += 64 * NW) {
                     const int w = w0 + lane;
                     if (w < nw) {
                         const int r = w / nsl, c = w - r * nsl;
@@ -237,12 +249,26 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
         }
     }
 
+    // direct A: this wave's A fragments of every chunk of its K-part (lane (row,
+    // quad) holds K 32 quad .. 32 quad + 31 of its row and chunk: 64 contiguous
+    // bytes, one 16-byte fragment per K sub-step); rows past M read row M - 1
+    Frag8 afd[ADIR ? CPW : 1][MT][4];
+    if constexpr (ADIR) {
+        const char* arow = (const char*)p.A + (size_t)min(col, rows - 1) * (p.K / 128) * AROW + quad * 64;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int c = min(cw0 + i, wlast);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) afd[i][0][t].u = *(const v4u*)(arow + (size_t)c * AROW + t * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = CH; i < CPW; ++i) issue_w(i);
-    // the LDS copies were issued before the last (CPW - CH) chunks' loads: once
-    // at most that many loads are outstanding, this wave's copies (and its
-    // first CH chunks) have landed
-    wait_vmcnt<SPW * (CPW - CH) * NB>();
+    // the LDS copies were issued before the last (CPW - CH) chunks' loads (and,
+    // direct A, before the A fragments): once at most that many loads are
+    // outstanding, this wave's copies (and its first CH chunks) have landed
+    wait_vmcnt<SPW * (CPW - CH) * NB + (ADIR ? CPW * MT * 4 : 0)>();
     lds_barrier();
 
     // ---- 3. decode + MFMA ----
@@ -282,12 +308,12 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     // 16-bit A formats: the LDS operands of chunk i+1 (A fragments, the strip's
     // scale and zero-point word, or its E8M0 byte) are read while chunk i computes
     constexpr bool A16 = AROW == 256;
-    Frag8 afb[2][A16 ? MT : 1][4];
+    Frag8 afb[2][A16 && !ADIR ? MT : 1][4];
     uint32_t sbb[2][SPW], zwb[2][SPW];
     auto lds_operands = [&](int i, auto slot) {
         constexpr int S = decltype(slot)::value;
         const int cl = min(cw0 + i, c1 - 1) - c0;
-        if constexpr (A16) {
+        if constexpr (A16 && !ADIR) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int row = arow_l[mt];
@@ -325,7 +351,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
             const int cl = min(c, c1 - 1) - c0;
             if constexpr (WNA16) {
                 constexpr bool BF = F == Fmt::WNA16_BF16;
-                const Frag8(&af)[MT][4] = afb[i & 1];
+                const Frag8(&af)[MT][4] = ADIR ? afd[ADIR ? i : 0] : afb[i & 1];
                 v4f rs[MT];
                 if constexpr (BF) {
 #pragma unroll
@@ -383,7 +409,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                 // INT8 -> exact 16-bit operands (the per-channel scale is applied in the
                 // epilogue); a chunk past the wave's part multiplies zeros
                 constexpr bool BF = w8bf(F);
-                const Frag8(&af)[MT][4] = afb[i & 1];
+                const Frag8(&af)[MT][4] = ADIR ? afd[ADIR ? i : 0] : afb[i & 1];
 #pragma unroll
                 for (int sp = 0; sp < SPW; ++sp)
 #pragma unroll
@@ -396,7 +422,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     }
             } else if constexpr (FP4B) {
                 // e2m1 x (2^(E-127) or E4M3 group scale) -> exact bf16 operands, bf16 MFMA
-                const Frag8(&af)[MT][4] = afb[i & 1];
+                const Frag8(&af)[MT][4] = ADIR ? afd[ADIR ? i : 0] : afb[i & 1];
 #pragma unroll
                 for (int sp = 0; sp < SPW; ++sp) {
                     const int j = ws * SPW + sp;
@@ -517,65 +543,78 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) acc[sp][mt] += red[((((k2 - 1) * WS + ws) * SPW + sp) * MT + mt) * 64 + lane];
     }
-    // ---- 5. split K: partial tile out (summed in slice order by the finalize pass) ----
-    if (p.splits > 1) {
-        if (wk == 0) {
+    // ---- 5./6. output (K-part 0): lane (col, quad) holds rows mt*16 + 4*quad + r of column col ----
+    // The K slice's fp32 / int32 partial tile (split K, summed in slice order by
+    // the finalize pass), or the output with the format's epilogue.  Stores go
+    // through a buffer resource over the rows 0 .. M-1 of the output (or of the
+    // slice's partial tile): rows past M and columns past N (Np) take an offset
+    // outside it and are dropped, so no store sits behind a branch, and the
+    // epilogue's scales are loaded before the first store.  The range fits 32
+    // bits: M <= 64 rows of at most 2^21 columns of 4 bytes.
+    if (wk != 0) return;
+    const bool partial = p.splits > 1;
+    constexpr bool ASC = F == Fmt::W4A8_MX || F == Fmt::W8A8_I8, WSC = F == Fmt::W8A8_I8 || w8a16(F);
+    float asr[ASC ? MT : 1][4], swn[WSC ? SPW : 1];
+    if (!partial) {
+        if constexpr (ASC) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = mt * 16 + quad * 4 + r;
+                    asr[mt][r] = m < rows ? p.a_scale[m] : 0.f;
+                }
+        }
+        if constexpr (WSC) {
 #pragma unroll
             for (int sp = 0; sp < SPW; ++sp) {
-                if (wstrip[sp] >= nstrips) continue;
                 const int n = wstrip[sp] * 16 + col;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int m = mt * 16 + quad * 4 + r;
-                        if (m >= rows) continue;
-                        const int64_t po = ((int64_t)split * p.M + m) * p.Np + n;
-                        if constexpr (F == Fmt::W8A8_I8) ((int*)p.part)[po] = acc[sp][mt][r];
-                        else ((float*)p.part)[po] = acc[sp][mt][r];
-                    }
+                swn[sp] = n < p.N ? ((const float*)Sb)[n] : 0.f;
             }
         }
-        return;
     }
-
-    // ---- 6. output (K-part 0): lane (col, quad) holds rows mt*16 + 4*quad + r of column col ----
+    auto outv = [&](int sp, int mt, int r) -> uint32_t {
+        if (partial) return bits32(acc[sp][mt][r]);
+        if constexpr (WNA16) return f32_to_16<F == Fmt::WNA16_BF16>(acc[sp][mt][r]);
+        else if constexpr (F == Fmt::W8A8_I8)
+            return p.raw_i32 ? (uint32_t)acc[sp][mt][r] : f32_to_bf16_bits((float)acc[sp][mt][r] * asr[mt][r] * swn[sp]);
+        else if constexpr (F == Fmt::W4A8_MX) return f32_to_bf16_bits(acc[sp][mt][r] * asr[mt][r]);
+        else if constexpr (F == Fmt::NVFP4_BF16) return f32_to_bf16_bits(acc[sp][mt][r] * *p.s2);
+        else if constexpr (w8a16(F)) return f32_to_16<w8bf(F)>(acc[sp][mt][r] * swn[sp]);
+        else return f32_to_bf16_bits(acc[sp][mt][r]);
+    };
+    const int es = partial || (F == Fmt::W8A8_I8 && p.raw_i32) ? 4 : 2;
+    const int ldo = partial ? p.Np : p.N;
+    char* obase = partial ? (char*)p.part + (int64_t)split * p.M * p.Np * 4 : (char*)p.D;
+    const rsrc_t rO = make_rsrc(obase, (uint32_t)rows * (uint32_t)ldo * (uint32_t)es);
+    constexpr uint32_t DROP = 0xFFFFFFF0u;
+    auto store = [&](auto kind) {
+        constexpr int K_ = decltype(kind)::value;  // 0: 16-bit, 1: 32-bit, 2: 32-bit non-temporal
 #pragma unroll
-    for (int sp = 0; sp < SPW; ++sp) {
-        const int n = wstrip[sp] * 16 + col;
-        if (wk != 0 || wstrip[sp] >= nstrips) continue;
+        for (int sp = 0; sp < SPW; ++sp) {
+            const int n = wstrip[sp] * 16 + col;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mt * 16 + quad * 4 + r;
-                if (m >= ROWS) continue;
-                if (m >= rows) continue;
-                const int drow = m;
-                if (n >= p.N) continue;
-                const int64_t o = (int64_t)drow * p.N + n;
-                if constexpr (WNA16) {
-                    ((uint16_t*)p.D)[o] = f32_to_16<F == Fmt::WNA16_BF16>(acc[sp][mt][r]);
-                } else if constexpr (F == Fmt::W8A8_I8) {
-                    if (p.raw_i32) ((int*)p.D)[o] = acc[sp][mt][r];
-                    else ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)acc[sp][mt][r] * p.a_scale[m] * ((const float*)Sb)[n]);
-                } else if constexpr (F == Fmt::W4A8_MX) {
-                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r] * p.a_scale[m]);
-                } else if constexpr (F == Fmt::NVFP4_BF16) {
-                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r] * *p.s2);
-                } else if constexpr (w8a16(F)) {
-                    ((uint16_t*)p.D)[o] = f32_to_16<w8bf(F)>(acc[sp][mt][r] * ((const float*)Sb)[n]);
-                } else {
-                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[sp][mt][r]);
+                for (int r = 0; r < 4; ++r) {
+                    const int m = mt * 16 + quad * 4 + r;
+                    const uint32_t off = m < rows && n < ldo ? ((uint32_t)m * (uint32_t)ldo + (uint32_t)n) * (uint32_t)es : DROP;
+                    const uint32_t v = outv(sp, mt, r);
+                    if constexpr (K_ == 0) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, rO, off, 0, 0);
+                    else if constexpr (K_ == 1) __builtin_amdgcn_raw_buffer_store_b32(v, rO, off, 0, 0);
+                    else __builtin_amdgcn_raw_buffer_store_b32(v, rO, off, 0, 2);
                 }
-            }
-    }
+        }
+    };
+    if (partial && p.part_nt) store(std::integral_constant<int, 2>{});
+    else if (es == 4) store(std::integral_constant<int, 1>{});
+    else store(std::integral_constant<int, 0>{});
 }
 
-template <Fmt F, int MT, int SPW, int CPW>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
+template <Fmt F, int MT, int SPW, int CPW, int NW>
+__global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];  // sized per launch (plan.lds_bytes)
-    skinny_item<F, MT, SPW, CPW>(p, blockIdx.y, lds);
+    skinny_item<F, MT, SPW, CPW, NW>(p, blockIdx.y, lds);
 }
 
 // ---- host-side plan ----
@@ -583,6 +622,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
 struct SkinnyPlan {
     bool ok;        // false: a forced K split that the slice's LDS or register batch cannot take
     int NS, WS, SPW, splits, MT, CPW;
+    int NW;         // waves per workgroup: 4, or 8 with direct A loads (16-bit A, M <= 16)
     int cps, cpk;   // chunks per slice, per wave K-part
     int a_off, s_off, z_off;
     int lds_bytes;  // dynamic LDS of one workgroup
@@ -632,13 +672,57 @@ inline int64_t skinny_lds_need(Fmt F, int64_t rows, int64_t cmax, int NS, int gc
     return skinny_lds(F, rows, cmax, NS, gch).bytes;
 }
 
+constexpr bool skinny_a16(Fmt F) {
+    return F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 ||
+           F == Fmt::MXINT4_BF16 || w8a16(F);
+}
+
+// The eight-wave schedule with direct A loads: one strip per workgroup, K in
+// eighths, no split.  It applies to 16-bit A at M <= 16 where a wave's eighth
+// of K fits one register batch with its A fragments.
+inline bool skinny_direct_fits(Fmt F, int64_t M, int64_t K) {
+    const int64_t nc = K / 128, cpk = (nc + 7) / 8;
+    return skinny_a16(F) && M >= 1 && M <= 16 && nc >= 8 && cpk <= 8;
+}
+inline int skinny_direct_cpw(int64_t cpk) { return cpk <= 2 ? 2 : cpk <= 4 ? 4 : cpk == 7 ? 7 : 8; }
+
 // Dense plan: strips per workgroup grow with M so the A slice is re-read about
 // nstrips / NS times; K slices until the grid covers the chip and the slice
-// fits in LDS.
-inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, int force_splits = 0) {
+// fits in LDS.  mode 0: the library's choice; 1: four waves with the A slice in
+// LDS (force_splits K slices, 0 = planned); 2: eight waves with direct A loads.
+inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, int force_splits = 0, int mode = 0) {
     const int64_t nstrips = Np / 16, nc = K / 128;
     const int gch = G >= 128 ? G / 128 : 1;
     SkinnyPlan p{};
+    p.NW = 4;
+    // The formats with the longer decodes (NVFP4, MXINT4, 8-bit weights) at up to
+    // 8 rows on a strip per CU or more: eight waves hide it better (N=4096,
+    // K=7168, M=1: INT8 9.8 -> 9.0 us, FP8 8.8 -> 8.6, MXINT4 9.3 -> 8.6, NVFP4
+    // 10.2 -> 9.7).  UINT4 and MXFP4 measured slower that way at 1..4 rows, and
+    // every format at 9..16 rows (more A read from L2 than the split's partials
+    // and finalize cost: fp16 UINT4 M=16 11.6 against 11.1 us).
+    const bool heavy = F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || w8a16(F);
+    const bool direct = mode == 2 || (mode == 0 && heavy && M <= 8 && nstrips >= 192 && skinny_direct_fits(F, M, K));
+    if (direct) {
+        p.ok = skinny_direct_fits(F, M, K) && force_splits <= 1;
+        p.NW = 8;
+        p.NS = p.SPW = p.WS = 1;
+        p.MT = 1;
+        p.groups_x = nstrips;
+        p.splits = 1;
+        p.cps = (int)nc;
+        p.cpk = (int)cdiv(nc, 8);
+        p.CPW = skinny_direct_cpw(p.cpk);
+        const SkinnyLds L = skinny_lds(F, 0, nc, 1, gch);  // scales only
+        p.a_off = (int)L.a_off;
+        p.s_off = (int)L.s_off;
+        p.z_off = (int)L.z_off;
+        const int64_t red = 7 * 1024;  // seven K-parts' 16 x 16 fp32 tiles
+        p.lds_bytes = (int)(L.bytes > red ? L.bytes : red);
+        if (p.lds_bytes < 1024) p.lds_bytes = 1024;
+        if (p.lds_bytes > kSkinnyLds) p.ok = false;
+        return p;
+    }
     p.NS = M <= 8 ? 1 : M <= 16 ? 2 : M <= 32 ? 4 : 8;
     // W4A8 at M <= 32: two strips per workgroup keep 224 workgroups at N = 7168
     // and the whole 8-bit A slice in LDS, so no K split (and no finalize pass)
@@ -683,20 +767,39 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
     return p;
 }
 
-template <Fmt F, int MT, int SPW, int CPW>
+template <Fmt F, int MT, int SPW, int CPW, int NW = 4>
 hipError_t launch_skinny_k(dim3 grid, int lds_bytes, const SkinnyArgs& a, hipStream_t st) {
     if (plan_recorder()) {
-        plan_record("skinny_kernel<%s,%d,%d,%d> grid=%ux%u splits=%d", fmt_name(F), MT, SPW, CPW, grid.x, grid.y, a.splits);
+        if (NW == 8)
+            plan_record("skinny_kernel<%s,%d,%d,%d,direct> grid=%ux%u splits=%d", fmt_name(F), MT, SPW, CPW, grid.x, grid.y, a.splits);
+        else
+            plan_record("skinny_kernel<%s,%d,%d,%d> grid=%ux%u splits=%d", fmt_name(F), MT, SPW, CPW, grid.x, grid.y, a.splits);
         if (a.splits > 1) plan_workspace((size_t)a.splits * (size_t)a.M * (size_t)a.Np * 4);
         return hipSuccess;
     }
     // allow dynamic LDS beyond the 64 KB default, once per instantiation
-    static const hipError_t attr = hipFuncSetAttribute((const void*)skinny_kernel<F, MT, SPW, CPW>,
+    static const hipError_t attr = hipFuncSetAttribute((const void*)skinny_kernel<F, MT, SPW, CPW, NW>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLds);
     if (attr != hipSuccess) return attr;
     if (lds_bytes < 1024 || lds_bytes > kSkinnyLds) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((skinny_kernel<F, MT, SPW, CPW>), grid, dim3(256), (size_t)lds_bytes, st, a);
+    hipLaunchKernelGGL((skinny_kernel<F, MT, SPW, CPW, NW>), grid, dim3(64 * NW), (size_t)lds_bytes, st, a);
     return hipGetLastError();
+}
+
+// eight waves, direct A loads (16-bit A formats only)
+template <Fmt F>
+hipError_t launch_skinny_direct(int cpw, dim3 grid, int lds_bytes, const SkinnyArgs& a, hipStream_t st) {
+    if constexpr (skinny_a16(F)) {
+        switch (cpw) {
+            case 2: return launch_skinny_k<F, 1, 1, 2, 8>(grid, lds_bytes, a, st);
+            case 4: return launch_skinny_k<F, 1, 1, 4, 8>(grid, lds_bytes, a, st);
+            case 7: return launch_skinny_k<F, 1, 1, 7, 8>(grid, lds_bytes, a, st);
+            case 8: return launch_skinny_k<F, 1, 1, 8, 8>(grid, lds_bytes, a, st);
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        return hipErrorNotSupported;
+    }
 }
 
 template <Fmt F, int MT, int SPW>
@@ -718,6 +821,7 @@ hipError_t launch_skinny_cpw(int cpw, dim3 grid, int lds_bytes, const SkinnyArgs
 template <Fmt F>
 hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t st) {
     s.splits = pl.splits;
+    s.part_nt = part_nontemporal(pl.splits, s.M, s.Np);
     s.cps = pl.cps;
     s.cpk = pl.cpk;
     s.NS = pl.NS;
@@ -727,13 +831,16 @@ hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t s
     s.z_off = pl.z_off;
     const dim3 grid((unsigned)pl.groups_x, (unsigned)pl.splits);
     if (pl.cpk > pl.CPW) return hipErrorInvalidValue;  // K-part beyond one register batch (planned out)
+    if (pl.NW == 8) return pl.splits == 1 ? launch_skinny_direct<F>(pl.CPW, grid, pl.lds_bytes, s, st) : hipErrorInvalidValue;
     hipError_t e;
     if (pl.SPW == 2) e = launch_skinny_cpw<F, 4, 2>(pl.CPW, grid, pl.lds_bytes, s, st);
     else if (pl.MT == 1) e = launch_skinny_cpw<F, 1, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
     else if (pl.MT == 2) e = launch_skinny_cpw<F, 2, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
     else e = launch_skinny_cpw<F, 4, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
     if (e != hipSuccess || pl.splits == 1) return e;
-    return launch_finalize<F>(FinalizeArgs{s.part, s.D, s.a_scale, (const float*)s.S, s.s2, s.M, s.N, s.Np, s.splits, s.raw_i32}, st);
+    return launch_finalize<F>(FinalizeArgs{s.part, s.D, s.a_scale, (const float*)s.S, s.s2, s.M, s.N, s.Np, s.splits, s.raw_i32,
+                                           s.part_nt},
+                              st);
 }
 
 
@@ -744,10 +851,12 @@ hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t s
 // row's result does not depend on M) changes the choice.
 template <Fmt F>
 hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
-    const bool tile_forced = a.tune_path >= TUNE_T128;
-    if (!a.invariant && !tile_forced && (a.tune_path == TUNE_STREAM || a.M <= skinny_max_m(F))) {
+    const bool tile_forced = a.tune_path >= TUNE_T128 && a.tune_path <= TUNE_W256;
+    const bool stream_forced = a.tune_path == TUNE_STREAM || a.tune_path == TUNE_STREAM8;
+    if (!a.invariant && !tile_forced && (stream_forced || a.M <= skinny_max_m(F))) {
         if (a.M > kSkinnyMaxM) return hipErrorNotSupported;
-        const SkinnyPlan pl = plan_skinny(F, a.M, a.Np, a.K, G, a.tune_splits);
+        const int mode = a.tune_path == TUNE_STREAM8 ? 2 : a.tune_path == TUNE_STREAM ? 1 : 0;
+        const SkinnyPlan pl = plan_skinny(F, a.M, a.Np, a.K, G, a.tune_splits, mode);
         if (!pl.ok) return hipErrorNotSupported;
         return launch_skinny_dense<F>(pl, s, a.stream);
     }

@@ -123,6 +123,7 @@ struct TileArgs {
     int tiles_m, tiles_n, splits;
     int max_splits;         // upper bound on splits (0: none; 1 in batch-invariant mode)
     int raw_i32;            // W8A8: store int32 accumulators
+    int part_nt;            // partial tiles stored non-temporally (set by the launcher)
     // MoE (tiles_m is an upper bound; the real count is *ntiles)
     const int* tile_info;   // per m-tile: expert, first sorted row, row count
     const int* ntiles;      // device count of valid m-tiles
@@ -133,6 +134,32 @@ struct TileArgs {
 // A-tile swizzle: the 16-byte unit u of row r is stored at u ^ swz(r).  Rows
 // of 4 units (fp4 A, 64 bytes) need none: a wave's fragment read covers 1 KB
 // of consecutive bytes.
+// Split-K partial tiles of 4..24 MB are stored and re-read non-temporally.
+// Measured on fp16 W4A16 at N=4096, K=7168 (graph replays, cold weights):
+// M = 64 (8 slices, 8.4 MB) 21.2 -> 19.0 us, M = 128 (8 slices, 16.8 MB)
+// 26.6 -> 21.4 us, W4A8 M = 64 / 128 (7.3 MB) 16.3 / 19.8 -> 14.8 / 18.4 us;
+// smaller sets gain nothing (INT8 at M = 16, 2.4 MB: 30.4 -> 31.8 us) and
+// larger ones lose (33.5 MB at M = 512: 44.4 -> 46.6 us).
+inline int part_nontemporal(int64_t splits, int64_t M, int64_t Np) {
+    const int64_t bytes = splits * M * Np * 4;
+    return splits > 1 && bytes >= (int64_t)4 << 20 && bytes <= (int64_t)24 << 20;
+}
+// The non-temporal path uses buffer stores / loads with the NT bit (a plain
+// access of the same address in the other branch would be merged with it and
+// the hint lost).  rP covers the partial tiles when nt is set (they are then
+// under 24 MB).
+// The 32 bits of an fp32 / int32 accumulator element.  The element is taken
+// by value: a bit cast of the vector element expression itself read element 0
+// of the vector (every row of a partial tile came out as row 0).
+template <typename T>
+__device__ __forceinline__ uint32_t bits32(T v) {
+    static_assert(sizeof(T) == 4, "32-bit element");
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ rsrc_t part_rsrc(void* part, int nt, int64_t splits, int64_t M, int64_t Np) {
+    return make_rsrc(part, nt ? (uint32_t)(splits * M * Np * 4) : 0u);
+}
+
 __device__ __forceinline__ int swz(int row, int units) {
     return units == 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : units == 8 ? ((row >> 1) & 7) : 0;
 }
@@ -1035,45 +1062,89 @@ void tile_gemm_kernel(TileArgs p) {
     }
 
     // ---- epilogue: lane (col, quad) holds rows 4*quad + r of column col in each 16x16 tile ----
+    // The epilogue's scales are loaded before the first store (stores and loads
+    // share one counter: a load between stores waits for every store before it).
+    constexpr bool ASC = F == Fmt::W4A8_MX || F == Fmt::W8A8_I8, WSC = F == Fmt::W8A8_I8 || w8a16(F);
     const bool partial = p.splits > 1;
+    float asr[ASC ? MT : 1][4], swn[WSC ? NT : 1];
+    if (!partial) {
+        if constexpr (ASC) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+            for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int lrow = wm * (BM / WM) + i * 16 + quad * 4 + r;
-            const int drow = rowinfo[BM + lrow];
-            if (drow < 0) continue;
-            float as = 1.f;
-            if constexpr (F == Fmt::W4A8_MX || F == Fmt::W8A8_I8)
-                if (!partial) as = p.a_scale[rowinfo[lrow]];
+                for (int r = 0; r < 4; ++r) {
+                    const int lrow = wm * (BM / WM) + i * 16 + quad * 4 + r;
+                    asr[i][r] = rowinfo[BM + lrow] >= 0 ? p.a_scale[rowinfo[lrow]] : 0.f;
+                }
+        }
+        if constexpr (WSC) {
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const int n = (pid_n * NSTRIP + wn * NT + j) * 16 + col;
-                if (partial) {
-                    if (n >= p.Np) continue;
-                    const int64_t po = ((int64_t)split * p.M + drow) * p.Np + n;
-                    if constexpr (F == Fmt::W8A8_I8) ((int*)p.part)[po] = acc[i][j][r];
-                    else ((float*)p.part)[po] = acc[i][j][r];
-                    continue;
-                }
-                if (n >= p.N) continue;
-                const int64_t o = (int64_t)drow * p.N + n;
-                if constexpr (F == Fmt::WNA16_F16) {
-                    ((uint16_t*)p.D)[o] = f32_to_16<false>(acc[i][j][r]);
-                } else if constexpr (F == Fmt::W8A8_I8) {
-                    if (p.raw_i32) ((int*)p.D)[o] = acc[i][j][r];
-                    else ((uint16_t*)p.D)[o] = f32_to_bf16_bits((float)acc[i][j][r] * as * ((const float*)Sbase)[n]);
-                } else if constexpr (F == Fmt::W4A8_MX) {
-                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r] * as);
-                } else if constexpr (F == Fmt::NVFP4_BF16) {
-                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r] * *p.s2);
-                } else if constexpr (w8a16(F)) {
-                    ((uint16_t*)p.D)[o] = f32_to_16<w8bf(F)>(acc[i][j][r] * ((const float*)Sbase)[n]);
-                } else {
-                    ((uint16_t*)p.D)[o] = f32_to_bf16_bits(acc[i][j][r]);
-                }
+                swn[j] = n < p.N ? ((const float*)Sbase)[n] : 0.f;
             }
         }
+    }
+    // the output value of accumulator (i, j, r): fp32 partial or int32 bits, or the format's epilogue
+    auto outv = [&](int i, int j, int r) -> uint32_t {
+        if (partial) return bits32(acc[i][j][r]);
+        if constexpr (F == Fmt::WNA16_F16) return f32_to_16<false>(acc[i][j][r]);
+        else if constexpr (F == Fmt::W8A8_I8)
+            return p.raw_i32 ? (uint32_t)acc[i][j][r] : f32_to_bf16_bits((float)acc[i][j][r] * asr[i][r] * swn[j]);
+        else if constexpr (F == Fmt::W4A8_MX) return f32_to_bf16_bits(acc[i][j][r] * asr[i][r]);
+        else if constexpr (F == Fmt::NVFP4_BF16) return f32_to_bf16_bits(acc[i][j][r] * *p.s2);
+        else if constexpr (w8a16(F)) return f32_to_16<w8bf(F)>(acc[i][j][r] * swn[j]);
+        else return f32_to_bf16_bits(acc[i][j][r]);
+    };
+    if constexpr (F != Fmt::MOE_MX) {
+        // dense: the tile's rows m0 .. m0 + mrows - 1 of the output, or of this K
+        // slice's fp32 / int32 partial tile, through a buffer resource that starts
+        // at the tile's first row.  Columns past N (Np for partials) and rows past
+        // M take an offset outside it and the store is dropped, so no store sits
+        // behind a branch (a branch per store makes the compiler wait for every
+        // store before it).  The range fits 32 bits: N <= 2^21 (checked at the call).
+        const int es = partial || (F == Fmt::W8A8_I8 && p.raw_i32) ? 4 : 2;  // bytes per output element
+        const int ld = partial ? p.Np : p.N;                                  // elements per row
+        char* base = partial ? (char*)p.part + (((int64_t)split * p.M + m0) * p.Np) * 4 : (char*)p.D + (int64_t)m0 * p.N * es;
+        const rsrc_t rO = make_rsrc(base, (uint32_t)mrows * (uint32_t)ld * (uint32_t)es);
+        constexpr uint32_t DROP = 0xFFFFFFF0u;  // beyond any range here (at most 2^31 bytes)
+        auto store = [&](auto kind) {
+            constexpr int K_ = decltype(kind)::value;  // 0: 16-bit, 1: 32-bit, 2: 32-bit non-temporal
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int lr = wm * (BM / WM) + i * 16 + quad * 4 + r;
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        const int n = (pid_n * NSTRIP + wn * NT + j) * 16 + col;
+                        const uint32_t off = lr < mrows && n < ld ? ((uint32_t)lr * (uint32_t)ld + (uint32_t)n) * (uint32_t)es : DROP;
+                        const uint32_t v = outv(i, j, r);
+                        if constexpr (K_ == 0) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, rO, off, 0, 0);
+                        else if constexpr (K_ == 1) __builtin_amdgcn_raw_buffer_store_b32(v, rO, off, 0, 0);
+                        else __builtin_amdgcn_raw_buffer_store_b32(v, rO, off, 0, 2);
+                    }
+                }
+        };
+        if (partial && p.part_nt) store(std::integral_constant<int, 2>{});
+        else if (es == 4) store(std::integral_constant<int, 1>{});
+        else store(std::integral_constant<int, 0>{});
+    } else {
+        // MoE: scattered output rows (a row's pair index), no K split
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int drow = rowinfo[BM + wm * (BM / WM) + i * 16 + quad * 4 + r];
+                if (drow < 0) continue;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int n = (pid_n * NSTRIP + wn * NT + j) * 16 + col;
+                    if (n >= p.N) continue;
+                    ((uint16_t*)p.D)[(int64_t)drow * p.N + n] = (uint16_t)outv(i, j, r);
+                }
+            }
+    }
 }
 
 // Split-K finalize shared by the dense launchers: sums the fp32 / int32
@@ -1087,6 +1158,7 @@ struct FinalizeArgs {
     const float* s_w;      // per-channel scale (W8A8)
     const float* s2;       // per-tensor second-level scale (NVFP4)
     int M, N, Np, splits, raw_i32;
+    int part_nt;           // the partial tiles were stored non-temporally: read them so too
 };
 
 template <Fmt F>
@@ -1099,16 +1171,28 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(FinalizeArgs p) {
     using V = typename std::conditional<I32, v4i, v4f>::type;
     const V* src = (const V*)((const char*)p.part + base * 4);
     const int64_t vstride = stride / 4;  // Np is a multiple of 16
-    V acc = src[0];
-    for (int s0 = 1; s0 < p.splits; s0 += 8) {
-        V v[8];
+    // non-temporal partial tiles are read with the NT bit (buffer loads; see
+    // store_part); one loop per kind, so each keeps its eight loads in flight
+    const rsrc_t rP = part_rsrc(const_cast<void*>(p.part), p.part_nt, p.splits, p.M, p.Np);
+    auto sum = [&](auto ntc) -> V {
+        constexpr bool NT = decltype(ntc)::value;
+        auto ld = [&](int s) -> V {
+            if constexpr (NT) return __builtin_bit_cast(V, buf16<true>(rP, (uint32_t)((base + (int64_t)s * stride) * 4), 0u));
+            else return src[s * vstride];
+        };
+        V a{};
+        for (int s0 = 0; s0 < p.splits; s0 += 8) {  // up to eight slices' loads at once, summed in slice order
+            V v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (s0 + j < p.splits) v[j] = src[(s0 + j) * vstride];
+            for (int j = 0; j < 8; ++j)
+                if (s0 + j < p.splits) v[j] = ld(s0 + j);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (s0 + j < p.splits) acc += v[j];
-    }
+            for (int j = 0; j < 8; ++j)
+                if (s0 + j < p.splits) a = s0 + j == 0 ? v[j] : a + v[j];
+        }
+        return a;
+    };
+    V acc = p.part_nt ? sum(std::true_type{}) : sum(std::false_type{});
     const int cnt = p.N - n < 4 ? p.N - n : 4;
     if constexpr (I32) {
         if (p.raw_i32) {
@@ -1149,7 +1233,7 @@ struct TilePlan {
 };
 
 // Tuning overrides of the kernel choice (the descriptor's tune field).
-enum TunePath { TUNE_AUTO = 0, TUNE_STREAM = 1, TUNE_T128 = 2, TUNE_T256 = 3, TUNE_W128 = 4, TUNE_W256 = 5 };
+enum TunePath { TUNE_AUTO = 0, TUNE_STREAM = 1, TUNE_T128 = 2, TUNE_T256 = 3, TUNE_W128 = 4, TUNE_W256 = 5, TUNE_STREAM8 = 6 };
 
 // The largest grids use 256-column tiles where the format has them (256 x 256,
 // else 128 x 256), then 256 x 128 tiles on 8 waves; smaller ones 128 x 128
@@ -1184,6 +1268,7 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
     if (p.max_splits > 0 && p.splits > p.max_splits) p.splits = p.max_splits;
     p.tiles_m = (int)((p.M + BM - 1) / BM);
     p.tiles_n = (int)((p.Np + BN - 1) / BN);
+    p.part_nt = part_nontemporal(p.splits, p.M, p.Np);
     const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.splits;
     if (plan_recorder()) {
         plan_record("tile_gemm_kernel<%s,%d,%d,%d,%d,%d> grid=%lld splits=%d", fmt_name(F), BM, BN, WM, WN, PD,
@@ -1195,7 +1280,9 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     if (p.splits == 1) return hipSuccess;
-    return launch_finalize<F>(FinalizeArgs{p.part, p.D, p.a_scale, (const float*)p.S, p.s2, p.M, p.N, p.Np, p.splits, p.raw_i32}, st);
+    return launch_finalize<F>(FinalizeArgs{p.part, p.D, p.a_scale, (const float*)p.S, p.s2, p.M, p.N, p.Np, p.splits, p.raw_i32,
+                                           p.part_nt},
+                              st);
 }
 
 // Formats with a 256-row tile.  4-bit weights with 16-bit A: 256 x 128 on 8

@@ -29,7 +29,7 @@ HQ_ASCALE_NONE, HQ_ASCALE_PER_TOKEN_F32, HQ_ASCALE_MX_E8M0, HQ_ASCALE_PER_BLOCK1
 HQ_S2_NONE, HQ_S2_PER_TENSOR_F32 = 0, 1
 HQ_MOE_INDEXED, HQ_MOE_GROUPED = 1, 2
 HQ_FLAG_BATCH_INVARIANT = 1
-HQ_TUNE_STREAM, HQ_TUNE_T128, HQ_TUNE_T256, HQ_TUNE_W128, HQ_TUNE_W256 = 1, 2, 3, 4, 5
+HQ_TUNE_STREAM, HQ_TUNE_T128, HQ_TUNE_T256, HQ_TUNE_W128, HQ_TUNE_W256, HQ_TUNE_STREAM8 = 1, 2, 3, 4, 5, 6
 
 
 def HQ_TUNE(path: int, splits: int = 0) -> int:

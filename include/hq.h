@@ -138,7 +138,8 @@ typedef enum hq_moe_mode {
  * FP4_E2M1 activations are packed two per byte along K, element k in the low
  * nibble of byte k/2 when k is even (rows of K/2 bytes).
  * Group sizes for 16-bit scales: a multiple of 128 that divides K.
- * K: a multiple of 128 (every format).  N: any value >= 1.
+ * K: a multiple of 128 (every format), at most 2^24.  N: 1 .. 2^21 (a row
+ * tile of the output is addressed through one 32-bit buffer range).
  * out_dtype INT32 returns the raw INT8 x INT8 accumulators (bit-exact).
  */
 typedef struct hq_layer_desc {
@@ -177,9 +178,13 @@ typedef struct hq_layer_desc {
  * candidates on the device, "Humming wird angekuendigt", section "Zukuenftige
  * Plaene").  tune = HQ_TUNE(path, splits); splits = K slices (0: the
  * planner's choice for the stream path, 1 for tiles).  Paths:
- *   HQ_TUNE_STREAM  the small-M weight stream (M <= 64)
+ *   HQ_TUNE_STREAM  the small-M weight stream (M <= 64), A slice in LDS
  *   HQ_TUNE_T128    128 x 128 tiles          HQ_TUNE_T256  the 256-row tile
  *   HQ_TUNE_W128    128 x 256 tiles          HQ_TUNE_W256  256 x 256 tiles
+ *   HQ_TUNE_STREAM8 the small-M weight stream on eight waves that load their
+ *                   A fragments directly, one 16-column strip per workgroup
+ *                   and no K split (16-bit activations, M <= 16, K / 128
+ *                   between 8 and 64; splits 0 or 1)
  * A path the layer's format lacks, or a split the slice cannot take, returns
  * HQ_ERR_UNSUPPORTED at the call.  hq_gemm_plan and hq_workspace_bytes follow
  * the override.
@@ -189,6 +194,7 @@ typedef struct hq_layer_desc {
 #define HQ_TUNE_T256 3
 #define HQ_TUNE_W128 4
 #define HQ_TUNE_W256 5
+#define HQ_TUNE_STREAM8 6
 #define HQ_TUNE(path, splits) ((int32_t)(path) | ((int32_t)(splits) << 8))
 
 /* ---------------------------------------------------------------------- */

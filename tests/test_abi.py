@@ -318,3 +318,23 @@ def test_probe_argument_checks_need_no_gpu():
     with pytest.raises(hq.HQError) as e:
         hq.hq_probe_mfma(hq.HQ_DT_FP16, 0, 1, None, stream=0)
     assert e.value.status == hq.HQ_ERR_INVALID_ARG
+
+
+def test_direct_stream_override_rejects_what_it_cannot_take():
+    """HQ_TUNE_STREAM8 (eight waves, direct A loads): more than 16 rows, a K split,
+    K beyond 64 chunks or 8-bit activations give HQ_ERR_UNSUPPORTED; 16-bit A at
+    M <= 16 plans one unsplit launch."""
+    from bit_quantized_gemm_w4a16_amd import autotune
+    t8 = hq.HQ_TUNE(hq.HQ_TUNE_STREAM8, 0)
+    desc = hq.desc_w4a16(4096, 7168, 128, bf16=False, zp=True)
+    plan = hq.hq_gemm_plan(autotune.with_tune(desc, t8), 8)
+    assert len(plan) == 1 and ",direct>" in plan[0] and "splits=1" in plan[0]
+    for d, M in ((autotune.with_tune(desc, t8), 17), (autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_STREAM8, 2)), 8),
+                 (autotune.with_tune(hq.desc_w4a16(4096, 8320, 128, bf16=False, zp=True), t8), 8),
+                 (autotune.with_tune(hq.desc_w4a8_mxfp4(7168, 4096), t8), 8)):
+        with pytest.raises(hq.HQError):
+            hq.hq_gemm_plan(d, M)
+    bad = hq.hq_layer_desc.from_buffer_copy(desc)
+    bad.tune = 7
+    with pytest.raises(hq.HQError):
+        hq.hq_gemm_plan(bad, 8)

@@ -43,7 +43,7 @@ def _write_trace(path, config, sweep, dur_of):
 
 
 def test_kernel_stats_attributes_dispatches_per_M(tmp_path):
-    sweep = [1, 16, 8192]
+    sweep = [1, 32, 8192]
 
     def dur(M, c, k):       # ns; the first two calls per M are untimed warm-ups
         if c < 2 * ncopy_ref[0]:
@@ -54,16 +54,16 @@ def test_kernel_stats_attributes_dispatches_per_M(tmp_path):
     p = tmp_path / "trace.csv"
     _write_trace(p, "c2", sweep, dur)
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--kernel-stats", str(p), "--config", "c2",
-                          "--sweep", "1,16,8192"], capture_output=True, text=True, check=True)
+                          "--sweep", "1,32,8192"], capture_output=True, text=True, check=True)
     rec = json.loads(out.stdout.strip().splitlines()[-1])
     by = {r["M"]: r for r in rec["kernel_only_us"]}
     assert [k["kernel"].split("<")[0] for k in by[1]["kernels"]] == ["skinny_kernel"]
     assert by[1]["calls"] == bench.REPS * ncopy_ref[0]
-    # M=1: one kernel of 10 us + 1 ns + {0,10,20} ns; M=16: 10 + 3 us + 2*16 ns + ...
+    # M=1: one kernel of 10 us + 1 ns + {0,10,20} ns; M=32 (K split): 10 + 3 us + 2*32 ns + 2*{0,10,20} ns
     assert 10.0 <= by[1]["p10_us"] <= by[1]["median_us"] <= by[1]["p90_us"] <= 10.03
-    assert 13.03 <= by[16]["median_us"] <= 13.06
-    assert [k["kernel"].split("<")[0] for k in by[16]["kernels"]] == ["skinny_kernel", "splitk_finalize_kernel"]
-    assert 3.0 <= by[16]["kernels"][1]["median_us"] <= 3.03
+    assert 13.06 <= by[32]["median_us"] <= 13.11
+    assert [k["kernel"].split("<")[0] for k in by[32]["kernels"]] == ["skinny_kernel", "splitk_finalize_kernel"]
+    assert 3.03 <= by[32]["kernels"][1]["median_us"] <= 3.06
 
 
 def test_kernel_stats_reads_counter_collections(tmp_path):
