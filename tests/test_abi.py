@@ -45,6 +45,9 @@ def test_descriptor_validation():
     assert status_of(hq.hq_desc_validate, hq.desc_w4a16(1024, 1000)) == hq.HQ_ERR_UNSUPPORTED       # K % G
     assert status_of(hq.hq_desc_validate, hq.desc_w4a16(1024, 1024, group_size=64)) == hq.HQ_ERR_UNSUPPORTED
     assert status_of(hq.hq_desc_validate, hq.desc_w4a16(0, 1024)) == hq.HQ_ERR_INVALID_ARG
+    # N up to 2^21 (a 256-row output tile is addressed through one 32-bit buffer range)
+    assert status_of(hq.hq_desc_validate, hq.desc_w4a16(1 << 21, 1024)) == hq.HQ_OK
+    assert status_of(hq.hq_desc_validate, hq.desc_w4a16((1 << 21) + 1, 1024)) == hq.HQ_ERR_INVALID_ARG
     r = hq.desc_w4a16(64, 128)
     r.reserved = 3
     assert status_of(hq.hq_desc_validate, r) == hq.HQ_ERR_INVALID_ARG
