@@ -60,6 +60,8 @@ def lib():
         L.hq_oracle_quant_act_e4m3.argtypes = [i64, i64, p, p, p]
         L.hq_oracle_gemm_wna16.restype = C.c_int
         L.hq_oracle_gemm_wna16.argtypes = [i64, i64, i64, i64, C.c_int, p, C.c_int, p, p, p, p, i64, p]
+        L.hq_oracle_gemm_wnlow.restype = C.c_int
+        L.hq_oracle_gemm_wnlow.argtypes = [i64, i64, i64, i64, C.c_int, C.c_int, C.c_int, p, p, p, p, p, i64, p]
         L.hq_oracle_gemm_w4a8_mxfp4.restype = C.c_int
         L.hq_oracle_gemm_w4a8_mxfp4.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
         L.hq_oracle_e2m1_encode.restype = C.c_uint
@@ -191,6 +193,21 @@ def gemm_wna16(A, q, s, z=None, *, N, K, G, a_bf16: bool, w_signed: bool, rows=N
                                     _ptr(_c(s, np.uint16)), _ptr(_c(z, np.uint32)), _ptr(r), R, _ptr(out))
     if rc:
         raise ValueError(f"oracle gemm_wna16 failed ({rc})")
+    return out
+
+
+def gemm_wnlow(A, codes, s, z=None, *, N, K, G, bits: int, a_bf16: bool, w_signed: bool, rows=None):
+    """Low-bit WnA16 (1, 2 or 3-bit codes, one per byte [K][N]; signed, or unsigned
+    with UINT4-container zero-points), fp64."""
+    A = _c(A, np.uint16)
+    M = A.shape[0]
+    r, R = _rows(rows, M)
+    out = np.empty((R, N), dtype=np.float64)
+    rc = lib().hq_oracle_gemm_wnlow(M, N, K, G, int(a_bf16), int(bits), int(w_signed), _ptr(A),
+                                    _ptr(_c(codes, np.int8)), _ptr(_c(s, np.uint16)), _ptr(_c(z, np.uint32)),
+                                    _ptr(r), R, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle gemm_wnlow failed ({rc})")
     return out
 
 

@@ -257,3 +257,25 @@ def moe_mxfp4(seed, T, E, top_k, N, K, cfg=C5, experts=None):
         ids=zipf_topk(seed, cfg, T, E, top_k),
         q=q, e=ex,
     )
+
+
+C11 = 11  # low-bit WnA16 (1, 2 or 3-bit codes)
+
+
+def wnlow(seed, M, N, K, bits, signed, G=128, dtype=torch.float16, cfg=C11):
+    """Low-bit WnA16: one code per byte [K][N], uniform over the width (two's
+    complement for signed widths, 0 .. 2^bits - 1 otherwise); 16-bit group scales
+    |N(0, 0.02)| + 1e-3 (wider steps for narrower codes do not change the test's
+    character); unsigned widths take UINT4-container zero-points uniform in
+    [0, 2^bits - 1]."""
+    lo, hi = (-(1 << (bits - 1)), (1 << (bits - 1)) - 1) if signed else (0, (1 << bits) - 1)
+    codes = _rng(seed, cfg, T_Q, bits).integers(lo, hi + 1, size=(K, N), dtype=np.int64).astype(np.int8)
+    out = dict(A=activations(seed, cfg, M, K, dtype), codes=codes,
+               s=abs_normal_scales(seed, cfg, T_S, (K // G, N), 0.02, 1e-3, dtype))
+    if not signed:
+        zn = _rng(seed, cfg, T_Z, bits).integers(0, 1 << bits, size=(K // G, (N + 7) // 8 * 8), dtype=np.int64)
+        words = np.zeros((K // G, (N + 7) // 8), dtype=np.uint32)
+        for i in range(8):
+            words |= (zn[:, i::8].astype(np.uint32) << np.uint32(4 * i))
+        out["z"] = words
+    return out

@@ -792,3 +792,63 @@ def test_fp8w_a16_exact_rational():
             acc = sum(Fraction(float(a[m, k])) * Fraction(float(E4M3_LUT[d["w"][k, n]])) for k in range(K))
             acc *= Fraction(float(d["s_w"][n]))
             assert abs(got[m, n] - float(acc)) <= 1e-13 * max(abs(float(acc)), 1e-30)
+
+
+# ---- low-bit WnA16 (1, 2, 3-bit codes): "Humming wird angekuendigt", section WnA16 ----
+
+def _pack_k_nibbles(codes):
+    """One code per byte [K][N] -> the W4A16 4-bit container uint32 [K/8][N] (two's-complement nibbles)."""
+    K, N = codes.shape
+    nib = (codes.astype(np.int64) & 15).astype(np.uint32)
+    q = np.zeros((K // 8, N), np.uint32)
+    for i in range(8):
+        q |= nib[i::8] << np.uint32(4 * i)
+    return q
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+@pytest.mark.parametrize("signed", [True, False])
+def test_wnlow_equals_w4a16_on_the_same_codes(bits, signed):
+    """A b-bit code is a 4-bit code of the same value: the low-bit oracle equals the
+    (separately pinned) W4A16 oracle fed the codes in 4-bit containers, with the same
+    zero-points (unsigned) or none (signed, two's complement)."""
+    M, N, K, G = 4, 24, 512, 128
+    d = syn.wnlow(bits, M, N, K, bits, signed)
+    for bf in (False, True):
+        A = d["A"]
+        got = oracle.gemm_wnlow(A, d["codes"], d["s"], d.get("z"), N=N, K=K, G=G, bits=bits, a_bf16=bf, w_signed=signed)
+        ref = oracle.gemm_wna16(A, _pack_k_nibbles(d["codes"]), d["s"], d.get("z"), N=N, K=K, G=G, a_bf16=bf,
+                                w_signed=signed)
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_wnlow_exact_rationals():
+    """Hand-computable cases against all-ones fp16 activations over one 128-K group:
+    INT2 code -2 (the most negative) under scale 0.5, UINT3 code 7 with zero-point 5
+    under 0.25 (and code 0 with the same zero-point), INT1 code -1 under 2.0."""
+    K, G = 128, 128
+    one16 = np.full((1, K), 0x3C00, np.uint16)  # fp16 1.0
+    # bits, signed, (code col 0, code col 1), zero-point, fp16 scale bits, expected (col 0, col 1)
+    cases = ((2, True, (-2, 0), 0, 0x3800, (-128.0, 0.0)),
+             (3, False, (7, 0), 5, 0x3400, (64.0, -160.0)),
+             (1, True, (-1, 0), 0, 0x4000, (-256.0, 0.0)))
+    for bits, signed, (c0, c1), zero, scale, want in cases:
+        codes = np.empty((K, 2), np.int8)
+        codes[:, 0], codes[:, 1] = c0, c1
+        s = np.full((1, 2), scale, np.uint16)
+        z = None if signed else np.array([[zero | (zero << 4)]], np.uint32)
+        got = oracle.gemm_wnlow(one16, codes, s, z, N=2, K=K, G=G, bits=bits, a_bf16=False, w_signed=signed)
+        assert tuple(got[0]) == want, (bits, signed, got[0], want)
+
+
+def test_wnlow_rejects_codes_outside_the_width():
+    codes = np.zeros((128, 16), np.int8)
+    codes[5, 3] = 2          # INT2 holds -2 .. 1
+    A = np.full((1, 128), 0x3C00, np.uint16)
+    s = np.full((1, 16), 0x3C00, np.uint16)
+    with pytest.raises(ValueError):
+        oracle.gemm_wnlow(A, codes, s, None, N=16, K=128, G=128, bits=2, a_bf16=False, w_signed=True)
+    codes[5, 3] = 8          # UINT3 holds 0 .. 7
+    with pytest.raises(ValueError):
+        oracle.gemm_wnlow(A, codes, s, np.zeros((1, 2), np.uint32), N=16, K=128, G=128, bits=3, a_bf16=False,
+                          w_signed=False)
