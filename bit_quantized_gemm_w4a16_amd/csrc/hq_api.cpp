@@ -40,7 +40,11 @@ thread_local PlanRecorder* g_plan = nullptr;
 PlanRecorder* plan_recorder() { return g_plan; }
 
 void plan_workspace(size_t bytes) {
-    if (g_plan && bytes > g_plan->ws) g_plan->ws = bytes;
+    if (g_plan && g_plan->base + bytes > g_plan->ws) g_plan->ws = g_plan->base + bytes;
+}
+
+void plan_workspace_base(size_t base) {
+    if (g_plan) g_plan->base = base;
 }
 
 void plan_record(const char* fmt, ...) {
@@ -57,6 +61,16 @@ void plan_record(const char* fmt, ...) {
 static hq_status ok() {
     g_err[0] = 0;
     return HQ_OK;
+}
+
+// code width of the low-bit weight dtypes (0 for the others)
+int lowbit_width(int w) {
+    switch (w) {
+        case HQ_DT_INT1: case HQ_DT_UINT1: return 1;
+        case HQ_DT_INT2: case HQ_DT_UINT2: return 2;
+        case HQ_DT_INT3: case HQ_DT_UINT3: return 3;
+        default: return 0;
+    }
 }
 
 hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
@@ -80,6 +94,7 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
     if (d->scale2 != HQ_S2_NONE && d->scale2 != HQ_S2_PER_TENSOR_F32)
         return set_error(HQ_ERR_INVALID_ARG, "bad scale2 kind %d", d->scale2);
     LayerInfo I{};
+    I.bits = 4;
     I.invariant = (d->flags & HQ_FLAG_BATCH_INVARIANT) != 0;
     I.tune_path = tune_path;
     I.tune_splits = tune_splits;
@@ -102,10 +117,13 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 takes no zero-points");
         if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x MXINT4 outputs bf16");
         I.G = 32;
-    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT4 || w == HQ_DT_UINT4)) {
+    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT4 || w == HQ_DT_UINT4 || lowbit_width(w))) {
+        // W4A16, and the low-bit widths on the same kernels (1-3-bit codes widened
+        // to 4-bit ones in registers)
         I.kind = Kind::WNA16;
         I.a_bf16 = a == HQ_DT_BF16;
-        I.zp = w == HQ_DT_UINT4;
+        I.bits = lowbit_width(w) ? lowbit_width(w) : 4;
+        I.zp = w == HQ_DT_UINT4 || w == HQ_DT_UINT1 || w == HQ_DT_UINT2 || w == HQ_DT_UINT3;
         if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 INT4/UINT4 is dense-only");
         if (d->w_scale_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 scale dtype must equal the activation dtype");
         if (d->w_scale_gran != HQ_GRAN_PER_GROUP_K) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 needs per-group scales");
@@ -113,7 +131,7 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
             return set_error(HQ_ERR_UNSUPPORTED, "W4A16 group_size=%d must be a multiple of 128 dividing K=%lld",
                              d->group_size, (long long)d->K);
         if (d->zp_dtype != (I.zp ? HQ_DT_UINT4 : HQ_DT_NONE))
-            return set_error(HQ_ERR_UNSUPPORTED, "zero-points: UINT4 codes need UINT4 zero-points, INT4 codes none");
+            return set_error(HQ_ERR_UNSUPPORTED, "zero-points: unsigned codes need UINT4 zero-points, signed codes none");
         if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 takes no activation scale");
         if (d->out_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 output dtype must equal the activation dtype");
     } else if (w == HQ_DT_FP4_E2M1 && (a == HQ_DT_FP8_E4M3 || a == HQ_DT_FP4_E2M1) && d->a_scale == HQ_ASCALE_MX_E8M0) {
@@ -240,7 +258,7 @@ static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
 // Runs the dense dispatch in planning mode (no HIP call): fills buf (if any)
 // with the launches and returns the workspace they need in *ws.
 static hq_status dense_plan(const LayerInfo& L, int64_t M, char* buf, size_t len, size_t* ws) {
-    PlanRecorder rec{buf, len, 0, 0};
+    PlanRecorder rec{buf, len, 0, 0, 0};
     if (buf) buf[0] = 0;
     if (M == 0) {
         *ws = 0;
@@ -256,6 +274,7 @@ static hq_status dense_plan(const LayerInfo& L, int64_t M, char* buf, size_t len
     a.invariant = L.invariant;
     a.tune_path = L.tune_path;
     a.tune_splits = L.tune_splits;
+    a.wbits = L.bits;
     const hq_status st = dense_launch(L, a);
     g_plan = nullptr;
     if (buf) buf[rec.used < len ? rec.used : len - 1] = 0;
@@ -365,6 +384,17 @@ hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale,
     const bool need_s2 = desc->scale2 != HQ_S2_NONE;
     if (need_s2 && (!scale2 || !s2_out)) return set_error(HQ_ERR_INVALID_ARG, "second-level scale buffers are required");
     if (!need_s2 && (scale2 || s2_out)) return set_error(HQ_ERR_INVALID_ARG, "second-level scale buffers must be NULL");
+    if (L.kind == Kind::WNA16 && L.bits < 4) {
+        // low-bit codes, one per byte: each must lie inside its width
+        const int lo = L.zp ? 0 : -(1 << (L.bits - 1)), hi = L.zp ? (1 << L.bits) - 1 : (1 << (L.bits - 1)) - 1;
+        const int8_t* c = (const int8_t*)w;
+        for (int64_t i = 0; i < L.K * L.N; ++i) {
+            const int v = L.zp ? (int)(uint8_t)c[i] : (int)c[i];
+            if (v < lo || v > hi)
+                return set_error(HQ_ERR_INVALID_ARG, "code %d at k=%lld n=%lld outside the %d-bit width", v,
+                                 (long long)(i / L.N), (long long)(i % L.N), L.bits);
+        }
+    }
     repack_all(L, w, scale, zp, scale2, w_out, s_out, z_out, s2_out);
     return ok();
 }
@@ -424,7 +454,7 @@ hq_status hq_gemm(const hq_layer_desc* desc, int64_t M, const void* A, const voi
     DenseArgs a{M, L.N, L.K, L.Np, (int)L.G, A, mx || blk ? nullptr : (const float*)a_scale,
                 mx ? (const uint8_t*)a_scale : nullptr, blk ? (const float*)a_scale : nullptr,
                 w, s, z, (const float*)s2, D, workspace, ws_bytes, (hipStream_t)stream,
-                L.invariant, L.tune_path, L.tune_splits};
+                L.invariant, L.tune_path, L.tune_splits, L.bits};
     return dense_launch(L, a);
 }
 

@@ -33,6 +33,7 @@ struct LayerInfo {
     bool nv;       // FP4_A16: NVFP4 (E4M3 per 16 K, per-tensor second-level scale), else MXFP4
     bool i4;       // FP4_A16: MXINT4 (two's-complement INT4 codes, E8M0 per 32 K) instead of e2m1
     bool w_fp8;    // W8A16: E4M3 weight codes instead of INT8
+    int bits;      // WNA16: weight code width (4, or 1 / 2 / 3 for the low-bit widths)
     bool invariant;        // HQ_FLAG_BATCH_INVARIANT
     int tune_path, tune_splits;  // HQ_TUNE override (0, 0: the library's choice)
 };

@@ -26,10 +26,12 @@ struct PlanRecorder {
     char* buf;     // launch names (may be null: only the workspace is wanted)
     size_t len, used;
     size_t ws;     // workspace bytes the planned launches need
+    size_t base;   // offset added to the needs noted from here on (a region in front is taken)
 };
 PlanRecorder* plan_recorder();                     // the active recorder of this thread, or null
 void plan_record(const char* fmt, ...);            // appends one launch (no-op without a recorder)
 void plan_workspace(size_t bytes);                 // notes a workspace need (no-op without a recorder)
+void plan_workspace_base(size_t base);             // the following needs start `base` bytes into the workspace
 
 struct DenseArgs {
     int64_t M, N, K, Np;
@@ -50,10 +52,11 @@ struct DenseArgs {
     bool invariant;       // batch-invariant mode: results per row independent of M
     int tune_path;        // 0: library's choice; else a TunePath override
     int tune_splits;      // K slices of the override (0: the planner's)
+    int wbits = 4;        // W4A16 kinds: weight code width (1-3: the low-bit planes)
 };
 
 // W4A16 (INT4 / UINT4+zp; bf16 / fp16 activations)
-hipError_t wna16_launch(const DenseArgs& a, bool bf16, bool zp);
+hipError_t wna16_launch(const DenseArgs& a, bool bf16, bool zp);  // also the 1-3-bit widths (a.wbits)
 
 // W4A8-MXFP4 and W8A8-INT8 (split-K workspace for mid M)
 hipError_t w4a8_launch(const DenseArgs& a);

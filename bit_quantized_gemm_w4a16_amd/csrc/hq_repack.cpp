@@ -48,6 +48,37 @@ void repack_4bit(const LayerInfo& L, const uint32_t* w, uint8_t* out, bool pair_
     }
 }
 
+// Low-bit codes (one per byte, [K][N]) into bit planes that widen in registers to
+// the 4-bit pair-order words: a 2-bit plane [Np/16][K/128][64 lanes][8 B] (widths
+// 2 and 3: the low two bits; sub-step t in 16-bit field t, 2-bit field p holding
+// code 8t + kPairOrder[p] of the lane's 32), then a 1-bit plane [Np/16][K/128][64
+// lanes][4 B] (widths 1 and 3: bit 0, or bit 2; byte t, bit p the same code).
+// Codes keep their two's-complement bits; padding columns hold 0.
+void repack_lowbit(const LayerInfo& L, const int8_t* w, uint8_t* out) {
+    const int64_t N = L.N, K = L.K, nst = L.Np / 16, nc = K / 128;
+    const int b = L.bits;
+    const bool two = b >= 2, one = b != 2;
+    uint16_t* p2 = (uint16_t*)out;
+    uint8_t* p1 = out + (two ? (size_t)(nst * nc * 512) : 0);
+    for (int64_t st = 0; st < nst; ++st)
+        for (int64_t c = 0; c < nc; ++c)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int64_t n = st * 16 + (lane & 15);
+                for (int t = 0; t < 4; ++t) {
+                    uint32_t f2 = 0, f1 = 0;
+                    for (int p = 0; p < 8; ++p) {
+                        const int64_t k = c * 128 + 32 * (lane >> 4) + 8 * t + kPairOrder[p];
+                        const uint32_t code = n < N ? (uint32_t)(uint8_t)w[k * N + n] : 0u;
+                        f2 |= (code & 3u) << (2 * p);
+                        f1 |= ((b == 1 ? code : code >> 2) & 1u) << p;
+                    }
+                    const int64_t slot = (st * nc + c) * 64 + lane;
+                    if (two) p2[slot * 4 + t] = (uint16_t)f2;
+                    if (one) p1[slot * 4 + t] = (uint8_t)f1;
+                }
+            }
+}
+
 void repack_int8(const LayerInfo& L, const int8_t* w, int8_t* out) {
     const int64_t N = L.N, K = L.K, nst = L.Np / 16, nc = K / 64;
     for (int64_t e = 0; e < L.E; ++e) {
@@ -162,7 +193,9 @@ void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s
     *w = *s = *z = *s2 = 0;
     switch (L.kind) {
         case Kind::WNA16:
-            *w = E * nst * (size_t)(L.K / 128) * 1024;
+            // 4-bit: 16 B per lane and chunk; low-bit: an 8-B plane (widths 2, 3)
+            // and a 4-B plane (widths 1, 3)
+            *w = E * nst * (size_t)(L.K / 128) * (L.bits == 4 ? 1024 : (L.bits >= 2 ? 512 : 0) + (L.bits != 2 ? 256 : 0));
             *s = E * nst * (size_t)(L.K / L.G) * 16 * 2;
             if (L.zp) *z = E * nst * (size_t)(L.K / L.G) * 8;
             break;
@@ -196,7 +229,8 @@ void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z,
                 void* s_out, void* z_out, void* s2_out) {
     switch (L.kind) {
         case Kind::WNA16:
-            repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, true);
+            if (L.bits < 4) repack_lowbit(L, (const int8_t*)w, (uint8_t*)w_out);
+            else repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, true);
             repack_scale16(L, (const uint16_t*)s, (uint16_t*)s_out, L.a_bf16 ? 0x3F80 : 0x3C00);
             if (L.zp) repack_zero4(L, (const uint32_t*)z, (uint64_t*)z_out);
             break;

@@ -40,6 +40,7 @@ hipError_t launch_all(const DenseArgs& a) {
     s.nc = (int)(a.K / 128);
     s.ngroups = (int)(a.K / a.group_size);
     s.gchunks = a.group_size / 128;
+    s.wbits = a.wbits;
     TileArgs p{};
     p.A = a.A;
     p.W = a.w;

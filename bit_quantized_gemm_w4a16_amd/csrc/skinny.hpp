@@ -87,6 +87,7 @@ struct SkinnyArgs {
     int NS, WS;             // strips per workgroup, wave strip-columns (WK = 4 / WS)
     int a_off, s_off, z_off;  // LDS layout (bytes); MX activation scales share z_off
     int raw_i32;            // W8A8: store the int32 accumulators
+    int wbits;              // W4A16 formats: code width (4, or 1-3 for the low-bit planes)
     int part_nt;            // partial tiles stored non-temporally (set by the launcher)
 };
 
@@ -119,7 +120,7 @@ __device__ __forceinline__ int skinny_swz(int row) {
 // in L2), all at once with the weights; no A slice in LDS, so K need not be
 // split to fit it (M = 9..16 otherwise splits K four ways and adds a finalize
 // launch).
-template <Fmt F, int MT, int SPW, int CPW, int NW>
+template <Fmt F, int MT, int SPW, int CPW, int NW, int WB>
 __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char* lds) {
     using Tr = SkinnyTraits<F>;
     using Acc = typename FmtTraits<F>::Acc;
@@ -128,7 +129,11 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     constexpr int SB = Tr::SB;
     constexpr int AROW = Tr::AROW, UPC = Tr::UPC, NB = Tr::NB;
     constexpr int ROWS = 16 * MT;
-    constexpr int NLOAD = SPW * CPW * NB;  // weight loads per wave and batch
+    // WB < 4 (W4A16 formats): 1-3-bit codes in bit planes, widened to 4-bit words
+    // after the load (a 2-bit plane of 8 B and a 1-bit plane of 4 B per lane and chunk)
+    static_assert(WB == 4 || Tr::WNA16, "low-bit codes: W4A16 formats");
+    constexpr int LPC = WB == 4 ? NB : WB == 3 ? 2 : 1;  // weight loads per chunk and lane
+    constexpr int NLOAD = SPW * CPW * LPC;  // weight loads per wave and batch
     static_assert(NLOAD < 64, "vmcnt counts at most 63 loads");
     constexpr bool ADIR = NW == 8;  // A fragments straight from global memory
     static_assert(NW == 4 || (ADIR && AROW == 256 && MT == 1 && SPW == 1), "direct A: 16-bit A, one m-tile and strip");
@@ -158,19 +163,38 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     const int wlast = cw1 > cw0 ? cw1 - 1 : c0;
     int wstrip[SPW];
     const v4u* wsrc[SPW];
+    const char* wp2[SPW];  // low-bit planes of the strip, at this lane
+    const char* wp1[SPW];
+    const size_t plane2 = WB >= 2 && WB < 4 ? (size_t)nstrips * p.nc * 512 : 0;  // bytes of the 2-bit plane
 #pragma unroll
     for (int sp = 0; sp < SPW; ++sp) {
         wstrip[sp] = strip_base + ws * SPW + sp;
         const int st = wstrip[sp] < nstrips ? wstrip[sp] : nstrips - 1;
         wsrc[sp] = (const v4u*)(Wb + (size_t)st * p.nc * FmtTraits<F>::BSTRIP) + lane;
+        wp2[sp] = Wb + (size_t)st * p.nc * 512 + lane * 8;
+        wp1[sp] = Wb + plane2 + (size_t)st * p.nc * 256 + lane * 4;
     }
     v4u w[CPW][SPW][NB];
     constexpr int CH = CPW / 2;
     auto issue_w = [&](int i) {
 #pragma unroll
-        for (int sp = 0; sp < SPW; ++sp)
+        for (int sp = 0; sp < SPW; ++sp) {
+            const size_t c = (size_t)min(cw0 + i, wlast);
+            if constexpr (WB == 4) {
 #pragma unroll
-            for (int h = 0; h < NB; ++h) w[i][sp][h] = ld_nt(wsrc[sp] + ((size_t)min(cw0 + i, wlast) * NB + h) * 64);
+                for (int h = 0; h < NB; ++h) w[i][sp][h] = ld_nt(wsrc[sp] + (c * NB + h) * 64);
+            } else {
+                // 2-bit plane into words 0-1, 1-bit plane into word 2
+                v4u x = v4u{0u, 0u, 0u, 0u};
+                if constexpr (WB >= 2) {
+                    const v2u a = __builtin_nontemporal_load((const v2u*)(wp2[sp] + c * 512));
+                    x[0] = a[0];
+                    x[1] = a[1];
+                }
+                if constexpr (WB != 2) x[2] = __builtin_nontemporal_load((const uint32_t*)(wp1[sp] + c * 256));
+                w[i][sp][0] = x;
+            }
+        }
         // keep the issue order = the consumption order, so each chunk waits only for its own loads
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -268,7 +292,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     // the LDS copies were issued before the last (CPW - CH) chunks' loads (and,
     // direct A, before the A fragments): once at most that many loads are
     // outstanding, this wave's copies (and its first CH chunks) have landed
-    wait_vmcnt<SPW * (CPW - CH) * NB + (ADIR ? CPW * MT * 4 : 0)>();
+    wait_vmcnt<SPW * (CPW - CH) * LPC + (ADIR ? CPW * MT * 4 : 0)>();
     lds_barrier();
 
     // ---- 3. decode + MFMA ----
@@ -289,6 +313,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     ones.u = v4u{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const bool zsel = p.Z != nullptr;
     const uint32_t wx = zsel ? 0u : 0x88888888u;  // symmetric INT4: two's complement -> offset binary
+    const uint32_t smask = zsel ? 0u : 0xFFFFFFFFu;  // low-bit codes: sign-extend the signed widths
     const uint32_t zmask = zsel ? 15u : 0u, zdef = zsel ? 0u : 8u;  // zero-point, or 8 for symmetric
 
     // WNA16: group of each chunk, relative to the slice's first group
@@ -366,6 +391,9 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     // the zero-point word was read even without zero-points (no branch
                     // around the LDS read: a branch here costs the per-load waits)
                     const uint32_t sbits = sbb[i & 1][sp], zw = zwb[i & 1][sp];
+                    v4u wq;  // this chunk's 4-bit codes (low-bit widths widened)
+                    if constexpr (WB == 4) wq = w[i][sp][0];
+                    else wq = widen_lowbit<WB>(w[i][sp][0], smask);
                     const uint32_t z = ((zw >> (4 * (col & 7))) & zmask) | zdef;
                     if constexpr (BF) {
                         // bf16: operand 128 + u is exact; the group scale and the
@@ -376,7 +404,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                         for (int mt = 0; mt < MT; ++mt) gacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
-                            const Frag8 b = deq4_bf16_offset(w[i][sp][0][t] ^ wx);
+                            const Frag8 b = deq4_bf16_offset(wq[t] ^ wx);
 #pragma unroll
                             for (int mt = 0; mt < MT; ++mt) gacc[mt] = mfma16<true>(af[mt][t], b, gacc[mt]);
                         }
@@ -397,7 +425,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                             for (int mt = 0; mt < MT; ++mt) gacc[q][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
-                            const Frag8 b = deq4_f16_exact(w[i][sp][0][t] ^ wx, nb2, nh2);
+                            const Frag8 b = deq4_f16_exact(wq[t] ^ wx, nb2, nh2);
 #pragma unroll
                             for (int mt = 0; mt < MT; ++mt) gacc[t & 1][mt] = mfma16<false>(af[mt][t], b, gacc[t & 1][mt]);
                         }
@@ -611,10 +639,10 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     else store(std::integral_constant<int, 0>{});
 }
 
-template <Fmt F, int MT, int SPW, int CPW, int NW>
+template <Fmt F, int MT, int SPW, int CPW, int NW, int WB>
 __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char lds[];  // sized per launch (plan.lds_bytes)
-    skinny_item<F, MT, SPW, CPW, NW>(p, blockIdx.y, lds);
+    skinny_item<F, MT, SPW, CPW, NW, WB>(p, blockIdx.y, lds);
 }
 
 // ---- host-side plan ----
@@ -690,7 +718,8 @@ inline int skinny_direct_cpw(int64_t cpk) { return cpk <= 2 ? 2 : cpk <= 4 ? 4 :
 // nstrips / NS times; K slices until the grid covers the chip and the slice
 // fits in LDS.  mode 0: the library's choice; 1: four waves with the A slice in
 // LDS (force_splits K slices, 0 = planned); 2: eight waves with direct A loads.
-inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, int force_splits = 0, int mode = 0) {
+inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, int force_splits = 0, int mode = 0,
+                              int wbits = 4) {
     const int64_t nstrips = Np / 16, nc = K / 128;
     const int gch = G >= 128 ? G / 128 : 1;
     SkinnyPlan p{};
@@ -741,7 +770,8 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
     const int64_t target = a16 && p.NS == 2 ? 512 : 256;
     int64_t S = p.groups_x >= 192 ? 1 : cdiv(target, p.groups_x);
     const int64_t smax = nc / WK > 0 ? nc / WK : 1;
-    const int nb = (F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B || w8a16(F)) ? 2 : 1;  // 16-byte weight loads per chunk
+    // weight loads per chunk (two 16-byte halves; or the two planes of 3-bit codes)
+    const int nb = (F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B || w8a16(F) || wbits == 3) ? 2 : 1;
     const int64_t cap = p.SPW * 16 * nb < 64 ? 16 : 8;  // largest register batch instantiated
     while (S < smax && (skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap)) ++S;
     if (S > smax) S = smax;
@@ -767,22 +797,25 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
     return p;
 }
 
-template <Fmt F, int MT, int SPW, int CPW, int NW = 4>
+template <Fmt F, int MT, int SPW, int CPW, int NW = 4, int WB = 4>
 hipError_t launch_skinny_k(dim3 grid, int lds_bytes, const SkinnyArgs& a, hipStream_t st) {
     if (plan_recorder()) {
         if (NW == 8)
             plan_record("skinny_kernel<%s,%d,%d,%d,direct> grid=%ux%u splits=%d", fmt_name(F), MT, SPW, CPW, grid.x, grid.y, a.splits);
+        else if (WB < 4)
+            plan_record("skinny_kernel<%s,%d,%d,%d,w%d> grid=%ux%u splits=%d", fmt_name(F), MT, SPW, CPW, WB, grid.x, grid.y,
+                        a.splits);
         else
             plan_record("skinny_kernel<%s,%d,%d,%d> grid=%ux%u splits=%d", fmt_name(F), MT, SPW, CPW, grid.x, grid.y, a.splits);
         if (a.splits > 1) plan_workspace((size_t)a.splits * (size_t)a.M * (size_t)a.Np * 4);
         return hipSuccess;
     }
     // allow dynamic LDS beyond the 64 KB default, once per instantiation
-    static const hipError_t attr = hipFuncSetAttribute((const void*)skinny_kernel<F, MT, SPW, CPW, NW>,
+    static const hipError_t attr = hipFuncSetAttribute((const void*)skinny_kernel<F, MT, SPW, CPW, NW, WB>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLds);
     if (attr != hipSuccess) return attr;
     if (lds_bytes < 1024 || lds_bytes > kSkinnyLds) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((skinny_kernel<F, MT, SPW, CPW, NW>), grid, dim3(64 * NW), (size_t)lds_bytes, st, a);
+    hipLaunchKernelGGL((skinny_kernel<F, MT, SPW, CPW, NW, WB>), grid, dim3(64 * NW), (size_t)lds_bytes, st, a);
     return hipGetLastError();
 }
 
@@ -802,18 +835,19 @@ hipError_t launch_skinny_direct(int cpw, dim3 grid, int lds_bytes, const SkinnyA
     }
 }
 
-template <Fmt F, int MT, int SPW>
+template <Fmt F, int MT, int SPW, int WB = 4>
 hipError_t launch_skinny_cpw(int cpw, dim3 grid, int lds_bytes, const SkinnyArgs& a, hipStream_t st) {
+    constexpr int LPC = WB == 4 ? FmtTraits<F>::BSTRIP / 1024 : WB == 3 ? 2 : 1;  // loads per chunk
     switch (cpw) {
-        case 2: return launch_skinny_k<F, MT, SPW, 2>(grid, lds_bytes, a, st);
-        case 4: return launch_skinny_k<F, MT, SPW, 4>(grid, lds_bytes, a, st);
-        case 8: return launch_skinny_k<F, MT, SPW, 8>(grid, lds_bytes, a, st);
+        case 2: return launch_skinny_k<F, MT, SPW, 2, 4, WB>(grid, lds_bytes, a, st);
+        case 4: return launch_skinny_k<F, MT, SPW, 4, 4, WB>(grid, lds_bytes, a, st);
+        case 8: return launch_skinny_k<F, MT, SPW, 8, 4, WB>(grid, lds_bytes, a, st);
         case 14:
-            if constexpr (SPW == 1) return launch_skinny_k<F, MT, SPW, 14>(grid, lds_bytes, a, st);
+            if constexpr (SPW == 1) return launch_skinny_k<F, MT, SPW, 14, 4, WB>(grid, lds_bytes, a, st);
             else return hipErrorInvalidValue;
         default:
-            if constexpr (SPW * 16 * FmtTraits<F>::BSTRIP / 1024 < 64) return launch_skinny_k<F, MT, SPW, 16>(grid, lds_bytes, a, st);
-            else return launch_skinny_k<F, MT, SPW, 8>(grid, lds_bytes, a, st);
+            if constexpr (SPW * 16 * LPC < 64) return launch_skinny_k<F, MT, SPW, 16, 4, WB>(grid, lds_bytes, a, st);
+            else return launch_skinny_k<F, MT, SPW, 8, 4, WB>(grid, lds_bytes, a, st);
     }
 }
 
@@ -832,17 +866,67 @@ hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t s
     const dim3 grid((unsigned)pl.groups_x, (unsigned)pl.splits);
     if (pl.cpk > pl.CPW) return hipErrorInvalidValue;  // K-part beyond one register batch (planned out)
     if (pl.NW == 8) return pl.splits == 1 ? launch_skinny_direct<F>(pl.CPW, grid, pl.lds_bytes, s, st) : hipErrorInvalidValue;
+    auto by_shape = [&](auto wbc) -> hipError_t {
+        constexpr int WB = decltype(wbc)::value;
+        if (pl.SPW == 2) return launch_skinny_cpw<F, 4, 2, WB>(pl.CPW, grid, pl.lds_bytes, s, st);
+        if (pl.MT == 1) return launch_skinny_cpw<F, 1, 1, WB>(pl.CPW, grid, pl.lds_bytes, s, st);
+        if (pl.MT == 2) return launch_skinny_cpw<F, 2, 1, WB>(pl.CPW, grid, pl.lds_bytes, s, st);
+        return launch_skinny_cpw<F, 4, 1, WB>(pl.CPW, grid, pl.lds_bytes, s, st);
+    };
     hipError_t e;
-    if (pl.SPW == 2) e = launch_skinny_cpw<F, 4, 2>(pl.CPW, grid, pl.lds_bytes, s, st);
-    else if (pl.MT == 1) e = launch_skinny_cpw<F, 1, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
-    else if (pl.MT == 2) e = launch_skinny_cpw<F, 2, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
-    else e = launch_skinny_cpw<F, 4, 1>(pl.CPW, grid, pl.lds_bytes, s, st);
+    if constexpr (F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16) {
+        switch (s.wbits) {
+            case 1: e = by_shape(std::integral_constant<int, 1>{}); break;
+            case 2: e = by_shape(std::integral_constant<int, 2>{}); break;
+            case 3: e = by_shape(std::integral_constant<int, 3>{}); break;
+            default: e = by_shape(std::integral_constant<int, 4>{}); break;
+        }
+    } else {
+        e = by_shape(std::integral_constant<int, 4>{});
+    }
     if (e != hipSuccess || pl.splits == 1) return e;
     return launch_finalize<F>(FinalizeArgs{s.part, s.D, s.a_scale, (const float*)s.S, s.s2, s.M, s.N, s.Np, s.splits, s.raw_i32,
                                            s.part_nt},
                               st);
 }
 
+
+// Low-bit planes -> the 4-bit W4A16 layout (one 16-byte word set per strip,
+// chunk and lane), for the tiled kernels.
+template <int WB>
+__global__ __launch_bounds__(256) void widen_lowbit_kernel(const char* __restrict__ planes, v4u* __restrict__ out,
+                                                           int64_t slots, uint32_t smask) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // slot = (strip * chunks + chunk) * 64 + lane
+    if (i >= slots) return;
+    const size_t plane2 = WB >= 2 ? (size_t)slots * 8 : 0;
+    v4u x = v4u{0u, 0u, 0u, 0u};
+    if constexpr (WB >= 2) {
+        const v2u a = __builtin_nontemporal_load((const v2u*)(planes + i * 8));
+        x[0] = a[0];
+        x[1] = a[1];
+    }
+    if constexpr (WB != 2) x[2] = __builtin_nontemporal_load((const uint32_t*)(planes + plane2 + i * 4));
+    out[i] = widen_lowbit<WB>(x, smask);
+}
+
+inline hipError_t launch_widen_lowbit(const void* planes, void* out, int wbits, bool is_signed, int64_t Np, int64_t K,
+                                      hipStream_t st) {
+    const int64_t slots = (Np / 16) * (K / 128) * 64, blocks = (slots + 255) / 256;
+    if (plan_recorder()) {
+        plan_record("widen_lowbit_kernel<%d> grid=%lld", wbits, (long long)blocks);
+        return hipSuccess;
+    }
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const uint32_t smask = is_signed ? 0xFFFFFFFFu : 0u;
+    const dim3 g((unsigned)blocks), b(256);
+    switch (wbits) {
+        case 1: hipLaunchKernelGGL(widen_lowbit_kernel<1>, g, b, 0, st, (const char*)planes, (v4u*)out, slots, smask); break;
+        case 2: hipLaunchKernelGGL(widen_lowbit_kernel<2>, g, b, 0, st, (const char*)planes, (v4u*)out, slots, smask); break;
+        case 3: hipLaunchKernelGGL(widen_lowbit_kernel<3>, g, b, 0, st, (const char*)planes, (v4u*)out, slots, smask); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 // Dense dispatch shared by the format launchers: the small-M weight stream up
 // to kSkinnyMaxM rows, the tiled kernels above; a tuning override (TunePath and
@@ -856,7 +940,9 @@ hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
     if (!a.invariant && !tile_forced && (stream_forced || a.M <= skinny_max_m(F))) {
         if (a.M > kSkinnyMaxM) return hipErrorNotSupported;
         const int mode = a.tune_path == TUNE_STREAM8 ? 2 : a.tune_path == TUNE_STREAM ? 1 : 0;
-        const SkinnyPlan pl = plan_skinny(F, a.M, a.Np, a.K, G, a.tune_splits, mode);
+        if (mode == 2 && a.wbits < 4) return hipErrorNotSupported;  // the direct stream reads 4-bit words only
+        s.wbits = a.wbits;
+        const SkinnyPlan pl = plan_skinny(F, a.M, a.Np, a.K, G, a.tune_splits, mode, a.wbits);
         if (!pl.ok) return hipErrorNotSupported;
         return launch_skinny_dense<F>(pl, s, a.stream);
     }
@@ -867,6 +953,22 @@ hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
         if (pl.splits > a.K / 128) return hipErrorNotSupported;
     }
     if (a.invariant) p.max_splits = 1;
+    if constexpr (F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16) {
+        if (a.wbits < 4) {
+            // low-bit widths on the tiles: the planes widen to the 4-bit layout at the
+            // front of the workspace, the tiles read that, partial tiles follow it
+            const size_t wide = (size_t)(a.Np / 16) * (size_t)(a.K / 128) * 1024, off = (wide + 255) & ~(size_t)255;
+            hipError_t e = launch_widen_lowbit(a.w, a.ws, a.wbits, a.z == nullptr, a.Np, a.K, a.stream);
+            if (e != hipSuccess) return e;
+            plan_workspace(wide);
+            plan_workspace_base(off);
+            p.W = a.ws;
+            p.part = (char*)a.ws + off;
+            e = launch_dense_plan<F>(pl, p, a.stream);
+            plan_workspace_base(0);
+            return e;
+        }
+    }
     return launch_dense_plan<F>(pl, p, a.stream);
 }
 

@@ -201,6 +201,45 @@ __device__ __forceinline__ Frag8 deq4_f16_exact(uint32_t w, uint32_t nb_lo, uint
     return f;
 }
 
+// Low-bit weight codes (widths 1-3) widened to the 4-bit pair-order words of
+// one lane and 128-K chunk (word t = K sub-step t, nibble p = code 8t +
+// {0,2,4,6,1,3,5,7}[p]): the 2-bit plane r[0..1] (16-bit field t) and the 1-bit
+// plane r[2] (byte t; bit 0 for width 1, bit 2 for width 3) spread to nibbles;
+// signed codes (smask all ones) are sign-extended to 4-bit two's complement,
+// unsigned ones (smask 0) stay 0 .. 2^width - 1.
+__device__ __forceinline__ uint32_t spread2(uint32_t v) {  // 8 two-bit fields -> low bits of 8 nibbles
+    v = (v | (v << 8)) & 0x00FF00FFu;
+    v = (v | (v << 4)) & 0x0F0F0F0Fu;
+    return (v | (v << 2)) & 0x33333333u;
+}
+__device__ __forceinline__ uint32_t spread1(uint32_t v) {  // 8 bits -> bit 0 of 8 nibbles
+    v = (v | (v << 12)) & 0x000F000Fu;
+    v = (v | (v << 6)) & 0x03030303u;
+    return (v | (v << 3)) & 0x11111111u;
+}
+template <int WB>
+__device__ __forceinline__ v4u widen_lowbit(const v4u& r, uint32_t smask) {
+    v4u o;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        uint32_t y;
+        if constexpr (WB == 1) {
+            y = spread1((r[2] >> (8 * t)) & 0xFFu);
+            const uint32_t y1 = y << 1;
+            y |= (y1 | (y1 << 1) | (y1 << 2)) & smask;  // -1 -> 0xF
+        } else if constexpr (WB == 2) {
+            y = spread2((r[t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
+            const uint32_t sg = y & 0x22222222u;
+            y |= ((sg << 1) | (sg << 2)) & smask;
+        } else {
+            y = spread2((r[t >> 1] >> (16 * (t & 1))) & 0xFFFFu) | (spread1((r[2] >> (8 * t)) & 0xFFu) << 2);
+            y |= ((y & 0x44444444u) << 1) & smask;
+        }
+        o[t] = y;
+    }
+    return o;
+}
+
 // bf16 128 + u (exact) for eight codes of one pair-ordered word.
 __device__ __forceinline__ Frag8 deq4_bf16_offset(uint32_t w) {
     const uint32_t m = 0x000F000Fu, c = 0x43004300u;

@@ -23,7 +23,8 @@ HQ_ABI_VERSION = 1
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_ALIGNMENT, HQ_ERR_WORKSPACE, HQ_ERR_ABI, HQ_ERR_HIP = range(7)
 # hq_dtype
 (HQ_DT_NONE, HQ_DT_BF16, HQ_DT_FP16, HQ_DT_FP32, HQ_DT_FP8_E4M3, HQ_DT_INT8, HQ_DT_INT4, HQ_DT_UINT4,
- HQ_DT_FP4_E2M1, HQ_DT_E8M0, HQ_DT_INT32) = range(11)
+ HQ_DT_FP4_E2M1, HQ_DT_E8M0, HQ_DT_INT32, HQ_DT_INT1, HQ_DT_UINT1, HQ_DT_INT2, HQ_DT_UINT2, HQ_DT_INT3,
+ HQ_DT_UINT3) = range(17)
 HQ_GRAN_NONE, HQ_GRAN_PER_GROUP_K, HQ_GRAN_PER_CHANNEL, HQ_GRAN_BLOCK_128x128 = range(4)
 HQ_ASCALE_NONE, HQ_ASCALE_PER_TOKEN_F32, HQ_ASCALE_MX_E8M0, HQ_ASCALE_PER_BLOCK128_F32 = range(4)
 HQ_S2_NONE, HQ_S2_PER_TENSOR_F32 = 0, 1
@@ -142,6 +143,15 @@ def desc_w4a16(N, K, group_size=128, bf16=True, zp=False) -> hq_layer_desc:
     a = HQ_DT_BF16 if bf16 else HQ_DT_FP16
     return make_desc(N, K, a, HQ_DT_UINT4 if zp else HQ_DT_INT4, a, HQ_GRAN_PER_GROUP_K, group_size, a,
                      zp_dtype=HQ_DT_UINT4 if zp else HQ_DT_NONE)
+
+
+def desc_wnlow(N, K, bits, signed, group_size=128, bf16=True) -> hq_layer_desc:
+    """Low-bit WnA16: 1-3-bit codes; unsigned widths take UINT4 zero-points."""
+    a = HQ_DT_BF16 if bf16 else HQ_DT_FP16
+    w = {(1, True): HQ_DT_INT1, (1, False): HQ_DT_UINT1, (2, True): HQ_DT_INT2, (2, False): HQ_DT_UINT2,
+         (3, True): HQ_DT_INT3, (3, False): HQ_DT_UINT3}[(bits, signed)]
+    return make_desc(N, K, a, w, a, HQ_GRAN_PER_GROUP_K, group_size, a,
+                     zp_dtype=HQ_DT_NONE if signed else HQ_DT_UINT4)
 
 
 def desc_w4a8_mxfp4(N, K) -> hq_layer_desc:

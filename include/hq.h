@@ -87,7 +87,15 @@ typedef enum hq_dtype {
     HQ_DT_UINT4 = 7,     /* 0..15; with zero-points: value = q - z     */
     HQ_DT_FP4_E2M1 = 8,  /* OCP MX E2M1                                */
     HQ_DT_E8M0 = 9,      /* OCP MX shared scale, 2^(e-127)             */
-    HQ_DT_INT32 = 10
+    HQ_DT_INT32 = 10,
+    /* low-bit weight codes (WnA16): signed widths are two's complement,
+       unsigned ones take 4-bit zero-points; one code per byte on input */
+    HQ_DT_INT1 = 11,     /* -1..0                                      */
+    HQ_DT_UINT1 = 12,    /* 0..1                                       */
+    HQ_DT_INT2 = 13,     /* -2..1                                      */
+    HQ_DT_UINT2 = 14,    /* 0..3                                       */
+    HQ_DT_INT3 = 15,     /* -4..3                                      */
+    HQ_DT_UINT3 = 16     /* 0..7                                       */
 } hq_dtype;
 
 typedef enum hq_scale_gran {
@@ -123,6 +131,8 @@ typedef enum hq_moe_mode {
  *   a_dtype   w_dtype    w_scale (gran, group)         zp      a_scale   out
  *   BF16|FP16 INT4       same as a_dtype, PER_GROUP_K  NONE    NONE      a_dtype
  *   BF16|FP16 UINT4      same as a_dtype, PER_GROUP_K  UINT4   NONE      a_dtype
+ *   BF16|FP16 INT1|INT2|INT3  same as a_dtype, PER_GROUP_K  NONE  NONE  a_dtype (low-bit WnA16)
+ *   BF16|FP16 UINT1|UINT2|UINT3  same, PER_GROUP_K     UINT4   NONE      a_dtype (low-bit WnA16)
  *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    PER_TOKEN BF16
  *   INT8      INT8       FP32, PER_CHANNEL             NONE    PER_TOKEN BF16|INT32
  *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    MX_E8M0   BF16   (MXFP8 x MXFP4)
@@ -228,6 +238,10 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  * Logical inputs (per expert, experts stacked along a leading axis):
  *   w  4-bit codes: uint32 [K/8][N]; code k = 8j+i of column n in bits
  *      4i..4i+3 of word [j][n]            INT8 / FP8_E4M3: one byte [K][N]
+ *      1-3-bit codes (WnA16 "Humming wird angekuendigt", section WnA16): one
+ *      int8 per code [K][N], the two's-complement value for INT1..INT3,
+ *      0 .. 2^b-1 for UINT1..UINT3; a code outside its width is
+ *      HQ_ERR_INVALID_ARG.  Unsigned widths take UINT4 zero-points (below).
  *   scale  [K/group][N] in w_scale_dtype (16-bit raw bits, uint8 for E8M0);
  *          PER_CHANNEL fp32: [N]; BLOCK_128x128 fp32: [K/128][ceil(N/128)]
  *   zp     UINT4: uint32 [K/group][ceil(N/8)]; column n = 8j+i in bits
@@ -243,6 +257,15 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *      natural order (j in nibble j%8); INT4/UINT4 codes are in pair order
  *      (nibble p holds j%8 = {0,2,4,6,1,3,5,7}[p]) so that one shift+mask
  *      yields two consecutive codes in the two 16-bit halves.
+ *      1-3-bit (WnA16): the codes' low two bits and their third (b = 3) or
+ *      only (b = 1) bit in separate planes, each over the 4-bit word order
+ *      above (slot = (strip * K/128 + chunk) * 64 + lane, sub-word t = 0..3,
+ *      code position p = pair order as for INT4):
+ *        2-bit plane (b = 2, 3), first: uint16 [slots][4]; bits 2p..2p+1 of
+ *          sub-word t hold the low two bits of the code at (t, p);
+ *        1-bit plane (b = 1, 3), after it: uint8 [slots][4]; bit p of byte t
+ *          holds bit 0 (b = 1) or bit 2 (b = 3) of the code at (t, p).
+ *      The kernels restore the 4-bit word (sign-extended for INT1..INT3).
  *      INT8 and FP8_E4M3 with 8-bit activations (W8A8, FP8 blockwise):
  *      [Np/16][K/64][64 lanes][16 B]; lane l holds column 16*strip + (l & 15),
  *      k = 64*chunk + 16*(l >> 4) + j, j = 0..15.

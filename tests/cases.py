@@ -82,6 +82,15 @@ W8A16_SMALL = [(M, 272, 1024) for M in (1, 3, 16, 24, 33, 64, 100, 300)] + [(M, 
 W8A16_TILES = [(2000, 4100, 384), (1100, 16000, 256), (700, 4100, 512)]
 W8A16_SWEEP = [(M, C2["N"], C2["K"]) for M in SWEEP]
 
+# ---- low-bit WnA16 (INT1/2/3, UINT1/2/3 + zero-points): (M, N, K, G, bits, signed, bf16) ----
+WNLOW_WIDTHS = [(b, sg) for b in (1, 2, 3) for sg in (True, False)]
+WNLOW_SMALL = [(M, 272, 1024, 128, b, sg, sg) for M in (1, 5, 16, 24, 64) for b, sg in WNLOW_WIDTHS]
+WNLOW_TILES = [(M, N, K, G, b, sg, not sg) for M, N, K, G in ((100, 384, 768, 128), (300, 1000, 512, 256),
+                                                             (2000, 4100, 384, 128)) for b, sg in WNLOW_WIDTHS]
+# the dense W4A16 shape with 3-bit (UINT3 + zero-points, fp16) and 2-bit (INT2, bf16) codes
+WNLOW_SWEEP = [(M, C2["N"], C2["K"], C2["G"], b, sg, bf) for b, sg, bf in ((3, False, False), (2, True, True))
+               for M in SWEEP]
+
 
 def all_dense_cases():
     """(format, M, N, K, G, flags) for every dense GPU case, flags a dict."""
@@ -105,6 +114,8 @@ def all_dense_cases():
             out.append(("fp4a16", M, N, K, 16 if kind == "nvfp4" else 32, dict(kind=kind)))
     for M, N, K in MXINT4_SMALL + MXINT4_TILES + MXINT4_SWEEP:
         out.append(("mxint4", M, N, K, 32, {}))
+    for M, N, K, G, b, sg, bf in WNLOW_SMALL + WNLOW_TILES + WNLOW_SWEEP:
+        out.append(("wnlow", M, N, K, G, dict(bits=b, signed=sg, bf16=bf)))
     for wf in ("w8a16", "fp8w"):
         for dt in ("bf16", "fp16"):
             for M, N, K in W8A16_SMALL + W8A16_TILES + W8A16_SWEEP:

@@ -18,6 +18,8 @@ from bit_quantized_gemm_w4a16_amd import hq
 def desc_of(fmt, N, K, G, flags):
     if fmt == "wna16":
         return hq.desc_w4a16(N, K, G, bf16=flags["bf16"], zp=flags["zp"])
+    if fmt == "wnlow":
+        return hq.desc_wnlow(N, K, flags["bits"], flags["signed"], G, bf16=flags["bf16"])
     if fmt == "w4a8":
         return hq.desc_w4a8_mxfp4(N, K)
     if fmt == "mxa":
@@ -68,6 +70,8 @@ BENCH = {
     "w8a16fp": ("w8a16", 4096, 7168, 7168, dict(bf16=False)),
     "fp8wbf": ("fp8w", 4096, 7168, 7168, dict(bf16=True)),
     "fp8wfp": ("fp8w", 4096, 7168, 7168, dict(bf16=False)),
+    "w3a16": ("wnlow", cases.C2["N"], cases.C2["K"], cases.C2["G"], dict(bits=3, signed=False, bf16=False)),
+    "w2a16": ("wnlow", cases.C2["N"], cases.C2["K"], cases.C2["G"], dict(bits=2, signed=True, bf16=True)),
 }
 
 
