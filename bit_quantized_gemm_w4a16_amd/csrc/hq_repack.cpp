@@ -48,34 +48,38 @@ void repack_4bit(const LayerInfo& L, const uint32_t* w, uint8_t* out, bool pair_
     }
 }
 
-// Low-bit codes (one per byte, [K][N]) into bit planes that widen in registers to
-// the 4-bit pair-order words: a 2-bit plane [Np/16][K/128][64 lanes][8 B] (widths
-// 2 and 3: the low two bits; sub-step t in 16-bit field t, 2-bit field p holding
-// code 8t + kPairOrder[p] of the lane's 32), then a 1-bit plane [Np/16][K/128][64
-// lanes][4 B] (widths 1 and 3: bit 0, or bit 2; byte t, bit p the same code).
-// Codes keep their two's-complement bits; padding columns hold 0.
+// Low-bit codes (one per byte, [K][N]) into bit planes: a 2-bit plane
+// [Np/16][K/128][64 lanes][2 words] (widths 2 and 3: the low two bits), then a
+// 1-bit plane [Np/16][K/128][64 lanes][1 word] (width 1: the bit; width 3: bit
+// 2).  Code j (0..7) of sub-step t (0..3) of the lane's 32 K (k = 128*chunk +
+// 32*(lane >> 4) + 8*t + j) sits at bit 16*(j&1) + 8*(t&1) + 2*(j>>1) of 2-bit
+// word t>>1 and at bit 16*(j&1) + 4*t + (j>>1) of the 1-bit word: the two codes
+// of a pair (2s, 2s+1) share an offset in the two 16-bit halves, as the two
+// 16-bit operands of the kernels' decode.  Codes keep their two's-complement
+// bits; padding columns hold 0.
 void repack_lowbit(const LayerInfo& L, const int8_t* w, uint8_t* out) {
     const int64_t N = L.N, K = L.K, nst = L.Np / 16, nc = K / 128;
     const int b = L.bits;
     const bool two = b >= 2, one = b != 2;
-    uint16_t* p2 = (uint16_t*)out;
-    uint8_t* p1 = out + (two ? (size_t)(nst * nc * 512) : 0);
+    uint32_t* p2 = (uint32_t*)out;
+    uint32_t* p1 = (uint32_t*)(out + (two ? (size_t)(nst * nc * 512) : 0));
     for (int64_t st = 0; st < nst; ++st)
         for (int64_t c = 0; c < nc; ++c)
             for (int lane = 0; lane < 64; ++lane) {
-                const int64_t n = st * 16 + (lane & 15);
-                for (int t = 0; t < 4; ++t) {
-                    uint32_t f2 = 0, f1 = 0;
-                    for (int p = 0; p < 8; ++p) {
-                        const int64_t k = c * 128 + 32 * (lane >> 4) + 8 * t + kPairOrder[p];
+                const int64_t n = st * 16 + (lane & 15), slot = (st * nc + c) * 64 + lane;
+                uint32_t x[2] = {0u, 0u}, y = 0u;
+                for (int t = 0; t < 4; ++t)
+                    for (int j = 0; j < 8; ++j) {
+                        const int64_t k = c * 128 + 32 * (lane >> 4) + 8 * t + j;
                         const uint32_t code = n < N ? (uint32_t)(uint8_t)w[k * N + n] : 0u;
-                        f2 |= (code & 3u) << (2 * p);
-                        f1 |= ((b == 1 ? code : code >> 2) & 1u) << p;
+                        x[t >> 1] |= (code & 3u) << (16 * (j & 1) + 8 * (t & 1) + 2 * (j >> 1));
+                        y |= ((b == 1 ? code : code >> 2) & 1u) << (16 * (j & 1) + 4 * t + (j >> 1));
                     }
-                    const int64_t slot = (st * nc + c) * 64 + lane;
-                    if (two) p2[slot * 4 + t] = (uint16_t)f2;
-                    if (one) p1[slot * 4 + t] = (uint8_t)f1;
+                if (two) {
+                    p2[slot * 2] = x[0];
+                    p2[slot * 2 + 1] = x[1];
                 }
+                if (one) p1[slot] = y;
             }
 }
 

@@ -313,8 +313,11 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     ones.u = v4u{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const bool zsel = p.Z != nullptr;
     const uint32_t wx = zsel ? 0u : 0x88888888u;  // symmetric INT4: two's complement -> offset binary
-    const uint32_t smask = zsel ? 0u : 0xFFFFFFFFu;  // low-bit codes: sign-extend the signed widths
-    const uint32_t zmask = zsel ? 15u : 0u, zdef = zsel ? 0u : 8u;  // zero-point, or 8 for symmetric
+    // low-bit codes: signed ones to offset binary (top bit flipped: the 2-bit
+    // plane's high bits for width 2, the 1-bit plane for widths 1 and 3)
+    const uint32_t lx2 = !zsel && WB == 2 ? 0xAAAAAAAAu : 0u, lx1 = !zsel && WB != 2 ? 0xFFFFFFFFu : 0u;
+    const uint32_t zmask = zsel ? 15u : 0u;  // zero-point, or the offset of the symmetric codes
+    const uint32_t zdef = zsel ? 0u : WB == 4 ? 8u : 1u << (WB - 1);
 
     // WNA16: group of each chunk, relative to the slice's first group
     const int g0 = WNA16 ? c0 / p.gchunks : 0, gslab = WNA16 ? (c1 - 1) / p.gchunks - g0 + 1 : 0;
@@ -391,9 +394,13 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     // the zero-point word was read even without zero-points (no branch
                     // around the LDS read: a branch here costs the per-load waits)
                     const uint32_t sbits = sbb[i & 1][sp], zw = zwb[i & 1][sp];
-                    v4u wq;  // this chunk's 4-bit codes (low-bit widths widened)
-                    if constexpr (WB == 4) wq = w[i][sp][0];
-                    else wq = widen_lowbit<WB>(w[i][sp][0], smask);
+                    // this chunk's codes: 4-bit words, or the low-bit planes in offset binary
+                    v4u wq = w[i][sp][0];
+                    if constexpr (WB < 4) {
+                        wq[0] ^= lx2;
+                        wq[1] ^= lx2;
+                        wq[2] ^= lx1;
+                    }
                     const uint32_t z = ((zw >> (4 * (col & 7))) & zmask) | zdef;
                     if constexpr (BF) {
                         // bf16: operand 128 + u is exact; the group scale and the
@@ -404,7 +411,9 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                         for (int mt = 0; mt < MT; ++mt) gacc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
-                            const Frag8 b = deq4_bf16_offset(wq[t] ^ wx);
+                            Frag8 b;
+                            if constexpr (WB == 4) b = deq4_bf16_offset(wq[t] ^ wx);
+                            else b = deq_low_bf16_offset<WB>(wq, t);
 #pragma unroll
                             for (int mt = 0; mt < MT; ++mt) gacc[mt] = mfma16<true>(af[mt][t], b, gacc[mt]);
                         }
@@ -418,6 +427,8 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                         const float sc = valid ? bits16_to_f32<false>((uint16_t)sbits) : 0.f;
                         const uint32_t nbz = 0xE400u | z, nhz = 0xD400u | (z << 4);  // -(1024 + z), -(64 + z)
                         const uint32_t nb2 = nbz | (nbz << 16), nh2 = nhz | (nhz << 16);
+                        uint32_t nbl[4];  // low-bit widths: -(base_s + z) per pair position
+                        if constexpr (WB < 4) low_f16_offsets<WB>(z, nbl);
                         v4f gacc[2][MT];
 #pragma unroll
                         for (int q = 0; q < 2; ++q)
@@ -425,7 +436,9 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                             for (int mt = 0; mt < MT; ++mt) gacc[q][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
-                            const Frag8 b = deq4_f16_exact(wq[t] ^ wx, nb2, nh2);
+                            Frag8 b;
+                            if constexpr (WB == 4) b = deq4_f16_exact(wq[t] ^ wx, nb2, nh2);
+                            else b = deq_low_f16<WB>(wq, t, nbl);
 #pragma unroll
                             for (int mt = 0; mt < MT; ++mt) gacc[t & 1][mt] = mfma16<false>(af[mt][t], b, gacc[t & 1][mt]);
                         }
@@ -906,7 +919,10 @@ __global__ __launch_bounds__(256) void widen_lowbit_kernel(const char* __restric
         x[1] = a[1];
     }
     if constexpr (WB != 2) x[2] = __builtin_nontemporal_load((const uint32_t*)(planes + plane2 + i * 4));
-    out[i] = widen_lowbit<WB>(x, smask);
+    v4u o;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t] = widen_lowbit_word<WB>(x, t, smask);
+    out[i] = o;
 }
 
 inline hipError_t launch_widen_lowbit(const void* planes, void* out, int wbits, bool is_signed, int64_t Np, int64_t K,

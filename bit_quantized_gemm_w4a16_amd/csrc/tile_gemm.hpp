@@ -164,12 +164,18 @@ __device__ __forceinline__ int swz(int row, int units) {
     return units == 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : units == 8 ? ((row >> 1) & 7) : 0;
 }
 
-// v_and_or_b32 with every operand in a VGPR (a gfx9 VOP3 instruction takes no
-// literal, and the compiler otherwise splits it into an AND and an OR).
+// A value the compiler keeps in a VGPR and cannot fold (an empty asm: no
+// instruction is emitted).
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
+// (a & m) | c as one v_and_or_b32 (or v_bitop3_b32): with the two constants
+// opaque VGPR values the compiler selects the three-operand form (a gfx9 VOP3
+// instruction takes no literal, so with literals it would emit an AND and an
+// OR) and, emitting the instruction itself, keeps its MFMA hazard waits.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
-    return r;
+    return (a & opaque_vgpr(m)) | opaque_vgpr(c);
 }
 
 // fp16 (q - z) * s for eight codes of one pair-ordered word.  A nibble in bits
@@ -201,43 +207,105 @@ __device__ __forceinline__ Frag8 deq4_f16_exact(uint32_t w, uint32_t nb_lo, uint
     return f;
 }
 
-// Low-bit weight codes (widths 1-3) widened to the 4-bit pair-order words of
-// one lane and 128-K chunk (word t = K sub-step t, nibble p = code 8t +
-// {0,2,4,6,1,3,5,7}[p]): the 2-bit plane r[0..1] (16-bit field t) and the 1-bit
-// plane r[2] (byte t; bit 0 for width 1, bit 2 for width 3) spread to nibbles;
-// signed codes (smask all ones) are sign-extended to 4-bit two's complement,
-// unsigned ones (smask 0) stay 0 .. 2^width - 1.
-__device__ __forceinline__ uint32_t spread2(uint32_t v) {  // 8 two-bit fields -> low bits of 8 nibbles
-    v = (v | (v << 8)) & 0x00FF00FFu;
+// Low-bit weight codes (widths 1-3) of one lane and 128-K chunk, as loaded:
+// r[0..1] = the 2-bit plane, r[2] = the 1-bit plane.  Code j (0..7) of K
+// sub-step t (0..3) keeps its low two bits at bit 16*(j&1) + 8*(t&1) + 2*(j>>1)
+// of r[t>>1], and its only bit (width 1) or third bit (width 3) at bit
+// 16*(j&1) + 4*t + (j>>1) of r[2]: the codes 2s and 2s+1 of a sub-step sit at
+// the same offset of the two 16-bit halves, so one and-or lifts the pair.
+//
+// Widening to the 4-bit pair-order word of sub-step t (nibble p = code
+// {0,2,4,6,1,3,5,7}[p]; signed codes, smask all ones, sign-extended to 4-bit
+// two's complement, unsigned ones, smask 0, kept), for the tiled kernels.
+__device__ __forceinline__ uint32_t spread2x4(uint32_t v) {  // 4 two-bit fields per half -> nibbles
+    v &= 0x00FF00FFu;
     v = (v | (v << 4)) & 0x0F0F0F0Fu;
     return (v | (v << 2)) & 0x33333333u;
 }
-__device__ __forceinline__ uint32_t spread1(uint32_t v) {  // 8 bits -> bit 0 of 8 nibbles
-    v = (v | (v << 12)) & 0x000F000Fu;
+__device__ __forceinline__ uint32_t spread1x4(uint32_t v) {  // 4 bits per half -> bit 0 of nibbles
+    v &= 0x000F000Fu;
     v = (v | (v << 6)) & 0x03030303u;
     return (v | (v << 3)) & 0x11111111u;
 }
 template <int WB>
-__device__ __forceinline__ v4u widen_lowbit(const v4u& r, uint32_t smask) {
-    v4u o;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        uint32_t y;
-        if constexpr (WB == 1) {
-            y = spread1((r[2] >> (8 * t)) & 0xFFu);
-            const uint32_t y1 = y << 1;
-            y |= (y1 | (y1 << 1) | (y1 << 2)) & smask;  // -1 -> 0xF
-        } else if constexpr (WB == 2) {
-            y = spread2((r[t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
-            const uint32_t sg = y & 0x22222222u;
-            y |= ((sg << 1) | (sg << 2)) & smask;
-        } else {
-            y = spread2((r[t >> 1] >> (16 * (t & 1))) & 0xFFFFu) | (spread1((r[2] >> (8 * t)) & 0xFFu) << 2);
-            y |= ((y & 0x44444444u) << 1) & smask;
-        }
-        o[t] = y;
+__device__ __forceinline__ uint32_t widen_lowbit_word(const v4u& r, int t, uint32_t smask) {
+    uint32_t y;
+    if constexpr (WB == 1) {
+        y = spread1x4(r[2] >> (4 * t));
+        y |= ((y << 1) | (y << 2) | (y << 3)) & smask;  // -1 -> 0xF
+    } else if constexpr (WB == 2) {
+        y = spread2x4(r[t >> 1] >> (8 * (t & 1)));
+        const uint32_t sg = y & 0x22222222u;
+        y |= ((sg << 1) | (sg << 2)) & smask;
+    } else {
+        y = spread2x4(r[t >> 1] >> (8 * (t & 1))) | (spread1x4(r[2] >> (4 * t)) << 2);
+        y |= ((y & 0x44444444u) << 1) & smask;
     }
-    return o;
+    return y;
+}
+
+// Low-bit fp16 operands, exact: pair s of sub-step t as base_s + u (the field
+// at its own bit offset under an fp16 exponent whose unit is that offset's
+// weight), plus nb[s] = -(base_s + z).  r is in offset binary (signed codes
+// with their top bit flipped, z = 2^(width-1)).  base_s = 1024 >> 2s for the
+// 2-bit plane (and width 3), 1024 >> s for width 1.
+template <int WB>
+__device__ __forceinline__ Frag8 deq_low_f16(const v4u& r, int t, const uint32_t (&nb)[4]) {
+    Frag8 f;
+    if constexpr (WB == 1) {
+        const uint32_t y = r[2] >> (4 * t);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            f.u[s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, and_or(y, 0x00010001u << s, (0x6400u - 0x400u * s) * 0x10001u)) +
+                                                      __builtin_bit_cast(v2h, nb[s]));
+    } else {
+        const uint32_t x = r[t >> 1] >> (8 * (t & 1));
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint32_t c = (0x6400u - 0x800u * s) * 0x10001u;  // 1024, 256, 64, 16
+            if constexpr (WB == 3) {
+                // the third bit from bit 4t + s of the 1-bit plane up to bit 2s + 2
+                const int sh = s + 2 - 4 * t;
+                const uint32_t y = sh >= 0 ? r[2] << sh : r[2] >> -sh;
+                c = and_or(y, 0x00040004u << (2 * s), c);
+            }
+            f.u[s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, and_or(x, 0x00030003u << (2 * s), c)) +
+                                                      __builtin_bit_cast(v2h, nb[s]));
+        }
+    }
+    return f;
+}
+
+// The nb[] constants of deq_low_f16 for a zero-point (or the signed offset) z.
+template <int WB>
+__device__ __forceinline__ void low_f16_offsets(uint32_t z, uint32_t (&nb)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        // -(base_s + z): the fp16 of -base_s with z in the mantissa at base_s's unit
+        const uint32_t h = WB == 1 ? ((0xE400u - 0x400u * s) | (z << s)) : ((0xE400u - 0x800u * s) | (z << (2 * s)));
+        nb[s] = h * 0x10001u;
+    }
+}
+
+// Low-bit bf16 operands 128 + u (exact; offset binary as above), pair s of sub-step t.
+template <int WB>
+__device__ __forceinline__ Frag8 deq_low_bf16_offset(const v4u& r, int t) {
+    Frag8 f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        if constexpr (WB == 1) {
+            f.u[s] = and_or(r[2] >> (4 * t + s), 0x00010001u, 0x43004300u);
+        } else {
+            uint32_t c = 0x43004300u;
+            if constexpr (WB == 3) {
+                const int sh = 4 * t + s - 2;
+                const uint32_t y = sh >= 0 ? r[2] >> sh : r[2] << -sh;
+                c = and_or(y, 0x00040004u, c);
+            }
+            f.u[s] = and_or(r[t >> 1] >> (8 * (t & 1) + 2 * s), 0x00030003u, c);
+        }
+    }
+    return f;
 }
 
 // bf16 128 + u (exact) for eight codes of one pair-ordered word.

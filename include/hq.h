@@ -258,14 +258,14 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *      (nibble p holds j%8 = {0,2,4,6,1,3,5,7}[p]) so that one shift+mask
  *      yields two consecutive codes in the two 16-bit halves.
  *      1-3-bit (WnA16): the codes' low two bits and their third (b = 3) or
- *      only (b = 1) bit in separate planes, each over the 4-bit word order
- *      above (slot = (strip * K/128 + chunk) * 64 + lane, sub-word t = 0..3,
- *      code position p = pair order as for INT4):
- *        2-bit plane (b = 2, 3), first: uint16 [slots][4]; bits 2p..2p+1 of
- *          sub-word t hold the low two bits of the code at (t, p);
- *        1-bit plane (b = 1, 3), after it: uint8 [slots][4]; bit p of byte t
- *          holds bit 0 (b = 1) or bit 2 (b = 3) of the code at (t, p).
- *      The kernels restore the 4-bit word (sign-extended for INT1..INT3).
+ *      only (b = 1) bit in separate planes.  Per slot = (strip * K/128 +
+ *      chunk) * 64 + lane, code j = 0..7 of sub-step t = 0..3 is the code at
+ *      k = 128*chunk + 32*(l >> 4) + 8*t + j of column 16*strip + (l & 15):
+ *        2-bit plane (b = 2, 3), first: uint32 [slots][2]; bits
+ *          16*(j&1) + 8*(t&1) + 2*(j>>1) .. +1 of word t>>1 hold its low two bits;
+ *        1-bit plane (b = 1, 3), after it: uint32 [slots]; bit
+ *          16*(j&1) + 4*t + (j>>1) holds its bit 0 (b = 1) or bit 2 (b = 3).
+ *      Codes 2s and 2s+1 thus share an offset in the two 16-bit halves.
  *      INT8 and FP8_E4M3 with 8-bit activations (W8A8, FP8 blockwise):
  *      [Np/16][K/64][64 lanes][16 B]; lane l holds column 16*strip + (l & 15),
  *      k = 64*chunk + 16*(l >> 4) + j, j = 0..15.

@@ -25,25 +25,38 @@ def nibble_words(codes, K, N):
     return q
 
 
-def planes_to_words(wp, bits, signed, Np, K):
-    """Decode the packed planes into the packed 4-bit words [slots][4] (uint32)."""
+def planes_to_codes(wp, bits, signed, Np, K):
+    """Decode the packed planes into the codes [slots][4 sub-steps][8] (int),
+    from the bit positions hq.h states."""
     slots = (Np // 16) * (K // 128) * 64
     two, one = bits >= 2, bits != 2
     off = slots * 8 if two else 0
     assert wp.size == (slots * 8 if two else 0) + (slots * 4 if one else 0)
-    p2 = wp[:off].view(np.uint16).reshape(slots, 4).astype(np.uint32) if two else None
-    p1 = wp[off:].reshape(slots, 4).astype(np.uint32) if one else None
-    out = np.zeros((slots, 4), dtype=np.uint32)
-    for p in range(8):
-        if bits == 1:
-            v = (p1 >> p) & 1
-        elif bits == 2:
-            v = (p2 >> (2 * p)) & 3
-        else:
-            v = ((p2 >> (2 * p)) & 3) | (((p1 >> p) & 1) << 2)
-        if signed:   # two's complement of the width, as a 4-bit nibble
-            v = np.where(v >> (bits - 1) & 1, v | (15 ^ ((1 << bits) - 1)), v)
-        out |= v << np.uint32(4 * p)
+    x = wp[:off].view(np.uint32).reshape(slots, 2).astype(np.int64) if two else None
+    y = wp[off:].view(np.uint32).reshape(slots).astype(np.int64) if one else None
+    out = np.zeros((slots, 4, 8), dtype=np.int64)
+    for t in range(4):
+        for j in range(8):
+            v = 0
+            if two:
+                v = (x[:, t >> 1] >> (16 * (j & 1) + 8 * (t & 1) + 2 * (j >> 1))) & 3
+            if one:
+                bit = (y >> (16 * (j & 1) + 4 * t + (j >> 1))) & 1
+                v = v | (bit << (0 if bits == 1 else 2))
+            if signed:
+                v = np.where(v >> (bits - 1) & 1, v - (1 << bits), v)
+            out[:, t, j] = v
+    return out
+
+
+def codes_of_4bit_words(w4, signed, Np, K):
+    """The packed 4-bit pair-order words [slots][4] -> codes [slots][4][8]."""
+    slots = (Np // 16) * (K // 128) * 64
+    words = w4.view(np.uint32).reshape(slots, 4).astype(np.int64)
+    out = np.zeros((slots, 4, 8), dtype=np.int64)
+    for p, j in enumerate((0, 2, 4, 6, 1, 3, 5, 7)):
+        v = (words >> (4 * p)) & 15
+        out[:, :, j] = np.where(v >= 8, v - 16, v) if signed else v
     return out
 
 
@@ -78,7 +91,7 @@ def test_planes_decode_to_the_4bit_layout_of_the_same_codes(bits, signed, N, K, 
     wp, sp, zp = hq.hq_repack(desc, d["codes"], d["s"], d.get("z"))
     d4 = hq.desc_w4a16(N, K, G, bf16=False, zp=not signed)
     w4, s4, z4 = hq.hq_repack(d4, nibble_words(d["codes"], K, N), d["s"], d.get("z"))
-    np.testing.assert_array_equal(planes_to_words(wp, bits, signed, Np, K), w4.view(np.uint32).reshape(slots, 4))
+    np.testing.assert_array_equal(planes_to_codes(wp, bits, signed, Np, K), codes_of_4bit_words(w4, signed, Np, K))
     np.testing.assert_array_equal(sp, s4)
     if signed:
         assert zp is None and zb == 0
@@ -87,24 +100,30 @@ def test_planes_decode_to_the_4bit_layout_of_the_same_codes(bits, signed, N, K, 
 
 
 def test_plane_hand_walkthrough_3bit():
-    """16 columns x 128 K of UINT3, code(k, n) = (k + n) % 8: lane 0 sub-word 0
-    holds k = 0..7 of column 0 in pair order {0,2,4,6,1,3,5,7}: codes 0,2,4,6,
-    1,3,5,7; low two bits 0,2,0,2,1,3,1,3 -> 0b11011101_10001000 = 0xDD88; third
-    bits 0,0,1,1,0,0,1,1 -> 0b11001100 = 0xCC."""
+    """16 columns x 128 K of UINT3, code(k, n) = (k + n) % 8.  Lane 0 (column 0,
+    k = 0..31): sub-step 0 holds codes 0..7, sub-step 1 codes 0..7 again.  2-bit
+    word 0: evens j = 0,2,4,6 of t = 0 (low bits 0,2,0,2) in bits 0-7, the same
+    for t = 1 in bits 8-15, odds j = 1,3,5,7 (low bits 1,3,1,3) in bits 16-23 and
+    24-31: bytes 0x88, 0x88, 0xDD, 0xDD.  1-bit word: bit 2 of the evens (codes
+    0,2,4,6 -> 0,0,1,1) at bits 4t + 0..3 = 0b1100 per t, of the odds (1,3,5,7
+    -> 0,0,1,1) at 16 + 4t + 0..3: 0xCCCC in each half."""
     N, K = 16, 128
     codes = ((np.arange(K)[:, None] + np.arange(N)[None, :]) % 8).astype(np.int8)
     s = np.full((1, N), 0x3C00, dtype=np.uint16)
     z = np.zeros((1, 2), dtype=np.uint32)
     wp, _, _ = hq.hq_repack(hq.desc_wnlow(N, K, 3, False, bf16=False), codes, s, z)
-    p2 = wp[:64 * 8].view(np.uint16).reshape(64, 4)
-    p1 = wp[64 * 8:].reshape(64, 4)
-    assert p2[0, 0] == 0xDD88 and p1[0, 0] == 0xCC
-    # lane 17: column 1, k = 32..39 -> codes 1..7,0 ; pair order -> 1,3,5,7,2,4,6,0
-    # low bits 1,3,1,3,2,0,2,0 -> fields (p0..p7) ; third bits 0,0,1,1,0,1,1,0
-    lo = [1, 3, 1, 3, 2, 0, 2, 0]
-    hi = [0, 0, 1, 1, 0, 1, 1, 0]
-    assert p2[17, 0] == sum(v << (2 * p) for p, v in enumerate(lo))
-    assert p1[17, 0] == sum(v << p for p, v in enumerate(hi))
+    x = wp[:64 * 8].view(np.uint32).reshape(64, 2)
+    y = wp[64 * 8:].view(np.uint32)
+    assert x[0, 0] == 0xDDDD8888 and x[0, 1] == 0xDDDD8888 and y[0] == 0xCCCCCCCC
+    # lane 17: column 1, k = 32..63 -> sub-step t holds codes (1 + j) % 8:
+    # evens j=0,2,4,6 -> 1,3,5,7 (low bits 1,3,1,3; bit 2: 0,0,1,1),
+    # odds j=1,3,5,7 -> 2,4,6,0 (low bits 2,0,2,0; bit 2: 0,1,1,0)
+    ev = sum(v << (2 * s) for s, v in enumerate([1, 3, 1, 3]))
+    od = sum(v << (2 * s) for s, v in enumerate([2, 0, 2, 0]))
+    assert x[17, 0] == ev | ev << 8 | od << 16 | od << 24
+    hb_e = sum(v << s for s, v in enumerate([0, 0, 1, 1]))
+    hb_o = sum(v << s for s, v in enumerate([0, 1, 1, 0]))
+    assert y[17] == sum(hb_e << 4 * t | hb_o << (16 + 4 * t) for t in range(4))
 
 
 @pytest.mark.parametrize("bits,signed", WIDTHS)
