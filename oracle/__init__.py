@@ -76,6 +76,10 @@ def lib():
         L.hq_oracle_gemm_fp8_blockwise.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
         L.hq_oracle_gemm_fp4_a16.restype = C.c_int
         L.hq_oracle_gemm_fp4_a16.argtypes = [i64, i64, i64, C.c_int, p, p, C.c_int, p, p, p, i64, p]
+        L.hq_oracle_fp6.restype = C.c_double
+        L.hq_oracle_fp6.argtypes = [C.c_uint, C.c_int]
+        L.hq_oracle_gemm_mxf_a16.restype = C.c_int
+        L.hq_oracle_gemm_mxf_a16.argtypes = [i64, i64, i64, C.c_int, p, C.c_int, p, p, p, i64, p]
         L.hq_oracle_gemm_fp8w_a16.restype = C.c_int
         L.hq_oracle_gemm_fp8w_a16.argtypes = [i64, i64, i64, C.c_int, p, p, p, p, i64, p]
         L.hq_oracle_gemm_w8a16.restype = C.c_int
@@ -124,6 +128,11 @@ def e8m0(e: int) -> float:
 
 def e4m3(code: int) -> float:
     return lib().hq_oracle_e4m3(code)
+
+
+def fp6(code: int, e3m2: bool) -> float:
+    """OCP MX FP6 decode: E2M3 (e3m2 False) or E3M2 (e3m2 True), 6-bit code."""
+    return lib().hq_oracle_fp6(code, int(e3m2))
 
 
 def e4m3_encode(x: float) -> int:
@@ -291,6 +300,25 @@ def gemm_fp8w_a16(A, w, s_w, *, a_bf16: bool, rows=None):
                                        R, _ptr(out))
     if rc:
         raise ValueError(f"oracle gemm_fp8w_a16 failed ({rc})")
+    return out
+
+
+MXF_ELEMS = {"e4m3": 0, "e2m3": 1, "e3m2": 2}
+
+
+def gemm_mxf_a16(A, codes, e8, *, elem: str, a_bf16: bool = True, rows=None):
+    """MX-scaled float weights (MXFP8 E4M3, MXFP6 E2M3 / E3M2: one code per byte
+    [K][N], E8M0 per 32 K [K/32][N]) with 16-bit activations, fp64."""
+    A = _c(A, np.uint16)
+    codes = _c(codes, np.uint8)
+    M, K = A.shape
+    N = codes.shape[1]
+    r, R = _rows(rows, M)
+    out = np.empty((R, N), dtype=np.float64)
+    rc = lib().hq_oracle_gemm_mxf_a16(M, N, K, int(a_bf16), _ptr(A), MXF_ELEMS[elem], _ptr(codes),
+                                      _ptr(_c(e8, np.uint8)), _ptr(r), R, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle gemm_mxf_a16 failed ({rc})")
     return out
 
 

@@ -69,6 +69,19 @@ double hq_oracle_e4m3(unsigned code)
     return s ? -mag : mag;
 }
 
+/* OCP MX v1.0, FP6: E2M3 (e3m2 = 0: 1 sign, 2 exponent bits with bias 1, 3
+ * mantissa bits) or E3M2 (e3m2 = 1: 3 exponent bits with bias 3, 2 mantissa
+ * bits); exponent field 0 is subnormal, 2^(1-bias) * m / 2^mbits; no
+ * infinities or NaN.  code: the 6 low bits. */
+double hq_oracle_fp6(unsigned code, int e3m2)
+{
+    const int eb = e3m2 ? 3 : 2, mb = e3m2 ? 2 : 3, bias = e3m2 ? 3 : 1;
+    unsigned s = (code >> 5) & 1u, e = (code >> mb) & ((1u << eb) - 1u), m = code & ((1u << mb) - 1u);
+    double frac = (double)m / (double)(1u << mb);
+    double mag = (e == 0) ? ldexp(frac, 1 - bias) : ldexp(1.0 + frac, (int)e - bias);
+    return s ? -mag : mag;
+}
+
 /* Round-to-nearest-even fp32 -> E4M3 with saturation to +-448 (satfinite). */
 unsigned hq_oracle_e4m3_encode(float x)
 {
@@ -521,6 +534,37 @@ int hq_oracle_gemm_fp8w_a16(int64_t M, int64_t N, int64_t K, int a_bf16, const u
         }
         for (int64_t r = 0; r < R; ++r) out[r * N + n] *= (double)s_w[n];
     }
+    free(a);
+    return 0;
+}
+
+/* MX-scaled float weights with 16-bit activations (the WnA16 float widths of
+ * "Humming wird angekuendigt", section WnA16, under the OCP MX v1.0 block
+ * scale): elem 0 = FP8 E4M3 (MXFP8), 1 = FP6 E2M3, 2 = FP6 E3M2 (MXFP6);
+ *   W_real[k][n] = elem(codes[k][n]) * 2^(e8[k/32][n] - 127),  D = A x W_real (fp64).
+ * codes uint8 [K][N] (FP6: the low 6 bits; returns 3 if a higher bit is set),
+ * e8 uint8 [K/32][N], A uint16 [M][K] (bf16 or fp16 bits). */
+int hq_oracle_gemm_mxf_a16(int64_t M, int64_t N, int64_t K, int a_bf16, const uint16_t* A, int elem,
+                           const uint8_t* codes, const uint8_t* e8, const int64_t* rows, int64_t nrows, double* out)
+{
+    if (K % 32 || elem < 0 || elem > 2) return 1;
+    if (elem)
+        for (int64_t i = 0; i < K * N; ++i)
+            if (codes[i] & 0xC0u) return 3;
+    int64_t R = rows ? nrows : M;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(R * K + 1));
+    if (!a) return 2;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k) a[r * K + k] = act16(a_bf16, A[row_of(rows, r) * K + k]);
+    memset(out, 0, sizeof(double) * (size_t)(R * N));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const unsigned c = codes[k * N + n];
+            double w = elem == 0 ? hq_oracle_e4m3(c) : hq_oracle_fp6(c, elem == 2);
+            w *= hq_oracle_e8m0(e8[(k / 32) * N + n]);
+            for (int64_t r = 0; r < R; ++r) out[r * N + n] += a[r * K + k] * w;
+        }
     free(a);
     return 0;
 }

@@ -279,3 +279,18 @@ def wnlow(seed, M, N, K, bits, signed, G=128, dtype=torch.float16, cfg=C11):
             words |= (zn[:, i::8].astype(np.uint32) << np.uint32(4 * i))
         out["z"] = words
     return out
+
+
+C12 = 12  # MX-scaled float weights (MXFP8 E4M3, MXFP6 E2M3 / E3M2) with 16-bit activations
+
+
+def mxf_a16(seed, M, N, K, elem, dtype=torch.bfloat16, cfg=C12):
+    """MX float WnA16: N(0,1) activations rounded to bf16, one code per byte [K][N]
+    (E4M3 uniform over the finite codes; FP6 uniform over all 64 six-bit codes),
+    E8M0 exponents in [118, 127] per 32 K."""
+    if elem == "e4m3":
+        codes = fp8_codes(seed, cfg, T_Q, (K, N))
+    else:
+        codes = _rng(seed, cfg, T_Q, {"e2m3": 1, "e3m2": 2}[elem]).integers(0, 64, size=(K, N)).astype(np.uint8)
+    return dict(A=activations(seed, cfg, M, K, dtype), codes=codes, e=e8m0_exponents(seed, cfg, (K // 32, N)))
+

@@ -852,3 +852,120 @@ def test_wnlow_rejects_codes_outside_the_width():
     with pytest.raises(ValueError):
         oracle.gemm_wnlow(A, codes, s, np.zeros((1, 2), np.uint32), N=16, K=128, G=128, bits=3, a_bf16=False,
                           w_signed=False)
+
+
+# ---- MX-scaled float weights (MXFP8 E4M3, MXFP6 E2M3 / E3M2): "Humming wird
+# angekuendigt", section WnA16 (float weights of any width), OCP MX v1.0 ----
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_matches_ocp_table_and_is_symmetric(fmt):
+    for code, v in golden(f"fp6_{fmt}_ocp_mx_v1.txt"):
+        assert oracle.fp6(code, fmt == "e3m2") == v, (fmt, code)
+        assert oracle.fp6(code | 0x20, fmt == "e3m2") == -v, (fmt, code)
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_subnormals_evenly_spaced_and_codes_monotone(fmt):
+    """The subnormal codes run in equal steps from 0 to the table's largest subnormal
+    (the step is the smallest subnormal); positive codes increase strictly, and every
+    value is an exact E4M3 value (torch's fp8 cast leaves it unchanged)."""
+    tab = dict(golden(f"fp6_{fmt}_ocp_mx_v1.txt"))
+    e3 = fmt == "e3m2"
+    mb = 2 if e3 else 3
+    step = tab[0x01]
+    for m in range(1 << mb):
+        assert oracle.fp6(m, e3) == m * step
+    assert oracle.fp6((1 << mb) - 1, e3) == tab[(1 << mb) - 1]
+    vals = [oracle.fp6(c, e3) for c in range(32)]
+    assert all(b > a for a, b in zip(vals, vals[1:]))
+    t = torch.tensor(vals + [-v for v in vals], dtype=torch.float32)
+    assert torch.equal(t.to(torch.float8_e4m3fn).to(torch.float32), t)
+
+
+def test_fp6_normal_codes_are_e2m1_and_e4m3_codes_with_shifted_fields():
+    """E2M3 s.ee.mm0 is E2M1 s.ee.m (same bias, golden E2M1 table); every normal
+    E2M3 s.ee.mmm is E4M3 s.(ee+6).mmm and every normal E3M2 s.eee.mm is E4M3
+    s.(eee+4).mm0 (the biases differ by 6 and 4; E4M3 pinned by its own table
+    and torch), so sign, exponent, bias and each mantissa bit are tied down."""
+    for s in (0, 1):
+        for e in range(4):
+            for m in range(8):
+                c = (s << 5) | (e << 3) | m
+                v = oracle.fp6(c, False)
+                if m % 4 == 0:
+                    assert v == E2M1_TABLE[(s << 3) | (e << 1) | (m >> 2)] or (v == 0 and m == 0 and e == 0)
+                if e:
+                    assert v == E4M3_LUT[(s << 7) | ((e + 6) << 3) | m]
+        for e in range(1, 8):
+            for m in range(4):
+                assert oracle.fp6((s << 5) | (e << 2) | m, True) == E4M3_LUT[(s << 7) | ((e + 4) << 3) | (m << 1)]
+
+
+def _mxf_exact(A, codes, e8, elem, a_dt):
+    a = torch16(A, a_dt)
+    M, K = A.shape
+    N = codes.shape[1]
+    dec = (lambda c: E4M3_LUT[c]) if elem == "e4m3" else (lambda c: oracle.fp6(int(c), elem == "e3m2"))
+    out = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(a[m, k])) * Fraction(float(dec(codes[k, n]))) * Fraction(2) ** (int(e8[k // 32, n]) - 127)
+            out[m, n] = float(acc)
+    return out
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e2m3", "e3m2"])
+def test_mxf_a16_exact_rational(elem):
+    M, N, K = 2, 8, 64
+    d = syn.mxf_a16(0, M, N, K, elem)
+    got = oracle.gemm_mxf_a16(d["A"], d["codes"], d["e"], elem=elem)
+    want = _mxf_exact(d["A"], d["codes"], d["e"], elem, torch.bfloat16)
+    assert np.all(np.abs(got - want) <= 1e-13 * np.maximum(np.abs(want), 1e-30))
+
+
+def test_mxf_a16_e2m3_on_e2m1_values_equals_mxfp4():
+    """E2M3 codes whose low two mantissa bits are zero carry exactly the E2M1 values:
+    with the same E8M0 blocks the MXFP4 weight-only oracle (another code path, 4-bit
+    words) gives the same result bit for bit."""
+    M, N, K = 5, 24, 256
+    d = syn.w4a16_fp4(3, M, N, K, nvfp4=False)
+    nib = unpack_k(d["q"], K)
+    codes = (((nib >> 3) & 1) << 5 | ((nib >> 1) & 3) << 3 | (nib & 1) << 2).astype(np.uint8)
+    got = oracle.gemm_mxf_a16(d["A"], codes, d["s"], elem="e2m3")
+    ref = oracle.gemm_fp4_a16(d["A"], d["q"], d["s"], N=N, K=K, a_bf16=True, nvfp4=False)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_mxf_a16_e4m3_unit_blocks_equal_fp8_weight_only():
+    """MXFP8 with every E8M0 exponent 127 is FP8 weight-only with unit column scales."""
+    M, N, K = 4, 40, 128
+    d = syn.mxf_a16(1, M, N, K, "e4m3")
+    e = np.full((K // 32, N), 127, np.uint8)
+    for bf in (True, False):
+        A = syn.mxf_a16(1, M, N, K, "e4m3", torch.bfloat16 if bf else torch.float16)["A"]
+        got = oracle.gemm_mxf_a16(A, d["codes"], e, elem="e4m3", a_bf16=bf)
+        ref = oracle.gemm_fp8w_a16(A, d["codes"], np.ones(N, np.float32), a_bf16=bf)
+        np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("elem", ["e2m3", "e3m2"])
+def test_mxf_a16_block_step_and_code_range(elem):
+    """Raising one 32-K block's exponent by one doubles exactly that block's share of
+    that column; a code with bit 6 or 7 set is rejected."""
+    M, N, K = 3, 16, 128
+    d = syn.mxf_a16(2, M, N, K, elem)
+    base = oracle.gemm_mxf_a16(d["A"], d["codes"], d["e"], elem=elem)
+    e2 = d["e"].copy()
+    e2[2, 7] += 1
+    moved = oracle.gemm_mxf_a16(d["A"], d["codes"], e2, elem=elem)
+    cols = [c for c in range(N) if c != 7]
+    np.testing.assert_array_equal(moved[:, cols], base[:, cols])
+    a = torch16(d["A"], torch.bfloat16)
+    w = np.array([oracle.fp6(int(c), elem == "e3m2") for c in d["codes"][64:96, 7]]) * 2.0 ** (int(d["e"][2, 7]) - 127)
+    assert rel_err(moved[:, 7] - base[:, 7], a[:, 64:96] @ w) < 1e-12
+    bad = d["codes"].copy()
+    bad[5, 3] |= 0x40
+    with pytest.raises(ValueError):
+        oracle.gemm_mxf_a16(d["A"], bad, d["e"], elem=elem)
