@@ -638,6 +638,42 @@ class DenseMXINT4A16(DenseFP4A16):
                     sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
 
 
+class DenseMXF(DenseFP4A16):
+    """bf16 activations x MX float weights (MXFP8 E4M3 or MXFP6 E2M3 codes, E8M0 per
+    32 K) at the dense W4A16 layer's shape, N=4096, K=7168."""
+
+    def __init__(self, elem, N=4096, K=7168, Mmax=8192, sweep=SWEEP):
+        self.N, self.K, self.Mmax, self.sweep, self.nv, self.elem = N, K, Mmax, sweep, False, elem
+        self.dtype = "bf16"
+        self.name = f"dense_w{'8' if elem == 'e4m3' else '6'}a16_mx{elem}_bf16_N{N}_K{K}"
+        log(f"[bench] generating {self.name}")
+        d = syn.mxf_a16(0, Mmax, N, K, elem)
+        self.host = d
+        self.desc = hq.desc_mxf_a16(N, K, elem)
+        wp, sp, _ = hq.hq_repack(self.desc, d["codes"], d["e"])
+        self.wbytes = wp.size + sp.size
+        self.copies = _copies((dev(wp), dev(sp), None), self.wbytes)
+        self.A = dev(d["A"])
+        self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in sweep)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def kernel_of(self, M):
+        f = "MXF8_BF16" if self.elem == "e4m3" else "MXF6E2_BF16"
+        if M <= 64:
+            return (f"skinny_kernel<{f}> (M<=64)", "hbm")
+        pre = "" if self.elem == "e4m3" else "widen_fp6_kernel + "
+        return (f"{pre}tile_gemm_kernel<MXF8_BF16> (M>64)", "mfma" if M >= 128 else "hbm")
+
+    def cpu_baseline(self, budget_s=8.0):
+        import oracle
+        d = self.host
+        f = lambda rows: oracle.gemm_mxf_a16(d["A"], d["codes"], d["e"], elem=self.elem, rows=rows)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, self.Mmax)), budget_s)
+        return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(), kind="oracle",
+                    sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
+
+
 class DenseW8A16:
     """8-bit weight-only: bf16 activations x INT8 (or FP8-E4M3) weights with fp32 per-channel
     scales at the dense W4A16 layer's shape, N=4096, K=7168."""
@@ -704,10 +740,12 @@ WORKLOADS = {
     "fp8w": lambda: DenseW8A16(fp8=True),
     "w3a16": lambda: DenseWnLow(3, False),
     "w2a16": lambda: DenseWnLow(2, True),
+    "mxfp8a16": lambda: DenseMXF("e4m3"),
+    "mxfp6a16": lambda: DenseMXF("e2m3"),
 }
 # the workloads the default run measures besides the headline one (c2)
 DEFAULT_EXTRA = ["c3", "c4", "c5", "w4a4", "w4a8mx", "fp8b", "mxfp4a16", "nvfp4a16", "mxint4a16", "w8a16", "fp8w",
-                 "w3a16", "w2a16"]
+                 "w3a16", "w2a16", "mxfp8a16", "mxfp6a16"]
 
 
 # ---------------------------------------------------------------------------
@@ -1085,6 +1123,8 @@ _DRY = {
     "fp8w": lambda: hq.desc_fp8w_a16(4096, 7168, bf16=True),
     "w3a16": lambda: hq.desc_wnlow(4096, 7168, 3, False, 128, bf16=False),
     "w2a16": lambda: hq.desc_wnlow(4096, 7168, 2, True, 128, bf16=True),
+    "mxfp8a16": lambda: hq.desc_mxf_a16(4096, 7168, "e4m3"),
+    "mxfp6a16": lambda: hq.desc_mxf_a16(4096, 7168, "e2m3"),
 }
 
 

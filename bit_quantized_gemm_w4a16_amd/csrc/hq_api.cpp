@@ -200,6 +200,20 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
             return set_error(HQ_ERR_UNSUPPORTED, "W8A8 outputs bf16 or raw int32");
         I.out_i32 = d->out_dtype == HQ_DT_INT32;
         I.G = d->K;
+    } else if (a == HQ_DT_BF16 && (w == HQ_DT_FP6_E2M3 || w == HQ_DT_FP6_E3M2 ||
+                                   (w == HQ_DT_FP8_E4M3 && d->w_scale_dtype == HQ_DT_E8M0))) {
+        // MX float weights: E4M3 (MXFP8) or E2M3 / E3M2 (MXFP6) codes with one
+        // E8M0 scale per 32 K, converted to bf16 operands with the scale (exact)
+        I.kind = Kind::FP4_A16;
+        I.mxf = w == HQ_DT_FP8_E4M3 ? 1 : w == HQ_DT_FP6_E2M3 ? 2 : 3;
+        if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "MX float weights are dense-only");
+        if (d->w_scale_dtype != HQ_DT_E8M0 || d->w_scale_gran != HQ_GRAN_PER_GROUP_K || d->group_size != 32)
+            return set_error(HQ_ERR_UNSUPPORTED, "MXFP8 / MXFP6 weights need E8M0 scales per 32 K elements");
+        if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MX float weight-only takes no activation scale");
+        if (d->K % 128) return set_error(HQ_ERR_UNSUPPORTED, "MX float weights need K %% 128 == 0 (K=%lld)", (long long)d->K);
+        if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MX float weights take no zero-points");
+        if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x MX float weights outputs bf16");
+        I.G = 32;
     } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT8 || w == HQ_DT_FP8_E4M3)) {
         I.kind = Kind::W8A16;
         I.a_bf16 = a == HQ_DT_BF16;
@@ -249,8 +263,9 @@ static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
         case Kind::MXA_MX: return hip_status(mx_act_launch(a, L.a_fp4), L.a_fp4 ? "hq_gemm(W4A4-MXFP4)" : "hq_gemm(W4A8-MXFP8xMXFP4)");
         case Kind::FP8_BLOCK: return hip_status(fp8_block_launch(a), "hq_gemm(FP8-blockwise)");
         case Kind::FP4_A16:
-            return hip_status(fp4_a16_launch(a, L.nv ? 1 : L.i4 ? 2 : 0),
-                              L.nv ? "hq_gemm(NVFP4-A16)" : L.i4 ? "hq_gemm(MXINT4-A16)" : "hq_gemm(MXFP4-A16)");
+            return hip_status(fp4_a16_launch(a, L.nv ? 1 : L.i4 ? 2 : L.mxf ? 2 + L.mxf : 0),
+                              L.nv ? "hq_gemm(NVFP4-A16)" : L.i4 ? "hq_gemm(MXINT4-A16)"
+                              : L.mxf == 1 ? "hq_gemm(MXFP8-A16)" : L.mxf ? "hq_gemm(MXFP6-A16)" : "hq_gemm(MXFP4-A16)");
         default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind runs through hq_moe_gemm");
     }
 }
@@ -384,6 +399,14 @@ hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale,
     const bool need_s2 = desc->scale2 != HQ_S2_NONE;
     if (need_s2 && (!scale2 || !s2_out)) return set_error(HQ_ERR_INVALID_ARG, "second-level scale buffers are required");
     if (!need_s2 && (scale2 || s2_out)) return set_error(HQ_ERR_INVALID_ARG, "second-level scale buffers must be NULL");
+    if (L.kind == Kind::FP4_A16 && L.mxf >= 2) {
+        // FP6 codes, one per byte: the low six bits
+        const uint8_t* c = (const uint8_t*)w;
+        for (int64_t i = 0; i < L.K * L.N; ++i)
+            if (c[i] & 0xC0u)
+                return set_error(HQ_ERR_INVALID_ARG, "FP6 code 0x%02x at k=%lld n=%lld has bits above bit 5", c[i],
+                                 (long long)(i / L.N), (long long)(i % L.N));
+    }
     if (L.kind == Kind::WNA16 && L.bits < 4) {
         // low-bit codes, one per byte: each must lie inside its width
         const int lo = L.zp ? 0 : -(1 << (L.bits - 1)), hi = L.zp ? (1 << L.bits) - 1 : (1 << (L.bits - 1)) - 1;

@@ -19,7 +19,8 @@ enum class Kind {
     MXA_MX,       // MX activations (E4M3 or E2M1, E8M0 per 32 K) x e2m1 W, E8M0 per 32 K
     FP8_BLOCK,    // fp8-e4m3 A (fp32 per row and 128-K block) x fp8-e4m3 W (fp32 per 128 x 128 block)
     FP4_A16,      // bf16 A, e2m1 W with E8M0 per 32 K (MXFP4) or E4M3 per 16 K + fp32 per tensor (NVFP4);
-                  // also INT4 W with E8M0 per 32 K (MXINT4)
+                  // also INT4 W with E8M0 per 32 K (MXINT4), and E4M3 / E2M3 / E3M2 W with
+                  // E8M0 per 32 K (MXFP8, MXFP6)
     W8A16,        // bf16/fp16 A, int8 or fp8-e4m3 W, fp32 per-channel
 };
 
@@ -33,6 +34,7 @@ struct LayerInfo {
     bool nv;       // FP4_A16: NVFP4 (E4M3 per 16 K, per-tensor second-level scale), else MXFP4
     bool i4;       // FP4_A16: MXINT4 (two's-complement INT4 codes, E8M0 per 32 K) instead of e2m1
     bool w_fp8;    // W8A16: E4M3 weight codes instead of INT8
+    int mxf;       // FP4_A16: MX float codes, 1 = E4M3 (MXFP8), 2 = E2M3, 3 = E3M2 (MXFP6); 0 = none
     int bits;      // WNA16: weight code width (4, or 1 / 2 / 3 for the low-bit widths)
     bool invariant;        // HQ_FLAG_BATCH_INVARIANT
     int tune_path, tune_splits;  // HQ_TUNE override (0, 0: the library's choice)

@@ -17,6 +17,8 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef unsigned v6u __attribute__((ext_vector_type(6)));
+typedef unsigned v16u __attribute__((ext_vector_type(16)));
 
 union Frag8 {  // eight 16-bit values = one MFMA A/B operand of 16x16x32 f16/bf16
     v4u u;

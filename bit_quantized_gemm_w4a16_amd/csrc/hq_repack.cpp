@@ -83,6 +83,35 @@ void repack_lowbit(const LayerInfo& L, const int8_t* w, uint8_t* out) {
             }
 }
 
+// FP6 codes (one per byte, [K][N], the low six bits) into two planes that
+// together hold a lane's 32 codes of a chunk as one 192-bit group, code j
+// (k = 128*chunk + 32*(lane >> 4) + j) at bits 6j..6j+5 (the element order of
+// the packed FP6 convert): bits 0-127 in a 16-byte plane [Np/16][K/128][64
+// lanes][16 B], bits 128-191 after it in an 8-byte plane [Np/16][K/128][64
+// lanes][8 B].  Padding columns hold code 0.
+void repack_fp6(const LayerInfo& L, const uint8_t* w, uint8_t* out) {
+    const int64_t N = L.N, K = L.K, nst = L.Np / 16, nc = K / 128;
+    uint32_t* pa = (uint32_t*)out;
+    uint32_t* pb = (uint32_t*)(out + (size_t)(nst * nc * 1024));
+    for (int64_t st = 0; st < nst; ++st)
+        for (int64_t c = 0; c < nc; ++c)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int64_t n = st * 16 + (lane & 15), slot = (st * nc + c) * 64 + lane;
+                uint32_t x[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+                for (int j = 0; j < 32; ++j) {
+                    const int64_t k = c * 128 + 32 * (lane >> 4) + j;
+                    const uint64_t code = n < N ? (uint64_t)(w[k * N + n] & 63u) : 0u;
+                    const int bit = 6 * j;
+                    const uint64_t v = code << (bit & 31);
+                    x[bit >> 5] |= (uint32_t)v;
+                    if ((bit & 31) > 26) x[(bit >> 5) + 1] |= (uint32_t)(v >> 32);
+                }
+                for (int d = 0; d < 4; ++d) pa[slot * 4 + d] = x[d];
+                pb[slot * 2] = x[4];
+                pb[slot * 2 + 1] = x[5];
+            }
+}
+
 void repack_int8(const LayerInfo& L, const int8_t* w, int8_t* out) {
     const int64_t N = L.N, K = L.K, nst = L.Np / 16, nc = K / 64;
     for (int64_t e = 0; e < L.E; ++e) {
@@ -218,7 +247,8 @@ void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s
             *s = E * (size_t)L.Np * 4;
             break;
         case Kind::FP4_A16:
-            *w = E * nst * (size_t)(L.K / 128) * 1024;
+            // MXFP8: the 8-bit weight-only layout; MXFP6: a 16-byte and an 8-byte plane
+            *w = E * nst * (size_t)(L.K / 128) * (L.mxf == 1 ? 2048 : L.mxf ? 1536 : 1024);
             *s = E * nst * (size_t)(L.K / 128) * (L.nv ? 128 : 64);
             if (L.nv) *s2 = E * 4;
             break;
@@ -253,7 +283,9 @@ void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z,
             repack_chan32(L, (const float*)s, (float*)s_out);
             break;
         case Kind::FP4_A16:
-            repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, false);
+            if (L.mxf == 1) repack_int8_k32(L, (const int8_t*)w, (int8_t*)w_out);
+            else if (L.mxf) repack_fp6(L, (const uint8_t*)w, (uint8_t*)w_out);
+            else repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, false);
             if (L.nv) repack_e4m3_g16(L, (const uint8_t*)s, (uint8_t*)s_out);
             else repack_e8m0(L, (const uint8_t*)s, (uint8_t*)s_out);
             if (L.nv) std::memcpy(s2_out, s2, (size_t)L.E * 4);

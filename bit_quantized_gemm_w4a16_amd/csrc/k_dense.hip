@@ -16,6 +16,9 @@
 // formats; NVFP4 with its second-level scale, section "Eine einheitliche
 // Quantisierungsdarstellung"): e2m1 codes converted to bf16 with the lane's
 // E8M0 or E4M3 group scale (exact), bf16 MFMA, the per-tensor scale on the output.
+// The same for the MX float widths (section "WnA16": float weights of any
+// width; OCP MX v1.0): E4M3 (MXFP8) and E2M3 / E3M2 (MXFP6) codes under E8M0
+// per 32 K, the FP6 ones converted 32 at a time by the packed FP6 convert.
 //
 // FP8 W8A8 with blockwise scales (same section: the Hopper-era FP8 path with
 // blockwise scaling; "Humming v0.1.0-0.1.4" for the per-K-block activation
@@ -88,8 +91,14 @@ hipError_t w8a16_launch(const DenseArgs& a, bool bf16, bool fp8) {
 }
 
 hipError_t fp4_a16_launch(const DenseArgs& a, int kind) {
-    return kind == 1 ? launch<Fmt::NVFP4_BF16>(a, 0) : kind == 2 ? launch<Fmt::MXINT4_BF16>(a, 0)
-                     : launch<Fmt::MXFP4_BF16>(a, 0);
+    switch (kind) {
+        case 1: return launch<Fmt::NVFP4_BF16>(a, 0);
+        case 2: return launch<Fmt::MXINT4_BF16>(a, 0);
+        case 3: return launch<Fmt::MXF8_BF16>(a, 0);
+        case 4: return launch<Fmt::MXF6E2_BF16>(a, 0);
+        case 5: return launch<Fmt::MXF6E3_BF16>(a, 0);
+        default: return launch<Fmt::MXFP4_BF16>(a, 0);
+    }
 }
 
 hipError_t mx_act_launch(const DenseArgs& a, bool fp4_act) {

@@ -96,7 +96,8 @@ struct SkinnyTraits {
     static constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
     static constexpr bool MX = mx_mfma(F);               // E8M0 weight scales per 32 K
     static constexpr bool MXA = mx_act(F);               // E8M0 activation scales per 32 K
-    static constexpr bool FP4B = F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16;  // 4-bit -> bf16 operands
+    // 4-, 6- or 8-bit codes -> bf16 operands under the lane's scale
+    static constexpr bool FP4B = F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || mxf8(F) || mxf6(F);
     static constexpr int SB = F == Fmt::NVFP4_BF16 ? 128 : 64;  // scale bytes per strip and chunk
     static constexpr int AROW = FmtTraits<F>::AROW;      // bytes of a row per 128-K chunk
     static constexpr int UPC = AROW / 16;                // 16-byte A units per 128-K chunk and row
@@ -166,6 +167,9 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     const char* wp2[SPW];  // low-bit planes of the strip, at this lane
     const char* wp1[SPW];
     const size_t plane2 = WB >= 2 && WB < 4 ? (size_t)nstrips * p.nc * 512 : 0;  // bytes of the 2-bit plane
+    // MXFP6: a 16-byte plane (codes 0-20 of the lane's 32, and two bits of code 21)
+    // then an 8-byte plane (the rest) per lane and chunk
+    const char* f6b[SPW];
 #pragma unroll
     for (int sp = 0; sp < SPW; ++sp) {
         wstrip[sp] = strip_base + ws * SPW + sp;
@@ -173,6 +177,10 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
         wsrc[sp] = (const v4u*)(Wb + (size_t)st * p.nc * FmtTraits<F>::BSTRIP) + lane;
         wp2[sp] = Wb + (size_t)st * p.nc * 512 + lane * 8;
         wp1[sp] = Wb + plane2 + (size_t)st * p.nc * 256 + lane * 4;
+        if constexpr (mxf6(F)) {
+            wsrc[sp] = (const v4u*)(Wb + (size_t)st * p.nc * 1024) + lane;
+            f6b[sp] = Wb + (size_t)nstrips * p.nc * 1024 + (size_t)st * p.nc * 512 + lane * 8;
+        }
     }
     v4u w[CPW][SPW][NB];
     constexpr int CH = CPW / 2;
@@ -180,7 +188,11 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
 #pragma unroll
         for (int sp = 0; sp < SPW; ++sp) {
             const size_t c = (size_t)min(cw0 + i, wlast);
-            if constexpr (WB == 4) {
+            if constexpr (mxf6(F)) {
+                w[i][sp][0] = ld_nt(wsrc[sp] + c * 64);
+                const v2u b = __builtin_nontemporal_load((const v2u*)(f6b[sp] + c * 512));
+                w[i][sp][1] = v4u{b[0], b[1], 0u, 0u};
+            } else if constexpr (WB == 4) {
 #pragma unroll
                 for (int h = 0; h < NB; ++h) w[i][sp][h] = ld_nt(wsrc[sp] + (c * NB + h) * 64);
             } else {
@@ -476,11 +488,28 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                         sf0 = sf1 = e8m0_to_f32(((const uint8_t*)(lds + p.s_off))[(j * nsl + cl) * SB + lane]);
                     }
                     if (!valid) sf0 = sf1 = 0.f;  // a chunk past the wave's part contributes exactly zero
+                    v16u y6;  // MXFP6: the chunk's 32 codes at once, 6 bits each (code j at bit 6j)
+                    if constexpr (mxf6(F)) {
+                        const v6u x6 = v6u{w[i][sp][0][0], w[i][sp][0][1], w[i][sp][0][2], w[i][sp][0][3],
+                                           w[i][sp][1][0], w[i][sp][1][1]};
+                        if constexpr (F == Fmt::MXF6E2_BF16)
+                            y6 = __builtin_bit_cast(v16u, __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(x6, sf0));
+                        else
+                            y6 = __builtin_bit_cast(v16u, __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(x6, sf0));
+                    }
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const Frag8 b = F == Fmt::NVFP4_BF16    ? fp4_to_bf16_mul(w[i][sp][0][t], t < 2 ? sf0 : sf1)
-                                        : F == Fmt::MXINT4_BF16 ? int4_to_bf16(w[i][sp][0][t], sf0)
-                                                                : fp4_to_bf16(w[i][sp][0][t], sf0);
+                        Frag8 b;
+                        if constexpr (F == Fmt::NVFP4_BF16) b = fp4_to_bf16_mul(w[i][sp][0][t], t < 2 ? sf0 : sf1);
+                        else if constexpr (F == Fmt::MXINT4_BF16) b = int4_to_bf16(w[i][sp][0][t], sf0);
+                        else if constexpr (mxf8(F)) b = fp8_to_bf16_scaled(w[i][sp][t >> 1], t & 1, sf0);
+                        else if constexpr (mxf6(F)) b.u = v4u{y6[4 * t], y6[4 * t + 1], y6[4 * t + 2], y6[4 * t + 3]};
+                        else b = fp4_to_bf16(w[i][sp][0][t], sf0);
+                        if constexpr (mxf8(F) || mxf6(F)) {
+                            // (the scaled converts take only the scale's exponent: a zero scale gives no zeros)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) b.u[e] = valid ? b.u[e] : 0u;
+                        }
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt) acc2[t & 1][sp][mt] = mfma16<true>(af[mt][t], b, acc2[t & 1][sp][mt]);
                     }
@@ -696,7 +725,7 @@ inline SkinnyLds skinny_lds(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) 
     } else if (mx_mfma(F)) {
         s = al(NS * cmax * 64);
         if (mx_act(F)) z = al(rows * cmax * 4);
-    } else if (F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16) {
+    } else if (F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || mxf8(F) || mxf6(F)) {
         s = al(NS * cmax * (F == Fmt::NVFP4_BF16 ? 128 : 64));
     } else if (F == Fmt::W8A8_F8B) {
         s = al(NS * cmax * 4);
@@ -715,7 +744,7 @@ inline int64_t skinny_lds_need(Fmt F, int64_t rows, int64_t cmax, int NS, int gc
 
 constexpr bool skinny_a16(Fmt F) {
     return F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 ||
-           F == Fmt::MXINT4_BF16 || w8a16(F);
+           F == Fmt::MXINT4_BF16 || w8a16(F) || mxf8(F) || mxf6(F);
 }
 
 // The eight-wave schedule with direct A loads: one strip per workgroup, K in
@@ -743,7 +772,7 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
     // 10.2 -> 9.7).  UINT4 and MXFP4 measured slower that way at 1..4 rows, and
     // every format at 9..16 rows (more A read from L2 than the split's partials
     // and finalize cost: fp16 UINT4 M=16 11.6 against 11.1 us).
-    const bool heavy = F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || w8a16(F);
+    const bool heavy = F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || w8a16(F) || mxf8(F) || mxf6(F);
     const bool direct = mode == 2 || (mode == 0 && heavy && M <= 8 && nstrips >= 192 && skinny_direct_fits(F, M, K));
     if (direct) {
         p.ok = skinny_direct_fits(F, M, K) && force_splits <= 1;
@@ -778,13 +807,12 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
     // strips alone leave a quarter of the chip idle (or the slice must shrink)
     // 16-bit A at 9..16 rows (two strips per workgroup): two workgroups per CU
     // (four slices at N=4096: 11.2 against 11.9 us with two)
-    const bool a16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 ||
-                     F == Fmt::MXINT4_BF16 || w8a16(F);
+    const bool a16 = skinny_a16(F);
     const int64_t target = a16 && p.NS == 2 ? 512 : 256;
     int64_t S = p.groups_x >= 192 ? 1 : cdiv(target, p.groups_x);
     const int64_t smax = nc / WK > 0 ? nc / WK : 1;
     // weight loads per chunk (two 16-byte halves; or the two planes of 3-bit codes)
-    const int nb = (F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B || w8a16(F) || wbits == 3) ? 2 : 1;
+    const int nb = (F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B || w8a16(F) || mxf8(F) || mxf6(F) || wbits == 3) ? 2 : 1;
     const int64_t cap = p.SPW * 16 * nb < 64 ? 16 : 8;  // largest register batch instantiated
     while (S < smax && (skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap)) ++S;
     if (S > smax) S = smax;
@@ -944,6 +972,51 @@ inline hipError_t launch_widen_lowbit(const void* planes, void* out, int wbits, 
     return hipGetLastError();
 }
 
+// MXFP6 planes -> MXFP8 codes (exact: every E2M3 and E3M2 value is an E4M3
+// value) in the 8-bit weight-only layout, for the tiled kernels: one thread per
+// lane and chunk, 24 bytes in, two 16-byte halves out; the packed FP6 convert
+// turns the 32 codes into bf16, the fp8 converts those into E4M3 (no rounding
+// happens: each value is representable).
+template <bool E3M2>
+__global__ __launch_bounds__(256) void widen_fp6_kernel(const char* __restrict__ planes, v4u* __restrict__ out,
+                                                        int64_t slots) {
+    typedef short v2s __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // slot = (strip * nc + chunk) * 64 + lane
+    if (i >= slots) return;
+    const v4u a = __builtin_nontemporal_load((const v4u*)(planes + i * 16));
+    const v2u b = __builtin_nontemporal_load((const v2u*)(planes + (size_t)slots * 16 + i * 8));
+    const v6u x6 = v6u{a[0], a[1], a[2], a[3], b[0], b[1]};
+    v16u y;
+    if constexpr (E3M2) y = __builtin_bit_cast(v16u, __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(x6, 1.0f));
+    else y = __builtin_bit_cast(v16u, __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(x6, 1.0f));
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {  // bf16 pairs 2q, 2q+1 (codes 4q .. 4q+3) -> one word of E4M3 bytes
+        const uint32_t lo = y[2 * q], hi = y[2 * q + 1];
+        v2s w = v2s{0, 0};
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(w, __builtin_bit_cast(v2bf, lo), 1.0f, false);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(w, __builtin_bit_cast(v2bf, hi), 1.0f, true);
+        o[q] = __builtin_bit_cast(uint32_t, w);
+    }
+    const int64_t sc = i >> 6, lane = i & 63;  // (strip * nc + chunk), lane
+    out[(sc * 2) * 64 + lane] = v4u{o[0], o[1], o[2], o[3]};
+    out[(sc * 2 + 1) * 64 + lane] = v4u{o[4], o[5], o[6], o[7]};
+}
+
+inline hipError_t launch_widen_fp6(const void* planes, void* out, bool e3m2, int64_t Np, int64_t K, hipStream_t st) {
+    const int64_t slots = (Np / 16) * (K / 128) * 64, blocks = (slots + 255) / 256;
+    if (plan_recorder()) {
+        plan_record("widen_fp6_kernel<%s> grid=%lld", e3m2 ? "e3m2" : "e2m3", (long long)blocks);
+        return hipSuccess;
+    }
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 g((unsigned)blocks), b(256);
+    if (e3m2) hipLaunchKernelGGL(widen_fp6_kernel<true>, g, b, 0, st, (const char*)planes, (v4u*)out, slots);
+    else hipLaunchKernelGGL(widen_fp6_kernel<false>, g, b, 0, st, (const char*)planes, (v4u*)out, slots);
+    return hipGetLastError();
+}
+
 // Dense dispatch shared by the format launchers: the small-M weight stream up
 // to kSkinnyMaxM rows, the tiled kernels above; a tuning override (TunePath and
 // K split) or batch-invariant mode (tiled kernels without K split at every M:
@@ -969,6 +1042,21 @@ hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
         if (pl.splits > a.K / 128) return hipErrorNotSupported;
     }
     if (a.invariant) p.max_splits = 1;
+    if constexpr (mxf6(F)) {
+        // MXFP6 on the tiles: the planes widen to MXFP8 codes (8-bit weight-only
+        // layout) at the front of the workspace, the MXFP8 tiles read them with the
+        // E8M0 scales as they are, partial tiles follow
+        const size_t wide = (size_t)(a.Np / 16) * (size_t)(a.K / 128) * 2048, off = (wide + 255) & ~(size_t)255;
+        hipError_t e = launch_widen_fp6(a.w, a.ws, F == Fmt::MXF6E3_BF16, a.Np, a.K, a.stream);
+        if (e != hipSuccess) return e;
+        plan_workspace(wide);
+        plan_workspace_base(off);
+        p.W = a.ws;
+        p.part = (char*)a.ws + off;
+        e = launch_dense_plan<Fmt::MXF8_BF16>(pl, p, a.stream);
+        plan_workspace_base(0);
+        return e;
+    } else {
     if constexpr (F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16) {
         if (a.wbits < 4) {
             // low-bit widths on the tiles: the planes widen to the 4-bit layout at the
@@ -986,6 +1074,7 @@ hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
         }
     }
     return launch_dense_plan<F>(pl, p, a.stream);
+    }
 }
 
 }  // namespace hq

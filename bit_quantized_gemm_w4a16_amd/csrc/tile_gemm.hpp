@@ -61,7 +61,7 @@
 namespace hq {
 
 enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B, MXFP4_BF16, NVFP4_BF16,
-                 MXINT4_BF16, W8A16_F16, W8A16_BF16, F8W_F16, F8W_BF16 };
+                 MXINT4_BF16, W8A16_F16, W8A16_BF16, F8W_F16, F8W_BF16, MXF8_BF16, MXF6E2_BF16, MXF6E3_BF16 };
 
 constexpr const char* fmt_name(Fmt F) {
     return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
@@ -69,7 +69,8 @@ constexpr const char* fmt_name(Fmt F) {
          : F == Fmt::W4A4_MX ? "W4A4_MX" : F == Fmt::W8A8_F8B ? "W8A8_F8B" : F == Fmt::MXFP4_BF16 ? "MXFP4_BF16"
          : F == Fmt::NVFP4_BF16 ? "NVFP4_BF16" : F == Fmt::MXINT4_BF16 ? "MXINT4_BF16"
          : F == Fmt::W8A16_F16 ? "W8A16_F16" : F == Fmt::W8A16_BF16 ? "W8A16_BF16" : F == Fmt::F8W_F16 ? "F8W_F16"
-         : "F8W_BF16";
+         : F == Fmt::F8W_BF16 ? "F8W_BF16" : F == Fmt::MXF8_BF16 ? "MXF8_BF16" : F == Fmt::MXF6E2_BF16 ? "MXF6E2_BF16"
+         : "MXF6E3_BF16";
 }
 // Formats whose activations carry OCP MX scales (E8M0 per 32 K, [rows][K/32]).
 constexpr bool mx_act(Fmt F) { return F == Fmt::W4A8_MXA || F == Fmt::W4A4_MX; }
@@ -95,10 +96,21 @@ template <> struct FmtTraits<Fmt::W8A16_F16> { static constexpr int AROW = 256, 
 template <> struct FmtTraits<Fmt::W8A16_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::F8W_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::F8W_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+// MXFP8 weight-only: E4M3 codes in the INT8 weight-only layout, E8M0 per lane and chunk
+template <> struct FmtTraits<Fmt::MXF8_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+// MXFP6 weight-only (the small-M stream; the tiles read it widened to MXFP8): a
+// 16-byte and an 8-byte plane per lane and chunk, two loads
+template <> struct FmtTraits<Fmt::MXF6E2_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::MXF6E3_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 // 8-bit weight-only formats: INT8 or FP8 (E4M3) codes in the same layout, per-channel fp32 scale
 constexpr bool f8w(Fmt F) { return F == Fmt::F8W_F16 || F == Fmt::F8W_BF16; }
 constexpr bool w8a16(Fmt F) { return F == Fmt::W8A16_F16 || F == Fmt::W8A16_BF16 || f8w(F); }
 constexpr bool w8bf(Fmt F) { return F == Fmt::W8A16_BF16 || F == Fmt::F8W_BF16; }
+// MX-scaled float weights with bf16 activations: E4M3 (MXFP8), E2M3 / E3M2 (MXFP6)
+constexpr bool mxf8(Fmt F) { return F == Fmt::MXF8_BF16; }
+constexpr bool mxf6(Fmt F) { return F == Fmt::MXF6E2_BF16 || F == Fmt::MXF6E3_BF16; }
+// 8-bit weight codes in the INT8 weight-only layout (two 16-byte halves per lane and chunk)
+constexpr bool w8load(Fmt F) { return w8a16(F) || mxf8(F); }
 // e2m1 weights converted to bf16 operands with a per-lane scale (bf16 MFMA)
 constexpr bool fp4_bf16(Fmt F) {
     return F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16;
@@ -403,6 +415,18 @@ __device__ __forceinline__ Frag8 deq8_fp8(uint32_t w0, uint32_t w1) {
     return f;
 }
 
+// E4M3 x 2^(E-127) -> bf16, exact for the E8M0 range the format reaches (4
+// significant bits); 8 codes (one K sub-step) of a lane's 16-byte half.
+__device__ __forceinline__ Frag8 fp8_to_bf16_scaled(const v4u& half, int pair, float scale) {
+    const uint32_t w0 = half[2 * pair], w1 = half[2 * pair + 1];
+    Frag8 f;
+    f.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false));
+    f.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true));
+    f.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false));
+    f.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true));
+    return f;
+}
+
 // 8 codes (one K sub-step) of a lane's 16-byte half: INT8 or E4M3
 template <Fmt F>
 __device__ __forceinline__ Frag8 deq8(const v4u& half, int pair) {
@@ -453,7 +477,8 @@ void tile_gemm_kernel(TileArgs p) {
     using Acc = typename T::Acc;
     constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
     constexpr bool NV = F == Fmt::NVFP4_BF16;             // E4M3 weight scales per 16 K
-    constexpr bool MX = mx_mfma(F) || F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::MXINT4_BF16 || NV;  // byte scales per lane
+    constexpr bool MX = mx_mfma(F) || F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::MXINT4_BF16 || NV || mxf8(F);  // byte scales per lane
+    static_assert(!mxf6(F), "MXFP6 reaches the tiles widened to MXFP8");
     constexpr bool MXA = mx_act(F);
     constexpr bool F8B = F == Fmt::W8A8_F8B;
     static_assert(!F8B || BN == 128, "blockwise fp8: one 128-column weight block per tile");
@@ -760,10 +785,10 @@ void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
             for (int h = 0; h < NBH; ++h) bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
 
-        if constexpr (F == Fmt::WNA16_F16 || fp4_bf16(F) || w8a16(F)) {
+        if constexpr (F == Fmt::WNA16_F16 || fp4_bf16(F) || w8load(F)) {
             // 16-bit A with 4-bit weights decoded into the operand: fp16 (q - z) * s,
             // or e2m1 x (2^(E-127) or an E4M3 value) -> bf16 (exact)
-            constexpr bool MOE = fp4_bf16(F);
+            constexpr bool MOE = fp4_bf16(F) || mxf8(F);  // bf16 operands under the lane's E8M0 or E4M3 scale
             constexpr bool BFA = MOE || w8bf(F);  // bf16 MFMA (else fp16)
             // A fragments read ahead (software pipeline): a whole sub-step, or
             // a ring of three for tall / wide wave tiles
@@ -798,6 +823,7 @@ void tile_gemm_kernel(TileArgs p) {
             auto mkb = [&](int j, int tt) -> Frag8 {
                 if constexpr (NV) return fp4_to_bf16_mul(bw[j][0][tt], sf[j][tt >> 1]);
                 else if constexpr (F == Fmt::MXINT4_BF16) return int4_to_bf16(bw[j][0][tt], sf[j][0]);
+                else if constexpr (mxf8(F)) return fp8_to_bf16_scaled(bw[j][tt >> 1], tt & 1, sf[j][0]);
                 else if constexpr (w8a16(F)) return deq8<F>(bw[j][tt >> 1], tt & 1);
                 else if constexpr (MOE) return fp4_to_bf16(bw[j][0][tt], sf[j][0]);
                 else return deq4_f16_scaled(bw[j][0][tt] ^ wx, nb2[j], nh2[j], s2[j]);
@@ -1399,19 +1425,20 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
 // halves the A traffic per flop and still fits two LDS stages.  bf16 A has no
 // 256-row variant (its row-sum MFMA needs a second accumulator set).
 // INT8 weight-only: 256-row tiles do not fit two stages of its 2 KB weight strips
-constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16 && !w8a16(F); }
+constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16 && !w8load(F) && !mxf6(F); }
 // fp16 A with 4-bit weights: 8 waves side by side, each dequantising its own
 // weight strips once: 256 x 256 tiles of 256 x 32 waves with a single weight
 // stage (each dequantised fragment feeds 16 MFMAs; 13 % faster than 128 x 256
 // at M = 8192), or 128 x 256 tiles of 128 x 32 waves where 256 x 256 would not
 // cover the chip (a K step loads 48 KB instead of the 80 KB of 256 x 128).
 constexpr bool has_wide_tile(Fmt F) {
-    return F == Fmt::WNA16_F16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || w8a16(F);
+    return F == Fmt::WNA16_F16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || w8load(F) ||
+           mxf6(F);
 }
 // INT8: 256 x 256 on 8 waves of 128 x 64, direct loads into two full stages
 // (M = 8192: 1126 us vs 1569 us for 256 x 128 with register-staged loads); the
 // 256 x 128 tile also loads directly (1498 us).
-constexpr bool has_wide256_tile(Fmt F) { return (has_wide_tile(F) && !w8a16(F)) || F == Fmt::W8A8_I8; }
+constexpr bool has_wide256_tile(Fmt F) { return (has_wide_tile(F) && !w8load(F) && !mxf6(F)) || F == Fmt::W8A8_I8; }
 // 256x256 tiles from this many on: INT8 keeps the 256x128 three-stage ring
 // until the wide tiles fill two rounds of the chip (measured: the ring is
 // faster at M=1024 and level at M=2048 for N=18432, K=7168)
@@ -1436,7 +1463,7 @@ hipError_t launch_forced(const TilePlan& pl, TileArgs p, hipStream_t st) {
             if constexpr (has_wide_tile(F)) return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
             else return hipErrorNotSupported;
         case TUNE_W256:
-            if constexpr (has_wide_tile(F) && !w8a16(F)) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
+            if constexpr (has_wide_tile(F) && !w8load(F)) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
             else if constexpr (F == Fmt::W8A8_I8) return launch_tile_kernel<F, 256, 256, 2, 4, 0>(p, st);
             else if constexpr (mx_mfma(F)) return launch_tile_kernel<F, 256, 256, 2, 4, 4>(p, st);
             else return hipErrorNotSupported;
@@ -1505,7 +1532,7 @@ hipError_t launch_dense_plan(const TilePlan& pl, TileArgs p, hipStream_t st) {
             }
         }
         if constexpr (has_wide_tile(F)) {
-            if constexpr (!w8a16(F))
+            if constexpr (!w8load(F))
                 if (pl.wide && pl.BM == 256) return launch_tile_kernel<F, 256, 256, 1, 8, 3>(p, st);
             if (pl.wide) return launch_tile_kernel<F, 128, 256, 1, 8, 0>(p, st);
             // from 512 rows, 128 x 256 tiles with the K split filling the chip

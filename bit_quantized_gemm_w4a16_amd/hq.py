@@ -24,7 +24,7 @@ HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_ALIGNMENT, HQ_ERR_WORKSPAC
 # hq_dtype
 (HQ_DT_NONE, HQ_DT_BF16, HQ_DT_FP16, HQ_DT_FP32, HQ_DT_FP8_E4M3, HQ_DT_INT8, HQ_DT_INT4, HQ_DT_UINT4,
  HQ_DT_FP4_E2M1, HQ_DT_E8M0, HQ_DT_INT32, HQ_DT_INT1, HQ_DT_UINT1, HQ_DT_INT2, HQ_DT_UINT2, HQ_DT_INT3,
- HQ_DT_UINT3) = range(17)
+ HQ_DT_UINT3, HQ_DT_FP6_E2M3, HQ_DT_FP6_E3M2) = range(19)
 HQ_GRAN_NONE, HQ_GRAN_PER_GROUP_K, HQ_GRAN_PER_CHANNEL, HQ_GRAN_BLOCK_128x128 = range(4)
 HQ_ASCALE_NONE, HQ_ASCALE_PER_TOKEN_F32, HQ_ASCALE_MX_E8M0, HQ_ASCALE_PER_BLOCK128_F32 = range(4)
 HQ_S2_NONE, HQ_S2_PER_TENSOR_F32 = 0, 1
@@ -143,6 +143,13 @@ def desc_w4a16(N, K, group_size=128, bf16=True, zp=False) -> hq_layer_desc:
     a = HQ_DT_BF16 if bf16 else HQ_DT_FP16
     return make_desc(N, K, a, HQ_DT_UINT4 if zp else HQ_DT_INT4, a, HQ_GRAN_PER_GROUP_K, group_size, a,
                      zp_dtype=HQ_DT_UINT4 if zp else HQ_DT_NONE)
+
+
+def desc_mxf_a16(N, K, elem) -> hq_layer_desc:
+    """bf16 activations x MX float weights: elem "e4m3" (MXFP8), "e2m3" or "e3m2"
+    (MXFP6), one E8M0 scale per 32 K."""
+    w = {"e4m3": HQ_DT_FP8_E4M3, "e2m3": HQ_DT_FP6_E2M3, "e3m2": HQ_DT_FP6_E3M2}[elem]
+    return make_desc(N, K, HQ_DT_BF16, w, HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K, 32, HQ_DT_BF16)
 
 
 def desc_wnlow(N, K, bits, signed, group_size=128, bf16=True) -> hq_layer_desc:

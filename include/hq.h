@@ -95,7 +95,10 @@ typedef enum hq_dtype {
     HQ_DT_INT2 = 13,     /* -2..1                                      */
     HQ_DT_UINT2 = 14,    /* 0..3                                       */
     HQ_DT_INT3 = 15,     /* -4..3                                      */
-    HQ_DT_UINT3 = 16     /* 0..7                                       */
+    HQ_DT_UINT3 = 16,    /* 0..7                                       */
+    /* OCP MX v1.0 FP6 element types (MXFP6 weights); one code per byte on input */
+    HQ_DT_FP6_E2M3 = 17, /* 2 exponent bits (bias 1), 3 mantissa bits  */
+    HQ_DT_FP6_E3M2 = 18  /* 3 exponent bits (bias 3), 2 mantissa bits  */
 } hq_dtype;
 
 typedef enum hq_scale_gran {

@@ -91,6 +91,13 @@ WNLOW_TILES = [(M, N, K, G, b, sg, not sg) for M, N, K, G in ((100, 384, 768, 12
 WNLOW_SWEEP = [(M, C2["N"], C2["K"], C2["G"], b, sg, bf) for b, sg, bf in ((3, False, False), (2, True, True))
                for M in SWEEP]
 
+# ---- MX float weights (MXFP8 E4M3, MXFP6 E2M3 / E3M2), bf16 activations: (M, N, K, elem) ----
+MXF_ELEMS = ["e4m3", "e2m3", "e3m2"]
+MXF_SMALL = [(M, 272, 1024, e) for M in (1, 5, 16, 33, 64) for e in MXF_ELEMS]
+MXF_TILES = [(M, N, K, e) for M, N, K in ((100, 384, 768), (300, 1000, 512), (2000, 4100, 384)) for e in MXF_ELEMS]
+# at the dense W4A16 layer's shape, the widths the benchmark times
+MXF_SWEEP = [(M, C2["N"], C2["K"], e) for e in ("e4m3", "e2m3") for M in SWEEP]
+
 
 def all_dense_cases():
     """(format, M, N, K, G, flags) for every dense GPU case, flags a dict."""
@@ -116,6 +123,8 @@ def all_dense_cases():
         out.append(("mxint4", M, N, K, 32, {}))
     for M, N, K, G, b, sg, bf in WNLOW_SMALL + WNLOW_TILES + WNLOW_SWEEP:
         out.append(("wnlow", M, N, K, G, dict(bits=b, signed=sg, bf16=bf)))
+    for M, N, K, e in MXF_SMALL + MXF_TILES + MXF_SWEEP:
+        out.append(("mxf", M, N, K, 32, dict(elem=e)))
     for wf in ("w8a16", "fp8w"):
         for dt in ("bf16", "fp16"):
             for M, N, K in W8A16_SMALL + W8A16_TILES + W8A16_SWEEP:

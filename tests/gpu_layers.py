@@ -9,10 +9,14 @@ from bit_quantized_gemm_w4a16_amd import hq
 from gpu_util import GATE, dev, empty, gate_error, to_f64
 
 FORMATS = ["wna16_f16_zp", "wna16_bf16_sym", "w4a8_mxfp4", "w8a8_bf16", "w8a8_raw", "w4a4_mx", "mxfp8_mx",
-           "fp8_blockwise", "mxfp4_a16", "nvfp4_a16", "mxint4_a16", "w8a16_bf16", "w8a16_f16", "fp8w_bf16", "fp8w_f16"]
-# formats with 16-bit activations
+           "fp8_blockwise", "mxfp4_a16", "nvfp4_a16", "mxint4_a16", "w8a16_bf16", "w8a16_f16", "fp8w_bf16", "fp8w_f16",
+           "mxfp8_a16", "mxfp6e2_a16", "mxfp6e3_a16", "w3a16_uint3", "w2a16_int2", "w1a16_int1"]
+# formats with 16-bit activations that every small-M schedule takes (the low-bit
+# widths have no eight-wave stream)
 A16_FORMATS = ["wna16_f16_zp", "wna16_bf16_sym", "mxfp4_a16", "nvfp4_a16", "mxint4_a16", "w8a16_bf16", "w8a16_f16",
-               "fp8w_bf16", "fp8w_f16"]
+               "fp8w_bf16", "fp8w_f16", "mxfp8_a16", "mxfp6e2_a16", "mxfp6e3_a16"]
+MXF_ELEM = {"mxfp8_a16": "e4m3", "mxfp6e2_a16": "e2m3", "mxfp6e3_a16": "e3m2"}
+LOWBIT = {"w3a16_uint3": (3, False), "w2a16_int2": (2, True), "w1a16_int1": (1, True)}
 
 
 class Layer:
@@ -71,6 +75,22 @@ class Layer:
             A, sa, arow, srow = d["A"], None, K * 2, 0
             ref = oracle.gemm_fp8w_a16 if fp8 else oracle.gemm_w8a16
             self.ref = lambda r: ref(d["A"], d["w"], d["s_w"], a_bf16=bf, rows=r)
+        elif fmt in MXF_ELEM:
+            elem = MXF_ELEM[fmt]
+            d = syn.mxf_a16(seed, M, N, K, elem)
+            self.desc = hq.desc_mxf_a16(N, K, elem)
+            packed = hq.hq_repack(self.desc, d["codes"], d["e"])
+            A, sa, arow, srow = d["A"], None, K * 2, 0
+            self.ref = lambda r: oracle.gemm_mxf_a16(d["A"], d["codes"], d["e"], elem=elem, rows=r)
+        elif fmt in LOWBIT:
+            bits, signed = LOWBIT[fmt]
+            self.out_dt = torch.bfloat16 if signed else torch.float16
+            d = syn.wnlow(seed, M, N, K, bits, signed, dtype=self.out_dt)
+            self.desc = hq.desc_wnlow(N, K, bits, signed, bf16=signed)
+            packed = hq.hq_repack(self.desc, d["codes"], d["s"], d.get("z"))
+            A, sa, arow, srow = d["A"], None, K * 2, 0
+            self.ref = lambda r: oracle.gemm_wnlow(d["A"], d["codes"], d["s"], d.get("z"), N=N, K=K, G=128, bits=bits,
+                                                   a_bf16=signed, w_signed=signed, rows=r)
         elif fmt == "mxint4_a16":
             d = syn.w4a16_mxint4(seed, M, N, K)
             self.desc = hq.desc_mxint4_a16(N, K)

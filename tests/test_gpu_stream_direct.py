@@ -32,14 +32,15 @@ def test_direct_stream_matches_the_oracle(fmt, M, K):
     L.check(L.run(d, M), np.arange(M))
 
 
-HEAVY = {"nvfp4_a16", "mxint4_a16", "w8a16_bf16", "w8a16_f16", "fp8w_bf16", "fp8w_f16"}
+HEAVY = {"nvfp4_a16", "mxint4_a16", "w8a16_bf16", "w8a16_f16", "fp8w_bf16", "fp8w_f16", "mxfp8_a16", "mxfp6e2_a16",
+         "mxfp6e3_a16"}
 
 
 @pytest.mark.parametrize("fmt", A16_FORMATS)
 def test_library_choice_up_to_eight_rows(fmt):
     """On a wide layer (256 strips) at M = 1 and 8 the library takes the direct
-    stream for the formats with the longer decodes (NVFP4, MXINT4, 8-bit
-    weights) and the four-wave stream for the others; both match the oracle."""
+    stream for the formats with the longer decodes (NVFP4, MXINT4, 8-bit and
+    MX float weights) and the four-wave stream for the others; both match the oracle."""
     K = 7168
     for M in (1, 8):
         L = Layer(fmt, M, 4096, K, seed=M)
