@@ -76,6 +76,8 @@ def lib():
         L.hq_oracle_gemm_fp8_blockwise.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
         L.hq_oracle_gemm_fp4_a16.restype = C.c_int
         L.hq_oracle_gemm_fp4_a16.argtypes = [i64, i64, i64, C.c_int, p, p, C.c_int, p, p, p, i64, p]
+        L.hq_oracle_e0m.restype = C.c_double
+        L.hq_oracle_e0m.argtypes = [C.c_uint, C.c_int, p]
         L.hq_oracle_fp6.restype = C.c_double
         L.hq_oracle_fp6.argtypes = [C.c_uint, C.c_int]
         L.hq_oracle_gemm_mxf_a16.restype = C.c_int
@@ -128,6 +130,24 @@ def e8m0(e: int) -> float:
 
 def e4m3(code: int) -> float:
     return lib().hq_oracle_e4m3(code)
+
+
+def e0m(code: int, n: int) -> float:
+    """Zero-exponent float e0mN: sign bit n, integer magnitude in bits 0..n-1."""
+    ok = C.c_int(0)
+    v = lib().hq_oracle_e0m(code, n, C.byref(ok))
+    if not ok.value:
+        raise ValueError(f"e0m{n} code 0x{code:x} has bits above bit {n}")
+    return v
+
+
+def e0m_to_int(codes, n: int) -> np.ndarray:
+    """Array of e0mN codes -> their integer values (int8), through the scalar decode."""
+    codes = np.asarray(codes)
+    lut = np.array([e0m(c, n) for c in range(1 << (n + 1))], dtype=np.int64)
+    if codes.size and int(codes.max()) >= (1 << (n + 1)):
+        raise ValueError(f"e0m{n} codes above {(1 << (n + 1)) - 1}")
+    return lut[codes.astype(np.int64)].astype(np.int8)
 
 
 def fp6(code: int, e3m2: bool) -> float:

@@ -82,6 +82,20 @@ double hq_oracle_fp6(unsigned code, int e3m2)
     return s ? -mag : mag;
 }
 
+/* Zero-exponent float e0mN ("Humming wird angekuendigt", section on the weight
+ * and activation combinations: a float format without exponent bits whose
+ * values are the symmetric integers of the same width): 1 sign bit (bit n)
+ * and n mantissa bits read as an integer magnitude, so the code's value is
+ * -m or +m (the sign with magnitude 0 is zero).  Returns 0 and sets *ok = 0 if
+ * the code has a bit above bit n. */
+double hq_oracle_e0m(unsigned code, int n, int* ok)
+{
+    *ok = (code >> (n + 1)) == 0u;
+    if (!*ok) return 0.0;
+    const unsigned m = code & ((1u << n) - 1u);
+    return ((code >> n) & 1u) ? -(double)m : (double)m;
+}
+
 /* Round-to-nearest-even fp32 -> E4M3 with saturation to +-448 (satfinite). */
 unsigned hq_oracle_e4m3_encode(float x)
 {

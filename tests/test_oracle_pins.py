@@ -969,3 +969,27 @@ def test_mxf_a16_block_step_and_code_range(elem):
     bad[5, 3] |= 0x40
     with pytest.raises(ValueError):
         oracle.gemm_mxf_a16(d["A"], bad, d["e"], elem=elem)
+
+
+# ---- zero-exponent floats e0mN: "Humming wird angekuendigt", the paragraph on the
+# format whose values are the symmetric integers of its width ----
+
+def test_e0m7_values_are_int8_without_minus_128():
+    """The pages' own example: e0m7 and INT8 without -128 both represent -127..127."""
+    vals = [oracle.e0m(c, 7) for c in range(256)]
+    assert sorted(set(vals)) == list(range(-127, 128))
+    assert vals.count(0) == 2 and all(vals.count(v) == 1 for v in range(-127, 128) if v)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 7])
+def test_e0m_sign_and_magnitude(n):
+    """Every magnitude m < 2^n appears once with each sign (the sign bit is bit n,
+    the magnitude the low n bits: code m and code 2^n + m negate each other); a
+    bit above n is rejected; the values are exactly the symmetric integers of the
+    width n + 1 (INT(n+1) without its most negative code)."""
+    for m in range(1 << n):
+        assert oracle.e0m(m, n) == m and oracle.e0m((1 << n) | m, n) == -m
+    with pytest.raises(ValueError):
+        oracle.e0m(1 << (n + 1), n)
+    lo = -(1 << n)
+    assert sorted({oracle.e0m(c, n) for c in range(1 << (n + 1))}) == list(range(lo + 1, -lo))
