@@ -63,6 +63,17 @@ static hq_status ok() {
     return HQ_OK;
 }
 
+// mantissa width n of the zero-exponent float dtypes e0mN (0 for the others)
+static int e0m_width(int w) {
+    switch (w) {
+        case HQ_DT_E0M1: return 1;
+        case HQ_DT_E0M2: return 2;
+        case HQ_DT_E0M3: return 3;
+        case HQ_DT_E0M7: return 7;
+        default: return 0;
+    }
+}
+
 // code width of the low-bit weight dtypes (0 for the others)
 int lowbit_width(int w) {
     switch (w) {
@@ -117,12 +128,15 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 takes no zero-points");
         if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x MXINT4 outputs bf16");
         I.G = 32;
-    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT4 || w == HQ_DT_UINT4 || lowbit_width(w))) {
-        // W4A16, and the low-bit widths on the same kernels (1-3-bit codes widened
-        // to 4-bit ones in registers)
+    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) &&
+               (w == HQ_DT_INT4 || w == HQ_DT_UINT4 || lowbit_width(w) || (e0m_width(w) && e0m_width(w) <= 3))) {
+        // W4A16, the low-bit widths on the same kernels (1-3-bit codes widened
+        // to 4-bit ones in registers), and e0m1..e0m3 (sign and magnitude,
+        // converted at repack to the two's-complement codes of width n + 1)
         I.kind = Kind::WNA16;
         I.a_bf16 = a == HQ_DT_BF16;
-        I.bits = lowbit_width(w) ? lowbit_width(w) : 4;
+        I.e0m = e0m_width(w);
+        I.bits = I.e0m ? I.e0m + 1 : lowbit_width(w) ? lowbit_width(w) : 4;
         I.zp = w == HQ_DT_UINT4 || w == HQ_DT_UINT1 || w == HQ_DT_UINT2 || w == HQ_DT_UINT3;
         if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 INT4/UINT4 is dense-only");
         if (d->w_scale_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "W4A16 scale dtype must equal the activation dtype");
@@ -214,8 +228,10 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MX float weights take no zero-points");
         if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x MX float weights outputs bf16");
         I.G = 32;
-    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT8 || w == HQ_DT_FP8_E4M3)) {
+    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT8 || w == HQ_DT_FP8_E4M3 || w == HQ_DT_E0M7)) {
+        // (e0m7: sign and magnitude, converted at repack to INT8 -127..127)
         I.kind = Kind::W8A16;
+        I.e0m = e0m_width(w);
         I.a_bf16 = a == HQ_DT_BF16;
         I.w_fp8 = w == HQ_DT_FP8_E4M3;
         if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "INT8 weight-only is dense-only");
@@ -407,7 +423,14 @@ hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale,
                 return set_error(HQ_ERR_INVALID_ARG, "FP6 code 0x%02x at k=%lld n=%lld has bits above bit 5", c[i],
                                  (long long)(i / L.N), (long long)(i % L.N));
     }
-    if (L.kind == Kind::WNA16 && L.bits < 4) {
+    if (L.e0m == 1 || L.e0m == 2) {
+        // e0m1 / e0m2 codes, one per byte: the sign bit n and n magnitude bits
+        const uint8_t* c = (const uint8_t*)w;
+        for (int64_t i = 0; i < L.K * L.N; ++i)
+            if (c[i] >> (L.e0m + 1))
+                return set_error(HQ_ERR_INVALID_ARG, "e0m%d code 0x%02x at k=%lld n=%lld has bits above bit %d", L.e0m,
+                                 c[i], (long long)(i / L.N), (long long)(i % L.N), L.e0m);
+    } else if (L.kind == Kind::WNA16 && L.bits < 4) {
         // low-bit codes, one per byte: each must lie inside its width
         const int lo = L.zp ? 0 : -(1 << (L.bits - 1)), hi = L.zp ? (1 << L.bits) - 1 : (1 << (L.bits - 1)) - 1;
         const int8_t* c = (const int8_t*)w;

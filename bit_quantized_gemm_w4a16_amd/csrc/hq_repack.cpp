@@ -11,6 +11,7 @@
 // fragment (see include/hq.h for the exact layout).
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "hq_common.h"
 
@@ -259,15 +260,48 @@ void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s
     }
 }
 
+// e0mN code (sign bit n, magnitude in bits 0..n-1) -> its two's-complement value
+static int8_t e0m_value(uint32_t c, int n) {
+    const int m = (int)(c & ((1u << n) - 1u));
+    return (int8_t)(((c >> n) & 1u) ? -m : m);
+}
+
+// e0mN codes -> the two's-complement container of width n + 1 in the logical
+// input form of that container (4-bit words for e0m3, one byte per code else)
+static std::vector<uint32_t> e0m_to_int(const LayerInfo& L, const void* w) {
+    const int64_t KN = L.E * L.K * L.N;
+    if (L.e0m == 3) {
+        std::vector<uint32_t> q((size_t)(KN / 8));
+        const uint32_t* src = (const uint32_t*)w;
+        for (int64_t i = 0; i < KN / 8; ++i) {
+            uint32_t o = 0;
+            for (int j = 0; j < 8; ++j) o |= ((uint32_t)e0m_value((src[i] >> (4 * j)) & 15u, 3) & 15u) << (4 * j);
+            q[(size_t)i] = o;
+        }
+        return q;
+    }
+    std::vector<uint32_t> q((size_t)((KN + 3) / 4));
+    const uint8_t* src = (const uint8_t*)w;
+    int8_t* dst = (int8_t*)q.data();
+    for (int64_t i = 0; i < KN; ++i) dst[i] = e0m_value(src[i], L.e0m);
+    return q;
+}
+
 void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z, const void* s2, void* w_out,
                 void* s_out, void* z_out, void* s2_out) {
     switch (L.kind) {
-        case Kind::WNA16:
+        case Kind::WNA16: {
+            std::vector<uint32_t> conv;
+            if (L.e0m) {
+                conv = e0m_to_int(L, w);
+                w = conv.data();
+            }
             if (L.bits < 4) repack_lowbit(L, (const int8_t*)w, (uint8_t*)w_out);
             else repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, true);
             repack_scale16(L, (const uint16_t*)s, (uint16_t*)s_out, L.a_bf16 ? 0x3F80 : 0x3C00);
             if (L.zp) repack_zero4(L, (const uint32_t*)z, (uint64_t*)z_out);
             break;
+        }
         case Kind::W4A8_MX:
         case Kind::MXA_MX:
         case Kind::MOE_MX_BF16:
@@ -278,10 +312,16 @@ void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z,
             repack_int8(L, (const int8_t*)w, (int8_t*)w_out);
             repack_chan32(L, (const float*)s, (float*)s_out);
             break;
-        case Kind::W8A16:
+        case Kind::W8A16: {
+            std::vector<uint32_t> conv;
+            if (L.e0m) {
+                conv = e0m_to_int(L, w);
+                w = conv.data();
+            }
             repack_int8_k32(L, (const int8_t*)w, (int8_t*)w_out);
             repack_chan32(L, (const float*)s, (float*)s_out);
             break;
+        }
         case Kind::FP4_A16:
             if (L.mxf == 1) repack_int8_k32(L, (const int8_t*)w, (int8_t*)w_out);
             else if (L.mxf) repack_fp6(L, (const uint8_t*)w, (uint8_t*)w_out);

@@ -98,7 +98,13 @@ typedef enum hq_dtype {
     HQ_DT_UINT3 = 16,    /* 0..7                                       */
     /* OCP MX v1.0 FP6 element types (MXFP6 weights); one code per byte on input */
     HQ_DT_FP6_E2M3 = 17, /* 2 exponent bits (bias 1), 3 mantissa bits  */
-    HQ_DT_FP6_E3M2 = 18  /* 3 exponent bits (bias 3), 2 mantissa bits  */
+    HQ_DT_FP6_E3M2 = 18, /* 3 exponent bits (bias 3), 2 mantissa bits  */
+    /* zero-exponent floats e0mN: sign bit n, integer magnitude in bits 0..n-1,
+       values -(2^n - 1) .. 2^n - 1 (the symmetric integers of width n + 1) */
+    HQ_DT_E0M1 = 19,     /* -1..1, one code per byte                   */
+    HQ_DT_E0M2 = 20,     /* -3..3, one code per byte                   */
+    HQ_DT_E0M3 = 21,     /* -7..7, 4-bit codes in the INT4 word layout */
+    HQ_DT_E0M7 = 22      /* -127..127, one code per byte               */
 } hq_dtype;
 
 typedef enum hq_scale_gran {
@@ -136,6 +142,10 @@ typedef enum hq_moe_mode {
  *   BF16|FP16 UINT4      same as a_dtype, PER_GROUP_K  UINT4   NONE      a_dtype
  *   BF16|FP16 INT1|INT2|INT3  same as a_dtype, PER_GROUP_K  NONE  NONE  a_dtype (low-bit WnA16)
  *   BF16|FP16 UINT1|UINT2|UINT3  same, PER_GROUP_K     UINT4   NONE      a_dtype (low-bit WnA16)
+ *   BF16|FP16 E0M1|E0M2|E0M3  same as a_dtype, PER_GROUP_K  NONE  NONE  a_dtype (e0mN: the INT2/3/4 kernels)
+ *   BF16|FP16 E0M7       FP32, PER_CHANNEL             NONE    NONE      a_dtype (e0m7: the INT8 kernels)
+ *   BF16      FP8_E4M3   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MXFP8 weight-only)
+ *   BF16      FP6_E2M3|FP6_E3M2  E8M0, PER_GROUP_K, 32  NONE   NONE      BF16   (MXFP6 weight-only)
  *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    PER_TOKEN BF16
  *   INT8      INT8       FP32, PER_CHANNEL             NONE    PER_TOKEN BF16|INT32
  *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    MX_E8M0   BF16   (MXFP8 x MXFP4)
@@ -245,6 +255,14 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *      int8 per code [K][N], the two's-complement value for INT1..INT3,
  *      0 .. 2^b-1 for UINT1..UINT3; a code outside its width is
  *      HQ_ERR_INVALID_ARG.  Unsigned widths take UINT4 zero-points (below).
+ *      e0mN ("Humming wird angekuendigt": the zero-exponent float whose values
+ *      are the symmetric integers of its width): e0m3 in the 4-bit word layout
+ *      above, e0m1 / e0m2 / e0m7 one code per byte [K][N]; bit n is the sign,
+ *      bits 0..n-1 the magnitude.  The repack stores each code as the two's-
+ *      complement code of width n + 1 (INT2, INT3, INT4, INT8) and the kernels of
+ *      that width run it; a code with a bit above bit n is HQ_ERR_INVALID_ARG.
+ *      MXFP8 / MXFP6: E4M3 / E2M3 / E3M2 codes, one per byte [K][N] (FP6 in the
+ *      low six bits, a higher bit is HQ_ERR_INVALID_ARG); E8M0 [K/32][N].
  *   scale  [K/group][N] in w_scale_dtype (16-bit raw bits, uint8 for E8M0);
  *          PER_CHANNEL fp32: [N]; BLOCK_128x128 fp32: [K/128][ceil(N/128)]
  *   zp     UINT4: uint32 [K/group][ceil(N/8)]; column n = 8j+i in bits
@@ -269,6 +287,11 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *        1-bit plane (b = 1, 3), after it: uint32 [slots]; bit
  *          16*(j&1) + 4*t + (j>>1) holds its bit 0 (b = 1) or bit 2 (b = 3).
  *      Codes 2s and 2s+1 thus share an offset in the two 16-bit halves.
+ *      MXFP6: a lane's 32 codes of a chunk as one 192-bit group, code j at
+ *        bits 6j..6j+5; bits 0-127 of every slot in a 16-byte plane
+ *        [Np/16][K/128][64 lanes][16 B], bits 128-191 after it in an 8-byte
+ *        plane [Np/16][K/128][64 lanes][8 B].  MXFP8: the INT8 weight-only
+ *        layout below; both with the E8M0 layout below.
  *      INT8 and FP8_E4M3 with 8-bit activations (W8A8, FP8 blockwise):
  *      [Np/16][K/64][64 lanes][16 B]; lane l holds column 16*strip + (l & 15),
  *      k = 64*chunk + 16*(l >> 4) + j, j = 0..15.
