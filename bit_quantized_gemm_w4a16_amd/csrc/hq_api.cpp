@@ -115,18 +115,19 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
     I.E = d->num_experts ? d->num_experts : 1;
     I.G = d->group_size;
     const int a = d->a_dtype, w = d->w_dtype;
-    if (w == HQ_DT_INT4 && a == HQ_DT_BF16 && d->w_scale_dtype == HQ_DT_E8M0) {
+    if (w == HQ_DT_INT4 && (a == HQ_DT_BF16 || a == HQ_DT_FP16) && d->w_scale_dtype == HQ_DT_E8M0) {
         // MXINT4: two's-complement INT4 codes with one E8M0 scale per 32 K (the
         // FP4 weight-only path with an integer decode)
         I.kind = Kind::FP4_A16;
         I.i4 = true;
+        I.a_bf16 = a == HQ_DT_BF16;
         if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 is dense-only");
         if (d->w_scale_gran != HQ_GRAN_PER_GROUP_K || d->group_size != 32)
             return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 needs E8M0 scales per 32 K elements");
-        if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x MXINT4 takes no activation scale");
+        if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "16-bit A x MXINT4 takes no activation scale");
         if (d->K % 128) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 needs K %% 128 == 0 (K=%lld)", (long long)d->K);
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 takes no zero-points");
-        if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x MXINT4 outputs bf16");
+        if (d->out_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 weight-only outputs the activation dtype");
         I.G = 32;
     } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) &&
                (w == HQ_DT_INT4 || w == HQ_DT_UINT4 || lowbit_width(w) || (e0m_width(w) && e0m_width(w) <= 3))) {
@@ -158,8 +159,9 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 takes no zero-points");
         if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "MXFP4 paths output bf16");
         I.G = 32;
-    } else if (w == HQ_DT_FP4_E2M1 && a == HQ_DT_BF16 && !d->num_experts) {
+    } else if (w == HQ_DT_FP4_E2M1 && (a == HQ_DT_BF16 || a == HQ_DT_FP16) && !d->num_experts) {
         I.kind = Kind::FP4_A16;
+        I.a_bf16 = a == HQ_DT_BF16;
         I.nv = d->w_scale_dtype == HQ_DT_FP8_E4M3;
         if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x FP4 takes no activation scale");
         if (I.nv) {
@@ -172,7 +174,7 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         }
         if (d->K % 128) return set_error(HQ_ERR_UNSUPPORTED, "FP4 weights need K %% 128 == 0 (K=%lld)", (long long)d->K);
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "FP4 weights take no zero-points");
-        if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x FP4 outputs bf16");
+        if (d->out_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "FP4 weight-only outputs the activation dtype");
         I.G = I.nv ? 16 : 32;
     } else if (w == HQ_DT_FP4_E2M1 && (a == HQ_DT_FP8_E4M3 || a == HQ_DT_BF16)) {
         const bool moe = d->num_experts > 0;
@@ -214,19 +216,20 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
             return set_error(HQ_ERR_UNSUPPORTED, "W8A8 outputs bf16 or raw int32");
         I.out_i32 = d->out_dtype == HQ_DT_INT32;
         I.G = d->K;
-    } else if (a == HQ_DT_BF16 && (w == HQ_DT_FP6_E2M3 || w == HQ_DT_FP6_E3M2 ||
-                                   (w == HQ_DT_FP8_E4M3 && d->w_scale_dtype == HQ_DT_E8M0))) {
+    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) &&
+               (w == HQ_DT_FP6_E2M3 || w == HQ_DT_FP6_E3M2 || (w == HQ_DT_FP8_E4M3 && d->w_scale_dtype == HQ_DT_E8M0))) {
         // MX float weights: E4M3 (MXFP8) or E2M3 / E3M2 (MXFP6) codes with one
         // E8M0 scale per 32 K, converted to bf16 operands with the scale (exact)
         I.kind = Kind::FP4_A16;
         I.mxf = w == HQ_DT_FP8_E4M3 ? 1 : w == HQ_DT_FP6_E2M3 ? 2 : 3;
+        I.a_bf16 = a == HQ_DT_BF16;
         if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "MX float weights are dense-only");
         if (d->w_scale_dtype != HQ_DT_E8M0 || d->w_scale_gran != HQ_GRAN_PER_GROUP_K || d->group_size != 32)
             return set_error(HQ_ERR_UNSUPPORTED, "MXFP8 / MXFP6 weights need E8M0 scales per 32 K elements");
         if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MX float weight-only takes no activation scale");
         if (d->K % 128) return set_error(HQ_ERR_UNSUPPORTED, "MX float weights need K %% 128 == 0 (K=%lld)", (long long)d->K);
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MX float weights take no zero-points");
-        if (d->out_dtype != HQ_DT_BF16) return set_error(HQ_ERR_UNSUPPORTED, "bf16 x MX float weights outputs bf16");
+        if (d->out_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "MX float weight-only outputs the activation dtype");
         I.G = 32;
     } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && (w == HQ_DT_INT8 || w == HQ_DT_FP8_E4M3 || w == HQ_DT_E0M7)) {
         // (e0m7: sign and magnitude, converted at repack to INT8 -127..127)
@@ -269,6 +272,11 @@ static hq_status hip_status(hipError_t e, const char* what) {
     return set_error(HQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+hipError_t fp4_a16_launch(const DenseArgs& a, int kind, bool bf16) {
+    if (kind >= 3) return bf16 ? mxfw_launch_bf16(a, kind) : mxfw_launch_f16(a, kind);
+    return bf16 ? fp4w_launch_bf16(a, kind) : fp4w_launch_f16(a, kind);
+}
+
 static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
     switch (L.kind) {
         case Kind::WNA16: return hip_status(wna16_launch(a, L.a_bf16, L.zp), "hq_gemm(W4A16)");
@@ -279,7 +287,7 @@ static hq_status dense_launch(const LayerInfo& L, const DenseArgs& a) {
         case Kind::MXA_MX: return hip_status(mx_act_launch(a, L.a_fp4), L.a_fp4 ? "hq_gemm(W4A4-MXFP4)" : "hq_gemm(W4A8-MXFP8xMXFP4)");
         case Kind::FP8_BLOCK: return hip_status(fp8_block_launch(a), "hq_gemm(FP8-blockwise)");
         case Kind::FP4_A16:
-            return hip_status(fp4_a16_launch(a, L.nv ? 1 : L.i4 ? 2 : L.mxf ? 2 + L.mxf : 0),
+            return hip_status(fp4_a16_launch(a, L.nv ? 1 : L.i4 ? 2 : L.mxf ? 2 + L.mxf : 0, L.a_bf16),
                               L.nv ? "hq_gemm(NVFP4-A16)" : L.i4 ? "hq_gemm(MXINT4-A16)"
                               : L.mxf == 1 ? "hq_gemm(MXFP8-A16)" : L.mxf ? "hq_gemm(MXFP6-A16)" : "hq_gemm(MXFP4-A16)");
         default: return set_error(HQ_ERR_UNSUPPORTED, "this layer kind runs through hq_moe_gemm");

@@ -64,7 +64,12 @@ hipError_t w8a8_launch(const DenseArgs& a, bool raw_i32);
 hipError_t mx_act_launch(const DenseArgs& a, bool fp4_act);  // MX activations x MXFP4 weights
 hipError_t fp8_block_launch(const DenseArgs& a);              // FP8 W8A8 with blockwise scales
 hipError_t w8a16_launch(const DenseArgs& a, bool bf16, bool fp8);  // bf16 / fp16 A x INT8 / E4M3 weights, per-channel scale
-hipError_t fp4_a16_launch(const DenseArgs& a, int kind);      // bf16 A x MXFP4 (0) / NVFP4 (1) / MXINT4 (2)
+// 16-bit A (bf16, or fp16 when !bf16) x MXFP4 (0) / NVFP4 (1) / MXINT4 (2) / MXFP8 (3) / MXFP6 E2M3 (4) / E3M2 (5)
+hipError_t fp4_a16_launch(const DenseArgs& a, int kind, bool bf16);
+hipError_t fp4w_launch_bf16(const DenseArgs& a, int kind);  // kinds 0-2 (k_fp4w_bf16.hip)
+hipError_t fp4w_launch_f16(const DenseArgs& a, int kind);
+hipError_t mxfw_launch_bf16(const DenseArgs& a, int kind);  // kinds 3-5 (k_mxfw_bf16.hip)
+hipError_t mxfw_launch_f16(const DenseArgs& a, int kind);
 
 // MoE
 struct MoeLayout {  // byte offsets into the MoE workspace

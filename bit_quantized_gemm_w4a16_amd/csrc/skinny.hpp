@@ -97,8 +97,8 @@ struct SkinnyTraits {
     static constexpr bool MX = mx_mfma(F);               // E8M0 weight scales per 32 K
     static constexpr bool MXA = mx_act(F);               // E8M0 activation scales per 32 K
     // 4-, 6- or 8-bit codes -> bf16 operands under the lane's scale
-    static constexpr bool FP4B = F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || mxf8(F) || mxf6(F);
-    static constexpr int SB = F == Fmt::NVFP4_BF16 ? 128 : 64;  // scale bytes per strip and chunk
+    static constexpr bool FP4B = mxfp4w(F) || nvfp4(F) || mxint4w(F) || mxf8(F) || mxf6(F);
+    static constexpr int SB = nvfp4(F) ? 128 : 64;  // scale bytes per strip and chunk
     static constexpr int AROW = FmtTraits<F>::AROW;      // bytes of a row per 128-K chunk
     static constexpr int UPC = AROW / 16;                // 16-byte A units per 128-K chunk and row
     static constexpr int NB = FmtTraits<F>::BSTRIP / 1024;  // 16-byte weight loads per chunk and lane
@@ -474,13 +474,15 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                         for (int mt = 0; mt < MT; ++mt) acc2[t & 1][sp][mt] = mfma16<BF>(af[mt][t], b, acc2[t & 1][sp][mt]);
                     }
             } else if constexpr (FP4B) {
-                // e2m1 x (2^(E-127) or E4M3 group scale) -> exact bf16 operands, bf16 MFMA
+                // e2m1 x (2^(E-127) or E4M3 group scale) -> exact 16-bit operands (bf16,
+                // or fp16 with fp16 activations), MFMA of that type
+                constexpr bool BFO = !f16_operand(F);
                 const Frag8(&af)[MT][4] = ADIR ? afd[ADIR ? i : 0] : afb[i & 1];
 #pragma unroll
                 for (int sp = 0; sp < SPW; ++sp) {
                     const int j = ws * SPW + sp;
                     float sf0, sf1;
-                    if constexpr (F == Fmt::NVFP4_BF16) {
+                    if constexpr (nvfp4(F)) {
                         const uint32_t two = ((const uint16_t*)(lds + p.s_off))[((j * nsl + cl) * SB) / 2 + lane];
                         sf0 = __builtin_amdgcn_cvt_f32_fp8((int)two, 0);
                         sf1 = __builtin_amdgcn_cvt_f32_fp8((int)two, 1);
@@ -492,26 +494,30 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     if constexpr (mxf6(F)) {
                         const v6u x6 = v6u{w[i][sp][0][0], w[i][sp][0][1], w[i][sp][0][2], w[i][sp][0][3],
                                            w[i][sp][1][0], w[i][sp][1][1]};
-                        if constexpr (F == Fmt::MXF6E2_BF16)
+                        if constexpr (!mxf6e3(F) && BFO)
                             y6 = __builtin_bit_cast(v16u, __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(x6, sf0));
-                        else
+                        else if constexpr (BFO)
                             y6 = __builtin_bit_cast(v16u, __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(x6, sf0));
+                        else if constexpr (!mxf6e3(F))
+                            y6 = __builtin_bit_cast(v16u, __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(x6, sf0));
+                        else
+                            y6 = __builtin_bit_cast(v16u, __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(x6, sf0));
                     }
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         Frag8 b;
-                        if constexpr (F == Fmt::NVFP4_BF16) b = fp4_to_bf16_mul(w[i][sp][0][t], t < 2 ? sf0 : sf1);
-                        else if constexpr (F == Fmt::MXINT4_BF16) b = int4_to_bf16(w[i][sp][0][t], sf0);
-                        else if constexpr (mxf8(F)) b = fp8_to_bf16_scaled(w[i][sp][t >> 1], t & 1, sf0);
+                        if constexpr (nvfp4(F)) b = fp4_to_bf16_mul<BFO>(w[i][sp][0][t], t < 2 ? sf0 : sf1);
+                        else if constexpr (mxint4w(F)) b = int4_to_bf16<BFO>(w[i][sp][0][t], sf0);
+                        else if constexpr (mxf8(F)) b = fp8_to_bf16_scaled<BFO>(w[i][sp][t >> 1], t & 1, sf0);
                         else if constexpr (mxf6(F)) b.u = v4u{y6[4 * t], y6[4 * t + 1], y6[4 * t + 2], y6[4 * t + 3]};
-                        else b = fp4_to_bf16(w[i][sp][0][t], sf0);
+                        else b = fp4_to_bf16<BFO>(w[i][sp][0][t], sf0);
                         if constexpr (mxf8(F) || mxf6(F)) {
                             // (the scaled converts take only the scale's exponent: a zero scale gives no zeros)
 #pragma unroll
                             for (int e = 0; e < 4; ++e) b.u[e] = valid ? b.u[e] : 0u;
                         }
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) acc2[t & 1][sp][mt] = mfma16<true>(af[mt][t], b, acc2[t & 1][sp][mt]);
+                        for (int mt = 0; mt < MT; ++mt) acc2[t & 1][sp][mt] = mfma16<BFO>(af[mt][t], b, acc2[t & 1][sp][mt]);
                     }
                 }
             } else if constexpr (MX) {
@@ -649,9 +655,9 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
         else if constexpr (F == Fmt::W8A8_I8)
             return p.raw_i32 ? (uint32_t)acc[sp][mt][r] : f32_to_bf16_bits((float)acc[sp][mt][r] * asr[mt][r] * swn[sp]);
         else if constexpr (F == Fmt::W4A8_MX) return f32_to_bf16_bits(acc[sp][mt][r] * asr[mt][r]);
-        else if constexpr (F == Fmt::NVFP4_BF16) return f32_to_bf16_bits(acc[sp][mt][r] * *p.s2);
+        else if constexpr (nvfp4(F)) return f32_to_16<!f16_operand(F)>(acc[sp][mt][r] * *p.s2);
         else if constexpr (w8a16(F)) return f32_to_16<w8bf(F)>(acc[sp][mt][r] * swn[sp]);
-        else return f32_to_bf16_bits(acc[sp][mt][r]);
+        else return f32_to_16<!f16_operand(F)>(acc[sp][mt][r]);
     };
     const int es = partial || (F == Fmt::W8A8_I8 && p.raw_i32) ? 4 : 2;
     const int ldo = partial ? p.Np : p.N;
@@ -725,8 +731,8 @@ inline SkinnyLds skinny_lds(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) 
     } else if (mx_mfma(F)) {
         s = al(NS * cmax * 64);
         if (mx_act(F)) z = al(rows * cmax * 4);
-    } else if (F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || mxf8(F) || mxf6(F)) {
-        s = al(NS * cmax * (F == Fmt::NVFP4_BF16 ? 128 : 64));
+    } else if (mxfp4w(F) || nvfp4(F) || mxint4w(F) || mxf8(F) || mxf6(F)) {
+        s = al(NS * cmax * (nvfp4(F) ? 128 : 64));
     } else if (F == Fmt::W8A8_F8B) {
         s = al(NS * cmax * 4);
         z = al(((rows + 15) / 16 * 16) * cmax * 4);
@@ -743,8 +749,8 @@ inline int64_t skinny_lds_need(Fmt F, int64_t rows, int64_t cmax, int NS, int gc
 }
 
 constexpr bool skinny_a16(Fmt F) {
-    return F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 ||
-           F == Fmt::MXINT4_BF16 || w8a16(F) || mxf8(F) || mxf6(F);
+    return F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || mxfp4w(F) || nvfp4(F) || mxint4w(F) || w8a16(F) || mxf8(F) ||
+           mxf6(F);
 }
 
 // The eight-wave schedule with direct A loads: one strip per workgroup, K in
@@ -772,7 +778,7 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
     // 10.2 -> 9.7).  UINT4 and MXFP4 measured slower that way at 1..4 rows, and
     // every format at 9..16 rows (more A read from L2 than the split's partials
     // and finalize cost: fp16 UINT4 M=16 11.6 against 11.1 us).
-    const bool heavy = F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || w8a16(F) || mxf8(F) || mxf6(F);
+    const bool heavy = nvfp4(F) || mxint4w(F) || w8a16(F) || mxf8(F) || mxf6(F);
     const bool direct = mode == 2 || (mode == 0 && heavy && M <= 8 && nstrips >= 192 && skinny_direct_fits(F, M, K));
     if (direct) {
         p.ok = skinny_direct_fits(F, M, K) && force_splits <= 1;
@@ -1047,13 +1053,13 @@ hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
         // layout) at the front of the workspace, the MXFP8 tiles read them with the
         // E8M0 scales as they are, partial tiles follow
         const size_t wide = (size_t)(a.Np / 16) * (size_t)(a.K / 128) * 2048, off = (wide + 255) & ~(size_t)255;
-        hipError_t e = launch_widen_fp6(a.w, a.ws, F == Fmt::MXF6E3_BF16, a.Np, a.K, a.stream);
+        hipError_t e = launch_widen_fp6(a.w, a.ws, mxf6e3(F), a.Np, a.K, a.stream);
         if (e != hipSuccess) return e;
         plan_workspace(wide);
         plan_workspace_base(off);
         p.W = a.ws;
         p.part = (char*)a.ws + off;
-        e = launch_dense_plan<Fmt::MXF8_BF16>(pl, p, a.stream);
+        e = launch_dense_plan<f16_operand(F) ? Fmt::MXF8_F16 : Fmt::MXF8_BF16>(pl, p, a.stream);
         plan_workspace_base(0);
         return e;
     } else {

@@ -61,7 +61,8 @@
 namespace hq {
 
 enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B, MXFP4_BF16, NVFP4_BF16,
-                 MXINT4_BF16, W8A16_F16, W8A16_BF16, F8W_F16, F8W_BF16, MXF8_BF16, MXF6E2_BF16, MXF6E3_BF16 };
+                 MXINT4_BF16, W8A16_F16, W8A16_BF16, F8W_F16, F8W_BF16, MXF8_BF16, MXF6E2_BF16, MXF6E3_BF16,
+                 MXFP4_F16, NVFP4_F16, MXINT4_F16, MXF8_F16, MXF6E2_F16, MXF6E3_F16 };
 
 constexpr const char* fmt_name(Fmt F) {
     return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
@@ -70,7 +71,9 @@ constexpr const char* fmt_name(Fmt F) {
          : F == Fmt::NVFP4_BF16 ? "NVFP4_BF16" : F == Fmt::MXINT4_BF16 ? "MXINT4_BF16"
          : F == Fmt::W8A16_F16 ? "W8A16_F16" : F == Fmt::W8A16_BF16 ? "W8A16_BF16" : F == Fmt::F8W_F16 ? "F8W_F16"
          : F == Fmt::F8W_BF16 ? "F8W_BF16" : F == Fmt::MXF8_BF16 ? "MXF8_BF16" : F == Fmt::MXF6E2_BF16 ? "MXF6E2_BF16"
-         : "MXF6E3_BF16";
+         : F == Fmt::MXF6E3_BF16 ? "MXF6E3_BF16" : F == Fmt::MXFP4_F16 ? "MXFP4_F16" : F == Fmt::NVFP4_F16 ? "NVFP4_F16"
+         : F == Fmt::MXINT4_F16 ? "MXINT4_F16" : F == Fmt::MXF8_F16 ? "MXF8_F16" : F == Fmt::MXF6E2_F16 ? "MXF6E2_F16"
+         : "MXF6E3_F16";
 }
 // Formats whose activations carry OCP MX scales (E8M0 per 32 K, [rows][K/32]).
 constexpr bool mx_act(Fmt F) { return F == Fmt::W4A8_MXA || F == Fmt::W4A4_MX; }
@@ -102,19 +105,35 @@ template <> struct FmtTraits<Fmt::MXF8_BF16> { static constexpr int AROW = 256, 
 // 16-byte and an 8-byte plane per lane and chunk, two loads
 template <> struct FmtTraits<Fmt::MXF6E2_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::MXF6E3_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+// the same weight formats with fp16 activations (fp16 operands and output)
+template <> struct FmtTraits<Fmt::MXFP4_F16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::NVFP4_F16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::MXINT4_F16> { static constexpr int AROW = 256, BSTRIP = 1024; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::MXF8_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::MXF6E2_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::MXF6E3_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 // 8-bit weight-only formats: INT8 or FP8 (E4M3) codes in the same layout, per-channel fp32 scale
 constexpr bool f8w(Fmt F) { return F == Fmt::F8W_F16 || F == Fmt::F8W_BF16; }
 constexpr bool w8a16(Fmt F) { return F == Fmt::W8A16_F16 || F == Fmt::W8A16_BF16 || f8w(F); }
 constexpr bool w8bf(Fmt F) { return F == Fmt::W8A16_BF16 || F == Fmt::F8W_BF16; }
 // MX-scaled float weights with bf16 activations: E4M3 (MXFP8), E2M3 / E3M2 (MXFP6)
-constexpr bool mxf8(Fmt F) { return F == Fmt::MXF8_BF16; }
-constexpr bool mxf6(Fmt F) { return F == Fmt::MXF6E2_BF16 || F == Fmt::MXF6E3_BF16; }
+constexpr bool mxf8(Fmt F) { return F == Fmt::MXF8_BF16 || F == Fmt::MXF8_F16; }
+constexpr bool mxf6e3(Fmt F) { return F == Fmt::MXF6E3_BF16 || F == Fmt::MXF6E3_F16; }
+constexpr bool mxf6(Fmt F) { return F == Fmt::MXF6E2_BF16 || F == Fmt::MXF6E2_F16 || mxf6e3(F); }
+// FP4 / INT4 weight-only with a per-lane byte scale, bf16 or fp16 activations
+constexpr bool nvfp4(Fmt F) { return F == Fmt::NVFP4_BF16 || F == Fmt::NVFP4_F16; }
+constexpr bool mxfp4w(Fmt F) { return F == Fmt::MXFP4_BF16 || F == Fmt::MXFP4_F16; }
+constexpr bool mxint4w(Fmt F) { return F == Fmt::MXINT4_BF16 || F == Fmt::MXINT4_F16; }
+// the weight-only formats of the scaled converts taken with fp16 activations (fp16
+// operands, fp16 MFMA and output; the others of these families are bf16)
+constexpr bool f16_operand(Fmt F) {
+    return F == Fmt::MXFP4_F16 || F == Fmt::NVFP4_F16 || F == Fmt::MXINT4_F16 || F == Fmt::MXF8_F16 ||
+           F == Fmt::MXF6E2_F16 || F == Fmt::MXF6E3_F16;
+}
 // 8-bit weight codes in the INT8 weight-only layout (two 16-byte halves per lane and chunk)
 constexpr bool w8load(Fmt F) { return w8a16(F) || mxf8(F); }
 // e2m1 weights converted to bf16 operands with a per-lane scale (bf16 MFMA)
-constexpr bool fp4_bf16(Fmt F) {
-    return F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16;
-}
+constexpr bool fp4w(Fmt F) { return F == Fmt::MOE_MX || mxfp4w(F) || nvfp4(F) || mxint4w(F); }
 
 // Work description of one launch.  Dense launches leave the MoE fields null.
 struct TileArgs {
@@ -329,13 +348,22 @@ __device__ __forceinline__ Frag8 deq4_bf16_offset(uint32_t w) {
     return f;
 }
 
-// e2m1 x 2^(e-127) -> bf16, exact; 8 natural-order codes of one word.
+// e2m1 x 2^(e-127) -> bf16 (exact) or fp16 (exact inside fp16's range); 8
+// natural-order codes of one word.
+template <bool BF = true>
 __device__ __forceinline__ Frag8 fp4_to_bf16(uint32_t w, float scale) {
     Frag8 f;
-    f.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-    f.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-    f.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-    f.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    if constexpr (BF) {
+        f.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+        f.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+        f.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+        f.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    } else {
+        f.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0));
+        f.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1));
+        f.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2));
+        f.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3));
+    }
     return f;
 }
 
@@ -343,28 +371,32 @@ __device__ __forceinline__ Frag8 fp4_to_bf16(uint32_t w, float scale) {
 // scale): the scaled convert applies only the exponent of its scale operand, so
 // the codes are converted unscaled (exact) and each value is multiplied by s
 // in fp32; e2m1 x e4m3 has at most 5 significant bits, so the RNE conversion
-// back to bf16 is exact.
+// back to bf16 is exact (fp16 too: the products lie in [2^-10, 2688]).
+template <bool BF = true>
 __device__ __forceinline__ Frag8 fp4_to_bf16_mul(uint32_t w, float s) {
-    Frag8 f = fp4_to_bf16(w, 1.0f);
+    Frag8 f = fp4_to_bf16<true>(w, 1.0f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float lo = __uint_as_float(f.u[i] << 16) * s, hi = __uint_as_float(f.u[i] & 0xFFFF0000u) * s;
-        f.u[i] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+        f.u[i] = (uint32_t)f32_to_16<BF>(lo) | ((uint32_t)f32_to_16<BF>(hi) << 16);
     }
     return f;
 }
 
 // two's-complement INT4 x 2^(e-127) -> bf16, exact (at most 3 significant bits);
 // 8 natural-order codes of one word, in the element order of fp4_to_bf16
+template <bool BF = true>
 __device__ __forceinline__ Frag8 int4_to_bf16(uint32_t w, float scale) {
     typedef float f2v __attribute__((ext_vector_type(2)));
     typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2v __attribute__((ext_vector_type(2)));
     Frag8 f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int lo = (int)(w << (28 - 8 * i)) >> 28, hi = (int)(w << (24 - 8 * i)) >> 28;
         const f2v v = f2v{(float)lo * scale, (float)hi * scale};
-        f.u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2v));
+        if constexpr (BF) f.u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2v));
+        else f.u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v));
     }
     return f;
 }
@@ -417,13 +449,21 @@ __device__ __forceinline__ Frag8 deq8_fp8(uint32_t w0, uint32_t w1) {
 
 // E4M3 x 2^(E-127) -> bf16, exact for the E8M0 range the format reaches (4
 // significant bits); 8 codes (one K sub-step) of a lane's 16-byte half.
+template <bool BF = true>
 __device__ __forceinline__ Frag8 fp8_to_bf16_scaled(const v4u& half, int pair, float scale) {
     const uint32_t w0 = half[2 * pair], w1 = half[2 * pair + 1];
     Frag8 f;
-    f.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false));
-    f.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true));
-    f.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false));
-    f.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true));
+    if constexpr (BF) {
+        f.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false));
+        f.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true));
+        f.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false));
+        f.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true));
+    } else {
+        f.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, scale, false));
+        f.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, scale, true));
+        f.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, scale, false));
+        f.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, scale, true));
+    }
     return f;
 }
 
@@ -476,8 +516,8 @@ void tile_gemm_kernel(TileArgs p) {
     using T = FmtTraits<F>;
     using Acc = typename T::Acc;
     constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
-    constexpr bool NV = F == Fmt::NVFP4_BF16;             // E4M3 weight scales per 16 K
-    constexpr bool MX = mx_mfma(F) || F == Fmt::MOE_MX || F == Fmt::MXFP4_BF16 || F == Fmt::MXINT4_BF16 || NV || mxf8(F);  // byte scales per lane
+    constexpr bool NV = nvfp4(F);                         // E4M3 weight scales per 16 K
+    constexpr bool MX = mx_mfma(F) || fp4w(F) || mxf8(F);  // byte scales per lane
     static_assert(!mxf6(F), "MXFP6 reaches the tiles widened to MXFP8");
     constexpr bool MXA = mx_act(F);
     constexpr bool F8B = F == Fmt::W8A8_F8B;
@@ -785,11 +825,11 @@ void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
             for (int h = 0; h < NBH; ++h) bw[j][h] = *(const v4u*)(sB + (wn * NT + j) * T::BSTRIP + h * 1024 + lane * 16);
 
-        if constexpr (F == Fmt::WNA16_F16 || fp4_bf16(F) || w8load(F)) {
+        if constexpr (F == Fmt::WNA16_F16 || fp4w(F) || w8load(F)) {
             // 16-bit A with 4-bit weights decoded into the operand: fp16 (q - z) * s,
             // or e2m1 x (2^(E-127) or an E4M3 value) -> bf16 (exact)
-            constexpr bool MOE = fp4_bf16(F) || mxf8(F);  // bf16 operands under the lane's E8M0 or E4M3 scale
-            constexpr bool BFA = MOE || w8bf(F);  // bf16 MFMA (else fp16)
+            constexpr bool MOE = fp4w(F) || mxf8(F);  // 16-bit operands under the lane's E8M0 or E4M3 scale
+            constexpr bool BFA = (MOE && !f16_operand(F)) || w8bf(F);  // bf16 MFMA (else fp16)
             // A fragments read ahead (software pipeline): a whole sub-step, or
             // a ring of three for tall / wide wave tiles
             Frag8 afr[(NT >= 4 || MT > 8) ? 1 : 2][(NT >= 4 || MT > 8) ? 3 : MT];
@@ -821,11 +861,11 @@ void tile_gemm_kernel(TileArgs p) {
             }
             // weight operand of strip j for K sub-step t
             auto mkb = [&](int j, int tt) -> Frag8 {
-                if constexpr (NV) return fp4_to_bf16_mul(bw[j][0][tt], sf[j][tt >> 1]);
-                else if constexpr (F == Fmt::MXINT4_BF16) return int4_to_bf16(bw[j][0][tt], sf[j][0]);
-                else if constexpr (mxf8(F)) return fp8_to_bf16_scaled(bw[j][tt >> 1], tt & 1, sf[j][0]);
+                if constexpr (NV) return fp4_to_bf16_mul<BFA>(bw[j][0][tt], sf[j][tt >> 1]);
+                else if constexpr (mxint4w(F)) return int4_to_bf16<BFA>(bw[j][0][tt], sf[j][0]);
+                else if constexpr (mxf8(F)) return fp8_to_bf16_scaled<BFA>(bw[j][tt >> 1], tt & 1, sf[j][0]);
                 else if constexpr (w8a16(F)) return deq8<F>(bw[j][tt >> 1], tt & 1);
-                else if constexpr (MOE) return fp4_to_bf16(bw[j][0][tt], sf[j][0]);
+                else if constexpr (MOE) return fp4_to_bf16<BFA>(bw[j][0][tt], sf[j][0]);
                 else return deq4_f16_scaled(bw[j][0][tt] ^ wx, nb2[j], nh2[j], s2[j]);
             };
 #pragma unroll
@@ -1225,9 +1265,9 @@ void tile_gemm_kernel(TileArgs p) {
         else if constexpr (F == Fmt::W8A8_I8)
             return p.raw_i32 ? (uint32_t)acc[i][j][r] : f32_to_bf16_bits((float)acc[i][j][r] * asr[i][r] * swn[j]);
         else if constexpr (F == Fmt::W4A8_MX) return f32_to_bf16_bits(acc[i][j][r] * asr[i][r]);
-        else if constexpr (F == Fmt::NVFP4_BF16) return f32_to_bf16_bits(acc[i][j][r] * *p.s2);
+        else if constexpr (nvfp4(F)) return f32_to_16<!f16_operand(F)>(acc[i][j][r] * *p.s2);
         else if constexpr (w8a16(F)) return f32_to_16<w8bf(F)>(acc[i][j][r] * swn[j]);
-        else return f32_to_bf16_bits(acc[i][j][r]);
+        else return f32_to_16<!f16_operand(F)>(acc[i][j][r]);
     };
     if constexpr (F != Fmt::MOE_MX) {
         // dense: the tile's rows m0 .. m0 + mrows - 1 of the output, or of this K
@@ -1336,9 +1376,9 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(FinalizeArgs p) {
         }
     } else {
         if constexpr (F == Fmt::W4A8_MX) acc *= p.a_scale[m];
-        if constexpr (F == Fmt::NVFP4_BF16) acc *= *p.s2;
+        if constexpr (nvfp4(F)) acc *= *p.s2;
         if constexpr (w8a16(F)) acc *= *(const v4f*)(p.s_w + n);  // (s_w padded to a multiple of 16)
-        constexpr bool BF = F != Fmt::WNA16_F16 && F != Fmt::W8A16_F16 && F != Fmt::F8W_F16;
+        constexpr bool BF = F != Fmt::WNA16_F16 && F != Fmt::W8A16_F16 && F != Fmt::F8W_F16 && !f16_operand(F);
         for (int j = 0; j < cnt; ++j) ((uint16_t*)p.D)[o + j] = f32_to_16<BF>(acc[j]);
     }
 }
@@ -1432,8 +1472,7 @@ constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16 && !w8load(F) &
 // at M = 8192), or 128 x 256 tiles of 128 x 32 waves where 256 x 256 would not
 // cover the chip (a K step loads 48 KB instead of the 80 KB of 256 x 128).
 constexpr bool has_wide_tile(Fmt F) {
-    return F == Fmt::WNA16_F16 || F == Fmt::MXFP4_BF16 || F == Fmt::NVFP4_BF16 || F == Fmt::MXINT4_BF16 || w8load(F) ||
-           mxf6(F);
+    return F == Fmt::WNA16_F16 || mxfp4w(F) || nvfp4(F) || mxint4w(F) || w8load(F) || mxf6(F);
 }
 // INT8: 256 x 256 on 8 waves of 128 x 64, direct loads into two full stages
 // (M = 8192: 1126 us vs 1569 us for 256 x 128 with register-staged loads); the

@@ -145,11 +145,12 @@ def desc_w4a16(N, K, group_size=128, bf16=True, zp=False) -> hq_layer_desc:
                      zp_dtype=HQ_DT_UINT4 if zp else HQ_DT_NONE)
 
 
-def desc_mxf_a16(N, K, elem) -> hq_layer_desc:
-    """bf16 activations x MX float weights: elem "e4m3" (MXFP8), "e2m3" or "e3m2"
+def desc_mxf_a16(N, K, elem, bf16: bool = True) -> hq_layer_desc:
+    """16-bit activations x MX float weights: elem "e4m3" (MXFP8), "e2m3" or "e3m2"
     (MXFP6), one E8M0 scale per 32 K."""
+    a = HQ_DT_BF16 if bf16 else HQ_DT_FP16
     w = {"e4m3": HQ_DT_FP8_E4M3, "e2m3": HQ_DT_FP6_E2M3, "e3m2": HQ_DT_FP6_E3M2}[elem]
-    return make_desc(N, K, HQ_DT_BF16, w, HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K, 32, HQ_DT_BF16)
+    return make_desc(N, K, a, w, HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K, 32, a)
 
 
 def desc_e0m(N, K, n, group_size=128, bf16=True) -> hq_layer_desc:
@@ -189,19 +190,21 @@ def desc_fp8_blockwise(N, K) -> hq_layer_desc:
                      a_scale=HQ_ASCALE_PER_BLOCK128_F32)
 
 
-def desc_fp4_a16(N, K, nvfp4: bool) -> hq_layer_desc:
-    """bf16 activations x FP4 (e2m1) weights: MXFP4 (E8M0 per 32 K) or NVFP4 (E4M3 per
-    16 K and a per-tensor fp32 second-level scale)."""
-    d = make_desc(N, K, HQ_DT_BF16, HQ_DT_FP4_E2M1, HQ_DT_FP8_E4M3 if nvfp4 else HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K,
-                  16 if nvfp4 else 32, HQ_DT_BF16)
+def desc_fp4_a16(N, K, nvfp4: bool, bf16: bool = True) -> hq_layer_desc:
+    """16-bit activations (bf16, or fp16) x FP4 (e2m1) weights: MXFP4 (E8M0 per 32 K) or
+    NVFP4 (E4M3 per 16 K and a per-tensor fp32 second-level scale)."""
+    a = HQ_DT_BF16 if bf16 else HQ_DT_FP16
+    d = make_desc(N, K, a, HQ_DT_FP4_E2M1, HQ_DT_FP8_E4M3 if nvfp4 else HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K,
+                  16 if nvfp4 else 32, a)
     if nvfp4:
         d.scale2 = HQ_S2_PER_TENSOR_F32
     return d
 
 
-def desc_mxint4_a16(N, K) -> hq_layer_desc:
-    """bf16 activations x MXINT4 weights (two's-complement INT4, E8M0 scale per 32 K)."""
-    return make_desc(N, K, HQ_DT_BF16, HQ_DT_INT4, HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K, 32, HQ_DT_BF16)
+def desc_mxint4_a16(N, K, bf16: bool = True) -> hq_layer_desc:
+    """16-bit activations x MXINT4 weights (two's-complement INT4, E8M0 scale per 32 K)."""
+    a = HQ_DT_BF16 if bf16 else HQ_DT_FP16
+    return make_desc(N, K, a, HQ_DT_INT4, HQ_DT_E8M0, HQ_GRAN_PER_GROUP_K, 32, a)
 
 
 def desc_w8a16(N, K, bf16=True) -> hq_layer_desc:

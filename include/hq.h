@@ -144,18 +144,21 @@ typedef enum hq_moe_mode {
  *   BF16|FP16 UINT1|UINT2|UINT3  same, PER_GROUP_K     UINT4   NONE      a_dtype (low-bit WnA16)
  *   BF16|FP16 E0M1|E0M2|E0M3  same as a_dtype, PER_GROUP_K  NONE  NONE  a_dtype (e0mN: the INT2/3/4 kernels)
  *   BF16|FP16 E0M7       FP32, PER_CHANNEL             NONE    NONE      a_dtype (e0m7: the INT8 kernels)
- *   BF16      FP8_E4M3   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MXFP8 weight-only)
- *   BF16      FP6_E2M3|FP6_E3M2  E8M0, PER_GROUP_K, 32  NONE   NONE      BF16   (MXFP6 weight-only)
+ *   BF16|FP16 FP8_E4M3   E8M0, PER_GROUP_K, group 32   NONE    NONE      a_dtype (MXFP8 weight-only)
+ *   BF16|FP16 FP6_E2M3|FP6_E3M2  E8M0, PER_GROUP_K, 32  NONE   NONE      a_dtype (MXFP6 weight-only)
+ * (With fp16 activations the E8M0- and E4M3-scaled weights become fp16
+ * operands: exact while code x scale stays inside fp16's range, about
+ * 2^-24 .. 65504; outside it they round to subnormals or saturate.)
  *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    PER_TOKEN BF16
  *   INT8      INT8       FP32, PER_CHANNEL             NONE    PER_TOKEN BF16|INT32
  *   FP8_E4M3  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    MX_E8M0   BF16   (MXFP8 x MXFP4)
  *   FP4_E2M1  FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    MX_E8M0   BF16   (W4A4 MXFP4)
  *   FP8_E4M3  FP8_E4M3   FP32, BLOCK_128x128           NONE    PER_BLOCK128 BF16 (FP8 blockwise)
- *   BF16      FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (FP4 WnA16, MXFP4)
- *   BF16      FP4_E2M1   FP8_E4M3, PER_GROUP_K, grp 16 NONE    NONE      BF16   (NVFP4; scale2
+ *   BF16|FP16 FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    NONE      a_dtype (FP4 WnA16, MXFP4)
+ *   BF16|FP16 FP4_E2M1   FP8_E4M3, PER_GROUP_K, grp 16 NONE    NONE      a_dtype (NVFP4; scale2
  *                                                                               PER_TENSOR_F32)
  *   BF16      FP4_E2M1   E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MoE)
- *   BF16      INT4       E8M0, PER_GROUP_K, group 32   NONE    NONE      BF16   (MXINT4)
+ *   BF16|FP16 INT4       E8M0, PER_GROUP_K, group 32   NONE    NONE      a_dtype (MXINT4)
  *   BF16|FP16 INT8       FP32, PER_CHANNEL             NONE    NONE      a_dtype (INT8 weight-only)
  *   BF16|FP16 FP8_E4M3   FP32, PER_CHANNEL             NONE    NONE      a_dtype (FP8 weight-only)
  * FP4_E2M1 activations are packed two per byte along K, element k in the low

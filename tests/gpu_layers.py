@@ -10,12 +10,13 @@ from gpu_util import GATE, dev, empty, gate_error, to_f64
 
 FORMATS = ["wna16_f16_zp", "wna16_bf16_sym", "w4a8_mxfp4", "w8a8_bf16", "w8a8_raw", "w4a4_mx", "mxfp8_mx",
            "fp8_blockwise", "mxfp4_a16", "nvfp4_a16", "mxint4_a16", "w8a16_bf16", "w8a16_f16", "fp8w_bf16", "fp8w_f16",
-           "mxfp8_a16", "mxfp6e2_a16", "mxfp6e3_a16", "w3a16_uint3", "w2a16_int2", "w1a16_int1"]
+           "mxfp8_a16", "mxfp6e2_a16", "mxfp6e3_a16", "w3a16_uint3", "w2a16_int2", "w1a16_int1",
+           "mxfp4_a16_f16", "mxfp6e2_a16_f16"]
 # formats with 16-bit activations that every small-M schedule takes (the low-bit
 # widths have no eight-wave stream)
 A16_FORMATS = ["wna16_f16_zp", "wna16_bf16_sym", "mxfp4_a16", "nvfp4_a16", "mxint4_a16", "w8a16_bf16", "w8a16_f16",
-               "fp8w_bf16", "fp8w_f16", "mxfp8_a16", "mxfp6e2_a16", "mxfp6e3_a16"]
-MXF_ELEM = {"mxfp8_a16": "e4m3", "mxfp6e2_a16": "e2m3", "mxfp6e3_a16": "e3m2"}
+               "fp8w_bf16", "fp8w_f16", "mxfp8_a16", "mxfp6e2_a16", "mxfp6e3_a16", "mxfp4_a16_f16", "mxfp6e2_a16_f16"]
+MXF_ELEM = {"mxfp8_a16": "e4m3", "mxfp6e2_a16": "e2m3", "mxfp6e3_a16": "e3m2", "mxfp6e2_a16_f16": "e2m3"}
 LOWBIT = {"w3a16_uint3": (3, False), "w2a16_int2": (2, True), "w1a16_int1": (1, True)}
 
 
@@ -25,6 +26,7 @@ class Layer:
 
     def __init__(self, fmt, M, N, K, seed):
         self.fmt, self.M, self.N, self.K = fmt, M, N, K
+        f16 = fmt.endswith("_a16_f16")   # a weight-only format of the scaled converts with fp16 activations
         self.raw = fmt == "w8a8_raw"
         self.out_dt = torch.float16 if fmt == "wna16_f16_zp" else torch.bfloat16
         s2 = None
@@ -77,11 +79,13 @@ class Layer:
             self.ref = lambda r: ref(d["A"], d["w"], d["s_w"], a_bf16=bf, rows=r)
         elif fmt in MXF_ELEM:
             elem = MXF_ELEM[fmt]
-            d = syn.mxf_a16(seed, M, N, K, elem)
-            self.desc = hq.desc_mxf_a16(N, K, elem)
+            if f16:
+                self.out_dt = torch.float16
+            d = syn.mxf_a16(seed, M, N, K, elem, dtype=self.out_dt)
+            self.desc = hq.desc_mxf_a16(N, K, elem, bf16=not f16)
             packed = hq.hq_repack(self.desc, d["codes"], d["e"])
             A, sa, arow, srow = d["A"], None, K * 2, 0
-            self.ref = lambda r: oracle.gemm_mxf_a16(d["A"], d["codes"], d["e"], elem=elem, rows=r)
+            self.ref = lambda r: oracle.gemm_mxf_a16(d["A"], d["codes"], d["e"], elem=elem, a_bf16=not f16, rows=r)
         elif fmt in LOWBIT:
             bits, signed = LOWBIT[fmt]
             self.out_dt = torch.bfloat16 if signed else torch.float16
@@ -99,15 +103,17 @@ class Layer:
             self.ref = lambda r: oracle.gemm_mxint4_a16(d["A"], d["q"], d["e"], N=N, K=K, rows=r)
         else:
             nv = fmt == "nvfp4_a16"
-            d = syn.w4a16_fp4(seed, M, N, K, nvfp4=nv)
-            self.desc = hq.desc_fp4_a16(N, K, nv)
+            if f16:
+                self.out_dt = torch.float16
+            d = syn.w4a16_fp4(seed, M, N, K, nvfp4=nv, dtype=self.out_dt)
+            self.desc = hq.desc_fp4_a16(N, K, nv, bf16=not f16)
             if nv:
                 wp, sp, _, s2p = hq.hq_repack(self.desc, d["q"], d["s"], None, d["s2"])
                 packed, s2 = (wp, sp, None), s2p
             else:
                 packed = hq.hq_repack(self.desc, d["q"], d["s"])
             A, sa, arow, srow = d["A"], None, K * 2, 0
-            self.ref = lambda r: oracle.gemm_fp4_a16(d["A"], d["q"], d["s"], N=N, K=K, a_bf16=True, nvfp4=nv,
+            self.ref = lambda r: oracle.gemm_fp4_a16(d["A"], d["q"], d["s"], N=N, K=K, a_bf16=not f16, nvfp4=nv,
                                                      s2=d.get("s2"), rows=r)
         self.A = dev(A)
         self.sa = dev(sa) if sa is not None else None

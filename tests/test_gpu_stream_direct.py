@@ -33,7 +33,7 @@ def test_direct_stream_matches_the_oracle(fmt, M, K):
 
 
 HEAVY = {"nvfp4_a16", "mxint4_a16", "w8a16_bf16", "w8a16_f16", "fp8w_bf16", "fp8w_f16", "mxfp8_a16", "mxfp6e2_a16",
-         "mxfp6e3_a16"}
+         "mxfp6e3_a16", "mxfp6e2_a16_f16"}
 
 
 @pytest.mark.parametrize("fmt", A16_FORMATS)
