@@ -63,6 +63,8 @@ def lib():
         L.hq_oracle_gemm_wnlow.restype = C.c_int
         L.hq_oracle_gemm_wnlow.argtypes = [i64, i64, i64, i64, C.c_int, C.c_int, C.c_int, p, p, p, p, p, i64, p]
         L.hq_oracle_gemm_w4a8_mxfp4.restype = C.c_int
+        L.hq_oracle_gemm_wnwide.restype = C.c_int
+        L.hq_oracle_gemm_wnwide.argtypes = [i64, i64, i64, i64, C.c_int, C.c_int, C.c_int, p, p, p, p, p, i64, p]
         L.hq_oracle_gemm_w4a8_mxfp4.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
         L.hq_oracle_e2m1_encode.restype = C.c_uint
         L.hq_oracle_e2m1_encode.argtypes = [d]
@@ -339,6 +341,22 @@ def gemm_mxf_a16(A, codes, e8, *, elem: str, a_bf16: bool = True, rows=None):
                                       _ptr(_c(e8, np.uint8)), _ptr(r), R, _ptr(out))
     if rc:
         raise ValueError(f"oracle gemm_mxf_a16 failed ({rc})")
+    return out
+
+
+def gemm_wnwide(A, codes, s, z8=None, *, N, K, G, bits: int, a_bf16: bool, w_signed: bool, rows=None):
+    """WnA16 at 5-8 bits: one code per byte [K][N] (int8 for signed widths, uint8
+    otherwise), 16-bit group scales [K/G][N], 8-bit zero-points [K/G][N] for
+    unsigned widths; fp64."""
+    A = _c(A, np.uint16)
+    M = A.shape[0]
+    r, R = _rows(rows, M)
+    out = np.empty((R, N), dtype=np.float64)
+    rc = lib().hq_oracle_gemm_wnwide(M, N, K, G, int(a_bf16), bits, int(w_signed), _ptr(A),
+                                     _ptr(np.ascontiguousarray(codes).view(np.uint8)), _ptr(_c(s, np.uint16)),
+                                     _ptr(_c(z8, np.uint8)), _ptr(r), R, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle gemm_wnwide failed ({rc})")
     return out
 
 

@@ -340,6 +340,42 @@ int hq_oracle_gemm_wnlow(int64_t M, int64_t N, int64_t K, int64_t G, int a_bf16,
     return 0;
 }
 
+/* WnA16 at the widths above 4 bits ("Humming wird angekuendigt", section
+ * WnA16: INT1-INT8 weights, symmetric or with dynamic zero-points): one code per
+ * byte, codes[k][n] (int8 two's complement for signed widths, uint8 0 .. 2^bits-1
+ * for unsigned ones), 16-bit group scales s[K/G][N]; unsigned widths take one
+ * 8-bit zero-point per group and column, z8[K/G][N] (uint8):
+ *   W = code * s (signed) or (code - z) * s (unsigned),  D = A x W in fp64.
+ * Returns 3 when a code lies outside its width. */
+int hq_oracle_gemm_wnwide(int64_t M, int64_t N, int64_t K, int64_t G, int a_bf16, int bits, int w_signed,
+                          const uint16_t* A, const uint8_t* codes, const uint16_t* s, const uint8_t* z8,
+                          const int64_t* rows, int64_t nrows, double* out)
+{
+    if (bits < 5 || bits > 8 || G <= 0 || K % G || (!w_signed && !z8)) return 1;
+    const int lo = w_signed ? -(1 << (bits - 1)) : 0, hi = w_signed ? (1 << (bits - 1)) - 1 : (1 << bits) - 1;
+    for (int64_t i = 0; i < K * N; ++i) {
+        const int c = w_signed ? (int)(int8_t)codes[i] : (int)codes[i];
+        if (c < lo || c > hi) return 3;
+    }
+    int64_t R = rows ? nrows : M;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(R * K + 1));
+    if (!a) return 2;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k) a[r * K + k] = act16(a_bf16, A[row_of(rows, r) * K + k]);
+    memset(out, 0, sizeof(double) * (size_t)(R * N));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t g = k / G;
+            const int c = w_signed ? (int)(int8_t)codes[k * N + n] : (int)codes[k * N + n];
+            const int zero = w_signed ? 0 : (int)z8[g * N + n];
+            const double w = (double)(c - zero) * act16(a_bf16, s[g * N + n]);
+            for (int64_t r = 0; r < R; ++r) out[r * N + n] += a[r * K + k] * w;
+        }
+    free(a);
+    return 0;
+}
+
 /* W4A8-MXFP4: W[k][n] = e2m1(code) * 2^(E[k/32][n]-127),
  * A_real[m][k] = e4m3(qa[m][k]) * s_a[m];  D = A_real x W. */
 int hq_oracle_gemm_w4a8_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* qa,

@@ -294,3 +294,21 @@ def mxf_a16(seed, M, N, K, elem, dtype=torch.bfloat16, cfg=C12):
         codes = _rng(seed, cfg, T_Q, {"e2m3": 1, "e3m2": 2}[elem]).integers(0, 64, size=(K, N)).astype(np.uint8)
     return dict(A=activations(seed, cfg, M, K, dtype), codes=codes, e=e8m0_exponents(seed, cfg, (K // 32, N)))
 
+
+C13 = 13  # WnA16 at 5-8 bits
+
+
+def wnwide(seed, M, N, K, bits, signed, G=128, dtype=torch.float16, cfg=C13):
+    """WnA16 at 5-8 bits: one code per byte [K][N] uniform over the width (int8 two's
+    complement for signed widths, uint8 0 .. 2^bits - 1 otherwise), 16-bit group scales
+    |N(0, 0.002)| + 1e-4 (the finer steps of a wider code), 8-bit zero-points uniform
+    over the width for unsigned widths."""
+    lo, hi = (-(1 << (bits - 1)), (1 << (bits - 1)) - 1) if signed else (0, (1 << bits) - 1)
+    v = _rng(seed, cfg, T_Q, bits).integers(lo, hi + 1, size=(K, N), dtype=np.int64)
+    codes = v.astype(np.int8) if signed else v.astype(np.uint8)
+    out = dict(A=activations(seed, cfg, M, K, dtype), codes=codes,
+               s=abs_normal_scales(seed, cfg, T_S, (K // G, N), 0.002, 1e-4, dtype))
+    if not signed:
+        out["z"] = _rng(seed, cfg, T_Z, bits).integers(0, 1 << bits, size=(K // G, N), dtype=np.int64).astype(np.uint8)
+    return out
+

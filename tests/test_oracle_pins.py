@@ -993,3 +993,85 @@ def test_e0m_sign_and_magnitude(n):
         oracle.e0m(1 << (n + 1), n)
     lo = -(1 << n)
     assert sorted({oracle.e0m(c, n) for c in range(1 << (n + 1))}) == list(range(lo + 1, -lo))
+
+
+# ---- WnA16 at 5-8 bits (INT5-INT8, UINT5-UINT8 with 8-bit zero-points):
+# "Humming wird angekuendigt", section WnA16 ----
+
+@pytest.mark.parametrize("bits", [5, 6, 7, 8])
+def test_wnwide_on_4bit_codes_equals_w4a16(bits):
+    """Codes that fit four bits give the W4A16 oracle's result on the same codes in
+    the 4-bit container (signed: -8..7, symmetric; unsigned: 0..15 with zero-points
+    0..15 in the UINT4 container), bit for bit."""
+    M, N, K, G = 4, 24, 256, 128
+    rng = np.random.default_rng(bits)
+    for signed in (True, False):
+        d = syn.wnwide(bits, M, N, K, bits, signed, G=G)
+        if signed:
+            codes = rng.integers(-8, 8, size=(K, N)).astype(np.int8)
+            got = oracle.gemm_wnwide(d["A"], codes, d["s"], N=N, K=K, G=G, bits=bits, a_bf16=False, w_signed=True)
+            ref = oracle.gemm_wna16(d["A"], _pack_k_nibbles(codes), d["s"], None, N=N, K=K, G=G, a_bf16=False,
+                                    w_signed=True)
+        else:
+            codes = rng.integers(0, 16, size=(K, N)).astype(np.uint8)
+            z8 = rng.integers(0, 16, size=(K // G, N)).astype(np.uint8)
+            zw = np.zeros((K // G, (N + 7) // 8), np.uint32)
+            for n in range(N):
+                zw[:, n // 8] |= z8[:, n].astype(np.uint32) << np.uint32(4 * (n % 8))
+            got = oracle.gemm_wnwide(d["A"], codes, d["s"], z8, N=N, K=K, G=G, bits=bits, a_bf16=False,
+                                     w_signed=False)
+            ref = oracle.gemm_wna16(d["A"], _pack_k_nibbles(codes.astype(np.int8)), d["s"], zw, N=N, K=K, G=G,
+                                    a_bf16=False, w_signed=False)
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_wnwide_uint8_with_zero_128_is_int8():
+    """UINT8 codes q with every zero-point 128 equal INT8 codes q - 128, bit for bit."""
+    M, N, K, G = 3, 16, 256, 128
+    d = syn.wnwide(1, M, N, K, 8, False, G=G)
+    z = np.full((K // G, N), 128, np.uint8)
+    got = oracle.gemm_wnwide(d["A"], d["codes"], d["s"], z, N=N, K=K, G=G, bits=8, a_bf16=False, w_signed=False)
+    q = (d["codes"].astype(np.int16) - 128).astype(np.int8)
+    ref = oracle.gemm_wnwide(d["A"], q, d["s"], N=N, K=K, G=G, bits=8, a_bf16=False, w_signed=True)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_wnwide_int8_one_group_per_column_is_int8_weight_only():
+    """INT8 with one group spanning K (G = K) is INT8 weight-only with the group
+    scale as the column scale (the other oracle scales the sum, this one each term)."""
+    M, N, K = 4, 32, 256
+    d = syn.wnwide(2, M, N, K, 8, True, G=K, dtype=torch.bfloat16)
+    got = oracle.gemm_wnwide(d["A"], d["codes"], d["s"], N=N, K=K, G=K, bits=8, a_bf16=True, w_signed=True)
+    sw = torch16(d["s"], torch.bfloat16)[0].astype(np.float32)
+    ref = oracle.gemm_w8a16(d["A"], d["codes"], sw, a_bf16=True)
+    assert rel_err(got, ref) < 1e-13
+
+
+@pytest.mark.parametrize("bits", [5, 8])
+@pytest.mark.parametrize("signed", [True, False])
+def test_wnwide_exact_rationals_and_range(bits, signed):
+    M, N, K, G = 2, 8, 256, 128
+    d = syn.wnwide(3, M, N, K, bits, signed, G=G)
+    lo, hi = (-(1 << (bits - 1)), (1 << (bits - 1)) - 1) if signed else (0, (1 << bits) - 1)
+    codes = d["codes"].copy()
+    codes[0, :] = lo
+    codes[1, :] = hi
+    got = oracle.gemm_wnwide(d["A"], codes, d["s"], d.get("z"), N=N, K=K, G=G, bits=bits, a_bf16=False,
+                             w_signed=signed)
+    a = torch16(d["A"], torch.float16)
+    s = torch16(d["s"], torch.float16)
+    cv = codes.astype(np.int64)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                z = 0 if signed else int(d["z"][k // G, n])
+                acc += Fraction(float(a[m, k])) * (int(cv[k, n]) - z) * Fraction(float(s[k // G, n]))
+            assert abs(got[m, n] - float(acc)) <= 1e-13 * max(abs(float(acc)), 1e-30)
+    for bad in ((hi + 1, lo - 1) if signed else (hi + 1,)):
+        if bits == 8 and (bad > 255 or bad < -128 or (signed and bad > 127)):
+            continue   # (an 8-bit byte cannot hold the value)
+        c = codes.copy()
+        c[5, 3] = bad
+        with pytest.raises(ValueError):
+            oracle.gemm_wnwide(d["A"], c, d["s"], d.get("z"), N=N, K=K, G=G, bits=bits, a_bf16=False, w_signed=signed)
