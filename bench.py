@@ -174,6 +174,45 @@ class DenseWnLow(DenseW4A16):
                     sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
 
 
+class DenseWnWide(DenseWnLow):
+    """5-8-bit WnA16 at the dense W4A16 layer's shape (N=4096, K=7168, group 128):
+    UINT5-8 codes with 8-bit zero-points and fp16, or INT5-8 codes and bf16."""
+
+    def __init__(self, bits, signed, N=4096, K=7168, G=128, Mmax=8192, sweep=SWEEP):
+        self.N, self.K, self.G, self.Mmax, self.sweep = N, K, G, Mmax, sweep
+        self.bits, self.signed, self.bf16, self.zp = bits, signed, signed, not signed
+        self.dtype = "bf16" if self.bf16 else "fp16"
+        self.name = f"dense_w{bits}a16_{'int' if signed else 'uint'}{bits}_{self.dtype}_N{N}_K{K}"
+        t = torch.bfloat16 if self.bf16 else torch.float16
+        log(f"[bench] generating {self.name}")
+        d = syn.wnwide(0, Mmax, N, K, bits, signed, G=G, dtype=t)
+        self.host = d
+        self.desc = hq.desc_wnwide(N, K, bits, signed, G, bf16=self.bf16)
+        wp, sp, zpk = hq.hq_repack(self.desc, d["codes"], d["s"], d.get("z"))
+        self.wbytes = wp.size + sp.size + (zpk.size if zpk is not None else 0)
+        self.copies = _copies((dev(wp), dev(sp), dev(zpk) if zpk is not None else None), self.wbytes)
+        self.A = dev(d["A"])
+        self.D = torch.empty(Mmax * N * 2, dtype=torch.uint8, device="cuda")
+        self.ws_bytes = max(hq.hq_workspace_bytes(self.desc, m) for m in sweep)
+        self.ws = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def kernel_of(self, M):
+        f = f"WNA16_{self.dtype.upper()}"
+        if M <= 64:
+            return (f"skinny_kernel<{f},w{self.bits}> (M<=64)", "hbm")
+        return (f"widen_wide_kernel<{self.bits}> + tile_gemm_kernel<W16_{self.dtype.upper()}> (M>64)",
+                "mfma" if M >= 128 else "hbm")
+
+    def cpu_baseline(self, budget_s=8.0):
+        import oracle
+        d = self.host
+        f = lambda rows: oracle.gemm_wnwide(d["A"], d["codes"], d["s"], d.get("z"), N=self.N, K=self.K, G=self.G,
+                                            bits=self.bits, a_bf16=self.bf16, w_signed=self.signed, rows=rows)
+        n, dt = _timed_oracle(f, lambda n: np.arange(min(n, self.Mmax)), budget_s)
+        return dict(value=round(self.flops(n) / dt / 1e12, 6), unit="TFLOP/s", cores=_cores(), kind="oracle",
+                    sample=f"{n} output rows x N={self.N} x K={self.K}, fp64 accumulation, {dt:.1f} s")
+
+
 class DenseW4A8:
     """Dense W4A8-MXFP4: tokenwise e4m3 activations (quantised on the GPU, untimed)."""
 
@@ -740,12 +779,14 @@ WORKLOADS = {
     "fp8w": lambda: DenseW8A16(fp8=True),
     "w3a16": lambda: DenseWnLow(3, False),
     "w2a16": lambda: DenseWnLow(2, True),
+    "w8a16g": lambda: DenseWnWide(8, False),
+    "w5a16": lambda: DenseWnWide(5, True),
     "mxfp8a16": lambda: DenseMXF("e4m3"),
     "mxfp6a16": lambda: DenseMXF("e2m3"),
 }
 # the workloads the default run measures besides the headline one (c2)
 DEFAULT_EXTRA = ["c3", "c4", "c5", "w4a4", "w4a8mx", "fp8b", "mxfp4a16", "nvfp4a16", "mxint4a16", "w8a16", "fp8w",
-                 "w3a16", "w2a16", "mxfp8a16", "mxfp6a16"]
+                 "w3a16", "w2a16", "w8a16g", "w5a16", "mxfp8a16", "mxfp6a16"]
 
 
 # ---------------------------------------------------------------------------
@@ -1123,6 +1164,8 @@ _DRY = {
     "fp8w": lambda: hq.desc_fp8w_a16(4096, 7168, bf16=True),
     "w3a16": lambda: hq.desc_wnlow(4096, 7168, 3, False, 128, bf16=False),
     "w2a16": lambda: hq.desc_wnlow(4096, 7168, 2, True, 128, bf16=True),
+    "w8a16g": lambda: hq.desc_wnwide(4096, 7168, 8, False, 128, bf16=False),
+    "w5a16": lambda: hq.desc_wnwide(4096, 7168, 5, True, 128, bf16=True),
     "mxfp8a16": lambda: hq.desc_mxf_a16(4096, 7168, "e4m3"),
     "mxfp6a16": lambda: hq.desc_mxf_a16(4096, 7168, "e2m3"),
 }

@@ -74,6 +74,20 @@ static int e0m_width(int w) {
     }
 }
 
+// code width and signedness of the 5-8-bit WnA16 dtypes (0 for the others; INT8
+// is one of them only with 16-bit group scales)
+static int wide_width(int w, int scale_dtype, bool* is_signed) {
+    *is_signed = w == HQ_DT_INT5 || w == HQ_DT_INT6 || w == HQ_DT_INT7 || w == HQ_DT_INT8;
+    switch (w) {
+        case HQ_DT_INT5: case HQ_DT_UINT5: return 5;
+        case HQ_DT_INT6: case HQ_DT_UINT6: return 6;
+        case HQ_DT_INT7: case HQ_DT_UINT7: return 7;
+        case HQ_DT_UINT8: return 8;
+        case HQ_DT_INT8: return scale_dtype == HQ_DT_BF16 || scale_dtype == HQ_DT_FP16 ? 8 : 0;
+        default: return 0;
+    }
+}
+
 // code width of the low-bit weight dtypes (0 for the others)
 int lowbit_width(int w) {
     switch (w) {
@@ -115,6 +129,7 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
     I.E = d->num_experts ? d->num_experts : 1;
     I.G = d->group_size;
     const int a = d->a_dtype, w = d->w_dtype;
+    bool wide_signed = false;
     if (w == HQ_DT_INT4 && (a == HQ_DT_BF16 || a == HQ_DT_FP16) && d->w_scale_dtype == HQ_DT_E8M0) {
         // MXINT4: two's-complement INT4 codes with one E8M0 scale per 32 K (the
         // FP4 weight-only path with an integer decode)
@@ -129,6 +144,23 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         if (d->zp_dtype != HQ_DT_NONE) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 takes no zero-points");
         if (d->out_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "MXINT4 weight-only outputs the activation dtype");
         I.G = 32;
+    } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) && wide_width(w, d->w_scale_dtype, &wide_signed)) {
+        // WnA16 at 5-8 bits: the low nibble in the 4-bit layout, the high bits in
+        // planes; 16-bit group scales, UINT8 zero-points for unsigned codes
+        I.kind = Kind::WNA16;
+        I.a_bf16 = a == HQ_DT_BF16;
+        I.bits = wide_width(w, d->w_scale_dtype, &wide_signed);
+        I.zp = I.zp8 = !wide_signed;
+        if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "WnA16 at 5-8 bits is dense-only");
+        if (d->w_scale_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "WnA16 scale dtype must equal the activation dtype");
+        if (d->w_scale_gran != HQ_GRAN_PER_GROUP_K) return set_error(HQ_ERR_UNSUPPORTED, "WnA16 needs per-group scales");
+        if (d->group_size < 128 || d->group_size % 128 || d->K % d->group_size)
+            return set_error(HQ_ERR_UNSUPPORTED, "WnA16 group_size=%d must be a multiple of 128 dividing K=%lld",
+                             d->group_size, (long long)d->K);
+        if (d->zp_dtype != (I.zp8 ? HQ_DT_UINT8 : HQ_DT_NONE))
+            return set_error(HQ_ERR_UNSUPPORTED, "zero-points: unsigned 5-8-bit codes need UINT8 zero-points, signed codes none");
+        if (d->a_scale != HQ_ASCALE_NONE) return set_error(HQ_ERR_UNSUPPORTED, "WnA16 takes no activation scale");
+        if (d->out_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "WnA16 output dtype must equal the activation dtype");
     } else if ((a == HQ_DT_BF16 || a == HQ_DT_FP16) &&
                (w == HQ_DT_INT4 || w == HQ_DT_UINT4 || lowbit_width(w) || (e0m_width(w) && e0m_width(w) <= 3))) {
         // W4A16, the low-bit widths on the same kernels (1-3-bit codes widened
@@ -438,6 +470,25 @@ hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale,
             if (c[i] >> (L.e0m + 1))
                 return set_error(HQ_ERR_INVALID_ARG, "e0m%d code 0x%02x at k=%lld n=%lld has bits above bit %d", L.e0m,
                                  c[i], (long long)(i / L.N), (long long)(i % L.N), L.e0m);
+    } else if (L.kind == Kind::WNA16 && L.bits > 4 && L.bits < 8) {
+        // 5-7-bit codes, one per byte: each must lie inside its width
+        const int lo = L.zp8 ? 0 : -(1 << (L.bits - 1)), hi = L.zp8 ? (1 << L.bits) - 1 : (1 << (L.bits - 1)) - 1;
+        const int8_t* c = (const int8_t*)w;
+        for (int64_t i = 0; i < L.K * L.N; ++i) {
+            const int v = L.zp8 ? (int)(uint8_t)c[i] : (int)c[i];
+            if (v < lo || v > hi)
+                return set_error(HQ_ERR_INVALID_ARG, "code %d at k=%lld n=%lld outside the %d-bit width", v,
+                                 (long long)(i / L.N), (long long)(i % L.N), L.bits);
+        }
+        if (L.zp8) {
+            // UINT8 zero-points [K/G][N]: inside the codes' width too
+            const uint8_t* z = (const uint8_t*)zp;
+            if (!z) return set_error(HQ_ERR_INVALID_ARG, "zero-points required");
+            for (int64_t i = 0; i < (L.K / L.G) * L.N; ++i)
+                if (z[i] >> L.bits)
+                    return set_error(HQ_ERR_INVALID_ARG, "zero-point %d at group %lld n=%lld outside the %d-bit width",
+                                     (int)z[i], (long long)(i / L.N), (long long)(i % L.N), L.bits);
+        }
     } else if (L.kind == Kind::WNA16 && L.bits < 4) {
         // low-bit codes, one per byte: each must lie inside its width
         const int lo = L.zp ? 0 : -(1 << (L.bits - 1)), hi = L.zp ? (1 << L.bits) - 1 : (1 << (L.bits - 1)) - 1;

@@ -36,6 +36,7 @@ struct LayerInfo {
     bool w_fp8;    // W8A16: E4M3 weight codes instead of INT8
     int mxf;       // FP4_A16: MX float codes, 1 = E4M3 (MXFP8), 2 = E2M3, 3 = E3M2 (MXFP6); 0 = none
     int bits;      // WNA16: weight code width (4, or 1 / 2 / 3 for the low-bit widths)
+    bool zp8;      // WNA16 at 5-8 bits: unsigned codes with UINT8 zero-points
     int e0m;       // WNA16 / W8A16: e0mN codes (n = 1, 2, 3 or 7; 0 = none), converted at repack to the
                    // two's-complement container of width n + 1
     bool invariant;        // HQ_FLAG_BATCH_INVARIANT

@@ -113,6 +113,44 @@ void repack_fp6(const LayerInfo& L, const uint8_t* w, uint8_t* out) {
             }
 }
 
+// 5-8-bit codes (one per byte, [K][N]): the low nibble of every code in the
+// 4-bit layout (pair order), then the high bits: width 5-7 as the low-bit planes
+// of a (bits - 4)-bit code (2-bit plane, then 1-bit plane), width 8 as a second
+// 4-bit word set.  Signed codes keep their two's-complement bits.
+void repack_wide(const LayerInfo& L, const uint8_t* w, uint8_t* out) {
+    const int64_t N = L.N, K = L.K, nst = L.Np / 16, nc = K / 128;
+    const int e = L.bits - 4;
+    std::vector<uint32_t> lo((size_t)(K / 8 * N), 0u), hi4(e == 4 ? (size_t)(K / 8 * N) : 0, 0u);
+    std::vector<int8_t> hi((size_t)(e < 4 ? K * N : 0));
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            const uint32_t c = w[k * N + n];
+            lo[(size_t)((k / 8) * N + n)] |= (c & 15u) << (4 * (k % 8));
+            if (e == 4) hi4[(size_t)((k / 8) * N + n)] |= ((c >> 4) & 15u) << (4 * (k % 8));
+            else hi[(size_t)(k * N + n)] = (int8_t)((c >> 4) & ((1u << e) - 1u));
+        }
+    repack_4bit(L, lo.data(), out, true);
+    uint8_t* o2 = out + (size_t)(nst * nc * 1024);
+    if (e == 4) {
+        repack_4bit(L, hi4.data(), o2, true);
+    } else {
+        LayerInfo Lh = L;
+        Lh.bits = e;
+        repack_lowbit(Lh, hi.data(), o2);
+    }
+}
+
+// UINT8 zero-points [K/G][N] -> [Np/16][K/G][16] bytes (padding columns 0)
+void repack_zero8(const LayerInfo& L, const uint8_t* z, uint8_t* out) {
+    const int64_t N = L.N, ng = L.K / L.G, nst = L.Np / 16;
+    for (int64_t st = 0; st < nst; ++st)
+        for (int64_t g = 0; g < ng; ++g)
+            for (int i = 0; i < 16; ++i) {
+                const int64_t n = st * 16 + i;
+                out[(st * ng + g) * 16 + i] = n < N ? z[g * N + n] : 0;
+            }
+}
+
 void repack_int8(const LayerInfo& L, const int8_t* w, int8_t* out) {
     const int64_t N = L.N, K = L.K, nst = L.Np / 16, nc = K / 64;
     for (int64_t e = 0; e < L.E; ++e) {
@@ -229,9 +267,12 @@ void packed_sizes(const LayerInfo& L, size_t* w, size_t* s, size_t* z, size_t* s
         case Kind::WNA16:
             // 4-bit: 16 B per lane and chunk; low-bit: an 8-B plane (widths 2, 3)
             // and a 4-B plane (widths 1, 3)
-            *w = E * nst * (size_t)(L.K / 128) * (L.bits == 4 ? 1024 : (L.bits >= 2 ? 512 : 0) + (L.bits != 2 ? 256 : 0));
+            // (5-8 bits: the 4-bit word set plus the high-bit planes, or a second word set)
+            *w = E * nst * (size_t)(L.K / 128) *
+                 (L.bits == 4 ? 1024 : L.bits < 4 ? (L.bits >= 2 ? 512 : 0) + (L.bits != 2 ? 256 : 0)
+                                : 1024 + (L.bits == 8 ? 1024 : (L.bits >= 6 ? 512 : 0) + (L.bits != 6 ? 256 : 0)));
             *s = E * nst * (size_t)(L.K / L.G) * 16 * 2;
-            if (L.zp) *z = E * nst * (size_t)(L.K / L.G) * 8;
+            if (L.zp) *z = E * nst * (size_t)(L.K / L.G) * (L.zp8 ? 16 : 8);
             break;
         case Kind::W4A8_MX:
         case Kind::MXA_MX:
@@ -296,10 +337,12 @@ void repack_all(const LayerInfo& L, const void* w, const void* s, const void* z,
                 conv = e0m_to_int(L, w);
                 w = conv.data();
             }
-            if (L.bits < 4) repack_lowbit(L, (const int8_t*)w, (uint8_t*)w_out);
+            if (L.bits > 4) repack_wide(L, (const uint8_t*)w, (uint8_t*)w_out);
+            else if (L.bits < 4) repack_lowbit(L, (const int8_t*)w, (uint8_t*)w_out);
             else repack_4bit(L, (const uint32_t*)w, (uint8_t*)w_out, true);
             repack_scale16(L, (const uint16_t*)s, (uint16_t*)s_out, L.a_bf16 ? 0x3F80 : 0x3C00);
-            if (L.zp) repack_zero4(L, (const uint32_t*)z, (uint64_t*)z_out);
+            if (L.zp8) repack_zero8(L, (const uint8_t*)z, (uint8_t*)z_out);
+            else if (L.zp) repack_zero4(L, (const uint32_t*)z, (uint64_t*)z_out);
             break;
         }
         case Kind::W4A8_MX:

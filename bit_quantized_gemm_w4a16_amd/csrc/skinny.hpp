@@ -133,7 +133,9 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     // WB < 4 (W4A16 formats): 1-3-bit codes in bit planes, widened to 4-bit words
     // after the load (a 2-bit plane of 8 B and a 1-bit plane of 4 B per lane and chunk)
     static_assert(WB == 4 || Tr::WNA16, "low-bit codes: W4A16 formats");
-    constexpr int LPC = WB == 4 ? NB : WB == 3 ? 2 : 1;  // weight loads per chunk and lane
+    // WB > 4 (W4A16 formats): 5-8-bit codes as the 4-bit word set plus the high
+    // bits (a second word set for 8 bits, the low-bit planes for 5-7)
+    constexpr int LPC = WB == 4 ? NB : WB == 3 ? 2 : WB < 4 ? 1 : WB == 7 ? 3 : 2;  // weight loads per chunk and lane
     constexpr int NLOAD = SPW * CPW * LPC;  // weight loads per wave and batch
     static_assert(NLOAD < 64, "vmcnt counts at most 63 loads");
     constexpr bool ADIR = NW == 8;  // A fragments straight from global memory
@@ -167,6 +169,10 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     const char* wp2[SPW];  // low-bit planes of the strip, at this lane
     const char* wp1[SPW];
     const size_t plane2 = WB >= 2 && WB < 4 ? (size_t)nstrips * p.nc * 512 : 0;  // bytes of the 2-bit plane
+    // 5-8 bits: the high planes follow the 4-bit word set
+    const size_t lowset = WB > 4 ? (size_t)nstrips * p.nc * 1024 : 0;
+    const size_t plane2w = WB == 6 || WB == 7 ? (size_t)nstrips * p.nc * 512 : 0;
+    const v4u* wh4[SPW];
     // MXFP6: a 16-byte plane (codes 0-20 of the lane's 32, and two bits of code 21)
     // then an 8-byte plane (the rest) per lane and chunk
     const char* f6b[SPW];
@@ -175,14 +181,16 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
         wstrip[sp] = strip_base + ws * SPW + sp;
         const int st = wstrip[sp] < nstrips ? wstrip[sp] : nstrips - 1;
         wsrc[sp] = (const v4u*)(Wb + (size_t)st * p.nc * FmtTraits<F>::BSTRIP) + lane;
-        wp2[sp] = Wb + (size_t)st * p.nc * 512 + lane * 8;
-        wp1[sp] = Wb + plane2 + (size_t)st * p.nc * 256 + lane * 4;
+        wp2[sp] = Wb + lowset + (size_t)st * p.nc * 512 + lane * 8;
+        wp1[sp] = Wb + lowset + (WB > 4 ? plane2w : plane2) + (size_t)st * p.nc * 256 + lane * 4;
+        wh4[sp] = (const v4u*)(Wb + lowset + (size_t)st * p.nc * 1024) + lane;
         if constexpr (mxf6(F)) {
             wsrc[sp] = (const v4u*)(Wb + (size_t)st * p.nc * 1024) + lane;
             f6b[sp] = Wb + (size_t)nstrips * p.nc * 1024 + (size_t)st * p.nc * 512 + lane * 8;
         }
     }
     v4u w[CPW][SPW][NB];
+    v4u wh[WB > 4 ? CPW : 1][SPW];  // 5-8 bits: the high bits of the chunk
     constexpr int CH = CPW / 2;
     auto issue_w = [&](int i) {
 #pragma unroll
@@ -195,6 +203,20 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
             } else if constexpr (WB == 4) {
 #pragma unroll
                 for (int h = 0; h < NB; ++h) w[i][sp][h] = ld_nt(wsrc[sp] + (c * NB + h) * 64);
+            } else if constexpr (WB > 4) {
+                w[i][sp][0] = ld_nt(wsrc[sp] + c * 64);
+                if constexpr (WB == 8) {
+                    wh[i][sp] = ld_nt(wh4[sp] + c * 64);
+                } else {
+                    v4u x = v4u{0u, 0u, 0u, 0u};
+                    if constexpr (WB == 6 || WB == 7) {
+                        const v2u a = __builtin_nontemporal_load((const v2u*)(wp2[sp] + c * 512));
+                        x[0] = a[0];
+                        x[1] = a[1];
+                    }
+                    if constexpr (WB != 6) x[2] = __builtin_nontemporal_load((const uint32_t*)(wp1[sp] + c * 256));
+                    wh[i][sp] = x;
+                }
             } else {
                 // 2-bit plane into words 0-1, 1-bit plane into word 2
                 v4u x = v4u{0u, 0u, 0u, 0u};
@@ -252,13 +274,12 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
             for (int j = 0; j < p.NS; ++j) {
                 const int st = strip_base + j < nstrips ? strip_base + j : nstrips - 1;
                 const char* sg = (const char*)Sb + ((size_t)st * p.ngroups + sg0) * 32;
-                const char* zg = (const char*)p.Z + ((size_t)st * p.ngroups + sg0) * 8;
-                for (int pos0 = wave * 64; pos0 < sgslab * 2; pos0 += 64 * NW) {
+                constexpr int ZW = WB > 4 ? 4 : 2;  // zero-point words per strip and group (UINT8 or UINT4)
+                const char* zg = (const char*)p.Z + ((size_t)st * p.ngroups + sg0) * ZW * 4;
+                for (int pos0 = wave * 64; pos0 < sgslab * ZW; pos0 += 64 * NW) {
                     const int pos = pos0 + lane;  // 16-byte scale units / 32-bit zero-point words
-                    if (pos < sgslab * 2) {
-                        lds_dma16(sg + pos * 16, lds + p.s_off + (j * sgslab * 2 + pos0) * 16);
-                        if (p.Z) lds_dma4(zg + pos * 4, lds + p.z_off + (j * sgslab * 2 + pos0) * 4);
-                    }
+                    if (pos < sgslab * 2) lds_dma16(sg + pos * 16, lds + p.s_off + (j * sgslab * 2 + pos0) * 16);
+                    if (p.Z && pos < sgslab * ZW) lds_dma4(zg + pos * 4, lds + p.z_off + (j * sgslab * ZW + pos0) * 4);
                 }
             }
         } else if constexpr (MX || FP4B) {
@@ -328,7 +349,12 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
     // low-bit codes: signed ones to offset binary (top bit flipped: the 2-bit
     // plane's high bits for width 2, the 1-bit plane for widths 1 and 3)
     const uint32_t lx2 = !zsel && WB == 2 ? 0xAAAAAAAAu : 0u, lx1 = !zsel && WB != 2 ? 0xFFFFFFFFu : 0u;
-    const uint32_t zmask = zsel ? 15u : 0u;  // zero-point, or the offset of the symmetric codes
+    // 5-8 bits: signed codes to offset binary (their top bit: bit 3 of the high
+    // nibble for 8 bits, the high bits of the 2-bit fields for 6, the 1-bit plane
+    // for 5 and 7)
+    const uint32_t hx4 = !zsel && WB == 8 ? 0x88888888u : 0u, hx2 = !zsel && WB == 6 ? 0xAAAAAAAAu : 0u;
+    const uint32_t hx1 = !zsel && (WB == 5 || WB == 7) ? 0xFFFFFFFFu : 0u;
+    const uint32_t zmask = zsel ? (WB > 4 ? 255u : 15u) : 0u;  // zero-point, or the offset of the symmetric codes
     const uint32_t zdef = zsel ? 0u : WB == 4 ? 8u : 1u << (WB - 1);
 
     // WNA16: group of each chunk, relative to the slice's first group
@@ -367,7 +393,10 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
             const int j = ws * SPW + sp;
             if constexpr (WNA16) {
                 sbb[S][sp] = ((const uint16_t*)(lds + p.s_off))[(j * gslab + gi[i]) * 16 + col];
-                zwb[S][sp] = ((const uint32_t*)(lds + p.z_off))[(j * gslab + gi[i]) * 2 + (col >> 3)];
+                if constexpr (WB > 4)  // UINT8 zero-points: four words per strip and group
+                    zwb[S][sp] = ((const uint32_t*)(lds + p.z_off))[(j * gslab + gi[i]) * 4 + (col >> 2)];
+                else
+                    zwb[S][sp] = ((const uint32_t*)(lds + p.z_off))[(j * gslab + gi[i]) * 2 + (col >> 3)];
             }
         }
     };
@@ -393,7 +422,7 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                 constexpr bool BF = F == Fmt::WNA16_BF16;
                 const Frag8(&af)[MT][4] = ADIR ? afd[ADIR ? i : 0] : afb[i & 1];
                 v4f rs[MT];
-                if constexpr (BF) {
+                if constexpr (BF && WB <= 4) {
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         rs[mt] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -413,8 +442,17 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                         wq[1] ^= lx2;
                         wq[2] ^= lx1;
                     }
-                    const uint32_t z = ((zw >> (4 * (col & 7))) & zmask) | zdef;
-                    if constexpr (BF) {
+                    v4u wk = v4u{0u, 0u, 0u, 0u};  // 5-8 bits: the high bits, in offset binary
+                    if constexpr (WB > 4) {
+                        wk = wh[i][sp];
+                        wk[0] ^= WB == 8 ? hx4 : hx2;
+                        wk[1] ^= WB == 8 ? hx4 : hx2;
+                        wk[2] ^= WB == 8 ? hx4 : hx1;
+                        wk[3] ^= hx4;
+                    }
+                    const uint32_t z = WB > 4 ? (((zw >> (8 * (col & 3))) & zmask) | zdef)
+                                              : (((zw >> (4 * (col & 7))) & zmask) | zdef);
+                    if constexpr (BF && WB <= 4) {
                         // bf16: operand 128 + u is exact; the group scale and the
                         // -(128 + z) offset (a row-sum MFMA) act on the fp32 partial
                         const float sc = valid ? bits16_to_f32<true>((uint16_t)sbits) : 0.f;
@@ -435,8 +473,10 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                     } else {
                         // fp16: the exact integer (q - z) as the operand, the group scale on
                         // the fp32 partial of the chunk (fewer VALU per code than scaling
-                        // every operand, and exact)
-                        const float sc = valid ? bits16_to_f32<false>((uint16_t)sbits) : 0.f;
+                        // every operand, and exact); bf16 at 5-8 bits the same, the
+                        // difference converted to bf16 (exact: at most 8 significant bits)
+                        const float sc = valid ? bits16_to_f32<BF>((uint16_t)sbits) : 0.f;
+                        const uint32_t nbw = (0xE400u | z) * 0x10001u;  // 5-8 bits: -(1024 + z)
                         const uint32_t nbz = 0xE400u | z, nhz = 0xD400u | (z << 4);  // -(1024 + z), -(64 + z)
                         const uint32_t nb2 = nbz | (nbz << 16), nh2 = nhz | (nhz << 16);
                         uint32_t nbl[4];  // low-bit widths: -(base_s + z) per pair position
@@ -450,9 +490,10 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int split, char
                         for (int t = 0; t < 4; ++t) {
                             Frag8 b;
                             if constexpr (WB == 4) b = deq4_f16_exact(wq[t] ^ wx, nb2, nh2);
+                            else if constexpr (WB > 4) b = deq_wide<WB, BF>(wq, wk, t, nbw);
                             else b = deq_low_f16<WB>(wq, t, nbl);
 #pragma unroll
-                            for (int mt = 0; mt < MT; ++mt) gacc[t & 1][mt] = mfma16<false>(af[mt][t], b, gacc[t & 1][mt]);
+                            for (int mt = 0; mt < MT; ++mt) gacc[t & 1][mt] = mfma16<BF>(af[mt][t], b, gacc[t & 1][mt]);
                         }
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt) acc2[i & 1][sp][mt] += sc * (gacc[0][mt] + gacc[1][mt]);
@@ -721,13 +762,13 @@ struct SkinnyLds {
 inline int skinny_arow(Fmt F) {
     return F == Fmt::W4A4_MX ? 64 : (F == Fmt::W4A8_MX || F == Fmt::W4A8_MXA || F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B) ? 128 : 256;
 }
-inline SkinnyLds skinny_lds(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) {
+inline SkinnyLds skinny_lds(Fmt F, int64_t rows, int64_t cmax, int NS, int gch, int zb = 8) {
     auto al = [](int64_t b) { return (b + 1023) / 1024 * 1024; };
     int64_t s = 0, z = 0;
     if (F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16) {
         const int64_t gmax = cmax / gch + 2;
         s = al(NS * gmax * 32);
-        z = al(NS * gmax * 8);
+        z = al(NS * gmax * zb);  // zero-point bytes per strip and group: 8 (UINT4) or 16 (UINT8)
     } else if (mx_mfma(F)) {
         s = al(NS * cmax * 64);
         if (mx_act(F)) z = al(rows * cmax * 4);
@@ -744,8 +785,8 @@ inline SkinnyLds skinny_lds(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) 
     L.bytes = L.z_off + z;
     return L;
 }
-inline int64_t skinny_lds_need(Fmt F, int64_t rows, int64_t cmax, int NS, int gch) {
-    return skinny_lds(F, rows, cmax, NS, gch).bytes;
+inline int64_t skinny_lds_need(Fmt F, int64_t rows, int64_t cmax, int NS, int gch, int zb = 8) {
+    return skinny_lds(F, rows, cmax, NS, gch, zb).bytes;
 }
 
 constexpr bool skinny_a16(Fmt F) {
@@ -770,6 +811,7 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
                               int wbits = 4) {
     const int64_t nstrips = Np / 16, nc = K / 128;
     const int gch = G >= 128 ? G / 128 : 1;
+    const int zb = wbits > 4 ? 16 : 8;  // zero-point bytes per strip and group
     SkinnyPlan p{};
     p.NW = 4;
     // The formats with the longer decodes (NVFP4, MXINT4, 8-bit weights) at up to
@@ -790,7 +832,7 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
         p.cps = (int)nc;
         p.cpk = (int)cdiv(nc, 8);
         p.CPW = skinny_direct_cpw(p.cpk);
-        const SkinnyLds L = skinny_lds(F, 0, nc, 1, gch);  // scales only
+        const SkinnyLds L = skinny_lds(F, 0, nc, 1, gch, zb);  // scales only
         p.a_off = (int)L.a_off;
         p.s_off = (int)L.s_off;
         p.z_off = (int)L.z_off;
@@ -818,21 +860,23 @@ inline SkinnyPlan plan_skinny(Fmt F, int64_t M, int64_t Np, int64_t K, int G, in
     int64_t S = p.groups_x >= 192 ? 1 : cdiv(target, p.groups_x);
     const int64_t smax = nc / WK > 0 ? nc / WK : 1;
     // weight loads per chunk (two 16-byte halves; or the two planes of 3-bit codes)
-    const int nb = (F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B || w8a16(F) || mxf8(F) || mxf6(F) || wbits == 3) ? 2 : 1;
+    const int nb = wbits == 7 ? 3
+                 : (F == Fmt::W8A8_I8 || F == Fmt::W8A8_F8B || w8a16(F) || mxf8(F) || mxf6(F) || wbits == 3 || wbits > 4) ? 2
+                                                                                                                     : 1;
     const int64_t cap = p.SPW * 16 * nb < 64 ? 16 : 8;  // largest register batch instantiated
-    while (S < smax && (skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap)) ++S;
+    while (S < smax && (skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch, zb) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap)) ++S;
     if (S > smax) S = smax;
     p.ok = true;
     if (force_splits > 0) {  // tuning override: the slice must still fit LDS and one register batch
         S = force_splits;
-        if (S > nc || skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap) p.ok = false;
+        if (S > nc || skinny_lds_need(F, M, cdiv(nc, S), p.NS, gch, zb) > kSkinnyLds || cdiv(cdiv(nc, S), WK) > cap) p.ok = false;
     }
     p.splits = (int)(S < 1 ? 1 : S);
     p.cps = (int)cdiv(nc, p.splits);
     p.splits = (int)cdiv(nc, p.cps);  // no empty slice
     p.cpk = (int)cdiv(p.cps, WK);
     const int64_t cmax = p.cps;
-    const SkinnyLds L = skinny_lds(F, M, cmax, p.NS, gch);
+    const SkinnyLds L = skinny_lds(F, M, cmax, p.NS, gch, zb);
     p.a_off = (int)L.a_off;
     p.s_off = (int)L.s_off;
     p.z_off = (int)L.z_off;
@@ -849,7 +893,7 @@ hipError_t launch_skinny_k(dim3 grid, int lds_bytes, const SkinnyArgs& a, hipStr
     if (plan_recorder()) {
         if (NW == 8)
             plan_record("skinny_kernel<%s,%d,%d,%d,direct> grid=%ux%u splits=%d", fmt_name(F), MT, SPW, CPW, grid.x, grid.y, a.splits);
-        else if (WB < 4)
+        else if (WB != 4)
             plan_record("skinny_kernel<%s,%d,%d,%d,w%d> grid=%ux%u splits=%d", fmt_name(F), MT, SPW, CPW, WB, grid.x, grid.y,
                         a.splits);
         else
@@ -884,7 +928,7 @@ hipError_t launch_skinny_direct(int cpw, dim3 grid, int lds_bytes, const SkinnyA
 
 template <Fmt F, int MT, int SPW, int WB = 4>
 hipError_t launch_skinny_cpw(int cpw, dim3 grid, int lds_bytes, const SkinnyArgs& a, hipStream_t st) {
-    constexpr int LPC = WB == 4 ? FmtTraits<F>::BSTRIP / 1024 : WB == 3 ? 2 : 1;  // loads per chunk
+    constexpr int LPC = WB == 4 ? FmtTraits<F>::BSTRIP / 1024 : WB == 3 ? 2 : WB < 4 ? 1 : WB == 7 ? 3 : 2;  // loads per chunk
     switch (cpw) {
         case 2: return launch_skinny_k<F, MT, SPW, 2, 4, WB>(grid, lds_bytes, a, st);
         case 4: return launch_skinny_k<F, MT, SPW, 4, 4, WB>(grid, lds_bytes, a, st);
@@ -926,6 +970,10 @@ hipError_t launch_skinny_dense(const SkinnyPlan& pl, SkinnyArgs s, hipStream_t s
             case 1: e = by_shape(std::integral_constant<int, 1>{}); break;
             case 2: e = by_shape(std::integral_constant<int, 2>{}); break;
             case 3: e = by_shape(std::integral_constant<int, 3>{}); break;
+            case 5: e = by_shape(std::integral_constant<int, 5>{}); break;
+            case 6: e = by_shape(std::integral_constant<int, 6>{}); break;
+            case 7: e = by_shape(std::integral_constant<int, 7>{}); break;
+            case 8: e = by_shape(std::integral_constant<int, 8>{}); break;
             default: e = by_shape(std::integral_constant<int, 4>{}); break;
         }
     } else {
@@ -975,6 +1023,78 @@ inline hipError_t launch_widen_lowbit(const void* planes, void* out, int wbits, 
         case 3: hipLaunchKernelGGL(widen_lowbit_kernel<3>, g, b, 0, st, (const char*)planes, (v4u*)out, slots, smask); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+// 5- to 8-bit WnA16 codes -> 16-bit weights q - z (exact in fp16 and bf16:
+// |q - z| < 256), for the tiled kernels, which apply the group scales to their
+// fp32 partials: per strip and chunk, four 1 KB fragments (one per K sub-step)
+// of 64 lanes x 8 values.  One thread per lane slot.  (Rounding (q - z) * s to
+// bf16 here instead would cost the bf16 results about 2^-9 of each weight.)
+template <int WB, bool BF>
+__global__ __launch_bounds__(256) void widen_wide_kernel(const char* __restrict__ planes, const uint8_t* __restrict__ Z,
+                                                         v4u* __restrict__ out, int64_t slots, int nc, int ngroups,
+                                                         int gchunks, bool sgn) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // slot = (strip * chunks + chunk) * 64 + lane
+    if (i >= slots) return;
+    const int col = (int)(i & 15);
+    const int64_t sc = i >> 6, st = sc / nc;
+    const int64_t sg = st * ngroups + (int)(sc - st * nc) / gchunks;  // strip * groups + group
+    const v4u wl = __builtin_nontemporal_load((const v4u*)planes + i);
+    const char* hp = planes + (size_t)slots * 16;
+    v4u wh = v4u{0u, 0u, 0u, 0u};
+    if constexpr (WB == 8) {
+        wh = __builtin_nontemporal_load((const v4u*)hp + i);
+    } else {
+        if constexpr (WB == 6 || WB == 7) {
+            const v2u a = __builtin_nontemporal_load((const v2u*)hp + i);
+            wh[0] = a[0];
+            wh[1] = a[1];
+        }
+        if constexpr (WB != 6) wh[2] = __builtin_nontemporal_load((const uint32_t*)(hp + (WB == 7 ? (size_t)slots * 8 : 0)) + i);
+    }
+    uint32_t z = 1u << (WB - 1);
+    if (sgn) {  // two's complement -> offset binary: flip the top bit
+        const uint32_t m4 = WB == 8 ? 0x88888888u : 0u, m2 = WB == 6 ? 0xAAAAAAAAu : m4;
+        const uint32_t m1 = WB == 5 || WB == 7 ? 0xFFFFFFFFu : m4;
+        wh[0] ^= m2;
+        wh[1] ^= m2;
+        wh[2] ^= m1;
+        wh[3] ^= m4;
+    } else {
+        z = Z[sg * 16 + col];
+    }
+    const uint32_t nb = (0xE400u | z) * 0x10001u;  // -(1024 + z), both halves
+    v4u* o = out + (i >> 6) * 256 + (i & 63);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t * 64] = deq_wide<WB, BF>(wl, wh, t, nb).u;
+}
+
+inline hipError_t launch_widen_wide(const void* planes, const void* Z, void* out, int wbits, bool bf16,
+                                    int64_t Np, int64_t K, int group_size, hipStream_t st) {
+    const int64_t slots = (Np / 16) * (K / 128) * 64, blocks = (slots + 255) / 256;
+    if (plan_recorder()) {
+        plan_record("widen_wide_kernel<%d,%s> grid=%lld", wbits, bf16 ? "bf16" : "f16", (long long)blocks);
+        return hipSuccess;
+    }
+    if (blocks > 0x7FFFFFFF || group_size < 128 || group_size % 128 || K % group_size) return hipErrorInvalidValue;
+    const dim3 g((unsigned)blocks), b(256);
+    const int nc = (int)(K / 128), ng = (int)(K / group_size), gc = group_size / 128;
+    const bool sgn = Z == nullptr;
+    const char* w = (const char*)planes;
+    const uint8_t* z = (const uint8_t*)Z;
+    v4u* o = (v4u*)out;
+#define HQ_WIDE(WBV)                                                                                              \
+    if (bf16) hipLaunchKernelGGL((widen_wide_kernel<WBV, true>), g, b, 0, st, w, z, o, slots, nc, ng, gc, sgn); \
+    else hipLaunchKernelGGL((widen_wide_kernel<WBV, false>), g, b, 0, st, w, z, o, slots, nc, ng, gc, sgn);
+    switch (wbits) {
+        case 5: HQ_WIDE(5) break;
+        case 6: HQ_WIDE(6) break;
+        case 7: HQ_WIDE(7) break;
+        case 8: HQ_WIDE(8) break;
+        default: return hipErrorInvalidValue;
+    }
+#undef HQ_WIDE
     return hipGetLastError();
 }
 
@@ -1035,7 +1155,7 @@ hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
     if (!a.invariant && !tile_forced && (stream_forced || a.M <= skinny_max_m(F))) {
         if (a.M > kSkinnyMaxM) return hipErrorNotSupported;
         const int mode = a.tune_path == TUNE_STREAM8 ? 2 : a.tune_path == TUNE_STREAM ? 1 : 0;
-        if (mode == 2 && a.wbits < 4) return hipErrorNotSupported;  // the direct stream reads 4-bit words only
+        if (mode == 2 && a.wbits != 4) return hipErrorNotSupported;  // the direct stream reads 4-bit words only
         s.wbits = a.wbits;
         const SkinnyPlan pl = plan_skinny(F, a.M, a.Np, a.K, G, a.tune_splits, mode, a.wbits);
         if (!pl.ok) return hipErrorNotSupported;
@@ -1075,6 +1195,29 @@ hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
             p.W = a.ws;
             p.part = (char*)a.ws + off;
             e = launch_dense_plan<F>(pl, p, a.stream);
+            plan_workspace_base(0);
+            return e;
+        }
+        if (a.wbits > 4) {
+            // 5-8-bit widths on the tiles: the codes widen to 16-bit q - z at the
+            // front of the workspace, 128 x 128 tiles read them with the group
+            // scales as they are, partial tiles follow
+            constexpr Fmt W = F == Fmt::WNA16_BF16 ? Fmt::W16_BF16 : Fmt::W16_F16;
+            const size_t wide = (size_t)(a.Np / 16) * (size_t)(a.K / 128) * 4096, off = (wide + 255) & ~(size_t)255;
+            TilePlan wp = plan_tile(a.M, a.Np, a.K, has_big_tile(W), has_wide256_tile(W), has_wide_tile(W), wide256_min_tiles(W));
+            if (tile_forced) {
+                if (a.tune_path != TUNE_T128) return hipErrorNotSupported;
+                wp.forced = a.tune_path;
+                wp.splits = a.tune_splits;
+            }
+            hipError_t e = launch_widen_wide(a.w, a.z, a.ws, a.wbits, F == Fmt::WNA16_BF16, a.Np, a.K, G, a.stream);
+            if (e != hipSuccess) return e;
+            plan_workspace(wide);
+            plan_workspace_base(off);
+            p.W = a.ws;
+            p.Z = nullptr;
+            p.part = (char*)a.ws + off;
+            e = launch_dense_plan<W>(wp, p, a.stream);
             plan_workspace_base(0);
             return e;
         }

@@ -62,7 +62,7 @@ namespace hq {
 
 enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B, MXFP4_BF16, NVFP4_BF16,
                  MXINT4_BF16, W8A16_F16, W8A16_BF16, F8W_F16, F8W_BF16, MXF8_BF16, MXF6E2_BF16, MXF6E3_BF16,
-                 MXFP4_F16, NVFP4_F16, MXINT4_F16, MXF8_F16, MXF6E2_F16, MXF6E3_F16 };
+                 MXFP4_F16, NVFP4_F16, MXINT4_F16, MXF8_F16, MXF6E2_F16, MXF6E3_F16, W16_F16, W16_BF16 };
 
 constexpr const char* fmt_name(Fmt F) {
     return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
@@ -73,7 +73,7 @@ constexpr const char* fmt_name(Fmt F) {
          : F == Fmt::F8W_BF16 ? "F8W_BF16" : F == Fmt::MXF8_BF16 ? "MXF8_BF16" : F == Fmt::MXF6E2_BF16 ? "MXF6E2_BF16"
          : F == Fmt::MXF6E3_BF16 ? "MXF6E3_BF16" : F == Fmt::MXFP4_F16 ? "MXFP4_F16" : F == Fmt::NVFP4_F16 ? "NVFP4_F16"
          : F == Fmt::MXINT4_F16 ? "MXINT4_F16" : F == Fmt::MXF8_F16 ? "MXF8_F16" : F == Fmt::MXF6E2_F16 ? "MXF6E2_F16"
-         : "MXF6E3_F16";
+         : F == Fmt::MXF6E3_F16 ? "MXF6E3_F16" : F == Fmt::W16_F16 ? "W16_F16" : "W16_BF16";
 }
 // Formats whose activations carry OCP MX scales (E8M0 per 32 K, [rows][K/32]).
 constexpr bool mx_act(Fmt F) { return F == Fmt::W4A8_MXA || F == Fmt::W4A4_MX; }
@@ -112,6 +112,11 @@ template <> struct FmtTraits<Fmt::MXINT4_F16> { static constexpr int AROW = 256,
 template <> struct FmtTraits<Fmt::MXF8_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::MXF6E2_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::MXF6E3_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+// 16-bit weights (5- to 8-bit WnA16 codes less their zero-points, q - z, exact
+// in fp16 and bf16): a lane's 8 values of one K sub-step per 16-byte fragment,
+// four fragments per strip and step; the group scales stay in the W4A16 layout
+template <> struct FmtTraits<Fmt::W16_F16> { static constexpr int AROW = 256, BSTRIP = 4096; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::W16_BF16> { static constexpr int AROW = 256, BSTRIP = 4096; using Acc = v4f; };
 // 8-bit weight-only formats: INT8 or FP8 (E4M3) codes in the same layout, per-channel fp32 scale
 constexpr bool f8w(Fmt F) { return F == Fmt::F8W_F16 || F == Fmt::F8W_BF16; }
 constexpr bool w8a16(Fmt F) { return F == Fmt::W8A16_F16 || F == Fmt::W8A16_BF16 || f8w(F); }
@@ -128,8 +133,10 @@ constexpr bool mxint4w(Fmt F) { return F == Fmt::MXINT4_BF16 || F == Fmt::MXINT4
 // operands, fp16 MFMA and output; the others of these families are bf16)
 constexpr bool f16_operand(Fmt F) {
     return F == Fmt::MXFP4_F16 || F == Fmt::NVFP4_F16 || F == Fmt::MXINT4_F16 || F == Fmt::MXF8_F16 ||
-           F == Fmt::MXF6E2_F16 || F == Fmt::MXF6E3_F16;
+           F == Fmt::MXF6E2_F16 || F == Fmt::MXF6E3_F16 || F == Fmt::W16_F16;
 }
+// 16-bit (q - z) weight operands (no decode; group scales on the fp32 partials)
+constexpr bool w16(Fmt F) { return F == Fmt::W16_F16 || F == Fmt::W16_BF16; }
 // 8-bit weight codes in the INT8 weight-only layout (two 16-byte halves per lane and chunk)
 constexpr bool w8load(Fmt F) { return w8a16(F) || mxf8(F); }
 // e2m1 weights converted to bf16 operands with a per-lane scale (bf16 MFMA)
@@ -316,6 +323,45 @@ __device__ __forceinline__ void low_f16_offsets(uint32_t z, uint32_t (&nb)[4]) {
         const uint32_t h = WB == 1 ? ((0xE400u - 0x400u * s) | (z << s)) : ((0xE400u - 0x800u * s) | (z << (2 * s)));
         nb[s] = h * 0x10001u;
     }
+}
+
+// 5-8-bit codes: the low nibble from the 4-bit pair-order word wl[t] and the
+// high bits from wh (width 8: a second pair-order word set, wh[t]; 6 and 7: the
+// 2-bit plane in wh[0..1]; 5 and 7: the 1-bit plane in wh[2], the bit above the
+// 2-bit field for width 7), placed as bits 4.. of each 16-bit half under the
+// exponent of 1024: the half reads 1024 + code (code < 256), and nb = -(1024 + z)
+// leaves code - z exactly (offset binary for signed codes, z = 2^(width-1)).
+// bf16 operands take that exact difference through fp32 (at most 8 significant
+// bits, exact in bf16).
+__device__ __forceinline__ uint32_t shl_signed(uint32_t x, int sh) { return sh >= 0 ? x << sh : x >> -sh; }
+template <int WB, bool BF>
+__device__ __forceinline__ Frag8 deq_wide(const v4u& wl, const v4u& wh, int t, uint32_t nb) {
+    Frag8 f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        uint32_t c = 0x64006400u;
+        if constexpr (WB == 8) {
+            c = and_or(shl_signed(wh[t], 4 - 4 * s), 0x00F000F0u, c);
+        } else {
+            if constexpr (WB == 6 || WB == 7)  // 2-bit field at 2s + 8 (t & 1) -> bits 4-5
+                c = and_or(shl_signed(wh[t >> 1], 4 - 2 * s - 8 * (t & 1)), 0x00300030u, c);
+            if constexpr (WB == 5)  // 1-bit field at 4t + s -> bit 4
+                c = and_or(shl_signed(wh[2], 4 - 4 * t - s), 0x00100010u, c);
+            if constexpr (WB == 7)  // -> bit 6
+                c = and_or(shl_signed(wh[2], 6 - 4 * t - s), 0x00400040u, c);
+        }
+        const uint32_t v = and_or(wl[t] >> (4 * s), 0x000F000Fu, c);
+        const v2h d = __builtin_bit_cast(v2h, v) + __builtin_bit_cast(v2h, nb);
+        if constexpr (BF) {
+            typedef float f2v __attribute__((ext_vector_type(2)));
+            typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+            const f2v x = f2v{(float)d[0], (float)d[1]};
+            f.u[s] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, b2v));
+        } else {
+            f.u[s] = __builtin_bit_cast(uint32_t, d);
+        }
+    }
+    return f;
 }
 
 // Low-bit bf16 operands 128 + u (exact; offset binary as above), pair s of sub-step t.
@@ -515,7 +561,9 @@ __attribute__((amdgpu_waves_per_eu(1, BM < 128 ? 4 : WM * WN <= 4 ? 1 : 2)))
 void tile_gemm_kernel(TileArgs p) {
     using T = FmtTraits<F>;
     using Acc = typename T::Acc;
-    constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16;
+    // group scales (and UINT4 zero-points) staged per step; the 16-bit (q - z)
+    // weights take the scales only (their zero-point buffer is null: reads zeros)
+    constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || w16(F);
     constexpr bool NV = nvfp4(F);                         // E4M3 weight scales per 16 K
     constexpr bool MX = mx_mfma(F) || fp4w(F) || mxf8(F);  // byte scales per lane
     static_assert(!mxf6(F), "MXFP6 reaches the tiles widened to MXFP8");
@@ -932,6 +980,39 @@ void tile_gemm_kernel(TileArgs p) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+        } else if constexpr (w16(F)) {
+            // (q - z) operands as loaded; each step's MFMA partial takes the
+            // column's group scale (a step lies inside one group)
+            constexpr bool BF = F == Fmt::W16_BF16;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) hook(t);
+            float sc[NT];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) sc[j] = bits16_to_f32<BF>(((const uint16_t*)sS)[(wn * NT + j) * 16 + col]);
+            v4f st[MT][NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) st[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    const int row = wm * (BM / WM) + i * 16 + col;
+                    Frag8 a;
+                    a.u = *(const v4u*)(sA + row * AROW + (((4 * quad + t) ^ swz(row, AUNITS)) * 16));
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        Frag8 b;
+                        b.u = bw[j][t];
+                        st[i][j] = mfma16<BF>(a, b, st[i][j]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc[i][j] += sc[j] * st[i][j];
         } else if constexpr (F == Fmt::WNA16_BF16) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) hook(t);
@@ -1465,7 +1546,7 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
 // halves the A traffic per flop and still fits two LDS stages.  bf16 A has no
 // 256-row variant (its row-sum MFMA needs a second accumulator set).
 // INT8 weight-only: 256-row tiles do not fit two stages of its 2 KB weight strips
-constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16 && !w8load(F) && !mxf6(F); }
+constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16 && !w8load(F) && !mxf6(F) && !w16(F); }
 // fp16 A with 4-bit weights: 8 waves side by side, each dequantising its own
 // weight strips once: 256 x 256 tiles of 256 x 32 waves with a single weight
 // stage (each dequantised fragment feeds 16 MFMAs; 13 % faster than 128 x 256

@@ -44,7 +44,9 @@
  *    faults surface at the caller's next synchronisation.
  *  - Device pointers must be 16-byte aligned (HQ_ERR_ALIGNMENT otherwise).
  *  - A workspace is needed only where hq_workspace_bytes() says so (split-K
- *    partial tiles, MoE routing metadata).  Every kernel writes what it later
+ *    partial tiles, MoE routing metadata, and at larger M the weights of the
+ *    1-3-bit, 5-8-bit and MXFP6 formats rewritten in the layout the tiled
+ *    kernels read: 4-bit words, 16-bit q - z values, or MXFP8 codes).  Every kernel writes what it later
  *    reads within the same call, so its contents need no initialisation and
  *    are meaningless between calls.  Two calls that share a workspace must not
  *    run concurrently.
@@ -104,7 +106,16 @@ typedef enum hq_dtype {
     HQ_DT_E0M1 = 19,     /* -1..1, one code per byte                   */
     HQ_DT_E0M2 = 20,     /* -3..3, one code per byte                   */
     HQ_DT_E0M3 = 21,     /* -7..7, 4-bit codes in the INT4 word layout */
-    HQ_DT_E0M7 = 22      /* -127..127, one code per byte               */
+    HQ_DT_E0M7 = 22,     /* -127..127, one code per byte               */
+    /* wider WnA16 codes, one per byte (INT8 = HQ_DT_INT8 with 16-bit group
+       scales); unsigned widths take UINT8 zero-points */
+    HQ_DT_INT5 = 23,     /* -16..15                                    */
+    HQ_DT_UINT5 = 24,    /* 0..31                                      */
+    HQ_DT_INT6 = 25,     /* -32..31                                    */
+    HQ_DT_UINT6 = 26,    /* 0..63                                      */
+    HQ_DT_INT7 = 27,     /* -64..63                                    */
+    HQ_DT_UINT7 = 28,    /* 0..127                                     */
+    HQ_DT_UINT8 = 29     /* 0..255; also the 8-bit zero-point dtype    */
 } hq_dtype;
 
 typedef enum hq_scale_gran {
@@ -142,6 +153,8 @@ typedef enum hq_moe_mode {
  *   BF16|FP16 UINT4      same as a_dtype, PER_GROUP_K  UINT4   NONE      a_dtype
  *   BF16|FP16 INT1|INT2|INT3  same as a_dtype, PER_GROUP_K  NONE  NONE  a_dtype (low-bit WnA16)
  *   BF16|FP16 UINT1|UINT2|UINT3  same, PER_GROUP_K     UINT4   NONE      a_dtype (low-bit WnA16)
+ *   BF16|FP16 INT5|INT6|INT7|INT8  same as a_dtype, PER_GROUP_K  NONE  NONE  a_dtype (5-8-bit WnA16)
+ *   BF16|FP16 UINT5|UINT6|UINT7|UINT8  same, PER_GROUP_K  UINT8  NONE     a_dtype (5-8-bit WnA16)
  *   BF16|FP16 E0M1|E0M2|E0M3  same as a_dtype, PER_GROUP_K  NONE  NONE  a_dtype (e0mN: the INT2/3/4 kernels)
  *   BF16|FP16 E0M7       FP32, PER_CHANNEL             NONE    NONE      a_dtype (e0m7: the INT8 kernels)
  *   BF16|FP16 FP8_E4M3   E8M0, PER_GROUP_K, group 32   NONE    NONE      a_dtype (MXFP8 weight-only)
@@ -258,6 +271,10 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *      int8 per code [K][N], the two's-complement value for INT1..INT3,
  *      0 .. 2^b-1 for UINT1..UINT3; a code outside its width is
  *      HQ_ERR_INVALID_ARG.  Unsigned widths take UINT4 zero-points (below).
+ *      5-8-bit codes (WnA16, same section): one byte per code [K][N], int8
+ *      two's complement for INT5..INT8, uint8 0 .. 2^b-1 for UINT5..UINT8; a
+ *      code outside its width is HQ_ERR_INVALID_ARG.  Unsigned widths take
+ *      UINT8 zero-points (below).
  *      e0mN ("Humming wird angekuendigt": the zero-exponent float whose values
  *      are the symmetric integers of its width): e0m3 in the 4-bit word layout
  *      above, e0m1 / e0m2 / e0m7 one code per byte [K][N]; bit n is the sign,
@@ -270,6 +287,8 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *          PER_CHANNEL fp32: [N]; BLOCK_128x128 fp32: [K/128][ceil(N/128)]
  *   zp     UINT4: uint32 [K/group][ceil(N/8)]; column n = 8j+i in bits
  *          4i..4i+3 of word [g][j]
+ *          UINT8 (5-8-bit widths): uint8 [K/group][N], each inside the codes'
+ *          width (else HQ_ERR_INVALID_ARG)
  *   scale2 PER_TENSOR_F32: fp32 [E] (one per expert); otherwise NULL
  *
  * Packed outputs (N padded to Np = ceil(N/16)*16; padding decodes to 0 with
@@ -290,6 +309,12 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *        1-bit plane (b = 1, 3), after it: uint32 [slots]; bit
  *          16*(j&1) + 4*t + (j>>1) holds its bit 0 (b = 1) or bit 2 (b = 3).
  *      Codes 2s and 2s+1 thus share an offset in the two 16-bit halves.
+ *      5-8-bit (WnA16): the codes' low four bits as a 4-bit word set in the
+ *        INT4/UINT4 layout above (pair order), then their high b - 4 bits:
+ *        for b = 8 a second 4-bit word set of the same layout; for b = 5..7
+ *        the planes above holding the (b - 4)-bit high code (a 2-bit plane for
+ *        b = 6, 7, then a 1-bit plane for b = 5, 7, whose bit is bit 4 for
+ *        b = 5 and bit 6 for b = 7 of the code).
  *      MXFP6: a lane's 32 codes of a chunk as one 192-bit group, code j at
  *        bits 6j..6j+5; bits 0-127 of every slot in a 16-byte plane
  *        [Np/16][K/128][64 lanes][16 B], bits 128-191 after it in an 8-byte
@@ -310,6 +335,8 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *          (padding columns hold 0x38 = 1.0);
  *          PER_CHANNEL fp32: [Np]; BLOCK_128x128 fp32: unchanged [K/128][ceil(N/128)]
  *   zp     [E][Np/16][K/group] uint64, column 16*strip + i in bits 4i..4i+3
+ *          UINT8: [Np/16][K/group][16] bytes, byte i for column 16*strip + i
+ *          (padding columns 0)
  *   scale2 fp32 [E], copied
  */
 hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale, const void* zp,

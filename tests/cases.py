@@ -91,6 +91,15 @@ WNLOW_TILES = [(M, N, K, G, b, sg, not sg) for M, N, K, G in ((100, 384, 768, 12
 WNLOW_SWEEP = [(M, C2["N"], C2["K"], C2["G"], b, sg, bf) for b, sg, bf in ((3, False, False), (2, True, True))
                for M in SWEEP]
 
+# ---- 5-8-bit WnA16 (INT5-8, UINT5-8 + 8-bit zero-points): (M, N, K, G, bits, signed, bf16) ----
+WNWIDE_WIDTHS = [(b, sg) for b in (5, 6, 7, 8) for sg in (True, False)]
+WNWIDE_SMALL = [(M, 1000, 1024, 128, b, sg, (b + sg) % 2 == 0) for M in (1, 5, 16, 33, 64) for b, sg in WNWIDE_WIDTHS]
+WNWIDE_TILES = [(M, N, K, G, b, sg, (b + sg) % 2 == 1) for M, N, K, G in ((130, 1000, 1024, 128), (300, 520, 2048, 256),
+                                                                         (2000, 4100, 384, 128)) for b, sg in WNWIDE_WIDTHS]
+# the dense W4A16 shape with 8-bit (UINT8 + zero-points, fp16) and 5-bit (INT5, bf16) codes
+WNWIDE_SWEEP = [(M, C2["N"], C2["K"], C2["G"], b, sg, bf) for b, sg, bf in ((8, False, False), (5, True, True))
+                for M in SWEEP]
+
 # ---- MX float weights (MXFP8 E4M3, MXFP6 E2M3 / E3M2), bf16 activations: (M, N, K, elem) ----
 MXF_ELEMS = ["e4m3", "e2m3", "e3m2"]
 MXF_SMALL = [(M, 272, 1024, e) for M in (1, 5, 16, 33, 64) for e in MXF_ELEMS]
@@ -123,6 +132,8 @@ def all_dense_cases():
         out.append(("mxint4", M, N, K, 32, {}))
     for M, N, K, G, b, sg, bf in WNLOW_SMALL + WNLOW_TILES + WNLOW_SWEEP:
         out.append(("wnlow", M, N, K, G, dict(bits=b, signed=sg, bf16=bf)))
+    for M, N, K, G, b, sg, bf in WNWIDE_SMALL + WNWIDE_TILES + WNWIDE_SWEEP:
+        out.append(("wnwide", M, N, K, G, dict(bits=b, signed=sg, bf16=bf)))
     for M, N, K, e in MXF_SMALL + MXF_TILES + MXF_SWEEP:
         out.append(("mxf", M, N, K, 32, dict(elem=e)))
     for wf in ("w8a16", "fp8w"):

@@ -18,13 +18,17 @@ A16_FORMATS = ["wna16_f16_zp", "wna16_bf16_sym", "mxfp4_a16", "nvfp4_a16", "mxin
                "fp8w_bf16", "fp8w_f16", "mxfp8_a16", "mxfp6e2_a16", "mxfp6e3_a16", "mxfp4_a16_f16", "mxfp6e2_a16_f16"]
 MXF_ELEM = {"mxfp8_a16": "e4m3", "mxfp6e2_a16": "e2m3", "mxfp6e3_a16": "e3m2", "mxfp6e2_a16_f16": "e2m3"}
 LOWBIT = {"w3a16_uint3": (3, False), "w2a16_int2": (2, True), "w1a16_int1": (1, True)}
+# 5-8-bit WnA16: (bits, signed, bf16 activations)
+WIDE = {"wn5_int5_bf16": (5, True, True), "wn5_uint5_f16": (5, False, False), "wn6_int6_f16": (6, True, False),
+        "wn6_uint6_bf16": (6, False, True), "wn7_int7_f16": (7, True, False), "wn7_uint7_bf16": (7, False, True),
+        "wn8_int8_bf16": (8, True, True), "wn8_uint8_f16": (8, False, False)}
 
 
 class Layer:
     """One dense layer of a format with seeded inputs on the device; `run` calls
     hq_gemm on rows r0 .. r0+M-1 of the activations."""
 
-    def __init__(self, fmt, M, N, K, seed):
+    def __init__(self, fmt, M, N, K, seed, G=128):
         self.fmt, self.M, self.N, self.K = fmt, M, N, K
         f16 = fmt.endswith("_a16_f16")   # a weight-only format of the scaled converts with fp16 activations
         self.raw = fmt == "w8a8_raw"
@@ -95,6 +99,15 @@ class Layer:
             A, sa, arow, srow = d["A"], None, K * 2, 0
             self.ref = lambda r: oracle.gemm_wnlow(d["A"], d["codes"], d["s"], d.get("z"), N=N, K=K, G=128, bits=bits,
                                                    a_bf16=signed, w_signed=signed, rows=r)
+        elif fmt in WIDE:
+            bits, signed, bf = WIDE[fmt]
+            self.out_dt = torch.bfloat16 if bf else torch.float16
+            d = syn.wnwide(seed, M, N, K, bits, signed, G=G, dtype=self.out_dt)
+            self.desc = hq.desc_wnwide(N, K, bits, signed, group_size=G, bf16=bf)
+            packed = hq.hq_repack(self.desc, d["codes"], d["s"], d.get("z"))
+            A, sa, arow, srow = d["A"], None, K * 2, 0
+            self.ref = lambda r: oracle.gemm_wnwide(d["A"], d["codes"], d["s"], d.get("z"), N=N, K=K, G=G, bits=bits,
+                                                    a_bf16=bf, w_signed=signed, rows=r)
         elif fmt == "mxint4_a16":
             d = syn.w4a16_mxint4(seed, M, N, K)
             self.desc = hq.desc_mxint4_a16(N, K)

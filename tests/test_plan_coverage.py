@@ -20,6 +20,8 @@ def desc_of(fmt, N, K, G, flags):
         return hq.desc_w4a16(N, K, G, bf16=flags["bf16"], zp=flags["zp"])
     if fmt == "wnlow":
         return hq.desc_wnlow(N, K, flags["bits"], flags["signed"], G, bf16=flags["bf16"])
+    if fmt == "wnwide":
+        return hq.desc_wnwide(N, K, flags["bits"], flags["signed"], G, bf16=flags["bf16"])
     if fmt == "mxf":
         return hq.desc_mxf_a16(N, K, flags["elem"])
     if fmt == "w4a8":
@@ -74,6 +76,8 @@ BENCH = {
     "fp8wfp": ("fp8w", 4096, 7168, 7168, dict(bf16=False)),
     "w3a16": ("wnlow", cases.C2["N"], cases.C2["K"], cases.C2["G"], dict(bits=3, signed=False, bf16=False)),
     "w2a16": ("wnlow", cases.C2["N"], cases.C2["K"], cases.C2["G"], dict(bits=2, signed=True, bf16=True)),
+    "w8a16g": ("wnwide", cases.C2["N"], cases.C2["K"], cases.C2["G"], dict(bits=8, signed=False, bf16=False)),
+    "w5a16": ("wnwide", cases.C2["N"], cases.C2["K"], cases.C2["G"], dict(bits=5, signed=True, bf16=True)),
     "mxfp8a16": ("mxf", cases.C2["N"], cases.C2["K"], 32, dict(elem="e4m3")),
     "mxfp6a16": ("mxf", cases.C2["N"], cases.C2["K"], 32, dict(elem="e2m3")),
 }

@@ -1,0 +1,153 @@
+"""Host-side tests of the 5-8-bit WnA16 weights (INT5-INT8, UINT5-UINT8; no GPU):
+descriptor validation, the packed layout (the low four bits in the 4-bit word set,
+the high bits in a second word set or in the low-bit planes), the UINT8
+zero-point layout, the code-range check of the repack and the launch plans.
+
+The layout is decoded here from what hq.h states and compared with the codes
+themselves; the 4-bit word order and the plane bit positions are those the
+hand walkthroughs of test_abi and test_lowbit_host pin."""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from bit_quantized_gemm_w4a16_amd import autotune, hq
+from test_lowbit_host import codes_of_4bit_words, planes_to_codes
+
+WIDTHS = [(b, sg) for b in (5, 6, 7, 8) for sg in (True, False)]
+
+
+def codes_in_chunk_order(codes, Np, K):
+    """Codes [K][N] -> [slots][4 sub-steps][8] in the lane order of the packed
+    layout (lane l of strip st holds column 16 st + (l & 15) and, in sub-step t,
+    K = 128 chunk + 32 (l >> 4) + 8 t + j; padding columns read 0)."""
+    N = codes.shape[1]
+    c = np.zeros((K, Np), dtype=np.int64)
+    c[:, :N] = codes.astype(np.int64)
+    nst, nc = Np // 16, K // 128
+    # [chunk][quarter][t][j] x [strip][col]
+    x = c.reshape(nc, 4, 4, 8, nst, 16)
+    # -> [strip][chunk][quarter][col][t][j] = slot (strip, chunk, lane = 16 quarter + col)
+    return x.transpose(4, 0, 1, 5, 2, 3).reshape(nst * nc * 64, 4, 8)
+
+
+@pytest.mark.parametrize("bits,signed", WIDTHS)
+def test_descriptor_validation(bits, signed):
+    d = hq.desc_wnwide(4096, 1024, bits, signed)
+    hq.hq_desc_validate(d)
+    hq.hq_desc_validate(hq.desc_wnwide(40, 512, bits, signed, group_size=512, bf16=False))
+    bad = hq.hq_layer_desc.from_buffer_copy(d)
+    bad.zp_dtype = hq.HQ_DT_UINT8 if signed else hq.HQ_DT_NONE   # signed take none, unsigned need UINT8
+    with pytest.raises(hq.HQError):
+        hq.hq_desc_validate(bad)
+    if not signed:
+        bad.zp_dtype = hq.HQ_DT_UINT4                              # the zero-points are bytes at these widths
+        with pytest.raises(hq.HQError):
+            hq.hq_desc_validate(bad)
+    bad = hq.hq_layer_desc.from_buffer_copy(d)
+    bad.group_size = 64
+    with pytest.raises(hq.HQError):
+        hq.hq_desc_validate(bad)
+    bad = hq.hq_layer_desc.from_buffer_copy(d)
+    bad.num_experts = 4
+    with pytest.raises(hq.HQError):
+        hq.hq_desc_validate(bad)
+
+
+@pytest.mark.parametrize("bits,signed", WIDTHS)
+@pytest.mark.parametrize("N,K,G", [(16, 128, 128), (40, 384, 128), (1000, 512, 256)])
+def test_packed_layout_holds_the_codes(bits, signed, N, K, G):
+    d = syn.wnwide(11 + bits, 1, N, K, bits, signed, G=G)
+    desc = hq.desc_wnwide(N, K, bits, signed, group_size=G, bf16=False)
+    wb, sb, zb, _ = hq.hq_repacked_bytes(desc)
+    Np = (N + 15) // 16 * 16
+    slots = (Np // 16) * (K // 128) * 64
+    e = bits - 4
+    high = slots * 16 if e == 4 else (slots * 8 if e >= 2 else 0) + (slots * 4 if e != 2 else 0)
+    assert wb == slots * 16 + high
+    wp, sp, zp = hq.hq_repack(desc, d["codes"], d["s"], d.get("z"))
+    lo = codes_of_4bit_words(wp[:slots * 16], False, Np, K)
+    hi = codes_of_4bit_words(wp[slots * 16:], False, Np, K) if e == 4 else planes_to_codes(wp[slots * 16:], e, False, Np, K)
+    u = lo | (hi << 4)                                    # the code's bits, unsigned
+    want = codes_in_chunk_order(d["codes"], Np, K)
+    if signed:
+        u = np.where(u >= 1 << (bits - 1), u - (1 << bits), u)
+    np.testing.assert_array_equal(u, want)
+    # scales: the 16-bit layout of the 4-bit formats
+    d4 = hq.desc_w4a16(N, K, G, bf16=False, zp=False)
+    _, s4, _ = hq.hq_repack(d4, np.zeros((K // 8, N), dtype=np.uint32), d["s"])
+    np.testing.assert_array_equal(sp, s4)
+    if signed:
+        assert zp is None and zb == 0
+    else:
+        # UINT8 zero-points [Np/16][K/G][16 columns], padding columns 0
+        ng = K // G
+        assert zb == (Np // 16) * ng * 16
+        z = np.zeros((ng, Np), dtype=np.uint8)
+        z[:, :N] = d["z"]
+        np.testing.assert_array_equal(zp.reshape(Np // 16, ng, 16), z.reshape(ng, Np // 16, 16).transpose(1, 0, 2))
+
+
+def test_layout_hand_walkthrough_uint8():
+    """16 columns x 128 K of UINT8, code(k, n) = 16 k + n (mod 256).  Lane 0
+    (column 0, K 0..31): the low nibbles are 0 throughout; the high nibble of
+    k is k mod 16, so sub-step 0 holds high nibbles 0..7 and sub-step 1 8..15,
+    in the pair order of the 4-bit words (nibble p holds j = 0,2,4,6,1,3,5,7):
+    word 0 = 0x75316420, word 1 = 0xFDB9ECA8."""
+    N, K = 16, 128
+    codes = ((16 * np.arange(K)[:, None] + np.arange(N)[None, :]) % 256).astype(np.uint8)
+    s = np.full((1, N), 0x3C00, dtype=np.uint16)
+    z = np.zeros((1, N), dtype=np.uint8)
+    wp, _, zp = hq.hq_repack(hq.desc_wnwide(N, K, 8, False, bf16=False), codes, s, z)
+    lo = wp[:64 * 16].view(np.uint32).reshape(64, 4)
+    hi = wp[64 * 16:].view(np.uint32).reshape(64, 4)
+    assert (lo[0] == 0).all()
+    assert hi[0, 0] == 0x75316420 and hi[0, 1] == 0xFDB9ECA8 and hi[0, 2] == 0x75316420
+    # lane 1: column 1, low nibble 1 everywhere
+    assert (lo[1] == 0x11111111).all()
+    assert zp.size == 16 and not zp.any()
+
+
+@pytest.mark.parametrize("bits,signed", WIDTHS)
+def test_repack_rejects_codes_outside_the_width(bits, signed):
+    N, K = 32, 256
+    d = syn.wnwide(1, 1, N, K, bits, signed)
+    desc = hq.desc_wnwide(N, K, bits, signed)
+    if bits == 8:
+        return                                            # every byte is a code at 8 bits
+    bad = [1 << (bits - 1), -(1 << (bits - 1)) - 1] if signed else [1 << bits, 255]
+    for v in bad:
+        c = d["codes"].astype(np.int64)
+        c[K - 1, N - 1] = v
+        c = c.astype(np.int8) if signed else c.astype(np.uint8)
+        with pytest.raises(hq.HQError) as e:
+            hq.hq_repack(desc, c, d["s"], d.get("z"))
+        assert e.value.status == hq.HQ_ERR_INVALID_ARG
+    if not signed:
+        z = d["z"].copy()
+        z[0, 0] = 1 << bits                               # a zero-point outside the width
+        with pytest.raises(hq.HQError):
+            hq.hq_repack(desc, d["codes"], d["s"], z)
+
+
+@pytest.mark.parametrize("bits", [5, 6, 7, 8])
+def test_plans_stream_natively_and_dequantise_for_the_tiles(bits):
+    N, K = 4096, 4096
+    desc = hq.desc_wnwide(N, K, bits, bits % 2 == 1, bf16=bits < 7)
+    small = hq.hq_gemm_plan(desc, 4)
+    assert f",w{bits}>" in small[0] and not any("widen" in p for p in small)
+    big = hq.hq_gemm_plan(desc, 1024)
+    assert big[0].startswith(f"widen_wide_kernel<{bits},") and "tile_gemm_kernel<W16_" in big[1]
+    assert "128,128" in big[1]
+    wide = (N // 16) * (K // 128) * 4096
+    assert hq.hq_workspace_bytes(desc, 1024) >= wide
+    assert hq.hq_workspace_bytes(desc, 4) < wide
+    mid = hq.hq_gemm_plan(desc, 128)
+    if "splits=1" not in mid[1]:
+        sp = int(mid[1].split("splits=")[1].split()[0])
+        assert hq.hq_workspace_bytes(desc, 128) >= ((wide + 255) // 256 * 256) + sp * 128 * N * 4
+    with pytest.raises(hq.HQError):
+        hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_STREAM8, 0)), 4)
+    with pytest.raises(hq.HQError):
+        hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_W128, 0)), 1024)
+    forced = hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_T128, 2)), 1024)
+    assert "tile_gemm_kernel<W16_" in forced[1] and "splits=2" in forced[1]
