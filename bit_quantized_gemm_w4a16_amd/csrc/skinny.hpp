@@ -1026,20 +1026,16 @@ inline hipError_t launch_widen_lowbit(const void* planes, void* out, int wbits, 
     return hipGetLastError();
 }
 
-// 5- to 8-bit WnA16 codes -> 16-bit weights q - z (exact in fp16 and bf16:
-// |q - z| < 256), for the tiled kernels, which apply the group scales to their
-// fp32 partials: per strip and chunk, four 1 KB fragments (one per K sub-step)
-// of 64 lanes x 8 values.  One thread per lane slot.  (Rounding (q - z) * s to
-// bf16 here instead would cost the bf16 results about 2^-9 of each weight.)
-template <int WB, bool BF>
-__global__ __launch_bounds__(256) void widen_wide_kernel(const char* __restrict__ planes, const uint8_t* __restrict__ Z,
-                                                         v4u* __restrict__ out, int64_t slots, int nc, int ngroups,
-                                                         int gchunks, bool sgn) {
+// 5- to 8-bit WnA16 codes -> one byte per code, u = q (unsigned) or q + 128
+// (signed), in the INT8 weight-only layout, for the tiled kernels (which
+// subtract the zero-point, 128 for signed codes, and apply the group scales to
+// their fp32 partials): per strip and chunk two 1 KB halves of 64 lanes x 16 B,
+// half h of lane l holding K = 32 (l >> 4) + 16 h + 0..15.  One thread per lane slot.
+template <int WB>
+__global__ __launch_bounds__(256) void widen_wide_kernel(const char* __restrict__ planes, v4u* __restrict__ out,
+                                                         int64_t slots, bool sgn) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // slot = (strip * chunks + chunk) * 64 + lane
     if (i >= slots) return;
-    const int col = (int)(i & 15);
-    const int64_t sc = i >> 6, st = sc / nc;
-    const int64_t sg = st * ngroups + (int)(sc - st * nc) / gchunks;  // strip * groups + group
     const v4u wl = __builtin_nontemporal_load((const v4u*)planes + i);
     const char* hp = planes + (size_t)slots * 16;
     v4u wh = v4u{0u, 0u, 0u, 0u};
@@ -1053,48 +1049,58 @@ __global__ __launch_bounds__(256) void widen_wide_kernel(const char* __restrict_
         }
         if constexpr (WB != 6) wh[2] = __builtin_nontemporal_load((const uint32_t*)(hp + (WB == 7 ? (size_t)slots * 8 : 0)) + i);
     }
-    uint32_t z = 1u << (WB - 1);
-    if (sgn) {  // two's complement -> offset binary: flip the top bit
+    // signed codes: the two's-complement code plus 2^(WB-1) (top bit flipped) is
+    // the offset-binary value; plus 128 - 2^(WB-1) more makes q + 128
+    const uint32_t add = sgn ? 128u - (1u << (WB - 1)) : 0u;
+    if (sgn) {
         const uint32_t m4 = WB == 8 ? 0x88888888u : 0u, m2 = WB == 6 ? 0xAAAAAAAAu : m4;
         const uint32_t m1 = WB == 5 || WB == 7 ? 0xFFFFFFFFu : m4;
         wh[0] ^= m2;
         wh[1] ^= m2;
         wh[2] ^= m1;
         wh[3] ^= m4;
-    } else {
-        z = Z[sg * 16 + col];
     }
-    const uint32_t nb = (0xE400u | z) * 0x10001u;  // -(1024 + z), both halves
-    v4u* o = out + (i >> 6) * 256 + (i & 63);
+    v4u o[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) o[t * 64] = deq_wide<WB, BF>(wl, wh, t, nb).u;
+    for (int t = 0; t < 4; ++t) {
+        // the code values 0..255 as exact fp16 integers (1024 + code - 1024)
+        const Frag8 d = deq_wide<WB, false>(wl, wh, t, 0xE400E400u);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t x = d.u[2 * h + e];
+                const uint32_t lo = (uint32_t)bits16_to_f32<false>((uint16_t)(x & 0xFFFFu)) + add;
+                const uint32_t hi = (uint32_t)bits16_to_f32<false>((uint16_t)(x >> 16)) + add;
+                w |= (lo | (hi << 8)) << (16 * e);
+            }
+            o[t >> 1][2 * (t & 1) + h] = w;
+        }
+    }
+    v4u* dst = out + (i >> 6) * 128 + (i & 63);
+    dst[0] = o[0];
+    dst[64] = o[1];
 }
 
-inline hipError_t launch_widen_wide(const void* planes, const void* Z, void* out, int wbits, bool bf16,
-                                    int64_t Np, int64_t K, int group_size, hipStream_t st) {
+inline hipError_t launch_widen_wide(const void* planes, void* out, int wbits, bool is_signed, int64_t Np, int64_t K,
+                                    hipStream_t st) {
     const int64_t slots = (Np / 16) * (K / 128) * 64, blocks = (slots + 255) / 256;
     if (plan_recorder()) {
-        plan_record("widen_wide_kernel<%d,%s> grid=%lld", wbits, bf16 ? "bf16" : "f16", (long long)blocks);
+        plan_record("widen_wide_kernel<%d> grid=%lld", wbits, (long long)blocks);
         return hipSuccess;
     }
-    if (blocks > 0x7FFFFFFF || group_size < 128 || group_size % 128 || K % group_size) return hipErrorInvalidValue;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 g((unsigned)blocks), b(256);
-    const int nc = (int)(K / 128), ng = (int)(K / group_size), gc = group_size / 128;
-    const bool sgn = Z == nullptr;
     const char* w = (const char*)planes;
-    const uint8_t* z = (const uint8_t*)Z;
     v4u* o = (v4u*)out;
-#define HQ_WIDE(WBV)                                                                                              \
-    if (bf16) hipLaunchKernelGGL((widen_wide_kernel<WBV, true>), g, b, 0, st, w, z, o, slots, nc, ng, gc, sgn); \
-    else hipLaunchKernelGGL((widen_wide_kernel<WBV, false>), g, b, 0, st, w, z, o, slots, nc, ng, gc, sgn);
     switch (wbits) {
-        case 5: HQ_WIDE(5) break;
-        case 6: HQ_WIDE(6) break;
-        case 7: HQ_WIDE(7) break;
-        case 8: HQ_WIDE(8) break;
+        case 5: hipLaunchKernelGGL(widen_wide_kernel<5>, g, b, 0, st, w, o, slots, is_signed); break;
+        case 6: hipLaunchKernelGGL(widen_wide_kernel<6>, g, b, 0, st, w, o, slots, is_signed); break;
+        case 7: hipLaunchKernelGGL(widen_wide_kernel<7>, g, b, 0, st, w, o, slots, is_signed); break;
+        case 8: hipLaunchKernelGGL(widen_wide_kernel<8>, g, b, 0, st, w, o, slots, is_signed); break;
         default: return hipErrorInvalidValue;
     }
-#undef HQ_WIDE
     return hipGetLastError();
 }
 
@@ -1199,23 +1205,20 @@ hipError_t dense_dispatch(const DenseArgs& a, SkinnyArgs s, TileArgs p, int G) {
             return e;
         }
         if (a.wbits > 4) {
-            // 5-8-bit widths on the tiles: the codes widen to 16-bit q - z at the
-            // front of the workspace, 128 x 128 tiles read them with the group
-            // scales as they are, partial tiles follow
-            constexpr Fmt W = F == Fmt::WNA16_BF16 ? Fmt::W16_BF16 : Fmt::W16_F16;
-            const size_t wide = (size_t)(a.Np / 16) * (size_t)(a.K / 128) * 4096, off = (wide + 255) & ~(size_t)255;
+            // 5-8-bit widths on the tiles: the codes widen to one byte each in the
+            // INT8 weight-only layout at the front of the workspace, the INT8
+            // weight-only tiles read them with the group scales and UINT8
+            // zero-points as they are, partial tiles follow
+            constexpr Fmt W = F == Fmt::WNA16_BF16 ? Fmt::W8G_BF16 : Fmt::W8G_F16;
+            const size_t wide = (size_t)(a.Np / 16) * (size_t)(a.K / 128) * 2048, off = (wide + 255) & ~(size_t)255;
             TilePlan wp = plan_tile(a.M, a.Np, a.K, has_big_tile(W), has_wide256_tile(W), has_wide_tile(W), wide256_min_tiles(W));
-            if (tile_forced) {
-                if (a.tune_path != TUNE_T128) return hipErrorNotSupported;
-                wp.forced = a.tune_path;
-                wp.splits = a.tune_splits;
-            }
-            hipError_t e = launch_widen_wide(a.w, a.z, a.ws, a.wbits, F == Fmt::WNA16_BF16, a.Np, a.K, G, a.stream);
+            wp.forced = pl.forced;
+            wp.splits = tile_forced ? pl.splits : wp.splits;
+            hipError_t e = launch_widen_wide(a.w, a.ws, a.wbits, a.z == nullptr, a.Np, a.K, a.stream);
             if (e != hipSuccess) return e;
             plan_workspace(wide);
             plan_workspace_base(off);
             p.W = a.ws;
-            p.Z = nullptr;
             p.part = (char*)a.ws + off;
             e = launch_dense_plan<W>(wp, p, a.stream);
             plan_workspace_base(0);

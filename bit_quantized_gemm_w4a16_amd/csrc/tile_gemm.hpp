@@ -62,7 +62,7 @@ namespace hq {
 
 enum class Fmt { WNA16_F16, WNA16_BF16, W4A8_MX, W8A8_I8, MOE_MX, W4A8_MXA, W4A4_MX, W8A8_F8B, MXFP4_BF16, NVFP4_BF16,
                  MXINT4_BF16, W8A16_F16, W8A16_BF16, F8W_F16, F8W_BF16, MXF8_BF16, MXF6E2_BF16, MXF6E3_BF16,
-                 MXFP4_F16, NVFP4_F16, MXINT4_F16, MXF8_F16, MXF6E2_F16, MXF6E3_F16, W16_F16, W16_BF16 };
+                 MXFP4_F16, NVFP4_F16, MXINT4_F16, MXF8_F16, MXF6E2_F16, MXF6E3_F16, W8G_F16, W8G_BF16 };
 
 constexpr const char* fmt_name(Fmt F) {
     return F == Fmt::WNA16_F16 ? "WNA16_F16" : F == Fmt::WNA16_BF16 ? "WNA16_BF16" : F == Fmt::W4A8_MX ? "W4A8_MX"
@@ -73,7 +73,7 @@ constexpr const char* fmt_name(Fmt F) {
          : F == Fmt::F8W_BF16 ? "F8W_BF16" : F == Fmt::MXF8_BF16 ? "MXF8_BF16" : F == Fmt::MXF6E2_BF16 ? "MXF6E2_BF16"
          : F == Fmt::MXF6E3_BF16 ? "MXF6E3_BF16" : F == Fmt::MXFP4_F16 ? "MXFP4_F16" : F == Fmt::NVFP4_F16 ? "NVFP4_F16"
          : F == Fmt::MXINT4_F16 ? "MXINT4_F16" : F == Fmt::MXF8_F16 ? "MXF8_F16" : F == Fmt::MXF6E2_F16 ? "MXF6E2_F16"
-         : F == Fmt::MXF6E3_F16 ? "MXF6E3_F16" : F == Fmt::W16_F16 ? "W16_F16" : "W16_BF16";
+         : F == Fmt::MXF6E3_F16 ? "MXF6E3_F16" : F == Fmt::W8G_F16 ? "W8G_F16" : "W8G_BF16";
 }
 // Formats whose activations carry OCP MX scales (E8M0 per 32 K, [rows][K/32]).
 constexpr bool mx_act(Fmt F) { return F == Fmt::W4A8_MXA || F == Fmt::W4A4_MX; }
@@ -112,11 +112,11 @@ template <> struct FmtTraits<Fmt::MXINT4_F16> { static constexpr int AROW = 256,
 template <> struct FmtTraits<Fmt::MXF8_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::MXF6E2_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 template <> struct FmtTraits<Fmt::MXF6E3_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
-// 16-bit weights (5- to 8-bit WnA16 codes less their zero-points, q - z, exact
-// in fp16 and bf16): a lane's 8 values of one K sub-step per 16-byte fragment,
-// four fragments per strip and step; the group scales stay in the W4A16 layout
-template <> struct FmtTraits<Fmt::W16_F16> { static constexpr int AROW = 256, BSTRIP = 4096; using Acc = v4f; };
-template <> struct FmtTraits<Fmt::W16_BF16> { static constexpr int AROW = 256, BSTRIP = 4096; using Acc = v4f; };
+// 5- to 8-bit WnA16 codes rewritten as bytes u (q, or q + 128 for signed codes)
+// in the INT8 weight-only layout; the group scales in the W4A16 layout and, for
+// unsigned codes, the UINT8 zero-points [Np/16][K/group][16]
+template <> struct FmtTraits<Fmt::W8G_F16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
+template <> struct FmtTraits<Fmt::W8G_BF16> { static constexpr int AROW = 256, BSTRIP = 2048; using Acc = v4f; };
 // 8-bit weight-only formats: INT8 or FP8 (E4M3) codes in the same layout, per-channel fp32 scale
 constexpr bool f8w(Fmt F) { return F == Fmt::F8W_F16 || F == Fmt::F8W_BF16; }
 constexpr bool w8a16(Fmt F) { return F == Fmt::W8A16_F16 || F == Fmt::W8A16_BF16 || f8w(F); }
@@ -133,12 +133,12 @@ constexpr bool mxint4w(Fmt F) { return F == Fmt::MXINT4_BF16 || F == Fmt::MXINT4
 // operands, fp16 MFMA and output; the others of these families are bf16)
 constexpr bool f16_operand(Fmt F) {
     return F == Fmt::MXFP4_F16 || F == Fmt::NVFP4_F16 || F == Fmt::MXINT4_F16 || F == Fmt::MXF8_F16 ||
-           F == Fmt::MXF6E2_F16 || F == Fmt::MXF6E3_F16 || F == Fmt::W16_F16;
+           F == Fmt::MXF6E2_F16 || F == Fmt::MXF6E3_F16 || F == Fmt::W8G_F16;
 }
-// 16-bit (q - z) weight operands (no decode; group scales on the fp32 partials)
-constexpr bool w16(Fmt F) { return F == Fmt::W16_F16 || F == Fmt::W16_BF16; }
+// byte codes with group scales and zero-points (group scales on the fp32 partials)
+constexpr bool w8g(Fmt F) { return F == Fmt::W8G_F16 || F == Fmt::W8G_BF16; }
 // 8-bit weight codes in the INT8 weight-only layout (two 16-byte halves per lane and chunk)
-constexpr bool w8load(Fmt F) { return w8a16(F) || mxf8(F); }
+constexpr bool w8load(Fmt F) { return w8a16(F) || mxf8(F) || w8g(F); }
 // e2m1 weights converted to bf16 operands with a per-lane scale (bf16 MFMA)
 constexpr bool fp4w(Fmt F) { return F == Fmt::MOE_MX || mxfp4w(F) || nvfp4(F) || mxint4w(F); }
 
@@ -513,6 +513,33 @@ __device__ __forceinline__ Frag8 fp8_to_bf16_scaled(const v4u& half, int pair, f
     return f;
 }
 
+// Bytes u -> u - z, exact (|u - z| < 256): fp16 by u under the exponent of 1024
+// and one packed add of -(1024 + z) (nbz, both halves); bf16 through fp32.  8
+// codes (one K sub-step) of a lane's 16-byte half.
+template <bool BF>
+__device__ __forceinline__ Frag8 deq8_zp(const v4u& half, int pair, uint32_t nbz, float zf) {
+    const uint32_t w0 = half[2 * pair], w1 = half[2 * pair + 1];
+    Frag8 f;
+    if constexpr (BF) {
+        typedef float f2v __attribute__((ext_vector_type(2)));
+        typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = i < 2 ? w0 : w1;
+            const float lo = (float)((w >> (16 * (i & 1))) & 0xFFu) - zf;
+            const float hi = (float)((w >> (16 * (i & 1) + 8)) & 0xFFu) - zf;
+            f.u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2v{lo, hi}, b2v));
+        }
+    } else {
+        const v2h nb = __builtin_bit_cast(v2h, nbz);
+        f.u[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)) + nb);
+        f.u[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u)) + nb);
+        f.u[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u)) + nb);
+        f.u[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u)) + nb);
+    }
+    return f;
+}
+
 // 8 codes (one K sub-step) of a lane's 16-byte half: INT8 or E4M3
 template <Fmt F>
 __device__ __forceinline__ Frag8 deq8(const v4u& half, int pair) {
@@ -561,9 +588,10 @@ __attribute__((amdgpu_waves_per_eu(1, BM < 128 ? 4 : WM * WN <= 4 ? 1 : 2)))
 void tile_gemm_kernel(TileArgs p) {
     using T = FmtTraits<F>;
     using Acc = typename T::Acc;
-    // group scales (and UINT4 zero-points) staged per step; the 16-bit (q - z)
-    // weights take the scales only (their zero-point buffer is null: reads zeros)
-    constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || w16(F);
+    // group scales and zero-points staged per step (UINT4 words, or the byte
+    // codes' UINT8 zero-points: 16 bytes per strip)
+    constexpr bool WNA16 = F == Fmt::WNA16_F16 || F == Fmt::WNA16_BF16 || w8g(F);
+    constexpr int ZB = w8g(F) ? 16 : 8;  // zero-point bytes per strip and group
     constexpr bool NV = nvfp4(F);                         // E4M3 weight scales per 16 K
     constexpr bool MX = mx_mfma(F) || fp4w(F) || mxf8(F);  // byte scales per lane
     static_assert(!mxf6(F), "MXFP6 reaches the tiles widened to MXFP8");
@@ -682,7 +710,7 @@ void tile_gemm_kernel(TileArgs p) {
     const uint32_t nbn = (uint32_t)((p.Np + 127) / 128);  // weight column blocks (blockwise fp8)
     const rsrc_t rS = make_rsrc(Sbase, WNA16 ? nstr * (uint32_t)p.ngroups * 32u : MX ? nstr * (uint32_t)nsteps * (NV ? 128u : 64u)
                                        : F8B ? (uint32_t)nsteps * nbn * 4u : 0u);
-    const rsrc_t rZ = make_rsrc(p.Z, WNA16 && p.Z ? nstr * (uint32_t)p.ngroups * 8u : 0u);
+    const rsrc_t rZ = make_rsrc(p.Z, WNA16 && p.Z ? nstr * (uint32_t)p.ngroups * (uint32_t)ZB : 0u);
 
     // per-thread byte offsets of the staged loads (fixed across K steps).  Dense
     // A rows are consecutive: one lane offset serves every load, load i adding
@@ -715,7 +743,7 @@ void tile_gemm_kernel(TileArgs p) {
     constexpr int SPT = NV ? 8 : 4;
     constexpr uint32_t SBYTES = NV ? 128u : 64u;  // scale bytes per strip and step
     const uint32_t sc_strip = (uint32_t)clamp_strip(strip0 + (WNA16 ? (tid < 2 * NSTRIP ? tid / 2 : tid - 2 * NSTRIP) : tid / SPT));
-    const uint32_t soff = WNA16 ? (tid < 2 * NSTRIP ? sc_strip * p.ngroups * 32u + (tid & 1) * 16u : sc_strip * p.ngroups * 8u)
+    const uint32_t soff = WNA16 ? (tid < 2 * NSTRIP ? sc_strip * p.ngroups * 32u + (tid & 1) * 16u : sc_strip * p.ngroups * (uint32_t)ZB)
                                 : sc_strip * (uint32_t)nsteps * SBYTES + (tid % SPT) * 16u;
 
     auto stage_lds = [&](auto stc) -> lds_char* {
@@ -782,9 +810,13 @@ void tile_gemm_kernel(TileArgs p) {
                 // the load would make the wave wait for it at once); without
                 // zero-points the buffer range is empty and the load reads zeros,
                 // which the symmetric decode ignores
-                const uint64_t z = buf8(rZ, soff, g * 8u);
-                rs[st][0] = (uint32_t)z;
-                rs[st][1] = (uint32_t)(z >> 32);
+                if constexpr (ZB == 16) {
+                    rs[st] = buf16(rZ, soff, g * 16u);
+                } else {
+                    const uint64_t z = buf8(rZ, soff, g * 8u);
+                    rs[st][0] = (uint32_t)z;
+                    rs[st][1] = (uint32_t)(z >> 32);
+                }
             }
         } else if constexpr (SC_DMA) {
             lds_char* sc = stage_lds(setc) + A_STAGE + B_STAGE;
@@ -808,8 +840,10 @@ void tile_gemm_kernel(TileArgs p) {
         if constexpr (SC_STAGE > 0 && !SC_DMA) {
             if constexpr (WNA16) {
                 if (tid < 2 * NSTRIP) *(v4u*)(sS + tid * 16) = rs[st];
-                else if (tid < 3 * NSTRIP)
-                    *(uint64_t*)(sS + SC_Z + (tid - 2 * NSTRIP) * 8) = ((uint64_t)rs[st][1] << 32) | rs[st][0];
+                else if (tid < 3 * NSTRIP) {
+                    if constexpr (ZB == 16) *(v4u*)(sS + SC_Z + (tid - 2 * NSTRIP) * 16) = rs[st];
+                    else *(uint64_t*)(sS + SC_Z + (tid - 2 * NSTRIP) * 8) = ((uint64_t)rs[st][1] << 32) | rs[st][0];
+                }
             } else if constexpr (F8B) {
                 if (tid <= BM) *(uint32_t*)(sS + tid * 4) = rsa[st];
             } else {
@@ -856,6 +890,7 @@ void tile_gemm_kernel(TileArgs p) {
     // scale block of a step: this lane's column in the wave's first strip
     const uint32_t sc_lane = (uint32_t)(wn * NT * 32 + col * 2), z_lane = (uint32_t)(wn * NT * 8 + (col >> 3) * 4);
     const uint32_t zshift = 4u * (uint32_t)(col & 7), zmask = p.Z ? 15u : 0u, zsym = p.Z ? 0u : 8u;
+    const uint32_t zsym8 = p.Z ? 0u : 128u;  // byte codes: signed ones are stored as q + 128
     constexpr int NBH = T::BSTRIP / 1024;  // 16-byte fragments per strip and step (two for INT8)
     // compute(stage, hook): hook(t) runs at the start of K sub-step t = 0..3,
     // after the step's scale block has been read from LDS; the pipelines issue
@@ -877,7 +912,22 @@ void tile_gemm_kernel(TileArgs p) {
             // 16-bit A with 4-bit weights decoded into the operand: fp16 (q - z) * s,
             // or e2m1 x (2^(E-127) or an E4M3 value) -> bf16 (exact)
             constexpr bool MOE = fp4w(F) || mxf8(F);  // 16-bit operands under the lane's E8M0 or E4M3 scale
-            constexpr bool BFA = (MOE && !f16_operand(F)) || w8bf(F);  // bf16 MFMA (else fp16)
+            constexpr bool BFA = (MOE && !f16_operand(F)) || w8bf(F) || F == Fmt::W8G_BF16;  // bf16 MFMA (else fp16)
+            // byte codes with group scales: each step's MFMA partials (st) take the
+            // column's group scale at the end of the step (a step lies inside one group)
+            constexpr bool GS = w8g(F);
+            Acc st[GS ? MT : 1][GS ? NT : 1];
+            if constexpr (GS) {
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) st[i][j] = Acc{0.f, 0.f, 0.f, 0.f};
+            }
+            auto mma = [&](int i, int j, const Frag8& a, const Frag8& b) {
+                if constexpr (GS) st[i][j] = mfma16<BFA>(a, b, st[i][j]);
+                else acc[i][j] = mfma16<BFA>(a, b, acc[i][j]);
+            };
+            float zf[GS ? NT : 1];
             // A fragments read ahead (software pipeline): a whole sub-step, or
             // a ring of three for tall / wide wave tiles
             Frag8 afr[(NT >= 4 || MT > 8) ? 1 : 2][(NT >= 4 || MT > 8) ? 3 : MT];
@@ -895,6 +945,13 @@ void tile_gemm_kernel(TileArgs p) {
                     sf[j][0] = e8m0_to_f32(((const uint8_t*)sS)[(wn * NT + j) * 64 + lane]);
                 } else if constexpr (w8a16(F)) {
                     // per-channel scale in the epilogue: nothing per step
+                } else if constexpr (GS) {
+                    // the column's group scale and zero-point (128 for signed codes,
+                    // whose zero-point buffer is null and reads zeros)
+                    sf[j][0] = bits16_to_f32<BFA>(*(const uint16_t*)(sS + sc_lane + j * 32));
+                    const uint32_t z = (uint32_t)((const uint8_t*)(sS + SC_Z))[(wn * NT + j) * 16 + col] | zsym8;
+                    zf[j] = (float)z;
+                    nb2[j] = (0xE400u | z) * 0x10001u;  // -(1024 + z), both halves
                 } else {
                     // one lane offset for every strip (strips are immediate offsets); the
                     // zero-point select is branch-free (symmetric INT4: z = 8)
@@ -912,6 +969,7 @@ void tile_gemm_kernel(TileArgs p) {
                 if constexpr (NV) return fp4_to_bf16_mul<BFA>(bw[j][0][tt], sf[j][tt >> 1]);
                 else if constexpr (mxint4w(F)) return int4_to_bf16<BFA>(bw[j][0][tt], sf[j][0]);
                 else if constexpr (mxf8(F)) return fp8_to_bf16_scaled<BFA>(bw[j][tt >> 1], tt & 1, sf[j][0]);
+                else if constexpr (GS) return deq8_zp<BFA>(bw[j][tt >> 1], tt & 1, nb2[j], GS ? zf[j] : 0.f);
                 else if constexpr (w8a16(F)) return deq8<F>(bw[j][tt >> 1], tt & 1);
                 else if constexpr (MOE) return fp4_to_bf16<BFA>(bw[j][0][tt], sf[j][0]);
                 else return deq4_f16_scaled(bw[j][0][tt] ^ wx, nb2[j], nh2[j], s2[j]);
@@ -941,7 +999,7 @@ void tile_gemm_kernel(TileArgs p) {
                             bq[(t + 1) & 1][i] = mkb(i, t + 1);
                         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<BFA>(afr[0][q % 3], bq[t & 1][j], acc[i][j]);
+                        for (int j = 0; j < NT; ++j) mma(i, j, afr[0][q % 3], bq[t & 1][j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 } else {
@@ -966,7 +1024,7 @@ void tile_gemm_kernel(TileArgs p) {
 #pragma unroll
                     for (int i = 0; i < MT; ++i)
 #pragma unroll
-                        for (int j = 0; j < NT; ++j) acc[i][j] = mfma16<BFA>(afr[t & 1][i], bq[t & 1][j], acc[i][j]);
+                        for (int j = 0; j < NT; ++j) mma(i, j, afr[t & 1][i], bq[t & 1][j]);
                     if (t < 3) {
                         // per A fragment: its read, the MFMAs of one fragment of
                         // this sub-step, a share of the next sub-step's dequant
@@ -980,39 +1038,12 @@ void tile_gemm_kernel(TileArgs p) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-        } else if constexpr (w16(F)) {
-            // (q - z) operands as loaded; each step's MFMA partial takes the
-            // column's group scale (a step lies inside one group)
-            constexpr bool BF = F == Fmt::W16_BF16;
+            if constexpr (GS) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) hook(t);
-            float sc[NT];
+                for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) sc[j] = bits16_to_f32<BF>(((const uint16_t*)sS)[(wn * NT + j) * 16 + col]);
-            v4f st[MT][NT];
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int j = 0; j < NT; ++j) st[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-#pragma unroll
-                for (int i = 0; i < MT; ++i) {
-                    const int row = wm * (BM / WM) + i * 16 + col;
-                    Frag8 a;
-                    a.u = *(const v4u*)(sA + row * AROW + (((4 * quad + t) ^ swz(row, AUNITS)) * 16));
-#pragma unroll
-                    for (int j = 0; j < NT; ++j) {
-                        Frag8 b;
-                        b.u = bw[j][t];
-                        st[i][j] = mfma16<BF>(a, b, st[i][j]);
-                    }
-                }
+                    for (int j = 0; j < NT; ++j) acc[i][j] += sf[j][0] * st[i][j];
             }
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int j = 0; j < NT; ++j) acc[i][j] += sc[j] * st[i][j];
         } else if constexpr (F == Fmt::WNA16_BF16) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) hook(t);
@@ -1546,14 +1577,17 @@ hipError_t launch_tile_kernel(TileArgs p, hipStream_t st) {
 // halves the A traffic per flop and still fits two LDS stages.  bf16 A has no
 // 256-row variant (its row-sum MFMA needs a second accumulator set).
 // INT8 weight-only: 256-row tiles do not fit two stages of its 2 KB weight strips
-constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16 && !w8load(F) && !mxf6(F) && !w16(F); }
+constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16 && !w8load(F) && !mxf6(F); }
 // fp16 A with 4-bit weights: 8 waves side by side, each dequantising its own
 // weight strips once: 256 x 256 tiles of 256 x 32 waves with a single weight
 // stage (each dequantised fragment feeds 16 MFMAs; 13 % faster than 128 x 256
 // at M = 8192), or 128 x 256 tiles of 128 x 32 waves where 256 x 256 would not
 // cover the chip (a K step loads 48 KB instead of the 80 KB of 256 x 128).
+// (Not the byte codes with group scales: the 128 x 256 tile's second set of
+// per-step accumulators spills, 172 bytes per lane, and ran 1.34x slower than
+// 128 x 128 tiles at M = 8192.)
 constexpr bool has_wide_tile(Fmt F) {
-    return F == Fmt::WNA16_F16 || mxfp4w(F) || nvfp4(F) || mxint4w(F) || w8load(F) || mxf6(F);
+    return F == Fmt::WNA16_F16 || mxfp4w(F) || nvfp4(F) || mxint4w(F) || (w8load(F) && !w8g(F)) || mxf6(F);
 }
 // INT8: 256 x 256 on 8 waves of 128 x 64, direct loads into two full stages
 // (M = 8192: 1126 us vs 1569 us for 256 x 128 with register-staged loads); the

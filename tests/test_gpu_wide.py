@@ -3,9 +3,10 @@ zero-points, 16-bit group scales; bf16 and fp16 activations) against the CPU
 oracle, through the C ABI.
 
 Small M runs the weight stream on the packed codes (the 4-bit word set plus the
-high bits); larger M first rewrites the codes as 16-bit q - z values in the
-workspace and runs the 128 x 128 tiles on them, which apply the group scales to
-their fp32 partials.  N = 1000 and 4100 end in a partial 16-column strip."""
+high bits); larger M first rewrites the codes as bytes in the
+workspace (u = q, or q + 128 for signed codes, in the INT8 weight-only layout)
+and runs the INT8 weight-only tiles on them, which subtract the zero-points
+exactly in the decode and apply the group scales to each step's fp32 partials.  N = 1000 and 4100 end in a partial 16-column strip."""
 import numpy as np
 import pytest
 import torch

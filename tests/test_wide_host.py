@@ -136,9 +136,8 @@ def test_plans_stream_natively_and_dequantise_for_the_tiles(bits):
     small = hq.hq_gemm_plan(desc, 4)
     assert f",w{bits}>" in small[0] and not any("widen" in p for p in small)
     big = hq.hq_gemm_plan(desc, 1024)
-    assert big[0].startswith(f"widen_wide_kernel<{bits},") and "tile_gemm_kernel<W16_" in big[1]
-    assert "128,128" in big[1]
-    wide = (N // 16) * (K // 128) * 4096
+    assert big[0].startswith(f"widen_wide_kernel<{bits}>") and "tile_gemm_kernel<W8G_" in big[1]
+    wide = (N // 16) * (K // 128) * 2048
     assert hq.hq_workspace_bytes(desc, 1024) >= wide
     assert hq.hq_workspace_bytes(desc, 4) < wide
     mid = hq.hq_gemm_plan(desc, 128)
@@ -148,6 +147,8 @@ def test_plans_stream_natively_and_dequantise_for_the_tiles(bits):
     with pytest.raises(hq.HQError):
         hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_STREAM8, 0)), 4)
     with pytest.raises(hq.HQError):
-        hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_W128, 0)), 1024)
+        hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_T256, 0)), 1024)
     forced = hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_T128, 2)), 1024)
-    assert "tile_gemm_kernel<W16_" in forced[1] and "splits=2" in forced[1]
+    assert "tile_gemm_kernel<W8G_" in forced[1] and ",128,128," in forced[1] and "splits=2" in forced[1]
+    with pytest.raises(hq.HQError):
+        hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_W128, 0)), 1024)
