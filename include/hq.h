@@ -46,7 +46,7 @@
  *  - A workspace is needed only where hq_workspace_bytes() says so (split-K
  *    partial tiles, MoE routing metadata, and at larger M the weights of the
  *    1-3-bit, 5-8-bit and MXFP6 formats rewritten in the layout the tiled
- *    kernels read: 4-bit words, 16-bit q - z values, or MXFP8 codes).  Every kernel writes what it later
+ *    kernels read: 4-bit words, one byte per code, or MXFP8 codes).  Every kernel writes what it later
  *    reads within the same call, so its contents need no initialisation and
  *    are meaningless between calls.  Two calls that share a workspace must not
  *    run concurrently.
