@@ -69,6 +69,9 @@ static int e0m_width(int w) {
         case HQ_DT_E0M1: return 1;
         case HQ_DT_E0M2: return 2;
         case HQ_DT_E0M3: return 3;
+        case HQ_DT_E0M4: return 4;
+        case HQ_DT_E0M5: return 5;
+        case HQ_DT_E0M6: return 6;
         case HQ_DT_E0M7: return 7;
         default: return 0;
     }
@@ -77,8 +80,12 @@ static int e0m_width(int w) {
 // code width and signedness of the 5-8-bit WnA16 dtypes (0 for the others; INT8
 // is one of them only with 16-bit group scales)
 static int wide_width(int w, int scale_dtype, bool* is_signed) {
-    *is_signed = w == HQ_DT_INT5 || w == HQ_DT_INT6 || w == HQ_DT_INT7 || w == HQ_DT_INT8;
+    *is_signed = w == HQ_DT_INT5 || w == HQ_DT_INT6 || w == HQ_DT_INT7 || w == HQ_DT_INT8 || w == HQ_DT_E0M4 ||
+                 w == HQ_DT_E0M5 || w == HQ_DT_E0M6;
     switch (w) {
+        case HQ_DT_E0M4: return 5;  // e0m4..e0m6: sign and magnitude, converted at repack
+        case HQ_DT_E0M5: return 6;  // to the two's-complement codes of width n + 1
+        case HQ_DT_E0M6: return 7;
         case HQ_DT_INT5: case HQ_DT_UINT5: return 5;
         case HQ_DT_INT6: case HQ_DT_UINT6: return 6;
         case HQ_DT_INT7: case HQ_DT_UINT7: return 7;
@@ -150,6 +157,7 @@ hq_status describe(const hq_layer_desc* d, LayerInfo* L) {
         I.kind = Kind::WNA16;
         I.a_bf16 = a == HQ_DT_BF16;
         I.bits = wide_width(w, d->w_scale_dtype, &wide_signed);
+        I.e0m = e0m_width(w);
         I.zp = I.zp8 = !wide_signed;
         if (d->num_experts) return set_error(HQ_ERR_UNSUPPORTED, "WnA16 at 5-8 bits is dense-only");
         if (d->w_scale_dtype != a) return set_error(HQ_ERR_UNSUPPORTED, "WnA16 scale dtype must equal the activation dtype");
@@ -463,8 +471,8 @@ hq_status hq_repack(const hq_layer_desc* desc, const void* w, const void* scale,
                 return set_error(HQ_ERR_INVALID_ARG, "FP6 code 0x%02x at k=%lld n=%lld has bits above bit 5", c[i],
                                  (long long)(i / L.N), (long long)(i % L.N));
     }
-    if (L.e0m == 1 || L.e0m == 2) {
-        // e0m1 / e0m2 codes, one per byte: the sign bit n and n magnitude bits
+    if (L.e0m && L.e0m != 3 && L.e0m != 7) {
+        // e0m1 / e0m2 / e0m4..e0m6 codes, one per byte: the sign bit n and n magnitude bits
         const uint8_t* c = (const uint8_t*)w;
         for (int64_t i = 0; i < L.K * L.N; ++i)
             if (c[i] >> (L.e0m + 1))

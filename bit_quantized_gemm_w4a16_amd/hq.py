@@ -25,7 +25,7 @@ HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_ALIGNMENT, HQ_ERR_WORKSPAC
 (HQ_DT_NONE, HQ_DT_BF16, HQ_DT_FP16, HQ_DT_FP32, HQ_DT_FP8_E4M3, HQ_DT_INT8, HQ_DT_INT4, HQ_DT_UINT4,
  HQ_DT_FP4_E2M1, HQ_DT_E8M0, HQ_DT_INT32, HQ_DT_INT1, HQ_DT_UINT1, HQ_DT_INT2, HQ_DT_UINT2, HQ_DT_INT3,
  HQ_DT_UINT3, HQ_DT_FP6_E2M3, HQ_DT_FP6_E3M2, HQ_DT_E0M1, HQ_DT_E0M2, HQ_DT_E0M3, HQ_DT_E0M7, HQ_DT_INT5, HQ_DT_UINT5,
- HQ_DT_INT6, HQ_DT_UINT6, HQ_DT_INT7, HQ_DT_UINT7, HQ_DT_UINT8) = range(30)
+ HQ_DT_INT6, HQ_DT_UINT6, HQ_DT_INT7, HQ_DT_UINT7, HQ_DT_UINT8, HQ_DT_E0M4, HQ_DT_E0M5, HQ_DT_E0M6) = range(33)
 HQ_GRAN_NONE, HQ_GRAN_PER_GROUP_K, HQ_GRAN_PER_CHANNEL, HQ_GRAN_BLOCK_128x128 = range(4)
 HQ_ASCALE_NONE, HQ_ASCALE_PER_TOKEN_F32, HQ_ASCALE_MX_E8M0, HQ_ASCALE_PER_BLOCK128_F32 = range(4)
 HQ_S2_NONE, HQ_S2_PER_TENSOR_F32 = 0, 1
@@ -155,10 +155,10 @@ def desc_mxf_a16(N, K, elem, bf16: bool = True) -> hq_layer_desc:
 
 
 def desc_e0m(N, K, n, group_size=128, bf16=True) -> hq_layer_desc:
-    """Zero-exponent float weights e0mN: n = 1, 2, 3 with 16-bit group scales (the
+    """Zero-exponent float weights e0mN: n = 1..6 with 16-bit group scales (the
     WnA16 kernels of width n + 1), n = 7 with fp32 per-channel scales (INT8 weight-only)."""
     a = HQ_DT_BF16 if bf16 else HQ_DT_FP16
-    w = {1: HQ_DT_E0M1, 2: HQ_DT_E0M2, 3: HQ_DT_E0M3, 7: HQ_DT_E0M7}[n]
+    w = {1: HQ_DT_E0M1, 2: HQ_DT_E0M2, 3: HQ_DT_E0M3, 4: HQ_DT_E0M4, 5: HQ_DT_E0M5, 6: HQ_DT_E0M6, 7: HQ_DT_E0M7}[n]
     if n == 7:
         return make_desc(N, K, a, w, HQ_DT_FP32, HQ_GRAN_PER_CHANNEL, K, a)
     return make_desc(N, K, a, w, a, HQ_GRAN_PER_GROUP_K, group_size, a)

@@ -115,7 +115,10 @@ typedef enum hq_dtype {
     HQ_DT_UINT6 = 26,    /* 0..63                                      */
     HQ_DT_INT7 = 27,     /* -64..63                                    */
     HQ_DT_UINT7 = 28,    /* 0..127                                     */
-    HQ_DT_UINT8 = 29     /* 0..255; also the 8-bit zero-point dtype    */
+    HQ_DT_UINT8 = 29,    /* 0..255; also the 8-bit zero-point dtype    */
+    HQ_DT_E0M4 = 30,     /* -15..15, one code per byte                 */
+    HQ_DT_E0M5 = 31,     /* -31..31, one code per byte                 */
+    HQ_DT_E0M6 = 32      /* -63..63, one code per byte                 */
 } hq_dtype;
 
 typedef enum hq_scale_gran {
@@ -156,6 +159,7 @@ typedef enum hq_moe_mode {
  *   BF16|FP16 INT5|INT6|INT7|INT8  same as a_dtype, PER_GROUP_K  NONE  NONE  a_dtype (5-8-bit WnA16)
  *   BF16|FP16 UINT5|UINT6|UINT7|UINT8  same, PER_GROUP_K  UINT8  NONE     a_dtype (5-8-bit WnA16)
  *   BF16|FP16 E0M1|E0M2|E0M3  same as a_dtype, PER_GROUP_K  NONE  NONE  a_dtype (e0mN: the INT2/3/4 kernels)
+ *   BF16|FP16 E0M4|E0M5|E0M6  same as a_dtype, PER_GROUP_K  NONE  NONE  a_dtype (e0mN: the INT5/6/7 kernels)
  *   BF16|FP16 E0M7       FP32, PER_CHANNEL             NONE    NONE      a_dtype (e0m7: the INT8 kernels)
  *   BF16|FP16 FP8_E4M3   E8M0, PER_GROUP_K, group 32   NONE    NONE      a_dtype (MXFP8 weight-only)
  *   BF16|FP16 FP6_E2M3|FP6_E3M2  E8M0, PER_GROUP_K, 32  NONE   NONE      a_dtype (MXFP6 weight-only)
@@ -277,9 +281,9 @@ hq_status hq_repacked_bytes(const hq_layer_desc* desc, size_t* w_bytes, size_t* 
  *      UINT8 zero-points (below).
  *      e0mN ("Humming wird angekuendigt": the zero-exponent float whose values
  *      are the symmetric integers of its width): e0m3 in the 4-bit word layout
- *      above, e0m1 / e0m2 / e0m7 one code per byte [K][N]; bit n is the sign,
+ *      above, e0m1 / e0m2 / e0m4..e0m7 one code per byte [K][N]; bit n is the sign,
  *      bits 0..n-1 the magnitude.  The repack stores each code as the two's-
- *      complement code of width n + 1 (INT2, INT3, INT4, INT8) and the kernels of
+ *      complement code of width n + 1 (INT2 .. INT8) and the kernels of
  *      that width run it; a code with a bit above bit n is HQ_ERR_INVALID_ARG.
  *      MXFP8 / MXFP6: E4M3 / E2M3 / E3M2 codes, one per byte [K][N] (FP6 in the
  *      low six bits, a higher bit is HQ_ERR_INVALID_ARG); E8M0 [K/32][N].

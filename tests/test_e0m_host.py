@@ -22,7 +22,7 @@ def e0m_codes(rng, n, K, N):
     return rng.integers(0, 1 << (n + 1), size=(K, N)).astype(np.uint8)
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 7])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7])
 def test_descriptor_validation(n):
     d = hq.desc_e0m(1024, 1024, n)
     hq.hq_desc_validate(d)
@@ -39,7 +39,7 @@ def test_descriptor_validation(n):
         hq.hq_desc_validate(bad)
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 7])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("N,K", [(16, 128), (40, 384), (1000, 256)])
 def test_repack_equals_the_twos_complement_container(n, N, K):
     rng = np.random.default_rng([n, N, K])
@@ -54,6 +54,7 @@ def test_repack_equals_the_twos_complement_container(n, N, K):
         w_in = words_of(codes.astype(np.int64), K, N) if n == 3 else codes
         got = hq.hq_repack(hq.desc_e0m(N, K, n), w_in, s)
         want = (hq.hq_repack(hq.desc_w4a16(N, K, 128, bf16=True, zp=False), words_of(ints, K, N), s) if n == 3
+                else hq.hq_repack(hq.desc_wnwide(N, K, n + 1, True), ints, s) if n >= 4
                 else hq.hq_repack(hq.desc_wnlow(N, K, n + 1, True), ints, s))
     for g, w in zip(got, want):
         if w is None:
@@ -62,7 +63,7 @@ def test_repack_equals_the_twos_complement_container(n, N, K):
             np.testing.assert_array_equal(g, w)
 
 
-@pytest.mark.parametrize("n", [1, 2])
+@pytest.mark.parametrize("n", [1, 2, 4, 5, 6])
 def test_repack_rejects_bits_above_the_sign(n):
     N, K = 32, 128
     codes = np.zeros((K, N), np.uint8)
@@ -75,6 +76,8 @@ def test_repack_rejects_bits_above_the_sign(n):
 def test_plans_are_those_of_the_container():
     N, K = 4096, 4096
     for n, ref in ((3, hq.desc_w4a16(N, K, 128, bf16=True, zp=False)), (2, hq.desc_wnlow(N, K, 3, True)),
-                   (1, hq.desc_wnlow(N, K, 2, True)), (7, hq.desc_w8a16(N, K, bf16=True))):
+                   (1, hq.desc_wnlow(N, K, 2, True)), (7, hq.desc_w8a16(N, K, bf16=True)),
+                   (4, hq.desc_wnwide(N, K, 5, True)), (5, hq.desc_wnwide(N, K, 6, True)),
+                   (6, hq.desc_wnwide(N, K, 7, True))):
         for M in (1, 64, 1024):
             assert hq.hq_gemm_plan(hq.desc_e0m(N, K, n), M) == hq.hq_gemm_plan(ref, M)

@@ -1,5 +1,5 @@
 """GPU parity of the zero-exponent float weights e0mN (sign bit and integer
-magnitude: e0m1..e0m3 with 16-bit group scales on the WnA16 kernels of width
+magnitude: e0m1..e0m6 with 16-bit group scales on the WnA16 kernels of width
 n + 1, e0m7 with fp32 per-channel scales on the INT8 weight-only kernels)
 against the CPU oracle (its e0mN decode, then the integer GEMM of the
 container), through the C ABI."""
@@ -14,7 +14,7 @@ from gpu_util import GATE, dev, empty, gate_error, note, sample_rows, to_f64
 
 pytestmark = pytest.mark.gpu
 
-CASES = [(M, N, K, n, bf) for n in (1, 2, 3, 7) for bf in (True, False)
+CASES = [(M, N, K, n, bf) for n in (1, 2, 3, 4, 5, 6, 7) for bf in (True, False)
          for M, N, K in ((1, 272, 1024), (24, 272, 1024), (300, 1000, 512))]
 
 
@@ -43,7 +43,10 @@ def test_e0m_matches_the_oracle(M, N, K, n, bf):
         s = torch.from_numpy((np.abs(rng.standard_normal((K // 128, N))) * 0.02 + 1e-3).astype(np.float32)).to(dt)
         s = s.view(torch.int16).numpy().view(np.uint16)
         packed = hq.hq_repack(desc, words_of(codes.astype(np.int64), K, N) if n == 3 else codes, s)
-        if n == 3:
+        if n >= 4:
+            ref = lambda r: oracle.gemm_wnwide(A, ints, s, None, N=N, K=K, G=128, bits=n + 1, a_bf16=bf,
+                                               w_signed=True, rows=r)
+        elif n == 3:
             ref = lambda r: oracle.gemm_wna16(A, words_of(ints, K, N), s, None, N=N, K=K, G=128, a_bf16=bf,
                                               w_signed=True, rows=r)
         else:

@@ -981,7 +981,7 @@ def test_e0m7_values_are_int8_without_minus_128():
     assert vals.count(0) == 2 and all(vals.count(v) == 1 for v in range(-127, 128) if v)
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 7])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7])
 def test_e0m_sign_and_magnitude(n):
     """Every magnitude m < 2^n appears once with each sign (the sign bit is bit n,
     the magnitude the low n bits: code m and code 2^n + m negate each other); a
