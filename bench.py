@@ -200,7 +200,7 @@ class DenseWnWide(DenseWnLow):
         f = f"WNA16_{self.dtype.upper()}"
         if M <= 64:
             return (f"skinny_kernel<{f},w{self.bits}> (M<=64)", "hbm")
-        return (f"widen_wide_kernel<{self.bits}> + tile_gemm_kernel<W16_{self.dtype.upper()}> (M>64)",
+        return (f"widen_wide_kernel<{self.bits}> + tile_gemm_kernel<W8G_{self.dtype.upper()}> (M>64)",
                 "mfma" if M >= 128 else "hbm")
 
     def cpu_baseline(self, budget_s=8.0):
