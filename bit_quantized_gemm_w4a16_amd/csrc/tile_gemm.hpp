@@ -913,9 +913,12 @@ void tile_gemm_kernel(TileArgs p) {
             // or e2m1 x (2^(E-127) or an E4M3 value) -> bf16 (exact)
             constexpr bool MOE = fp4w(F) || mxf8(F);  // 16-bit operands under the lane's E8M0 or E4M3 scale
             constexpr bool BFA = (MOE && !f16_operand(F)) || w8bf(F) || F == Fmt::W8G_BF16;  // bf16 MFMA (else fp16)
-            // byte codes with group scales: each step's MFMA partials (st) take the
-            // column's group scale at the end of the step (a step lies inside one group)
-            constexpr bool GS = w8g(F);
+            // bf16 byte codes with group scales: each step's MFMA partials (st) take
+            // the column's group scale at the end of the step (a step lies inside one
+            // group); fp16 ones take it in the decode, (q - z) * s rounded once to
+            // fp16 as for the 4-bit codes (no second accumulator set, so the 128 x 256
+            // tile fits its registers)
+            constexpr bool GS = F == Fmt::W8G_BF16;
             Acc st[GS ? MT : 1][GS ? NT : 1];
             if constexpr (GS) {
 #pragma unroll
@@ -945,12 +948,14 @@ void tile_gemm_kernel(TileArgs p) {
                     sf[j][0] = e8m0_to_f32(((const uint8_t*)sS)[(wn * NT + j) * 64 + lane]);
                 } else if constexpr (w8a16(F)) {
                     // per-channel scale in the epilogue: nothing per step
-                } else if constexpr (GS) {
+                } else if constexpr (w8g(F)) {
                     // the column's group scale and zero-point (128 for signed codes,
                     // whose zero-point buffer is null and reads zeros)
-                    sf[j][0] = bits16_to_f32<BFA>(*(const uint16_t*)(sS + sc_lane + j * 32));
+                    const uint32_t sc = *(const uint16_t*)(sS + sc_lane + j * 32);
+                    sf[j][0] = bits16_to_f32<BFA>((uint16_t)sc);
+                    s2[j] = sc | (sc << 16);
                     const uint32_t z = (uint32_t)((const uint8_t*)(sS + SC_Z))[(wn * NT + j) * 16 + col] | zsym8;
-                    zf[j] = (float)z;
+                    if constexpr (GS) zf[j] = (float)z;
                     nb2[j] = (0xE400u | z) * 0x10001u;  // -(1024 + z), both halves
                 } else {
                     // one lane offset for every strip (strips are immediate offsets); the
@@ -969,7 +974,16 @@ void tile_gemm_kernel(TileArgs p) {
                 if constexpr (NV) return fp4_to_bf16_mul<BFA>(bw[j][0][tt], sf[j][tt >> 1]);
                 else if constexpr (mxint4w(F)) return int4_to_bf16<BFA>(bw[j][0][tt], sf[j][0]);
                 else if constexpr (mxf8(F)) return fp8_to_bf16_scaled<BFA>(bw[j][tt >> 1], tt & 1, sf[j][0]);
-                else if constexpr (GS) return deq8_zp<BFA>(bw[j][tt >> 1], tt & 1, nb2[j], GS ? zf[j] : 0.f);
+                else if constexpr (GS) return deq8_zp<true>(bw[j][tt >> 1], tt & 1, nb2[j], zf[j]);
+                else if constexpr (w8g(F)) {
+                    Frag8 f = deq8_zp<false>(bw[j][tt >> 1], tt & 1, nb2[j], 0.f);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t x = f.u[u];  // (a bit cast of a vector element reads element 0)
+                        f.u[u] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h, x) * __builtin_bit_cast(v2h, s2[j]));
+                    }
+                    return f;
+                }
                 else if constexpr (w8a16(F)) return deq8<F>(bw[j][tt >> 1], tt & 1);
                 else if constexpr (MOE) return fp4_to_bf16<BFA>(bw[j][0][tt], sf[j][0]);
                 else return deq4_f16_scaled(bw[j][0][tt] ^ wx, nb2[j], nh2[j], s2[j]);
@@ -1583,11 +1597,11 @@ constexpr bool has_big_tile(Fmt F) { return F != Fmt::WNA16_BF16 && !w8load(F) &
 // stage (each dequantised fragment feeds 16 MFMAs; 13 % faster than 128 x 256
 // at M = 8192), or 128 x 256 tiles of 128 x 32 waves where 256 x 256 would not
 // cover the chip (a K step loads 48 KB instead of the 80 KB of 256 x 128).
-// (Not the byte codes with group scales: the 128 x 256 tile's second set of
-// per-step accumulators spills, 172 bytes per lane, and ran 1.34x slower than
-// 128 x 128 tiles at M = 8192.)
+// (Not the bf16 byte codes with group scales: the 128 x 256 tile's second set
+// of per-step accumulators spills, 172 bytes per lane, and ran 1.34x slower
+// than 128 x 128 tiles at M = 8192.)
 constexpr bool has_wide_tile(Fmt F) {
-    return F == Fmt::WNA16_F16 || mxfp4w(F) || nvfp4(F) || mxint4w(F) || (w8load(F) && !w8g(F)) || mxf6(F);
+    return F == Fmt::WNA16_F16 || mxfp4w(F) || nvfp4(F) || mxint4w(F) || (w8load(F) && F != Fmt::W8G_BF16) || mxf6(F);
 }
 // INT8: 256 x 256 on 8 waves of 128 x 64, direct loads into two full stages
 // (M = 8192: 1126 us vs 1569 us for 256 x 128 with register-staged loads); the

@@ -110,8 +110,11 @@ def test_tuned_paths_and_row_offset(bits, signed, bf16):
     """Forced K splits on the 128 x 128 tiles and on the stream, and rows taken
     from an offset into the activations."""
     L = Wide(160, 1000, 3072, 128, bits, signed, bf16, seed=3)
-    for tune, M in ((hq.HQ_TUNE(hq.HQ_TUNE_T128, 3), 150), (hq.HQ_TUNE(hq.HQ_TUNE_T128, 1), 40),
-                    (hq.HQ_TUNE(hq.HQ_TUNE_STREAM, 2), 9)):
+    tunes = [(hq.HQ_TUNE(hq.HQ_TUNE_T128, 3), 150), (hq.HQ_TUNE(hq.HQ_TUNE_T128, 1), 40),
+             (hq.HQ_TUNE(hq.HQ_TUNE_STREAM, 2), 9)]
+    if not bf16:     # fp16 also has the 128 x 256 tiles
+        tunes += [(hq.HQ_TUNE(hq.HQ_TUNE_W128, 2), 150), (hq.HQ_TUNE(hq.HQ_TUNE_W128, 1), 20)]
+    for tune, M in tunes:
         d = autotune.with_tune(L.desc, tune)
         note(f"wnwide tuned bits={bits} M={M} {hq.hq_gemm_plan(d, M)}")
         L.check(L.run(d, M), np.arange(M))

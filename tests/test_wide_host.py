@@ -150,5 +150,9 @@ def test_plans_stream_natively_and_dequantise_for_the_tiles(bits):
         hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_T256, 0)), 1024)
     forced = hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_T128, 2)), 1024)
     assert "tile_gemm_kernel<W8G_" in forced[1] and ",128,128," in forced[1] and "splits=2" in forced[1]
-    with pytest.raises(hq.HQError):
-        hq.hq_gemm_plan(autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_W128, 0)), 1024)
+    wide = autotune.with_tune(desc, hq.HQ_TUNE(hq.HQ_TUNE_W128, 0))
+    if bits < 7:     # bf16: 128 x 128 tiles only (group scales on per-step partials)
+        with pytest.raises(hq.HQError):
+            hq.hq_gemm_plan(wide, 1024)
+    else:            # fp16: the group scale in the decode, 128 x 256 tiles too
+        assert "tile_gemm_kernel<W8G_F16,128,256," in hq.hq_gemm_plan(wide, 1024)[1]
